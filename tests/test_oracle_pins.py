@@ -1,0 +1,440 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: a worked
+example printed on the pages (tests/golden/), a closed form, an identity, a
+special case that reduces to a textbook computation, or brute force on tiny
+inputs.  No GPU is needed.
+"""
+import itertools
+import json
+import math
+from pathlib import Path
+
+import numpy as np
+import pytest
+from scipy.special import softmax as sp_softmax, ndtr
+
+import oracle as O
+
+GOLD = Path(__file__).parent / "golden"
+
+
+def _rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- bf16 format
+
+def test_bf16_rounding_known_values():
+    vals = np.array([1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -2.0,
+                     1.0 + 2.0 ** -8 + 2.0 ** -20, 3.140625, 0.0, -0.0])
+    bits = O.f64_to_bf16_bits(vals)
+    # 1+2^-8 is halfway between 1 and 1+2^-7: ties to the even mantissa (1.0);
+    # 1+3*2^-8 is halfway between 1+2^-7 (odd) and 1+2^-6 (even).
+    assert [hex(int(b)) for b in bits] == ["0x3f80", "0x3f80", "0x3f82", "0xc000",
+                                          "0x3f81", "0x4049", "0x0", "0x8000"]
+    assert O.bf16_to_f64(np.array([0x3F80, 0x4049, 0xC000], np.uint16)).tolist() == [1.0, 3.140625, -2.0]
+
+
+def test_bf16_roundtrip_exact():
+    bits = np.arange(0, 0x7F80, 7, dtype=np.uint16)  # finite positive patterns
+    assert np.array_equal(O.f64_to_bf16_bits(O.bf16_to_f64(bits)), bits)
+
+
+# ---------------------------------------------------------------- capacity
+
+def test_capacity_table():
+    for c in json.loads((GOLD / "capacity.json").read_text())["cases"]:
+        assert O.capacity(c["T"], c["k"], c["E"], c["cf"]) == c["capacity"], c
+
+
+def test_capacity_is_smallest_integer_bound():
+    rng = _rng(1)
+    for _ in range(300):
+        T = int(rng.integers(0, 5000))
+        k = int(rng.integers(1, 9))
+        E = int(rng.integers(1, 100))
+        a = int(rng.integers(1, 64))
+        C = O.capacity(T, k, E, a / 16.0)               # cf = a/16 is exact in binary
+        # smallest integer C with 16*E*C >= T*k*a, clamped to T
+        c0 = -(-(T * k * a) // (16 * E))
+        assert C == min(c0, T)
+        assert 16 * E * C >= min(T * k * a, 16 * E * T)
+
+
+# ---------------------------------------------------------------- RMSNorm / r-scale
+
+def test_rmsnorm_closed_forms():
+    x = np.array([[3.0, 4.0], [2.0, 2.0], [0.0, 0.0]])
+    r = O.rmsnorm_scale(x, 0.0 + 1e-6)
+    assert r[0] == pytest.approx(1.0 / math.sqrt(12.5 + 1e-6), rel=1e-15)
+    assert r[1] == pytest.approx(1.0 / math.sqrt(4.0 + 1e-6), rel=1e-15)
+    assert r[2] == pytest.approx(1.0 / math.sqrt(1e-6), rel=1e-15)
+    # scale invariance (eps = 0) and unit RMS of the normalised output
+    z = _rng(2).standard_normal((5, 33))
+    assert np.allclose(O.rmsnorm_scale(7.5 * z, 0.0), O.rmsnorm_scale(z, 0.0) / 7.5, rtol=1e-14)
+    y = O.rmsnorm(z, None, 0.0)
+    assert np.allclose(np.sqrt(np.mean(y * y, axis=1)), 1.0, rtol=1e-14)
+    g = _rng(3).standard_normal(33)
+    assert np.allclose(O.rmsnorm(z, g, 0.0), y * g, rtol=1e-14)
+
+
+def test_r_scale_epilogue_equals_unfused_rmsnorm():
+    rng = _rng(4)
+    x = rng.standard_normal((40, 64))
+    gamma = 1 + 0.1 * rng.standard_normal(64)
+    w = 0.02 * rng.standard_normal((64, 6))
+    b = rng.standard_normal(6)
+    r = O.rmsnorm_scale(x, 1e-6)
+    fused = O.router_logits(x, gamma, r, w, b)
+    unfused = O.router_logits_unfused(x, gamma, 1e-6, w, b)
+    assert np.max(np.abs(fused - unfused)) <= 1e-12 * np.max(np.abs(unfused))
+
+
+# ---------------------------------------------------------------- top-k and gates
+
+def _brute_topk(l, k):
+    """Best ordered k-tuple of distinct experts by the key sequence (l desc, e asc)."""
+    best, best_key = None, None
+    for perm in itertools.permutations(range(len(l)), k):
+        key = [(l[e], -e) for e in perm]
+        if best_key is None or key > best_key:
+            best, best_key = perm, key
+    return list(best)
+
+
+def test_topk_bruteforce_with_ties():
+    rng = _rng(5)
+    for E in range(1, 7):
+        for k in range(1, E + 1):
+            l = rng.integers(-2, 3, size=(12, E)).astype(np.float64)  # many exact ties
+            ids = O.select_topk(l, k)
+            for t in range(l.shape[0]):
+                assert ids[t].tolist() == _brute_topk(l[t].tolist(), k)
+
+
+def test_topk_crafted_ties_go_to_lower_index():
+    assert O.select_topk(np.array([[1.0, 3.0, 3.0, 2.0]]), 2).tolist() == [[1, 2]]
+    assert O.select_topk(np.array([[5.0, 5.0, 5.0, 5.0]]), 3).tolist() == [[0, 1, 2]]
+    assert O.select_topk(np.array([[0.0, -0.0, 1.0]]), 2).tolist() == [[2, 0]]
+    assert O.select_topk(np.array([[-1.0, -3.0, -2.0]]), 1).tolist() == [[0]]
+
+
+def test_gates_properties():
+    rng = _rng(6)
+    l = rng.standard_normal((30, 8)) * 3
+    for k in (1, 2, 5, 8):
+        ids = O.select_topk(l, k)
+        g = O.gates(l, ids, renorm=1)
+        assert np.allclose(g.sum(axis=1), 1.0, rtol=1e-14)
+        assert np.all(np.diff(g, axis=1) <= 0)           # slot 0 is the best
+        full = np.take_along_axis(sp_softmax(l, axis=1), ids.astype(np.int64), axis=1)
+        assert np.allclose(O.gates(l, ids, renorm=0), full, rtol=1e-13)
+    ids = O.select_topk(l, 8)
+    assert np.allclose(O.gates(l, ids, 1), O.gates(l, ids, 0), rtol=1e-13)
+    assert np.all(O.gates(l, O.select_topk(l, 1), 1) == 1.0)
+
+
+# ---------------------------------------------------------------- dispatch
+
+def _dispatch_brute(ids, E, cap, pad):
+    T, k = ids.shape
+    rank = np.zeros((T, k), int)
+    for t in range(T):
+        for j in range(k):
+            rank[t, j] = sum(1 for t2 in range(t) for j2 in range(k) if ids[t2, j2] == ids[t, j])
+    counts = [int((ids == e).sum()) for e in range(E)]
+    kept = [min(c, cap) for c in counts]
+    offs = [0]
+    for e in range(E):
+        offs.append(offs[-1] + -(-kept[e] // pad) * pad)
+    pos = np.where(rank < cap, np.array(offs)[ids] + rank, -1)
+    return counts, kept, offs, rank, pos
+
+
+@pytest.mark.parametrize("cap,pad", [(1, 1), (3, 1), (100, 1), (2, 4), (100, 8)])
+def test_dispatch_bruteforce(cap, pad):
+    rng = _rng(7 + cap + pad)
+    T, E, k = 40, 5, 2
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    d = O.dispatch(ids, E, cap, pad)
+    counts, kept, offs, rank, pos = _dispatch_brute(ids, E, cap, pad)
+    assert d["counts"].tolist() == counts and sum(counts) == T * k
+    assert d["kept"].tolist() == kept
+    assert d["offsets"].tolist() == offs
+    assert np.array_equal(d["rank"], rank)
+    assert np.array_equal(d["pos"], pos)
+    assert set(zip(*np.nonzero(d["pos"] < 0))) == set(zip(*np.nonzero(rank >= cap)))
+    p = d["pos"][d["pos"] >= 0]
+    assert len(set(p.tolist())) == len(p)                          # injective
+    for e in range(E):
+        rows = d["row_token"][offs[e]:offs[e] + kept[e]]
+        assert np.all(np.diff(rows) > 0)                          # token order
+        assert np.all(d["row_token"][offs[e] + kept[e]:offs[e + 1]] == -1)   # padding
+        assert all(e in ids[t] for t in rows)                     # rows chose e
+    assert d["dropped"] == int((rank >= cap).sum())
+
+
+# ---------------------------------------------------------------- variable sizes / BCSR
+
+def test_expert_layout_worked_example():
+    g = json.loads((GOLD / "variable_experts_layout.json").read_text())
+    lay = O.expert_layout([tuple(s) for s in g["expert_sizes_spec"]], g["num_experts"], g["block_size"])
+    assert lay["sizes"] == g["expert_sizes"]
+    assert lay["offsets"] == g["expert_offsets"]
+    assert lay["total"] == g["total_expert_width"]
+    assert [g["n_embd"], lay["total"]] == g["w1_shape"]
+    assert lay["offsets"][0:2] == g["w1_columns_expert0"]
+    assert lay["offsets"][1:3] == g["w1_columns_expert1"]
+    assert lay["size_blocks"][:3] == g["expert_size_blocks_prefix"]
+    assert lay["block_offsets"][:3] == g["expert_block_offsets_prefix"]
+    with pytest.raises(ValueError):
+        O.expert_layout([(1, 2048), (6, 1024)], 8)
+    # sizes are rounded up to the block
+    assert O.expert_layout([(2, 100), (1, 129)], 3, 128)["sizes"] == [128, 128, 256]
+
+
+def test_topology_worked_example():
+    g = json.loads((GOLD / "variable_experts_layout.json").read_text())
+    lay = O.expert_layout([tuple(s) for s in g["expert_sizes_spec"]], 8, 128)
+    tb = [2, 1, 0, 3, 1, 1, 1, 2]                      # token blocks per expert
+    offsets = [0]
+    for n in tb:
+        offsets.append(offsets[-1] + 128 * n)
+    topo = O.bcsr_topology(offsets, lay["size_blocks"], lay["block_offsets"], 128)
+    assert topo["block_rows"] == sum(tb)
+    assert topo["nnz"] == sum(n * s for n, s in zip(tb, lay["size_blocks"]))
+    # first row block belongs to the 2048-wide expert: 16 column blocks 0..15
+    ro, ci = topo["row_offsets"], topo["column_indices"]
+    assert ci[ro[0]:ro[1]].tolist() == list(range(16))
+    assert ci[ro[1]:ro[2]].tolist() == list(range(16))
+    assert ci[ro[2]:ro[3]].tolist() == list(range(16, 24))       # expert 1
+    assert ci[ro[3]:ro[4]].tolist() == list(range(32, 40))       # expert 3 (expert 2 empty)
+    assert np.all(np.diff(ro) == np.repeat(lay["size_blocks"], tb))
+
+
+def test_topology_output_offsets_regression():
+    g = json.loads((GOLD / "output_offsets_regression.json").read_text())
+    sizes = g["expert_sizes"]
+    B = g["block_size"]
+    lay = O.expert_layout([(1, s) for s in sizes], len(sizes), B)
+    small = [g["token_blocks_small_total"] // 31] * 31
+    small[-1] += g["token_blocks_small_total"] - sum(small)
+    tb = small + [g["token_blocks_large"]]
+    offsets = [0]
+    for n in tb:
+        offsets.append(offsets[-1] + B * n)
+    topo = O.bcsr_topology(offsets, lay["size_blocks"], lay["block_offsets"], B)
+    large = len(sizes) - 1
+    assert topo["output_offsets"][large] == g["expected_large_output_offset"]
+    assert topo["output_offsets"][large] != g["buggy_large_output_offset"]
+    assert topo["nnz"] == g["token_blocks_small_total"] + 4 * g["token_blocks_large"]
+    first = topo["row_offsets"][sum(small)]
+    assert topo["column_indices"][first:first + 4].tolist() == [31, 32, 33, 34]
+
+
+@pytest.mark.parametrize("act,sizes", [("gelu", [256, 128, 384]), ("swiglu", [128, 256, 128]),
+                                       ("gelu", [256, 256, 256])])
+def test_bcsr_walk_equals_per_expert_dense(act, sizes):
+    rng = _rng(8)
+    T, d, E, k, B = 70, 64, 3, 2, 128
+    x = rng.standard_normal((T, d))
+    F = sum(sizes)
+    w1 = 0.05 * rng.standard_normal((d, F))
+    w3 = 0.05 * rng.standard_normal((d, F)) if act == "swiglu" else None
+    w2 = 0.05 * rng.standard_normal((F, d))
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)])
+    disp = O.dispatch(ids, E, T, B)
+    lay = O.expert_layout([(1, s) for s in sizes], E, B)
+    topo = O.bcsr_topology(disp["offsets"], lay["size_blocks"], lay["block_offsets"], B)
+    r = O.rmsnorm_scale(x, 1e-6)
+    rt = disp["row_token"]
+    x_perm = np.where(rt[:, None] >= 0, x[np.maximum(rt, 0)], 0.0)
+    r_perm = np.where(rt >= 0, r[np.maximum(rt, 0)], 0.0)
+    y_bcsr = O.bcsr_expert_ffn(x_perm, r_perm, topo, w1, w2, act, B, w3)
+    valid = rt >= 0
+    e_of_row = np.searchsorted(disp["offsets"], np.nonzero(valid)[0], side="right") - 1
+    y_dense = O.grouped_expert_ffn(x_perm[valid], r_perm[valid], e_of_row, w1, w2,
+                                   lay["offsets"], act, w3)
+    assert np.allclose(y_bcsr[valid], y_dense, rtol=1e-12, atol=1e-14)
+    assert np.all(y_bcsr[~valid] == 0)
+
+
+# ---------------------------------------------------------------- activations
+
+def test_activation_values():
+    assert O.gelu(0.0) == 0.0
+    assert float(O.gelu(1.0)) == pytest.approx(float(ndtr(1.0)), rel=1e-15)
+    assert float(O.gelu(1.0)) == pytest.approx(0.8413447460685429, rel=1e-15)
+    assert float(O.gelu(-1.0)) == pytest.approx(-0.15865525393145707, rel=1e-14)
+    assert float(O.gelu(40.0)) == 40.0 and float(O.gelu(-40.0)) == pytest.approx(0.0, abs=1e-300)
+    assert float(O.silu(1.0)) == pytest.approx(0.7310585786300049, rel=1e-15)
+    assert float(O.silu(0.0)) == 0.0
+    assert float(O.gelu_tanh(1.0)) == pytest.approx(0.8411919906082768, rel=1e-12)
+
+
+# ---------------------------------------------------------------- whole-layer special cases
+
+def _layer(rng, T, d, E, k, f, act, cf=0.0, renorm=1, gamma=False, bias=False):
+    p = dict(k=k, eps=1e-6, renorm=renorm, cf=cf, act=act, residual=True,
+             w_router=0.3 * rng.standard_normal((d, E)),
+             bias=rng.standard_normal(E) if bias else None,
+             gamma=(1 + 0.1 * rng.standard_normal(d)) if gamma else None,
+             w1=0.05 * rng.standard_normal((d, E * f)),
+             w2=0.05 * rng.standard_normal((E * f, d)),
+             f_offsets=[e * f for e in range(E + 1)])
+    if act == "swiglu":
+        p["w3"] = 0.05 * rng.standard_normal((d, E * f))
+    return p
+
+
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+def test_k_equals_E_is_dense_softmax_mixture(act):
+    rng = _rng(9)
+    T, d, E, f = 25, 32, 4, 48
+    p = _layer(rng, T, d, E, E, f, act, gamma=True, bias=True)
+    x = rng.standard_normal((T, d))
+    res = O.layer_forward(p, x)
+    xn = O.rmsnorm(x, p["gamma"], 1e-6)
+    prob = sp_softmax(xn @ p["w_router"] + p["bias"], axis=1)
+    dense = x.copy()
+    for e in range(E):
+        sl = slice(e * f, (e + 1) * f)
+        a = xn @ p["w1"][:, sl]
+        h = (a / (1 + np.exp(-a))) * (xn @ p["w3"][:, sl]) if act == "swiglu" else a * ndtr(a)
+        dense += prob[:, e:e + 1] * (h @ p["w2"][sl, :])
+    assert np.max(np.abs(res["out"] - dense)) <= 1e-12 * np.max(np.abs(dense))
+
+
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+def test_single_expert_is_dense_ffn(act):
+    rng = _rng(10)
+    T, d, f = 30, 48, 64
+    p = _layer(rng, T, d, 1, 1, f, act)
+    x = rng.standard_normal((T, d))
+    res = O.layer_forward(p, x)
+    assert np.all(res["w"] == 1.0)
+    xn = O.rmsnorm(x, None, 1e-6)
+    a = xn @ p["w1"]
+    h = (a / (1 + np.exp(-a))) * (xn @ p["w3"]) if act == "swiglu" else a * ndtr(a)
+    ref = x + h @ p["w2"]
+    assert np.max(np.abs(res["out"] - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_fully_dropped_tokens_pass_through_bit_exactly():
+    rng = _rng(11)
+    T, d, E, k = 64, 32, 4, 2
+    p = _layer(rng, T, d, E, k, 32, "gelu", cf=0.25)       # capacity 8 per expert
+    xb = O.f64_to_bf16_bits(rng.standard_normal((T, d)))
+    for faithful in (False, True):
+        res = O.layer_forward(p, xb, faithful=faithful)
+        assert res["capacity"] == 8
+        gone = np.all(res["pos"] < 0, axis=1)
+        assert gone.sum() > 0
+        assert np.array_equal(res["out"][gone], O.bf16_to_f64(xb[gone]))
+        kept_any = ~gone
+        assert not np.array_equal(res["out"][kept_any], O.bf16_to_f64(xb[kept_any]))
+
+
+def test_shared_experts_concatenate():
+    rng = _rng(12)
+    T, d, f = 20, 32, 40
+    x = rng.standard_normal((T, d))
+    r = O.rmsnorm_scale(x, 1e-6)
+    a1, a3, a2 = (0.05 * rng.standard_normal(s) for s in [(d, f), (d, f), (f, d)])
+    b1, b3, b2 = (0.05 * rng.standard_normal(s) for s in [(d, f), (d, f), (f, d)])
+    two = O.ffn(x, r, a1, a2, "swiglu", a3) + O.ffn(x, r, b1, b2, "swiglu", b3)
+    one = O.ffn(x, r, np.hstack([a1, b1]), np.vstack([a2, b2]), "swiglu", np.hstack([a3, b3]))
+    assert np.allclose(two, one, rtol=1e-12, atol=1e-15)
+
+
+def test_uniform_sizes_through_variable_spec_match_uniform():
+    a = O.expert_layout([(8, 1024)], 8, 128)
+    b = O.expert_layout(None, 8, 128, default_size=1024)
+    assert a == b
+
+
+# ---------------------------------------------------------------- Cartesian router / atomic experts
+
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_cartesian_two_stage_equals_bruteforce(dtype):
+    rng = _rng(13)
+    T, Nr, Nc, k = 24, 32, 32, 8
+    s1 = rng.standard_normal((T, Nr)).astype(dtype)
+    s2 = rng.standard_normal((T, Nc)).astype(dtype)
+    a, sa = O.cartesian_topk(s1, s2, k)
+    b, sb = O.cartesian_topk_bruteforce(s1, s2, k)
+    assert np.array_equal(a, b) and np.array_equal(sa, sb)
+    # integer scores: many exact ties, ties go to the lower flat index
+    s1 = rng.integers(-2, 3, (T, 6)).astype(dtype)
+    s2 = rng.integers(-2, 3, (T, 5)).astype(dtype)
+    for kk in (1, 4, 9):
+        assert np.array_equal(O.cartesian_topk(s1, s2, kk)[0], O.cartesian_topk_bruteforce(s1, s2, kk)[0])
+
+
+def test_cartesian_scores_are_row_plus_column():
+    rng = _rng(14)
+    T, d, Nr, Nc = 5, 16, 4, 3
+    x = rng.standard_normal((T, d))
+    Kr, Kc = rng.standard_normal((d, Nr)), rng.standard_normal((d, Nc))
+    r = O.rmsnorm_scale(x, 1e-6)
+    s1, s2 = O.cartesian_scores(x, None, r, Kr, Kc)
+    xn = O.rmsnorm(x, None, 1e-6)
+    for i in range(Nr):
+        for j in range(Nc):
+            # score of expert n = i*Nc + j, against a dense router with the concatenated key
+            assert np.allclose(s1[:, i] + s2[:, j], xn @ (Kr[:, i] + Kc[:, j]), rtol=1e-12)
+
+
+def test_atomic_all_experts_is_dense_gelu_ffn():
+    rng = _rng(15)
+    T, d, Nr, Nc = 10, 24, 4, 4
+    N = Nr * Nc
+    x = rng.standard_normal((T, d))
+    W, V = 0.3 * rng.standard_normal((N, d)), 0.3 * rng.standard_normal((N, d))
+    r = O.rmsnorm_scale(x, 1e-6)
+    ids = np.tile(np.arange(N), (T, 1))
+    g = sp_softmax(rng.standard_normal((T, N)), axis=1)
+    routed = O.atomic_experts_token_centric(x, r, ids, g, W, V)
+    xn = O.rmsnorm(x, None, 1e-6)
+    a = xn @ W.T
+    dense = (g * a * ndtr(a)) @ V
+    assert np.allclose(routed, dense, rtol=1e-12, atol=1e-14)
+
+
+def test_atomic_expert_centric_equals_token_centric():
+    rng = _rng(16)
+    T, d, N, k = 30, 16, 20, 5
+    x = rng.standard_normal((T, d))
+    W, V = rng.standard_normal((N, d)), rng.standard_normal((N, d))
+    r = O.rmsnorm_scale(x, 1e-6)
+    ids = np.stack([rng.choice(N, size=k, replace=False) for _ in range(T)])
+    g = sp_softmax(rng.standard_normal((T, k)), axis=1)
+    a = O.atomic_experts_token_centric(x, r, ids, g, W, V)
+    b = O.atomic_experts_expert_centric(x, r, ids, g, W, V)
+    assert np.allclose(a, b, rtol=1e-12, atol=1e-13)
+
+
+def test_cartesian_layer_matches_bruteforce_routing():
+    rng = _rng(17)
+    T, d, Nr, Nc, k = 12, 32, 8, 8, 6
+    p = dict(router="cartesian", k=k, eps=1e-6, act="gelu", residual=True,
+             k_rows=rng.standard_normal((d, Nr)), k_cols=rng.standard_normal((d, Nc)),
+             W=0.2 * rng.standard_normal((Nr * Nc, d)), V=0.2 * rng.standard_normal((Nr * Nc, d)),
+             ws1=0.05 * rng.standard_normal((d, 40)), ws2=0.05 * rng.standard_normal((40, d)),
+             shared_act="gelu")
+    x = rng.standard_normal((T, d))
+    res = O.layer_forward(p, x)
+    xn = O.rmsnorm(x, None, 1e-6)
+    full = np.stack([(xn @ p["k_rows"])[:, i:i + 1] + xn @ p["k_cols"] for i in range(Nr)], axis=1)
+    full = full.reshape(T, Nr * Nc)
+    for t in range(T):
+        # definition: the k best flat ids by (score desc, id asc), by a plain sort
+        assert res["ids"][t].tolist() == sorted(range(Nr * Nc), key=lambda n: (-full[t, n], n))[:k]
+    gg = sp_softmax(np.take_along_axis(full, res["ids"], axis=1), axis=1)
+    assert np.allclose(res["w"], gg, rtol=1e-12)
+    a = xn @ p["ws1"]
+    shared = (a * ndtr(a)) @ p["ws2"]
+    routed = np.stack([sum(gg[t, j] * O.gelu(xn[t] @ p["W"][n]) * p["V"][n]
+                           for j, n in enumerate(res["ids"][t])) for t in range(T)])
+    assert np.allclose(res["out"], x + shared + routed, rtol=1e-11, atol=1e-13)
