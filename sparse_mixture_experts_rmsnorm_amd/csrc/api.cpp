@@ -1,0 +1,960 @@
+// Host side of libmoe_mi355x: argument checks, workspace carving and the
+// launch sequence of the MoE layer forward.  Nothing here allocates device
+// memory or waits for the device (except the explicit timer read-out).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+#include "moe.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+int ok() {
+  g_err.clear();
+  return MOE_OK;
+}
+
+#define MOE_HIP(call)                                                                   \
+  do {                                                                                  \
+    hipError_t e_ = (call);                                                             \
+    if (e_ != hipSuccess) return fail(MOE_EHIP, "%s: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+#define REQUIRE(cond, code, ...) \
+  do {                           \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+size_t esize(int dtype) { return dtype == MOE_F32 ? 4 : 2; }
+
+// Bump allocator over a caller workspace (or a null base to measure).
+struct Carve {
+  char* base;
+  size_t used = 0;
+  explicit Carve(void* b) : base(static_cast<char*>(b)) {}
+  void* take(size_t bytes) {
+    void* p = base ? base + used : nullptr;
+    used += align_up(std::max<size_t>(bytes, 1));
+    return p;
+  }
+  template <typename T> T* take_n(int64_t n) { return static_cast<T*>(take(size_t(n) * sizeof(T))); }
+};
+
+bool valid_dtype(int dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+
+// ---------------------------------------------------------------- expert geometry
+
+struct ExpertGeo {
+  int64_t E = 0, F = 0, Fmax = 0;
+  int pf = 1;          // packed rows per hidden unit in the first linear
+  int bf1 = 256;       // packed weight rows per first-linear tile
+  int bf2 = 256;       // output features per second-linear tile
+  int bt = 256;        // GEMM rows per tile
+  int fold = 1;        // first-linear output columns = packed features / fold
+  bool bcsr = false, atomic = false;
+};
+
+int check_experts(const moe_experts_desc* X, int dtype, int64_t d, ExpertGeo* g) {
+  REQUIRE(X, MOE_EINVAL, "experts descriptor is NULL");
+  REQUIRE(valid_dtype(dtype), MOE_EDTYPE, "unknown dtype %d", dtype);
+  REQUIRE(X->kind >= MOE_EXPERTS_GROUPED && X->kind <= MOE_EXPERTS_ATOMIC, MOE_EDTYPE,
+          "unknown experts kind %d", X->kind);
+  REQUIRE(X->act >= MOE_ACT_GELU && X->act <= MOE_ACT_SWIGLU, MOE_EDTYPE, "unknown activation %d",
+          X->act);
+  REQUIRE(X->E >= 1, MOE_EINVAL, "experts E must be >= 1 (got %lld)", (long long)X->E);
+  ExpertGeo geo;
+  geo.E = X->E;
+  geo.bcsr = X->kind == MOE_EXPERTS_BCSR;
+  geo.atomic = X->kind == MOE_EXPERTS_ATOMIC;
+  if (geo.atomic) {
+    REQUIRE(dtype == MOE_BF16, MOE_EUNSUPPORTED, "atomic experts are implemented for bf16 only");
+    REQUIRE(X->act != MOE_ACT_SWIGLU, MOE_EUNSUPPORTED, "atomic experts take GELU activations");
+    REQUIRE(d == 512 || d == 1024 || d == 2048 || d == 4096, MOE_ESHAPE,
+            "atomic experts need d in {512, 1024, 2048, 4096} (got %lld)", (long long)d);
+    REQUIRE(X->W && X->V, MOE_EINVAL, "atomic experts need W and V");
+    *g = geo;
+    return MOE_OK;
+  }
+  REQUIRE(X->ffn_sizes, MOE_EINVAL, "ffn_sizes is NULL");
+  REQUIRE(X->ffn_offsets, MOE_EINVAL, "ffn_offsets (device prefix sum) is NULL");
+  REQUIRE(X->w13_t && X->w2_t, MOE_EINVAL, "packed expert weights are NULL");
+  REQUIRE(X->E <= 2048, MOE_EUNSUPPORTED, "grouped / BCSR experts support E <= 2048");
+  geo.pf = X->act == MOE_ACT_SWIGLU ? 2 : 1;
+  if (dtype == MOE_F32) {
+    REQUIRE(!geo.bcsr, MOE_EUNSUPPORTED, "the BCSR walk is implemented for bf16 only");
+    REQUIRE(d % 64 == 0 && d > 0, MOE_ESHAPE, "f32 experts need d %% 64 == 0 (got %lld)", (long long)d);
+    geo.bf1 = 64 * geo.pf;
+    geo.bf2 = 64;
+    geo.bt = 64;
+  } else {
+    REQUIRE(d % 256 == 0 && d > 0, MOE_ESHAPE, "bf16 experts need d %% 256 == 0 (got %lld)", (long long)d);
+    geo.bf1 = 256;
+    geo.bf2 = 256;
+    geo.bt = 128;
+  }
+  geo.fold = geo.pf;
+  for (int64_t e = 0; e < X->E; ++e) {
+    const int64_t f = X->ffn_sizes[e];
+    REQUIRE(f > 0, MOE_ESHAPE, "ffn_sizes[%lld] must be positive", (long long)e);
+    if (dtype == MOE_F32)
+      REQUIRE(f % 64 == 0, MOE_ESHAPE, "f32 ffn sizes must be multiples of 64 (expert %lld: %lld)",
+              (long long)e, (long long)f);
+    else
+      REQUIRE((f * geo.pf) % geo.bf1 == 0, MOE_ESHAPE,
+              "bf16 ffn sizes must be multiples of %d for this activation (expert %lld: %lld)",
+              256 / geo.pf, (long long)e, (long long)f);
+    geo.F += f;
+    geo.Fmax = std::max(geo.Fmax, f);
+  }
+  REQUIRE(geo.F < (int64_t(1) << 31) / 2, MOE_ESHAPE, "total ffn width too large");
+  if (geo.bcsr) {
+    REQUIRE(X->block == 128, MOE_EUNSUPPORTED, "BCSR block must be 128 (got %d)", X->block);
+    REQUIRE(X->size_blocks && X->block_offsets, MOE_EINVAL, "BCSR needs size_blocks and block_offsets");
+  }
+  *g = geo;
+  return MOE_OK;
+}
+
+// Upper bounds on the tile lists (the real counts are only known on the
+// device): sum_e ceil(rows_e / bt) * nf_e <= (rows_max / bt + E) * max_e nf_e.
+int64_t max_tiles_gemm1(const ExpertGeo& g, int64_t rows_max, int64_t nnz_max) {
+  if (g.bcsr) return nnz_max * 128 * g.pf / g.bf1;
+  return (rows_max / g.bt + g.E) * ((g.Fmax * g.pf + g.bf1 - 1) / g.bf1);
+}
+int64_t max_tiles_gemm2(const ExpertGeo& g, int64_t d, int64_t rows_max) {
+  const int64_t nf = d / g.bf2;
+  if (g.bcsr) return (rows_max / 128) * nf;
+  return (rows_max / g.bt + g.E) * nf;
+}
+
+int64_t nnz_max_of(const moe_experts_desc* X, int64_t rows_max) {
+  int64_t sbmax = 0;
+  for (int64_t e = 0; e < X->E; ++e) sbmax = std::max(sbmax, X->ffn_sizes[e] / 128);
+  return (rows_max / 128) * sbmax;
+}
+
+struct ExpertWs {
+  void* h = nullptr;
+  Tile* tiles1 = nullptr;
+  Tile* tiles2 = nullptr;
+  int* nt = nullptr;   // [2]
+  float* a_rows = nullptr;
+  int64_t mt1 = 0, mt2 = 0;
+};
+
+void carve_expert_ws(Carve& c, const ExpertGeo& g, int dtype, int64_t d, int64_t rows_max,
+                     int64_t nnz_max, ExpertWs* w) {
+  if (g.atomic) {
+    w->a_rows = c.take_n<float>(rows_max);
+    return;
+  }
+  w->mt1 = std::max<int64_t>(1, max_tiles_gemm1(g, rows_max, nnz_max));
+  w->mt2 = std::max<int64_t>(1, max_tiles_gemm2(g, d, rows_max));
+  w->h = c.take(size_t(rows_max) * g.Fmax * esize(dtype));
+  w->tiles1 = c.take_n<Tile>(w->mt1);
+  w->tiles2 = c.take_n<Tile>(w->mt2);
+  w->nt = c.take_n<int>(2);
+}
+
+// Launch the two expert GEMMs of a grouped / BCSR expert set over the rows of
+// a routing (or, for the shared FFN, one dense group of T rows).
+int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, int64_t d,
+                     const int32_t* offsets, int dense_rows, const int32_t* row_offsets,
+                     const int32_t* column_indices, const void* x_in, const float* row_r,
+                     const float* row_w, void* y, const ExpertWs& w, hipStream_t s,
+                     moe_timer* timer, int call);
+
+}  // namespace
+
+// ---------------------------------------------------------------- timer
+
+struct moe_timer {
+  int max_calls = 0;
+  int ncalls = 0;
+  std::vector<hipEvent_t> ev;   // max_calls x (MOE_STAGE_COUNT + 1)
+};
+
+namespace {
+void timer_mark(moe_timer* t, int call, int idx, hipStream_t s) {
+  if (!t || call < 0) return;
+  (void)hipEventRecord(t->ev[size_t(call) * (MOE_STAGE_COUNT + 1) + idx], s);
+}
+
+int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, int64_t d,
+                     const int32_t* offsets, int dense_rows, const int32_t* row_offsets,
+                     const int32_t* column_indices, const void* x_in, const float* row_r,
+                     const float* row_w, void* y, const ExpertWs& w, hipStream_t s,
+                     moe_timer* timer, int call) {
+  PlanArgs p{};
+  p.offsets = offsets;
+  p.dense_rows = dense_rows;
+  p.foff = X->ffn_offsets;
+  p.E = int(X->E);
+  p.swiglu = X->act == MOE_ACT_SWIGLU;
+  p.d = int(d);
+  p.bt = g.bt;
+  p.row_offsets = g.bcsr ? row_offsets : nullptr;
+  p.column_indices = column_indices;
+  p.block_offsets = X->block_offsets;
+  p.block = 128;
+  // first linear
+  p.gemm = 1;
+  p.bf = g.bf1;
+  p.fold = g.fold;
+  p.dense_n = int(g.Fmax * g.pf);
+  p.tiles = w.tiles1;
+  p.ntiles = w.nt;
+  p.max_tiles = int(w.mt1);
+  MOE_HIP(launch_plan(p, s));
+  // second linear
+  p.gemm = 2;
+  p.bf = g.bf2;
+  p.fold = 1;
+  p.dense_n = int(d);
+  p.tiles = w.tiles2;
+  p.ntiles = w.nt + 1;
+  p.max_tiles = int(w.mt2);
+  MOE_HIP(launch_plan(p, s));
+  timer_mark(timer, call, MOE_STAGE_PLAN + 1, s);
+
+  GemmArgs a{};
+  a.X = x_in;
+  a.ldx = d;
+  a.W = X->w13_t;
+  a.ldw = d;
+  a.tiles = w.tiles1;
+  a.ntiles = w.nt;
+  a.Y = w.h;
+  a.ldy = g.Fmax;
+  a.row_r = row_r;
+  a.row_w = nullptr;
+  a.epi = X->act == MOE_ACT_SWIGLU ? EPI_SWIGLU : EPI_ACT;
+  a.act = X->act == MOE_ACT_GELU_TANH ? 1 : 0;
+  MOE_HIP(launch_gemm(dtype, a, g.bf1, g.bt, int(w.mt1), s));
+  timer_mark(timer, call, MOE_STAGE_GEMM1 + 1, s);
+
+  GemmArgs b{};
+  b.X = w.h;
+  b.ldx = g.Fmax;
+  b.W = X->w2_t;
+  b.ldw = g.F;
+  b.tiles = w.tiles2;
+  b.ntiles = w.nt + 1;
+  b.Y = y;
+  b.ldy = d;
+  b.row_r = nullptr;
+  b.row_w = row_w;
+  b.epi = EPI_GATE;
+  MOE_HIP(launch_gemm(dtype, b, g.bf2, g.bt, int(w.mt2), s));
+  timer_mark(timer, call, MOE_STAGE_GEMM2 + 1, s);
+  return MOE_OK;
+}
+
+__int128 i128(int64_t v) { return __int128(v); }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+const char* moe_version(void) { return "moe_mi355x 0.1 (gfx950)"; }
+
+int64_t moe_capacity(int64_t T, int k, int64_t E, double cf) {
+  if (T < 0 || k <= 0 || E <= 0 || std::isnan(cf)) return -1;
+  if (!(cf > 0)) return T;
+  if (T == 0) return 0;
+  const double est = double(T) * double(k) * cf / double(E);
+  if (!(est < double(T) + 2.0)) return T;          // includes +inf
+  if (est < 0.25) return std::min<int64_t>(1, T);  // 0 < exact <= 1
+  // exact: cf = m * 2^e2 with integer m
+  int ex = 0;
+  const double mant = std::frexp(cf, &ex);
+  int64_t m = int64_t(std::ldexp(mant, 53));
+  int e2 = ex - 53;
+  while (m % 2 == 0 && e2 < 0) {
+    m /= 2;
+    ++e2;
+  }
+  unsigned __int128 num = (unsigned __int128)(i128(T) * k) * (unsigned __int128)m;
+  unsigned __int128 den = (unsigned __int128)E;
+  if (e2 >= 0) num <<= e2;
+  else den <<= -e2;
+  const unsigned __int128 c = (num + den - 1) / den;
+  return c > (unsigned __int128)T ? T : int64_t(c);
+}
+
+int64_t moe_rows_max(int64_t T, int k, int64_t E, int64_t capacity, int pad) {
+  if (T < 0 || k <= 0 || E <= 0 || capacity < 0 || pad < 1) return -1;
+  const int64_t kept = std::min(T * k, E * std::min(capacity, T));
+  return kept + E * (pad - 1);
+}
+
+// ---------------------------------------------------------------- packing
+
+int moe_pack_transpose(const void* src, int dtype, int64_t K, int64_t N, void* dst,
+                       hipStream_t stream) {
+  REQUIRE(valid_dtype(dtype), MOE_EDTYPE, "unknown dtype %d", dtype);
+  REQUIRE(K >= 0 && N >= 0, MOE_ESHAPE, "negative size");
+  REQUIRE((src && dst) || K * N == 0, MOE_EINVAL, "NULL pointer");
+  REQUIRE(src != dst || K * N == 0, MOE_EINVAL, "transpose cannot run in place");
+  MOE_HIP(launch_pack_transpose(src, dtype, K, N, dst, stream));
+  return ok();
+}
+
+int moe_pack_swiglu(const void* w1, const void* w3, int dtype, int64_t d, const int64_t* ffn_sizes,
+                    int64_t E, void* w13_t, hipStream_t stream) {
+  REQUIRE(valid_dtype(dtype), MOE_EDTYPE, "unknown dtype %d", dtype);
+  REQUIRE(w1 && w3 && w13_t && ffn_sizes, MOE_EINVAL, "NULL pointer");
+  REQUIRE(d > 0 && E > 0, MOE_ESHAPE, "d and E must be positive");
+  int64_t F = 0;
+  for (int64_t e = 0; e < E; ++e) {
+    REQUIRE(ffn_sizes[e] > 0 && ffn_sizes[e] % 32 == 0, MOE_ESHAPE,
+            "SwiGLU pack needs ffn sizes that are positive multiples of 32 (expert %lld: %lld)",
+            (long long)e, (long long)ffn_sizes[e]);
+    F += ffn_sizes[e];
+  }
+  MOE_HIP(launch_pack_swiglu(w1, w3, dtype, d, F, nullptr, ffn_sizes, E, w13_t, stream));
+  return ok();
+}
+
+// ---------------------------------------------------------------- stages
+
+int moe_rmsnorm_stats(const void* x, int dtype, int64_t T, int64_t d, const void* gamma, float eps,
+                      float* r, void* xg, hipStream_t stream) {
+  REQUIRE(valid_dtype(dtype), MOE_EDTYPE, "unknown dtype %d", dtype);
+  REQUIRE(T >= 0 && d > 0, MOE_ESHAPE, "bad sizes T=%lld d=%lld", (long long)T, (long long)d);
+  REQUIRE(d % (16 / esize(dtype)) == 0, MOE_ESHAPE, "d must fill 16-byte vectors");
+  REQUIRE(T == 0 || (x && r), MOE_EINVAL, "x and r are required");
+  REQUIRE(!gamma || xg, MOE_EINVAL, "a gain needs the xg output");
+  REQUIRE(eps >= 0.f, MOE_EINVAL, "eps must be >= 0");
+  MOE_HIP(launch_rmsnorm(x, dtype, T, d, gamma, eps, r, gamma ? xg : nullptr, stream));
+  return ok();
+}
+
+size_t moe_router_workspace_size(const moe_router_desc* R, int64_t T) {
+  if (!R || T < 0) return 0;
+  if (R->kind == MOE_ROUTER_CARTESIAN) {
+    Carve c(nullptr);
+    c.take(size_t(T) * (R->Nr + R->Nc) * sizeof(float));   // scores
+    c.take_n<Tile>(std::max<int64_t>(1, ((T + 127) / 128) * ((R->Nr + R->Nc) / 256)));
+    c.take_n<int>(1);
+    return c.used;
+  }
+  return 0;
+}
+
+namespace {
+int check_router(const moe_router_desc* R, int dtype, int64_t T, int64_t d, int k) {
+  REQUIRE(R, MOE_EINVAL, "router descriptor is NULL");
+  REQUIRE(valid_dtype(dtype), MOE_EDTYPE, "unknown dtype %d", dtype);
+  REQUIRE(T >= 0 && d > 0, MOE_ESHAPE, "bad sizes");
+  if (R->kind == MOE_ROUTER_DENSE) {
+    REQUIRE(R->E >= 1 && R->E <= 256, MOE_EUNSUPPORTED, "dense router supports 1 <= E <= 256 (got %lld)",
+            (long long)R->E);
+    REQUIRE(k >= 1 && k <= R->E, MOE_EINVAL, "k must be in [1, E] (k=%d, E=%lld)", k, (long long)R->E);
+    REQUIRE(R->wr_t, MOE_EINVAL, "router weights are NULL");
+    if (dtype == MOE_BF16)
+      REQUIRE(d % 128 == 0, MOE_ESHAPE, "bf16 router needs d %% 128 == 0");
+    return MOE_OK;
+  }
+  REQUIRE(R->kind == MOE_ROUTER_CARTESIAN, MOE_EDTYPE, "unknown router kind %d", R->kind);
+  REQUIRE(dtype == MOE_BF16, MOE_EUNSUPPORTED, "the Cartesian router is implemented for bf16 only");
+  REQUIRE(R->Nr >= 1 && R->Nc >= 1 && R->E == R->Nr * R->Nc, MOE_ESHAPE, "Cartesian router needs E = Nr*Nc");
+  REQUIRE(k >= 1 && k <= 64 && k <= R->Nr && k <= R->Nc, MOE_EINVAL,
+          "Cartesian router needs 1 <= k <= min(64, Nr, Nc)");
+  REQUIRE((R->Nr + R->Nc) % 256 == 0 && R->Nr + R->Nc <= 8192, MOE_ESHAPE,
+          "Cartesian router needs Nr + Nc a multiple of 256 (at most 8192)");
+  REQUIRE(int64_t(k) * k <= 4096, MOE_EUNSUPPORTED, "k*k too large");
+  REQUIRE(d % 256 == 0, MOE_ESHAPE, "Cartesian router needs d %% 256 == 0");
+  REQUIRE(R->keys_t, MOE_EINVAL, "router keys are NULL");
+  REQUIRE(R->E < (int64_t(1) << 31), MOE_ESHAPE, "too many experts");
+  return MOE_OK;
+}
+
+int router_run(const moe_router_desc* R, const void* x, int dtype, int64_t T, int64_t d,
+               const float* r_in, float eps, float* r_out, int k, int renorm, int32_t* ids, float* w,
+               float* logits, void* ws, hipStream_t stream) {
+  if (R->kind == MOE_ROUTER_DENSE) {
+    MOE_HIP(launch_router_dense(x, dtype, T, d, R->wr_t, R->bias, R->E, r_in, eps, r_out, k, renorm,
+                                ids, w, logits, stream));
+    return MOE_OK;
+  }
+  Carve c(ws);
+  float* scores = logits ? logits : c.take_n<float>(T * (R->Nr + R->Nc));
+  if (logits) c.take_n<float>(T * (R->Nr + R->Nc));
+  const int64_t ntile_max = std::max<int64_t>(1, ((T + 127) / 128) * ((R->Nr + R->Nc) / 256));
+  Tile* tiles = c.take_n<Tile>(ntile_max);
+  int* nt = c.take_n<int>(1);
+  const float* r = r_in;
+  if (!r) {
+    MOE_HIP(launch_rmsnorm(x, dtype, T, d, nullptr, eps, r_out, nullptr, stream));
+    r = r_out;
+  }
+  if (T > 0) {
+    PlanArgs p{};
+    p.offsets = nullptr;
+    p.dense_rows = int(T);
+    p.dense_n = int(R->Nr + R->Nc);
+    p.gemm = 1;
+    p.d = int(d);
+    p.bt = 128;
+    p.bf = 256;
+    p.fold = 1;
+    p.tiles = tiles;
+    p.ntiles = nt;
+    p.max_tiles = int(ntile_max);
+    MOE_HIP(launch_plan(p, stream));
+    GemmArgs a{};
+    a.X = x;
+    a.ldx = d;
+    a.W = R->keys_t;
+    a.ldw = d;
+    a.tiles = tiles;
+    a.ntiles = nt;
+    a.Y = scores;
+    a.ldy = R->Nr + R->Nc;
+    a.row_r = r;
+    a.epi = EPI_SCALE_F32;
+    MOE_HIP(launch_gemm(dtype, a, 256, 128, int(ntile_max), stream));
+  }
+  MOE_HIP(launch_cartesian_topk(scores, T, R->Nr, R->Nc, k, renorm, ids, w, stream));
+  return MOE_OK;
+}
+}  // namespace
+
+int moe_router_topk(const moe_router_desc* R, const void* x, int dtype, int64_t T, int64_t d,
+                    const float* r_in, float eps, float* r_out, int k, int renorm, int32_t* ids,
+                    float* w, float* logits, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_router(R, dtype, T, d, k);
+  if (rc) return rc;
+  REQUIRE(T == 0 || (x && ids && w), MOE_EINVAL, "x, ids and w are required");
+  REQUIRE(r_in || r_out || T == 0, MOE_EINVAL, "r_in or r_out is required");
+  REQUIRE(renorm == 0 || renorm == 1, MOE_EINVAL, "renorm must be 0 or 1");
+  if (R->kind == MOE_ROUTER_DENSE && dtype == MOE_F32)
+    REQUIRE(logits || T == 0, MOE_EINVAL, "the f32 router needs the logits buffer");
+  const size_t need = moe_router_workspace_size(R, T);
+  REQUIRE(ws_bytes >= need && (need == 0 || ws), MOE_EWORKSPACE, "router workspace needs %zu bytes",
+          need);
+  rc = router_run(R, x, dtype, T, d, r_in, eps, r_out, k, renorm, ids, w, logits, ws, stream);
+  return rc ? rc : ok();
+}
+
+size_t moe_dispatch_workspace_size(int64_t T, int k, int64_t E) {
+  if (T < 0 || k <= 0 || E <= 0) return 0;
+  return dispatch_ws_bytes(T, k, E);
+}
+
+int moe_dispatch(const int32_t* ids, const float* w, const float* r, const void* x, int dtype,
+                 int64_t T, int64_t d, int64_t E, int k, int64_t capacity, int pad, int64_t rows_max,
+                 int32_t* counts, int32_t* offsets, int32_t* pos, int32_t* row_token, float* row_r,
+                 float* row_w, int32_t* row_expert, void* x_perm, moe_stats* stats, void* ws,
+                 size_t ws_bytes, hipStream_t stream) {
+  REQUIRE(valid_dtype(dtype), MOE_EDTYPE, "unknown dtype %d", dtype);
+  REQUIRE(T >= 0 && k >= 1 && E >= 1 && E < (int64_t(1) << 22), MOE_ESHAPE,
+          "bad sizes T=%lld k=%d E=%lld", (long long)T, k, (long long)E);
+  REQUIRE(T * k < (int64_t(1) << 31), MOE_ESHAPE, "T*k too large");
+  REQUIRE(capacity >= 0, MOE_EINVAL, "capacity must be >= 0");
+  REQUIRE(pad >= 1 && pad <= 1024, MOE_EINVAL, "pad must be in [1, 1024]");
+  const int64_t need_rows = moe_rows_max(T, k, E, capacity, pad);
+  REQUIRE(rows_max >= need_rows, MOE_ESHAPE, "rows_max %lld < required %lld", (long long)rows_max,
+          (long long)need_rows);
+  REQUIRE(rows_max < (int64_t(1) << 31), MOE_ESHAPE, "rows_max too large");
+  REQUIRE(counts && offsets && (T == 0 || (ids && w && r && pos)) &&
+              (rows_max == 0 || (row_token && row_r && row_w)),
+          MOE_EINVAL, "NULL output");
+  REQUIRE(!x_perm || (x && d > 0 && d % (16 / esize(dtype)) == 0), MOE_EINVAL,
+          "x_perm needs x and d filling 16-byte vectors");
+  if (E > 2048) {
+    REQUIRE(pad == 1 && capacity >= T, MOE_EUNSUPPORTED,
+            "the radix-sort dispatch (E > 2048) supports pad 1 and no capacity limit only");
+  }
+  const size_t need = moe_dispatch_workspace_size(T, k, E);
+  REQUIRE(ws && ws_bytes >= need, MOE_EWORKSPACE, "dispatch workspace needs %zu bytes", need);
+  DispatchArgs a{};
+  a.ids = ids;
+  a.w = w;
+  a.r = r;
+  a.x = x;
+  a.dtype = dtype;
+  a.T = T;
+  a.d = d;
+  a.E = E;
+  a.k = k;
+  a.cap = std::min(capacity, T);
+  a.pad = pad;
+  a.rows_max = rows_max;
+  a.counts = counts;
+  a.offsets = offsets;
+  a.pos = pos;
+  a.row_token = row_token;
+  a.row_r = row_r;
+  a.row_w = row_w;
+  a.row_expert = row_expert;
+  a.x_perm = x_perm;
+  a.stats = stats;
+  a.ws = ws;
+  a.ws_bytes = ws_bytes;
+  MOE_HIP(launch_dispatch(a, stream));
+  return ok();
+}
+
+int64_t moe_topology_nnz_max(int64_t rows_max, int block, const int64_t* ffn_sizes, int64_t E) {
+  if (rows_max < 0 || block <= 0 || !ffn_sizes || E <= 0) return -1;
+  int64_t sbmax = 0;
+  for (int64_t e = 0; e < E; ++e) sbmax = std::max(sbmax, (ffn_sizes[e] + block - 1) / block);
+  return (rows_max / block) * sbmax;
+}
+
+int moe_build_topology(const int32_t* offsets, const int32_t* size_blocks,
+                       const int32_t* block_offsets, int64_t E, int block, int64_t rows_max,
+                       int32_t* row_offsets, int32_t* column_indices, int32_t* nnz,
+                       hipStream_t stream) {
+  REQUIRE(E >= 1 && E <= 2048, MOE_EUNSUPPORTED, "topology supports 1 <= E <= 2048");
+  REQUIRE(block > 0 && rows_max >= 0 && rows_max % block == 0, MOE_ESHAPE,
+          "rows_max must be a multiple of the block");
+  REQUIRE(offsets && size_blocks && block_offsets && row_offsets && column_indices && nnz,
+          MOE_EINVAL, "NULL pointer");
+  MOE_HIP(launch_topology(offsets, size_blocks, block_offsets, E, block, rows_max, row_offsets,
+                          column_indices, nnz, stream));
+  return ok();
+}
+
+size_t moe_expert_workspace_size(const moe_experts_desc* X, int dtype, int64_t d, int64_t T, int k,
+                                 int64_t rows_max) {
+  ExpertGeo g;
+  if (check_experts(X, dtype, d, &g) || T < 0 || k <= 0 || rows_max < 0) return 0;
+  Carve c(nullptr);
+  ExpertWs w;
+  carve_expert_ws(c, g, dtype, d, rows_max, g.bcsr ? nnz_max_of(X, rows_max) : 0, &w);
+  return c.used;
+}
+
+int moe_expert_gemm(const moe_experts_desc* X, int dtype, int64_t d, const moe_routing* rt,
+                    const void* x_in, void* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  ExpertGeo g;
+  int rc = check_experts(X, dtype, d, &g);
+  if (rc) return rc;
+  REQUIRE(rt, MOE_EINVAL, "routing is NULL");
+  REQUIRE(rt->E == X->E, MOE_ESHAPE, "routing E %lld != experts E %lld", (long long)rt->E,
+          (long long)X->E);
+  REQUIRE(rt->T >= 0 && rt->k >= 1 && rt->rows_max >= 0 && rt->rows_max < (int64_t(1) << 31),
+          MOE_ESHAPE, "bad routing sizes");
+  REQUIRE(x_in && y && rt->offsets && rt->row_r && rt->row_w, MOE_EINVAL, "NULL pointer");
+  if (g.bcsr) {
+    REQUIRE(rt->pad == 128, MOE_ESHAPE, "BCSR experts need a dispatch padded to 128");
+    REQUIRE(X->row_offsets && X->column_indices, MOE_EINVAL, "BCSR needs the topology");
+    REQUIRE(rt->rows_max % 128 == 0, MOE_ESHAPE, "BCSR rows_max must be a multiple of 128");
+    REQUIRE(rt->rows_max / 128 <= 4096, MOE_EUNSUPPORTED, "BCSR supports at most 4096 token blocks");
+  }
+  if (g.atomic)
+    REQUIRE(rt->ids && rt->pos && rt->row_token && rt->row_expert, MOE_EINVAL,
+            "atomic experts need ids, pos, row_token and row_expert");
+  const size_t need = moe_expert_workspace_size(X, dtype, d, rt->T, rt->k, rt->rows_max);
+  REQUIRE(ws && ws_bytes >= need, MOE_EWORKSPACE, "expert workspace needs %zu bytes", need);
+  Carve c(ws);
+  ExpertWs w;
+  carve_expert_ws(c, g, dtype, d, rt->rows_max, g.bcsr ? nnz_max_of(X, rt->rows_max) : 0, &w);
+  if (g.atomic) {
+    AtomicArgs a{};
+    a.xhat = x_in;
+    a.dtype = dtype;
+    a.T = rt->T;
+    a.d = d;
+    a.k = rt->k;
+    a.N = X->E;
+    a.W = X->W;
+    a.V = X->V;
+    a.act = X->act == MOE_ACT_GELU_TANH ? 1 : 0;
+    a.ids = rt->ids;
+    a.pos = rt->pos;
+    a.row_token = rt->row_token;
+    a.row_expert = rt->row_expert;
+    a.row_r = rt->row_r;
+    a.row_w = rt->row_w;
+    a.rows_used = rt->offsets + rt->E;
+    a.rows = rt->rows_max;
+    a.a_rows = w.a_rows;
+    a.routed = y;
+    MOE_HIP(launch_atomic(a, stream));
+    return ok();
+  }
+  rc = run_expert_gemms(X, g, dtype, d, rt->offsets, 0, X->row_offsets, X->column_indices, x_in,
+                        rt->row_r, rt->row_w, y, w, stream, nullptr, -1);
+  return rc ? rc : ok();
+}
+
+size_t moe_shared_workspace_size(const moe_experts_desc* S, int dtype, int64_t d, int64_t T) {
+  ExpertGeo g;
+  if (check_experts(S, dtype, d, &g) || S->E != 1 || S->kind != MOE_EXPERTS_GROUPED || T < 0) return 0;
+  Carve c(nullptr);
+  ExpertWs w;
+  // dense group of T rows: rows_max = T
+  carve_expert_ws(c, g, dtype, d, T, 0, &w);
+  return c.used;
+}
+
+int moe_shared_ffn(const moe_experts_desc* S, int dtype, int64_t d, int64_t T, const void* xhat,
+                   const float* r, void* s, void* ws, size_t ws_bytes, hipStream_t stream) {
+  ExpertGeo g;
+  int rc = check_experts(S, dtype, d, &g);
+  if (rc) return rc;
+  REQUIRE(S->kind == MOE_EXPERTS_GROUPED && S->E == 1, MOE_EUNSUPPORTED,
+          "the shared FFN is one grouped expert");
+  REQUIRE(T >= 0 && T < (int64_t(1) << 31), MOE_ESHAPE, "bad T");
+  REQUIRE(T == 0 || (xhat && r && s), MOE_EINVAL, "NULL pointer");
+  const size_t need = moe_shared_workspace_size(S, dtype, d, T);
+  REQUIRE(ws && ws_bytes >= need, MOE_EWORKSPACE, "shared workspace needs %zu bytes", need);
+  if (T == 0) return ok();
+  Carve c(ws);
+  ExpertWs w;
+  carve_expert_ws(c, g, dtype, d, T, 0, &w);
+  rc = run_expert_gemms(S, g, dtype, d, nullptr, int(T), nullptr, nullptr, xhat, r, nullptr, s, w,
+                        stream, nullptr, -1);
+  return rc ? rc : ok();
+}
+
+int moe_combine(const void* y, const int32_t* pos, const void* residual, const void* shared,
+                int dtype, int64_t T, int64_t d, int k, void* out, hipStream_t stream) {
+  REQUIRE(valid_dtype(dtype), MOE_EDTYPE, "unknown dtype %d", dtype);
+  REQUIRE(T >= 0 && d > 0 && k >= 1, MOE_ESHAPE, "bad sizes");
+  REQUIRE(d % (16 / esize(dtype)) == 0, MOE_ESHAPE, "d must fill 16-byte vectors");
+  REQUIRE(T == 0 || (y && out), MOE_EINVAL, "NULL pointer");
+  MOE_HIP(launch_combine(y, pos, residual, shared, dtype, T, d, k, out, stream));
+  return ok();
+}
+
+// ---------------------------------------------------------------- the layer
+
+}  // extern "C"
+
+namespace {
+
+struct LayerWs {
+  float* r;
+  void* xg;
+  int32_t* ids;
+  float* w;
+  float* logits;
+  void* router_ws;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* pos;
+  int32_t* row_token;
+  float* row_r;
+  float* row_w;
+  int32_t* row_expert;
+  void* x_perm;
+  moe_stats* stats;
+  void* disp_ws;
+  size_t disp_ws_bytes;
+  int32_t* row_offsets;
+  int32_t* column_indices;
+  int32_t* nnz;
+  ExpertWs ex;
+  void* y;          // y_perm [rows_max, d] or routed [T, d]
+  ExpertWs sh;
+  void* s;          // shared output [T, d]
+  int64_t rows_max, cap;
+};
+
+int check_layer(const moe_layer_desc* L, int64_t T, ExpertGeo* g, ExpertGeo* gs) {
+  REQUIRE(L, MOE_EINVAL, "layer descriptor is NULL");
+  REQUIRE(T >= 0 && T < (int64_t(1) << 30), MOE_ESHAPE, "bad T");
+  int rc = check_router(&L->router, L->dtype, T, L->d, L->k);
+  if (rc) return rc;
+  rc = check_experts(&L->experts, L->dtype, L->d, g);
+  if (rc) return rc;
+  REQUIRE(L->experts.E == L->router.E, MOE_ESHAPE, "router E %lld != experts E %lld",
+          (long long)L->router.E, (long long)L->experts.E);
+  REQUIRE((L->router.kind == MOE_ROUTER_CARTESIAN) == g->atomic, MOE_EUNSUPPORTED,
+          "the Cartesian router pairs with atomic experts (and only with them)");
+  REQUIRE(L->renorm == 0 || L->renorm == 1, MOE_EINVAL, "renorm must be 0 or 1");
+  REQUIRE(L->eps >= 0.f, MOE_EINVAL, "eps must be >= 0");
+  if (L->shared) {
+    rc = check_experts(L->shared, L->dtype, L->d, gs);
+    if (rc) return rc;
+    REQUIRE(L->shared->kind == MOE_EXPERTS_GROUPED && L->shared->E == 1, MOE_EUNSUPPORTED,
+            "the shared FFN is one grouped expert");
+  }
+  if (g->bcsr) {
+    const int64_t cap = moe_capacity(T, L->k, L->experts.E, L->capacity_factor);
+    REQUIRE(moe_rows_max(T, L->k, L->experts.E, cap, 128) / 128 < 4096, MOE_EUNSUPPORTED,
+            "BCSR supports at most 4096 token blocks");
+  }
+  if (g->atomic)
+    REQUIRE(!(L->capacity_factor > 0) || moe_capacity(T, L->k, L->experts.E, L->capacity_factor) >= T,
+            MOE_EUNSUPPORTED, "atomic experts run without a capacity limit");
+  return MOE_OK;
+}
+
+void carve_layer(Carve& c, const moe_layer_desc* L, int64_t T, const ExpertGeo& g,
+                 const ExpertGeo& gs, LayerWs* w) {
+  const int64_t d = L->d, E = L->experts.E;
+  const int k = L->k;
+  const size_t es = esize(L->dtype);
+  const int pad = g.bcsr ? 128 : 1;
+  w->cap = moe_capacity(T, k, E, L->capacity_factor);
+  w->rows_max = moe_rows_max(T, k, E, w->cap, pad);
+  if (g.bcsr) w->rows_max = (w->rows_max + 127) / 128 * 128;
+  w->r = c.take_n<float>(T);
+  w->xg = L->gamma ? c.take(size_t(T) * d * es) : nullptr;
+  w->ids = c.take_n<int32_t>(T * k);
+  w->w = c.take_n<float>(T * k);
+  w->logits = (L->router.kind == MOE_ROUTER_DENSE && L->dtype == MOE_F32) ? c.take_n<float>(T * E)
+                                                                          : nullptr;
+  const size_t rws = moe_router_workspace_size(&L->router, T);
+  w->router_ws = rws ? c.take(rws) : nullptr;
+  w->counts = c.take_n<int32_t>(E);
+  w->offsets = c.take_n<int32_t>(E + 1);
+  w->pos = c.take_n<int32_t>(T * k);
+  w->row_token = c.take_n<int32_t>(w->rows_max);
+  w->row_r = c.take_n<float>(w->rows_max);
+  w->row_w = c.take_n<float>(w->rows_max);
+  w->row_expert = c.take_n<int32_t>(w->rows_max);
+  w->x_perm = g.atomic ? nullptr : c.take(size_t(w->rows_max) * d * es);
+  w->stats = c.take_n<moe_stats>(1);
+  w->disp_ws_bytes = moe_dispatch_workspace_size(T, k, E);
+  w->disp_ws = c.take(w->disp_ws_bytes);
+  int64_t nnz_max = 0;
+  if (g.bcsr) {
+    nnz_max = nnz_max_of(&L->experts, w->rows_max);
+    w->row_offsets = c.take_n<int32_t>(w->rows_max / 128 + 1);
+    w->column_indices = c.take_n<int32_t>(std::max<int64_t>(1, nnz_max));
+    w->nnz = c.take_n<int32_t>(1);
+  } else {
+    w->row_offsets = w->column_indices = w->nnz = nullptr;
+  }
+  carve_expert_ws(c, g, L->dtype, d, w->rows_max, nnz_max, &w->ex);
+  w->y = c.take(size_t(g.atomic ? T : w->rows_max) * d * es);
+  if (L->shared) {
+    carve_expert_ws(c, gs, L->dtype, d, T, 0, &w->sh);
+    w->s = c.take(size_t(T) * d * es);
+  } else {
+    w->s = nullptr;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_layer_workspace_size(const moe_layer_desc* L, int64_t T) {
+  ExpertGeo g, gs;
+  if (check_layer(L, T, &g, &gs)) return 0;
+  Carve c(nullptr);
+  LayerWs w;
+  carve_layer(c, L, T, g, gs, &w);
+  return c.used;
+}
+
+int moe_layer_routing(const moe_layer_desc* L, int64_t T, void* ws, size_t ws_bytes, moe_routing* rt) {
+  ExpertGeo g, gs;
+  int rc = check_layer(L, T, &g, &gs);
+  if (rc) return rc;
+  REQUIRE(ws && rt, MOE_EINVAL, "NULL pointer");
+  Carve c(ws);
+  LayerWs w;
+  carve_layer(c, L, T, g, gs, &w);
+  REQUIRE(ws_bytes >= c.used, MOE_EWORKSPACE, "workspace too small");
+  rt->T = T;
+  rt->k = L->k;
+  rt->E = L->experts.E;
+  rt->rows_max = w.rows_max;
+  rt->pad = g.bcsr ? 128 : 1;
+  rt->ids = w.ids;
+  rt->w = w.w;
+  rt->r = w.r;
+  rt->counts = w.counts;
+  rt->offsets = w.offsets;
+  rt->pos = w.pos;
+  rt->row_token = w.row_token;
+  rt->row_r = w.row_r;
+  rt->row_w = w.row_w;
+  rt->row_expert = w.row_expert;
+  return ok();
+}
+
+int moe_layer_forward(const moe_layer_desc* L, const void* x, int64_t T, void* out, moe_stats* stats,
+                      void* ws, size_t ws_bytes, hipStream_t stream) {
+  ExpertGeo g, gs;
+  int rc = check_layer(L, T, &g, &gs);
+  if (rc) return rc;
+  REQUIRE(T == 0 || (x && out), MOE_EINVAL, "x and out are required");
+  Carve c(ws);
+  LayerWs w;
+  carve_layer(c, L, T, g, gs, &w);
+  REQUIRE(ws && ws_bytes >= c.used, MOE_EWORKSPACE, "layer workspace needs %zu bytes (got %zu)",
+          c.used, ws_bytes);
+  const int64_t d = L->d, E = L->experts.E;
+  const int k = L->k;
+  moe_timer* tm = L->timer;
+  int call = -1;
+  if (tm && tm->ncalls < tm->max_calls) call = tm->ncalls++;
+  timer_mark(tm, call, 0, stream);
+
+  // 1-2. RMSNorm statistic, router, top-k
+  const void* xhat = x;
+  if (L->gamma) {
+    MOE_HIP(launch_rmsnorm(x, L->dtype, T, d, L->gamma, L->eps, w.r, w.xg, stream));
+    xhat = w.xg;
+    rc = router_run(&L->router, xhat, L->dtype, T, d, w.r, L->eps, nullptr, k, L->renorm, w.ids, w.w,
+                    w.logits, w.router_ws, stream);
+  } else {
+    rc = router_run(&L->router, xhat, L->dtype, T, d, nullptr, L->eps, w.r, k, L->renorm, w.ids, w.w,
+                    w.logits, w.router_ws, stream);
+  }
+  if (rc) return rc;
+  timer_mark(tm, call, MOE_STAGE_ROUTER + 1, stream);
+
+  // 3. capacity + dispatch
+  moe_stats* st = stats ? stats : w.stats;
+  {
+    DispatchArgs a{};
+    a.ids = w.ids;
+    a.w = w.w;
+    a.r = w.r;
+    a.x = xhat;
+    a.dtype = L->dtype;
+    a.T = T;
+    a.d = d;
+    a.E = E;
+    a.k = k;
+    a.cap = w.cap;
+    a.pad = g.bcsr ? 128 : 1;
+    a.rows_max = w.rows_max;
+    a.counts = w.counts;
+    a.offsets = w.offsets;
+    a.pos = w.pos;
+    a.row_token = w.row_token;
+    a.row_r = w.row_r;
+    a.row_w = w.row_w;
+    a.row_expert = w.row_expert;
+    a.x_perm = w.x_perm;
+    a.stats = st;
+    a.ws = w.disp_ws;
+    a.ws_bytes = w.disp_ws_bytes;
+    MOE_HIP(launch_dispatch(a, stream));
+  }
+  timer_mark(tm, call, MOE_STAGE_DISPATCH + 1, stream);
+
+  // 4. experts
+  if (g.atomic) {
+    timer_mark(tm, call, MOE_STAGE_PLAN + 1, stream);
+    AtomicArgs a{};
+    a.xhat = xhat;
+    a.dtype = L->dtype;
+    a.T = T;
+    a.d = d;
+    a.k = k;
+    a.N = E;
+    a.W = L->experts.W;
+    a.V = L->experts.V;
+    a.act = L->experts.act == MOE_ACT_GELU_TANH ? 1 : 0;
+    a.ids = w.ids;
+    a.pos = w.pos;
+    a.row_token = w.row_token;
+    a.row_expert = w.row_expert;
+    a.row_r = w.row_r;
+    a.row_w = w.row_w;
+    a.rows_used = w.offsets + E;
+    a.rows = w.rows_max;
+    a.a_rows = w.ex.a_rows;
+    a.routed = w.y;
+    MOE_HIP(launch_atomic(a, stream));
+    timer_mark(tm, call, MOE_STAGE_GEMM1 + 1, stream);
+    timer_mark(tm, call, MOE_STAGE_GEMM2 + 1, stream);
+  } else {
+    if (g.bcsr)
+      MOE_HIP(launch_topology(w.offsets, L->experts.size_blocks, L->experts.block_offsets, E, 128,
+                              w.rows_max, w.row_offsets, w.column_indices, w.nnz, stream));
+    rc = run_expert_gemms(&L->experts, g, L->dtype, d, w.offsets, 0, w.row_offsets, w.column_indices,
+                          w.x_perm, w.row_r, w.row_w, w.y, w.ex, stream, tm, call);
+    if (rc) return rc;
+  }
+  // shared experts: dense, gate 1, r in the first epilogue
+  if (L->shared && T > 0) {
+    rc = run_expert_gemms(L->shared, gs, L->dtype, d, nullptr, int(T), nullptr, nullptr, xhat, w.r,
+                          nullptr, w.s, w.sh, stream, nullptr, -1);
+    if (rc) return rc;
+  }
+  timer_mark(tm, call, MOE_STAGE_SHARED + 1, stream);
+
+  // 5. combine
+  MOE_HIP(launch_combine(w.y, g.atomic ? nullptr : w.pos, L->residual ? x : nullptr, w.s, L->dtype,
+                         T, d, k, out, stream));
+  timer_mark(tm, call, MOE_STAGE_COMBINE + 1, stream);
+  return ok();
+}
+
+// ---------------------------------------------------------------- timer
+
+int moe_timer_create(moe_timer** out, int max_calls) {
+  REQUIRE(out && max_calls > 0 && max_calls <= 100000, MOE_EINVAL, "bad timer arguments");
+  moe_timer* t = new moe_timer;
+  t->max_calls = max_calls;
+  t->ev.resize(size_t(max_calls) * (MOE_STAGE_COUNT + 1));
+  for (auto& e : t->ev) {
+    if (hipEventCreate(&e) != hipSuccess) {
+      for (auto& f : t->ev)
+        if (f) (void)hipEventDestroy(f);
+      delete t;
+      return fail(MOE_EHIP, "hipEventCreate failed");
+    }
+  }
+  *out = t;
+  return ok();
+}
+
+int moe_timer_destroy(moe_timer* t) {
+  if (!t) return ok();
+  for (auto& e : t->ev) (void)hipEventDestroy(e);
+  delete t;
+  return ok();
+}
+
+int moe_timer_reset(moe_timer* t) {
+  REQUIRE(t, MOE_EINVAL, "timer is NULL");
+  t->ncalls = 0;
+  return ok();
+}
+
+int moe_timer_stage_ms(moe_timer* t, int stage, double* total_ms, int* calls) {
+  REQUIRE(t && total_ms && stage >= 0 && stage < MOE_STAGE_COUNT, MOE_EINVAL, "bad timer query");
+  double tot = 0;
+  for (int c = 0; c < t->ncalls; ++c) {
+    hipEvent_t a = t->ev[size_t(c) * (MOE_STAGE_COUNT + 1) + stage];
+    hipEvent_t b = t->ev[size_t(c) * (MOE_STAGE_COUNT + 1) + stage + 1];
+    MOE_HIP(hipEventSynchronize(b));
+    float ms = 0;
+    MOE_HIP(hipEventElapsedTime(&ms, a, b));
+    tot += ms;
+  }
+  *total_ms = tot;
+  if (calls) *calls = t->ncalls;
+  return ok();
+}
+
+}  // extern "C"

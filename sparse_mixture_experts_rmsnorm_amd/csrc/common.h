@@ -1,0 +1,78 @@
+// Device helpers shared by the HIP kernels of libmoe_mi355x (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+// Native 16-byte vector (HIP's uint4 is a struct that can defeat SROA when
+// kept in arrays, sending them to scratch or LDS).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// fp32 -> bf16 with round-to-nearest-even (quiet NaN kept).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+// element <-> float for the two storage types (float, or bf16 bits)
+__device__ __forceinline__ float tof(float v) { return v; }
+__device__ __forceinline__ float tof(uint16_t v) { return bf2f(v); }
+template <typename T> __device__ __forceinline__ T fromf(float v);
+template <> __device__ __forceinline__ float fromf<float>(float v) { return v; }
+template <> __device__ __forceinline__ uint16_t fromf<uint16_t>(float v) { return f2bf(v); }
+
+// elements per 16-byte vector
+template <typename T> struct Vec16 { static constexpr int N = 16 / sizeof(T); };
+
+__device__ __forceinline__ void unpack16(const uint4& v, float* o, const float*) {
+  o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
+  o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
+}
+__device__ __forceinline__ void unpack16(const uint4& v, float* o, const uint16_t*) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = __uint_as_float(w[i] << 16);
+    o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ uint4 pack16(const float* o, const float*) {
+  return make_uint4(__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
+                    __float_as_uint(o[3]));
+}
+__device__ __forceinline__ uint4 pack16(const float* o, const uint16_t*) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = uint32_t(f2bf(o[2 * i])) | (uint32_t(f2bf(o[2 * i + 1])) << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
+__device__ __forceinline__ float gelu_tanh(float z) {
+  const float c = 0.79788456080286536f;  // sqrt(2/pi)
+  return 0.5f * z * (1.0f + tanhf(c * (z + 0.044715f * z * z * z)));
+}
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  return (uint64_t(1) << (threadIdx.x & 63)) - 1;
+}
+
+// Wave-wide sum (all 64 lanes get the result).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+}  // namespace moe

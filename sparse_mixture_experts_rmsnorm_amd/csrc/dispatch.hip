@@ -1,0 +1,512 @@
+// Capacity rule + dispatch: histogram, prefix sum and a stable permutation of
+// the (token, slot) assignments into expert-contiguous rows.
+//
+// The expert-capacity entry of the "Mixture of Experts (MoE)" glossary fixes
+// the per-expert limit; overflow slots are dropped.  Within an expert the
+// rows keep token order (the OmniMoE summary, 2.2, sorts tasks by token id
+// inside each expert group), which also decides which slots overflow.  The
+// permuted rows carry the RMSNorm statistic r and the gate (the CODA thread:
+// the r-scale must travel with the dispatched tokens).
+//
+// Determinism without ordering atomics: the slot list is cut into chunks of
+// kChunkTokens tokens.  Pass 1 counts per (chunk, expert) (LDS atomics, which
+// only count), pass 2 turns the counts into per-(chunk, expert) bases and the
+// expert offsets, pass 3 ranks every slot inside its chunk with wavefront
+// ballots -- lanes holding the same expert id find each other bit by bit, a
+// lane's rank is the popcount of its peers below it, and per-wave totals are
+// combined in wave order -- so the permutation is a stable counting sort.
+//
+// Very large expert counts (the 2^20 atomic experts of OmniMoE) use the same
+// ballot ranking as the scatter of a two-pass LSD radix sort of the slots by
+// expert id; offsets then come from a lower-bound search of the sorted keys.
+#include <algorithm>
+
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kChunkTokens = 256;   // dense path: tokens per chunk
+constexpr int kThreads = 256;       // 4 waves
+constexpr int kRadixChunk = 2048;   // radix path: slots per chunk
+constexpr int kDenseMaxE = 2048;
+
+// stats layout: [0] rows, [1] dropped, [2] max_load, [3] errors
+__device__ __forceinline__ uint64_t match_peers(int key, bool ok, int nbits) {
+  uint64_t peers = __ballot(ok);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = ok && ((key >> b) & 1);
+    const uint64_t m = __ballot(bit);
+    peers &= bit ? m : ~m;
+  }
+  return peers;
+}
+
+__global__ void k_fill_rows(int64_t rows_max, int32_t* row_token, float* row_r, float* row_w,
+                            int32_t* row_expert) {
+  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < rows_max;
+       i += int64_t(gridDim.x) * blockDim.x) {
+    row_token[i] = -1;
+    row_r[i] = 0.f;
+    row_w[i] = 0.f;
+    if (row_expert) row_expert[i] = -1;
+  }
+}
+
+// ---------------------------------------------------------------- dense path
+
+// Pass 1: per-chunk expert histogram.
+__global__ void __launch_bounds__(kThreads) k_count(const int32_t* __restrict__ ids, int T, int k,
+                                                    int E, int32_t* __restrict__ cc,
+                                                    int32_t* __restrict__ cerr) {
+  extern __shared__ int hist[];
+  __shared__ int err_s;
+  const int c = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += kThreads) hist[e] = 0;
+  if (threadIdx.x == 0) err_s = 0;
+  __syncthreads();
+  const int t0 = c * kChunkTokens;
+  const int n = min(kChunkTokens, T - t0) * k;
+  int err = 0;
+  for (int i = threadIdx.x; i < n; i += kThreads) {
+    const int e = ids[int64_t(t0) * k + i];
+    if (unsigned(e) < unsigned(E)) atomicAdd(&hist[e], 1);
+    else ++err;
+  }
+  if (err) atomicAdd(&err_s, err);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kThreads) cc[int64_t(c) * E + e] = hist[e];
+  if (threadIdx.x == 0) cerr[c] = err_s;
+}
+
+// Block-wide exclusive scan, one value per thread (blockDim a multiple of 64,
+// at most 1024).  sh needs 33 ints.
+__device__ long long block_exscan(long long v, long long* total, long long* sh) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  long long incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const long long u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) sh[wid] = incl;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    long long run = 0;
+    for (int w = 0; w < nw; ++w) {
+      const long long t = sh[w];
+      sh[w] = run;
+      run += t;
+    }
+    sh[32] = run;
+  }
+  __syncthreads();
+  const long long res = sh[wid] + incl - v;
+  *total = sh[32];
+  __syncthreads();
+  return res;
+}
+
+// Pass 2: chunk bases, expert counts, capacity, padded offsets, statistics.
+__global__ void __launch_bounds__(1024) k_scan(int32_t* __restrict__ cc,
+                                               const int32_t* __restrict__ cerr, int nchunks,
+                                               int E, int cap, int pad,
+                                               int32_t* __restrict__ counts,
+                                               int32_t* __restrict__ offsets,
+                                               int32_t* __restrict__ stats) {
+  __shared__ long long sh[33];
+  __shared__ int padded_s[kDenseMaxE];
+  long long dropped = 0, errs = 0;
+  int maxl = 0;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int run = 0;
+    for (int c = 0; c < nchunks; ++c) {
+      const int v = cc[int64_t(c) * E + e];
+      cc[int64_t(c) * E + e] = run;
+      run += v;
+    }
+    counts[e] = run;
+    const int kept = min(run, cap);
+    padded_s[e] = (kept + pad - 1) / pad * pad;
+    dropped += run - kept;
+    maxl = max(maxl, run);
+  }
+  for (int c = threadIdx.x; c < nchunks; c += blockDim.x) errs += cerr[c];
+  __syncthreads();
+  // exclusive scan of padded_s: each thread owns a contiguous run
+  const int per = (E + blockDim.x - 1) / blockDim.x;
+  const int lo = min(E, int(threadIdx.x) * per), hi = min(E, lo + per);
+  long long local = 0;
+  for (int e = lo; e < hi; ++e) local += padded_s[e];
+  long long total;
+  long long base = block_exscan(local, &total, sh);
+  for (int e = lo; e < hi; ++e) {
+    offsets[e] = int(base);
+    base += padded_s[e];
+  }
+  if (threadIdx.x == 0) offsets[E] = int(total);
+  // statistics
+  long long tot;
+  block_exscan(dropped, &tot, sh);
+  const long long all_dropped = tot;
+  block_exscan(errs, &tot, sh);
+  const long long all_errs = tot;
+  // max via shuffles + LDS
+  int m = maxl;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = max(m, __shfl_xor(m, o, 64));
+  __shared__ int mx[16];
+  if ((threadIdx.x & 63) == 0) mx[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0 && stats) {
+    int mm = 0;
+    for (int w = 0; w < int(blockDim.x >> 6); ++w) mm = max(mm, mx[w]);
+    stats[0] = int(total);
+    stats[1] = int(all_dropped);
+    stats[2] = mm;
+    stats[3] = int(all_errs);
+  }
+}
+
+// Pass 3: stable rank inside the chunk, capacity test, row metadata.
+__global__ void __launch_bounds__(kThreads) k_rank(
+    const int32_t* __restrict__ ids, const float* __restrict__ w, const float* __restrict__ r,
+    int T, int k, int E, int nbits, int cap, const int32_t* __restrict__ cc,
+    const int32_t* __restrict__ offsets, int32_t* __restrict__ pos,
+    int32_t* __restrict__ row_token, float* __restrict__ row_r, float* __restrict__ row_w,
+    int32_t* __restrict__ row_expert) {
+  extern __shared__ int sm[];
+  int* running = sm;          // [E]
+  int* wtag = sm + E;         // [4][E]: (batch + 1) << 8 | count
+  const int c = blockIdx.x;
+  const int wid = threadIdx.x >> 6;
+  for (int e = threadIdx.x; e < E; e += kThreads) {
+    running[e] = cc[int64_t(c) * E + e];
+    wtag[e] = wtag[E + e] = wtag[2 * E + e] = wtag[3 * E + e] = 0;
+  }
+  __syncthreads();
+  const int t0 = c * kChunkTokens;
+  const int n = min(kChunkTokens, T - t0) * k;
+  const int64_t base_flat = int64_t(t0) * k;
+  for (int b = 0; b * kThreads < n; ++b) {
+    const int i = b * kThreads + threadIdx.x;
+    const bool valid = i < n;
+    int e = valid ? ids[base_flat + i] : -1;
+    if (unsigned(e) >= unsigned(E)) e = -1;
+    const bool ok = e >= 0;
+    const uint64_t peers = match_peers(e, ok, nbits);
+    const int lr = __popcll(peers & lanemask_lt());
+    const int tag = b + 1;
+    if (ok && lr == 0) wtag[wid * E + e] = (tag << 8) | __popcll(peers);
+    __syncthreads();
+    if (valid) {
+      const int64_t flat = base_flat + i;
+      int p = -1;
+      if (ok) {
+        int rank = running[e] + lr;
+        for (int w2 = 0; w2 < wid; ++w2) {
+          const int v = wtag[w2 * E + e];
+          if ((v >> 8) == tag) rank += v & 255;
+        }
+        if (rank < cap) {
+          p = offsets[e] + rank;
+          const int t = int(flat / k);
+          row_token[p] = t;
+          row_r[p] = r[t];
+          row_w[p] = w[flat];
+          if (row_expert) row_expert[p] = e;
+        }
+      }
+      pos[flat] = p;
+    }
+    __syncthreads();
+    if (ok && lr == 0) {
+      bool last = true;
+      for (int w2 = wid + 1; w2 < 4; ++w2)
+        if ((wtag[w2 * E + e] >> 8) == tag) last = false;
+      if (last) {
+        int tot = 0;
+        for (int w2 = 0; w2 <= wid; ++w2) {
+          const int v = wtag[w2 * E + e];
+          if ((v >> 8) == tag) tot += v & 255;
+        }
+        running[e] += tot;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Row gather: x_perm[row] = x[row_token[row]] (zeros on padding rows).
+template <typename T>
+__global__ void __launch_bounds__(kThreads) k_gather(const T* __restrict__ x, int64_t d,
+                                                     const int32_t* __restrict__ rows_used,
+                                                     const int32_t* __restrict__ row_token,
+                                                     T* __restrict__ x_perm) {
+  const int rows = *rows_used;
+  const int64_t nvec = d / Vec16<T>::N;
+  const uint4* __restrict__ xs = reinterpret_cast<const uint4*>(x);
+  uint4* __restrict__ xp = reinterpret_cast<uint4*>(x_perm);
+  const int lane = threadIdx.x & 63;
+  for (int row = blockIdx.x * 4 + (threadIdx.x >> 6); row < rows; row += gridDim.x * 4) {
+    const int t = row_token[row];
+    if (t >= 0) {
+      const uint4* src = xs + int64_t(t) * nvec;
+      uint4* dst = xp + int64_t(row) * nvec;
+      for (int64_t v = lane; v < nvec; v += 64) dst[v] = src[v];
+    } else {
+      uint4* dst = xp + int64_t(row) * nvec;
+      for (int64_t v = lane; v < nvec; v += 64) dst[v] = make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- radix path
+
+// Keys = expert id, or E for an invalid id (sorts last).
+__global__ void k_radix_prep(const int32_t* __restrict__ ids, int64_t N, int E,
+                             int32_t* __restrict__ keys) {
+  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < N;
+       i += int64_t(gridDim.x) * blockDim.x) {
+    const int e = ids[i];
+    keys[i] = unsigned(e) < unsigned(E) ? e : E;
+  }
+}
+
+__global__ void __launch_bounds__(kThreads) k_radix_count(const int32_t* __restrict__ keys,
+                                                          int64_t N, int shift, int bits,
+                                                          int nch, int32_t* __restrict__ cc) {
+  extern __shared__ int hist[];
+  const int nb = 1 << bits;
+  const int c = blockIdx.x;
+  for (int b = threadIdx.x; b < nb; b += kThreads) hist[b] = 0;
+  __syncthreads();
+  const int64_t i0 = int64_t(c) * kRadixChunk;
+  const int n = int(min<int64_t>(kRadixChunk, N - i0));
+  for (int i = threadIdx.x; i < n; i += kThreads)
+    atomicAdd(&hist[(keys[i0 + i] >> shift) & (nb - 1)], 1);
+  __syncthreads();
+  for (int b = threadIdx.x; b < nb; b += kThreads) cc[int64_t(b) * nch + c] = hist[b];
+}
+
+// Exclusive scan of n ints in place with one block of 1024 threads.
+__global__ void __launch_bounds__(1024) k_scan_inplace(int32_t* __restrict__ v, int64_t n) {
+  __shared__ long long sh[33];
+  const int64_t per = (n + blockDim.x - 1) / blockDim.x;
+  const int64_t lo = min<int64_t>(n, threadIdx.x * per), hi = min<int64_t>(n, lo + per);
+  long long local = 0;
+  for (int64_t i = lo; i < hi; ++i) local += v[i];
+  long long total;
+  long long base = block_exscan(local, &total, sh);
+  for (int64_t i = lo; i < hi; ++i) {
+    const int x = v[i];
+    v[i] = int(base);
+    base += x;
+  }
+}
+
+__global__ void __launch_bounds__(kThreads) k_radix_scatter(
+    const int32_t* __restrict__ keys_in, const int32_t* __restrict__ vals_in, int64_t N,
+    int shift, int bits, int nch, const int32_t* __restrict__ cc,
+    int32_t* __restrict__ keys_out, int32_t* __restrict__ vals_out) {
+  extern __shared__ int sm[];
+  const int nb = 1 << bits;
+  int* running = sm;
+  int* wtag = sm + nb;
+  const int c = blockIdx.x;
+  const int wid = threadIdx.x >> 6;
+  for (int b = threadIdx.x; b < nb; b += kThreads) {
+    running[b] = cc[int64_t(b) * nch + c];
+    wtag[b] = wtag[nb + b] = wtag[2 * nb + b] = wtag[3 * nb + b] = 0;
+  }
+  __syncthreads();
+  const int64_t i0 = int64_t(c) * kRadixChunk;
+  const int n = int(min<int64_t>(kRadixChunk, N - i0));
+  for (int b = 0; b * kThreads < n; ++b) {
+    const int i = b * kThreads + threadIdx.x;
+    const bool ok = i < n;
+    const int key = ok ? keys_in[i0 + i] : 0;
+    const int dig = (key >> shift) & (nb - 1);
+    const uint64_t peers = match_peers(dig, ok, bits);
+    const int lr = __popcll(peers & lanemask_lt());
+    const int tag = b + 1;
+    if (ok && lr == 0) wtag[wid * nb + dig] = (tag << 8) | __popcll(peers);
+    __syncthreads();
+    if (ok) {
+      int dst = running[dig] + lr;
+      for (int w2 = 0; w2 < wid; ++w2) {
+        const int v = wtag[w2 * nb + dig];
+        if ((v >> 8) == tag) dst += v & 255;
+      }
+      keys_out[dst] = key;
+      vals_out[dst] = vals_in ? vals_in[i0 + i] : int(i0 + i);
+    }
+    __syncthreads();
+    if (ok && lr == 0) {
+      bool last = true;
+      for (int w2 = wid + 1; w2 < 4; ++w2)
+        if ((wtag[w2 * nb + dig] >> 8) == tag) last = false;
+      if (last) {
+        int tot = 0;
+        for (int w2 = 0; w2 <= wid; ++w2) {
+          const int v = wtag[w2 * nb + dig];
+          if ((v >> 8) == tag) tot += v & 255;
+        }
+        running[dig] += tot;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+__device__ __forceinline__ int lower_bound(const int32_t* __restrict__ a, int n, int key) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] < key) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// offsets[e] = first sorted slot with key >= e; counts[e] = slots of e.
+__global__ void k_radix_offsets(const int32_t* __restrict__ keys, int N, int E,
+                                int32_t* __restrict__ offsets, int32_t* __restrict__ counts,
+                                int32_t* __restrict__ stats) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e > E) return;
+  const int lo = lower_bound(keys, N, e);
+  offsets[e] = lo;
+  if (e < E) {
+    const int cnt = lower_bound(keys, N, e + 1) - lo;
+    counts[e] = cnt;
+    if (stats && cnt) atomicMax(&stats[2], cnt);
+  } else if (stats) {
+    stats[0] = lo;
+    stats[1] = 0;
+    stats[3] = N - lo;
+  }
+}
+
+__global__ void k_zero_stat(int32_t* stats) {
+  if (threadIdx.x == 0) stats[2] = 0;
+}
+
+__global__ void k_radix_rows(const int32_t* __restrict__ keys, const int32_t* __restrict__ vals,
+                             int64_t N, int E, int k, const float* __restrict__ w,
+                             const float* __restrict__ r, int32_t* __restrict__ pos,
+                             int32_t* __restrict__ row_token, float* __restrict__ row_r,
+                             float* __restrict__ row_w, int32_t* __restrict__ row_expert) {
+  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < N;
+       i += int64_t(gridDim.x) * blockDim.x) {
+    const int key = keys[i];
+    const int flat = vals[i];
+    if (key >= E) {
+      pos[flat] = -1;
+      continue;
+    }
+    const int t = flat / k;
+    pos[flat] = int(i);
+    row_token[i] = t;
+    row_r[i] = r[t];
+    row_w[i] = w[flat];
+    if (row_expert) row_expert[i] = key;
+  }
+}
+
+int ceil_log2(int64_t v) {
+  int b = 0;
+  while ((int64_t(1) << b) < v) ++b;
+  return b;
+}
+
+}  // namespace
+
+size_t dispatch_ws_bytes(int64_t T, int k, int64_t E) {
+  if (E <= kDenseMaxE) {
+    const int64_t nch = (T + kChunkTokens - 1) / kChunkTokens;
+    return size_t(nch * E + nch + 64) * sizeof(int32_t);
+  }
+  const int64_t N = T * k;
+  const int64_t nch = (N + kRadixChunk - 1) / kRadixChunk;
+  const int B = ceil_log2(E + 1);
+  const int b1 = (B + 1) / 2;
+  return size_t(4 * N + (int64_t(1) << b1) * nch + 64) * sizeof(int32_t);
+}
+
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
+  const int T = int(a.T), k = a.k, E = int(a.E);
+  int32_t* stats = reinterpret_cast<int32_t*>(a.stats);
+  {
+    const int64_t blocks = std::min<int64_t>(4096, (a.rows_max + 255) / 256);
+    if (blocks > 0)
+      hipLaunchKernelGGL(k_fill_rows, dim3(unsigned(blocks)), dim3(256), 0, s, a.rows_max,
+                         a.row_token, a.row_r, a.row_w, a.row_expert);
+  }
+  if (E <= kDenseMaxE) {
+    const int nch = (T + kChunkTokens - 1) / kChunkTokens;
+    int32_t* cc = reinterpret_cast<int32_t*>(a.ws);
+    int32_t* cerr = cc + int64_t(nch) * E;
+    if (nch > 0)
+      hipLaunchKernelGGL(k_count, dim3(nch), dim3(kThreads), E * sizeof(int), s, a.ids, T, k, E,
+                         cc, cerr);
+    const int cap = int(std::min<int64_t>(a.cap, int64_t(1) << 30));
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, cc, cerr, nch, E, cap, a.pad,
+                       a.counts, a.offsets, stats);
+    const int nbits = ceil_log2(E);
+    if (nch > 0)
+      hipLaunchKernelGGL(k_rank, dim3(nch), dim3(kThreads), 5 * E * sizeof(int), s, a.ids, a.w,
+                         a.r, T, k, E, nbits, cap, cc, a.offsets, a.pos, a.row_token, a.row_r,
+                         a.row_w, a.row_expert);
+  } else {
+    // two-pass LSD radix sort of the slots by expert id (keys < 2^B, E = sentinel)
+    const int64_t N = int64_t(T) * k;
+    const int nch = int((N + kRadixChunk - 1) / kRadixChunk);
+    const int B = ceil_log2(int64_t(E) + 1);
+    const int b1 = (B + 1) / 2, b2 = B - b1;
+    int32_t* keys0 = reinterpret_cast<int32_t*>(a.ws);
+    int32_t* vals0 = keys0 + N;
+    int32_t* keys1 = vals0 + N;
+    int32_t* vals1 = keys1 + N;
+    int32_t* cc = vals1 + N;
+    if (N > 0) {
+      const unsigned g = unsigned(std::min<int64_t>(4096, (N + 255) / 256));
+      hipLaunchKernelGGL(k_radix_prep, dim3(g), dim3(256), 0, s, a.ids, N, E, keys1);
+      // pass 1: low b1 bits, keys1 -> keys0 / vals0
+      hipLaunchKernelGGL(k_radix_count, dim3(nch), dim3(kThreads), (1 << b1) * sizeof(int), s,
+                         keys1, N, 0, b1, nch, cc);
+      hipLaunchKernelGGL(k_scan_inplace, dim3(1), dim3(1024), 0, s, cc, int64_t(nch) << b1);
+      hipLaunchKernelGGL(k_radix_scatter, dim3(nch), dim3(kThreads), 5 * (1 << b1) * sizeof(int),
+                         s, keys1, (const int32_t*)nullptr, N, 0, b1, nch, cc, keys0, vals0);
+      // pass 2: high b2 bits, keys0 -> keys1 / vals1
+      hipLaunchKernelGGL(k_radix_count, dim3(nch), dim3(kThreads), (1 << b2) * sizeof(int), s,
+                         keys0, N, b1, b2, nch, cc);
+      hipLaunchKernelGGL(k_scan_inplace, dim3(1), dim3(1024), 0, s, cc, int64_t(nch) << b2);
+      hipLaunchKernelGGL(k_radix_scatter, dim3(nch), dim3(kThreads), 5 * (1 << b2) * sizeof(int),
+                         s, keys0, vals0, N, b1, b2, nch, cc, keys1, vals1);
+    }
+    if (stats) hipLaunchKernelGGL(k_zero_stat, dim3(1), dim3(64), 0, s, stats);
+    hipLaunchKernelGGL(k_radix_offsets, dim3(unsigned((E + 1 + 255) / 256)), dim3(256), 0, s,
+                       keys1, int(N), E, a.offsets, a.counts, stats);
+    if (N > 0) {
+      const unsigned g = unsigned(std::min<int64_t>(4096, (N + 255) / 256));
+      hipLaunchKernelGGL(k_radix_rows, dim3(g), dim3(256), 0, s, keys1, vals1, N, E, k, a.w,
+                         a.r, a.pos, a.row_token, a.row_r, a.row_w, a.row_expert);
+    }
+  }
+  if (a.x_perm) {
+    const unsigned g = unsigned(std::max<int64_t>(1, std::min<int64_t>(8192, (a.rows_max + 3) / 4)));
+    if (a.dtype == 0)
+      hipLaunchKernelGGL(k_gather<float>, dim3(g), dim3(kThreads), 0, s,
+                         static_cast<const float*>(a.x), a.d, a.offsets + E, a.row_token,
+                         static_cast<float*>(a.x_perm));
+    else
+      hipLaunchKernelGGL(k_gather<uint16_t>, dim3(g), dim3(kThreads), 0, s,
+                         static_cast<const uint16_t*>(a.x), a.d, a.offsets + E, a.row_token,
+                         static_cast<uint16_t*>(a.x_perm));
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,534 @@
+// Expert GEMMs: grouped / block-sparse (BCSR) / dense tiles on bf16 MFMA,
+// with the epilogues that carry the layer's elementwise work.
+//
+//   first linear   h = act(r * (x_perm . W1_e))   or, SwiGLU,
+//                  h = silu(r * x_perm.W1_e) * (r * x_perm.W3_e)
+//   second linear  y = g * (h . W2_e)
+//   router scores  s = r * (x . K)                (fp32 output)
+//
+// CODA sparse-MoE thread: the RMSNorm statistic r is commuted across the
+// first expert GEMM into its epilogue (it reaches the experts with the
+// dispatched rows), and the other per-row factors that straddle the
+// dispatch / combine boundary -- the gate -- go into the second GEMM's
+// epilogue, so combine is a plain sum.
+//
+// Every tile of every group comes from a device-built tile list (expert row
+// counts are only known on the device), so one launch covers all experts
+// with no host round trip.  For the BCSR kind the list is produced by
+// walking the topology of the "Variable-size experts" nanoMOE notes
+// (sections 3-4): first linear = one tile per run of nonzero column blocks
+// of a token-block row (SDD), second linear = one tile per token-block row
+// and output slice, with K over that row's nonzero blocks (DSD).
+//
+// Tiling for gfx950: 256 threads = 4 wave64s in a 2 x 2 grid; operands are
+// both K-contiguous (weights packed as [features, K]), staged through
+// double-buffered LDS with a 16-byte-chunk XOR swizzle, and fed to
+// v_mfma_f32_32x32x16_bf16 with the weights as the A operand (features =
+// MFMA rows) and tokens as B (MFMA columns), so a lane's accumulators hold
+// four consecutive features of one token -- the epilogue stores 8 bytes
+// per group.  Tiles are remapped so that each XCD (workgroup id mod 8) runs
+// a contiguous run of the list, which shares weight tiles in its own L2.
+#include <algorithm>
+
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int BK = 64;
+
+__device__ __forceinline__ int remap_xcd(int b, int nt) {
+  const int xcd = b & 7, slot = b >> 3;
+  const int q = nt >> 3, rem = nt & 7;
+  return xcd * q + min(xcd, rem) + slot;
+}
+
+__device__ __forceinline__ float apply_act(float z, int act) {
+  return act == 1 ? gelu_tanh(z) : gelu_erf(z);
+}
+
+// ---------------------------------------------------------------- bf16 MFMA GEMM
+
+template <int BF, int BT, int EPI>
+__global__ void __launch_bounds__(256) k_gemm_bf16(GemmArgs a) {
+  constexpr int MF = BF / 64;           // 32-row feature blocks per wave
+  constexpr int MT = BT / 64;           // 32-col token blocks per wave
+  constexpr int WCH = BF / 32;          // 16-byte W chunks per thread per K step
+  constexpr int XCH = BT / 32;
+  constexpr int LW = BF * BK, LX = BT * BK;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (LW + LX)];
+
+  const int nt = *a.ntiles;
+  if (int(blockIdx.x) >= nt) return;
+  const Tile tile = a.tiles[remap_xcd(blockIdx.x, nt)];
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wf = wid >> 1, wt = wid & 1;
+  const uint16_t* __restrict__ X = static_cast<const uint16_t*>(a.X);
+  const uint16_t* __restrict__ W = static_cast<const uint16_t*>(a.W);
+
+  // global -> LDS mapping: chunk (row = tid/8 + 32 i, q = tid % 8)
+  const int lq = tid & 7;
+  const int lrow = tid >> 3;
+  const int lswz = (lq ^ (lrow & 7)) * 8;
+  const uint16_t* wsrc = W + int64_t(tile.wrow0 + lrow) * a.ldw + tile.kofs + lq * 8;
+  const int64_t wstep = int64_t(32) * a.ldw;
+  // X rows past the tile end are clamped to its last row (their results are
+  // never stored; every output column depends only on its own X row)
+  const uint16_t* xsrc = X + lq * 8;
+  const int xlast = tile.row_end - 1;
+  const int xr0 = tile.row0 + lrow;
+  u32x4 wreg[WCH], xreg[XCH];
+  f32x16 acc[MF][MT];
+#pragma unroll
+  for (int i = 0; i < MF; ++i)
+#pragma unroll
+    for (int j = 0; j < MT; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  // fragment addressing: row = base + (lane & 31), chunk q = 2 ks + (lane >> 5)
+  const int fr = lane & 31, fh = lane >> 5, fswz = lane & 7;
+  const int nk = tile.klen / BK;
+#define MOE_GLOAD(KT)                                                                     \
+  {                                                                                       \
+    const int ko_ = (KT) * BK;                                                            \
+    _Pragma("unroll") for (int i = 0; i < WCH; ++i)                                       \
+      wreg[i] = *reinterpret_cast<const u32x4*>(wsrc + i * wstep + ko_);                  \
+    _Pragma("unroll") for (int i = 0; i < XCH; ++i)                                       \
+      xreg[i] = *reinterpret_cast<const u32x4*>(                                          \
+          xsrc + int64_t(min(xr0 + 32 * i, xlast)) * a.ldx + ko_);                        \
+  }
+#define MOE_LSTORE(BUF)                                                                   \
+  {                                                                                       \
+    uint16_t* sw_ = lds + (BUF) * (LW + LX);                                              \
+    uint16_t* sx_ = sw_ + LW;                                                             \
+    _Pragma("unroll") for (int i = 0; i < WCH; ++i)                                       \
+      *reinterpret_cast<u32x4*>(sw_ + (lrow + 32 * i) * BK + lswz) = wreg[i];             \
+    _Pragma("unroll") for (int i = 0; i < XCH; ++i)                                       \
+      *reinterpret_cast<u32x4*>(sx_ + (lrow + 32 * i) * BK + lswz) = xreg[i];             \
+  }
+  MOE_GLOAD(0)
+  MOE_LSTORE(0)
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) MOE_GLOAD(kt + 1)
+    const uint16_t* sw = lds + (kt & 1) * (LW + LX);
+    const uint16_t* sx = sw + LW;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int qo = ((2 * ks + fh) ^ fswz) * 8;
+      bf16x8 af[MF], bfr[MT];
+#pragma unroll
+      for (int i = 0; i < MF; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(sw + (wf * (BF / 2) + i * 32 + fr) * BK + qo);
+#pragma unroll
+      for (int j = 0; j < MT; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8*>(sx + (wt * (BT / 2) + j * 32 + fr) * BK + qo);
+#pragma unroll
+      for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int j = 0; j < MT; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) MOE_LSTORE((kt + 1) & 1)
+    __syncthreads();
+  }
+#undef MOE_GLOAD
+#undef MOE_LSTORE
+
+  // epilogue: lane holds token column (lane & 31) of each 32x32 block and
+  // features 8 g + 4 (lane >> 5) + {0..3} for g = 0..3.
+#pragma unroll
+  for (int j = 0; j < MT; ++j) {
+    const int row = tile.row0 + wt * (BT / 2) + j * 32 + fr;
+    if (row >= tile.row_end) continue;
+    float rs = 1.f;
+    if (EPI == EPI_ACT || EPI == EPI_SWIGLU || EPI == EPI_SCALE_F32) rs = a.row_r[row];
+    if (EPI == EPI_GATE) rs = a.row_w ? a.row_w[row] : 1.f;
+    if (EPI == EPI_SWIGLU) {
+      uint16_t* Y = static_cast<uint16_t*>(a.Y) + int64_t(row) * a.ldy + tile.ocol0 + wf * (BF / 4);
+#pragma unroll
+      for (int p = 0; p < MF / 2; ++p)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          uint32_t pk[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            float o[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const int v = g * 4 + h * 2 + e;
+              const float gate = rs * acc[2 * p][j][v];
+              const float up = rs * acc[2 * p + 1][j][v];
+              o[e] = silu(gate) * up;
+            }
+            pk[h] = uint32_t(f2bf(o[0])) | (uint32_t(f2bf(o[1])) << 16);
+          }
+          *reinterpret_cast<uint2*>(Y + p * 32 + g * 8 + fh * 4) = make_uint2(pk[0], pk[1]);
+        }
+    } else if (EPI == EPI_SCALE_F32) {
+      float* Y = static_cast<float*>(a.Y) + int64_t(row) * a.ldy + tile.ocol0 + wf * (BF / 2);
+#pragma unroll
+      for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float4 o;
+          o.x = rs * acc[i][j][g * 4 + 0];
+          o.y = rs * acc[i][j][g * 4 + 1];
+          o.z = rs * acc[i][j][g * 4 + 2];
+          o.w = rs * acc[i][j][g * 4 + 3];
+          *reinterpret_cast<float4*>(Y + i * 32 + g * 8 + fh * 4) = o;
+        }
+    } else {
+      uint16_t* Y = static_cast<uint16_t*>(a.Y) + int64_t(row) * a.ldy + tile.ocol0 + wf * (BF / 2);
+#pragma unroll
+      for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          uint32_t pk[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            float o[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const float z = rs * acc[i][j][g * 4 + h * 2 + e];
+              o[e] = EPI == EPI_ACT ? apply_act(z, a.act) : z;
+            }
+            pk[h] = uint32_t(f2bf(o[0])) | (uint32_t(f2bf(o[1])) << 16);
+          }
+          *reinterpret_cast<uint2*>(Y + i * 32 + g * 8 + fh * 4) = make_uint2(pk[0], pk[1]);
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- fp32 SIMT GEMM
+
+// Tile: 64 output columns x 64 rows, K step 16.  SwiGLU tiles read 128 packed
+// rows (gate rows 32 g + c, up rows 32 g + 32 + c of each 64-row group).
+template <int EPI>
+__global__ void __launch_bounds__(256) k_gemm_f32(GemmArgs a) {
+  constexpr int NW = EPI == EPI_SWIGLU ? 128 : 64;
+  __shared__ float sW[16][NW + 4];
+  __shared__ float sX[16][64 + 4];
+  const int nt = *a.ntiles;
+  if (int(blockIdx.x) >= nt) return;
+  const Tile tile = a.tiles[remap_xcd(blockIdx.x, nt)];
+  const float* __restrict__ X = static_cast<const float*>(a.X);
+  const float* __restrict__ W = static_cast<const float*>(a.W);
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  float acc[4][4], accu[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = accu[i][j] = 0.f;
+  const int lr = tid >> 2, lq = tid & 3;   // 64 rows x 4 float4 chunks
+  for (int k0 = 0; k0 < tile.klen; k0 += 16) {
+    // W rows -> sW[k][col]; col c < 64: gate (or plain) row; c >= 64: up row
+#pragma unroll
+    for (int half = 0; half < NW / 64; ++half) {
+      const int c = lr;
+      const int prow = EPI == EPI_SWIGLU ? (c / 32) * 64 + (c % 32) + half * 32 : c;
+      const float4 v = *reinterpret_cast<const float4*>(
+          W + int64_t(tile.wrow0 + prow) * a.ldw + tile.kofs + k0 + lq * 4);
+      sW[lq * 4 + 0][half * 64 + c] = v.x;
+      sW[lq * 4 + 1][half * 64 + c] = v.y;
+      sW[lq * 4 + 2][half * 64 + c] = v.z;
+      sW[lq * 4 + 3][half * 64 + c] = v.w;
+    }
+    {
+      const int row = min(tile.row0 + lr, tile.row_end - 1);
+      const float4 v = *reinterpret_cast<const float4*>(X + int64_t(row) * a.ldx + k0 + lq * 4);
+      sX[lq * 4 + 0][lr] = v.x;
+      sX[lq * 4 + 1][lr] = v.y;
+      sX[lq * 4 + 2][lr] = v.z;
+      sX[lq * 4 + 3][lr] = v.w;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float wv[4], uv[4], xv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        wv[i] = sW[kk][tx + 16 * i];
+        if (EPI == EPI_SWIGLU) uv[i] = sW[kk][64 + tx + 16 * i];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xv[j] = sX[kk][ty + 16 * j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[i][j] = fmaf(wv[i], xv[j], acc[i][j]);
+          if (EPI == EPI_SWIGLU) accu[i][j] = fmaf(uv[i], xv[j], accu[i][j]);
+        }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = tile.row0 + ty + 16 * j;
+    if (row >= tile.row_end) continue;
+    float rs = 1.f;
+    if (EPI == EPI_ACT || EPI == EPI_SWIGLU || EPI == EPI_SCALE_F32) rs = a.row_r[row];
+    if (EPI == EPI_GATE) rs = a.row_w ? a.row_w[row] : 1.f;
+    float* Y = static_cast<float*>(a.Y) + int64_t(row) * a.ldy + tile.ocol0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tx + 16 * i;
+      float o;
+      if (EPI == EPI_SWIGLU) o = silu(rs * acc[i][j]) * (rs * accu[i][j]);
+      else if (EPI == EPI_ACT) o = apply_act(rs * acc[i][j], a.act);
+      else o = rs * acc[i][j];
+      Y[c] = o;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- tile plans
+
+__device__ __forceinline__ int upper_bound_i(const int* a, int n, int key) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] <= key) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+constexpr int kPlanMax = 4096;   // experts (grouped) or token-block rows (BCSR)
+
+__global__ void __launch_bounds__(1024) k_plan(PlanArgs p) {
+  __shared__ int base_s[kPlanMax + 1];
+  __shared__ long long sh[33];
+  const bool dense = p.offsets == nullptr;
+  const bool bcsr = !dense && p.row_offsets != nullptr;
+  const int pf = p.swiglu && p.gemm == 1 ? 2 : 1;   // packed rows per hidden unit
+  const int nunits = dense ? 1 : bcsr ? p.offsets[p.E] / p.block : p.E;
+  // per unit tile count, then exclusive scan (each thread owns a contiguous run)
+  const int per = (nunits + blockDim.x - 1) / blockDim.x;
+  const int lo = min(nunits, int(threadIdx.x) * per), hi = min(nunits, lo + per);
+  long long local = 0;
+  for (int u = lo; u < hi; ++u) {
+    int cnt;
+    if (dense) {
+      cnt = ((p.dense_rows + p.bt - 1) / p.bt) * (p.dense_n / p.bf);
+    } else if (bcsr) {
+      const int nz = p.row_offsets[u + 1] - p.row_offsets[u];
+      cnt = p.gemm == 1 ? nz * p.block * pf / p.bf : p.d / p.bf;
+    } else {
+      const int rows = p.offsets[u + 1] - p.offsets[u];
+      const int mt = (rows + p.bt - 1) / p.bt;
+      const int nf = p.gemm == 1 ? (p.foff[u + 1] - p.foff[u]) * pf / p.bf : p.d / p.bf;
+      cnt = mt * nf;
+    }
+    base_s[u] = cnt;
+    local += cnt;
+  }
+  long long total;
+  {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    long long incl = local;
+    for (int o = 1; o < 64; o <<= 1) {
+      const long long u = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += u;
+    }
+    if (lane == 63) sh[wid] = incl;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      long long run = 0;
+      for (int w = 0; w < nw; ++w) {
+        const long long t = sh[w];
+        sh[w] = run;
+        run += t;
+      }
+      sh[32] = run;
+    }
+    __syncthreads();
+    long long b = sh[wid] + incl - local;
+    total = sh[32];
+    for (int u = lo; u < hi; ++u) {
+      const int c = base_s[u];
+      base_s[u] = int(b);
+      b += c;
+    }
+    if (threadIdx.x == 0) base_s[nunits] = int(total);
+  }
+  __syncthreads();
+  const int ntot = int(min<long long>(total, p.max_tiles));
+  if (threadIdx.x == 0) *p.ntiles = ntot;
+  for (int idx = threadIdx.x; idx < ntot; idx += blockDim.x) {
+    const int u = upper_bound_i(base_s, nunits + 1, idx) - 1;
+    const int n = idx - base_s[u];
+    Tile t;
+    t.spare = 0;
+    if (dense) {
+      const int mt = (p.dense_rows + p.bt - 1) / p.bt;
+      const int nf = n / mt, m = n - nf * mt;
+      t.expert = 0;
+      t.row0 = m * p.bt;
+      t.row_end = min(p.dense_rows, t.row0 + p.bt);
+      t.wrow0 = nf * p.bf;
+      if (p.gemm == 1) {
+        t.kofs = 0;
+        t.klen = p.d;
+      } else {
+        t.kofs = p.foff[0];
+        t.klen = p.foff[1] - p.foff[0];
+      }
+      t.ocol0 = nf * p.bf / p.fold;
+    } else if (bcsr) {
+      const int first = p.row_offsets[u];
+      const int cb0 = p.column_indices[first];
+      const int e = upper_bound_i(p.block_offsets, p.E + 1, cb0) - 1;
+      t.expert = e;
+      t.row0 = u * p.block;
+      t.row_end = t.row0 + p.block;
+      if (p.gemm == 1) {
+        const int cb = p.column_indices[first + n * (p.bf / (p.block * pf))];
+        t.wrow0 = cb * p.block * pf;
+        t.kofs = 0;
+        t.klen = p.d;
+        t.ocol0 = (cb - p.block_offsets[e]) * p.block;
+      } else {
+        const int nz = p.row_offsets[u + 1] - first;
+        t.wrow0 = n * p.bf;
+        t.kofs = cb0 * p.block;
+        t.klen = nz * p.block;
+        t.ocol0 = n * p.bf;
+      }
+    } else {
+      const int rows = p.offsets[u + 1] - p.offsets[u];
+      const int mt = (rows + p.bt - 1) / p.bt;
+      const int nf = n / mt, m = n - nf * mt;
+      t.expert = u;
+      t.row0 = p.offsets[u] + m * p.bt;
+      t.row_end = min(p.offsets[u + 1], t.row0 + p.bt);
+      if (p.gemm == 1) {
+        t.wrow0 = p.foff[u] * pf + nf * p.bf;
+        t.kofs = 0;
+        t.klen = p.d;
+        t.ocol0 = nf * p.bf / p.fold;
+      } else {
+        t.wrow0 = nf * p.bf;
+        t.kofs = p.foff[u];
+        t.klen = p.foff[u + 1] - p.foff[u];
+        t.ocol0 = nf * p.bf;
+      }
+    }
+    p.tiles[idx] = t;
+  }
+}
+
+// ---------------------------------------------------------------- packing
+
+// dst[n, k] = src[k, n], 32 x 32 tiles through LDS.
+template <typename T>
+__global__ void __launch_bounds__(256) k_transpose(const T* __restrict__ src, int64_t K, int64_t N,
+                                                   T* __restrict__ dst) {
+  __shared__ T tile[32][33];
+  const int64_t n0 = int64_t(blockIdx.x) * 32, k0 = int64_t(blockIdx.y) * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 32 x 8
+  for (int i = ty; i < 32; i += 8) {
+    const int64_t kk = k0 + i, nn = n0 + tx;
+    if (kk < K && nn < N) tile[i][tx] = src[kk * N + nn];
+  }
+  __syncthreads();
+  for (int i = ty; i < 32; i += 8) {
+    const int64_t nn = n0 + i, kk = k0 + tx;
+    if (kk < K && nn < N) dst[nn * K + kk] = tile[tx][i];
+  }
+}
+
+// SwiGLU interleave: packed row p <- column 32 (p / 64) + p % 32 of w1 (p % 64 < 32)
+// or of w3 (p % 64 >= 32); every expert width is a multiple of 32, so the
+// mapping is the same for every expert.
+template <typename T>
+__global__ void __launch_bounds__(256) k_pack_swiglu(const T* __restrict__ w1,
+                                                     const T* __restrict__ w3, int64_t d,
+                                                     int64_t F, T* __restrict__ dst) {
+  __shared__ T tile[32][33];
+  const int64_t p0 = int64_t(blockIdx.x) * 32;   // 32 packed rows, one source matrix
+  const int64_t k0 = int64_t(blockIdx.y) * 32;
+  const T* src = ((p0 / 32) & 1) ? w3 : w1;
+  const int64_t c0 = (p0 / 64) * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  for (int i = ty; i < 32; i += 8) {
+    const int64_t kk = k0 + i;
+    if (kk < d) tile[i][tx] = src[kk * F + c0 + tx];
+  }
+  __syncthreads();
+  for (int i = ty; i < 32; i += 8) {
+    const int64_t kk = k0 + tx;
+    if (kk < d) dst[(p0 + i) * d + kk] = tile[tx][i];
+  }
+}
+
+}  // namespace
+
+int gemm_tile_bf(int dtype) { return dtype == 0 ? 64 : 256; }
+int gemm_tile_bt(int dtype, int) { return dtype == 0 ? 64 : 128; }
+
+hipError_t launch_plan(const PlanArgs& p, hipStream_t s) {
+  hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(int dtype, const GemmArgs& a, int bf, int bt, int grid, hipStream_t s) {
+  if (grid <= 0) return hipSuccess;
+  const dim3 g(grid), b(256);
+  if (dtype == 0) {
+    switch (a.epi) {
+      case EPI_ACT: hipLaunchKernelGGL(k_gemm_f32<EPI_ACT>, g, b, 0, s, a); break;
+      case EPI_SWIGLU: hipLaunchKernelGGL(k_gemm_f32<EPI_SWIGLU>, g, b, 0, s, a); break;
+      case EPI_GATE: hipLaunchKernelGGL(k_gemm_f32<EPI_GATE>, g, b, 0, s, a); break;
+      default: hipLaunchKernelGGL(k_gemm_f32<EPI_SCALE_F32>, g, b, 0, s, a); break;
+    }
+    return hipGetLastError();
+  }
+  if (bf != 256 || bt != 128) return hipErrorInvalidValue;
+#define MOE_GEMM_CASE(BTV)                                                                   \
+  switch (a.epi) {                                                                           \
+    case EPI_ACT: hipLaunchKernelGGL((k_gemm_bf16<256, BTV, EPI_ACT>), g, b, 0, s, a); break; \
+    case EPI_SWIGLU:                                                                         \
+      hipLaunchKernelGGL((k_gemm_bf16<256, BTV, EPI_SWIGLU>), g, b, 0, s, a);                \
+      break;                                                                                 \
+    case EPI_GATE: hipLaunchKernelGGL((k_gemm_bf16<256, BTV, EPI_GATE>), g, b, 0, s, a); break; \
+    default: hipLaunchKernelGGL((k_gemm_bf16<256, BTV, EPI_SCALE_F32>), g, b, 0, s, a); break; \
+  }
+  MOE_GEMM_CASE(128)
+#undef MOE_GEMM_CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_transpose(const void* src, int dtype, int64_t K, int64_t N, void* dst,
+                                 hipStream_t s) {
+  if (K == 0 || N == 0) return hipSuccess;
+  const dim3 g(unsigned((N + 31) / 32), unsigned((K + 31) / 32));
+  if (dtype == 0)
+    hipLaunchKernelGGL(k_transpose<float>, g, dim3(256), 0, s, static_cast<const float*>(src), K,
+                       N, static_cast<float*>(dst));
+  else
+    hipLaunchKernelGGL(k_transpose<uint16_t>, g, dim3(256), 0, s,
+                       static_cast<const uint16_t*>(src), K, N, static_cast<uint16_t*>(dst));
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_swiglu(const void* w1, const void* w3, int dtype, int64_t d, int64_t F,
+                              const int32_t*, const int64_t*, int64_t, void* dst, hipStream_t s) {
+  if (d == 0 || F == 0) return hipSuccess;
+  const dim3 g(unsigned(2 * F / 32), unsigned((d + 31) / 32));
+  if (dtype == 0)
+    hipLaunchKernelGGL(k_pack_swiglu<float>, g, dim3(256), 0, s, static_cast<const float*>(w1),
+                       static_cast<const float*>(w3), d, F, static_cast<float*>(dst));
+  else
+    hipLaunchKernelGGL(k_pack_swiglu<uint16_t>, g, dim3(256), 0, s,
+                       static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(w3), d, F,
+                       static_cast<uint16_t*>(dst));
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,460 @@
+// RMSNorm statistic, router GEMM with the r-scale epilogue, top-k gating,
+// and the two-stage top-k of the Cartesian-product router.
+//
+// CODA sparse-MoE thread (router-fusion paragraph): the router is a plain
+// GEMM right after the RMSNorm, and the per-token statistic r is applied to
+// its output just before the top-k.  The GEMM therefore reads the raw rows
+// of x once; the sum of squares that gives r is accumulated from the same
+// registers that feed the matrix cores.
+//
+// "Mixture of Experts (MoE)" glossary, top-k gating: the k highest-scoring
+// experts are selected (k = 1 is switch routing) and weighted by their
+// scores -- here a softmax over the k selected logits (or the full-softmax
+// probability).  Ties go to the lower expert index; slot 0 is the best.
+//
+// OmniMoE summary, 2.2 (Cartesian-product router): expert n = i*Nc + j
+// scores s1[i] + s2[j].  The exact top-k over the Nr x Nc grid is found
+// among the k x k pairs of the row top-k and the column top-k.
+#include <algorithm>
+
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+// ---------------------------------------------------------------- RMSNorm
+
+template <typename T>
+__global__ void __launch_bounds__(256) k_rmsnorm(const T* __restrict__ x, int64_t T_, int64_t d,
+                                                 const T* __restrict__ gamma, float eps,
+                                                 float* __restrict__ r, T* __restrict__ xg) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T_) return;
+  constexpr int N = Vec16<T>::N;
+  const int64_t nvec = d / N;
+  const uint4* xs = reinterpret_cast<const uint4*>(x + t * d);
+  float ss = 0.f;
+  for (int64_t v = lane; v < nvec; v += 64) {
+    float f[8];
+    unpack16(xs[v], f, (const T*)nullptr);
+#pragma unroll
+    for (int i = 0; i < N; ++i) ss = fmaf(f[i], f[i], ss);
+  }
+  ss = wave_sum(ss);
+  const float rr = 1.0f / sqrtf(ss / float(d) + eps);
+  if (lane == 0) r[t] = rr;
+  if (gamma && xg) {
+    const uint4* gs = reinterpret_cast<const uint4*>(gamma);
+    uint4* xo = reinterpret_cast<uint4*>(xg + t * d);
+    for (int64_t v = lane; v < nvec; v += 64) {
+      float f[8], g[8];
+      unpack16(xs[v], f, (const T*)nullptr);
+      unpack16(gs[v], g, (const T*)nullptr);
+#pragma unroll
+      for (int i = 0; i < N; ++i) f[i] *= g[i];
+      xo[v] = pack16(f, (const T*)nullptr);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- top-k helpers
+
+struct KV {
+  float v;
+  int i;
+};
+__device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
+  return av > bv || (av == bv && ai < bi);
+}
+// Wave-wide best (value desc, index asc); every lane gets the result.
+__device__ __forceinline__ KV wave_best(float v, int i) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(v, o, 64);
+    const int oi = __shfl_xor(i, o, 64);
+    if (better(ov, oi, v, i)) {
+      v = ov;
+      i = oi;
+    }
+  }
+  return KV{v, i};
+}
+
+// Top-k of n values held as lane-strided registers vals[q] (index lane + 64q),
+// q < Q.  Selection j (j < k <= 64*QS) lands in lane j % 64, register j / 64.
+template <int Q, int QS>
+__device__ void wave_topk(const float (&vals)[Q], int n, int k, float (&sv)[QS], int (&si)[QS]) {
+  const int lane = threadIdx.x & 63;
+  bool live[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) live[q] = lane + 64 * q < n;
+#pragma unroll
+  for (int q = 0; q < QS; ++q) {
+    sv[q] = -INFINITY;
+    si[q] = 0;
+  }
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int idx = lane + 64 * q;
+      if (live[q] && better(vals[q], idx, bv, bi)) {
+        bv = vals[q];
+        bi = idx;
+      }
+    }
+    const KV w = wave_best(bv, bi);
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+      if (lane + 64 * q == w.i) live[q] = false;
+#pragma unroll
+    for (int q = 0; q < QS; ++q)
+      if ((j >> 6) == q && (j & 63) == lane) {
+        sv[q] = w.v;
+        si[q] = w.i;
+      }
+  }
+}
+
+// Gates of the k selections held as in wave_topk; writes ids / w of token t.
+template <int QS, int Q>
+__device__ void write_gates(const float (&sv)[QS], const int (&si)[QS], const float (&vals)[Q],
+                            int n, int k, int renorm, int64_t t, int32_t* ids, float* wout) {
+  const int lane = threadIdx.x & 63;
+  const float mx = __shfl(sv[0], 0, 64);
+  float denom = 0.f;
+  if (renorm) {
+#pragma unroll
+    for (int q = 0; q < QS; ++q)
+      if (lane + 64 * q < k) denom += expf(sv[q] - mx);
+  } else {
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+      if (lane + 64 * q < n) denom += expf(vals[q] - mx);
+  }
+  denom = wave_sum(denom);
+#pragma unroll
+  for (int q = 0; q < QS; ++q) {
+    const int j = lane + 64 * q;
+    if (j < k) {
+      ids[t * k + j] = si[q];
+      wout[t * k + j] = expf(sv[q] - mx) / denom;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dense router, bf16 (MFMA)
+
+constexpr int kRouterTok = 16;  // tokens per workgroup (one 16-wide MFMA block)
+
+// Workgroup: 4 waves split K; each wave runs 16x16x32 MFMAs with the router
+// rows as the A operand (16 experts per block) and 16 token rows as B.
+template <int NB>
+__global__ void __launch_bounds__(256) k_router_bf16(
+    const uint16_t* __restrict__ x, int T, int d, const uint16_t* __restrict__ wr,
+    const float* __restrict__ bias, int E, const float* __restrict__ r_in, float eps,
+    float* __restrict__ r_out, int k, int renorm, int32_t* __restrict__ ids,
+    float* __restrict__ wout, float* __restrict__ logits) {
+  __shared__ float lg[kRouterTok][NB * 16 + 1];
+  __shared__ float ssq[kRouterTok];
+  __shared__ float rs[kRouterTok];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * kRouterTok;
+  const int tl = lane & 15;       // token within the block (B column)
+  const int kg = lane >> 4;       // which 8-element K group
+  const int t = t0 + tl;
+  const bool tok_ok = t < T;
+  const int kw = d / 4;           // K range of this wave
+  const int kb = wid * kw;
+
+  f32x4 acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float ss = 0.f;
+  const uint16_t* xrow = x + int64_t(tok_ok ? t : 0) * d + kb + kg * 8;
+  const uint16_t* wrow[NB];
+  bool wok[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int e = b * 16 + tl;
+    wok[b] = e < E;
+    wrow[b] = wr + int64_t(wok[b] ? e : 0) * d + kb + kg * 8;
+  }
+  for (int kk = 0; kk < kw; kk += 32) {
+    uint4 xv = tok_ok ? *reinterpret_cast<const uint4*>(xrow + kk) : make_uint4(0, 0, 0, 0);
+    {
+      float f[8];
+      unpack16(xv, f, (const uint16_t*)nullptr);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss = fmaf(f[i], f[i], ss);
+    }
+    const bf16x8 bx = __builtin_bit_cast(bf16x8, xv);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const uint4 wv = wok[b] ? *reinterpret_cast<const uint4*>(wrow[b] + kk) : make_uint4(0, 0, 0, 0);
+      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wv), bx, acc[b], 0, 0, 0);
+    }
+  }
+  // sum of squares of the token over this wave's K range (lanes tl, tl+16, ...)
+  ss += __shfl_xor(ss, 16, 64);
+  ss += __shfl_xor(ss, 32, 64);
+  // ordered cross-wave reduction (wave 0, then 1, 2, 3): deterministic
+  for (int w = 0; w < 4; ++w) {
+    if (wid == w) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int e = b * 16 + kg * 4 + v;
+          if (w == 0) lg[tl][e] = acc[b][v];
+          else lg[tl][e] += acc[b][v];
+        }
+      if (lane < 16) {
+        if (w == 0) ssq[tl] = ss;
+        else ssq[tl] += ss;
+      }
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x < kRouterTok) {
+    const int tt = t0 + threadIdx.x;
+    float rr = 0.f;
+    if (tt < T) {
+      rr = r_in ? r_in[tt] : 1.0f / sqrtf(ssq[threadIdx.x] / float(d) + eps);
+      if (!r_in && r_out) r_out[tt] = rr;
+    }
+    rs[threadIdx.x] = rr;
+  }
+  __syncthreads();
+  // epilogue: r-scale + bias, then top-k per token (each wave: 4 tokens)
+  for (int q = 0; q < kRouterTok / 4; ++q) {
+    const int tl2 = wid * (kRouterTok / 4) + q;
+    const int tt = t0 + tl2;
+    if (tt >= T) break;
+    const float rr = rs[tl2];
+    float vals[4];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int e = lane + 64 * qq;
+      vals[qq] = -INFINITY;
+      if (e < E) {
+        vals[qq] = rr * lg[tl2][e] + (bias ? bias[e] : 0.f);
+        if (logits) logits[int64_t(tt) * E + e] = vals[qq];
+      }
+    }
+    float sv[4];
+    int si[4];
+    wave_topk<4, 4>(vals, E, k, sv, si);
+    write_gates<4, 4>(sv, si, vals, E, k, renorm, tt, ids, wout);
+  }
+}
+
+// ---------------------------------------------------------------- dense router, fp32
+
+__global__ void k_router_logits_f32(const float* __restrict__ x, int T, int d,
+                                    const float* __restrict__ wr, const float* __restrict__ bias,
+                                    int E, const float* __restrict__ r_in, float eps,
+                                    float* __restrict__ r_out, float* __restrict__ lg) {
+  const int64_t g = blockIdx.x * int64_t(blockDim.x) + threadIdx.x;
+  if (g >= int64_t(T) * E) return;
+  const int t = int(g / E), e = int(g % E);
+  const float* xr = x + int64_t(t) * d;
+  const float* wrow = wr + int64_t(e) * d;
+  float acc = 0.f, ss = 0.f;
+  for (int i = 0; i < d; ++i) {
+    acc = fmaf(xr[i], wrow[i], acc);
+    ss = fmaf(xr[i], xr[i], ss);
+  }
+  const float rr = r_in ? r_in[t] : 1.0f / sqrtf(ss / float(d) + eps);
+  if (!r_in && r_out && e == 0) r_out[t] = rr;
+  lg[g] = rr * acc + (bias ? bias[e] : 0.f);
+}
+
+__global__ void __launch_bounds__(256) k_topk_rows(const float* __restrict__ lg, int T, int E, int k,
+                                                   int renorm, int32_t* __restrict__ ids,
+                                                   float* __restrict__ wout) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wid;
+  if (t >= T) return;
+  float vals[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = lane + 64 * q;
+    vals[q] = e < E ? lg[int64_t(t) * E + e] : -INFINITY;
+  }
+  float sv[4];
+  int si[4];
+  wave_topk<4, 4>(vals, E, k, sv, si);
+  write_gates<4, 4>(sv, si, vals, E, k, renorm, t, ids, wout);
+}
+
+// ---------------------------------------------------------------- Cartesian two-stage top-k
+
+// One wave per token.  scores row = [s1 (Nr) | s2 (Nc)] fp32.  Q = ceil(max(Nr,Nc,k*k)/64).
+template <int Q>
+__global__ void __launch_bounds__(256) k_cartesian_topk(const float* __restrict__ scores, int T,
+                                                        int Nr, int Nc, int k, int renorm,
+                                                        int32_t* __restrict__ ids,
+                                                        float* __restrict__ wout) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wid;
+  if (t >= T) return;
+  const float* row = scores + int64_t(t) * (Nr + Nc);
+  float vals[Q];
+  float m1 = -INFINITY, z1 = 0.f, m2 = -INFINITY, z2 = 0.f;
+  // stage 1a: the k best rows of s1 (lane a holds row choice a)
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int i = lane + 64 * q;
+    vals[q] = i < Nr ? row[i] : -INFINITY;
+  }
+  if (!renorm) {
+#pragma unroll
+    for (int q = 0; q < Q; ++q) m1 = fmaxf(m1, vals[q]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m1 = fmaxf(m1, __shfl_xor(m1, o, 64));
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+      if (lane + 64 * q < Nr) z1 += expf(vals[q] - m1);
+    z1 = wave_sum(z1);
+  }
+  float v1[1], v2[1];
+  int i1[1], i2[1];
+  wave_topk<Q, 1>(vals, Nr, k, v1, i1);
+  // stage 1b: the k best columns of s2
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int j = lane + 64 * q;
+    vals[q] = j < Nc ? row[Nr + j] : -INFINITY;
+  }
+  if (!renorm) {
+#pragma unroll
+    for (int q = 0; q < Q; ++q) m2 = fmaxf(m2, vals[q]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m2 = fmaxf(m2, __shfl_xor(m2, o, 64));
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+      if (lane + 64 * q < Nc) z2 += expf(vals[q] - m2);
+    z2 = wave_sum(z2);
+  }
+  wave_topk<Q, 1>(vals, Nc, k, v2, i2);
+  // stage 2: the k*k pairs; candidate c = a*k + b -> (row choice a, column choice b).
+  // Key: (s1 + s2 in fp32) descending, then flat id I[a]*Nc + J[b] ascending.
+  const int nc = k * k;
+  int cid[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int c = lane + 64 * q;
+    const int a = c / k, b = c - (c / k) * k;
+    const float va = __shfl(v1[0], a & 63, 64), vb = __shfl(v2[0], b & 63, 64);
+    const int ia = __shfl(i1[0], a & 63, 64), ib = __shfl(i2[0], b & 63, 64);
+    vals[q] = c < nc ? va + vb : -INFINITY;
+    cid[q] = c < nc ? ia * Nc + ib : 0x7fffffff;
+  }
+  bool live[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) live[q] = lane + 64 * q < nc;
+  float sv = -INFINITY;
+  int si = 0;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+      if (live[q] && better(vals[q], cid[q], bv, bi)) {
+        bv = vals[q];
+        bi = cid[q];
+      }
+    const KV w = wave_best(bv, bi);
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+      if (live[q] && cid[q] == w.i) live[q] = false;
+    if (j == lane) {
+      sv = w.v;
+      si = w.i;
+    }
+  }
+  const float mx = __shfl(sv, 0, 64);
+  if (renorm) {
+    const float dd = wave_sum(lane < k ? expf(sv - mx) : 0.f);
+    if (lane < k) {
+      ids[int64_t(t) * k + lane] = si;
+      wout[int64_t(t) * k + lane] = expf(sv - mx) / dd;
+    }
+  } else if (lane < k) {
+    // full softmax over the grid: sum_ij exp(s1_i + s2_j) = (sum_i e^s1_i)(sum_j e^s2_j)
+    ids[int64_t(t) * k + lane] = si;
+    const float s1 = row[si / Nc], s2 = row[Nr + si % Nc];
+    wout[int64_t(t) * k + lane] = expf(s1 - m1) * expf(s2 - m2) / (z1 * z2);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm(const void* x, int dtype, int64_t T, int64_t d, const void* gamma,
+                          float eps, float* r, void* xg, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const dim3 g(unsigned((T + 3) / 4));
+  if (dtype == 0)
+    hipLaunchKernelGGL(k_rmsnorm<float>, g, dim3(256), 0, s, static_cast<const float*>(x), T, d,
+                       static_cast<const float*>(gamma), eps, r, static_cast<float*>(xg));
+  else
+    hipLaunchKernelGGL(k_rmsnorm<uint16_t>, g, dim3(256), 0, s, static_cast<const uint16_t*>(x), T,
+                       d, static_cast<const uint16_t*>(gamma), eps, r, static_cast<uint16_t*>(xg));
+  return hipGetLastError();
+}
+
+hipError_t launch_router_dense(const void* x, int dtype, int64_t T, int64_t d, const void* wr_t,
+                               const float* bias, int64_t E, const float* r_in, float eps,
+                               float* r_out, int k, int renorm, int32_t* ids, float* w,
+                               float* logits, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (dtype == 0) {
+    // fp32: logits into the caller's buffer (required), then top-k per row
+    const int64_t n = T * E;
+    hipLaunchKernelGGL(k_router_logits_f32, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const float*>(x), int(T), int(d),
+                       static_cast<const float*>(wr_t), bias, int(E), r_in, eps, r_out, logits);
+    hipLaunchKernelGGL(k_topk_rows, dim3(unsigned((T + 3) / 4)), dim3(256), 0, s, logits, int(T),
+                       int(E), k, renorm, ids, w);
+    return hipGetLastError();
+  }
+  const dim3 g(unsigned((T + kRouterTok - 1) / kRouterTok));
+  const int nb = int((E + 15) / 16);
+#define MOE_ROUTER_CASE(NBV)                                                                     \
+  hipLaunchKernelGGL(k_router_bf16<NBV>, g, dim3(256), 0, s, static_cast<const uint16_t*>(x),     \
+                     int(T), int(d), static_cast<const uint16_t*>(wr_t), bias, int(E), r_in, eps, \
+                     r_out, k, renorm, ids, w, logits)
+  if (nb <= 1) MOE_ROUTER_CASE(1);
+  else if (nb <= 2) MOE_ROUTER_CASE(2);
+  else if (nb <= 4) MOE_ROUTER_CASE(4);
+  else if (nb <= 8) MOE_ROUTER_CASE(8);
+  else MOE_ROUTER_CASE(16);
+#undef MOE_ROUTER_CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_cartesian_topk(const float* scores, int64_t T, int64_t Nr, int64_t Nc, int k,
+                                 int renorm, int32_t* ids, float* w, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int64_t need = std::max<int64_t>(std::max<int64_t>(Nr, Nc), int64_t(k) * k);
+  const dim3 g(unsigned((T + 3) / 4));
+  if (need <= 64 * 4)
+    hipLaunchKernelGGL(k_cartesian_topk<4>, g, dim3(256), 0, s, scores, int(T), int(Nr), int(Nc),
+                       k, renorm, ids, w);
+  else if (need <= 64 * 16)
+    hipLaunchKernelGGL(k_cartesian_topk<16>, g, dim3(256), 0, s, scores, int(T), int(Nr),
+                       int(Nc), k, renorm, ids, w);
+  else if (need <= 64 * 32)
+    hipLaunchKernelGGL(k_cartesian_topk<32>, g, dim3(256), 0, s, scores, int(T), int(Nr),
+                       int(Nc), k, renorm, ids, w);
+  else
+    hipLaunchKernelGGL(k_cartesian_topk<64>, g, dim3(256), 0, s, scores, int(T), int(Nr),
+                       int(Nc), k, renorm, ids, w);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,171 @@
+"""One MoE FFN layer on the GPU: weight packing, descriptors, workspace.
+
+A thin owner of device buffers around the C ABI: it packs the weights once
+(moe_pack_transpose / moe_pack_swiglu), fills the moe_layer_desc and calls
+moe_layer_forward.  No arithmetic of the layer happens here.
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+from . import binding as B
+from .workloads import Workload
+
+
+class MoELayer:
+    def __init__(self, wl: Workload, params: dict, device="cuda"):
+        import torch
+        self.wl = wl
+        self.device = device
+        self.tdtype = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+        self.dtype = B.MOE_F32 if wl.dtype == "f32" else B.MOE_BF16
+        d = wl.d
+        keep = []
+        desc = B.LayerDesc()
+        desc.d = d
+        desc.dtype = self.dtype
+        desc.gamma = B.ptr(params.get("gamma"))
+        keep.append(params.get("gamma"))
+        desc.eps = wl.eps
+        desc.k = wl.k
+        desc.renorm = wl.renorm
+        desc.capacity_factor = wl.cf
+        desc.residual = 1
+        desc.timer = None
+
+        def empty(*shape):
+            return torch.empty(shape, dtype=self.tdtype, device=device)
+
+        # router
+        R = desc.router
+        if wl.router == "cartesian":
+            R.kind = B.ROUTER_CARTESIAN
+            R.E = wl.Nr * wl.Nc
+            R.Nr, R.Nc = wl.Nr, wl.Nc
+            keys_t = empty(wl.Nr + wl.Nc, d)
+            B.pack_transpose(params["k_rows"], keys_t[: wl.Nr])
+            B.pack_transpose(params["k_cols"], keys_t[wl.Nr:])
+            R.keys_t = keys_t.data_ptr()
+            keep.append(keys_t)
+        else:
+            R.kind = B.ROUTER_DENSE
+            R.E = wl.E
+            wr_t = empty(wl.E, d)
+            B.pack_transpose(params["w_router"], wr_t)
+            R.wr_t = wr_t.data_ptr()
+            keep.append(wr_t)
+            bias = params.get("bias")
+            if bias is not None:
+                bias = bias.to(device=device, dtype=torch.float32).contiguous()
+                R.bias = bias.data_ptr()
+                keep.append(bias)
+        # routed experts
+        X = desc.experts
+        self._fill_experts(X, wl, params, keep, "w1", "w3", "w2", wl.sizes, wl.act,
+                           {"grouped": B.EXPERTS_GROUPED, "bcsr": B.EXPERTS_BCSR,
+                            "atomic": B.EXPERTS_ATOMIC}[wl.expert_kind])
+        # shared experts
+        self.shared_desc = None
+        if wl.shared_ffn:
+            S = B.ExpertsDesc()
+            self._fill_experts(S, wl, params, keep, "ws1", "ws3", "ws2", [wl.shared_ffn],
+                               wl.shared_act, B.EXPERTS_GROUPED)
+            self.shared_desc = S
+            desc.shared = C.pointer(S)
+        self.desc = desc
+        self._keep = keep
+        torch.cuda.current_stream().synchronize()
+
+    def _fill_experts(self, X, wl, params, keep, n1, n3, n2, sizes, act, kind):
+        import torch
+        d = wl.d
+        X.kind = kind
+        X.act = B.ACT[act]
+        if kind == B.EXPERTS_ATOMIC:
+            X.E = wl.Nr * wl.Nc
+            X.W = params["W"].data_ptr()
+            X.V = params["V"].data_ptr()
+            keep += [params["W"], params["V"]]
+            return
+        E = len(sizes)
+        X.E = E
+        F = sum(sizes)
+        arr = B.i64_array(sizes)
+        keep.append(arr)
+        X.ffn_sizes = C.cast(arr, C.POINTER(C.c_int64))
+        off = [0]
+        for s in sizes:
+            off.append(off[-1] + s)
+        foff = torch.tensor(off, dtype=torch.int32, device=self.device)
+        X.ffn_offsets = foff.data_ptr()
+        keep.append(foff)
+        if act == "swiglu":
+            w13 = torch.empty((2 * F, d), dtype=self.tdtype, device=self.device)
+            B.pack_swiglu(params[n1], params[n3], sizes, w13)
+        else:
+            w13 = torch.empty((F, d), dtype=self.tdtype, device=self.device)
+            B.pack_transpose(params[n1], w13)
+        w2t = torch.empty((d, F), dtype=self.tdtype, device=self.device)
+        B.pack_transpose(params[n2], w2t)
+        X.w13_t = w13.data_ptr()
+        X.w2_t = w2t.data_ptr()
+        keep += [w13, w2t]
+        X.block = 128
+        if kind == B.EXPERTS_BCSR:
+            sb = torch.tensor([s // 128 for s in sizes], dtype=torch.int32, device=self.device)
+            bo = torch.tensor([o // 128 for o in off], dtype=torch.int32, device=self.device)
+            X.size_blocks = sb.data_ptr()
+            X.block_offsets = bo.data_ptr()
+            keep += [sb, bo]
+
+    # ------------------------------------------------------------ calls
+
+    def workspace_size(self, T: int) -> int:
+        n = int(B.lib().moe_layer_workspace_size(C.byref(self.desc), T))
+        if n == 0:
+            raise B.MoeError(-1, B.last_error() or "invalid layer descriptor")
+        return n
+
+    def alloc_workspace(self, T: int):
+        import torch
+        return torch.empty(self.workspace_size(T), dtype=torch.uint8, device=self.device)
+
+    def forward(self, x, out=None, ws=None, stats=None, timer: B.StageTimer | None = None,
+                stream=None):
+        import torch
+        T = x.shape[0]
+        if out is None:
+            out = torch.empty_like(x)
+        if ws is None:
+            ws = self.alloc_workspace(T)
+        self.desc.timer = None if timer is None else timer.handle
+        try:
+            B.check(B.lib().moe_layer_forward(C.byref(self.desc), B.ptr(x), T, B.ptr(out),
+                                              B.ptr(stats), B.ptr(ws), ws.numel(),
+                                              B.stream_handle(stream)))
+        finally:
+            self.desc.timer = None
+        return out
+
+    def routing(self, T: int, ws) -> dict:
+        """Views into the workspace of the routing of the last forward."""
+        import torch
+        rt = B.Routing()
+        B.check(B.lib().moe_layer_routing(C.byref(self.desc), T, B.ptr(ws), ws.numel(),
+                                          C.byref(rt)))
+        base = ws.data_ptr()
+        k, E, R = rt.k, rt.E, rt.rows_max
+
+        def view(p, n, dt):
+            nbytes = n * torch.empty(0, dtype=dt).element_size()
+            o = p - base
+            return ws[o:o + nbytes].view(dt)
+
+        i32, f32 = torch.int32, torch.float32
+        return dict(
+            ids=view(rt.ids, T * k, i32).view(T, k), w=view(rt.w, T * k, f32).view(T, k),
+            r=view(rt.r, T, f32), counts=view(rt.counts, E, i32),
+            offsets=view(rt.offsets, E + 1, i32), pos=view(rt.pos, T * k, i32).view(T, k),
+            row_token=view(rt.row_token, R, i32), row_r=view(rt.row_r, R, f32),
+            row_w=view(rt.row_w, R, f32), row_expert=view(rt.row_expert, R, i32),
+            rows_max=R, pad=rt.pad)

@@ -1,0 +1,62 @@
+"""Shared helpers of the GPU parity tests: workload cases, oracle parameters,
+error metrics.  Inputs come from the seeded generator; expected values come
+only from the oracle."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle as O
+from sparse_mixture_experts_rmsnorm_amd.workloads import WORKLOADS, Workload
+
+# Small layers the oracle finishes in seconds; each spans several GEMM tiles
+# (256 features x 128 rows) with ragged tails, and together they cover every
+# router / expert kind, drops, empty experts, a gain, k = 1 and k = E.
+SMALL = {
+    "tiny_fp32": WORKLOADS["tiny_fp32"],
+    "fp32_swiglu_drops": Workload("fp32_swiglu_drops", T=100, d=128, E=4, k=2, dtype="f32",
+                                  act="swiglu", ffn=128, cf=0.75, bias="normal", seed=16),
+    "mixtral_small_drops": Workload("mixtral_small_drops", T=300, d=512, E=8, k=2, act="swiglu",
+                                    ffn=384, cf=1.0, bias="normal", seed=11),
+    "mixtral_small": Workload("mixtral_small", T=700, d=512, E=8, k=2, act="swiglu", ffn=640,
+                              cf=1.25, seed=17),
+    "gelu_gamma_switch": Workload("gelu_gamma_switch", T=257, d=256, E=4, k=1, act="gelu",
+                                  ffn=512, cf=2.0, gamma=True, seed=12),
+    "gelu_tanh_dense_mixture": Workload("gelu_tanh_dense_mixture", T=130, d=256, E=4, k=4,
+                                        act="gelu_tanh", ffn=256, cf=0.0, seed=18),
+    "bcsr_small": Workload("bcsr_small", T=600, d=256, E=4, k=2, act="gelu",
+                           expert_sizes=((1, 512), (3, 256)), bias="normal", expert_kind="bcsr",
+                           seed=13),
+    "finegrained_small": Workload("finegrained_small", T=500, d=256, E=64, k=6, act="swiglu",
+                                  ffn=128, cf=1.5, bias="zipf", shared_ffn=256, seed=14),
+    "atomic_small": Workload("atomic_small", T=200, d=512, E=128 * 128, k=8, act="gelu",
+                             router="cartesian", Nr=128, Nc=128, expert_kind="atomic",
+                             shared_ffn=512, shared_act="gelu", seed=15),
+}
+
+# max |gpu - ref| / max |ref| per output tensor
+TOL = {"f32": 1e-3, "bf16": 2e-2}
+
+
+def rel_err(gpu, ref) -> float:
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.max(np.abs(ref)) if ref.size else 1.0
+    return float(np.max(np.abs(gpu - ref)) / den) if ref.size else 0.0
+
+
+def oracle_params(wl: Workload, inp: dict) -> dict:
+    p = dict(k=wl.k, eps=wl.eps, renorm=wl.renorm, cf=wl.cf, act=wl.act, residual=True,
+             gamma=inp.get("gamma"), pad=wl.pad)
+    if wl.router == "cartesian":
+        p.update(router="cartesian", k_rows=inp["k_rows"], k_cols=inp["k_cols"], W=inp["W"],
+                 V=inp["V"])
+    else:
+        p.update(router="dense", w_router=inp["w_router"], bias=inp.get("bias"), w1=inp["w1"],
+                 w3=inp.get("w3"), w2=inp["w2"], f_offsets=wl.f_offsets)
+    if wl.shared_ffn:
+        p.update(ws1=inp["ws1"], ws3=inp.get("ws3"), ws2=inp["ws2"], shared_act=wl.shared_act)
+    return p
+
+
+def f64(a) -> np.ndarray:
+    return O.as_f64(a)

@@ -1,0 +1,274 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Integer results (ids, counts, offsets, permutation, dropped set, topology)
+must match bit-exactly; floating-point outputs within max|gpu-ref|/max|ref|
+of 1e-3 (fp32) or 2e-2 (bf16).  Routing follows a stage-wise protocol: the
+top-k decision is checked bit-exactly on the GPU's own logits, then every
+later stage is compared on the GPU's ids.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from gpu_cases import SMALL, TOL, f64, oracle_params, rel_err
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from sparse_mixture_experts_rmsnorm_amd import binding as B  # noqa: E402
+from sparse_mixture_experts_rmsnorm_amd import synth  # noqa: E402
+from sparse_mixture_experts_rmsnorm_amd.layer import MoELayer  # noqa: E402
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()   # fail loudly if the library is missing
+    return "cuda"
+
+
+def _setup(name, dev):
+    wl = SMALL[name]
+    inp = synth.make_numpy(wl)
+    params = {k: synth.to_device(v, dev) for k, v in inp.items()}
+    layer = MoELayer(wl, params, dev)
+    return wl, inp, params, layer
+
+
+def _gpu_logits(wl, layer, params, r):
+    """Run the router alone with its logits output (fp32)."""
+    T = wl.T
+    x = params["xg"] if "xg" in params else params["x"]
+    E = wl.E if wl.router == "dense" else wl.Nr + wl.Nc
+    logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    ids = torch.empty((T, wl.k), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, wl.k), dtype=torch.float32, device=x.device)
+    nws = B.router_workspace_size(layer.desc.router, T)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=x.device)
+    B.router_topk(layer.desc.router, x, wl.k, wl.renorm, ids, w, r_in=r, logits=logits, ws=ws)
+    return logits, ids, w
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layer_parity(name, dev):
+    _say(f"[gpu] layer parity {name}")
+    wl, inp, params, layer = _setup(name, dev)
+    x = params["x"]
+    ws = layer.alloc_workspace(wl.T)
+    stats = torch.zeros(4, dtype=torch.int32, device=dev)
+    out = layer.forward(x, ws=ws, stats=stats)
+    torch.cuda.synchronize()
+    rt = layer.routing(wl.T, ws)
+    ids = rt["ids"].cpu().numpy()
+    w = rt["w"].cpu().numpy()
+    r = rt["r"].cpu().numpy()
+    p = oracle_params(wl, inp)
+
+    # r: RMSNorm statistic
+    r_ref = O.rmsnorm_scale(inp["x"], wl.eps)
+    assert rel_err(r, r_ref) < 1e-5
+
+    # router: bit-exact selection on the GPU's logits, logits within tolerance
+    if wl.gamma:
+        xg = torch.empty_like(x)
+        B.rmsnorm_stats(x, wl.eps, torch.empty(wl.T, device=dev), gamma=params["gamma"], xg=xg)
+        params["xg"] = xg
+    logits, ids2, w2 = _gpu_logits(wl, layer, params, rt["r"])
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy()
+    assert np.array_equal(ids2.cpu().numpy(), ids)          # the same decision twice
+    if wl.router == "dense":
+        assert np.array_equal(O.select_topk(lg, wl.k), ids)
+        l_ref = O.router_logits(inp["x"], inp.get("gamma"), r_ref, inp["w_router"], inp.get("bias"))
+        assert rel_err(lg, l_ref) < (1e-5 if wl.dtype == "f32" else 1e-2)
+        g_ref = O.gates(lg.astype(np.float64), ids, wl.renorm)
+        assert rel_err(w, g_ref) < 1e-5
+        # against the oracle's own routing: only near-ties may differ
+        own = O.select_topk(l_ref, wl.k)
+        bad = np.nonzero(np.any(own != ids, axis=1))[0]
+        srt = -np.sort(-l_ref, axis=1)
+        for t in bad:
+            gap = srt[t, wl.k - 1] - srt[t, wl.k] if wl.k < wl.E else np.inf
+            assert gap < 1e-3 * np.max(np.abs(l_ref)), (t, gap)
+    else:
+        s1, s2 = lg[:, :wl.Nr], lg[:, wl.Nr:]
+        sel, sc = O.cartesian_topk(s1, s2, wl.k)               # float32 sums, as the kernel
+        assert np.array_equal(sel, ids)
+        s1r, s2r = O.cartesian_scores(inp["x"], inp.get("gamma"), r_ref, inp["k_rows"], inp["k_cols"])
+        assert rel_err(lg, np.hstack([s1r, s2r])) < 1e-2
+        e = np.exp(sc.astype(np.float64) - sc[:, :1])
+        assert rel_err(w, e / e.sum(axis=1, keepdims=True)) < 1e-5
+
+    # dispatch on the GPU's ids: bit-exact
+    E = wl.E if wl.router == "dense" else wl.Nr * wl.Nc
+    cap = O.capacity(wl.T, wl.k, E, wl.cf)
+    disp = O.dispatch(ids, E, cap, wl.pad)
+    assert np.array_equal(rt["counts"].cpu().numpy(), disp["counts"])
+    assert np.array_equal(rt["offsets"].cpu().numpy(), disp["offsets"])
+    pos = rt["pos"].cpu().numpy()
+    assert np.array_equal(pos, disp["pos"])
+    rows = disp["rows"]
+    row_token = rt["row_token"].cpu().numpy()
+    assert np.array_equal(row_token[:rows], disp["row_token"])
+    assert np.all(row_token[rows:] == -1)
+    kept = pos >= 0
+    row_w = rt["row_w"].cpu().numpy()
+    row_r = rt["row_r"].cpu().numpy()
+    assert np.array_equal(row_w[pos[kept]], w[kept])
+    assert np.array_equal(row_r[pos[kept]], r[np.nonzero(kept)[0]])
+    st = stats.cpu().numpy()
+    assert st[0] == rows and st[1] == disp["dropped"] and st[2] == disp["max_load"] and st[3] == 0
+
+    # whole layer on the GPU's routing
+    ref = O.layer_forward(p, inp["x"], ids_override=ids)
+    out_np = f64(synth.to_host(out))
+    x64 = f64(inp["x"])
+    tol = TOL[wl.dtype]
+    e_out = rel_err(out_np, ref["out"])
+    e_moe = rel_err(out_np - x64, ref["out"] - x64)
+    _say(f"  {name}: rel err out {e_out:.2e}, experts-only {e_moe:.2e}, dropped {disp['dropped']}")
+    assert e_out <= tol
+    assert e_moe <= (tol if wl.dtype == "f32" else 3 * tol)
+    # fully dropped tokens pass through bit-exactly
+    gone = np.all(pos < 0, axis=1)
+    if gone.any():
+        xb = synth.to_host(x)
+        assert np.array_equal(synth.to_host(out)[gone], xb[gone])
+
+
+@pytest.mark.parametrize("name", ["mixtral_small_drops", "finegrained_small", "atomic_small"])
+def test_determinism(name, dev):
+    _say(f"[gpu] determinism {name}")
+    wl, inp, params, layer = _setup(name, dev)
+    ws = layer.alloc_workspace(wl.T)
+    a = layer.forward(params["x"], ws=ws).clone()
+    ra = {k: v.clone() for k, v in layer.routing(wl.T, ws).items() if torch.is_tensor(v)}
+    b = layer.forward(params["x"], ws=ws)
+    rb = layer.routing(wl.T, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                       b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+    for k, v in ra.items():
+        assert torch.equal(v, rb[k]), k
+
+
+@pytest.mark.parametrize("E,k,cap,pad,T", [(8, 2, 5, 1, 40), (8, 2, 1000, 128, 300),
+                                           (64, 6, 30, 1, 1000), (5, 3, 2, 4, 1),
+                                           (256, 8, 7, 1, 513), (3000, 4, 10 ** 6, 1, 777),
+                                           (1 << 20, 32, 10 ** 6, 1, 300)])
+def test_dispatch_bit_exact(E, k, cap, pad, T, dev):
+    _say(f"[gpu] dispatch E={E} k={k} cap={cap} pad={pad} T={T}")
+    rng = np.random.default_rng(E + k + T)
+    # skewed ids (many ties in token order), distinct within a token
+    pop = rng.zipf(1.3, size=E * 4) % E
+    ids = np.empty((T, k), dtype=np.int32)
+    for t in range(T):
+        ch = []
+        while len(ch) < k:
+            e = int(pop[rng.integers(0, len(pop))]) if rng.random() < 0.7 else int(rng.integers(0, E))
+            if e not in ch:
+                ch.append(e)
+        ids[t] = ch
+    w = rng.random((T, k)).astype(np.float32)
+    r = rng.random(T).astype(np.float32)
+    capc = min(cap, T)
+    R = B.rows_max(T, k, E, capc, pad)
+    out = dict(counts=torch.empty(E, dtype=torch.int32, device=dev),
+               offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+               pos=torch.empty((T, k), dtype=torch.int32, device=dev),
+               row_token=torch.empty(max(R, 1), dtype=torch.int32, device=dev),
+               row_r=torch.empty(max(R, 1), dtype=torch.float32, device=dev),
+               row_w=torch.empty(max(R, 1), dtype=torch.float32, device=dev),
+               row_expert=torch.empty(max(R, 1), dtype=torch.int32, device=dev))
+    d = 256
+    xb = O.f64_to_bf16_bits(rng.standard_normal((T, d)))
+    x = synth.to_device(xb, dev)
+    x_perm = torch.empty((max(R, 1), d), dtype=torch.bfloat16, device=dev) if E <= 2048 else None
+    stats = torch.zeros(4, dtype=torch.int32, device=dev)
+    ws = torch.empty(B.dispatch_workspace_size(T, k, E), dtype=torch.uint8, device=dev)
+    B.dispatch(torch.from_numpy(ids).to(dev), torch.from_numpy(w).to(dev), torch.from_numpy(r).to(dev),
+               E, capc, pad, R, out, x=x if x_perm is not None else None, x_perm=x_perm,
+               stats=stats, ws=ws)
+    torch.cuda.synchronize()
+    ref = O.dispatch(ids, E, capc, pad)
+    assert np.array_equal(out["counts"].cpu().numpy(), ref["counts"])
+    assert np.array_equal(out["offsets"].cpu().numpy(), ref["offsets"])
+    assert np.array_equal(out["pos"].cpu().numpy(), ref["pos"])
+    rows = ref["rows"]
+    rtok = out["row_token"].cpu().numpy()
+    assert np.array_equal(rtok[:rows], ref["row_token"])
+    assert np.all(rtok[rows:R] == -1)
+    rex = out["row_expert"].cpu().numpy()[:rows]
+    valid = ref["row_token"] >= 0
+    exp_of_row = np.repeat(np.arange(E), np.diff(ref["offsets"]))
+    assert np.array_equal(rex[valid], exp_of_row[valid]) and np.all(rex[~valid] == -1)
+    pos = ref["pos"]
+    kept = pos >= 0
+    assert np.array_equal(out["row_w"].cpu().numpy()[pos[kept]], w[kept])
+    assert np.array_equal(out["row_r"].cpu().numpy()[pos[kept]], r[np.nonzero(kept)[0]])
+    st = stats.cpu().numpy()
+    assert st[0] == rows and st[1] == ref["dropped"] and st[2] == ref["max_load"] and st[3] == 0
+    if x_perm is not None:
+        xp = synth.to_host(x_perm)[:rows]
+        want = np.where(ref["row_token"][:, None] >= 0, xb[np.maximum(ref["row_token"], 0)], 0)
+        assert np.array_equal(xp, want.astype(np.uint16))
+
+
+def test_dispatch_counts_bad_ids(dev):
+    _say("[gpu] dispatch with out-of-range ids")
+    T, k, E = 50, 2, 8
+    ids = np.tile(np.array([[0, 1]], dtype=np.int32), (T, 1))
+    ids[3, 1] = 9
+    ids[7, 0] = -2
+    R = B.rows_max(T, k, E, T, 1)
+    out = {n: torch.empty(sz, dtype=torch.int32, device=dev) for n, sz in
+           [("counts", E), ("offsets", E + 1), ("pos", (T, k)), ("row_token", R)]}
+    out["row_r"] = torch.empty(R, device=dev)
+    out["row_w"] = torch.empty(R, device=dev)
+    stats = torch.zeros(4, dtype=torch.int32, device=dev)
+    ws = torch.empty(B.dispatch_workspace_size(T, k, E), dtype=torch.uint8, device=dev)
+    B.dispatch(torch.from_numpy(ids).to(dev), torch.ones((T, k), device=dev), torch.ones(T, device=dev),
+               E, T, 1, R, out, stats=stats, ws=ws)
+    torch.cuda.synchronize()
+    pos = out["pos"].cpu().numpy()
+    assert pos[3, 1] == -1 and pos[7, 0] == -1
+    assert stats.cpu().numpy()[3] == 2
+    assert out["counts"].cpu().numpy()[:2].tolist() == [T - 1, T - 1]
+
+
+def test_topology_matches_oracle(dev):
+    _say("[gpu] BCSR topology")
+    sizes = [2048] + [1024] * 7
+    lay = O.expert_layout([(1, 2048), (7, 1024)], 8, 128)
+    tb = [5, 0, 2, 9, 1, 1, 3, 4]
+    offsets = np.concatenate([[0], np.cumsum(np.array(tb) * 128)]).astype(np.int32)
+    rows_max = int(offsets[-1]) + 3 * 128
+    ref = O.bcsr_topology(offsets, lay["size_blocks"], lay["block_offsets"], 128)
+    nnz_max = B.topology_nnz_max(rows_max, 128, sizes)
+    ro = torch.full((rows_max // 128 + 1,), -7, dtype=torch.int32, device=dev)
+    ci = torch.full((nnz_max,), -7, dtype=torch.int32, device=dev)
+    nnz = torch.zeros(1, dtype=torch.int32, device=dev)
+    t = lambda a: torch.tensor(a, dtype=torch.int32, device=dev)  # noqa: E731
+    B.build_topology(t(offsets), t(lay["size_blocks"]), t(lay["block_offsets"]), 8, 128, rows_max,
+                     ro, ci, nnz)
+    torch.cuda.synchronize()
+    n = int(nnz.item())
+    assert n == ref["nnz"]
+    rb = ref["block_rows"]
+    assert np.array_equal(ro.cpu().numpy()[:rb + 1], ref["row_offsets"])
+    assert np.all(ro.cpu().numpy()[rb + 1:] == n)
+    assert np.array_equal(ci.cpu().numpy()[:n], ref["column_indices"])
+
+
+def test_empty_batch(dev):
+    _say("[gpu] T = 0")
+    wl, inp, params, layer = _setup("mixtral_small", dev)
+    x = params["x"][:0]
+    out = layer.forward(x)
+    torch.cuda.synchronize()
+    assert out.shape == (0, wl.d)
