@@ -1,0 +1,176 @@
+"""Benchmark: forward pass of one sparse MoE FFN layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral_bf16]
+                    [--no-cpu-baseline] [--cpu-sample TOKENS]
+
+One step = one moe_layer_forward (RMSNorm statistic + router + top-k,
+capacity + dispatch, tile plans, expert GEMM 1 + 2 with their epilogues,
+combine) over one batch of T tokens already resident in HBM.  Prints ONE
+JSON line with tokens/s, the per-stage times from hipEvents recorded by the
+library on its own stream, the roofline of the dominant kernel (the first
+expert GEMM) and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer fwd tokens/s + expert-GEMM TFLOP/s (% bf16 MFMA peak), 1 MI355X"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA bf16 / fp32 vector
+PEAK_HBM_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mixtral_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=512,
+                    help="tokens whose expert FFNs the CPU oracle computes")
+    return ap.parse_args()
+
+
+def flops_gemm1(wl, kept):
+    mult = 2 if wl.act == "swiglu" else 1
+    return sum(2.0 * wl.d * f * mult * m for f, m in zip(wl.sizes, kept))
+
+
+def flops_gemm2(wl, kept):
+    return sum(2.0 * wl.d * f * m for f, m in zip(wl.sizes, kept))
+
+
+def cpu_baseline(wl, params, sample_tokens):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle as O
+    from sparse_mixture_experts_rmsnorm_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    host = {k: synth.to_host(v) for k, v in params.items()}
+    p = dict(k=wl.k, eps=wl.eps, renorm=wl.renorm, cf=wl.cf, act=wl.act, residual=True,
+             gamma=host.get("gamma"), pad=wl.pad)
+    if wl.router == "cartesian":
+        p.update(router="cartesian", k_rows=host["k_rows"], k_cols=host["k_cols"], W=host["W"],
+                 V=host["V"])
+    else:
+        p.update(w_router=host["w_router"], bias=host.get("bias"), w1=host["w1"],
+                 w3=host.get("w3"), w2=host["w2"], f_offsets=wl.f_offsets)
+    if wl.shared_ffn:
+        p.update(ws1=host["ws1"], ws3=host.get("ws3"), ws2=host["ws2"], shared_act=wl.shared_act)
+    rng = np.random.default_rng(0)
+    tok = np.sort(rng.choice(wl.T, size=min(sample_tokens, wl.T), replace=False))
+    t0 = time.perf_counter()
+    O.layer_forward(p, host["x"], tokens=tok)
+    dt = time.perf_counter() - t0
+    return {"value": len(tok) / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "seconds": dt,
+            "sample": (f"{len(tok)} of {wl.T} tokens through the float64 oracle "
+                       f"(routing, capacity and dispatch over all {wl.T} tokens; expert FFNs, "
+                       f"shared FFN and combine for the sample; weights widened to float64 "
+                       f"inside the timed call)")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the MoE layer here runs on a single MI355X "
+              f"(--gpus {args.gpus} is not supported; how the layer would shard is described "
+              f"in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from sparse_mixture_experts_rmsnorm_amd import binding as B, synth
+    from sparse_mixture_experts_rmsnorm_amd.layer import MoELayer
+    from sparse_mixture_experts_rmsnorm_amd.workloads import WORKLOADS
+
+    B.lib()
+    wl = WORKLOADS[args.workload]
+    dev = "cuda"
+    torch.manual_seed(0)
+    params = synth.make_torch(wl, dev)
+    layer = MoELayer(wl, params, dev)
+    x = params["x"]
+    ws = layer.alloc_workspace(wl.T)
+    out = torch.empty_like(x)
+    stats = torch.zeros(4, dtype=torch.int32, device=dev)
+    for _ in range(args.warmup):
+        layer.forward(x, out=out, ws=ws, stats=stats)
+    torch.cuda.synchronize()
+
+    timer = B.StageTimer(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        layer.forward(x, out=out, ws=ws, stats=stats, timer=timer)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    stages = {}
+    for s in B.STAGES:
+        tot, n = timer.stage_ms(s)
+        stages[s] = tot / max(n, 1)
+    timer.close()
+
+    st = stats.cpu().numpy().tolist()
+    rt = layer.routing(wl.T, ws)
+    counts = rt["counts"].cpu().numpy()
+    offsets = rt["offsets"].cpu().numpy()
+    tokens_per_s = wl.T / (ms_per_step / 1e3)
+    dtype = "bf16" if wl.dtype == "bf16" else "f32"
+
+    result = {
+        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "data": "synthetic: seeded x ~ N(0,1), weights ~ N(0, 0.02^2), device generator",
+        "config": {"workload": wl.name, "tokens": wl.T, "d_model": wl.d, "experts": wl.E,
+                   "top_k": wl.k, "d_ffn": wl.sizes[0] if wl.sizes else 1, "act": wl.act,
+                   "capacity_factor": wl.cf, "expert_kind": wl.expert_kind,
+                   "router": wl.router, "shared_ffn": wl.shared_ffn},
+        "stages_ms": stages,
+        "routing": {"rows": st[0], "dropped": st[1], "max_load": st[2], "errors": st[3]},
+    }
+    if wl.expert_kind != "atomic":
+        pad = wl.pad
+        kept = [int(offsets[e + 1] - offsets[e]) for e in range(wl.E)]
+        if pad > 1:   # algorithmic work excludes the padding rows
+            kept = [int(min(c, offsets[e + 1] - offsets[e])) for e, c in enumerate(counts)]
+        f1, f2 = flops_gemm1(wl, kept), flops_gemm2(wl, kept)
+        g1, g2 = stages["gemm1"], stages["gemm2"]
+        a1 = f1 / (g1 * 1e-3) / 1e12
+        result["expert_gemm"] = {
+            "tflop": (f1 + f2) / 1e12, "ms": g1 + g2,
+            "tflops": (f1 + f2) / ((g1 + g2) * 1e-3) / 1e12,
+            "frac_peak": (f1 + f2) / ((g1 + g2) * 1e-3) / 1e12 / PEAK_TFLOPS[dtype],
+            "gemm1_tflops": a1, "gemm2_tflops": f2 / (g2 * 1e-3) / 1e12}
+        result["roofline"] = {"bound": "mfma", "achieved": a1, "peak": PEAK_TFLOPS[dtype],
+                              "unit": "TFLOP/s", "frac": a1 / PEAK_TFLOPS[dtype],
+                              "traffic": None, "kernel": "k_gemm_bf16 (first expert linear)",
+                              "algorithmic_flop_per_launch": f1}
+        es = 2 if dtype == "bf16" else 4
+        rows = int(offsets[-1])
+        # dispatch: read every token row once, write every permuted row once
+        disp_bytes = (wl.T + rows) * wl.d * es
+        comb_bytes = (rows + 2 * wl.T) * wl.d * es
+        result["memory_bound"] = {
+            "dispatch_GBps": disp_bytes / (stages["dispatch"] * 1e-3) / 1e9,
+            "combine_GBps": comb_bytes / (stages["combine"] * 1e-3) / 1e9,
+            "peak_GBps": PEAK_HBM_GBPS}
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, params, args.cpu_sample)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()
