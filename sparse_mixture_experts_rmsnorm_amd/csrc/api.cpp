@@ -112,7 +112,7 @@ int check_experts(const moe_experts_desc* X, int dtype, int64_t d, ExpertGeo* g)
     REQUIRE(d % 256 == 0 && d > 0, MOE_ESHAPE, "bf16 experts need d %% 256 == 0 (got %lld)", (long long)d);
     geo.bf1 = 256;
     geo.bf2 = 256;
-    geo.bt = 128;
+    geo.bt = geo.bcsr ? 128 : 256;
   }
   geo.fold = geo.pf;
   for (int64_t e = 0; e < X->E; ++e) {
@@ -359,7 +359,7 @@ size_t moe_router_workspace_size(const moe_router_desc* R, int64_t T) {
   if (R->kind == MOE_ROUTER_CARTESIAN) {
     Carve c(nullptr);
     c.take(size_t(T) * (R->Nr + R->Nc) * sizeof(float));   // scores
-    c.take_n<Tile>(std::max<int64_t>(1, ((T + 127) / 128) * ((R->Nr + R->Nc) / 256)));
+    c.take_n<Tile>(std::max<int64_t>(1, ((T + 255) / 256) * ((R->Nr + R->Nc) / 256)));
     c.take_n<int>(1);
     return c.used;
   }
@@ -405,7 +405,7 @@ int router_run(const moe_router_desc* R, const void* x, int dtype, int64_t T, in
   Carve c(ws);
   float* scores = logits ? logits : c.take_n<float>(T * (R->Nr + R->Nc));
   if (logits) c.take_n<float>(T * (R->Nr + R->Nc));
-  const int64_t ntile_max = std::max<int64_t>(1, ((T + 127) / 128) * ((R->Nr + R->Nc) / 256));
+  const int64_t ntile_max = std::max<int64_t>(1, ((T + 255) / 256) * ((R->Nr + R->Nc) / 256));
   Tile* tiles = c.take_n<Tile>(ntile_max);
   int* nt = c.take_n<int>(1);
   const float* r = r_in;
@@ -420,7 +420,7 @@ int router_run(const moe_router_desc* R, const void* x, int dtype, int64_t T, in
     p.dense_n = int(R->Nr + R->Nc);
     p.gemm = 1;
     p.d = int(d);
-    p.bt = 128;
+    p.bt = 256;
     p.bf = 256;
     p.fold = 1;
     p.tiles = tiles;
@@ -438,7 +438,7 @@ int router_run(const moe_router_desc* R, const void* x, int dtype, int64_t T, in
     a.ldy = R->Nr + R->Nc;
     a.row_r = r;
     a.epi = EPI_SCALE_F32;
-    MOE_HIP(launch_gemm(dtype, a, 256, 128, int(ntile_max), stream));
+    MOE_HIP(launch_gemm(dtype, a, 256, 256, int(ntile_max), stream));
   }
   MOE_HIP(launch_cartesian_topk(scores, T, R->Nr, R->Nc, k, renorm, ids, w, stream));
   return MOE_OK;

@@ -20,14 +20,18 @@
 // of a token-block row (SDD), second linear = one tile per token-block row
 // and output slice, with K over that row's nonzero blocks (DSD).
 //
-// Tiling for gfx950: 256 threads = 4 wave64s in a 2 x 2 grid; operands are
-// both K-contiguous (weights packed as [features, K]), staged through
-// double-buffered LDS with a 16-byte-chunk XOR swizzle, and fed to
-// v_mfma_f32_32x32x16_bf16 with the weights as the A operand (features =
-// MFMA rows) and tokens as B (MFMA columns), so a lane's accumulators hold
-// four consecutive features of one token -- the epilogue stores 8 bytes
-// per group.  Tiles are remapped so that each XCD (workgroup id mod 8) runs
-// a contiguous run of the list, which shares weight tiles in its own L2.
+// Tiling for gfx950: a 256 x 256 output tile per workgroup of 8 wave64s (a
+// 4 x 2 grid of 64 x 128 wave tiles; 128-row BCSR blocks use 4 waves).
+// Operands are both K-contiguous (weights packed as [features, K]) and move
+// global -> LDS by the global_load_lds_dwordx4 DMA into a double-buffered
+// ring with a 16-byte-chunk XOR swizzle (conflict-free for the 64-bank LDS),
+// so no registers are spent on staging.  v_mfma_f32_32x32x16_bf16 takes the
+// weights as the A operand (features = MFMA rows) and tokens as B (MFMA
+// columns), so a lane's accumulators hold four consecutive features of one
+// token and the epilogue stores 8 bytes per group.  Fragments of the next
+// K sub-step are read from LDS while the current MFMAs run.  Tiles are
+// remapped so that each XCD (workgroup id mod 8) runs a contiguous run of
+// the list: the row tiles that share a weight tile run together in one L2.
 #include <algorithm>
 
 #include "common.h"
@@ -36,7 +40,6 @@
 namespace moe {
 namespace {
 
-constexpr int BK = 64;
 
 __device__ __forceinline__ int remap_xcd(int b, int nt) {
   const int xcd = b & 7, slot = b >> 3;
@@ -48,107 +51,22 @@ __device__ __forceinline__ float apply_act(float z, int act) {
   return act == 1 ? gelu_tanh(z) : gelu_erf(z);
 }
 
-// ---------------------------------------------------------------- bf16 MFMA GEMM
-
-template <int BF, int BT, int EPI>
-__global__ void __launch_bounds__(256) k_gemm_bf16(GemmArgs a) {
-  constexpr int MF = BF / 64;           // 32-row feature blocks per wave
-  constexpr int MT = BT / 64;           // 32-col token blocks per wave
-  constexpr int WCH = BF / 32;          // 16-byte W chunks per thread per K step
-  constexpr int XCH = BT / 32;
-  constexpr int LW = BF * BK, LX = BT * BK;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (LW + LX)];
-
-  const int nt = *a.ntiles;
-  if (int(blockIdx.x) >= nt) return;
-  const Tile tile = a.tiles[remap_xcd(blockIdx.x, nt)];
-
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wf = wid >> 1, wt = wid & 1;
-  const uint16_t* __restrict__ X = static_cast<const uint16_t*>(a.X);
-  const uint16_t* __restrict__ W = static_cast<const uint16_t*>(a.W);
-
-  // global -> LDS mapping: chunk (row = tid/8 + 32 i, q = tid % 8)
-  const int lq = tid & 7;
-  const int lrow = tid >> 3;
-  const int lswz = (lq ^ (lrow & 7)) * 8;
-  const uint16_t* wsrc = W + int64_t(tile.wrow0 + lrow) * a.ldw + tile.kofs + lq * 8;
-  const int64_t wstep = int64_t(32) * a.ldw;
-  // X rows past the tile end are clamped to its last row (their results are
-  // never stored; every output column depends only on its own X row)
-  const uint16_t* xsrc = X + lq * 8;
-  const int xlast = tile.row_end - 1;
-  const int xr0 = tile.row0 + lrow;
-  u32x4 wreg[WCH], xreg[XCH];
-  f32x16 acc[MF][MT];
-#pragma unroll
-  for (int i = 0; i < MF; ++i)
-#pragma unroll
-    for (int j = 0; j < MT; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-  // fragment addressing: row = base + (lane & 31), chunk q = 2 ks + (lane >> 5)
-  const int fr = lane & 31, fh = lane >> 5, fswz = lane & 7;
-  const int nk = tile.klen / BK;
-#define MOE_GLOAD(KT)                                                                     \
-  {                                                                                       \
-    const int ko_ = (KT) * BK;                                                            \
-    _Pragma("unroll") for (int i = 0; i < WCH; ++i)                                       \
-      wreg[i] = *reinterpret_cast<const u32x4*>(wsrc + i * wstep + ko_);                  \
-    _Pragma("unroll") for (int i = 0; i < XCH; ++i)                                       \
-      xreg[i] = *reinterpret_cast<const u32x4*>(                                          \
-          xsrc + int64_t(min(xr0 + 32 * i, xlast)) * a.ldx + ko_);                        \
-  }
-#define MOE_LSTORE(BUF)                                                                   \
-  {                                                                                       \
-    uint16_t* sw_ = lds + (BUF) * (LW + LX);                                              \
-    uint16_t* sx_ = sw_ + LW;                                                             \
-    _Pragma("unroll") for (int i = 0; i < WCH; ++i)                                       \
-      *reinterpret_cast<u32x4*>(sw_ + (lrow + 32 * i) * BK + lswz) = wreg[i];             \
-    _Pragma("unroll") for (int i = 0; i < XCH; ++i)                                       \
-      *reinterpret_cast<u32x4*>(sx_ + (lrow + 32 * i) * BK + lswz) = xreg[i];             \
-  }
-  MOE_GLOAD(0)
-  MOE_LSTORE(0)
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) MOE_GLOAD(kt + 1)
-    const uint16_t* sw = lds + (kt & 1) * (LW + LX);
-    const uint16_t* sx = sw + LW;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int qo = ((2 * ks + fh) ^ fswz) * 8;
-      bf16x8 af[MF], bfr[MT];
-#pragma unroll
-      for (int i = 0; i < MF; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(sw + (wf * (BF / 2) + i * 32 + fr) * BK + qo);
-#pragma unroll
-      for (int j = 0; j < MT; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(sx + (wt * (BT / 2) + j * 32 + fr) * BK + qo);
-#pragma unroll
-      for (int i = 0; i < MF; ++i)
-#pragma unroll
-        for (int j = 0; j < MT; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) MOE_LSTORE((kt + 1) & 1)
-    __syncthreads();
-  }
-#undef MOE_GLOAD
-#undef MOE_LSTORE
-
-  // epilogue: lane holds token column (lane & 31) of each 32x32 block and
-  // features 8 g + 4 (lane >> 5) + {0..3} for g = 0..3.
+// Epilogue shared by the GEMM kernels: lane holds token column (lane & 31) of
+// each 32x32 block and features 8 g + 4 (lane >> 5) + {0..3} for g = 0..3.
+template <int BF, int BT, int WGF, int WGT, int EPI, int MF, int MT>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const Tile& tile,
+                                              f32x16 (&acc)[MF][MT], int wf, int wt, int fr,
+                                              int fh) {
+  constexpr int WTF = BF / WGF, WTT = BT / WGT;
 #pragma unroll
   for (int j = 0; j < MT; ++j) {
-    const int row = tile.row0 + wt * (BT / 2) + j * 32 + fr;
+    const int row = tile.row0 + wt * WTT + j * 32 + fr;
     if (row >= tile.row_end) continue;
     float rs = 1.f;
     if (EPI == EPI_ACT || EPI == EPI_SWIGLU || EPI == EPI_SCALE_F32) rs = a.row_r[row];
     if (EPI == EPI_GATE) rs = a.row_w ? a.row_w[row] : 1.f;
     if (EPI == EPI_SWIGLU) {
-      uint16_t* Y = static_cast<uint16_t*>(a.Y) + int64_t(row) * a.ldy + tile.ocol0 + wf * (BF / 4);
+      uint16_t* Y = static_cast<uint16_t*>(a.Y) + int64_t(row) * a.ldy + tile.ocol0 + wf * (WTF / 2);
 #pragma unroll
       for (int p = 0; p < MF / 2; ++p)
 #pragma unroll
@@ -169,7 +87,7 @@ __global__ void __launch_bounds__(256) k_gemm_bf16(GemmArgs a) {
           *reinterpret_cast<uint2*>(Y + p * 32 + g * 8 + fh * 4) = make_uint2(pk[0], pk[1]);
         }
     } else if (EPI == EPI_SCALE_F32) {
-      float* Y = static_cast<float*>(a.Y) + int64_t(row) * a.ldy + tile.ocol0 + wf * (BF / 2);
+      float* Y = static_cast<float*>(a.Y) + int64_t(row) * a.ldy + tile.ocol0 + wf * WTF;
 #pragma unroll
       for (int i = 0; i < MF; ++i)
 #pragma unroll
@@ -182,7 +100,7 @@ __global__ void __launch_bounds__(256) k_gemm_bf16(GemmArgs a) {
           *reinterpret_cast<float4*>(Y + i * 32 + g * 8 + fh * 4) = o;
         }
     } else {
-      uint16_t* Y = static_cast<uint16_t*>(a.Y) + int64_t(row) * a.ldy + tile.ocol0 + wf * (BF / 2);
+      uint16_t* Y = static_cast<uint16_t*>(a.Y) + int64_t(row) * a.ldy + tile.ocol0 + wf * WTF;
 #pragma unroll
       for (int i = 0; i < MF; ++i)
 #pragma unroll
@@ -202,6 +120,141 @@ __global__ void __launch_bounds__(256) k_gemm_bf16(GemmArgs a) {
         }
     }
   }
+}
+
+// ---------------------------------------------------------------- bf16 MFMA GEMM, LDS-DMA ring
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(1))) const void* global_void_ptr;
+
+// s_waitcnt vmcnt(n) with the other counters left free (gfx9 encoding).
+#define MOE_WAIT_VMCNT(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+
+// Swizzle of 16-byte chunk q in row r for C chunks per row: any 16 consecutive
+// rows read at one logical chunk land in 16 distinct 16-byte bank groups.  It
+// depends on r & 15 only, so a fragment read (rows base + lane & 31, base a
+// multiple of 32) can compute it from the lane index.
+template <int C>
+__device__ __forceinline__ int chunk_swz(int r) {
+  if constexpr (C == 8) return (r & 7) ^ ((r >> 3) & 1);
+  else return (r >> 2) & 3;
+}
+
+// BF features x BT rows per workgroup, WGF x WGT waves, each wave a
+// (BF / WGF) x (BT / WGT) sub-tile of 32 x 32 MFMA blocks.  Global -> LDS
+// moves by the global_load_lds_dwordx4 DMA (each wave instruction writes
+// 1 KB of LDS, lane i at byte 16 i) through a ring of NS LDS stages of BKD
+// columns: stages kt + 1 .. kt + NS - 1 are in flight while stage kt is
+// computed.
+template <int BF, int BT, int WGF, int WGT, int BKD, int NS, int EPI, int SCHED = 1>
+__global__ void __launch_bounds__(64 * WGF * WGT) k_gemm_bf16_dma(GemmArgs a) {
+  constexpr int NW = WGF * WGT;
+  constexpr int WTF = BF / WGF, WTT = BT / WGT;
+  constexpr int MF = WTF / 32, MT = WTT / 32;
+  constexpr int C = BKD / 8;                    // 16-byte chunks per LDS row
+  constexpr int RSEG = 64 / C;                  // rows per 1 KB DMA segment
+  constexpr int SEGW = BF / RSEG, SEGX = BT / RSEG;
+  constexpr int SPW = (SEGW + SEGX) / NW;       // DMA instructions per wave per stage
+  constexpr int LS = (BF + BT) * BKD;           // elements per stage
+  static_assert((SEGW + SEGX) % NW == 0, "segments must divide among waves");
+  static_assert(MF >= 1 && MT >= 1, "tile too small for the waves");
+  static_assert(EPI != EPI_SWIGLU || MF % 2 == 0, "SwiGLU needs gate/up block pairs per wave");
+  static_assert(BKD == 32 || BKD == 64, "BKD must be 32 or 64");
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * LS];
+
+  const int nt = *a.ntiles;
+  if (int(blockIdx.x) >= nt) return;
+  const Tile tile = a.tiles[remap_xcd(blockIdx.x, nt)];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wf = wid / WGT, wt = wid % WGT;
+  const uint16_t* __restrict__ X = static_cast<const uint16_t*>(a.X);
+  const uint16_t* __restrict__ W = static_cast<const uint16_t*>(a.W);
+
+  // this lane's source row / chunk inside each of its wave's segments
+  const int srow = lane / C;                  // row within a segment
+  const int xlast = tile.row_end - 1;
+  auto issue = [&](int kt, int stage) {
+    uint16_t* base = lds + stage * LS;
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) {
+      const int sg = wid * SPW + u;           // wave-uniform segment index
+      const uint16_t* g;
+      int row;
+      if (sg < SEGW) {
+        row = sg * RSEG + srow;
+        g = W + int64_t(tile.wrow0 + row) * a.ldw + tile.kofs;
+      } else {
+        row = (sg - SEGW) * RSEG + srow;
+        g = X + int64_t(min(tile.row0 + row, xlast)) * a.ldx;
+      }
+      const int q = (lane % C) ^ chunk_swz<C>(row);
+      __builtin_amdgcn_global_load_lds((global_void_ptr)(g + kt * BKD + q * 8),
+                                       (lds_void_ptr)(base + sg * 512), 16, 0, 0);
+    }
+  };
+
+  f32x16 acc[MF][MT];
+#pragma unroll
+  for (int i = 0; i < MF; ++i)
+#pragma unroll
+    for (int j = 0; j < MT; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  const int fr = lane & 31, fh = lane >> 5, fswz = chunk_swz<C>(lane & 15);
+  const int nk = tile.klen / BKD;
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) issue(s, s);
+  for (int kt = 0; kt < nk; ++kt) {
+    // stage kt is complete once at most (NS - 2) later stages are pending
+    if (kt + NS - 2 < nk) MOE_WAIT_VMCNT((NS - 2) * SPW);
+    else MOE_WAIT_VMCNT(0);
+    // Workgroup barrier without the memory fence of __syncthreads (which would
+    // drain every in-flight stage): each wave has waited for its own part of
+    // stage kt above, so after the barrier all of stage kt is in LDS, and every
+    // wave's reads of stage kt - 1 (consumed by its MFMAs) are done, so that
+    // buffer may be refilled.  The empty asm statements keep the compiler
+    // from moving LDS accesses across the barrier.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
+    const uint16_t* sw = lds + (kt % NS) * LS;
+    const uint16_t* sx = sw + BF * BKD;
+    // fragments of sub-step ks + 1 are read while the MFMAs of ks run
+    constexpr int KS = BKD / 16;
+    bf16x8 af[2][MF], bfr[2][MT];
+#define MOE_FRAGS(KSV, SLOT)                                                                 \
+    {                                                                                        \
+      const int qo_ = ((2 * (KSV) + fh) ^ fswz) * 8;                                         \
+      _Pragma("unroll") for (int i = 0; i < MF; ++i)                                         \
+        af[SLOT][i] = *reinterpret_cast<const bf16x8*>(sw + (wf * WTF + i * 32 + fr) * BKD + qo_); \
+      _Pragma("unroll") for (int j = 0; j < MT; ++j)                                         \
+        bfr[SLOT][j] = *reinterpret_cast<const bf16x8*>(sx + (wt * WTT + j * 32 + fr) * BKD + qo_); \
+    }
+    MOE_FRAGS(0, 0)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) MOE_FRAGS(ks + 1, (ks + 1) & 1)
+#pragma unroll
+      for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int j = 0; j < MT; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j],
+                                                              acc[i][j], 0, 0, 0);
+      if (SCHED == 1 && ks + 1 < KS) {
+        // keep the next sub-step's LDS reads ahead of this sub-step's MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, MF + MT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, MF * MT, 0);
+      }
+      if (SCHED == 2) __builtin_amdgcn_iglp_opt(0);
+      if (SCHED == 3) __builtin_amdgcn_iglp_opt(1);
+    }
+#undef MOE_FRAGS
+  }
+  gemm_epilogue<BF, BT, WGF, WGT, EPI>(a, tile, acc, wf, wt, fr, fh);
 }
 
 // ---------------------------------------------------------------- fp32 SIMT GEMM
@@ -470,7 +523,7 @@ __global__ void __launch_bounds__(256) k_pack_swiglu(const T* __restrict__ w1,
 }  // namespace
 
 int gemm_tile_bf(int dtype) { return dtype == 0 ? 64 : 256; }
-int gemm_tile_bt(int dtype, int) { return dtype == 0 ? 64 : 128; }
+int gemm_tile_bt(int dtype, int bcsr) { return dtype == 0 ? 64 : (bcsr ? 128 : 256); }
 
 hipError_t launch_plan(const PlanArgs& p, hipStream_t s) {
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, p);
@@ -489,18 +542,23 @@ hipError_t launch_gemm(int dtype, const GemmArgs& a, int bf, int bt, int grid, h
     }
     return hipGetLastError();
   }
-  if (bf != 256 || bt != 128) return hipErrorInvalidValue;
-#define MOE_GEMM_CASE(BTV)                                                                   \
-  switch (a.epi) {                                                                           \
-    case EPI_ACT: hipLaunchKernelGGL((k_gemm_bf16<256, BTV, EPI_ACT>), g, b, 0, s, a); break; \
-    case EPI_SWIGLU:                                                                         \
-      hipLaunchKernelGGL((k_gemm_bf16<256, BTV, EPI_SWIGLU>), g, b, 0, s, a);                \
-      break;                                                                                 \
-    case EPI_GATE: hipLaunchKernelGGL((k_gemm_bf16<256, BTV, EPI_GATE>), g, b, 0, s, a); break; \
-    default: hipLaunchKernelGGL((k_gemm_bf16<256, BTV, EPI_SCALE_F32>), g, b, 0, s, a); break; \
+  if (bf != 256 || (bt != 256 && bt != 128)) return hipErrorInvalidValue;
+  if (bt == 256) {
+    const dim3 b8(512);
+    switch (a.epi) {
+      case EPI_ACT: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_ACT>), g, b8, 0, s, a); break;
+      case EPI_SWIGLU: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_SWIGLU>), g, b8, 0, s, a); break;
+      case EPI_GATE: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_GATE>), g, b8, 0, s, a); break;
+      default: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_SCALE_F32>), g, b8, 0, s, a); break;
+    }
+  } else {
+    switch (a.epi) {
+      case EPI_ACT: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 128, 2, 2, 64, 2, EPI_ACT>), g, b, 0, s, a); break;
+      case EPI_SWIGLU: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 128, 2, 2, 64, 2, EPI_SWIGLU>), g, b, 0, s, a); break;
+      case EPI_GATE: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 128, 2, 2, 64, 2, EPI_GATE>), g, b, 0, s, a); break;
+      default: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 128, 2, 2, 64, 2, EPI_SCALE_F32>), g, b, 0, s, a); break;
+    }
   }
-  MOE_GEMM_CASE(128)
-#undef MOE_GEMM_CASE
   return hipGetLastError();
 }
 
