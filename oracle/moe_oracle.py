@@ -385,15 +385,17 @@ def grouped_expert_ffn(xhat_rows, r_rows, e_of_row, w1, w2, f_offsets, act,
 
     w1, w3 are [d, sum f] and w2 is [sum f, d]; expert e owns columns
     f_offsets[e]:f_offsets[e+1] of w1/w3 and the same rows of w2 ([VAREXP]
-    sec. 2, weight allocation).
+    sec. 2, weight allocation).  Weights may be bf16 bit patterns; only the
+    slices of experts that have rows are widened to float64.
     """
-    d = w2.shape[1]
+    d = np.asarray(w2).shape[1]
     out = np.zeros((len(e_of_row), d), dtype=np.float64)
     for e in np.unique(e_of_row):
         m = e_of_row == e
         lo, hi = int(f_offsets[e]), int(f_offsets[e + 1])
-        out[m] = ffn(xhat_rows[m], r_rows[m], w1[:, lo:hi], w2[lo:hi, :], act,
-                     None if w3 is None else w3[:, lo:hi], faithful)
+        out[m] = ffn(xhat_rows[m], r_rows[m], as_f64(np.asarray(w1)[:, lo:hi]),
+                     as_f64(np.asarray(w2)[lo:hi, :]), act,
+                     None if w3 is None else as_f64(np.asarray(w3)[:, lo:hi]), faithful)
     return out
 
 
@@ -495,18 +497,18 @@ def atomic_experts_token_centric(xhat, r, ids, g, W, V, act="gelu"):
 
     For token t, its k atomic experts' rows W[n], V[n] are gathered into a
     token-specific block; routed[t] = sum_j g[t,j] * act(r_t * xhat_t.W[n_j]) * V[n_j].
+    Only the gathered rows are widened to float64.
     """
     xhat = np.asarray(xhat, dtype=np.float64)
     r = np.asarray(r, dtype=np.float64)
-    W = as_f64(W) if not (isinstance(W, np.ndarray) and W.dtype == np.float64) else W
-    V = as_f64(V) if not (isinstance(V, np.ndarray) and V.dtype == np.float64) else V
     T = xhat.shape[0]
-    out = np.zeros((T, V.shape[1]), dtype=np.float64)
+    out = np.zeros((T, np.asarray(V).shape[1]), dtype=np.float64)
     f = _act(act)
     for t in range(T):
-        Wt = W[ids[t]]                       # [k, d] assembled block
+        Wt = as_f64(np.asarray(W)[ids[t]])      # [k, d] assembled block
+        Vt = as_f64(np.asarray(V)[ids[t]])
         a = np.asarray(g[t], dtype=np.float64) * f(r[t] * (Wt @ xhat[t]))
-        out[t] = a @ V[ids[t]]
+        out[t] = a @ Vt
     return out
 
 
@@ -631,9 +633,7 @@ def layer_forward(p: dict, x, ids_override=None, tokens=None, faithful=False) ->
     disp = dispatch(ids, E, cap, int(p.get("pad", 1)))
     res.update(logits=logits, ids=ids.astype(np.int32), w=g, capacity=cap, **disp)
 
-    w1 = as_f64(p["w1"])
-    w2 = as_f64(p["w2"])
-    w3 = as_f64(p.get("w3"))
+    w1, w2, w3 = p["w1"], p["w2"], p.get("w3")
     foff = np.asarray(p["f_offsets"], dtype=np.int64)
     act = p["act"]
     pos = disp["pos"][tok]

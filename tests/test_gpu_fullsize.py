@@ -1,0 +1,107 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (same workload shapes, device-generated inputs, one
+moe_layer_forward over all tokens).
+
+Integer results are checked over every token: the top-k decision against
+the GPU's own logits / scores, and the whole dispatch (counts, offsets,
+positions, dropped set, row order) against the oracle on the same ids.
+Floating-point outputs are checked on a sample of tokens the oracle computes
+one by one, within max|gpu-ref|/max|ref| <= 2e-2 (bf16).
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from gpu_cases import TOL, f64, oracle_params, rel_err
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from sparse_mixture_experts_rmsnorm_amd import binding as B  # noqa: E402
+from sparse_mixture_experts_rmsnorm_amd import synth  # noqa: E402
+from sparse_mixture_experts_rmsnorm_amd.layer import MoELayer  # noqa: E402
+from sparse_mixture_experts_rmsnorm_amd.workloads import WORKLOADS  # noqa: E402
+
+SAMPLE = 24
+
+
+@pytest.mark.parametrize("name", ["mixtral_bf16", "variable_bcsr_bf16", "finegrained_bf16",
+                                  "atomic_bf16"])
+def test_fullsize_parity(name):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    print(f"[gpu] full-size parity {name}", flush=True)
+    B.lib()
+    wl = WORKLOADS[name]
+    dev = "cuda"
+    params = synth.make_torch(wl, dev)
+    layer = MoELayer(wl, params, dev)
+    x = params["x"]
+    ws = layer.alloc_workspace(wl.T)
+    stats = torch.zeros(4, dtype=torch.int32, device=dev)
+    out = layer.forward(x, ws=ws, stats=stats)
+    torch.cuda.synchronize()
+    rt = layer.routing(wl.T, ws)
+    ids = rt["ids"].cpu().numpy()
+    r = rt["r"].cpu().numpy()
+    inp = {k: synth.to_host(v) for k, v in params.items()}
+    if wl.router == "dense":
+        del params["w1"], params["w2"]
+        params.pop("w3", None)
+    torch.cuda.empty_cache()
+
+    # RMSNorm statistic over all tokens
+    r_ref = O.rmsnorm_scale(inp["x"], wl.eps)
+    assert rel_err(r, r_ref) < 1e-5
+
+    # top-k decision on the GPU's own logits (all tokens)
+    nl = wl.E if wl.router == "dense" else wl.Nr + wl.Nc
+    logits = torch.empty((wl.T, nl), dtype=torch.float32, device=dev)
+    ids2 = torch.empty_like(rt["ids"])
+    w2 = torch.empty_like(rt["w"])
+    nws = B.router_workspace_size(layer.desc.router, wl.T)
+    rws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    B.router_topk(layer.desc.router, x, wl.k, wl.renorm, ids2, w2, r_in=rt["r"], logits=logits,
+                  ws=rws)
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy()
+    assert np.array_equal(ids2.cpu().numpy(), ids)
+    if wl.router == "dense":
+        assert np.array_equal(O.select_topk(lg, wl.k), ids)
+        l_ref = O.router_logits(inp["x"], None, r_ref, inp["w_router"], inp.get("bias"))
+        assert rel_err(lg, l_ref) < 1e-2
+        E = wl.E
+    else:
+        sel, _ = O.cartesian_topk(lg[:, :wl.Nr], lg[:, wl.Nr:], wl.k)
+        assert np.array_equal(sel, ids)
+        E = wl.Nr * wl.Nc
+    del logits, rws
+
+    # dispatch over all tokens: bit-exact
+    cap = O.capacity(wl.T, wl.k, E, wl.cf)
+    disp = O.dispatch(ids, E, cap, wl.pad)
+    assert np.array_equal(rt["counts"].cpu().numpy(), disp["counts"])
+    assert np.array_equal(rt["offsets"].cpu().numpy(), disp["offsets"])
+    pos = rt["pos"].cpu().numpy()
+    assert np.array_equal(pos, disp["pos"])
+    assert np.array_equal(rt["row_token"].cpu().numpy()[:disp["rows"]], disp["row_token"])
+    st = stats.cpu().numpy()
+    assert st[0] == disp["rows"] and st[1] == disp["dropped"] and st[3] == 0
+
+    # sampled outputs against the oracle on the GPU's routing
+    rng = np.random.default_rng(wl.seed)
+    tok = np.sort(rng.choice(wl.T, size=SAMPLE, replace=False))
+    gone = np.nonzero(np.all(pos < 0, axis=1))[0]
+    if len(gone) and not wl.shared_ffn:
+        tok = np.unique(np.concatenate([tok, gone[:4]]))   # include dropped tokens
+    p = oracle_params(wl, inp)
+    ref = O.layer_forward(p, inp["x"], ids_override=ids, tokens=tok)
+    got = f64(synth.to_host(out))[tok]
+    err = rel_err(got, ref["out"])
+    print(f"  {name}: sampled rel err {err:.2e} over {len(tok)} tokens, "
+          f"dropped {disp['dropped']}, rows {disp['rows']}", flush=True)
+    assert err <= TOL["bf16"]
+    if len(gone) and not wl.shared_ffn:
+        xb = synth.to_host(x)
+        g = np.intersect1d(tok, gone)
+        assert np.array_equal(synth.to_host(out)[g], xb[g])
