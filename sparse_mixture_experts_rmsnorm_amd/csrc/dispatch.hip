@@ -290,19 +290,55 @@ __global__ void __launch_bounds__(kThreads) k_radix_count(const int32_t* __restr
   for (int b = threadIdx.x; b < nb; b += kThreads) cc[int64_t(b) * nch + c] = hist[b];
 }
 
-// Exclusive scan of n ints in place with one block of 1024 threads.
-__global__ void __launch_bounds__(1024) k_scan_inplace(int32_t* __restrict__ v, int64_t n) {
+// Exclusive scan of n ints in place: block partial sums, a scan of the block
+// sums, then each block scans its run and adds its prefix.
+constexpr int kScanPerThread = 16;
+constexpr int kScanBlock = 256 * kScanPerThread;
+
+__global__ void __launch_bounds__(256) k_scan_partial(const int32_t* __restrict__ v, int64_t n,
+                                                      int32_t* __restrict__ part) {
   __shared__ long long sh[33];
-  const int64_t per = (n + blockDim.x - 1) / blockDim.x;
-  const int64_t lo = min<int64_t>(n, threadIdx.x * per), hi = min<int64_t>(n, lo + per);
+  const int64_t lo = int64_t(blockIdx.x) * kScanBlock + threadIdx.x * kScanPerThread;
   long long local = 0;
-  for (int64_t i = lo; i < hi; ++i) local += v[i];
+  for (int i = 0; i < kScanPerThread; ++i)
+    if (lo + i < n) local += v[lo + i];
+  long long total;
+  block_exscan(local, &total, sh);
+  if (threadIdx.x == 0) part[blockIdx.x] = int(total);
+}
+
+__global__ void __launch_bounds__(1024) k_scan_top(int32_t* __restrict__ part, int nb) {
+  __shared__ long long sh[33];
+  const int per = (nb + blockDim.x - 1) / blockDim.x;
+  const int lo = min(nb, int(threadIdx.x) * per), hi = min(nb, lo + per);
+  long long local = 0;
+  for (int i = lo; i < hi; ++i) local += part[i];
   long long total;
   long long base = block_exscan(local, &total, sh);
-  for (int64_t i = lo; i < hi; ++i) {
-    const int x = v[i];
-    v[i] = int(base);
+  for (int i = lo; i < hi; ++i) {
+    const int x = part[i];
+    part[i] = int(base);
     base += x;
+  }
+}
+
+__global__ void __launch_bounds__(256) k_scan_final(int32_t* __restrict__ v, int64_t n,
+                                                    const int32_t* __restrict__ part) {
+  __shared__ long long sh[33];
+  const int64_t lo = int64_t(blockIdx.x) * kScanBlock + threadIdx.x * kScanPerThread;
+  int x[kScanPerThread];
+  long long local = 0;
+#pragma unroll
+  for (int i = 0; i < kScanPerThread; ++i) {
+    x[i] = lo + i < n ? v[lo + i] : 0;
+    local += x[i];
+  }
+  long long total;
+  long long base = block_exscan(local, &total, sh) + part[blockIdx.x];
+#pragma unroll
+  for (int i = 0; i < kScanPerThread; ++i) {
+    if (lo + i < n) v[lo + i] = int(base);
+    base += x[i];
   }
 }
 
@@ -360,32 +396,39 @@ __global__ void __launch_bounds__(kThreads) k_radix_scatter(
   }
 }
 
-__device__ __forceinline__ int lower_bound(const int32_t* __restrict__ a, int n, int key) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (a[mid] < key) lo = mid + 1;
-    else hi = mid;
+// offsets[e] = first sorted slot with key >= e, for every e in [0, E]:
+// slot i fills the experts in (key[i-1], key[i]] (the gap before its key),
+// slot N fills the tail; every e is written exactly once.
+__global__ void k_radix_offsets(const int32_t* __restrict__ keys, int N, int E,
+                                int32_t* __restrict__ offsets) {
+  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i <= N;
+       i += int64_t(gridDim.x) * blockDim.x) {
+    const int prev = i == 0 ? -1 : min(keys[i - 1], E);
+    const int cur = i == N ? E : min(keys[i], E);
+    for (int e = prev + 1; e <= cur; ++e) offsets[e] = int(i);
   }
-  return lo;
 }
 
-// offsets[e] = first sorted slot with key >= e; counts[e] = slots of e.
-__global__ void k_radix_offsets(const int32_t* __restrict__ keys, int N, int E,
-                                int32_t* __restrict__ offsets, int32_t* __restrict__ counts,
-                                int32_t* __restrict__ stats) {
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e > E) return;
-  const int lo = lower_bound(keys, N, e);
-  offsets[e] = lo;
-  if (e < E) {
-    const int cnt = lower_bound(keys, N, e + 1) - lo;
-    counts[e] = cnt;
-    if (stats && cnt) atomicMax(&stats[2], cnt);
-  } else if (stats) {
-    stats[0] = lo;
-    stats[1] = 0;
-    stats[3] = N - lo;
+// counts[e] = offsets[e+1] - offsets[e]; statistics of the radix path.
+__global__ void k_radix_counts(const int32_t* __restrict__ offsets, int N, int E,
+                               int32_t* __restrict__ counts, int32_t* __restrict__ stats) {
+  int mx = 0;
+  for (int64_t e = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; e < E;
+       e += int64_t(gridDim.x) * blockDim.x) {
+    const int c = offsets[e + 1] - offsets[e];
+    counts[e] = c;
+    mx = max(mx, c);
+  }
+  if (stats) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o, 64));
+    if ((threadIdx.x & 63) == 0 && mx > 0) atomicMax(&stats[2], mx);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      const int rows = offsets[E];
+      stats[0] = rows;
+      stats[1] = 0;
+      stats[3] = N - rows;
+    }
   }
 }
 
@@ -415,6 +458,13 @@ __global__ void k_radix_rows(const int32_t* __restrict__ keys, const int32_t* __
   }
 }
 
+void scan_inplace(int32_t* v, int64_t n, int32_t* part, hipStream_t s) {
+  const int nb = int((n + kScanBlock - 1) / kScanBlock);
+  hipLaunchKernelGGL(k_scan_partial, dim3(nb), dim3(256), 0, s, v, n, part);
+  hipLaunchKernelGGL(k_scan_top, dim3(1), dim3(1024), 0, s, part, nb);
+  hipLaunchKernelGGL(k_scan_final, dim3(nb), dim3(256), 0, s, v, n, part);
+}
+
 int ceil_log2(int64_t v) {
   int b = 0;
   while ((int64_t(1) << b) < v) ++b;
@@ -432,7 +482,8 @@ size_t dispatch_ws_bytes(int64_t T, int k, int64_t E) {
   const int64_t nch = (N + kRadixChunk - 1) / kRadixChunk;
   const int B = ceil_log2(E + 1);
   const int b1 = (B + 1) / 2;
-  return size_t(4 * N + (int64_t(1) << b1) * nch + 64) * sizeof(int32_t);
+  const int64_t nscan = (int64_t(1) << b1) * nch;
+  return size_t(4 * N + nscan + nscan / kScanBlock + 64) * sizeof(int32_t);
 }
 
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
@@ -470,25 +521,28 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
     int32_t* keys1 = vals0 + N;
     int32_t* vals1 = keys1 + N;
     int32_t* cc = vals1 + N;
+    int32_t* part = cc + (int64_t(nch) << b1);
     if (N > 0) {
       const unsigned g = unsigned(std::min<int64_t>(4096, (N + 255) / 256));
       hipLaunchKernelGGL(k_radix_prep, dim3(g), dim3(256), 0, s, a.ids, N, E, keys1);
       // pass 1: low b1 bits, keys1 -> keys0 / vals0
       hipLaunchKernelGGL(k_radix_count, dim3(nch), dim3(kThreads), (1 << b1) * sizeof(int), s,
                          keys1, N, 0, b1, nch, cc);
-      hipLaunchKernelGGL(k_scan_inplace, dim3(1), dim3(1024), 0, s, cc, int64_t(nch) << b1);
+      scan_inplace(cc, int64_t(nch) << b1, part, s);
       hipLaunchKernelGGL(k_radix_scatter, dim3(nch), dim3(kThreads), 5 * (1 << b1) * sizeof(int),
                          s, keys1, (const int32_t*)nullptr, N, 0, b1, nch, cc, keys0, vals0);
       // pass 2: high b2 bits, keys0 -> keys1 / vals1
       hipLaunchKernelGGL(k_radix_count, dim3(nch), dim3(kThreads), (1 << b2) * sizeof(int), s,
                          keys0, N, b1, b2, nch, cc);
-      hipLaunchKernelGGL(k_scan_inplace, dim3(1), dim3(1024), 0, s, cc, int64_t(nch) << b2);
+      scan_inplace(cc, int64_t(nch) << b2, part, s);
       hipLaunchKernelGGL(k_radix_scatter, dim3(nch), dim3(kThreads), 5 * (1 << b2) * sizeof(int),
                          s, keys0, vals0, N, b1, b2, nch, cc, keys1, vals1);
     }
     if (stats) hipLaunchKernelGGL(k_zero_stat, dim3(1), dim3(64), 0, s, stats);
-    hipLaunchKernelGGL(k_radix_offsets, dim3(unsigned((E + 1 + 255) / 256)), dim3(256), 0, s,
-                       keys1, int(N), E, a.offsets, a.counts, stats);
+    hipLaunchKernelGGL(k_radix_offsets, dim3(unsigned(std::min<int64_t>(4096, (N + 1 + 255) / 256))),
+                       dim3(256), 0, s, keys1, int(N), E, a.offsets);
+    hipLaunchKernelGGL(k_radix_counts, dim3(unsigned(std::min<int64_t>(4096, (E + 255) / 256))),
+                       dim3(256), 0, s, a.offsets, int(N), E, a.counts, stats);
     if (N > 0) {
       const unsigned g = unsigned(std::min<int64_t>(4096, (N + 255) / 256));
       hipLaunchKernelGGL(k_radix_rows, dim3(g), dim3(256), 0, s, keys1, vals1, N, E, k, a.w,
