@@ -162,16 +162,50 @@ struct ExpertWs {
   int* nt = nullptr;   // [2]
   float* a_rows = nullptr;
   int64_t mt1 = 0, mt2 = 0;
+  int ksplit = 1;        // K halves of the second linear
+  float* ypart = nullptr;  // [ksplit][rows_max][d] fp32 gated partials (ksplit 2)
+  int64_t plane = 0;
 };
 
+// Compute units of the current device (cached; a host query, no sync).
+int device_cus() {
+  static thread_local int dev_cached = -1, cus = 256;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return cus;
+  if (dev != dev_cached) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus = n;
+    dev_cached = dev;
+  }
+  return cus;
+}
+
+// Second-linear K split: the tile count of a grouped layer is only known on
+// the device, so the host estimates it (T k / bt + E / 2 row tiles per output
+// slice) and splits K in two when that evens out the last round of tiles
+// across the compute units (the two fp32 partials are summed by combine).
+int choose_ksplit(const ExpertGeo& g, int dtype, int64_t d, int64_t rows_used_est) {
+  if (g.bcsr || g.atomic || dtype != MOE_BF16) return 1;
+  const double cus = device_cus();
+  const double n = (double(rows_used_est) / g.bt + 0.5 * double(g.E)) * double(d / g.bf2);
+  auto eff = [&](double t) { return t <= 0 ? 1.0 : (t / cus) / std::ceil(t / cus); };
+  return eff(2 * n) > eff(n) + 0.08 ? 2 : 1;
+}
+
 void carve_expert_ws(Carve& c, const ExpertGeo& g, int dtype, int64_t d, int64_t rows_max,
-                     int64_t nnz_max, ExpertWs* w) {
+                     int64_t nnz_max, ExpertWs* w, int ksplit = 1) {
   if (g.atomic) {
     w->a_rows = c.take_n<float>(rows_max);
     return;
   }
+  w->ksplit = ksplit;
   w->mt1 = std::max<int64_t>(1, max_tiles_gemm1(g, rows_max, nnz_max));
-  w->mt2 = std::max<int64_t>(1, max_tiles_gemm2(g, d, rows_max));
+  w->mt2 = std::max<int64_t>(1, max_tiles_gemm2(g, d, rows_max) * ksplit);
+  if (ksplit > 1) {
+    w->plane = rows_max * d;
+    w->ypart = c.take_n<float>(ksplit * w->plane);
+  }
   w->h = c.take(size_t(rows_max) * g.Fmax * esize(dtype));
   w->tiles1 = c.take_n<Tile>(w->mt1);
   w->tiles2 = c.take_n<Tile>(w->mt2);
@@ -219,6 +253,7 @@ int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, i
   p.column_indices = column_indices;
   p.block_offsets = X->block_offsets;
   p.block = 128;
+  p.ksplit = 1;
   // first linear
   p.gemm = 1;
   p.bf = g.bf1;
@@ -236,6 +271,7 @@ int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, i
   p.tiles = w.tiles2;
   p.ntiles = w.nt + 1;
   p.max_tiles = int(w.mt2);
+  p.ksplit = w.ksplit;
   MOE_HIP(launch_plan(p, s));
   timer_mark(timer, call, MOE_STAGE_PLAN + 1, s);
 
@@ -267,6 +303,11 @@ int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, i
   b.row_r = nullptr;
   b.row_w = row_w;
   b.epi = EPI_GATE;
+  if (w.ksplit > 1) {
+    b.epi = EPI_GATE_F32;
+    b.Y = w.ypart;
+    b.ysplit = w.plane;
+  }
   MOE_HIP(launch_gemm(dtype, b, g.bf2, g.bt, int(w.mt2), s));
   timer_mark(timer, call, MOE_STAGE_GEMM2 + 1, s);
   return MOE_OK;
@@ -426,6 +467,7 @@ int router_run(const moe_router_desc* R, const void* x, int dtype, int64_t T, in
     p.tiles = tiles;
     p.ntiles = nt;
     p.max_tiles = int(ntile_max);
+    p.ksplit = 1;
     MOE_HIP(launch_plan(p, stream));
     GemmArgs a{};
     a.X = x;
@@ -747,8 +789,10 @@ void carve_layer(Carve& c, const moe_layer_desc* L, int64_t T, const ExpertGeo& 
   } else {
     w->row_offsets = w->column_indices = w->nnz = nullptr;
   }
-  carve_expert_ws(c, g, L->dtype, d, w->rows_max, nnz_max, &w->ex);
-  w->y = c.take(size_t(g.atomic ? T : w->rows_max) * d * es);
+  const int64_t rows_est = std::min(T * k, E * std::min(w->cap, T));
+  const int ks = choose_ksplit(g, L->dtype, d, rows_est);
+  carve_expert_ws(c, g, L->dtype, d, w->rows_max, nnz_max, &w->ex, ks);
+  w->y = ks > 1 ? nullptr : c.take(size_t(g.atomic ? T : w->rows_max) * d * es);
   if (L->shared) {
     carve_expert_ws(c, gs, L->dtype, d, T, 0, &w->sh);
     w->s = c.take(size_t(T) * d * es);
@@ -903,8 +947,12 @@ int moe_layer_forward(const moe_layer_desc* L, const void* x, int64_t T, void* o
   timer_mark(tm, call, MOE_STAGE_SHARED + 1, stream);
 
   // 5. combine
-  MOE_HIP(launch_combine(w.y, g.atomic ? nullptr : w.pos, L->residual ? x : nullptr, w.s, L->dtype,
-                         T, d, k, out, stream));
+  if (w.ex.ksplit > 1)
+    MOE_HIP(launch_combine_split(w.ex.ypart, w.rows_max, w.pos, L->residual ? x : nullptr, w.s,
+                                 L->dtype, T, d, k, out, stream));
+  else
+    MOE_HIP(launch_combine(w.y, g.atomic ? nullptr : w.pos, L->residual ? x : nullptr, w.s,
+                           L->dtype, T, d, k, out, stream));
   timer_mark(tm, call, MOE_STAGE_COMBINE + 1, stream);
   return ok();
 }

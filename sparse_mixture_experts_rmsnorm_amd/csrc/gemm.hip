@@ -64,7 +64,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const Tile& til
     if (row >= tile.row_end) continue;
     float rs = 1.f;
     if (EPI == EPI_ACT || EPI == EPI_SWIGLU || EPI == EPI_SCALE_F32) rs = a.row_r[row];
-    if (EPI == EPI_GATE) rs = a.row_w ? a.row_w[row] : 1.f;
+    if (EPI == EPI_GATE || EPI == EPI_GATE_F32) rs = a.row_w ? a.row_w[row] : 1.f;
     if (EPI == EPI_SWIGLU) {
       uint16_t* Y = static_cast<uint16_t*>(a.Y) + int64_t(row) * a.ldy + tile.ocol0 + wf * (WTF / 2);
 #pragma unroll
@@ -86,8 +86,9 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const Tile& til
           }
           *reinterpret_cast<uint2*>(Y + p * 32 + g * 8 + fh * 4) = make_uint2(pk[0], pk[1]);
         }
-    } else if (EPI == EPI_SCALE_F32) {
-      float* Y = static_cast<float*>(a.Y) + int64_t(row) * a.ldy + tile.ocol0 + wf * WTF;
+    } else if (EPI == EPI_SCALE_F32 || EPI == EPI_GATE_F32) {
+      float* Y = static_cast<float*>(a.Y) + int64_t(row) * a.ldy + tile.ocol0 + wf * WTF +
+                 (EPI == EPI_GATE_F32 ? int64_t(tile.spare) * a.ysplit : 0);
 #pragma unroll
       for (int i = 0; i < MF; ++i)
 #pragma unroll
@@ -147,8 +148,8 @@ __device__ __forceinline__ int chunk_swz(int r) {
 // 1 KB of LDS, lane i at byte 16 i) through a ring of NS LDS stages of BKD
 // columns: stages kt + 1 .. kt + NS - 1 are in flight while stage kt is
 // computed.
-template <int BF, int BT, int WGF, int WGT, int BKD, int NS, int EPI, int SCHED = 1>
-__global__ void __launch_bounds__(64 * WGF * WGT) k_gemm_bf16_dma(GemmArgs a) {
+template <int BF, int BT, int WGF, int WGT, int BKD, int NS, int EPI, int SCHED = 1, int MINB = 1>
+__global__ void __launch_bounds__(64 * WGF * WGT, MINB) k_gemm_bf16_dma(GemmArgs a) {
   constexpr int NW = WGF * WGT;
   constexpr int WTF = BF / WGF, WTT = BT / WGT;
   constexpr int MF = WTF / 32, MT = WTT / 32;
@@ -171,27 +172,33 @@ __global__ void __launch_bounds__(64 * WGF * WGT) k_gemm_bf16_dma(GemmArgs a) {
   const uint16_t* __restrict__ X = static_cast<const uint16_t*>(a.X);
   const uint16_t* __restrict__ W = static_cast<const uint16_t*>(a.W);
 
-  // this lane's source row / chunk inside each of its wave's segments
+  // this lane's source address inside each of its wave's segments (loop
+  // invariant; a K step only adds kt * BKD)
   const int srow = lane / C;                  // row within a segment
   const int xlast = tile.row_end - 1;
+  const uint16_t* src[SPW];
+#pragma unroll
+  for (int u = 0; u < SPW; ++u) {
+    const int sg = wid * SPW + u;             // wave-uniform segment index
+    int row;
+    const uint16_t* g;
+    if (sg < SEGW) {
+      row = sg * RSEG + srow;
+      g = W + int64_t(tile.wrow0 + row) * a.ldw + tile.kofs;
+    } else {
+      row = (sg - SEGW) * RSEG + srow;
+      // a K-split tile reads its own half of the activation row
+      const int xk0 = EPI == EPI_GATE_F32 ? tile.spare * tile.klen : 0;
+      g = X + int64_t(min(tile.row0 + row, xlast)) * a.ldx + xk0;
+    }
+    src[u] = g + ((lane % C) ^ chunk_swz<C>(row)) * 8;
+  }
   auto issue = [&](int kt, int stage) {
     uint16_t* base = lds + stage * LS;
 #pragma unroll
-    for (int u = 0; u < SPW; ++u) {
-      const int sg = wid * SPW + u;           // wave-uniform segment index
-      const uint16_t* g;
-      int row;
-      if (sg < SEGW) {
-        row = sg * RSEG + srow;
-        g = W + int64_t(tile.wrow0 + row) * a.ldw + tile.kofs;
-      } else {
-        row = (sg - SEGW) * RSEG + srow;
-        g = X + int64_t(min(tile.row0 + row, xlast)) * a.ldx;
-      }
-      const int q = (lane % C) ^ chunk_swz<C>(row);
-      __builtin_amdgcn_global_load_lds((global_void_ptr)(g + kt * BKD + q * 8),
-                                       (lds_void_ptr)(base + sg * 512), 16, 0, 0);
-    }
+    for (int u = 0; u < SPW; ++u)
+      __builtin_amdgcn_global_load_lds((global_void_ptr)(src[u] + kt * BKD),
+                                       (lds_void_ptr)(base + (wid * SPW + u) * 512), 16, 0, 0);
   };
 
   f32x16 acc[MF][MT];
@@ -326,7 +333,7 @@ __global__ void __launch_bounds__(256) k_gemm_f32(GemmArgs a) {
     if (row >= tile.row_end) continue;
     float rs = 1.f;
     if (EPI == EPI_ACT || EPI == EPI_SWIGLU || EPI == EPI_SCALE_F32) rs = a.row_r[row];
-    if (EPI == EPI_GATE) rs = a.row_w ? a.row_w[row] : 1.f;
+    if (EPI == EPI_GATE || EPI == EPI_GATE_F32) rs = a.row_w ? a.row_w[row] : 1.f;
     float* Y = static_cast<float*>(a.Y) + int64_t(row) * a.ldy + tile.ocol0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -376,7 +383,7 @@ __global__ void __launch_bounds__(1024) k_plan(PlanArgs p) {
       const int rows = p.offsets[u + 1] - p.offsets[u];
       const int mt = (rows + p.bt - 1) / p.bt;
       const int nf = p.gemm == 1 ? (p.foff[u + 1] - p.foff[u]) * pf / p.bf : p.d / p.bf;
-      cnt = mt * nf;
+      cnt = mt * nf * (p.gemm == 2 ? p.ksplit : 1);
     }
     base_s[u] = cnt;
     local += cnt;
@@ -456,8 +463,12 @@ __global__ void __launch_bounds__(1024) k_plan(PlanArgs p) {
     } else {
       const int rows = p.offsets[u + 1] - p.offsets[u];
       const int mt = (rows + p.bt - 1) / p.bt;
-      const int nf = n / mt, m = n - nf * mt;
+      const int nfe = p.gemm == 1 ? (p.foff[u + 1] - p.foff[u]) * pf / p.bf : p.d / p.bf;
+      const int sp = n / (mt * nfe);           // K split (second linear only)
+      const int nn = n - sp * mt * nfe;
+      const int nf = nn / mt, m = nn - nf * mt;
       t.expert = u;
+      t.spare = sp;
       t.row0 = p.offsets[u] + m * p.bt;
       t.row_end = min(p.offsets[u + 1], t.row0 + p.bt);
       if (p.gemm == 1) {
@@ -466,9 +477,10 @@ __global__ void __launch_bounds__(1024) k_plan(PlanArgs p) {
         t.klen = p.d;
         t.ocol0 = nf * p.bf / p.fold;
       } else {
+        const int kl = (p.foff[u + 1] - p.foff[u]) / p.ksplit;
         t.wrow0 = nf * p.bf;
-        t.kofs = p.foff[u];
-        t.klen = p.foff[u + 1] - p.foff[u];
+        t.kofs = p.foff[u] + sp * kl;
+        t.klen = kl;
         t.ocol0 = nf * p.bf;
       }
     }
@@ -538,7 +550,8 @@ hipError_t launch_gemm(int dtype, const GemmArgs& a, int bf, int bt, int grid, h
       case EPI_ACT: hipLaunchKernelGGL(k_gemm_f32<EPI_ACT>, g, b, 0, s, a); break;
       case EPI_SWIGLU: hipLaunchKernelGGL(k_gemm_f32<EPI_SWIGLU>, g, b, 0, s, a); break;
       case EPI_GATE: hipLaunchKernelGGL(k_gemm_f32<EPI_GATE>, g, b, 0, s, a); break;
-      default: hipLaunchKernelGGL(k_gemm_f32<EPI_SCALE_F32>, g, b, 0, s, a); break;
+      case EPI_SCALE_F32: hipLaunchKernelGGL(k_gemm_f32<EPI_SCALE_F32>, g, b, 0, s, a); break;
+      default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
   }
@@ -549,14 +562,16 @@ hipError_t launch_gemm(int dtype, const GemmArgs& a, int bf, int bt, int grid, h
       case EPI_ACT: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_ACT>), g, b8, 0, s, a); break;
       case EPI_SWIGLU: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_SWIGLU>), g, b8, 0, s, a); break;
       case EPI_GATE: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_GATE>), g, b8, 0, s, a); break;
-      default: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_SCALE_F32>), g, b8, 0, s, a); break;
+      case EPI_SCALE_F32: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_SCALE_F32>), g, b8, 0, s, a); break;
+      default: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_GATE_F32>), g, b8, 0, s, a); break;
     }
   } else {
     switch (a.epi) {
       case EPI_ACT: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 128, 2, 2, 64, 2, EPI_ACT>), g, b, 0, s, a); break;
       case EPI_SWIGLU: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 128, 2, 2, 64, 2, EPI_SWIGLU>), g, b, 0, s, a); break;
       case EPI_GATE: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 128, 2, 2, 64, 2, EPI_GATE>), g, b, 0, s, a); break;
-      default: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 128, 2, 2, 64, 2, EPI_SCALE_F32>), g, b, 0, s, a); break;
+      case EPI_SCALE_F32: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 128, 2, 2, 64, 2, EPI_SCALE_F32>), g, b, 0, s, a); break;
+      default: return hipErrorInvalidValue;
     }
   }
   return hipGetLastError();
