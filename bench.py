@@ -48,6 +48,35 @@ def flops_gemm2(wl, kept):
     return sum(2.0 * wl.d * f * m for f, m in zip(wl.sizes, kept))
 
 
+def time_dispatch_gather(B, wl, layer, ws, x, steps):
+    """moe_dispatch with the token-row permutation, on the layer's own routing."""
+    import torch
+    rt = layer.routing(wl.T, ws)
+    E, R = rt["counts"].numel(), rt["rows_max"]
+    dev = x.device
+    i32 = torch.int32
+    out = dict(counts=torch.empty(E, dtype=i32, device=dev),
+               offsets=torch.empty(E + 1, dtype=i32, device=dev),
+               pos=torch.empty((wl.T, wl.k), dtype=i32, device=dev),
+               row_token=torch.empty(R, dtype=i32, device=dev),
+               row_r=torch.empty(R, device=dev), row_w=torch.empty(R, device=dev),
+               row_expert=torch.empty(R, dtype=i32, device=dev))
+    x_perm = torch.empty((R, wl.d), dtype=x.dtype, device=dev)
+    dws = torch.empty(B.dispatch_workspace_size(wl.T, wl.k, E), dtype=torch.uint8, device=dev)
+    cap = B.capacity(wl.T, wl.k, E, wl.cf)
+    ids, w, r = rt["ids"].clone(), rt["w"].clone(), rt["r"].clone()
+    run = lambda: B.dispatch(ids, w, r, E, cap, rt["pad"], R, out, x=x, x_perm=x_perm, ws=dws)  # noqa: E731
+    for _ in range(2):
+        run()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def cpu_baseline(wl, params, sample_tokens):
     """The oracle, as it stands, on a bounded sample of the same workload."""
     import numpy as np
@@ -160,13 +189,20 @@ def main():
                               "algorithmic_flop_per_launch": f1}
         es = 2 if dtype == "bf16" else 4
         rows = int(offsets[-1])
-        # dispatch: read every token row once, write every permuted row once
-        disp_bytes = (wl.T + rows) * wl.d * es
+        # combine: read every kept expert row (two K-split planes when the second
+        # GEMM is split), read x, write out; the layer's dispatch moves indices
+        # only (the first GEMM gathers token rows through row_token)
         comb_bytes = (rows + 2 * wl.T) * wl.d * es
+        gather_ms = time_dispatch_gather(B, wl, layer, ws, x, args.steps)
+        disp_bytes = (wl.T + rows) * wl.d * es
         result["memory_bound"] = {
-            "dispatch_GBps": disp_bytes / (stages["dispatch"] * 1e-3) / 1e9,
             "combine_GBps": comb_bytes / (stages["combine"] * 1e-3) / 1e9,
-            "peak_GBps": PEAK_HBM_GBPS}
+            "dispatch_gather_ms": gather_ms,
+            "dispatch_gather_GBps": disp_bytes / (gather_ms * 1e-3) / 1e9,
+            "peak_GBps": PEAK_HBM_GBPS,
+            "note": ("combine bytes count one bf16 row per kept slot; dispatch_gather is "
+                     "moe_dispatch with the row permutation into x_perm (read each token "
+                     "row once, write each permuted row once) timed on the layer's ids")}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, params, args.cpu_sample)
     print(json.dumps(result))

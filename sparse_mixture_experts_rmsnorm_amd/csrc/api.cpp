@@ -163,7 +163,7 @@ struct ExpertWs {
   float* a_rows = nullptr;
   int64_t mt1 = 0, mt2 = 0;
   int ksplit = 1;        // K halves of the second linear
-  float* ypart = nullptr;  // [ksplit][rows_max][d] fp32 gated partials (ksplit 2)
+  void* ypart = nullptr;   // [ksplit][rows_max][d] gated partials (ksplit 2), dtype
   int64_t plane = 0;
 };
 
@@ -204,7 +204,7 @@ void carve_expert_ws(Carve& c, const ExpertGeo& g, int dtype, int64_t d, int64_t
   w->mt2 = std::max<int64_t>(1, max_tiles_gemm2(g, d, rows_max) * ksplit);
   if (ksplit > 1) {
     w->plane = rows_max * d;
-    w->ypart = c.take_n<float>(ksplit * w->plane);
+    w->ypart = c.take(size_t(ksplit * w->plane) * esize(dtype));
   }
   w->h = c.take(size_t(rows_max) * g.Fmax * esize(dtype));
   w->tiles1 = c.take_n<Tile>(w->mt1);
@@ -218,7 +218,7 @@ int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, i
                      const int32_t* offsets, int dense_rows, const int32_t* row_offsets,
                      const int32_t* column_indices, const void* x_in, const float* row_r,
                      const float* row_w, void* y, const ExpertWs& w, hipStream_t s,
-                     moe_timer* timer, int call);
+                     moe_timer* timer, int call, const int32_t* xrow = nullptr);
 
 }  // namespace
 
@@ -240,7 +240,7 @@ int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, i
                      const int32_t* offsets, int dense_rows, const int32_t* row_offsets,
                      const int32_t* column_indices, const void* x_in, const float* row_r,
                      const float* row_w, void* y, const ExpertWs& w, hipStream_t s,
-                     moe_timer* timer, int call) {
+                     moe_timer* timer, int call, const int32_t* xrow) {
   PlanArgs p{};
   p.offsets = offsets;
   p.dense_rows = dense_rows;
@@ -286,6 +286,7 @@ int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, i
   a.ldy = g.Fmax;
   a.row_r = row_r;
   a.row_w = nullptr;
+  a.xrow = xrow;
   a.epi = X->act == MOE_ACT_SWIGLU ? EPI_SWIGLU : EPI_ACT;
   a.act = X->act == MOE_ACT_GELU_TANH ? 1 : 0;
   MOE_HIP(launch_gemm(dtype, a, g.bf1, g.bt, int(w.mt1), s));
@@ -304,7 +305,7 @@ int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, i
   b.row_w = row_w;
   b.epi = EPI_GATE;
   if (w.ksplit > 1) {
-    b.epi = EPI_GATE_F32;
+    b.epi = EPI_GATE_SPLIT;
     b.Y = w.ypart;
     b.ysplit = w.plane;
   }
@@ -776,7 +777,9 @@ void carve_layer(Carve& c, const moe_layer_desc* L, int64_t T, const ExpertGeo& 
   w->row_r = c.take_n<float>(w->rows_max);
   w->row_w = c.take_n<float>(w->rows_max);
   w->row_expert = c.take_n<int32_t>(w->rows_max);
-  w->x_perm = g.atomic ? nullptr : c.take(size_t(w->rows_max) * d * es);
+  // the first expert GEMM gathers its rows from x through row_token, so the
+  // layer never materialises x_perm
+  w->x_perm = nullptr;
   w->stats = c.take_n<moe_stats>(1);
   w->disp_ws_bytes = moe_dispatch_workspace_size(T, k, E);
   w->disp_ws = c.take(w->disp_ws_bytes);
@@ -935,7 +938,7 @@ int moe_layer_forward(const moe_layer_desc* L, const void* x, int64_t T, void* o
       MOE_HIP(launch_topology(w.offsets, L->experts.size_blocks, L->experts.block_offsets, E, 128,
                               w.rows_max, w.row_offsets, w.column_indices, w.nnz, stream));
     rc = run_expert_gemms(&L->experts, g, L->dtype, d, w.offsets, 0, w.row_offsets, w.column_indices,
-                          w.x_perm, w.row_r, w.row_w, w.y, w.ex, stream, tm, call);
+                          xhat, w.row_r, w.row_w, w.y, w.ex, stream, tm, call, w.row_token);
     if (rc) return rc;
   }
   // shared experts: dense, gate 1, r in the first epilogue

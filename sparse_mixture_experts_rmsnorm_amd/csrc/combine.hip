@@ -62,11 +62,11 @@ __global__ void __launch_bounds__(256) k_combine(const T* __restrict__ y,
   }
 }
 
-// Same sum with the expert outputs held as two fp32 partial planes of a
-// K-split second GEMM: slot j adds (p0[pos] + p1[pos]).
+// Same sum with the expert outputs held as two partial planes of a K-split
+// second GEMM: slot j adds (p0[pos] + p1[pos]).
 template <typename T>
-__global__ void __launch_bounds__(256) k_combine_split(const float* __restrict__ y0,
-                                                       int64_t plane, const int32_t* __restrict__ pos,
+__global__ void __launch_bounds__(256) k_combine_split(const T* __restrict__ y0, int64_t plane,
+                                                       const int32_t* __restrict__ pos,
                                                        const T* __restrict__ x,
                                                        const T* __restrict__ sh, int64_t Tn,
                                                        int64_t d, int k, T* __restrict__ out) {
@@ -75,6 +75,8 @@ __global__ void __launch_bounds__(256) k_combine_split(const float* __restrict__
   const int64_t t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= Tn) return;
   const int64_t nvec = d / N;
+  const uint4* ys = reinterpret_cast<const uint4*>(y0);
+  const int64_t pv = plane / N;
   for (int64_t v = lane; v < nvec; v += 64) {
     float acc[8];
 #pragma unroll
@@ -94,16 +96,11 @@ __global__ void __launch_bounds__(256) k_combine_split(const float* __restrict__
     for (int j = 0; j < k; ++j) {
       const int p = pos[t * k + j];
       if (p < 0) continue;
-      const float4* a0 = reinterpret_cast<const float4*>(y0 + int64_t(p) * d + v * N);
-      const float4* a1 = reinterpret_cast<const float4*>(y0 + plane + int64_t(p) * d + v * N);
+      float f0[8], f1[8];
+      unpack16(ys[int64_t(p) * nvec + v], f0, (const T*)nullptr);
+      unpack16(ys[pv + int64_t(p) * nvec + v], f1, (const T*)nullptr);
 #pragma unroll
-      for (int h = 0; h < N / 4; ++h) {
-        const float4 u0 = a0[h], u1 = a1[h];
-        acc[4 * h + 0] += u0.x + u1.x;
-        acc[4 * h + 1] += u0.y + u1.y;
-        acc[4 * h + 2] += u0.z + u1.z;
-        acc[4 * h + 3] += u0.w + u1.w;
-      }
+      for (int i = 0; i < N; ++i) acc[i] += f0[i] + f1[i];
     }
     reinterpret_cast<uint4*>(out)[t * nvec + v] = pack16(acc, (const T*)nullptr);
   }
@@ -111,17 +108,19 @@ __global__ void __launch_bounds__(256) k_combine_split(const float* __restrict__
 
 }  // namespace
 
-hipError_t launch_combine_split(const float* y0, int64_t rows_max, const int32_t* pos,
+hipError_t launch_combine_split(const void* y0, int64_t rows_max, const int32_t* pos,
                                 const void* x, const void* shared, int dtype, int64_t T,
                                 int64_t d, int k, void* out, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const dim3 g(unsigned((T + 3) / 4));
   if (dtype == 0)
-    hipLaunchKernelGGL(k_combine_split<float>, g, dim3(256), 0, s, y0, rows_max * d, pos,
+    hipLaunchKernelGGL(k_combine_split<float>, g, dim3(256), 0, s, static_cast<const float*>(y0),
+                       rows_max * d, pos,
                        static_cast<const float*>(x), static_cast<const float*>(shared), T, d, k,
                        static_cast<float*>(out));
   else
-    hipLaunchKernelGGL(k_combine_split<uint16_t>, g, dim3(256), 0, s, y0, rows_max * d, pos,
+    hipLaunchKernelGGL(k_combine_split<uint16_t>, g, dim3(256), 0, s,
+                       static_cast<const uint16_t*>(y0), rows_max * d, pos,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(shared), T,
                        d, k, static_cast<uint16_t*>(out));
   return hipGetLastError();

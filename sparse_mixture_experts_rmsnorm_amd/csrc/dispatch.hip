@@ -59,10 +59,26 @@ __global__ void k_fill_rows(int64_t rows_max, int32_t* row_token, float* row_r, 
 // Pass 1: per-chunk expert histogram.
 __global__ void __launch_bounds__(kThreads) k_count(const int32_t* __restrict__ ids, int T, int k,
                                                     int E, int32_t* __restrict__ cc,
-                                                    int32_t* __restrict__ cerr) {
+                                                    int32_t* __restrict__ cerr, int nchunks,
+                                                    int64_t rows_max, int32_t* __restrict__ row_token,
+                                                    float* __restrict__ row_r,
+                                                    float* __restrict__ row_w,
+                                                    int32_t* __restrict__ row_expert) {
   extern __shared__ int hist[];
   __shared__ int err_s;
   const int c = blockIdx.x;
+  if (c >= nchunks) {
+    // the remaining blocks reset the per-row metadata
+    const int64_t nb = gridDim.x - nchunks;
+    for (int64_t i = (c - nchunks) * int64_t(kThreads) + threadIdx.x; i < rows_max;
+         i += nb * kThreads) {
+      row_token[i] = -1;
+      row_r[i] = 0.f;
+      row_w[i] = 0.f;
+      if (row_expert) row_expert[i] = -1;
+    }
+    return;
+  }
   for (int e = threadIdx.x; e < E; e += kThreads) hist[e] = 0;
   if (threadIdx.x == 0) err_s = 0;
   __syncthreads();
@@ -121,7 +137,19 @@ __global__ void __launch_bounds__(1024) k_scan(int32_t* __restrict__ cc,
   int maxl = 0;
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     int run = 0;
-    for (int c = 0; c < nchunks; ++c) {
+    int c = 0;
+    // eight independent loads in flight per step (the chunk walk is serial)
+    for (; c + 8 <= nchunks; c += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = cc[int64_t(c + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        cc[int64_t(c + u) * E + e] = run;
+        run += v[u];
+      }
+    }
+    for (; c < nchunks; ++c) {
       const int v = cc[int64_t(c) * E + e];
       cc[int64_t(c) * E + e] = run;
       run += v;
@@ -489,19 +517,15 @@ size_t dispatch_ws_bytes(int64_t T, int k, int64_t E) {
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   const int T = int(a.T), k = a.k, E = int(a.E);
   int32_t* stats = reinterpret_cast<int32_t*>(a.stats);
-  {
-    const int64_t blocks = std::min<int64_t>(4096, (a.rows_max + 255) / 256);
-    if (blocks > 0)
-      hipLaunchKernelGGL(k_fill_rows, dim3(unsigned(blocks)), dim3(256), 0, s, a.rows_max,
-                         a.row_token, a.row_r, a.row_w, a.row_expert);
-  }
+  const int64_t fill_blocks = std::min<int64_t>(1024, (a.rows_max + 255) / 256);
   if (E <= kDenseMaxE) {
     const int nch = (T + kChunkTokens - 1) / kChunkTokens;
     int32_t* cc = reinterpret_cast<int32_t*>(a.ws);
     int32_t* cerr = cc + int64_t(nch) * E;
-    if (nch > 0)
-      hipLaunchKernelGGL(k_count, dim3(nch), dim3(kThreads), E * sizeof(int), s, a.ids, T, k, E,
-                         cc, cerr);
+    if (nch + fill_blocks > 0)
+      hipLaunchKernelGGL(k_count, dim3(unsigned(nch + fill_blocks)), dim3(kThreads),
+                         E * sizeof(int), s, a.ids, T, k, E, cc, cerr, nch, a.rows_max,
+                         a.row_token, a.row_r, a.row_w, a.row_expert);
     const int cap = int(std::min<int64_t>(a.cap, int64_t(1) << 30));
     hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, cc, cerr, nch, E, cap, a.pad,
                        a.counts, a.offsets, stats);
@@ -522,6 +546,9 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
     int32_t* vals1 = keys1 + N;
     int32_t* cc = vals1 + N;
     int32_t* part = cc + (int64_t(nch) << b1);
+    if (fill_blocks > 0)
+      hipLaunchKernelGGL(k_fill_rows, dim3(unsigned(fill_blocks)), dim3(256), 0, s, a.rows_max,
+                         a.row_token, a.row_r, a.row_w, a.row_expert);
     if (N > 0) {
       const unsigned g = unsigned(std::min<int64_t>(4096, (N + 255) / 256));
       hipLaunchKernelGGL(k_radix_prep, dim3(g), dim3(256), 0, s, a.ids, N, E, keys1);

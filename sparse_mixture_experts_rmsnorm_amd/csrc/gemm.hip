@@ -64,7 +64,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const Tile& til
     if (row >= tile.row_end) continue;
     float rs = 1.f;
     if (EPI == EPI_ACT || EPI == EPI_SWIGLU || EPI == EPI_SCALE_F32) rs = a.row_r[row];
-    if (EPI == EPI_GATE || EPI == EPI_GATE_F32) rs = a.row_w ? a.row_w[row] : 1.f;
+    if (EPI == EPI_GATE || EPI == EPI_GATE_SPLIT) rs = a.row_w ? a.row_w[row] : 1.f;
     if (EPI == EPI_SWIGLU) {
       uint16_t* Y = static_cast<uint16_t*>(a.Y) + int64_t(row) * a.ldy + tile.ocol0 + wf * (WTF / 2);
 #pragma unroll
@@ -86,9 +86,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const Tile& til
           }
           *reinterpret_cast<uint2*>(Y + p * 32 + g * 8 + fh * 4) = make_uint2(pk[0], pk[1]);
         }
-    } else if (EPI == EPI_SCALE_F32 || EPI == EPI_GATE_F32) {
-      float* Y = static_cast<float*>(a.Y) + int64_t(row) * a.ldy + tile.ocol0 + wf * WTF +
-                 (EPI == EPI_GATE_F32 ? int64_t(tile.spare) * a.ysplit : 0);
+    } else if (EPI == EPI_SCALE_F32) {
+      float* Y = static_cast<float*>(a.Y) + int64_t(row) * a.ldy + tile.ocol0 + wf * WTF;
 #pragma unroll
       for (int i = 0; i < MF; ++i)
 #pragma unroll
@@ -101,7 +100,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const Tile& til
           *reinterpret_cast<float4*>(Y + i * 32 + g * 8 + fh * 4) = o;
         }
     } else {
-      uint16_t* Y = static_cast<uint16_t*>(a.Y) + int64_t(row) * a.ldy + tile.ocol0 + wf * WTF;
+      uint16_t* Y = static_cast<uint16_t*>(a.Y) + int64_t(row) * a.ldy + tile.ocol0 + wf * WTF +
+                    (EPI == EPI_GATE_SPLIT ? int64_t(tile.spare) * a.ysplit : 0);
 #pragma unroll
       for (int i = 0; i < MF; ++i)
 #pragma unroll
@@ -187,9 +187,12 @@ __global__ void __launch_bounds__(64 * WGF * WGT, MINB) k_gemm_bf16_dma(GemmArgs
       g = W + int64_t(tile.wrow0 + row) * a.ldw + tile.kofs;
     } else {
       row = (sg - SEGW) * RSEG + srow;
-      // a K-split tile reads its own half of the activation row
-      const int xk0 = EPI == EPI_GATE_F32 ? tile.spare * tile.klen : 0;
-      g = X + int64_t(min(tile.row0 + row, xlast)) * a.ldx + xk0;
+      // a K-split tile reads its own half of the activation row; with a row
+      // map the rows are gathered from the token rows (dispatch fused here)
+      const int xk0 = EPI == EPI_GATE_SPLIT ? tile.spare * tile.klen : 0;
+      int xr = min(tile.row0 + row, xlast);
+      if (a.xrow) xr = max(a.xrow[xr], 0);
+      g = X + int64_t(xr) * a.ldx + xk0;
     }
     src[u] = g + ((lane % C) ^ chunk_swz<C>(row)) * 8;
   }
@@ -299,7 +302,8 @@ __global__ void __launch_bounds__(256) k_gemm_f32(GemmArgs a) {
       sW[lq * 4 + 3][half * 64 + c] = v.w;
     }
     {
-      const int row = min(tile.row0 + lr, tile.row_end - 1);
+      int row = min(tile.row0 + lr, tile.row_end - 1);
+      if (a.xrow) row = max(a.xrow[row], 0);
       const float4 v = *reinterpret_cast<const float4*>(X + int64_t(row) * a.ldx + k0 + lq * 4);
       sX[lq * 4 + 0][lr] = v.x;
       sX[lq * 4 + 1][lr] = v.y;
@@ -333,7 +337,7 @@ __global__ void __launch_bounds__(256) k_gemm_f32(GemmArgs a) {
     if (row >= tile.row_end) continue;
     float rs = 1.f;
     if (EPI == EPI_ACT || EPI == EPI_SWIGLU || EPI == EPI_SCALE_F32) rs = a.row_r[row];
-    if (EPI == EPI_GATE || EPI == EPI_GATE_F32) rs = a.row_w ? a.row_w[row] : 1.f;
+    if (EPI == EPI_GATE || EPI == EPI_GATE_SPLIT) rs = a.row_w ? a.row_w[row] : 1.f;
     float* Y = static_cast<float*>(a.Y) + int64_t(row) * a.ldy + tile.ocol0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -563,7 +567,7 @@ hipError_t launch_gemm(int dtype, const GemmArgs& a, int bf, int bt, int grid, h
       case EPI_SWIGLU: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_SWIGLU>), g, b8, 0, s, a); break;
       case EPI_GATE: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_GATE>), g, b8, 0, s, a); break;
       case EPI_SCALE_F32: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_SCALE_F32>), g, b8, 0, s, a); break;
-      default: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_GATE_F32>), g, b8, 0, s, a); break;
+      default: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_GATE_SPLIT>), g, b8, 0, s, a); break;
     }
   } else {
     switch (a.epi) {

@@ -18,8 +18,8 @@ struct Tile {
   int spare;
 };
 
-// EPI_GATE_F32: fp32 gated partial of one K split, written to Y + split * ysplit.
-enum Epi { EPI_ACT = 0, EPI_SWIGLU = 1, EPI_GATE = 2, EPI_SCALE_F32 = 3, EPI_GATE_F32 = 4 };
+// EPI_GATE_SPLIT: gated partial of one K split, written to Y + split * ysplit.
+enum Epi { EPI_ACT = 0, EPI_SWIGLU = 1, EPI_GATE = 2, EPI_SCALE_F32 = 3, EPI_GATE_SPLIT = 4 };
 
 struct GemmArgs {
   const void* X; int64_t ldx;      // activations, row = GEMM row
@@ -29,7 +29,9 @@ struct GemmArgs {
   const float* row_r;              // r per GEMM row (EPI_ACT / SWIGLU / SCALE)
   const float* row_w;              // gate per GEMM row (EPI_GATE), NULL = 1
   int epi; int act;                // act: 0 GELU erf, 1 GELU tanh
-  int64_t ysplit;                  // EPI_GATE_F32: elements between split planes
+  int64_t ysplit;                  // EPI_GATE_SPLIT: elements between split planes
+  const int32_t* xrow;             // NULL, or X row of each GEMM row (-1: any row;
+                                   // its result is never read)
 };
 
 // Plan of GEMM tiles for grouped experts.  gemm = 1: first linear (features
@@ -88,8 +90,8 @@ hipError_t launch_topology(const int32_t* offsets, const int32_t* size_blocks,
 
 hipError_t launch_combine(const void* y, const int32_t* pos, const void* x, const void* shared,
                           int dtype, int64_t T, int64_t d, int k, void* out, hipStream_t s);
-// Combine over the two fp32 K-split partial planes (y0, y0 + rows_max * d).
-hipError_t launch_combine_split(const float* y0, int64_t rows_max, const int32_t* pos, const void* x,
+// Combine over the two K-split partial planes (y0, y0 + rows_max * d), dtype.
+hipError_t launch_combine_split(const void* y0, int64_t rows_max, const int32_t* pos, const void* x,
                                 const void* shared, int dtype, int64_t T, int64_t d, int k,
                                 void* out, hipStream_t s);
 
