@@ -36,7 +36,21 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=512,
                     help="tokens whose expert FFNs the CPU oracle computes")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (to scale HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain device copy of known size: 1 GiB read + 1 GiB written per launch."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
 
 
 def flops_gemm1(wl, kept):
@@ -113,6 +127,9 @@ def cpu_baseline(wl, params, sample_tokens):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the MoE layer here runs on a single MI355X "
               f"(--gpus {args.gpus} is not supported; how the layer would shard is described "

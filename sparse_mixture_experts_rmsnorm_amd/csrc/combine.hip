@@ -27,6 +27,7 @@ __global__ void __launch_bounds__(256) k_combine(const T* __restrict__ y,
   if (t >= Tn) return;
   const int64_t nvec = d / N;
   const uint4* ys = reinterpret_cast<const uint4*>(y);
+#pragma unroll 2
   for (int64_t v = lane; v < nvec; v += 64) {
     float acc[8];
 #pragma unroll
@@ -77,6 +78,7 @@ __global__ void __launch_bounds__(256) k_combine_split(const T* __restrict__ y0,
   const int64_t nvec = d / N;
   const uint4* ys = reinterpret_cast<const uint4*>(y0);
   const int64_t pv = plane / N;
+#pragma unroll 2
   for (int64_t v = lane; v < nvec; v += 64) {
     float acc[8];
 #pragma unroll

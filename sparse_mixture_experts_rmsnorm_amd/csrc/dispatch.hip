@@ -266,7 +266,9 @@ __global__ void __launch_bounds__(kThreads) k_rank(
   }
 }
 
-// Row gather: x_perm[row] = x[row_token[row]] (zeros on padding rows).
+// Row gather: x_perm[row] = x[row_token[row]] (zeros on padding rows).  A
+// wave copies one row; each lane moves up to 8 16-byte chunks, all loads
+// issued before the stores.
 template <typename T>
 __global__ void __launch_bounds__(kThreads) k_gather(const T* __restrict__ x, int64_t d,
                                                      const int32_t* __restrict__ rows_used,
@@ -274,18 +276,25 @@ __global__ void __launch_bounds__(kThreads) k_gather(const T* __restrict__ x, in
                                                      T* __restrict__ x_perm) {
   const int rows = *rows_used;
   const int64_t nvec = d / Vec16<T>::N;
-  const uint4* __restrict__ xs = reinterpret_cast<const uint4*>(x);
-  uint4* __restrict__ xp = reinterpret_cast<uint4*>(x_perm);
+  const u32x4* __restrict__ xs = reinterpret_cast<const u32x4*>(x);
+  u32x4* __restrict__ xp = reinterpret_cast<u32x4*>(x_perm);
   const int lane = threadIdx.x & 63;
   for (int row = blockIdx.x * 4 + (threadIdx.x >> 6); row < rows; row += gridDim.x * 4) {
     const int t = row_token[row];
-    if (t >= 0) {
-      const uint4* src = xs + int64_t(t) * nvec;
-      uint4* dst = xp + int64_t(row) * nvec;
-      for (int64_t v = lane; v < nvec; v += 64) dst[v] = src[v];
-    } else {
-      uint4* dst = xp + int64_t(row) * nvec;
-      for (int64_t v = lane; v < nvec; v += 64) dst[v] = make_uint4(0, 0, 0, 0);
+    const u32x4* src = xs + int64_t(t < 0 ? 0 : t) * nvec;
+    u32x4* dst = xp + int64_t(row) * nvec;
+    for (int64_t v0 = 0; v0 < nvec; v0 += 64 * 8) {
+      u32x4 buf[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t v = v0 + u * 64 + lane;
+        buf[u] = (v < nvec && t >= 0) ? src[v] : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t v = v0 + u * 64 + lane;
+        if (v < nvec) dst[v] = buf[u];
+      }
     }
   }
 }

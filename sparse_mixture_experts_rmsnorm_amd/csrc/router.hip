@@ -183,6 +183,7 @@ __global__ void __launch_bounds__(256) k_router_bf16(
     wok[b] = e < E;
     wrow[b] = wr + int64_t(wok[b] ? e : 0) * d + kb + kg * 8;
   }
+#pragma unroll 8
   for (int kk = 0; kk < kw; kk += 32) {
     uint4 xv = tok_ok ? *reinterpret_cast<const uint4*>(xrow + kk) : make_uint4(0, 0, 0, 0);
     {
