@@ -26,6 +26,36 @@ METRIC = "MoE layer fwd tokens/s + expert-GEMM TFLOP/s (% bf16 MFMA peak), 1 MI3
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA bf16 / fp32 vector
 PEAK_HBM_GBPS = 8000.0
 
+# HBM bytes per launch of the first expert GEMM on the Mixtral-shaped workload,
+# from two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)
+# scaled by what the same counters read for a plain 1 GiB device copy
+# (bench.py --copy-calibration).  Valid only for the kernel source it was
+# taken on: any change to gemm.hip or internal.h reports null.
+TRAFFIC = {
+    "workload": "mixtral_bf16",
+    "source_sha256": "b5e8b90d6f78cc49bc100df5d260f1d313ba117ed05930c2e7ecadb78335a95f",
+    "fetch_kib": 1885557.0, "write_kib": 229511.4,
+    "fetch_scale": 1048576.0 / 524302.4, "write_scale": 1048576.0 / 1048576.0,
+}
+
+
+def gemm_source_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "internal.h"):
+        with open(os.path.join(ROOT, "sparse_mixture_experts_rmsnorm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    t = TRAFFIC
+    if t["source_sha256"] is None or workload != t["workload"]:
+        return None
+    if gemm_source_sha256() != t["source_sha256"]:
+        return None
+    return (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024.0
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -34,7 +64,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mixtral_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=512,
+    ap.add_argument("--cpu-sample", type=int, default=4096,
                     help="tokens whose expert FFNs the CPU oracle computes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale HBM byte counters)")
@@ -202,7 +232,9 @@ def main():
             "gemm1_tflops": a1, "gemm2_tflops": f2 / (g2 * 1e-3) / 1e12}
         result["roofline"] = {"bound": "mfma", "achieved": a1, "peak": PEAK_TFLOPS[dtype],
                               "unit": "TFLOP/s", "frac": a1 / PEAK_TFLOPS[dtype],
-                              "traffic": None, "kernel": "k_gemm_bf16 (first expert linear)",
+                              "traffic": measured_traffic(wl.name),
+                              "traffic_unit": "bytes per launch (HBM, from PMC counters)",
+                              "kernel": "k_gemm_bf16_dma (first expert linear, SwiGLU epilogue)",
                               "algorithmic_flop_per_launch": f1}
         es = 2 if dtype == "bf16" else 4
         rows = int(offsets[-1])

@@ -142,13 +142,31 @@ __device__ __forceinline__ int chunk_swz(int r) {
   else return (r >> 2) & 3;
 }
 
+// Scheduling pattern for one K sub-step: NR fragment reads of the next
+// sub-step spread over the first MFMAs of this one (one MFMA, two reads, ...),
+// then the remaining MFMAs, so that the reads are in flight under MFMAs and
+// have had most of the sub-step to land before they are waited for.
+template <int NR, int NM>
+__device__ __forceinline__ void sched_interleave() {
+  if constexpr (NR > 0 && NM > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, NR >= 2 ? 2 : 1, 0);
+    sched_interleave<NR - (NR >= 2 ? 2 : 1), NM - 1>();
+  } else if constexpr (NR > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+  } else if constexpr (NM > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+  }
+}
+
 // BF features x BT rows per workgroup, WGF x WGT waves, each wave a
 // (BF / WGF) x (BT / WGT) sub-tile of 32 x 32 MFMA blocks.  Global -> LDS
 // moves by the global_load_lds_dwordx4 DMA (each wave instruction writes
 // 1 KB of LDS, lane i at byte 16 i) through a ring of NS LDS stages of BKD
-// columns: stages kt + 1 .. kt + NS - 1 are in flight while stage kt is
-// computed.
-template <int BF, int BT, int WGF, int WGT, int BKD, int NS, int EPI, int SCHED = 1, int MINB = 1>
+// columns.  EARLY (two stages) places the one barrier per stage before its
+// last K sub-step; otherwise stages kt + 1 .. kt + NS - 1 are in flight while
+// stage kt is computed and the barrier opens each stage.
+template <int BF, int BT, int WGF, int WGT, int BKD, int NS, int EPI, bool EARLY = true, int MINB = 1>
 __global__ void __launch_bounds__(64 * WGF * WGT, MINB) k_gemm_bf16_dma(GemmArgs a) {
   constexpr int NW = WGF * WGT;
   constexpr int WTF = BF / WGF, WTT = BT / WGT;
@@ -214,6 +232,70 @@ __global__ void __launch_bounds__(64 * WGF * WGT, MINB) k_gemm_bf16_dma(GemmArgs
 
   const int fr = lane & 31, fh = lane >> 5, fswz = chunk_swz<C>(lane & 15);
   const int nk = tile.klen / BKD;
+  constexpr int KS = BKD / 16;
+  if constexpr (EARLY) {
+    // Two LDS buffers; the barrier sits before the last K sub-step of each
+    // stage instead of at its start.  By then every wave holds the last
+    // sub-step's fragments in registers, so after the barrier the MFMAs of
+    // that sub-step cover both the refill of the buffer just drained (stage
+    // kt + 2) and the first fragment reads of stage kt + 1.
+    static_assert(NS == 2 && KS % 2 == 0, "early-barrier ring is two stages of even sub-steps");
+    bf16x8 af[2][MF], bfr[2][MT];
+#define MOE_FRAGS2(SW, SX, KSV, SLOT)                                                          \
+    {                                                                                        \
+      const int qo_ = ((2 * (KSV) + fh) ^ fswz) * 8;                                         \
+      _Pragma("unroll") for (int i = 0; i < MF; ++i)                                         \
+        af[SLOT][i] = *reinterpret_cast<const bf16x8*>((SW) + (wf * WTF + i * 32 + fr) * BKD + qo_); \
+      _Pragma("unroll") for (int j = 0; j < MT; ++j)                                         \
+        bfr[SLOT][j] = *reinterpret_cast<const bf16x8*>((SX) + (wt * WTT + j * 32 + fr) * BKD + qo_); \
+    }
+    if (nk > 0) issue(0, 0);
+    if (nk > 1) issue(1, 1);
+    if (nk > 1) MOE_WAIT_VMCNT(SPW);
+    else MOE_WAIT_VMCNT(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (nk > 0) MOE_FRAGS2(lds, lds + BF * BKD, 0, 0)
+    __builtin_amdgcn_sched_barrier(0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const uint16_t* sw = lds + (kt & 1) * LS;
+      const uint16_t* sx = sw + BF * BKD;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) {
+          MOE_FRAGS2(sw, sx, ks + 1, (ks + 1) & 1)
+        } else {
+          // the last sub-step's fragments in registers on every path, so the
+          // MFMAs below never wait for the next stage's reads
+          __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+        }
+        if (ks + 1 == KS && kt + 1 < nk) {
+          // this wave's reads of stage kt are in registers and its share of
+          // stage kt + 1 has landed; after the barrier the same holds for
+          // every wave, so buffer kt & 1 may be refilled with stage kt + 2
+          __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+          asm volatile("" ::: "memory");
+          __builtin_amdgcn_s_barrier();
+          asm volatile("" ::: "memory");
+          if (kt + 2 < nk) issue(kt + 2, kt & 1);
+          const uint16_t* nw = lds + ((kt + 1) & 1) * LS;
+          MOE_FRAGS2(nw, nw + BF * BKD, 0, 0)
+        }
+#pragma unroll
+        for (int i = 0; i < MF; ++i)
+#pragma unroll
+          for (int j = 0; j < MT; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j],
+                                                                acc[i][j], 0, 0, 0);
+        sched_interleave<MF + MT, MF * MT>();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#undef MOE_FRAGS2
+    gemm_epilogue<BF, BT, WGF, WGT, EPI>(a, tile, acc, wf, wt, fr, fh);
+    return;
+  }
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     if (s < nk) issue(s, s);
@@ -234,7 +316,6 @@ __global__ void __launch_bounds__(64 * WGF * WGT, MINB) k_gemm_bf16_dma(GemmArgs
     const uint16_t* sw = lds + (kt % NS) * LS;
     const uint16_t* sx = sw + BF * BKD;
     // fragments of sub-step ks + 1 are read while the MFMAs of ks run
-    constexpr int KS = BKD / 16;
     bf16x8 af[2][MF], bfr[2][MT];
 #define MOE_FRAGS(KSV, SLOT)                                                                 \
     {                                                                                        \
@@ -245,6 +326,7 @@ __global__ void __launch_bounds__(64 * WGF * WGT, MINB) k_gemm_bf16_dma(GemmArgs
         bfr[SLOT][j] = *reinterpret_cast<const bf16x8*>(sx + (wt * WTT + j * 32 + fr) * BKD + qo_); \
     }
     MOE_FRAGS(0, 0)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (ks + 1 < KS) MOE_FRAGS(ks + 1, (ks + 1) & 1)
@@ -254,13 +336,8 @@ __global__ void __launch_bounds__(64 * WGF * WGT, MINB) k_gemm_bf16_dma(GemmArgs
         for (int j = 0; j < MT; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j],
                                                               acc[i][j], 0, 0, 0);
-      if (SCHED == 1 && ks + 1 < KS) {
-        // keep the next sub-step's LDS reads ahead of this sub-step's MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, MF + MT, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, MF * MT, 0);
-      }
-      if (SCHED == 2) __builtin_amdgcn_iglp_opt(0);
-      if (SCHED == 3) __builtin_amdgcn_iglp_opt(1);
+      if (ks + 1 < KS) sched_interleave<MF + MT, MF * MT>();
+      __builtin_amdgcn_sched_barrier(0);
     }
 #undef MOE_FRAGS
   }
