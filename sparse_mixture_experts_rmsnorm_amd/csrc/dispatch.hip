@@ -457,9 +457,16 @@ __global__ void k_radix_counts(const int32_t* __restrict__ offsets, int N, int E
     mx = max(mx, c);
   }
   if (stats) {
+    // one atomic per workgroup: same-address atomics serialise in L2
+    __shared__ int wmax[4];
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o, 64));
-    if ((threadIdx.x & 63) == 0 && mx > 0) atomicMax(&stats[2], mx);
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      mx = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+      if (mx > 0) atomicMax(&stats[2], mx);
+    }
     if (blockIdx.x == 0 && threadIdx.x == 0) {
       const int rows = offsets[E];
       stats[0] = rows;
@@ -577,7 +584,7 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
     if (stats) hipLaunchKernelGGL(k_zero_stat, dim3(1), dim3(64), 0, s, stats);
     hipLaunchKernelGGL(k_radix_offsets, dim3(unsigned(std::min<int64_t>(4096, (N + 1 + 255) / 256))),
                        dim3(256), 0, s, keys1, int(N), E, a.offsets);
-    hipLaunchKernelGGL(k_radix_counts, dim3(unsigned(std::min<int64_t>(4096, (E + 255) / 256))),
+    hipLaunchKernelGGL(k_radix_counts, dim3(unsigned(std::min<int64_t>(256, (E + 255) / 256))),
                        dim3(256), 0, s, a.offsets, int(N), E, a.counts, stats);
     if (N > 0) {
       const unsigned g = unsigned(std::min<int64_t>(4096, (N + 255) / 256));

@@ -294,102 +294,186 @@ __global__ void __launch_bounds__(256) k_topk_rows(const float* __restrict__ lg,
 
 // ---------------------------------------------------------------- Cartesian two-stage top-k
 
-// One wave per token.  scores row = [s1 (Nr) | s2 (Nc)] fp32.  Q = ceil(max(Nr,Nc,k*k)/64).
+// Order-preserving map of an fp32 score to uint32 (larger score, larger
+// key); NaN maps to 0, below every number, and so does padding.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  const uint32_t b = __float_as_uint(f);
+  if (f != f) return 0u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Largest key th with at least k of the wave's keys >= th, i.e. the k-th
+// largest key, found bit by bit from the top.  Counts come from ballots
+// (one compare per held key, popcounts in scalar registers), so no
+// cross-lane shuffles sit on the dependency chain.
+template <int Q>
+__device__ __forceinline__ uint32_t kth_largest_key(const uint32_t (&u)[Q], int k) {
+  uint32_t th = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = th | (1u << b);
+    int cnt = 0;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) cnt += __popcll(__ballot(u[q] >= cand));
+    if (cnt >= k) th = cand;
+  }
+  return th;
+}
+
+// One wave per token.  scores row = [s1 (Nr) | s2 (Nc)] fp32; lane l holds
+// elements l + 64 q.  Stage 1 selects the k best rows of s1 and the k best
+// columns of s2 (score descending, index ascending); stage 2 selects the k
+// best of the k * k pair sums (sum descending, flat id row * Nc + col
+// ascending), which contain the k best pairs of the whole grid.  Each
+// selection finds the k-th largest key, keeps everything above it and the
+// needed number of ties at it in index order, and compacts the winners
+// into LDS; the final k are placed by rank.  Q = ceil(max(Nr, Nc, k*k)/64).
 template <int Q>
 __global__ void __launch_bounds__(256) k_cartesian_topk(const float* __restrict__ scores, int T,
                                                         int Nr, int Nc, int k, int renorm,
                                                         int32_t* __restrict__ ids,
                                                         float* __restrict__ wout) {
+  __shared__ float sel_v[4][2][64];
+  __shared__ int sel_i[4][2][64];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wid;
   if (t >= T) return;
   const float* row = scores + int64_t(t) * (Nr + Nc);
-  float vals[Q];
-  float m1 = -INFINITY, z1 = 0.f, m2 = -INFINITY, z2 = 0.f;
-  // stage 1a: the k best rows of s1 (lane a holds row choice a)
+  const uint64_t below = lanemask_lt();
+  float m[2] = {-INFINITY, -INFINITY}, z[2] = {0.f, 0.f};
+
+  // stage 1: list 0 = rows of s1, list 1 = columns of s2
 #pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    const int i = lane + 64 * q;
-    vals[q] = i < Nr ? row[i] : -INFINITY;
+  for (int list = 0; list < 2; ++list) {
+    const int n = list == 0 ? Nr : Nc;
+    const float* src = row + (list == 0 ? 0 : Nr);
+    float v[Q];
+    uint32_t u[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int i = lane + 64 * q;
+      v[q] = i < n ? src[i] : -INFINITY;
+      u[q] = i < n ? score_key(v[q]) : 0u;
+    }
+    if (!renorm) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < Q; ++q) mx = fmaxf(mx, v[q]);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+      float zz = 0.f;
+#pragma unroll
+      for (int q = 0; q < Q; ++q)
+        if (lane + 64 * q < n) zz += expf(v[q] - mx);
+      m[list] = mx;
+      z[list] = wave_sum(zz);
+    }
+    const uint32_t th = kth_largest_key<Q>(u, k);
+    int need = k;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) need -= __popcll(__ballot(u[q] > th));
+    int base = 0;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      // ties at the threshold go to the lowest indices: q ascending, then lane
+      const uint64_t eq = __ballot(u[q] == th);
+      const bool take_eq = ((eq >> lane) & 1) && __popcll(eq & below) < need;
+      need -= min(need, __popcll(eq));
+      const bool sel = u[q] > th || take_eq;
+      const uint64_t sm = __ballot(sel);
+      if (sel) {
+        const int p = base + __popcll(sm & below);
+        sel_v[wid][list][p] = v[q];
+        sel_i[wid][list][p] = lane + 64 * q;
+      }
+      base += __popcll(sm);
+    }
   }
-  if (!renorm) {
-#pragma unroll
-    for (int q = 0; q < Q; ++q) m1 = fmaxf(m1, vals[q]);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m1 = fmaxf(m1, __shfl_xor(m1, o, 64));
-#pragma unroll
-    for (int q = 0; q < Q; ++q)
-      if (lane + 64 * q < Nr) z1 += expf(vals[q] - m1);
-    z1 = wave_sum(z1);
-  }
-  float v1[1], v2[1];
-  int i1[1], i2[1];
-  wave_topk<Q, 1>(vals, Nr, k, v1, i1);
-  // stage 1b: the k best columns of s2
-#pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    const int j = lane + 64 * q;
-    vals[q] = j < Nc ? row[Nr + j] : -INFINITY;
-  }
-  if (!renorm) {
-#pragma unroll
-    for (int q = 0; q < Q; ++q) m2 = fmaxf(m2, vals[q]);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m2 = fmaxf(m2, __shfl_xor(m2, o, 64));
-#pragma unroll
-    for (int q = 0; q < Q; ++q)
-      if (lane + 64 * q < Nc) z2 += expf(vals[q] - m2);
-    z2 = wave_sum(z2);
-  }
-  wave_topk<Q, 1>(vals, Nc, k, v2, i2);
-  // stage 2: the k*k pairs; candidate c = a*k + b -> (row choice a, column choice b).
-  // Key: (s1 + s2 in fp32) descending, then flat id I[a]*Nc + J[b] ascending.
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // stage 2: candidate c = a * k + b pairs row choice a with column choice b
   const int nc = k * k;
+  float cv[Q];
   int cid[Q];
+  uint32_t cu[Q];
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
     const int c = lane + 64 * q;
-    const int a = c / k, b = c - (c / k) * k;
-    const float va = __shfl(v1[0], a & 63, 64), vb = __shfl(v2[0], b & 63, 64);
-    const int ia = __shfl(i1[0], a & 63, 64), ib = __shfl(i2[0], b & 63, 64);
-    vals[q] = c < nc ? va + vb : -INFINITY;
-    cid[q] = c < nc ? ia * Nc + ib : 0x7fffffff;
+    if (c < nc) {
+      const int a = c / k, b = c - a * k;
+      cv[q] = sel_v[wid][0][a] + sel_v[wid][1][b];
+      cid[q] = sel_i[wid][0][a] * Nc + sel_i[wid][1][b];
+      cu[q] = score_key(cv[q]);
+    } else {
+      cv[q] = -INFINITY;
+      cid[q] = 0x7fffffff;
+      cu[q] = 0u;
+    }
   }
-  bool live[Q];
+  const uint32_t th = kth_largest_key<Q>(cu, k);
+  int need = k;
+  bool sel[Q];
 #pragma unroll
-  for (int q = 0; q < Q; ++q) live[q] = lane + 64 * q < nc;
-  float sv = -INFINITY;
-  int si = 0;
+  for (int q = 0; q < Q; ++q) {
+    sel[q] = cu[q] > th;
+    need -= __popcll(__ballot(sel[q]));
+  }
+  // ties at the threshold go to the lowest flat ids (exact fp32 ties only)
+  while (need > 0) {
+    int best = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+      if (cu[q] == th && !sel[q]) best = min(best, cid[q]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) best = min(best, __shfl_xor(best, o, 64));
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+      if (cu[q] == th && !sel[q] && cid[q] == best) sel[q] = true;
+    --need;
+  }
+  // compact the k winners to lanes 0 .. k-1 (through LDS list 0)
+  __builtin_amdgcn_wave_barrier();
+  int base = 0;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const uint64_t sm = __ballot(sel[q]);
+    if (sel[q]) {
+      const int p = base + __popcll(sm & below);
+      sel_v[wid][0][p] = cv[q];
+      sel_i[wid][0][p] = cid[q];
+    }
+    base += __popcll(sm);
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const bool mine = lane < k;
+  const float sv = mine ? sel_v[wid][0][lane] : -INFINITY;
+  const int si = mine ? sel_i[wid][0][lane] : 0x7fffffff;
+  const uint32_t su = mine ? score_key(sv) : 0u;
+  // slot = rank among the k winners (sum descending, flat id ascending)
+  int rank = 0;
   for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int q = 0; q < Q; ++q)
-      if (live[q] && better(vals[q], cid[q], bv, bi)) {
-        bv = vals[q];
-        bi = cid[q];
-      }
-    const KV w = wave_best(bv, bi);
-#pragma unroll
-    for (int q = 0; q < Q; ++q)
-      if (live[q] && cid[q] == w.i) live[q] = false;
-    if (j == lane) {
-      sv = w.v;
-      si = w.i;
-    }
+    const uint32_t uj = __builtin_amdgcn_readlane(su, j);
+    const int ij = __builtin_amdgcn_readlane(si, j);
+    rank += (uj > su || (uj == su && ij < si)) ? 1 : 0;
   }
-  const float mx = __shfl(sv, 0, 64);
+  // the best sum is the one of rank 0
+  const uint64_t top = __ballot(mine && rank == 0);
+  const float mx = __shfl(sv, int(__builtin_ctzll(top)), 64);
   if (renorm) {
-    const float dd = wave_sum(lane < k ? expf(sv - mx) : 0.f);
-    if (lane < k) {
-      ids[int64_t(t) * k + lane] = si;
-      wout[int64_t(t) * k + lane] = expf(sv - mx) / dd;
-    }
-  } else if (lane < k) {
+    const float e = mine ? expf(sv - mx) : 0.f;
+    const float dd = wave_sum(e);
+    if (!mine) return;
+    ids[int64_t(t) * k + rank] = si;
+    wout[int64_t(t) * k + rank] = e / dd;
+  } else {
+    if (!mine) return;
     // full softmax over the grid: sum_ij exp(s1_i + s2_j) = (sum_i e^s1_i)(sum_j e^s2_j)
-    ids[int64_t(t) * k + lane] = si;
+    ids[int64_t(t) * k + rank] = si;
     const float s1 = row[si / Nc], s2 = row[Nr + si % Nc];
-    wout[int64_t(t) * k + lane] = expf(s1 - m1) * expf(s2 - m2) / (z1 * z2);
+    wout[int64_t(t) * k + rank] = expf(s1 - m[0]) * expf(s2 - m[1]) / (z[0] * z[1]);
   }
 }
 

@@ -281,3 +281,48 @@ def test_empty_batch(dev):
     out = layer.forward(x)
     torch.cuda.synchronize()
     assert out.shape == (0, wl.d)
+
+
+@pytest.mark.parametrize("renorm", [1, 0])
+def test_cartesian_topk_ties(dev, renorm):
+    """Key tables with repeated columns: many rows / columns score exactly alike
+    and many pair sums tie, so every selection decides ties by index."""
+    _say(f"[gpu] Cartesian top-k with exact ties, renorm={renorm}")
+    rng = np.random.default_rng(77)
+    T, d, Nr, Nc, k = 300, 256, 128, 128, 8
+    base_r = rng.standard_normal((d, 16)).astype(np.float32) * 0.05
+    base_c = rng.standard_normal((d, 8)).astype(np.float32) * 0.05
+    kr = np.ascontiguousarray(base_r[:, rng.permutation(np.arange(Nr) % 16)])
+    kc = np.ascontiguousarray(base_c[:, rng.permutation(np.arange(Nc) % 8)])
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    to_bf16 = lambda a: torch.from_numpy(a).to(dev).to(torch.bfloat16)  # noqa: E731
+    keys_t = torch.empty((Nr + Nc, d), dtype=torch.bfloat16, device=dev)
+    B.pack_transpose(to_bf16(kr), keys_t[:Nr])
+    B.pack_transpose(to_bf16(kc), keys_t[Nr:])
+    R = B.RouterDesc()
+    R.kind, R.E, R.Nr, R.Nc, R.keys_t = B.ROUTER_CARTESIAN, Nr * Nc, Nr, Nc, keys_t.data_ptr()
+    xb = to_bf16(x)
+    logits = torch.empty((T, Nr + Nc), dtype=torch.float32, device=dev)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    r = torch.empty(T, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(B.router_workspace_size(R, T), 1), dtype=torch.uint8, device=dev)
+    B.router_topk(R, xb, k, renorm, ids, w, r_out=r, logits=logits, ws=ws)
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy()
+    s1, s2 = lg[:, :Nr], lg[:, Nr:]
+    # the ties are really there: 16 distinct row scores and 8 distinct column scores
+    assert max(len(np.unique(s1[t])) for t in range(T)) <= 16
+    assert max(len(np.unique(s2[t])) for t in range(T)) <= 8
+    sel, sc = O.cartesian_topk(s1, s2, k)
+    assert np.array_equal(ids.cpu().numpy(), sel)
+    got = w.cpu().numpy().astype(np.float64)
+    if renorm:
+        e = np.exp(sc.astype(np.float64) - sc[:, :1])
+        ref = e / e.sum(axis=1, keepdims=True)
+    else:
+        full = s1.astype(np.float64)[:, :, None] + s2.astype(np.float64)[:, None, :]
+        m = full.reshape(T, -1).max(axis=1)
+        z = np.exp(full.reshape(T, -1) - m[:, None]).sum(axis=1)
+        ref = np.exp(sc.astype(np.float64) - m[:, None]) / z[:, None]
+    assert rel_err(got, ref) < 1e-5
