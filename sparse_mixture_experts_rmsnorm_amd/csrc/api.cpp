@@ -72,6 +72,7 @@ struct ExpertGeo {
   int bf1 = 256;       // packed weight rows per first-linear tile
   int bf2 = 256;       // output features per second-linear tile
   int bt = 256;        // GEMM rows per tile
+  int bt2 = 256;       // rows per tile of the second linear (128 fills a small dense layer)
   int fold = 1;        // first-linear output columns = packed features / fold
   bool bcsr = false, atomic = false;
 };
@@ -114,6 +115,7 @@ int check_experts(const moe_experts_desc* X, int dtype, int64_t d, ExpertGeo* g)
     geo.bf2 = 256;
     geo.bt = geo.bcsr ? 128 : 256;
   }
+  geo.bt2 = geo.bt;
   geo.fold = geo.pf;
   for (int64_t e = 0; e < X->E; ++e) {
     const int64_t f = X->ffn_sizes[e];
@@ -143,10 +145,12 @@ int64_t max_tiles_gemm1(const ExpertGeo& g, int64_t rows_max, int64_t nnz_max) {
   if (g.bcsr) return nnz_max * 128 * g.pf / g.bf1;
   return (rows_max / g.bt + g.E) * ((g.Fmax * g.pf + g.bf1 - 1) / g.bf1);
 }
+// (bf16 grouped sets are bounded for 128-row tiles, which a dense layer may
+// choose for its second linear.)
 int64_t max_tiles_gemm2(const ExpertGeo& g, int64_t d, int64_t rows_max) {
   const int64_t nf = d / g.bf2;
   if (g.bcsr) return (rows_max / 128) * nf;
-  return (rows_max / g.bt + g.E) * nf;
+  return (rows_max / std::min(g.bt, 128) + g.E) * nf;
 }
 
 int64_t nnz_max_of(const moe_experts_desc* X, int64_t rows_max) {
@@ -179,6 +183,14 @@ int device_cus() {
     dev_cached = dev;
   }
   return cus;
+}
+
+// A dense layer (the shared FFN) whose second linear has fewer 256-row tiles
+// than compute units takes 128-row tiles there instead.
+void fit_dense_tiles(ExpertGeo* g, int dtype, int64_t d, int64_t T) {
+  if (dtype != MOE_BF16 || g->bcsr || g->atomic) return;
+  const int64_t tiles = (T + 255) / 256 * (d / g->bf2);
+  if (tiles < device_cus()) g->bt2 = 128;
 }
 
 // Second-linear K split: the tile count of a grouped layer is only known on
@@ -272,6 +284,7 @@ int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, i
   p.ntiles = w.nt + 1;
   p.max_tiles = int(w.mt2);
   p.ksplit = w.ksplit;
+  p.bt = g.bt2;
   MOE_HIP(launch_plan(p, s));
   timer_mark(timer, call, MOE_STAGE_PLAN + 1, s);
 
@@ -309,7 +322,7 @@ int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, i
     b.Y = w.ypart;
     b.ysplit = w.plane;
   }
-  MOE_HIP(launch_gemm(dtype, b, g.bf2, g.bt, int(w.mt2), s));
+  MOE_HIP(launch_gemm(dtype, b, g.bf2, g.bt2, int(w.mt2), s));
   timer_mark(timer, call, MOE_STAGE_GEMM2 + 1, s);
   return MOE_OK;
 }
@@ -674,6 +687,7 @@ int moe_shared_ffn(const moe_experts_desc* S, int dtype, int64_t d, int64_t T, c
   Carve c(ws);
   ExpertWs w;
   carve_expert_ws(c, g, dtype, d, T, 0, &w);
+  fit_dense_tiles(&g, dtype, d, T);
   rc = run_expert_gemms(S, g, dtype, d, nullptr, int(T), nullptr, nullptr, xhat, r, nullptr, s, w,
                         stream, nullptr, -1);
   return rc ? rc : ok();
@@ -943,7 +957,9 @@ int moe_layer_forward(const moe_layer_desc* L, const void* x, int64_t T, void* o
   }
   // shared experts: dense, gate 1, r in the first epilogue
   if (L->shared && T > 0) {
-    rc = run_expert_gemms(L->shared, gs, L->dtype, d, nullptr, int(T), nullptr, nullptr, xhat, w.r,
+    ExpertGeo gt = gs;
+    fit_dense_tiles(&gt, L->dtype, d, T);
+    rc = run_expert_gemms(L->shared, gt, L->dtype, d, nullptr, int(T), nullptr, nullptr, xhat, w.r,
                           nullptr, w.s, w.sh, stream, nullptr, -1);
     if (rc) return rc;
   }

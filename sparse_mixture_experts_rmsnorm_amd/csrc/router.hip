@@ -119,6 +119,131 @@ __device__ void wave_topk(const float (&vals)[Q], int n, int k, float (&sv)[QS],
   }
 }
 
+// Order-preserving map of an fp32 score to uint32 (larger score, larger
+// key); NaN maps to 0, below every number, and so does padding.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  const uint32_t b = __float_as_uint(f);
+  if (f != f) return 0u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Largest key th with at least k of the wave's keys >= th, i.e. the k-th
+// largest key, found bit by bit from the top.  Counts come from ballots
+// (one compare per held key, popcounts in scalar registers), so no
+// cross-lane shuffles sit on the dependency chain.
+template <int Q>
+__device__ __forceinline__ uint32_t kth_largest_key(const uint32_t (&u)[Q], int k) {
+  uint32_t th = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = th | (1u << b);
+    int cnt = 0;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) cnt += __popcll(__ballot(u[q] >= cand));
+    if (cnt >= k) th = cand;
+  }
+  return th;
+}
+
+// The same threshold, usually from far fewer ballots: the k-th largest of the
+// 64 lane maxima is a lower bound L (k lane maxima are >= L); when at most 64
+// keys reach L they are compacted one per lane (through the wave's LDS
+// slice `cand`) and the threshold is searched among them alone.
+template <int Q>
+__device__ __forceinline__ uint32_t kth_largest_key_fast(const uint32_t (&u)[Q], int k,
+                                                         uint32_t* cand) {
+  uint32_t mx[1] = {u[0]};
+#pragma unroll
+  for (int q = 1; q < Q; ++q) mx[0] = max(mx[0], u[q]);
+  const uint32_t lo = kth_largest_key<1>(mx, k);
+  int c = 0;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) c += __popcll(__ballot(u[q] >= lo));
+  if (c > 64) return kth_largest_key<Q>(u, k);
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = lanemask_lt();
+  int base = 0;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const uint64_t m = __ballot(u[q] >= lo);
+    if (u[q] >= lo) cand[base + __popcll(m & below)] = u[q];
+    base += __popcll(m);
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  uint32_t cu[1] = {lane < c ? cand[lane] : 0u};
+  __builtin_amdgcn_wave_barrier();
+  return kth_largest_key<1>(cu, k);
+}
+
+// Top-k of one token's n values (lane l holds index l + 64 q) for k <= 64,
+// slots ordered by (value descending, index ascending), and their gates
+// (softmax over the k, or over all n when renorm is 0); writes ids / w of
+// token t.  Selection by threshold: the k-th largest key, everything above
+// it and the lowest-index ties at it, compacted through the wave's LDS
+// slices (64 entries each); a winner's slot is its rank among the k.
+template <int Q>
+__device__ void wave_select_gates(const float (&vals)[Q], int n, int k, int renorm, int64_t t,
+                                  int32_t* __restrict__ ids, float* __restrict__ wout,
+                                  uint32_t* cand, float* selv, int* seli) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = lanemask_lt();
+  uint32_t u[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) u[q] = lane + 64 * q < n ? score_key(vals[q]) : 0u;
+  uint32_t th;
+  if constexpr (Q == 1) th = kth_largest_key<1>(u, k);
+  else th = kth_largest_key_fast<Q>(u, k, cand);
+  int need = k;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) need -= __popcll(__ballot(u[q] > th));
+  int base = 0;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const uint64_t eq = __ballot(u[q] == th);
+    const bool take_eq = ((eq >> lane) & 1) && __popcll(eq & below) < need;
+    need -= min(need, __popcll(eq));
+    const bool sel = u[q] > th || take_eq;
+    const uint64_t sm = __ballot(sel);
+    if (sel) {
+      const int p = base + __popcll(sm & below);
+      selv[p] = vals[q];
+      seli[p] = lane + 64 * q;
+    }
+    base += __popcll(sm);
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const bool mine = lane < k;
+  const float sv = mine ? selv[lane] : -INFINITY;
+  const int si = mine ? seli[lane] : 0x7fffffff;
+  const uint32_t su = mine ? score_key(sv) : 0u;
+  __builtin_amdgcn_wave_barrier();
+  int rank = 0;
+  for (int j = 0; j < k; ++j) {
+    const uint32_t uj = __builtin_amdgcn_readlane(su, j);
+    const int ij = __builtin_amdgcn_readlane(si, j);
+    rank += (uj > su || (uj == su && ij < si)) ? 1 : 0;
+  }
+  const uint64_t top = __ballot(mine && rank == 0);
+  const float mx =
+      __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv), int(__builtin_ctzll(top))));
+  float den = 0.f;
+  if (renorm) {
+    den = mine ? expf(sv - mx) : 0.f;
+  } else {
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+      if (lane + 64 * q < n) den += expf(vals[q] - mx);
+  }
+  den = wave_sum(den);
+  if (mine) {
+    ids[t * k + rank] = si;
+    wout[t * k + rank] = expf(sv - mx) / den;
+  }
+}
+
 // Gates of the k selections held as in wave_topk; writes ids / w of token t.
 template <int QS, int Q>
 __device__ void write_gates(const float (&sv)[QS], const int (&si)[QS], const float (&vals)[Q],
@@ -158,9 +283,13 @@ __global__ void __launch_bounds__(256) k_router_bf16(
     const float* __restrict__ bias, int E, const float* __restrict__ r_in, float eps,
     float* __restrict__ r_out, int k, int renorm, int32_t* __restrict__ ids,
     float* __restrict__ wout, float* __restrict__ logits) {
+  constexpr int QV = (NB * 16 + 63) / 64;   // logits per lane in the top-k
   __shared__ float lg[kRouterTok][NB * 16 + 1];
   __shared__ float ssq[kRouterTok];
   __shared__ float rs[kRouterTok];
+  __shared__ uint32_t cand_s[4][64];
+  __shared__ float selv_s[4][64];
+  __shared__ int seli_s[4][64];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int t0 = blockIdx.x * kRouterTok;
   const int tl = lane & 15;       // token within the block (B column)
@@ -236,9 +365,9 @@ __global__ void __launch_bounds__(256) k_router_bf16(
     const int tt = t0 + tl2;
     if (tt >= T) break;
     const float rr = rs[tl2];
-    float vals[4];
+    float vals[QV];
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
+    for (int qq = 0; qq < QV; ++qq) {
       const int e = lane + 64 * qq;
       vals[qq] = -INFINITY;
       if (e < E) {
@@ -246,10 +375,16 @@ __global__ void __launch_bounds__(256) k_router_bf16(
         if (logits) logits[int64_t(tt) * E + e] = vals[qq];
       }
     }
-    float sv[4];
-    int si[4];
-    wave_topk<4, 4>(vals, E, k, sv, si);
-    write_gates<4, 4>(sv, si, vals, E, k, renorm, tt, ids, wout);
+    if (k <= 64) {
+      wave_select_gates<QV>(vals, E, k, renorm, tt, ids, wout, cand_s[wid], selv_s[wid],
+                            seli_s[wid]);
+    } else {
+      float sv[QV];
+      int si[QV];
+      wave_topk<QV, QV>(vals, E, k, sv, si);
+      write_gates<QV, QV>(sv, si, vals, E, k, renorm, tt, ids, wout);
+    }
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -278,6 +413,9 @@ __global__ void __launch_bounds__(256) k_topk_rows(const float* __restrict__ lg,
                                                    int renorm, int32_t* __restrict__ ids,
                                                    float* __restrict__ wout) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  __shared__ uint32_t cand_s[4][64];
+  __shared__ float selv_s[4][64];
+  __shared__ int seli_s[4][64];
   const int t = blockIdx.x * 4 + wid;
   if (t >= T) return;
   float vals[4];
@@ -286,38 +424,17 @@ __global__ void __launch_bounds__(256) k_topk_rows(const float* __restrict__ lg,
     const int e = lane + 64 * q;
     vals[q] = e < E ? lg[int64_t(t) * E + e] : -INFINITY;
   }
-  float sv[4];
-  int si[4];
-  wave_topk<4, 4>(vals, E, k, sv, si);
-  write_gates<4, 4>(sv, si, vals, E, k, renorm, t, ids, wout);
+  if (k <= 64) {
+    wave_select_gates<4>(vals, E, k, renorm, t, ids, wout, cand_s[wid], selv_s[wid], seli_s[wid]);
+  } else {
+    float sv[4];
+    int si[4];
+    wave_topk<4, 4>(vals, E, k, sv, si);
+    write_gates<4, 4>(sv, si, vals, E, k, renorm, t, ids, wout);
+  }
 }
 
 // ---------------------------------------------------------------- Cartesian two-stage top-k
-
-// Order-preserving map of an fp32 score to uint32 (larger score, larger
-// key); NaN maps to 0, below every number, and so does padding.
-__device__ __forceinline__ uint32_t score_key(float f) {
-  const uint32_t b = __float_as_uint(f);
-  if (f != f) return 0u;
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-
-// Largest key th with at least k of the wave's keys >= th, i.e. the k-th
-// largest key, found bit by bit from the top.  Counts come from ballots
-// (one compare per held key, popcounts in scalar registers), so no
-// cross-lane shuffles sit on the dependency chain.
-template <int Q>
-__device__ __forceinline__ uint32_t kth_largest_key(const uint32_t (&u)[Q], int k) {
-  uint32_t th = 0;
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t cand = th | (1u << b);
-    int cnt = 0;
-#pragma unroll
-    for (int q = 0; q < Q; ++q) cnt += __popcll(__ballot(u[q] >= cand));
-    if (cnt >= k) th = cand;
-  }
-  return th;
-}
 
 // One wave per token.  scores row = [s1 (Nr) | s2 (Nc)] fp32; lane l holds
 // elements l + 64 q.  Stage 1 selects the k best rows of s1 and the k best
@@ -334,6 +451,7 @@ __global__ void __launch_bounds__(256) k_cartesian_topk(const float* __restrict_
                                                         float* __restrict__ wout) {
   __shared__ float sel_v[4][2][64];
   __shared__ int sel_i[4][2][64];
+  __shared__ uint32_t cand_s[4][64];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wid;
   if (t >= T) return;
@@ -367,7 +485,7 @@ __global__ void __launch_bounds__(256) k_cartesian_topk(const float* __restrict_
       m[list] = mx;
       z[list] = wave_sum(zz);
     }
-    const uint32_t th = kth_largest_key<Q>(u, k);
+    const uint32_t th = kth_largest_key_fast<Q>(u, k, cand_s[wid]);
     int need = k;
 #pragma unroll
     for (int q = 0; q < Q; ++q) need -= __popcll(__ballot(u[q] > th));
@@ -411,7 +529,7 @@ __global__ void __launch_bounds__(256) k_cartesian_topk(const float* __restrict_
       cu[q] = 0u;
     }
   }
-  const uint32_t th = kth_largest_key<Q>(cu, k);
+  const uint32_t th = kth_largest_key_fast<Q>(cu, k, cand_s[wid]);
   int need = k;
   bool sel[Q];
 #pragma unroll

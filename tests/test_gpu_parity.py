@@ -326,3 +326,33 @@ def test_cartesian_topk_ties(dev, renorm):
         z = np.exp(full.reshape(T, -1) - m[:, None]).sum(axis=1)
         ref = np.exp(sc.astype(np.float64) - m[:, None]) / z[:, None]
     assert rel_err(got, ref) < 1e-5
+
+
+@pytest.mark.parametrize("E,k,renorm", [(8, 2, 1), (64, 6, 0), (160, 40, 1)])
+def test_dense_topk_ties(dev, E, k, renorm):
+    """Router columns repeated: logits tie exactly and the top-k must take the
+    lower expert index first, in slot order (logit descending)."""
+    _say(f"[gpu] dense router top-k with exact ties E={E} k={k} renorm={renorm}")
+    rng = np.random.default_rng(E * 100 + k)
+    T, d = 333, 256
+    distinct = max(2, E // 4)
+    base = rng.standard_normal((d, distinct)).astype(np.float32) * 0.05
+    wr = np.ascontiguousarray(base[:, rng.permutation(np.arange(E) % distinct)])
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    wr_t = torch.empty((E, d), dtype=torch.bfloat16, device=dev)
+    B.pack_transpose(torch.from_numpy(wr).to(dev).to(torch.bfloat16), wr_t)
+    R = B.RouterDesc()
+    R.kind, R.E, R.wr_t = B.ROUTER_DENSE, E, wr_t.data_ptr()
+    xb = torch.from_numpy(x).to(dev).to(torch.bfloat16)
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    r = torch.empty(T, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(B.router_workspace_size(R, T), 1), dtype=torch.uint8, device=dev)
+    B.router_topk(R, xb, k, renorm, ids, w, r_out=r, logits=logits, ws=ws)
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy()
+    assert max(len(np.unique(lg[t])) for t in range(T)) <= distinct
+    sel = O.select_topk(lg, k)
+    assert np.array_equal(ids.cpu().numpy(), sel)
+    assert rel_err(w.cpu().numpy(), O.gates(lg.astype(np.float64), sel, renorm)) < 1e-5
