@@ -328,13 +328,14 @@ def test_cartesian_topk_ties(dev, renorm):
     assert rel_err(got, ref) < 1e-5
 
 
-@pytest.mark.parametrize("E,k,renorm", [(8, 2, 1), (64, 6, 0), (160, 40, 1)])
-def test_dense_topk_ties(dev, E, k, renorm):
+@pytest.mark.parametrize("E,k,renorm,T", [(8, 2, 1, 333), (64, 6, 0, 333), (160, 40, 1, 333),
+                                          (32, 4, 1, 8200), (64, 6, 1, 16400)])
+def test_dense_topk_ties(dev, E, k, renorm, T):
     """Router columns repeated: logits tie exactly and the top-k must take the
     lower expert index first, in slot order (logit descending)."""
-    _say(f"[gpu] dense router top-k with exact ties E={E} k={k} renorm={renorm}")
+    _say(f"[gpu] dense router top-k with exact ties E={E} k={k} renorm={renorm} T={T}")
     rng = np.random.default_rng(E * 100 + k)
-    T, d = 333, 256
+    d = 256
     distinct = max(2, E // 4)
     base = rng.standard_normal((d, distinct)).astype(np.float32) * 0.05
     wr = np.ascontiguousarray(base[:, rng.permutation(np.arange(E) % distinct)])
