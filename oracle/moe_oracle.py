@@ -32,6 +32,11 @@ Readings taken where the pages are silent (each is listed in the design doc):
     expert index; slots are ordered by descending logit.
   * Gate = softmax over the k selected logits (renorm=1) or the full-softmax
     probability (renorm=0).
+  * Noise top-k adds noise_std * (caller-supplied N(0,1) draws) to the logits
+    before selection; gates and statistics use the noisy logits.
+  * The load-balancing auxiliary loss is the squared coefficient of
+    variation (population variance / mean^2) across experts of the summed
+    full-softmax router probabilities.
   * Capacity = ceil(T*k*cf/E) computed exactly, clamped to [0, T]; cf <= 0
     means "no limit" (= T).  Within an expert, tokens are kept in token order.
   * Dropped slots contribute zero; kept gates are not renormalised.  The
@@ -61,7 +66,8 @@ from scipy.special import erf
 __all__ = [
     "bf16_to_f64", "f64_to_bf16_bits", "as_f64",
     "capacity", "rmsnorm_scale", "rmsnorm", "router_logits", "router_logits_unfused",
-    "select_topk", "gates", "dispatch", "expert_layout", "bcsr_topology",
+    "select_topk", "gates", "noisy_logits", "router_probabilities", "squared_cv", "router_stats",
+    "dispatch", "expert_layout", "bcsr_topology",
     "gelu", "gelu_tanh", "silu", "ffn", "grouped_expert_ffn", "bcsr_expert_ffn",
     "cartesian_scores", "cartesian_topk", "cartesian_topk_bruteforce",
     "atomic_experts_token_centric", "atomic_experts_expert_centric",
@@ -217,6 +223,65 @@ def gates(logits: np.ndarray, ids: np.ndarray, renorm: int = 1) -> np.ndarray:
     m = l.max(axis=1, keepdims=True)
     z = np.exp(l - m).sum(axis=1, keepdims=True)
     return np.exp(sel - m) / z
+
+
+# --------------------------------------------------------------------------
+# [GLOSS] noise top-k gating; load balancing and its auxiliary loss;
+# [CODA] metrics computed in epilogues
+# --------------------------------------------------------------------------
+
+def noisy_logits(logits, noise, noise_std: float) -> np.ndarray:
+    """Logits with tunable Gaussian noise added before selection ([GLOSS]
+    gating network: noise top-k).  `noise` holds standard-normal draws
+    [T, E] supplied by the caller; `noise_std` scales them.  Selection,
+    gates and the routing statistics all use the noisy logits.  float64.
+    """
+    return np.asarray(logits, dtype=np.float64) + float(noise_std) * np.asarray(noise, dtype=np.float64)
+
+
+def router_probabilities(logits) -> np.ndarray:
+    """The router's probability distribution over all E experts per token:
+    softmax of the (post-scale, post-bias) logits.  float64 [T, E]."""
+    l = np.asarray(logits, dtype=np.float64)
+    m = l.max(axis=1, keepdims=True)
+    e = np.exp(l - m)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def squared_cv(v) -> float:
+    """Squared coefficient of variation across experts: population variance
+    over the squared mean ([GLOSS] load balancing / auxiliary loss).  NaN
+    when the mean is zero."""
+    v = np.asarray(v, dtype=np.float64)
+    mean = v.mean()
+    if mean == 0:
+        return float("nan")
+    return float(((v - mean) ** 2).mean() / mean ** 2)
+
+
+def router_stats(logits, ids, w, counts=None) -> dict:
+    """Per-expert routing statistics and the load-balancing quantities.
+
+    prob_sum[e] = sum over tokens of the router probability of e (full
+    softmax); gate_sum[e] = sum over tokens of the gate weight given to e in
+    the selected slots; aux = [CV^2(prob_sum), CV^2(gate_sum), CV^2(counts)]
+    (the last NaN without counts).  The squared CV of the routing
+    probability mass per expert is the auxiliary load loss the glossary
+    names; the other two are the same statistic of the gates actually used
+    and of the hard per-expert load.
+    """
+    l = np.asarray(logits, dtype=np.float64)
+    T, E = l.shape
+    prob_sum = router_probabilities(l).sum(axis=0)
+    gate_sum = np.zeros(E, dtype=np.float64)
+    ids = np.asarray(ids)
+    w = np.asarray(w, dtype=np.float64)
+    for t in range(T):
+        for j in range(ids.shape[1]):
+            gate_sum[ids[t, j]] += w[t, j]
+    aux = [squared_cv(prob_sum), squared_cv(gate_sum),
+           squared_cv(counts) if counts is not None else float("nan")]
+    return {"prob_sum": prob_sum, "gate_sum": gate_sum, "aux": np.array(aux)}
 
 
 # --------------------------------------------------------------------------

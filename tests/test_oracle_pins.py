@@ -438,3 +438,63 @@ def test_cartesian_layer_matches_bruteforce_routing():
     routed = np.stack([sum(gg[t, j] * O.gelu(xn[t] @ p["W"][n]) * p["V"][n]
                            for j, n in enumerate(res["ids"][t])) for t in range(T)])
     assert np.allclose(res["out"], x + shared + routed, rtol=1e-11, atol=1e-13)
+
+
+# ---------------------------------------------------------------- routing statistics / noisy top-k
+
+def test_squared_cv_closed_forms():
+    assert O.squared_cv(np.full(8, 3.0)) == 0.0
+    # all mass on one of E experts: CV^2 = E - 1
+    for E in (2, 8, 64):
+        v = np.zeros(E)
+        v[3 % E] = 5.0
+        assert abs(O.squared_cv(v) - (E - 1)) < 1e-12
+    # two levels a, b over halves: CV^2 = ((a - b) / (a + b))^2
+    a, b = 3.0, 1.0
+    assert abs(O.squared_cv(np.array([a] * 4 + [b] * 4)) - ((a - b) / (a + b)) ** 2) < 1e-15
+    assert np.isnan(O.squared_cv(np.zeros(4)))
+
+
+def test_router_stats_uniform_and_collapsed():
+    T, E, k = 50, 8, 2
+    # equal logits: every expert gets T / E probability mass, CV^2 = 0
+    st = O.router_stats(np.zeros((T, E)), np.tile(np.arange(k), (T, 1)), np.full((T, k), 0.5))
+    assert np.allclose(st["prob_sum"], T / E, rtol=0, atol=1e-12)
+    assert abs(st["aux"][0]) < 1e-24
+    # one expert dominates every token: the mass is all on it, CV^2 = E - 1
+    l = np.full((T, E), -800.0)
+    l[:, 5] = 0.0
+    st = O.router_stats(l, np.tile([5, 0], (T, 1)), np.tile([1.0, 0.0], (T, 1)))
+    assert abs(st["prob_sum"][5] - T) < 1e-9 and abs(st["aux"][0] - (E - 1)) < 1e-9
+    assert st["gate_sum"][5] == T and abs(st["aux"][1] - (E - 1)) < 1e-12
+    assert np.isnan(st["aux"][2])
+
+
+def test_router_stats_sums_and_scatter():
+    rng = np.random.default_rng(11)
+    T, E, k = 40, 16, 3
+    l = rng.standard_normal((T, E))
+    ids = O.select_topk(l, k)
+    w = O.gates(l, ids, 1)
+    counts = np.bincount(ids.ravel(), minlength=E)
+    st = O.router_stats(l, ids, w, counts)
+    # every token's probabilities and renormalised gates sum to one
+    assert abs(st["prob_sum"].sum() - T) < 1e-9
+    assert abs(st["gate_sum"].sum() - T) < 1e-9
+    # the gate sum scatters each slot's weight to its expert (checked by expert)
+    for e in range(E):
+        assert abs(st["gate_sum"][e] - w[ids == e].sum()) < 1e-12
+    # full-softmax mass of expert e equals the column sum of exp(l - m) / z
+    p = np.exp(l - l.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    assert np.allclose(st["prob_sum"], p.sum(0), rtol=1e-13)
+    assert abs(st["aux"][2] - counts.var() / counts.mean() ** 2) < 1e-12
+
+
+def test_noisy_logits_flip_selection():
+    l = np.array([[1.0, 0.5, -1.0]])
+    n = np.array([[0.0, 1.0, 0.0]])
+    assert O.select_topk(O.noisy_logits(l, n, 0.0), 1)[0, 0] == 0
+    assert O.select_topk(O.noisy_logits(l, n, 1.0), 1)[0, 0] == 1       # 0.5 + 1 > 1
+    assert O.select_topk(O.noisy_logits(l, n, 0.4), 1)[0, 0] == 0       # 0.9 < 1
+    assert np.array_equal(O.noisy_logits(l, n, 2.5), l + 2.5 * n)
