@@ -121,6 +121,32 @@ def time_dispatch_gather(B, wl, layer, ws, x, steps):
     return e0.elapsed_time(e1) / steps
 
 
+def time_router_extras(B, wl, layer, x, out, ws, steps):
+    """The layer with noise top-k and the routing statistics switched on
+    (outside the headline figure): router stage and whole-step times."""
+    import torch
+    dev = x.device
+    g = torch.Generator(device=dev).manual_seed(0)
+    noise = torch.randn((wl.T, wl.E), generator=g, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    ex = B.router_extras(noise=noise, noise_std=1.0, prob_sum=torch.empty(wl.E, **f32),
+                         gate_sum=torch.empty(wl.E, **f32), aux=torch.empty(3, **f32))
+    for _ in range(2):
+        layer.forward(x, out=out, ws=ws, router_extras=ex)
+    timer = B.StageTimer(steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer.forward(x, out=out, ws=ws, timer=timer, router_extras=ex)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    tot, n = timer.stage_ms("router")
+    timer.close()
+    return {"router_ms": tot / max(n, 1), "ms_per_step": ms,
+            "note": "noise top-k (N(0,1) draws x 1.0) plus per-expert probability / gate sums "
+                    "and the three squared-CV statistics"}
+
+
 def cpu_baseline(wl, params, sample_tokens):
     """The oracle, as it stands, on a bounded sample of the same workload."""
     import numpy as np
@@ -252,6 +278,8 @@ def main():
             "note": ("combine bytes count one bf16 row per kept slot; dispatch_gather is "
                      "moe_dispatch with the row permutation into x_perm (read each token "
                      "row once, write each permuted row once) timed on the layer's ids")}
+    if wl.router == "dense":
+        result["router_extras"] = time_router_extras(B, wl, layer, x, out, ws, args.steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, params, args.cpu_sample)
     print(json.dumps(result))

@@ -164,6 +164,30 @@ enum {
   MOE_STAGE_COUNT
 };
 
+/* Router extras (dense router): noise top-k and routing statistics.
+ * Glossary "Mixture of Experts (MoE)": the gating-network entry (noise
+ * top-k: tunable Gaussian noise added to the logits before selection) and
+ * the load-balancing / auxiliary-loss entries (the squared coefficient of
+ * variation of the routing probability across experts); the CODA thread's
+ * point that metrics ride in epilogues.  All pointers are device pointers
+ * and may be NULL.  The noise is an input: the caller draws it.  With noise,
+ * selection, gates, the logits output and the statistics all use
+ * logits + noise_std * noise.  Statistics are summed per workgroup and then
+ * over workgroups in a fixed order, so they are deterministic. */
+typedef struct moe_router_extras {
+  const float* noise;   /* [T, E] fp32 standard-normal draws, or NULL        */
+  float noise_std;      /* scale of the noise                                */
+  float* prob_sum;      /* [E] out: sum over tokens of the full-softmax
+                           router probability of each expert                */
+  float* gate_sum;      /* [E] out: sum over tokens of the gate each expert
+                           receives in the selected slots                   */
+  float* aux;           /* [3] out: squared CV across experts (population
+                           variance / mean^2) of prob_sum (the auxiliary
+                           load loss), of gate_sum, and of the per-expert
+                           slot counts (before capacity); NaN for a zero
+                           mean                                              */
+} moe_router_extras;
+
 typedef struct moe_layer_desc {
   int64_t d;                       /* model width                              */
   int dtype;                       /* MOE_F32 or MOE_BF16                      */
@@ -180,6 +204,8 @@ typedef struct moe_layer_desc {
   int residual;                    /* 1: out includes x (dropped tokens pass
                                       through); 0: experts only                */
   moe_timer* timer;                /* NULL, or per-stage event timing          */
+  const moe_router_extras* router_extras;  /* [host] NULL, or noise / statistics
+                                               of the dense router            */
 } moe_layer_desc;
 
 /* Last error message of the calling thread ("" after success). */
@@ -221,14 +247,23 @@ int moe_rmsnorm_stats(const void* x, int dtype, int64_t T, int64_t d, const void
  * (int32, slot 0 = best, ordered by logit descending with ties to the lower
  * expert index), w [T, k] gates (renorm as in moe_layer_desc), and, when
  * non-NULL, logits: DENSE [T, E]; CARTESIAN [T, Nr + Nc] = (s1 | s2).
- * DENSE supports E <= 256 and k <= E; bf16 needs no workspace, f32 needs
- * logits (non-NULL).  CARTESIAN needs k <= 64, Nr, Nc >= k, Nr + Nc a
- * multiple of 256 and a workspace of moe_router_workspace_size bytes. */
+ * DENSE supports E <= 256 and k <= E; f32 needs logits (non-NULL).
+ * CARTESIAN needs k <= 64, Nr, Nc >= k, Nr + Nc a multiple of 256.  Both
+ * take a workspace of moe_router_workspace_size bytes (DENSE: room for the
+ * per-workgroup statistics of moe_router_topk_ex). */
 size_t moe_router_workspace_size(const moe_router_desc* R, int64_t T);
 int moe_router_topk(const moe_router_desc* R, const void* x, int dtype, int64_t T, int64_t d,
                     const float* r_in, float eps, float* r_out, int k, int renorm,
                     int32_t* ids, float* w, float* logits, void* ws, size_t ws_bytes,
                     hipStream_t stream);
+/* moe_router_topk with extras [host, may be NULL]: noise top-k and the
+ * routing statistics of moe_router_extras.  DENSE router only, k <= 64;
+ * otherwise MOE_EUNSUPPORTED when any extra is requested. */
+int moe_router_topk_ex(const moe_router_desc* R, const void* x, int dtype, int64_t T, int64_t d,
+                       const float* r_in, float eps, float* r_out, int k, int renorm,
+                       int32_t* ids, float* w, float* logits,
+                       const moe_router_extras* extras, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
 
 /* ---- step 3: capacity + dispatch ----
  * Deterministic and stable: within an expert, slots keep token order; a

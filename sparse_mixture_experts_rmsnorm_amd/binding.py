@@ -22,6 +22,7 @@ STAGES = ["router", "dispatch", "plan", "gemm1", "gemm2", "shared", "combine"]
 EXPORTED = [
     "moe_last_error", "moe_version", "moe_capacity", "moe_rows_max", "moe_pack_transpose",
     "moe_pack_swiglu", "moe_rmsnorm_stats", "moe_router_workspace_size", "moe_router_topk",
+    "moe_router_topk_ex",
     "moe_dispatch_workspace_size", "moe_dispatch", "moe_topology_nnz_max", "moe_build_topology",
     "moe_expert_workspace_size", "moe_expert_gemm", "moe_shared_workspace_size", "moe_shared_ffn",
     "moe_combine", "moe_layer_workspace_size", "moe_layer_forward", "moe_layer_routing",
@@ -50,11 +51,17 @@ class Routing(C.Structure):
                 ("row_expert", C.c_void_p)]
 
 
+class RouterExtras(C.Structure):
+    _fields_ = [("noise", C.c_void_p), ("noise_std", C.c_float), ("prob_sum", C.c_void_p),
+                ("gate_sum", C.c_void_p), ("aux", C.c_void_p)]
+
+
 class LayerDesc(C.Structure):
     _fields_ = [("d", C.c_int64), ("dtype", C.c_int), ("gamma", C.c_void_p), ("eps", C.c_float),
                 ("router", RouterDesc), ("k", C.c_int), ("renorm", C.c_int),
                 ("capacity_factor", C.c_double), ("experts", ExpertsDesc),
-                ("shared", C.POINTER(ExpertsDesc)), ("residual", C.c_int), ("timer", C.c_void_p)]
+                ("shared", C.POINTER(ExpertsDesc)), ("residual", C.c_int), ("timer", C.c_void_p),
+                ("router_extras", C.POINTER(RouterExtras))]
 
 
 class Stats(C.Structure):
@@ -85,6 +92,8 @@ def lib() -> C.CDLL:
             "moe_router_workspace_size": (SZ, [C.POINTER(RouterDesc), I64]),
             "moe_router_topk": (I, [C.POINTER(RouterDesc), P, I, I64, I64, P, F, P, I, I, P, P, P,
                                     P, SZ, P]),
+            "moe_router_topk_ex": (I, [C.POINTER(RouterDesc), P, I, I64, I64, P, F, P, I, I, P, P,
+                                       P, C.POINTER(RouterExtras), P, SZ, P]),
             "moe_dispatch_workspace_size": (SZ, [I64, I, I64]),
             "moe_dispatch": (I, [P, P, P, P, I, I64, I64, I64, I, I64, I, I64, P, P, P, P, P, P, P,
                                  P, P, P, SZ, P]),
@@ -190,12 +199,21 @@ def rmsnorm_stats(x, eps, r, gamma=None, xg=None, stream=None) -> None:
 
 
 def router_topk(router: RouterDesc, x, k, renorm, ids, w, r_in=None, r_out=None, eps=1e-6,
-                logits=None, ws=None, stream=None) -> None:
+                logits=None, ws=None, stream=None, extras: "RouterExtras | None" = None) -> None:
     T, d = x.shape
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
-    check(lib().moe_router_topk(C.byref(router), ptr(x), dtype_code(x), T, d, ptr(r_in), float(eps),
-                                ptr(r_out), k, renorm, ptr(ids), ptr(w), ptr(logits), ptr(ws),
-                                nbytes, stream_handle(stream)))
+    ex = C.byref(extras) if extras is not None else None
+    check(lib().moe_router_topk_ex(C.byref(router), ptr(x), dtype_code(x), T, d, ptr(r_in),
+                                   float(eps), ptr(r_out), k, renorm, ptr(ids), ptr(w), ptr(logits),
+                                   ex, ptr(ws), nbytes, stream_handle(stream)))
+
+
+def router_extras(noise=None, noise_std=0.0, prob_sum=None, gate_sum=None, aux=None) -> RouterExtras:
+    """Noise top-k input and routing-statistics outputs (device tensors or None)."""
+    ex = RouterExtras()
+    ex.noise, ex.noise_std = ptr(noise), float(noise_std)
+    ex.prob_sum, ex.gate_sum, ex.aux = ptr(prob_sum), ptr(gate_sum), ptr(aux)
+    return ex
 
 
 def router_workspace_size(router: RouterDesc, T: int) -> int:

@@ -418,7 +418,12 @@ size_t moe_router_workspace_size(const moe_router_desc* R, int64_t T) {
     c.take_n<int>(1);
     return c.used;
   }
-  return 0;
+  // dense: per-workgroup partial sums of the routing statistics (the f32
+  // router's 4-token workgroups bound the bf16 router's 16-token ones)
+  Carve c(nullptr);
+  c.take_n<float>(((T + 3) / 4) * R->E);
+  c.take_n<float>(((T + 3) / 4) * R->E);
+  return c.used;
 }
 
 namespace {
@@ -449,12 +454,38 @@ int check_router(const moe_router_desc* R, int dtype, int64_t T, int64_t d, int 
   return MOE_OK;
 }
 
+bool extras_requested(const moe_router_extras* ex) {
+  return ex && (ex->noise || ex->prob_sum || ex->gate_sum || ex->aux);
+}
+
+int check_extras(const moe_router_desc* R, int k, const moe_router_extras* ex) {
+  if (!extras_requested(ex)) return MOE_OK;
+  REQUIRE(R->kind == MOE_ROUTER_DENSE, MOE_EUNSUPPORTED,
+          "router noise / statistics are implemented for the dense router");
+  REQUIRE(k <= 64, MOE_EUNSUPPORTED, "router noise / statistics need k <= 64");
+  REQUIRE(std::isfinite(ex->noise_std), MOE_EINVAL, "noise_std must be finite");
+  return MOE_OK;
+}
+
 int router_run(const moe_router_desc* R, const void* x, int dtype, int64_t T, int64_t d,
                const float* r_in, float eps, float* r_out, int k, int renorm, int32_t* ids, float* w,
-               float* logits, void* ws, hipStream_t stream) {
+               float* logits, void* ws, hipStream_t stream, const moe_router_extras* extras) {
   if (R->kind == MOE_ROUTER_DENSE) {
+    RouterExtras ex;
+    if (extras) {
+      ex.noise = extras->noise;
+      ex.noise_std = extras->noise_std;
+      if (extras->prob_sum || extras->gate_sum || extras->aux) {
+        Carve c(ws);
+        ex.part_p = c.take_n<float>(((T + 3) / 4) * R->E);
+        ex.part_g = c.take_n<float>(((T + 3) / 4) * R->E);
+        ex.prob_sum = extras->prob_sum;
+        ex.gate_sum = extras->gate_sum;
+        ex.aux = extras->aux;
+      }
+    }
     MOE_HIP(launch_router_dense(x, dtype, T, d, R->wr_t, R->bias, R->E, r_in, eps, r_out, k, renorm,
-                                ids, w, logits, stream));
+                                ids, w, logits, ex, stream));
     return MOE_OK;
   }
   Carve c(ws);
@@ -504,7 +535,17 @@ int router_run(const moe_router_desc* R, const void* x, int dtype, int64_t T, in
 int moe_router_topk(const moe_router_desc* R, const void* x, int dtype, int64_t T, int64_t d,
                     const float* r_in, float eps, float* r_out, int k, int renorm, int32_t* ids,
                     float* w, float* logits, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return moe_router_topk_ex(R, x, dtype, T, d, r_in, eps, r_out, k, renorm, ids, w, logits, nullptr,
+                            ws, ws_bytes, stream);
+}
+
+int moe_router_topk_ex(const moe_router_desc* R, const void* x, int dtype, int64_t T, int64_t d,
+                       const float* r_in, float eps, float* r_out, int k, int renorm, int32_t* ids,
+                       float* w, float* logits, const moe_router_extras* extras, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
   int rc = check_router(R, dtype, T, d, k);
+  if (rc) return rc;
+  rc = check_extras(R, k, extras);
   if (rc) return rc;
   REQUIRE(T == 0 || (x && ids && w), MOE_EINVAL, "x, ids and w are required");
   REQUIRE(r_in || r_out || T == 0, MOE_EINVAL, "r_in or r_out is required");
@@ -514,7 +555,7 @@ int moe_router_topk(const moe_router_desc* R, const void* x, int dtype, int64_t 
   const size_t need = moe_router_workspace_size(R, T);
   REQUIRE(ws_bytes >= need && (need == 0 || ws), MOE_EWORKSPACE, "router workspace needs %zu bytes",
           need);
-  rc = router_run(R, x, dtype, T, d, r_in, eps, r_out, k, renorm, ids, w, logits, ws, stream);
+  rc = router_run(R, x, dtype, T, d, r_in, eps, r_out, k, renorm, ids, w, logits, ws, stream, extras);
   return rc ? rc : ok();
 }
 
@@ -742,6 +783,8 @@ int check_layer(const moe_layer_desc* L, int64_t T, ExpertGeo* g, ExpertGeo* gs)
   REQUIRE(T >= 0 && T < (int64_t(1) << 30), MOE_ESHAPE, "bad T");
   int rc = check_router(&L->router, L->dtype, T, L->d, L->k);
   if (rc) return rc;
+  rc = check_extras(&L->router, L->k, L->router_extras);
+  if (rc) return rc;
   rc = check_experts(&L->experts, L->dtype, L->d, g);
   if (rc) return rc;
   REQUIRE(L->experts.E == L->router.E, MOE_ESHAPE, "router E %lld != experts E %lld",
@@ -882,10 +925,10 @@ int moe_layer_forward(const moe_layer_desc* L, const void* x, int64_t T, void* o
     MOE_HIP(launch_rmsnorm(x, L->dtype, T, d, L->gamma, L->eps, w.r, w.xg, stream));
     xhat = w.xg;
     rc = router_run(&L->router, xhat, L->dtype, T, d, w.r, L->eps, nullptr, k, L->renorm, w.ids, w.w,
-                    w.logits, w.router_ws, stream);
+                    w.logits, w.router_ws, stream, L->router_extras);
   } else {
     rc = router_run(&L->router, xhat, L->dtype, T, d, nullptr, L->eps, w.r, k, L->renorm, w.ids, w.w,
-                    w.logits, w.router_ws, stream);
+                    w.logits, w.router_ws, stream, L->router_extras);
   }
   if (rc) return rc;
   timer_mark(tm, call, MOE_STAGE_ROUTER + 1, stream);

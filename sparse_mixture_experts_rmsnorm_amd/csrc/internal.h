@@ -66,10 +66,24 @@ hipError_t launch_pack_swiglu(const void* w1, const void* w3, int dtype, int64_t
 
 hipError_t launch_rmsnorm(const void* x, int dtype, int64_t T, int64_t d, const void* gamma,
                           float eps, float* r, void* xg, hipStream_t s);
+// Noise and statistics of the dense router (all nullable).  part_p /
+// part_g: per-workgroup partial sums [blocks][E] (workspace).
+struct RouterExtras {
+  const float* noise = nullptr;
+  float noise_std = 0.f;
+  float* part_p = nullptr;
+  float* part_g = nullptr;
+  float* prob_sum = nullptr;
+  float* gate_sum = nullptr;
+  float* aux = nullptr;
+};
+// Workgroups of the dense router launch for T tokens (the rows of the
+// partial-sum arrays).
+int64_t router_dense_blocks(int dtype, int64_t T);
 hipError_t launch_router_dense(const void* x, int dtype, int64_t T, int64_t d, const void* wr_t,
                                const float* bias, int64_t E, const float* r_in, float eps,
                                float* r_out, int k, int renorm, int32_t* ids, float* w,
-                               float* logits, hipStream_t s);
+                               float* logits, const RouterExtras& ex, hipStream_t s);
 hipError_t launch_cartesian_topk(const float* scores, int64_t T, int64_t Nr, int64_t Nc, int k,
                                  int renorm, int32_t* ids, float* w, hipStream_t s);
 

@@ -182,10 +182,13 @@ __device__ __forceinline__ uint32_t kth_largest_key_fast(const uint32_t (&u)[Q],
 // token t.  Selection by threshold: the k-th largest key, everything above
 // it and the lowest-index ties at it, compacted through the wave's LDS
 // slices (64 entries each); a winner's slot is its rank among the k.
+// pacc / gacc (the wave's LDS rows of n floats, or NULL) accumulate the
+// token's full-softmax probabilities and its gates per expert.
 template <int Q>
 __device__ void wave_select_gates(const float (&vals)[Q], int n, int k, int renorm, int64_t t,
                                   int32_t* __restrict__ ids, float* __restrict__ wout,
-                                  uint32_t* cand, float* selv, int* seli) {
+                                  uint32_t* cand, float* selv, int* seli, float* pacc = nullptr,
+                                  float* gacc = nullptr) {
   const int lane = threadIdx.x & 63;
   const uint64_t below = lanemask_lt();
   uint32_t u[Q];
@@ -238,10 +241,25 @@ __device__ void wave_select_gates(const float (&vals)[Q], int n, int k, int reno
       if (lane + 64 * q < n) den += expf(vals[q] - mx);
   }
   den = wave_sum(den);
+  const float gate = expf(sv - mx) / den;
   if (mine) {
     ids[t * k + rank] = si;
-    wout[t * k + rank] = expf(sv - mx) / den;
+    wout[t * k + rank] = gate;
   }
+  if (pacc) {
+    float zall = den;
+    if (renorm) {
+      float zz = 0.f;
+#pragma unroll
+      for (int q = 0; q < Q; ++q)
+        if (lane + 64 * q < n) zz += expf(vals[q] - mx);
+      zall = wave_sum(zz);
+    }
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+      if (lane + 64 * q < n) pacc[lane + 64 * q] += expf(vals[q] - mx) / zall;
+  }
+  if (gacc && mine) gacc[si] += gate;
 }
 
 // Gates of the k selections held as in wave_topk; writes ids / w of token t.
@@ -282,7 +300,7 @@ __global__ void __launch_bounds__(256) k_router_bf16(
     const uint16_t* __restrict__ x, int T, int d, const uint16_t* __restrict__ wr,
     const float* __restrict__ bias, int E, const float* __restrict__ r_in, float eps,
     float* __restrict__ r_out, int k, int renorm, int32_t* __restrict__ ids,
-    float* __restrict__ wout, float* __restrict__ logits) {
+    float* __restrict__ wout, float* __restrict__ logits, RouterExtras ex) {
   constexpr int QV = (NB * 16 + 63) / 64;   // logits per lane in the top-k
   __shared__ float lg[kRouterTok][NB * 16 + 1];
   __shared__ float ssq[kRouterTok];
@@ -290,6 +308,9 @@ __global__ void __launch_bounds__(256) k_router_bf16(
   __shared__ uint32_t cand_s[4][64];
   __shared__ float selv_s[4][64];
   __shared__ int seli_s[4][64];
+  __shared__ float pacc_s[4][NB * 16];
+  __shared__ float gacc_s[4][NB * 16];
+  const bool stats = ex.part_p != nullptr;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int t0 = blockIdx.x * kRouterTok;
   const int tl = lane & 15;       // token within the block (B column)
@@ -298,6 +319,8 @@ __global__ void __launch_bounds__(256) k_router_bf16(
   const bool tok_ok = t < T;
   const int kw = d / 4;           // K range of this wave
   const int kb = wid * kw;
+  if (stats)
+    for (int e = lane; e < NB * 16; e += 64) pacc_s[wid][e] = gacc_s[wid][e] = 0.f;
 
   f32x4 acc[NB];
 #pragma unroll
@@ -372,12 +395,14 @@ __global__ void __launch_bounds__(256) k_router_bf16(
       vals[qq] = -INFINITY;
       if (e < E) {
         vals[qq] = rr * lg[tl2][e] + (bias ? bias[e] : 0.f);
+        if (ex.noise) vals[qq] += ex.noise_std * ex.noise[int64_t(tt) * E + e];
         if (logits) logits[int64_t(tt) * E + e] = vals[qq];
       }
     }
     if (k <= 64) {
       wave_select_gates<QV>(vals, E, k, renorm, tt, ids, wout, cand_s[wid], selv_s[wid],
-                            seli_s[wid]);
+                            seli_s[wid], stats ? pacc_s[wid] : nullptr,
+                            stats ? gacc_s[wid] : nullptr);
     } else {
       float sv[QV];
       int si[QV];
@@ -385,6 +410,16 @@ __global__ void __launch_bounds__(256) k_router_bf16(
       write_gates<QV, QV>(sv, si, vals, E, k, renorm, tt, ids, wout);
     }
     __builtin_amdgcn_wave_barrier();
+  }
+  if (stats) {
+    // the workgroup's partial sums: waves combined in a fixed order
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256) {
+      ex.part_p[int64_t(blockIdx.x) * E + e] =
+          ((pacc_s[0][e] + pacc_s[1][e]) + pacc_s[2][e]) + pacc_s[3][e];
+      ex.part_g[int64_t(blockIdx.x) * E + e] =
+          ((gacc_s[0][e] + gacc_s[1][e]) + gacc_s[2][e]) + gacc_s[3][e];
+    }
   }
 }
 
@@ -409,28 +444,109 @@ __global__ void k_router_logits_f32(const float* __restrict__ x, int T, int d,
   lg[g] = rr * acc + (bias ? bias[e] : 0.f);
 }
 
-__global__ void __launch_bounds__(256) k_topk_rows(const float* __restrict__ lg, int T, int E, int k,
+__global__ void __launch_bounds__(256) k_topk_rows(float* __restrict__ lg, int T, int E, int k,
                                                    int renorm, int32_t* __restrict__ ids,
-                                                   float* __restrict__ wout) {
+                                                   float* __restrict__ wout, RouterExtras ex) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   __shared__ uint32_t cand_s[4][64];
   __shared__ float selv_s[4][64];
   __shared__ int seli_s[4][64];
+  __shared__ float pacc_s[4][256];
+  __shared__ float gacc_s[4][256];
+  const bool stats = ex.part_p != nullptr;
   const int t = blockIdx.x * 4 + wid;
-  if (t >= T) return;
-  float vals[4];
+  if (stats)
+    for (int e = lane; e < E; e += 64) pacc_s[wid][e] = gacc_s[wid][e] = 0.f;
+  if (t < T) {
+    float vals[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = lane + 64 * q;
-    vals[q] = e < E ? lg[int64_t(t) * E + e] : -INFINITY;
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane + 64 * q;
+      vals[q] = -INFINITY;
+      if (e < E) {
+        vals[q] = lg[int64_t(t) * E + e];
+        if (ex.noise) {
+          vals[q] += ex.noise_std * ex.noise[int64_t(t) * E + e];
+          lg[int64_t(t) * E + e] = vals[q];
+        }
+      }
+    }
+    if (k <= 64) {
+      wave_select_gates<4>(vals, E, k, renorm, t, ids, wout, cand_s[wid], selv_s[wid],
+                           seli_s[wid], stats ? pacc_s[wid] : nullptr,
+                           stats ? gacc_s[wid] : nullptr);
+    } else {
+      float sv[4];
+      int si[4];
+      wave_topk<4, 4>(vals, E, k, sv, si);
+      write_gates<4, 4>(sv, si, vals, E, k, renorm, t, ids, wout);
+    }
   }
-  if (k <= 64) {
-    wave_select_gates<4>(vals, E, k, renorm, t, ids, wout, cand_s[wid], selv_s[wid], seli_s[wid]);
-  } else {
-    float sv[4];
-    int si[4];
-    wave_topk<4, 4>(vals, E, k, sv, si);
-    write_gates<4, 4>(sv, si, vals, E, k, renorm, t, ids, wout);
+  if (stats) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256) {
+      ex.part_p[int64_t(blockIdx.x) * E + e] =
+          ((pacc_s[0][e] + pacc_s[1][e]) + pacc_s[2][e]) + pacc_s[3][e];
+      ex.part_g[int64_t(blockIdx.x) * E + e] =
+          ((gacc_s[0][e] + gacc_s[1][e]) + gacc_s[2][e]) + gacc_s[3][e];
+    }
+  }
+}
+
+// Routing statistics from the per-workgroup partial sums (one workgroup):
+// each expert's sums over workgroups in a fixed order, the slot count per
+// expert from the ids, and the squared coefficient of variation of the three.
+__global__ void __launch_bounds__(256) k_router_stats(const float* __restrict__ part_p,
+                                                      const float* __restrict__ part_g, int nblk,
+                                                      int E, const int32_t* __restrict__ ids,
+                                                      int64_t nids, float* __restrict__ prob_sum,
+                                                      float* __restrict__ gate_sum,
+                                                      float* __restrict__ aux) {
+  __shared__ float sp[256], sg[256], fp[256], fg[256];
+  __shared__ int hist[256];
+  const int tid = threadIdx.x;
+  int ep = 1;
+  while (ep < E) ep <<= 1;
+  const int R = 256 / ep;                      // threads per expert
+  const int e = tid % ep, rr = tid / ep;
+  float ap = 0.f, ag = 0.f;
+  if (e < E)
+    for (int b = rr; b < nblk; b += R) {
+      ap += part_p[int64_t(b) * E + e];
+      ag += part_g[int64_t(b) * E + e];
+    }
+  sp[tid] = ap;
+  sg[tid] = ag;
+  hist[tid] = 0;
+  __syncthreads();
+  for (int64_t i = tid; i < nids; i += 256) {
+    const int x = ids[i];
+    if (x >= 0 && x < E) atomicAdd(&hist[x], 1);
+  }
+  if (tid < E) {
+    float P = 0.f, G = 0.f;
+    for (int r = 0; r < R; ++r) {
+      P += sp[r * ep + tid];
+      G += sg[r * ep + tid];
+    }
+    fp[tid] = P;
+    fg[tid] = G;
+    if (prob_sum) prob_sum[tid] = P;
+    if (gate_sum) gate_sum[tid] = G;
+  }
+  __syncthreads();
+  if (tid == 0 && aux) {
+    for (int which = 0; which < 3; ++which) {
+      double s1 = 0.0;
+      for (int i = 0; i < E; ++i) s1 += which == 0 ? fp[i] : which == 1 ? fg[i] : double(hist[i]);
+      const double mean = s1 / E;
+      double s2 = 0.0;
+      for (int i = 0; i < E; ++i) {
+        const double v = (which == 0 ? fp[i] : which == 1 ? fg[i] : double(hist[i])) - mean;
+        s2 += v * v;
+      }
+      aux[which] = mean != 0.0 ? float((s2 / E) / (mean * mean)) : __int_as_float(0x7fc00000);
+    }
   }
 }
 
@@ -610,10 +726,14 @@ hipError_t launch_rmsnorm(const void* x, int dtype, int64_t T, int64_t d, const 
   return hipGetLastError();
 }
 
+int64_t router_dense_blocks(int dtype, int64_t T) {
+  return dtype == 0 ? (T + 3) / 4 : (T + kRouterTok - 1) / kRouterTok;
+}
+
 hipError_t launch_router_dense(const void* x, int dtype, int64_t T, int64_t d, const void* wr_t,
                                const float* bias, int64_t E, const float* r_in, float eps,
                                float* r_out, int k, int renorm, int32_t* ids, float* w,
-                               float* logits, hipStream_t s) {
+                               float* logits, const RouterExtras& ex, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (dtype == 0) {
     // fp32: logits into the caller's buffer (required), then top-k per row
@@ -622,21 +742,25 @@ hipError_t launch_router_dense(const void* x, int dtype, int64_t T, int64_t d, c
                        static_cast<const float*>(x), int(T), int(d),
                        static_cast<const float*>(wr_t), bias, int(E), r_in, eps, r_out, logits);
     hipLaunchKernelGGL(k_topk_rows, dim3(unsigned((T + 3) / 4)), dim3(256), 0, s, logits, int(T),
-                       int(E), k, renorm, ids, w);
-    return hipGetLastError();
-  }
-  const dim3 g(unsigned((T + kRouterTok - 1) / kRouterTok));
-  const int nb = int((E + 15) / 16);
-#define MOE_ROUTER_CASE(NBV)                                                                     \
-  hipLaunchKernelGGL(k_router_bf16<NBV>, g, dim3(256), 0, s, static_cast<const uint16_t*>(x),     \
-                     int(T), int(d), static_cast<const uint16_t*>(wr_t), bias, int(E), r_in, eps, \
-                     r_out, k, renorm, ids, w, logits)
-  if (nb <= 1) MOE_ROUTER_CASE(1);
-  else if (nb <= 2) MOE_ROUTER_CASE(2);
-  else if (nb <= 4) MOE_ROUTER_CASE(4);
-  else if (nb <= 8) MOE_ROUTER_CASE(8);
-  else MOE_ROUTER_CASE(16);
+                       int(E), k, renorm, ids, w, ex);
+  } else {
+    const dim3 g(unsigned((T + kRouterTok - 1) / kRouterTok));
+    const int nb = int((E + 15) / 16);
+#define MOE_ROUTER_CASE(NBV)                                                                   \
+    hipLaunchKernelGGL(k_router_bf16<NBV>, g, dim3(256), 0, s, static_cast<const uint16_t*>(x),   \
+                       int(T), int(d), static_cast<const uint16_t*>(wr_t), bias, int(E), r_in,     \
+                       eps, r_out, k, renorm, ids, w, logits, ex)
+    if (nb <= 1) MOE_ROUTER_CASE(1);
+    else if (nb <= 2) MOE_ROUTER_CASE(2);
+    else if (nb <= 4) MOE_ROUTER_CASE(4);
+    else if (nb <= 8) MOE_ROUTER_CASE(8);
+    else MOE_ROUTER_CASE(16);
 #undef MOE_ROUTER_CASE
+  }
+  if (ex.part_p)
+    hipLaunchKernelGGL(k_router_stats, dim3(1), dim3(256), 0, s, ex.part_p, ex.part_g,
+                       int(router_dense_blocks(dtype, T)), int(E), ids, T * k, ex.prob_sum,
+                       ex.gate_sum, ex.aux);
   return hipGetLastError();
 }
 

@@ -131,7 +131,7 @@ class MoELayer:
         return torch.empty(self.workspace_size(T), dtype=torch.uint8, device=self.device)
 
     def forward(self, x, out=None, ws=None, stats=None, timer: B.StageTimer | None = None,
-                stream=None):
+                stream=None, router_extras: B.RouterExtras | None = None):
         import torch
         T = x.shape[0]
         if out is None:
@@ -139,12 +139,15 @@ class MoELayer:
         if ws is None:
             ws = self.alloc_workspace(T)
         self.desc.timer = None if timer is None else timer.handle
+        if router_extras is not None:
+            self.desc.router_extras = C.pointer(router_extras)
         try:
             B.check(B.lib().moe_layer_forward(C.byref(self.desc), B.ptr(x), T, B.ptr(out),
                                               B.ptr(stats), B.ptr(ws), ws.numel(),
                                               B.stream_handle(stream)))
         finally:
             self.desc.timer = None
+            self.desc.router_extras = None
         return out
 
     def routing(self, T: int, ws) -> dict:

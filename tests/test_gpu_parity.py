@@ -357,3 +357,106 @@ def test_dense_topk_ties(dev, E, k, renorm, T):
     sel = O.select_topk(lg, k)
     assert np.array_equal(ids.cpu().numpy(), sel)
     assert rel_err(w.cpu().numpy(), O.gates(lg.astype(np.float64), sel, renorm)) < 1e-5
+
+
+def _dense_router(dev, E, d, dtype, seed):
+    rng = np.random.default_rng(seed)
+    wr = (rng.standard_normal((d, E)) * 0.05).astype(np.float32)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    wr_t = torch.empty((E, d), dtype=tdt, device=dev)
+    B.pack_transpose(torch.from_numpy(wr).to(dev).to(tdt), wr_t)
+    R = B.RouterDesc()
+    R.kind, R.E, R.wr_t = B.ROUTER_DENSE, E, wr_t.data_ptr()
+    return R, wr_t, rng, tdt
+
+
+@pytest.mark.parametrize("dtype,E,k,renorm,noisy", [
+    ("bf16", 8, 2, 1, False), ("bf16", 8, 2, 1, True), ("bf16", 64, 6, 0, True),
+    ("bf16", 160, 40, 1, True), ("f32", 24, 3, 1, True), ("f32", 24, 3, 0, False)])
+def test_router_stats_and_noise(dev, dtype, E, k, renorm, noisy):
+    """Noise top-k and the routing statistics against the oracle on the GPU's
+    own (noisy) logits; the statistics are bit-identical run to run."""
+    _say(f"[gpu] router statistics dtype={dtype} E={E} k={k} renorm={renorm} noise={noisy}")
+    T, d = 1000, 256
+    R, keep, rng, tdt = _dense_router(dev, E, d, dtype, 5000 + E + k)
+    x = torch.from_numpy(rng.standard_normal((T, d)).astype(np.float32)).to(dev).to(tdt)
+    noise = torch.from_numpy(rng.standard_normal((T, E)).astype(np.float32)).to(dev) if noisy else None
+    std = 0.7 if noisy else 0.0
+    ws = torch.empty(max(B.router_workspace_size(R, T), 1), dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+
+    def run(with_noise):
+        logits = torch.empty((T, E), **f32)
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        w = torch.empty((T, k), **f32)
+        r = torch.empty(T, **f32)
+        ps, gs, aux = torch.empty(E, **f32), torch.empty(E, **f32), torch.empty(3, **f32)
+        ex = B.router_extras(noise=noise if with_noise else None, noise_std=std, prob_sum=ps,
+                             gate_sum=gs, aux=aux)
+        B.router_topk(R, x, k, renorm, ids, w, r_out=r, logits=logits, ws=ws, extras=ex)
+        torch.cuda.synchronize()
+        return [t.cpu().numpy() for t in (logits, ids, w, ps, gs, aux)]
+
+    lg, ids, w, ps, gs, aux = run(noisy)
+    if noisy:
+        clean = run(False)[0]
+        assert rel_err(lg, clean.astype(np.float64) + std * noise.cpu().numpy()) < 1e-6
+    assert np.array_equal(ids, O.select_topk(lg, k))
+    assert rel_err(w, O.gates(lg.astype(np.float64), ids, renorm)) < 1e-5
+    st = O.router_stats(lg.astype(np.float64), ids, w, np.bincount(ids.ravel(), minlength=E))
+    assert rel_err(ps, st["prob_sum"]) < 1e-5
+    assert rel_err(gs, st["gate_sum"]) < 1e-5
+    assert np.allclose(aux, st["aux"], rtol=1e-4, atol=1e-6), (aux, st["aux"])
+    again = run(noisy)
+    for a, b in zip((ps, gs, aux), again[3:]):
+        assert np.array_equal(a, b)
+
+
+def test_router_extras_rejected(dev):
+    _say("[gpu] router extras: unsupported requests")
+    T, d, E = 64, 256, 8
+    R, keep, rng, tdt = _dense_router(dev, E, d, "bf16", 1)
+    x = torch.zeros((T, d), dtype=tdt, device=dev)
+    ids = torch.empty((T, E), dtype=torch.int32, device=dev)
+    w = torch.empty((T, E), dtype=torch.float32, device=dev)
+    r = torch.empty(T, dtype=torch.float32, device=dev)
+    aux = torch.empty(3, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(B.router_workspace_size(R, T), 1), dtype=torch.uint8, device=dev)
+    ex = B.router_extras(aux=aux, noise_std=float("nan"))
+    with pytest.raises(B.MoeError):
+        B.router_topk(R, x, 2, 1, ids, w, r_out=r, ws=ws, extras=ex)
+
+
+def test_layer_router_extras(dev):
+    """The layer forward with noise and statistics: its routing equals the
+    router's own on the same noisy logits, and the statistics match it."""
+    _say("[gpu] layer forward with router noise and statistics")
+    wl, inp, params, layer = _setup("mixtral_small", dev)
+    x = params["x"]
+    T, E = wl.T, wl.E
+    g = torch.Generator(device=dev).manual_seed(3)
+    noise = torch.randn((T, E), generator=g, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    ps, gs, aux = torch.empty(E, **f32), torch.empty(E, **f32), torch.empty(3, **f32)
+    ex = B.router_extras(noise=noise, noise_std=0.5, prob_sum=ps, gate_sum=gs, aux=aux)
+    ws = layer.alloc_workspace(T)
+    layer.forward(x, ws=ws, router_extras=ex)
+    torch.cuda.synchronize()
+    rt = layer.routing(T, ws)
+    ids, w = rt["ids"].cpu().numpy(), rt["w"].cpu().numpy()
+    # the router alone, same noise, with its logits
+    logits = torch.empty((T, E), **f32)
+    ids2 = torch.empty_like(rt["ids"])
+    w2 = torch.empty_like(rt["w"])
+    rws = torch.empty(max(B.router_workspace_size(layer.desc.router, T), 1), dtype=torch.uint8,
+                      device=dev)
+    B.router_topk(layer.desc.router, x, wl.k, wl.renorm, ids2, w2, r_in=rt["r"], logits=logits,
+                  ws=rws, extras=B.router_extras(noise=noise, noise_std=0.5))
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy()
+    assert np.array_equal(ids2.cpu().numpy(), ids)
+    assert np.array_equal(ids, O.select_topk(lg, wl.k))
+    st = O.router_stats(lg.astype(np.float64), ids, w, np.bincount(ids.ravel(), minlength=E))
+    assert rel_err(ps.cpu().numpy(), st["prob_sum"]) < 1e-5
+    assert rel_err(gs.cpu().numpy(), st["gate_sum"]) < 1e-5
+    assert np.allclose(aux.cpu().numpy(), st["aux"], rtol=1e-4, atol=1e-6)
