@@ -30,11 +30,11 @@ PEAK_HBM_GBPS = 8000.0
 # from two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)
 # scaled by what the same counters read for a plain 1 GiB device copy
 # (bench.py --copy-calibration).  Valid only for the kernel source it was
-# taken on: any change to gemm.hip or internal.h reports null.
+# taken on: any change to gemm.hip, gemm_args.h or common.h reports null.
 TRAFFIC = {
     "workload": "mixtral_bf16",
-    "source_sha256": "b5e8b90d6f78cc49bc100df5d260f1d313ba117ed05930c2e7ecadb78335a95f",
-    "fetch_kib": 1885557.0, "write_kib": 229511.4,
+    "source_sha256": "f96c9ab6daf8f20ec49cb3c2efe1d92b3b29ea3002c8a64a9c0e840eb2dddee9",
+    "fetch_kib": 1888629.7, "write_kib": 229522.2,
     "fetch_scale": 1048576.0 / 524302.4, "write_scale": 1048576.0 / 1048576.0,
 }
 
@@ -42,7 +42,7 @@ TRAFFIC = {
 def gemm_source_sha256():
     import hashlib
     h = hashlib.sha256()
-    for f in ("gemm.hip", "internal.h"):
+    for f in ("gemm.hip", "gemm_args.h", "common.h"):
         with open(os.path.join(ROOT, "sparse_mixture_experts_rmsnorm_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
