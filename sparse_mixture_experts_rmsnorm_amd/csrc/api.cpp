@@ -423,6 +423,7 @@ size_t moe_router_workspace_size(const moe_router_desc* R, int64_t T) {
   Carve c(nullptr);
   c.take_n<float>(((T + 3) / 4) * R->E);
   c.take_n<float>(((T + 3) / 4) * R->E);
+  c.take_n<int>(((T + 3) / 4) * R->E);
   return c.used;
 }
 
@@ -479,6 +480,7 @@ int router_run(const moe_router_desc* R, const void* x, int dtype, int64_t T, in
         Carve c(ws);
         ex.part_p = c.take_n<float>(((T + 3) / 4) * R->E);
         ex.part_g = c.take_n<float>(((T + 3) / 4) * R->E);
+        ex.part_c = c.take_n<int>(((T + 3) / 4) * R->E);
         ex.prob_sum = extras->prob_sum;
         ex.gate_sum = extras->gate_sum;
         ex.aux = extras->aux;

@@ -17,12 +17,13 @@ hipError_t launch_pack_swiglu(const void* w1, const void* w3, int dtype, int64_t
 hipError_t launch_rmsnorm(const void* x, int dtype, int64_t T, int64_t d, const void* gamma,
                           float eps, float* r, void* xg, hipStream_t s);
 // Noise and statistics of the dense router (all nullable).  part_p /
-// part_g: per-workgroup partial sums [blocks][E] (workspace).
+// part_g / part_c: per-workgroup partial sums [blocks][E] (workspace).
 struct RouterExtras {
   const float* noise = nullptr;
   float noise_std = 0.f;
   float* part_p = nullptr;
   float* part_g = nullptr;
+  int* part_c = nullptr;
   float* prob_sum = nullptr;
   float* gate_sum = nullptr;
   float* aux = nullptr;

@@ -182,13 +182,13 @@ __device__ __forceinline__ uint32_t kth_largest_key_fast(const uint32_t (&u)[Q],
 // token t.  Selection by threshold: the k-th largest key, everything above
 // it and the lowest-index ties at it, compacted through the wave's LDS
 // slices (64 entries each); a winner's slot is its rank among the k.
-// pacc / gacc (the wave's LDS rows of n floats, or NULL) accumulate the
-// token's full-softmax probabilities and its gates per expert.
+// pacc / gacc / cacc (the wave's LDS rows of n, or NULL) accumulate the
+// token's full-softmax probabilities, its gates and its slots per expert.
 template <int Q>
 __device__ void wave_select_gates(const float (&vals)[Q], int n, int k, int renorm, int64_t t,
                                   int32_t* __restrict__ ids, float* __restrict__ wout,
                                   uint32_t* cand, float* selv, int* seli, float* pacc = nullptr,
-                                  float* gacc = nullptr) {
+                                  float* gacc = nullptr, int* cacc = nullptr) {
   const int lane = threadIdx.x & 63;
   const uint64_t below = lanemask_lt();
   uint32_t u[Q];
@@ -259,7 +259,10 @@ __device__ void wave_select_gates(const float (&vals)[Q], int n, int k, int reno
     for (int q = 0; q < Q; ++q)
       if (lane + 64 * q < n) pacc[lane + 64 * q] += expf(vals[q] - mx) / zall;
   }
-  if (gacc && mine) gacc[si] += gate;
+  if (gacc && mine) {
+    gacc[si] += gate;
+    cacc[si] += 1;
+  }
 }
 
 // Gates of the k selections held as in wave_topk; writes ids / w of token t.
@@ -310,6 +313,7 @@ __global__ void __launch_bounds__(256) k_router_bf16(
   __shared__ int seli_s[4][64];
   __shared__ float pacc_s[4][NB * 16];
   __shared__ float gacc_s[4][NB * 16];
+  __shared__ int cacc_s[4][NB * 16];
   const bool stats = ex.part_p != nullptr;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int t0 = blockIdx.x * kRouterTok;
@@ -320,7 +324,10 @@ __global__ void __launch_bounds__(256) k_router_bf16(
   const int kw = d / 4;           // K range of this wave
   const int kb = wid * kw;
   if (stats)
-    for (int e = lane; e < NB * 16; e += 64) pacc_s[wid][e] = gacc_s[wid][e] = 0.f;
+    for (int e = lane; e < NB * 16; e += 64) {
+      pacc_s[wid][e] = gacc_s[wid][e] = 0.f;
+      cacc_s[wid][e] = 0;
+    }
 
   f32x4 acc[NB];
 #pragma unroll
@@ -402,7 +409,7 @@ __global__ void __launch_bounds__(256) k_router_bf16(
     if (k <= 64) {
       wave_select_gates<QV>(vals, E, k, renorm, tt, ids, wout, cand_s[wid], selv_s[wid],
                             seli_s[wid], stats ? pacc_s[wid] : nullptr,
-                            stats ? gacc_s[wid] : nullptr);
+                            stats ? gacc_s[wid] : nullptr, stats ? cacc_s[wid] : nullptr);
     } else {
       float sv[QV];
       int si[QV];
@@ -419,6 +426,7 @@ __global__ void __launch_bounds__(256) k_router_bf16(
           ((pacc_s[0][e] + pacc_s[1][e]) + pacc_s[2][e]) + pacc_s[3][e];
       ex.part_g[int64_t(blockIdx.x) * E + e] =
           ((gacc_s[0][e] + gacc_s[1][e]) + gacc_s[2][e]) + gacc_s[3][e];
+      ex.part_c[int64_t(blockIdx.x) * E + e] = cacc_s[0][e] + cacc_s[1][e] + cacc_s[2][e] + cacc_s[3][e];
     }
   }
 }
@@ -453,10 +461,14 @@ __global__ void __launch_bounds__(256) k_topk_rows(float* __restrict__ lg, int T
   __shared__ int seli_s[4][64];
   __shared__ float pacc_s[4][256];
   __shared__ float gacc_s[4][256];
+  __shared__ int cacc_s[4][256];
   const bool stats = ex.part_p != nullptr;
   const int t = blockIdx.x * 4 + wid;
   if (stats)
-    for (int e = lane; e < E; e += 64) pacc_s[wid][e] = gacc_s[wid][e] = 0.f;
+    for (int e = lane; e < E; e += 64) {
+      pacc_s[wid][e] = gacc_s[wid][e] = 0.f;
+      cacc_s[wid][e] = 0;
+    }
   if (t < T) {
     float vals[4];
 #pragma unroll
@@ -474,7 +486,7 @@ __global__ void __launch_bounds__(256) k_topk_rows(float* __restrict__ lg, int T
     if (k <= 64) {
       wave_select_gates<4>(vals, E, k, renorm, t, ids, wout, cand_s[wid], selv_s[wid],
                            seli_s[wid], stats ? pacc_s[wid] : nullptr,
-                           stats ? gacc_s[wid] : nullptr);
+                           stats ? gacc_s[wid] : nullptr, stats ? cacc_s[wid] : nullptr);
     } else {
       float sv[4];
       int si[4];
@@ -489,64 +501,64 @@ __global__ void __launch_bounds__(256) k_topk_rows(float* __restrict__ lg, int T
           ((pacc_s[0][e] + pacc_s[1][e]) + pacc_s[2][e]) + pacc_s[3][e];
       ex.part_g[int64_t(blockIdx.x) * E + e] =
           ((gacc_s[0][e] + gacc_s[1][e]) + gacc_s[2][e]) + gacc_s[3][e];
+      ex.part_c[int64_t(blockIdx.x) * E + e] = cacc_s[0][e] + cacc_s[1][e] + cacc_s[2][e] + cacc_s[3][e];
     }
   }
 }
 
 // Routing statistics from the per-workgroup partial sums (one workgroup):
-// each expert's sums over workgroups in a fixed order, the slot count per
-// expert from the ids, and the squared coefficient of variation of the three.
+// each expert's sums over workgroups in a fixed order and the squared
+// coefficient of variation of the probability sums, gate sums and slot counts.
 __global__ void __launch_bounds__(256) k_router_stats(const float* __restrict__ part_p,
-                                                      const float* __restrict__ part_g, int nblk,
-                                                      int E, const int32_t* __restrict__ ids,
-                                                      int64_t nids, float* __restrict__ prob_sum,
+                                                      const float* __restrict__ part_g,
+                                                      const int* __restrict__ part_c, int nblk,
+                                                      int E, float* __restrict__ prob_sum,
                                                       float* __restrict__ gate_sum,
                                                       float* __restrict__ aux) {
   __shared__ float sp[256], sg[256], fp[256], fg[256];
-  __shared__ int hist[256];
+  __shared__ long long sc[256], fc[256];
   const int tid = threadIdx.x;
   int ep = 1;
   while (ep < E) ep <<= 1;
   const int R = 256 / ep;                      // threads per expert
   const int e = tid % ep, rr = tid / ep;
   float ap = 0.f, ag = 0.f;
+  long long ac = 0;
   if (e < E)
     for (int b = rr; b < nblk; b += R) {
       ap += part_p[int64_t(b) * E + e];
       ag += part_g[int64_t(b) * E + e];
+      ac += part_c[int64_t(b) * E + e];
     }
   sp[tid] = ap;
   sg[tid] = ag;
-  hist[tid] = 0;
+  sc[tid] = ac;
   __syncthreads();
-  for (int64_t i = tid; i < nids; i += 256) {
-    const int x = ids[i];
-    if (x >= 0 && x < E) atomicAdd(&hist[x], 1);
-  }
   if (tid < E) {
     float P = 0.f, G = 0.f;
+    long long Cn = 0;
     for (int r = 0; r < R; ++r) {
       P += sp[r * ep + tid];
       G += sg[r * ep + tid];
+      Cn += sc[r * ep + tid];
     }
     fp[tid] = P;
     fg[tid] = G;
+    fc[tid] = Cn;
     if (prob_sum) prob_sum[tid] = P;
     if (gate_sum) gate_sum[tid] = G;
   }
   __syncthreads();
-  if (tid == 0 && aux) {
-    for (int which = 0; which < 3; ++which) {
-      double s1 = 0.0;
-      for (int i = 0; i < E; ++i) s1 += which == 0 ? fp[i] : which == 1 ? fg[i] : double(hist[i]);
-      const double mean = s1 / E;
-      double s2 = 0.0;
-      for (int i = 0; i < E; ++i) {
-        const double v = (which == 0 ? fp[i] : which == 1 ? fg[i] : double(hist[i])) - mean;
-        s2 += v * v;
-      }
-      aux[which] = mean != 0.0 ? float((s2 / E) / (mean * mean)) : __int_as_float(0x7fc00000);
+  if (tid < 3 && aux) {
+    double s1 = 0.0;
+    for (int i = 0; i < E; ++i) s1 += tid == 0 ? fp[i] : tid == 1 ? fg[i] : double(fc[i]);
+    const double mean = s1 / E;
+    double s2 = 0.0;
+    for (int i = 0; i < E; ++i) {
+      const double v = (tid == 0 ? fp[i] : tid == 1 ? fg[i] : double(fc[i])) - mean;
+      s2 += v * v;
     }
+    aux[tid] = mean != 0.0 ? float((s2 / E) / (mean * mean)) : __int_as_float(0x7fc00000);
   }
 }
 
@@ -758,9 +770,9 @@ hipError_t launch_router_dense(const void* x, int dtype, int64_t T, int64_t d, c
 #undef MOE_ROUTER_CASE
   }
   if (ex.part_p)
-    hipLaunchKernelGGL(k_router_stats, dim3(1), dim3(256), 0, s, ex.part_p, ex.part_g,
-                       int(router_dense_blocks(dtype, T)), int(E), ids, T * k, ex.prob_sum,
-                       ex.gate_sum, ex.aux);
+    hipLaunchKernelGGL(k_router_stats, dim3(1), dim3(256), 0, s, ex.part_p, ex.part_g, ex.part_c,
+                       int(router_dense_blocks(dtype, T)), int(E), ex.prob_sum, ex.gate_sum,
+                       ex.aux);
   return hipGetLastError();
 }
 
