@@ -83,7 +83,10 @@ enum { MOE_ACT_GELU = 0, MOE_ACT_GELU_TANH = 1, MOE_ACT_SWIGLU = 2 };
 enum { MOE_ROUTER_DENSE = 0, MOE_ROUTER_CARTESIAN = 1 };
 enum { MOE_EXPERTS_GROUPED = 0, MOE_EXPERTS_BCSR = 1, MOE_EXPERTS_ATOMIC = 2 };
 
-/* Counters written by moe_dispatch (device memory, overwritten each call). */
+/* Counters written by moe_dispatch (device memory, overwritten each call).
+ * A layer of ATOMIC experts runs no dispatch: it writes rows = T*k slots,
+ * dropped = 0, max_load = -1 (not counted) and errors = 0 (its Cartesian
+ * router produces ids in range by construction). */
 typedef struct moe_stats {
   int32_t rows;      /* permuted rows in use: offsets[E]                     */
   int32_t dropped;   /* (token, slot) assignments over capacity              */
@@ -304,8 +307,12 @@ int moe_build_topology(const int32_t* offsets, const int32_t* size_blocks,
  *   y[row] = row_w[row] * FFN_e(row_r[row] * x_perm[row]) for rows in use
  *   (the gate and r epilogues; rows past offsets[E] are not written).
  * ATOMIC: x_in = xhat [T, d]; y = routed [T, d],
- *   routed[t] = sum_j w[t,j] * act(r[t] xhat[t].W[n]) V[n], n = ids[t,j].
- * Hidden activations live in the workspace. */
+ *   routed[t] = sum_j w[t,j] * act(r[t] xhat[t].W[n]) V[n], n = ids[t,j],
+ *   summed in slot order.  With the dispatch's task list (row_expert, sorted
+ *   by expert as OmniMoE 2.2 schedules it) the two-phase expert-centric
+ *   form runs; with row_expert NULL the single-pass token-centric form runs
+ *   from ids, w and r alone (moe_layer_forward uses it).  Both give the same
+ *   bits.  Hidden activations live in the workspace. */
 size_t moe_expert_workspace_size(const moe_experts_desc* X, int dtype, int64_t d,
                                  int64_t T, int k, int64_t rows_max);
 int moe_expert_gemm(const moe_experts_desc* X, int dtype, int64_t d, const moe_routing* rt,

@@ -661,16 +661,20 @@ int moe_expert_gemm(const moe_experts_desc* X, int dtype, int64_t d, const moe_r
           (long long)X->E);
   REQUIRE(rt->T >= 0 && rt->k >= 1 && rt->rows_max >= 0 && rt->rows_max < (int64_t(1) << 31),
           MOE_ESHAPE, "bad routing sizes");
-  REQUIRE(x_in && y && rt->offsets && rt->row_r && rt->row_w, MOE_EINVAL, "NULL pointer");
+  if (g.atomic && !rt->row_expert)
+    REQUIRE(x_in && y && rt->ids && rt->w && rt->r, MOE_EINVAL,
+            "token-centric atomic experts need ids, w and r");
+  else
+    REQUIRE(x_in && y && rt->offsets && rt->row_r && rt->row_w, MOE_EINVAL, "NULL pointer");
   if (g.bcsr) {
     REQUIRE(rt->pad == 128, MOE_ESHAPE, "BCSR experts need a dispatch padded to 128");
     REQUIRE(X->row_offsets && X->column_indices, MOE_EINVAL, "BCSR needs the topology");
     REQUIRE(rt->rows_max % 128 == 0, MOE_ESHAPE, "BCSR rows_max must be a multiple of 128");
     REQUIRE(rt->rows_max / 128 <= 4096, MOE_EUNSUPPORTED, "BCSR supports at most 4096 token blocks");
   }
-  if (g.atomic)
-    REQUIRE(rt->ids && rt->pos && rt->row_token && rt->row_expert, MOE_EINVAL,
-            "atomic experts need ids, pos, row_token and row_expert");
+  if (g.atomic && rt->row_expert)
+    REQUIRE(rt->ids && rt->pos && rt->row_token, MOE_EINVAL,
+            "expert-centric atomic experts need ids, pos, row_token and row_expert");
   const size_t need = moe_expert_workspace_size(X, dtype, d, rt->T, rt->k, rt->rows_max);
   REQUIRE(ws && ws_bytes >= need, MOE_EWORKSPACE, "expert workspace needs %zu bytes", need);
   Carve c(ws);
@@ -693,10 +697,13 @@ int moe_expert_gemm(const moe_experts_desc* X, int dtype, int64_t d, const moe_r
     a.row_expert = rt->row_expert;
     a.row_r = rt->row_r;
     a.row_w = rt->row_w;
-    a.rows_used = rt->offsets + rt->E;
+    a.rows_used = rt->offsets ? rt->offsets + rt->E : nullptr;
     a.rows = rt->rows_max;
     a.a_rows = w.a_rows;
     a.routed = y;
+    a.token_centric = rt->row_expert ? 0 : 1;
+    a.w_tok = rt->w;
+    a.r_tok = rt->r;
     MOE_HIP(launch_atomic(a, stream));
     return ok();
   }
@@ -935,9 +942,12 @@ int moe_layer_forward(const moe_layer_desc* L, const void* x, int64_t T, void* o
   if (rc) return rc;
   timer_mark(tm, call, MOE_STAGE_ROUTER + 1, stream);
 
-  // 3. capacity + dispatch
+  // 3. capacity + dispatch (atomic experts read the routing by token and need
+  // no task list: only their slot counters are written)
   moe_stats* st = stats ? stats : w.stats;
-  {
+  if (g.atomic) {
+    MOE_HIP(launch_slot_stats(T * k, st, stream));
+  } else {
     DispatchArgs a{};
     a.ids = w.ids;
     a.w = w.w;
@@ -982,13 +992,10 @@ int moe_layer_forward(const moe_layer_desc* L, const void* x, int64_t T, void* o
     a.ids = w.ids;
     a.pos = w.pos;
     a.row_token = w.row_token;
-    a.row_expert = w.row_expert;
-    a.row_r = w.row_r;
-    a.row_w = w.row_w;
-    a.rows_used = w.offsets + E;
-    a.rows = w.rows_max;
-    a.a_rows = w.ex.a_rows;
     a.routed = w.y;
+    a.token_centric = 1;
+    a.w_tok = w.w;
+    a.r_tok = w.r;
     MOE_HIP(launch_atomic(a, stream));
     timer_mark(tm, call, MOE_STAGE_GEMM1 + 1, stream);
     timer_mark(tm, call, MOE_STAGE_GEMM2 + 1, stream);

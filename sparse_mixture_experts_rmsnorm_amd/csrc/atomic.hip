@@ -22,6 +22,12 @@ namespace {
 
 constexpr int kTasksPerWave = 16;
 
+// Tasks (phase 1) or slots (phase 2) whose rows are in flight together: the
+// row loads of a batch are all issued before any is used, so a wave keeps
+// NB * 2 KB (d = 1024) of gathers outstanding instead of one row.
+template <int CH>
+constexpr int batch_of() { return CH >= 8 ? 1 : 8 / CH; }
+
 // CH = d / 512 16-byte chunks per lane (bf16), d in {512, 1024, 2048, 4096}.
 template <int CH>
 __global__ void __launch_bounds__(256) k_atomic_phase1(
@@ -29,45 +35,61 @@ __global__ void __launch_bounds__(256) k_atomic_phase1(
     const int32_t* __restrict__ rows_used, const int32_t* __restrict__ row_token,
     const int32_t* __restrict__ row_expert, const float* __restrict__ row_r,
     const float* __restrict__ row_w, int act, float* __restrict__ a_rows) {
+  constexpr int NB = batch_of<CH>();
   const int rows = *rows_used;
   const int lane = threadIdx.x & 63;
   const int64_t first = (int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6)) * kTasksPerWave;
   if (first >= rows) return;
-  const int nvec = d / 8;
-  int cur = -1;
-  u32x4 wv[CH];
-  for (int i = 0; i < kTasksPerWave; ++i) {
-    const int64_t row = first + i;
-    if (row >= rows) break;
-    const int n = row_expert[row];
-    const int t = row_token[row];
-    if (n < 0 || t < 0) {
-      if (lane == 0) a_rows[row] = 0.f;
-      continue;
-    }
-    if (n != cur) {
-      const u32x4* ws = reinterpret_cast<const u32x4*>(W + int64_t(n) * d);
+  for (int i0 = 0; i0 < kTasksPerWave; i0 += NB) {
+    u32x4 wv[NB][CH], xv[NB][CH];
+    bool live[NB];
 #pragma unroll
-      for (int c = 0; c < CH; ++c) wv[c] = ws[lane + 64 * c];
-      cur = n;
-    }
-    const uint4* xs = reinterpret_cast<const uint4*>(xhat + int64_t(t) * d);
-    float dot = 0.f;
+    for (int b = 0; b < NB; ++b) {
+      const int64_t row = first + i0 + b;
+      const int n = row < rows ? row_expert[row] : -1;
+      const int t = row < rows ? row_token[row] : -1;
+      live[b] = n >= 0 && t >= 0;
+      const u32x4* ws = reinterpret_cast<const u32x4*>(W + int64_t(live[b] ? n : 0) * d);
+      const u32x4* xs = reinterpret_cast<const u32x4*>(xhat + int64_t(live[b] ? t : 0) * d);
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      float xf[8], wf[8];
-      unpack16(xs[lane + 64 * c], xf, (const uint16_t*)nullptr);
-      unpack16(make_uint4(wv[c].x, wv[c].y, wv[c].z, wv[c].w), wf, (const uint16_t*)nullptr);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) dot = fmaf(xf[q], wf[q], dot);
+      for (int c = 0; c < CH; ++c) {
+        wv[b][c] = live[b] ? ws[lane + 64 * c] : u32x4{0u, 0u, 0u, 0u};
+        xv[b][c] = live[b] ? xs[lane + 64 * c] : u32x4{0u, 0u, 0u, 0u};
+      }
     }
-    dot = wave_sum(dot);
-    if (lane == 0) {
-      const float z = row_r[row] * dot;
-      a_rows[row] = row_w[row] * (act == 1 ? gelu_tanh(z) : gelu_erf(z));
+    float dot[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      dot[b] = 0.f;
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        float xf[8], wf[8];
+        unpack16(make_uint4(xv[b][c].x, xv[b][c].y, xv[b][c].z, xv[b][c].w), xf,
+                 (const uint16_t*)nullptr);
+        unpack16(make_uint4(wv[b][c].x, wv[b][c].y, wv[b][c].z, wv[b][c].w), wf,
+                 (const uint16_t*)nullptr);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) dot[b] = fmaf(xf[q], wf[q], dot[b]);
+      }
+    }
+    // NB independent butterfly reductions, interleaved step by step
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) dot[b] += __shfl_xor(dot[b], o, 64);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int64_t row = first + i0 + b;
+      if (lane == b && row < rows) {
+        float av = 0.f;
+        if (live[b]) {
+          const float z = row_r[row] * dot[b];
+          av = row_w[row] * (act == 1 ? gelu_tanh(z) : gelu_erf(z));
+        }
+        a_rows[row] = av;
+      }
     }
   }
-  (void)nvec;
 }
 
 template <int CH>
@@ -75,6 +97,7 @@ __global__ void __launch_bounds__(256) k_atomic_phase2(
     const uint16_t* __restrict__ V, int d, int64_t Tn, int k, const int32_t* __restrict__ ids,
     const int32_t* __restrict__ pos, const float* __restrict__ a_rows,
     uint16_t* __restrict__ routed) {
+  constexpr int NB = batch_of<CH>();
   const int lane = threadIdx.x & 63;
   const int64_t t = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (t >= Tn) return;
@@ -83,17 +106,109 @@ __global__ void __launch_bounds__(256) k_atomic_phase2(
   for (int c = 0; c < CH; ++c)
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[c][q] = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int p = pos[t * k + j];
-    if (p < 0) continue;
-    const float a = a_rows[p];
-    const uint4* vs = reinterpret_cast<const uint4*>(V + int64_t(ids[t * k + j]) * d);
+  for (int j0 = 0; j0 < k; j0 += NB) {
+    u32x4 vv[NB][CH];
+    float a[NB];
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      float vf[8];
-      unpack16(vs[lane + 64 * c], vf, (const uint16_t*)nullptr);
+    for (int b = 0; b < NB; ++b) {
+      const int j = j0 + b;
+      const int p = j < k ? pos[t * k + j] : -1;
+      a[b] = p >= 0 ? a_rows[p] : 0.f;
+      const u32x4* vs =
+          reinterpret_cast<const u32x4*>(V + int64_t(p >= 0 ? ids[t * k + j] : 0) * d);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[c][q] = fmaf(a, vf[q], acc[c][q]);
+      for (int c = 0; c < CH; ++c) vv[b][c] = p >= 0 ? vs[lane + 64 * c] : u32x4{0u, 0u, 0u, 0u};
+    }
+    // slots added in slot order: the sum is the same as one slot at a time
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        float vf[8];
+        unpack16(make_uint4(vv[b][c].x, vv[b][c].y, vv[b][c].z, vv[b][c].w), vf,
+                 (const uint16_t*)nullptr);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[c][q] = fmaf(a[b], vf[q], acc[c][q]);
+      }
+  }
+  uint4* out = reinterpret_cast<uint4*>(routed + t * d);
+#pragma unroll
+  for (int c = 0; c < CH; ++c) out[lane + 64 * c] = pack16(acc[c], (const uint16_t*)nullptr);
+}
+
+// Token-centric single pass: one wave per token keeps x[t] in registers and
+// walks its k slots in order, NB at a time with all 2 NB row gathers (W[n]
+// and V[n]) issued before any is used: a = g * act(r * x.W[n]), then
+// routed[t] += a * V[n] in slot order (the same sum as the two phases).
+template <int CH>
+__global__ void __launch_bounds__(256) k_atomic_token(
+    const uint16_t* __restrict__ xhat, int d, const uint16_t* __restrict__ W,
+    const uint16_t* __restrict__ V, int64_t Tn, int k, const int32_t* __restrict__ ids,
+    const float* __restrict__ w_tok, const float* __restrict__ r_tok, int act,
+    uint16_t* __restrict__ routed) {
+  constexpr int NB = CH >= 4 ? 2 : 4;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= Tn) return;
+  u32x4 xv[CH];
+  {
+    const u32x4* xs = reinterpret_cast<const u32x4*>(xhat + t * d);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) xv[c] = xs[lane + 64 * c];
+  }
+  const float rt = r_tok[t];
+  float acc[CH][8];
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[c][q] = 0.f;
+  for (int j0 = 0; j0 < k; j0 += NB) {
+    u32x4 wv[NB][CH], vv[NB][CH];
+    float g[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int j = j0 + b;
+      const bool live = j < k;
+      const int n = live ? ids[t * k + j] : 0;
+      g[b] = live ? w_tok[t * k + j] : 0.f;
+      const u32x4* ws = reinterpret_cast<const u32x4*>(W + int64_t(n) * d);
+      const u32x4* vs = reinterpret_cast<const u32x4*>(V + int64_t(n) * d);
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        wv[b][c] = live ? ws[lane + 64 * c] : u32x4{0u, 0u, 0u, 0u};
+        vv[b][c] = live ? vs[lane + 64 * c] : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    float dot[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      dot[b] = 0.f;
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        float wf[8], xf[8];
+        unpack16(make_uint4(wv[b][c].x, wv[b][c].y, wv[b][c].z, wv[b][c].w), wf,
+                 (const uint16_t*)nullptr);
+        unpack16(make_uint4(xv[c].x, xv[c].y, xv[c].z, xv[c].w), xf, (const uint16_t*)nullptr);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) dot[b] = fmaf(xf[q], wf[q], dot[b]);
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) dot[b] += __shfl_xor(dot[b], o, 64);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const float z = rt * dot[b];
+      const float a = g[b] * (act == 1 ? gelu_tanh(z) : gelu_erf(z));
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        float vf[8];
+        unpack16(make_uint4(vv[b][c].x, vv[b][c].y, vv[b][c].z, vv[b][c].w), vf,
+                 (const uint16_t*)nullptr);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[c][q] = fmaf(a, vf[q], acc[c][q]);
+      }
     }
   }
   uint4* out = reinterpret_cast<uint4*>(routed + t * d);
@@ -103,6 +218,14 @@ __global__ void __launch_bounds__(256) k_atomic_phase2(
 
 template <int CH>
 hipError_t launch_ch(const AtomicArgs& a, hipStream_t s) {
+  if (a.token_centric) {
+    if (a.T > 0)
+      hipLaunchKernelGGL(k_atomic_token<CH>, dim3(unsigned((a.T + 3) / 4)), dim3(256), 0, s,
+                         static_cast<const uint16_t*>(a.xhat), int(a.d),
+                         static_cast<const uint16_t*>(a.W), static_cast<const uint16_t*>(a.V), a.T,
+                         a.k, a.ids, a.w_tok, a.r_tok, a.act, static_cast<uint16_t*>(a.routed));
+    return hipGetLastError();
+  }
   const int64_t waves1 = (a.rows + kTasksPerWave - 1) / kTasksPerWave;
   if (waves1 > 0)
     hipLaunchKernelGGL(k_atomic_phase1<CH>, dim3(unsigned((waves1 + 3) / 4)), dim3(256), 0, s,
@@ -116,7 +239,23 @@ hipError_t launch_ch(const AtomicArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The four counters of a layer whose ids come from its own router (in range
+// by construction): all T k slots are rows, none dropped, load not counted.
+__global__ void k_slot_stats(int64_t n, int32_t* __restrict__ st) {
+  if (threadIdx.x == 0) {
+    st[0] = int32_t(n);
+    st[1] = 0;
+    st[2] = -1;
+    st[3] = 0;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_slot_stats(int64_t n, void* stats, hipStream_t s) {
+  hipLaunchKernelGGL(k_slot_stats, dim3(1), dim3(64), 0, s, n, static_cast<int32_t*>(stats));
+  return hipGetLastError();
+}
 
 hipError_t launch_atomic(const AtomicArgs& a, hipStream_t s) {
   switch (a.d) {

@@ -69,7 +69,15 @@ struct AtomicArgs {
   int64_t rows;               // host upper bound on rows
   float* a_rows;   // [rows] workspace: gated activation per task
   void* routed;    // [T, d]
+  // token-centric form (one pass per token over its slots, no task list):
+  // the router's gates and the RMSNorm statistic by token
+  int token_centric = 0;
+  const float* w_tok = nullptr;   // [T, k]
+  const float* r_tok = nullptr;   // [T]
 };
 hipError_t launch_atomic(const AtomicArgs& a, hipStream_t s);
+// Slot counters of a layer that runs no dispatch (its router's ids are in
+// range by construction): rows = n, dropped = 0, max_load = -1, errors = 0.
+hipError_t launch_slot_stats(int64_t n, void* stats, hipStream_t s);
 
 }  // namespace moe

@@ -77,15 +77,21 @@ def test_fullsize_parity(name):
         E = wl.Nr * wl.Nc
     del logits, rws
 
-    # dispatch over all tokens: bit-exact
+    # dispatch over all tokens: bit-exact (atomic experts: the standalone
+    # dispatch on the layer's ids, since that layer runs none)
     cap = O.capacity(wl.T, wl.k, E, wl.cf)
     disp = O.dispatch(ids, E, cap, wl.pad)
+    st = stats.cpu().numpy()
+    if wl.expert_kind == "atomic":
+        assert st[0] == wl.T * wl.k and st[1] == 0 and st[2] == -1 and st[3] == 0
+        from test_gpu_parity import _standalone_dispatch
+        rt = _standalone_dispatch(rt, E, cap, wl.pad, dev)
+        st = rt["stats"].cpu().numpy()
     assert np.array_equal(rt["counts"].cpu().numpy(), disp["counts"])
     assert np.array_equal(rt["offsets"].cpu().numpy(), disp["offsets"])
     pos = rt["pos"].cpu().numpy()
     assert np.array_equal(pos, disp["pos"])
     assert np.array_equal(rt["row_token"].cpu().numpy()[:disp["rows"]], disp["row_token"])
-    st = stats.cpu().numpy()
     assert st[0] == disp["rows"] and st[1] == disp["dropped"] and st[3] == 0
 
     # sampled outputs against the oracle on the GPU's routing

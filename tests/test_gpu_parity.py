@@ -54,6 +54,22 @@ def _gpu_logits(wl, layer, params, r):
     return logits, ids, w
 
 
+def _standalone_dispatch(rt, E, cap, pad, dev):
+    """moe_dispatch on a layer's ids / gates / r; returns its outputs by name."""
+    T, k = rt["ids"].shape
+    R = B.rows_max(T, k, E, cap, pad)
+    i32, f32 = dict(dtype=torch.int32, device=dev), dict(dtype=torch.float32, device=dev)
+    out = dict(counts=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32),
+               pos=torch.empty((T, k), **i32), row_token=torch.empty(R, **i32),
+               row_r=torch.empty(R, **f32), row_w=torch.empty(R, **f32),
+               row_expert=torch.empty(R, **i32))
+    stats = torch.zeros(4, **i32)
+    ws = torch.empty(max(B.dispatch_workspace_size(T, k, E), 1), dtype=torch.uint8, device=dev)
+    B.dispatch(rt["ids"], rt["w"], rt["r"], E, cap, pad, R, out, stats=stats, ws=ws)
+    torch.cuda.synchronize()
+    return dict(out, stats=stats)
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_layer_parity(name, dev):
     _say(f"[gpu] layer parity {name}")
@@ -104,10 +120,16 @@ def test_layer_parity(name, dev):
         e = np.exp(sc.astype(np.float64) - sc[:, :1])
         assert rel_err(w, e / e.sum(axis=1, keepdims=True)) < 1e-5
 
-    # dispatch on the GPU's ids: bit-exact
+    # dispatch on the GPU's ids: bit-exact.  A layer of atomic experts reads
+    # its routing by token and runs no dispatch: the standalone dispatch (the
+    # expert-sorted task list) is checked on the same ids instead.
     E = wl.E if wl.router == "dense" else wl.Nr * wl.Nc
     cap = O.capacity(wl.T, wl.k, E, wl.cf)
     disp = O.dispatch(ids, E, cap, wl.pad)
+    st = stats.cpu().numpy()
+    if wl.expert_kind == "atomic":
+        assert st[0] == wl.T * wl.k and st[1] == 0 and st[2] == -1 and st[3] == 0
+        rt = _standalone_dispatch(rt, E, cap, wl.pad, dev)
     assert np.array_equal(rt["counts"].cpu().numpy(), disp["counts"])
     assert np.array_equal(rt["offsets"].cpu().numpy(), disp["offsets"])
     pos = rt["pos"].cpu().numpy()
@@ -121,7 +143,8 @@ def test_layer_parity(name, dev):
     row_r = rt["row_r"].cpu().numpy()
     assert np.array_equal(row_w[pos[kept]], w[kept])
     assert np.array_equal(row_r[pos[kept]], r[np.nonzero(kept)[0]])
-    st = stats.cpu().numpy()
+    if "stats" in rt:
+        st = rt["stats"].cpu().numpy()
     assert st[0] == rows and st[1] == disp["dropped"] and st[2] == disp["max_load"] and st[3] == 0
 
     # whole layer on the GPU's routing
@@ -460,3 +483,35 @@ def test_layer_router_extras(dev):
     assert rel_err(ps.cpu().numpy(), st["prob_sum"]) < 1e-5
     assert rel_err(gs.cpu().numpy(), st["gate_sum"]) < 1e-5
     assert np.allclose(aux.cpu().numpy(), st["aux"], rtol=1e-4, atol=1e-6)
+
+
+def test_atomic_schedules_agree(dev):
+    """Atomic experts through moe_expert_gemm: the expert-centric two-phase
+    schedule (on the dispatch's task list) and the token-centric single pass
+    (ids, w, r only) give the same bits, and match the oracle."""
+    _say("[gpu] atomic experts: expert-centric == token-centric")
+    wl, inp, params, layer = _setup("atomic_small", dev)
+    ws = layer.alloc_workspace(wl.T)
+    layer.forward(params["x"], ws=ws)
+    torch.cuda.synchronize()
+    rt = layer.routing(wl.T, ws)
+    E = wl.Nr * wl.Nc
+    full = _standalone_dispatch(rt, E, wl.T, 1, dev)
+    full.update(ids=rt["ids"], w=rt["w"], r=rt["r"])
+    X = layer.desc.experts
+    R = B.rows_max(wl.T, wl.k, E, wl.T, 1)
+    nws = B.expert_workspace_size(X, B.MOE_BF16, wl.d, wl.T, wl.k, R)
+    ews = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    x = params["x"]
+    y_ec = torch.empty_like(x)
+    y_tc = torch.empty_like(x)
+    B.expert_gemm(X, B.MOE_BF16, wl.d, B.make_routing(wl.T, wl.k, E, R, 1, full), x, y_ec, ews)
+    tok = dict(ids=rt["ids"], w=rt["w"], r=rt["r"])
+    B.expert_gemm(X, B.MOE_BF16, wl.d, B.make_routing(wl.T, wl.k, E, R, 1, tok), x, y_tc, ews)
+    torch.cuda.synchronize()
+    assert torch.equal(y_ec.view(torch.int16), y_tc.view(torch.int16))
+    ids = rt["ids"].cpu().numpy()
+    ref = O.atomic_experts_token_centric(O.as_f64(inp["x"]), rt["r"].cpu().numpy().astype(np.float64),
+                                         ids, rt["w"].cpu().numpy().astype(np.float64),
+                                         O.as_f64(inp["W"]), O.as_f64(inp["V"]))
+    assert rel_err(f64(synth.to_host(y_tc)), ref) < TOL["bf16"]
