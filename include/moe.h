@@ -328,7 +328,7 @@ int moe_shared_ffn(const moe_experts_desc* S, int dtype, int64_t d, int64_t T, c
  * out[t] = x[t] + shared[t] + sum_{j : pos[t,j] >= 0} y[pos[t,j]], summed in
  * fp32 in exactly that order and stored once.  residual / shared may be
  * NULL.  With pos == NULL, y is [T, d] in token order (the atomic branch).
- * A token whose slots are all dropped gets out = x bit-exactly. */
+ * A token whose slots are all dropped gets out = x bit-exactly.  k <= 256. */
 int moe_combine(const void* y, const int32_t* pos, const void* residual, const void* shared,
                 int dtype, int64_t T, int64_t d, int k, void* out, hipStream_t stream);
 

@@ -424,6 +424,9 @@ size_t moe_router_workspace_size(const moe_router_desc* R, int64_t T) {
   c.take_n<float>(((T + 3) / 4) * R->E);
   c.take_n<float>(((T + 3) / 4) * R->E);
   c.take_n<int>(((T + 3) / 4) * R->E);
+  c.take_n<float>(R->E);
+  c.take_n<float>(R->E);
+  c.take_n<long long>(R->E);
   return c.used;
 }
 
@@ -481,6 +484,9 @@ int router_run(const moe_router_desc* R, const void* x, int dtype, int64_t T, in
         ex.part_p = c.take_n<float>(((T + 3) / 4) * R->E);
         ex.part_g = c.take_n<float>(((T + 3) / 4) * R->E);
         ex.part_c = c.take_n<int>(((T + 3) / 4) * R->E);
+        ex.sum_p = c.take_n<float>(R->E);
+        ex.sum_g = c.take_n<float>(R->E);
+        ex.sum_c = c.take_n<long long>(R->E);
         ex.prob_sum = extras->prob_sum;
         ex.gate_sum = extras->gate_sum;
         ex.aux = extras->aux;
@@ -747,6 +753,7 @@ int moe_combine(const void* y, const int32_t* pos, const void* residual, const v
                 int dtype, int64_t T, int64_t d, int k, void* out, hipStream_t stream) {
   REQUIRE(valid_dtype(dtype), MOE_EDTYPE, "unknown dtype %d", dtype);
   REQUIRE(T >= 0 && d > 0 && k >= 1, MOE_ESHAPE, "bad sizes");
+  REQUIRE(k <= 256, MOE_EUNSUPPORTED, "combine supports k <= 256");
   REQUIRE(d % (16 / esize(dtype)) == 0, MOE_ESHAPE, "d must fill 16-byte vectors");
   REQUIRE(T == 0 || (y && out), MOE_EINVAL, "NULL pointer");
   MOE_HIP(launch_combine(y, pos, residual, shared, dtype, T, d, k, out, stream));

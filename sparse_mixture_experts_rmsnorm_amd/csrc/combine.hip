@@ -16,27 +16,39 @@
 namespace moe {
 namespace {
 
-template <typename T>
-__global__ void __launch_bounds__(256) k_combine(const T* __restrict__ y,
+// One wave per token.  The token's slot positions are read once (lane j holds
+// slot j + 64 q) and broadcast slot by slot; the expert rows of four slots
+// are loaded together before they are added, so several gathers are in
+// flight.  SPLIT: each expert row is the sum of two K-split partial planes
+// (y0 and y0 + plane), added as (p0 + p1).  The sum starts from x itself, so
+// a token whose slots were all dropped stores x bit for bit.
+template <typename T, int SPLIT>
+__global__ void __launch_bounds__(256) k_combine(const T* __restrict__ y, int64_t plane,
                                                  const int32_t* __restrict__ pos,
                                                  const T* __restrict__ x, const T* __restrict__ sh,
                                                  int64_t Tn, int64_t d, int k, T* __restrict__ out) {
   constexpr int N = Vec16<T>::N;
+  constexpr int SB = 4;                         // slots per batch of loads
   const int lane = threadIdx.x & 63;
   const int64_t t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= Tn) return;
   const int64_t nvec = d / N;
   const uint4* ys = reinterpret_cast<const uint4*>(y);
+  const int64_t pv = plane / N;
+  int pl[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int j = lane + 64 * q;
+    pl[q] = (pos && j < k) ? pos[t * k + j] : -1;
+  }
 #pragma unroll 2
   for (int64_t v = lane; v < nvec; v += 64) {
     float acc[8];
-#pragma unroll
-    for (int i = 0; i < N; ++i) acc[i] = 0.f;
     if (x) {
-      float f[8];
-      unpack16(reinterpret_cast<const uint4*>(x)[t * nvec + v], f, (const T*)nullptr);
+      unpack16(reinterpret_cast<const uint4*>(x)[t * nvec + v], acc, (const T*)nullptr);
+    } else {
 #pragma unroll
-      for (int i = 0; i < N; ++i) acc[i] += f[i];
+      for (int i = 0; i < N; ++i) acc[i] = 0.f;
     }
     if (sh) {
       float f[8];
@@ -45,64 +57,41 @@ __global__ void __launch_bounds__(256) k_combine(const T* __restrict__ y,
       for (int i = 0; i < N; ++i) acc[i] += f[i];
     }
     if (pos) {
-      for (int j = 0; j < k; ++j) {
-        const int p = pos[t * k + j];
-        if (p < 0) continue;
-        float f[8];
-        unpack16(ys[int64_t(p) * nvec + v], f, (const T*)nullptr);
 #pragma unroll
-        for (int i = 0; i < N; ++i) acc[i] += f[i];
+      for (int q = 0; q < 4; ++q) {
+        const int nq = min(64, k - 64 * q);
+        for (int j0 = 0; j0 < nq; j0 += SB) {
+          uint4 a[SB], b[SB];
+          bool ok[SB];
+#pragma unroll
+          for (int u = 0; u < SB; ++u) {
+            const int p = j0 + u < nq ? __builtin_amdgcn_readlane(pl[q], j0 + u) : -1;
+            ok[u] = p >= 0;
+            a[u] = ok[u] ? ys[int64_t(p) * nvec + v] : make_uint4(0, 0, 0, 0);
+            if (SPLIT) b[u] = ok[u] ? ys[pv + int64_t(p) * nvec + v] : make_uint4(0, 0, 0, 0);
+          }
+#pragma unroll
+          for (int u = 0; u < SB; ++u) {
+            if (!ok[u]) continue;
+            float f0[8];
+            unpack16(a[u], f0, (const T*)nullptr);
+            if (SPLIT) {
+              float f1[8];
+              unpack16(b[u], f1, (const T*)nullptr);
+#pragma unroll
+              for (int i = 0; i < N; ++i) acc[i] += f0[i] + f1[i];
+            } else {
+#pragma unroll
+              for (int i = 0; i < N; ++i) acc[i] += f0[i];
+            }
+          }
+        }
       }
     } else {
       float f[8];
       unpack16(ys[t * nvec + v], f, (const T*)nullptr);
 #pragma unroll
       for (int i = 0; i < N; ++i) acc[i] += f[i];
-    }
-    reinterpret_cast<uint4*>(out)[t * nvec + v] = pack16(acc, (const T*)nullptr);
-  }
-}
-
-// Same sum with the expert outputs held as two partial planes of a K-split
-// second GEMM: slot j adds (p0[pos] + p1[pos]).
-template <typename T>
-__global__ void __launch_bounds__(256) k_combine_split(const T* __restrict__ y0, int64_t plane,
-                                                       const int32_t* __restrict__ pos,
-                                                       const T* __restrict__ x,
-                                                       const T* __restrict__ sh, int64_t Tn,
-                                                       int64_t d, int k, T* __restrict__ out) {
-  constexpr int N = Vec16<T>::N;
-  const int lane = threadIdx.x & 63;
-  const int64_t t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= Tn) return;
-  const int64_t nvec = d / N;
-  const uint4* ys = reinterpret_cast<const uint4*>(y0);
-  const int64_t pv = plane / N;
-#pragma unroll 2
-  for (int64_t v = lane; v < nvec; v += 64) {
-    float acc[8];
-#pragma unroll
-    for (int i = 0; i < N; ++i) acc[i] = 0.f;
-    if (x) {
-      float f[8];
-      unpack16(reinterpret_cast<const uint4*>(x)[t * nvec + v], f, (const T*)nullptr);
-#pragma unroll
-      for (int i = 0; i < N; ++i) acc[i] += f[i];
-    }
-    if (sh) {
-      float f[8];
-      unpack16(reinterpret_cast<const uint4*>(sh)[t * nvec + v], f, (const T*)nullptr);
-#pragma unroll
-      for (int i = 0; i < N; ++i) acc[i] += f[i];
-    }
-    for (int j = 0; j < k; ++j) {
-      const int p = pos[t * k + j];
-      if (p < 0) continue;
-      float f0[8], f1[8];
-      unpack16(ys[int64_t(p) * nvec + v], f0, (const T*)nullptr);
-      unpack16(ys[pv + int64_t(p) * nvec + v], f1, (const T*)nullptr);
-#pragma unroll
-      for (int i = 0; i < N; ++i) acc[i] += f0[i] + f1[i];
     }
     reinterpret_cast<uint4*>(out)[t * nvec + v] = pack16(acc, (const T*)nullptr);
   }
@@ -116,12 +105,11 @@ hipError_t launch_combine_split(const void* y0, int64_t rows_max, const int32_t*
   if (T == 0) return hipSuccess;
   const dim3 g(unsigned((T + 3) / 4));
   if (dtype == 0)
-    hipLaunchKernelGGL(k_combine_split<float>, g, dim3(256), 0, s, static_cast<const float*>(y0),
-                       rows_max * d, pos,
-                       static_cast<const float*>(x), static_cast<const float*>(shared), T, d, k,
-                       static_cast<float*>(out));
+    hipLaunchKernelGGL((k_combine<float, 1>), g, dim3(256), 0, s, static_cast<const float*>(y0),
+                       rows_max * d, pos, static_cast<const float*>(x),
+                       static_cast<const float*>(shared), T, d, k, static_cast<float*>(out));
   else
-    hipLaunchKernelGGL(k_combine_split<uint16_t>, g, dim3(256), 0, s,
+    hipLaunchKernelGGL((k_combine<uint16_t, 1>), g, dim3(256), 0, s,
                        static_cast<const uint16_t*>(y0), rows_max * d, pos,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(shared), T,
                        d, k, static_cast<uint16_t*>(out));
@@ -133,13 +121,14 @@ hipError_t launch_combine(const void* y, const int32_t* pos, const void* x, cons
   if (T == 0) return hipSuccess;
   const dim3 g(unsigned((T + 3) / 4));
   if (dtype == 0)
-    hipLaunchKernelGGL(k_combine<float>, g, dim3(256), 0, s, static_cast<const float*>(y), pos,
-                       static_cast<const float*>(x), static_cast<const float*>(shared), T, d, k,
-                       static_cast<float*>(out));
+    hipLaunchKernelGGL((k_combine<float, 0>), g, dim3(256), 0, s, static_cast<const float*>(y),
+                       int64_t(0), pos, static_cast<const float*>(x),
+                       static_cast<const float*>(shared), T, d, k, static_cast<float*>(out));
   else
-    hipLaunchKernelGGL(k_combine<uint16_t>, g, dim3(256), 0, s, static_cast<const uint16_t*>(y),
-                       pos, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(shared),
-                       T, d, k, static_cast<uint16_t*>(out));
+    hipLaunchKernelGGL((k_combine<uint16_t, 0>), g, dim3(256), 0, s,
+                       static_cast<const uint16_t*>(y), int64_t(0), pos,
+                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(shared), T,
+                       d, k, static_cast<uint16_t*>(out));
   return hipGetLastError();
 }
 

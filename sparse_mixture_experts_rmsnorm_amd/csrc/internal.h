@@ -24,6 +24,9 @@ struct RouterExtras {
   float* part_p = nullptr;
   float* part_g = nullptr;
   int* part_c = nullptr;
+  float* sum_p = nullptr;       // [E] workspace: per-expert totals
+  float* sum_g = nullptr;
+  long long* sum_c = nullptr;
   float* prob_sum = nullptr;
   float* gate_sum = nullptr;
   float* aux = nullptr;

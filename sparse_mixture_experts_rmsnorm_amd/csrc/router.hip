@@ -506,56 +506,67 @@ __global__ void __launch_bounds__(256) k_topk_rows(float* __restrict__ lg, int T
   }
 }
 
-// Routing statistics from the per-workgroup partial sums (one workgroup):
-// each expert's sums over workgroups in a fixed order and the squared
-// coefficient of variation of the probability sums, gate sums and slot counts.
-__global__ void __launch_bounds__(256) k_router_stats(const float* __restrict__ part_p,
-                                                      const float* __restrict__ part_g,
-                                                      const int* __restrict__ part_c, int nblk,
-                                                      int E, float* __restrict__ prob_sum,
-                                                      float* __restrict__ gate_sum,
-                                                      float* __restrict__ aux) {
-  __shared__ float sp[256], sg[256], fp[256], fg[256];
-  __shared__ long long sc[256], fc[256];
-  const int tid = threadIdx.x;
-  int ep = 1;
-  while (ep < E) ep <<= 1;
-  const int R = 256 / ep;                      // threads per expert
-  const int e = tid % ep, rr = tid / ep;
+// Routing statistics from the per-workgroup partial sums.  k_router_sums:
+// one workgroup per expert; thread i adds the partial rows i, i + 256, ...
+// and a fixed-shape tree combines the 256 sums, so the order never varies.
+__global__ void __launch_bounds__(256) k_router_sums(const float* __restrict__ part_p,
+                                                     const float* __restrict__ part_g,
+                                                     const int* __restrict__ part_c, int nblk,
+                                                     int E, float* __restrict__ sum_p,
+                                                     float* __restrict__ sum_g,
+                                                     long long* __restrict__ sum_c) {
+  __shared__ float sp[256], sg[256];
+  __shared__ long long sc[256];
+  const int e = blockIdx.x, tid = threadIdx.x;
   float ap = 0.f, ag = 0.f;
   long long ac = 0;
-  if (e < E)
-    for (int b = rr; b < nblk; b += R) {
-      ap += part_p[int64_t(b) * E + e];
-      ag += part_g[int64_t(b) * E + e];
-      ac += part_c[int64_t(b) * E + e];
-    }
+  for (int b = tid; b < nblk; b += 256) {
+    ap += part_p[int64_t(b) * E + e];
+    ag += part_g[int64_t(b) * E + e];
+    ac += part_c[int64_t(b) * E + e];
+  }
   sp[tid] = ap;
   sg[tid] = ag;
   sc[tid] = ac;
   __syncthreads();
-  if (tid < E) {
-    float P = 0.f, G = 0.f;
-    long long Cn = 0;
-    for (int r = 0; r < R; ++r) {
-      P += sp[r * ep + tid];
-      G += sg[r * ep + tid];
-      Cn += sc[r * ep + tid];
+  for (int h = 128; h > 0; h >>= 1) {
+    if (tid < h) {
+      sp[tid] += sp[tid + h];
+      sg[tid] += sg[tid + h];
+      sc[tid] += sc[tid + h];
     }
-    fp[tid] = P;
-    fg[tid] = G;
-    fc[tid] = Cn;
-    if (prob_sum) prob_sum[tid] = P;
-    if (gate_sum) gate_sum[tid] = G;
+    __syncthreads();
   }
-  __syncthreads();
+  if (tid == 0) {
+    sum_p[e] = sp[0];
+    sum_g[e] = sg[0];
+    sum_c[e] = sc[0];
+  }
+}
+
+// The squared coefficient of variation (population variance / mean^2) of the
+// three per-expert sums, in float64 (one workgroup, three threads).
+__global__ void __launch_bounds__(64) k_router_cv2(const float* __restrict__ sum_p,
+                                                   const float* __restrict__ sum_g,
+                                                   const long long* __restrict__ sum_c, int E,
+                                                   float* __restrict__ prob_sum,
+                                                   float* __restrict__ gate_sum,
+                                                   float* __restrict__ aux) {
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 64) {
+    if (prob_sum) prob_sum[e] = sum_p[e];
+    if (gate_sum) gate_sum[e] = sum_g[e];
+  }
   if (tid < 3 && aux) {
+    auto val = [&](int i) {
+      return tid == 0 ? double(sum_p[i]) : tid == 1 ? double(sum_g[i]) : double(sum_c[i]);
+    };
     double s1 = 0.0;
-    for (int i = 0; i < E; ++i) s1 += tid == 0 ? fp[i] : tid == 1 ? fg[i] : double(fc[i]);
+    for (int i = 0; i < E; ++i) s1 += val(i);
     const double mean = s1 / E;
     double s2 = 0.0;
     for (int i = 0; i < E; ++i) {
-      const double v = (tid == 0 ? fp[i] : tid == 1 ? fg[i] : double(fc[i])) - mean;
+      const double v = val(i) - mean;
       s2 += v * v;
     }
     aux[tid] = mean != 0.0 ? float((s2 / E) / (mean * mean)) : __int_as_float(0x7fc00000);
@@ -769,10 +780,13 @@ hipError_t launch_router_dense(const void* x, int dtype, int64_t T, int64_t d, c
     else MOE_ROUTER_CASE(16);
 #undef MOE_ROUTER_CASE
   }
-  if (ex.part_p)
-    hipLaunchKernelGGL(k_router_stats, dim3(1), dim3(256), 0, s, ex.part_p, ex.part_g, ex.part_c,
-                       int(router_dense_blocks(dtype, T)), int(E), ex.prob_sum, ex.gate_sum,
-                       ex.aux);
+  if (ex.part_p) {
+    hipLaunchKernelGGL(k_router_sums, dim3(unsigned(E)), dim3(256), 0, s, ex.part_p, ex.part_g,
+                       ex.part_c, int(router_dense_blocks(dtype, T)), int(E), ex.sum_p, ex.sum_g,
+                       ex.sum_c);
+    hipLaunchKernelGGL(k_router_cv2, dim3(1), dim3(64), 0, s, ex.sum_p, ex.sum_g, ex.sum_c,
+                       int(E), ex.prob_sum, ex.gate_sum, ex.aux);
+  }
   return hipGetLastError();
 }
 
