@@ -66,6 +66,8 @@ from scipy.special import erf
 __all__ = [
     "bf16_to_f64", "f64_to_bf16_bits", "as_f64",
     "capacity", "rmsnorm_scale", "rmsnorm", "router_logits", "router_logits_unfused",
+    "E4M3_MAX", "MX_BLOCK", "e4m3_decode", "e4m3_round", "e4m3_encode", "mx_quantize",
+    "mx_dequantize", "mx_qdq", "ffn_mxfp8",
     "select_topk", "gates", "noisy_logits", "router_probabilities", "squared_cv", "router_stats",
     "dispatch", "expert_layout", "bcsr_topology",
     "gelu", "gelu_tanh", "silu", "ffn", "grouped_expert_ffn", "bcsr_expert_ffn",
@@ -187,6 +189,89 @@ def router_logits_unfused(x, gamma, eps, w_router, bias=None) -> np.ndarray:
     if bias is not None:
         logits = logits + as_f64(bias)[None, :]
     return logits
+
+
+# --------------------------------------------------------------------------
+# [CODA] low precision: MXFP8 (OCP Microscaling Formats v1.0: blocks of 32
+# elements sharing an E8M0 power-of-two scale, elements in FP8 E4M3)
+# --------------------------------------------------------------------------
+
+E4M3_MAX = 448.0          # largest finite E4M3 value, 1.75 * 2^8
+E4M3_EMAX = 8             # exponent of the largest normal
+MX_BLOCK = 32
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Value of each E4M3 code (sign, 4 exponent bits with bias 7, 3 mantissa
+    bits; exponent 0 is subnormal m * 2^-9; S.1111.111 is NaN; no infinities)."""
+    c = np.asarray(codes, dtype=np.int64) & 0xFF
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    val = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    val = np.where((e == 15) & (m == 7), np.nan, val)
+    return sign * val
+
+
+def e4m3_round(v) -> np.ndarray:
+    """Nearest E4M3 value, ties to even, magnitudes above 448 saturated to
+    448 (the MX conversion clamps to the largest normal).  float64 in, out."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    _, e2 = np.frexp(np.where(a > 0, a, 1.0))
+    e = np.maximum(e2 - 1, -6)                 # exponent of the binade; subnormals share 2^-6's
+    quantum = np.exp2(e - 3.0)                  # 3 mantissa bits
+    q = np.rint(a / quantum) * quantum          # rint: ties to even
+    q = np.minimum(q, E4M3_MAX)
+    return np.copysign(q, v)
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """E4M3 code of values already on the E4M3 grid (|v| <= 448)."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    sign = np.where(np.signbit(v), 0x80, 0)
+    _, e2 = np.frexp(np.where(a > 0, a, 1.0))
+    e = e2 - 1
+    sub = a < 2.0 ** -6
+    m_sub = np.rint(a / 2.0 ** -9)
+    ebits = np.where(sub, 0, e + 7)
+    m = np.where(sub, m_sub, np.rint((a / np.exp2(e) - 1.0) * 8.0))
+    return (sign | (ebits.astype(np.int64) << 3) | m.astype(np.int64)).astype(np.uint8)
+
+
+def mx_quantize(v, axis: int = -1):
+    """MXFP8 quantisation of v along `axis` in blocks of 32 (the length along
+    axis must be a multiple of 32).  Per block: shared exponent
+    s = floor(log2(max |v|)) - 8, clamped to [-127, 127] (s = -127 for an
+    all-zero block); elements P = e4m3_round(v / 2^s).  Returns (codes uint8
+    shaped like v, scale codes uint8 = s + 127 with the axis length / 32)."""
+    v = np.moveaxis(np.asarray(v, dtype=np.float64), axis, -1)
+    n = v.shape[-1]
+    if n % MX_BLOCK:
+        raise ValueError("length along the axis must be a multiple of 32")
+    b = v.reshape(v.shape[:-1] + (n // MX_BLOCK, MX_BLOCK))
+    amax = np.abs(b).max(axis=-1)
+    _, e2 = np.frexp(np.where(amax > 0, amax, 1.0))
+    s = np.where(amax > 0, (e2 - 1) - E4M3_EMAX, -127)
+    s = np.clip(s, -127, 127)
+    p = e4m3_round(b / np.exp2(s)[..., None])
+    codes = e4m3_encode(p).reshape(v.shape)
+    return np.moveaxis(codes, -1, axis), np.moveaxis((s + 127).astype(np.uint8), -1, axis)
+
+
+def mx_dequantize(codes, scales, axis: int = -1) -> np.ndarray:
+    """Values of MXFP8 data: element value times its block's 2^(scale - 127)."""
+    c = np.moveaxis(np.asarray(codes), axis, -1)
+    sc = np.moveaxis(np.asarray(scales, dtype=np.int64), axis, -1)
+    x = np.exp2(np.repeat(sc - 127, MX_BLOCK, axis=-1).astype(np.float64))
+    return np.moveaxis(e4m3_decode(c) * x, -1, axis)
+
+
+def mx_qdq(v, axis: int = -1) -> np.ndarray:
+    """Quantise to MXFP8 along `axis` and return the represented values."""
+    c, sc = mx_quantize(v, axis)
+    return mx_dequantize(c, sc, axis)
 
 
 # --------------------------------------------------------------------------
@@ -444,8 +529,26 @@ def ffn(xhat, r, w1, w2, act: str, w3=None, faithful: bool = False):
     return h @ w2
 
 
+def ffn_mxfp8(xhat, r, w1, w2, act: str, w3=None):
+    """One expert FFN with MXFP8 operands ([CODA]: low-precision conversions
+    at the epilogues).  The activation rows are quantised along d before the
+    first linear and the weights along their K dimension (w1 / w3 per column
+    along d, w2 per column along f); r multiplies the first linear's
+    accumulator as in the bf16 path; the hidden activation is quantised along
+    f (blocks of 32 features) before the second linear.
+    """
+    xq = mx_qdq(np.asarray(xhat, dtype=np.float64), axis=1)
+    r = np.asarray(r, dtype=np.float64)[:, None]
+    a = r * (xq @ mx_qdq(w1, axis=0))
+    if act == "swiglu":
+        h = silu(a) * (r * (xq @ mx_qdq(w3, axis=0)))
+    else:
+        h = _act(act)(a)
+    return mx_qdq(h, axis=1) @ mx_qdq(w2, axis=0)
+
+
 def grouped_expert_ffn(xhat_rows, r_rows, e_of_row, w1, w2, f_offsets, act,
-                       w3=None, faithful=False):
+                       w3=None, faithful=False, quant=None):
     """Per-row expert FFN output for rows that each name their expert.
 
     w1, w3 are [d, sum f] and w2 is [sum f, d]; expert e owns columns
@@ -458,9 +561,13 @@ def grouped_expert_ffn(xhat_rows, r_rows, e_of_row, w1, w2, f_offsets, act,
     for e in np.unique(e_of_row):
         m = e_of_row == e
         lo, hi = int(f_offsets[e]), int(f_offsets[e + 1])
-        out[m] = ffn(xhat_rows[m], r_rows[m], as_f64(np.asarray(w1)[:, lo:hi]),
-                     as_f64(np.asarray(w2)[lo:hi, :]), act,
-                     None if w3 is None else as_f64(np.asarray(w3)[:, lo:hi]), faithful)
+        w3e = None if w3 is None else as_f64(np.asarray(w3)[:, lo:hi])
+        if quant == "mxfp8":
+            out[m] = ffn_mxfp8(xhat_rows[m], r_rows[m], as_f64(np.asarray(w1)[:, lo:hi]),
+                               as_f64(np.asarray(w2)[lo:hi, :]), act, w3e)
+        else:
+            out[m] = ffn(xhat_rows[m], r_rows[m], as_f64(np.asarray(w1)[:, lo:hi]),
+                         as_f64(np.asarray(w2)[lo:hi, :]), act, w3e, faithful)
     return out
 
 
@@ -645,7 +752,8 @@ def layer_forward(p: dict, x, ids_override=None, tokens=None, faithful=False) ->
       router 'dense': w_router [d,E], bias [E] or None, expert weights
         w1 [d,sum f], w3 (SwiGLU) and w2 [sum f,d], f_offsets [E+1]
       router 'cartesian': k_rows [d,Nr], k_cols [d,Nc], atomic W, V [N,d]
-    plus optional shared-expert weights ws1, ws3, ws2 (always active, gate 1).
+    plus optional shared-expert weights ws1, ws3, ws2 (always active, gate 1),
+    and quant='mxfp8' for routed experts with MXFP8 operands (ffn_mxfp8).
 
     ids_override replaces the selected ids (the stage-wise protocol: compare
     downstream stages on the GPU's own routing).  tokens restricts the FFN
@@ -706,7 +814,8 @@ def layer_forward(p: dict, x, ids_override=None, tokens=None, faithful=False) ->
     tt, jj = np.nonzero(pos >= 0)
     if len(tt):
         e_rows = np.asarray(ids)[tok[tt], jj].astype(np.int64)
-        y = grouped_expert_ffn(xh[tok[tt]], r[tok[tt]], e_rows, w1, w2, foff, act, w3, faithful)
+        y = grouped_expert_ffn(xh[tok[tt]], r[tok[tt]], e_rows, w1, w2, foff, act, w3, faithful,
+                               quant=p.get("quant"))
         slot_out[tt, jj] = rnd(g[tok[tt], jj][:, None] * y)
     shared = _shared_ffn(xh[tok], r[tok], p, faithful) if p.get("ws1") is not None else None
     if shared is not None:

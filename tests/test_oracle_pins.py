@@ -498,3 +498,101 @@ def test_noisy_logits_flip_selection():
     assert O.select_topk(O.noisy_logits(l, n, 1.0), 1)[0, 0] == 1       # 0.5 + 1 > 1
     assert O.select_topk(O.noisy_logits(l, n, 0.4), 1)[0, 0] == 0       # 0.9 < 1
     assert np.array_equal(O.noisy_logits(l, n, 2.5), l + 2.5 * n)
+
+
+# ---------------------------------------------------------------- MXFP8 (OCP MX v1.0, E4M3 elements)
+
+def test_e4m3_code_table():
+    codes = np.arange(256, dtype=np.uint8)
+    v = O.e4m3_decode(codes)
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF]) and np.sum(np.isnan(v)) == 2
+    assert v[0x7E] == 448.0 and v[0xFE] == -448.0          # largest finite
+    assert v[0x38] == 1.0 and v[0x08] == 2.0 ** -6          # 1.0, smallest normal
+    assert v[0x01] == 2.0 ** -9 and v[0x07] == 7 * 2.0 ** -9  # subnormals
+    assert v[0x00] == 0.0 and np.signbit(v[0x80])
+    fin = ~np.isnan(v)
+    assert np.array_equal(O.e4m3_encode(v[fin]), codes[fin])
+    # the finite values are distinct except +-0, and symmetric
+    pos = np.sort(v[fin & ~np.signbit(v)])
+    assert len(np.unique(pos)) == 127 and np.all(np.diff(pos) > 0)
+    assert np.array_equal(np.sort(-v[fin & np.signbit(v)]), np.sort(v[fin & ~np.signbit(v)]))
+
+
+def test_e4m3_round_is_nearest_even_on_the_grid():
+    grid = O.e4m3_decode(np.arange(256, dtype=np.uint8))
+    ok = ~np.isnan(grid)
+    gv, gc = grid[ok], np.arange(256)[ok]
+    rng = np.random.default_rng(3)
+    v = np.concatenate([rng.standard_normal(4000) * 50, rng.standard_normal(2000) * 0.01,
+                        (gv[:-1] + np.roll(gv, -1)[:-1]) / 2])      # include midpoints
+    v = v[np.abs(v) <= 448]
+    got = O.e4m3_round(v)
+    for x, y in zip(v, got):
+        dist = np.abs(gv - x)
+        best = np.nonzero(dist == dist.min())[0]
+        if len(best) > 1:          # a tie: the even mantissa (code bit 0 clear) wins
+            best = [b for b in best if gc[b] % 2 == 0 and np.signbit(gv[b]) == np.signbit(x)] or best
+        assert y == gv[best[0]] or (y == 0 and gv[best[0]] == 0), (x, y, gv[best])
+
+
+def test_e4m3_saturation_and_ties():
+    r = O.e4m3_round
+    assert r(470.0) == 448.0 and r(-1000.0) == -448.0 and r(464.0) == 448.0
+    assert r(1.0625) == 1.0 and r(1.1875) == 1.25            # ties to the even mantissa
+    assert r(2.0 ** -10) == 0.0 and r(3 * 2.0 ** -10) == 2 * 2.0 ** -9
+
+
+def test_mx_block_scale_closed_form():
+    # a block whose largest magnitude lies in [2^j, 2^(j+1)) gets scale 2^(j - 8)
+    for j in (-20, -3, 0, 5, 40):
+        v = np.zeros(32)
+        v[7] = 1.5 * 2.0 ** j
+        v[3] = -0.25 * 2.0 ** j
+        c, s = O.mx_quantize(v)
+        assert s.tolist() == [j - 8 + 127]
+        deq = O.mx_dequantize(c, s)
+        assert deq[7] == 1.5 * 2.0 ** j and deq[3] == -0.25 * 2.0 ** j
+    c, s = O.mx_quantize(np.zeros(64))
+    assert s.tolist() == [0, 0] and not c.any()
+
+
+def test_mx_quantize_matches_brute_force():
+    rng = np.random.default_rng(9)
+    v = rng.standard_normal((4, 96)) * np.exp2(rng.integers(-6, 6, size=(4, 1)))
+    c, s = O.mx_quantize(v, axis=1)
+    deq = O.mx_dequantize(c, s, axis=1)
+    grid = O.e4m3_decode(np.arange(256, dtype=np.uint8))
+    grid = np.unique(grid[~np.isnan(grid)])
+    for i in range(4):
+        for b in range(3):
+            blk = v[i, 32 * b:32 * b + 32]
+            e = int(np.floor(np.log2(np.abs(blk).max())))
+            scale = 2.0 ** (e - 8)
+            assert s[i, b] == e - 8 + 127
+            for x, y in zip(blk, deq[i, 32 * b:32 * b + 32]):
+                t = min(abs(x) / scale, 448.0)
+                near = grid[np.argmin(np.abs(grid - t))]
+                assert abs(abs(y) / scale - t) <= abs(near - t) + 1e-15
+    # quantisation along axis 0 is the same as along axis 1 of the transpose
+    c0, s0 = O.mx_quantize(v.T, axis=0)
+    assert np.array_equal(c0, c.T) and np.array_equal(s0, s.T)
+
+
+def test_mx_ffn_reduces_to_dense_on_grid_values():
+    """Inputs already exact in MXFP8 pass the quantisers unchanged, so the MX
+    FFN equals the plain FFN on them (the hidden layer is also put on the grid
+    by making the second linear act on an exact hidden value: GELU of 0 = 0)."""
+    rng = np.random.default_rng(4)
+    d, f, T = 64, 64, 5
+    on_grid = lambda a, ax: O.mx_qdq(a, axis=ax)  # noqa: E731
+    x = on_grid(rng.standard_normal((T, d)), 1)
+    w1 = on_grid(rng.standard_normal((d, f)) * 0.1, 0)
+    w2 = on_grid(rng.standard_normal((f, d)) * 0.1, 0)
+    r = np.ones(T)
+    a = x @ w1
+    h = O.gelu(a)
+    ref = O.mx_qdq(h, axis=1) @ w2
+    assert np.allclose(O.ffn_mxfp8(x, r, w1, w2, "gelu"), ref, rtol=0, atol=1e-12)
+    # and MX quantisation error stays within the E4M3 bound relative to block max
+    full = O.ffn(x, r, w1, w2, "gelu")
+    assert np.max(np.abs(O.ffn_mxfp8(x, r, w1, w2, "gelu") - full)) < 0.1 * np.max(np.abs(full))
