@@ -23,14 +23,15 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "MoE layer fwd tokens/s + expert-GEMM TFLOP/s (% bf16 MFMA peak), 1 MI355X"
-PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA bf16 / fp32 vector
+# MI355X dense peaks: MFMA bf16, MFMA fp8 (the MXFP8 GEMMs), fp32 vector
+PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "f32": 157.3}
 PEAK_HBM_GBPS = 8000.0
 
 # HBM bytes per launch of the first expert GEMM on the Mixtral-shaped workload,
 # from two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)
 # scaled by what the same counters read for a plain 1 GiB device copy
 # (bench.py --copy-calibration).  Valid only for the kernel source it was
-# taken on: any change to gemm.hip, gemm_args.h or common.h reports null.
+# taken on: any change to gemm.hip or the headers it uses reports null.
 TRAFFIC = {
     "workload": "mixtral_bf16",
     "source_sha256": "f96c9ab6daf8f20ec49cb3c2efe1d92b3b29ea3002c8a64a9c0e840eb2dddee9",
@@ -42,7 +43,7 @@ TRAFFIC = {
 def gemm_source_sha256():
     import hashlib
     h = hashlib.sha256()
-    for f in ("gemm.hip", "gemm_args.h", "common.h"):
+    for f in ("gemm.hip", "gemm_args.h", "gemm_common.h", "common.h"):
         with open(os.path.join(ROOT, "sparse_mixture_experts_rmsnorm_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -64,6 +65,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mixtral_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mx", action="store_true",
+                    help="skip the MXFP8 variant of a grouped bf16 workload")
     ap.add_argument("--cpu-sample", type=int, default=4096,
                     help="tokens whose expert FFNs the CPU oracle computes")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -147,6 +150,63 @@ def time_router_extras(B, wl, layer, x, out, ws, steps):
                     "and the three squared-CV statistics"}
 
 
+def time_layer(B, layer, x, out, ws, stats, steps, warmup):
+    """W untimed forwards, then K timed ones bracketed by device syncs; the
+    per-stage times come from the library's hipEvents on its own stream."""
+    import torch
+    for _ in range(warmup):
+        layer.forward(x, out=out, ws=ws, stats=stats)
+    torch.cuda.synchronize()
+    timer = B.StageTimer(steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer.forward(x, out=out, ws=ws, stats=stats, timer=timer)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stages = {}
+    for s in B.STAGES:
+        tot, n = timer.stage_ms(s)
+        stages[s] = tot / max(n, 1)
+    timer.close()
+    return (t1 - t0) * 1e3 / steps, stages
+
+
+def expert_kept(wl, layer, ws):
+    """Rows each expert computes, without padding rows."""
+    rt = layer.routing(wl.T, ws)
+    counts = rt["counts"].cpu().numpy()
+    offsets = rt["offsets"].cpu().numpy()
+    kept = [int(offsets[e + 1] - offsets[e]) for e in range(wl.E)]
+    if wl.pad > 1:
+        kept = [int(min(c, offsets[e + 1] - offsets[e])) for e, c in enumerate(counts)]
+    return kept, offsets
+
+
+def mx_variant(B, wl, params, x, steps, warmup):
+    """The same layer and weights with MXFP8 routed experts (E4M3 operands,
+    E8M0 block scales, fp32 accumulation on the scaled MFMA)."""
+    import torch
+    from sparse_mixture_experts_rmsnorm_amd.layer import MoELayer
+    wq = wl.scaled(name=wl.name.replace("bf16", "mxfp8"), quant="mxfp8")
+    layer = MoELayer(wq, params, x.device)
+    ws = layer.alloc_workspace(wq.T)
+    out = torch.empty_like(x)
+    stats = torch.zeros(4, dtype=torch.int32, device=x.device)
+    ms, stages = time_layer(B, layer, x, out, ws, stats, steps, warmup)
+    kept, _ = expert_kept(wq, layer, ws)
+    f1, f2 = flops_gemm1(wq, kept), flops_gemm2(wq, kept)
+    g1, g2 = stages["gemm1"], stages["gemm2"]
+    res = {"workload": wq.name, "ms_per_step": ms, "tokens_per_s": wq.T / (ms * 1e-3),
+           "stages_ms": stages, "gemm1_tflops": f1 / (g1 * 1e-3) / 1e12,
+           "gemm2_tflops": f2 / (g2 * 1e-3) / 1e12,
+           "frac_fp8_peak": (f1 + f2) / ((g1 + g2) * 1e-3) / 1e12 / PEAK_TFLOPS["mxfp8"],
+           "note": "gemm1 includes the per-slot MXFP8 quantisation of the gathered rows"}
+    del layer, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(wl, params, sample_tokens):
     """The oracle, as it stands, on a bounded sample of the same workload."""
     import numpy as np
@@ -168,6 +228,8 @@ def cpu_baseline(wl, params, sample_tokens):
                  w3=host.get("w3"), w2=host["w2"], f_offsets=wl.f_offsets)
     if wl.shared_ffn:
         p.update(ws1=host["ws1"], ws3=host.get("ws3"), ws2=host["ws2"], shared_act=wl.shared_act)
+    if wl.quant != "none":
+        p.update(quant=wl.quant)
     rng = np.random.default_rng(0)
     tok = np.sort(rng.choice(wl.T, size=min(sample_tokens, wl.T), replace=False))
     t0 = time.perf_counter()
@@ -206,30 +268,10 @@ def main():
     ws = layer.alloc_workspace(wl.T)
     out = torch.empty_like(x)
     stats = torch.zeros(4, dtype=torch.int32, device=dev)
-    for _ in range(args.warmup):
-        layer.forward(x, out=out, ws=ws, stats=stats)
-    torch.cuda.synchronize()
-
-    timer = B.StageTimer(args.steps)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        layer.forward(x, out=out, ws=ws, stats=stats, timer=timer)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    stages = {}
-    for s in B.STAGES:
-        tot, n = timer.stage_ms(s)
-        stages[s] = tot / max(n, 1)
-    timer.close()
-
+    ms_per_step, stages = time_layer(B, layer, x, out, ws, stats, args.steps, args.warmup)
     st = stats.cpu().numpy().tolist()
-    rt = layer.routing(wl.T, ws)
-    counts = rt["counts"].cpu().numpy()
-    offsets = rt["offsets"].cpu().numpy()
     tokens_per_s = wl.T / (ms_per_step / 1e3)
-    dtype = "bf16" if wl.dtype == "bf16" else "f32"
+    dtype = "f32" if wl.dtype == "f32" else ("mxfp8" if wl.quant == "mxfp8" else "bf16")
 
     result = {
         "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
@@ -239,15 +281,12 @@ def main():
         "config": {"workload": wl.name, "tokens": wl.T, "d_model": wl.d, "experts": wl.E,
                    "top_k": wl.k, "d_ffn": wl.sizes[0] if wl.sizes else 1, "act": wl.act,
                    "capacity_factor": wl.cf, "expert_kind": wl.expert_kind,
-                   "router": wl.router, "shared_ffn": wl.shared_ffn},
+                   "router": wl.router, "shared_ffn": wl.shared_ffn, "quant": wl.quant},
         "stages_ms": stages,
         "routing": {"rows": st[0], "dropped": st[1], "max_load": st[2], "errors": st[3]},
     }
     if wl.expert_kind != "atomic":
-        pad = wl.pad
-        kept = [int(offsets[e + 1] - offsets[e]) for e in range(wl.E)]
-        if pad > 1:   # algorithmic work excludes the padding rows
-            kept = [int(min(c, offsets[e + 1] - offsets[e])) for e, c in enumerate(counts)]
+        kept, offsets = expert_kept(wl, layer, ws)
         f1, f2 = flops_gemm1(wl, kept), flops_gemm2(wl, kept)
         g1, g2 = stages["gemm1"], stages["gemm2"]
         a1 = f1 / (g1 * 1e-3) / 1e12
@@ -260,9 +299,12 @@ def main():
                               "unit": "TFLOP/s", "frac": a1 / PEAK_TFLOPS[dtype],
                               "traffic": measured_traffic(wl.name),
                               "traffic_unit": "bytes per launch (HBM, from PMC counters)",
-                              "kernel": "k_gemm_bf16_dma (first expert linear, SwiGLU epilogue)",
+                              "kernel": ("k_gemm_mx (first expert linear, SwiGLU epilogue, "
+                                         "MXFP8; includes the row quantiser)"
+                                         if dtype == "mxfp8" else
+                                         "k_gemm_bf16_dma (first expert linear, SwiGLU epilogue)"),
                               "algorithmic_flop_per_launch": f1}
-        es = 2 if dtype == "bf16" else 4
+        es = 4 if dtype == "f32" else 2
         rows = int(offsets[-1])
         # combine: read every kept expert row (two K-split planes when the second
         # GEMM is split), read x, write out; the layer's dispatch moves indices
@@ -280,6 +322,11 @@ def main():
                      "row once, write each permuted row once) timed on the layer's ids")}
     if wl.router == "dense":
         result["router_extras"] = time_router_extras(B, wl, layer, x, out, ws, args.steps)
+    if (not args.no_mx and wl.expert_kind == "grouped" and wl.dtype == "bf16"
+            and wl.quant == "none" and all(f % 128 == 0 for f in wl.sizes)):
+        del layer, ws
+        torch.cuda.empty_cache()
+        result["mxfp8_variant"] = mx_variant(B, wl, params, x, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, params, args.cpu_sample)
     print(json.dumps(result))

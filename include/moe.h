@@ -82,6 +82,7 @@ enum { MOE_F32 = 0, MOE_BF16 = 1 };
 enum { MOE_ACT_GELU = 0, MOE_ACT_GELU_TANH = 1, MOE_ACT_SWIGLU = 2 };
 enum { MOE_ROUTER_DENSE = 0, MOE_ROUTER_CARTESIAN = 1 };
 enum { MOE_EXPERTS_GROUPED = 0, MOE_EXPERTS_BCSR = 1, MOE_EXPERTS_ATOMIC = 2 };
+enum { MOE_QUANT_NONE = 0, MOE_QUANT_MXFP8 = 1 };
 
 /* Counters written by moe_dispatch (device memory, overwritten each call).
  * A layer of ATOMIC experts runs no dispatch: it writes rows = T*k slots,
@@ -132,6 +133,20 @@ typedef struct moe_experts_desc {
   const int32_t* block_offsets; /* [E+1] prefix sum of size_blocks            */
   const int32_t* row_offsets;   /* [rows_max/block + 1] CSR row pointer       */
   const int32_t* column_indices;/* [nnz_max] column block of each nonzero     */
+  /* MOE_QUANT_MXFP8 (GROUPED, bf16 layers only): w13_t and w2_t hold E4M3
+   * codes (one byte per element, same packed layouts) and w13_scale [P, d/32],
+   * w2_scale [d, F/32] their E8M0 block scales, as written by moe_pack_mxfp8
+   * from the bf16 packs (P = F, or 2F for SwiGLU).  Following the CODA
+   * thread's point that low-precision conversions are free in epilogues, the
+   * expert rows are quantised once per (token, slot) as they are gathered,
+   * the first linear's epilogue writes the hidden activation h as MXFP8, and
+   * both GEMMs run on the scaled MFMA with fp32 accumulators; r, gates,
+   * expert outputs and the layer output stay as in the bf16 path.  Needs
+   * every ffn size a multiple of 128.  MOE_QUANT_NONE: the fields below are
+   * ignored. */
+  int quant;
+  const uint8_t* w13_scale;
+  const uint8_t* w2_scale;
 } moe_experts_desc;
 
 /* Results of moe_dispatch, consumed by moe_expert_gemm and moe_combine. */
@@ -236,6 +251,20 @@ int moe_pack_transpose(const void* src, int dtype, int64_t K, int64_t N, void* d
  * groups of 32 rows (ffn_sizes [host] [E], each a multiple of 32). */
 int moe_pack_swiglu(const void* w1, const void* w3, int dtype, int64_t d,
                     const int64_t* ffn_sizes, int64_t E, void* w13_t, hipStream_t stream);
+
+/* MXFP8 pack (OCP Microscaling format, MXFP8 with E4M3 elements): each row
+ * of the bf16 matrix src [R, K] (row stride lds elements) is cut into blocks
+ * of 32 consecutive elements; a block's shared exponent is
+ * s = floor(log2(max |v|)) - 8 (the largest E4M3 normal is 1.75 * 2^8),
+ * clamped to [-127, 127] (-127 for an all-zero block), stored as the E8M0
+ * byte s + 127 in scales [R, K/32] (row stride ldsc bytes); its elements are
+ * stored as the E4M3 code (bias 7, 3 mantissa bits, subnormals on the 2^-9
+ * grid) of v * 2^-s rounded to nearest-even, magnitudes of 448 and above
+ * saturated to 448, in codes [R, K] (row stride ldc bytes).  K % 32 == 0,
+ * ldc % 8 == 0.  Used once on the packed expert weights (w13_t, w2_t); the
+ * layer quantises its activations with the same kernel. */
+int moe_pack_mxfp8(const void* src, int64_t R, int64_t K, int64_t lds, void* codes, int64_t ldc,
+                   void* scales, int64_t ldsc, hipStream_t stream);
 
 /* ---- step 1: RMSNorm statistic ----
  * r[T] fp32.  If gamma is non-NULL, also writes xg[T, d] = x * gamma (dtype,

@@ -17,11 +17,12 @@ MOE_F32, MOE_BF16 = 0, 1
 ACT = {"gelu": 0, "gelu_tanh": 1, "swiglu": 2}
 ROUTER_DENSE, ROUTER_CARTESIAN = 0, 1
 EXPERTS_GROUPED, EXPERTS_BCSR, EXPERTS_ATOMIC = 0, 1, 2
+QUANT_NONE, QUANT_MXFP8 = 0, 1
 STAGES = ["router", "dispatch", "plan", "gemm1", "gemm2", "shared", "combine"]
 
 EXPORTED = [
     "moe_last_error", "moe_version", "moe_capacity", "moe_rows_max", "moe_pack_transpose",
-    "moe_pack_swiglu", "moe_rmsnorm_stats", "moe_router_workspace_size", "moe_router_topk",
+    "moe_pack_swiglu", "moe_pack_mxfp8", "moe_rmsnorm_stats", "moe_router_workspace_size", "moe_router_topk",
     "moe_router_topk_ex",
     "moe_dispatch_workspace_size", "moe_dispatch", "moe_topology_nnz_max", "moe_build_topology",
     "moe_expert_workspace_size", "moe_expert_gemm", "moe_shared_workspace_size", "moe_shared_ffn",
@@ -40,7 +41,8 @@ class ExpertsDesc(C.Structure):
                 ("ffn_sizes", C.POINTER(C.c_int64)), ("ffn_offsets", C.c_void_p),
                 ("w13_t", C.c_void_p), ("w2_t", C.c_void_p), ("W", C.c_void_p), ("V", C.c_void_p),
                 ("block", C.c_int), ("size_blocks", C.c_void_p), ("block_offsets", C.c_void_p),
-                ("row_offsets", C.c_void_p), ("column_indices", C.c_void_p)]
+                ("row_offsets", C.c_void_p), ("column_indices", C.c_void_p),
+                ("quant", C.c_int), ("w13_scale", C.c_void_p), ("w2_scale", C.c_void_p)]
 
 
 class Routing(C.Structure):
@@ -88,6 +90,7 @@ def lib() -> C.CDLL:
             "moe_rows_max": (I64, [I64, I, I64, I64, I]),
             "moe_pack_transpose": (I, [P, I, I64, I64, P, P]),
             "moe_pack_swiglu": (I, [P, P, I, I64, C.POINTER(I64), I64, P, P]),
+            "moe_pack_mxfp8": (I, [P, I64, I64, I64, P, I64, P, I64, P]),
             "moe_rmsnorm_stats": (I, [P, I, I64, I64, P, F, P, P, P]),
             "moe_router_workspace_size": (SZ, [C.POINTER(RouterDesc), I64]),
             "moe_router_topk": (I, [C.POINTER(RouterDesc), P, I, I64, I64, P, F, P, I, I, P, P, P,
@@ -190,6 +193,16 @@ def pack_swiglu(w1, w3, ffn_sizes, dst, stream=None) -> None:
     arr = i64_array(ffn_sizes)
     check(lib().moe_pack_swiglu(ptr(w1), ptr(w3), dtype_code(w1), d, arr, len(ffn_sizes), ptr(dst),
                                 stream_handle(stream)))
+
+
+def pack_mxfp8(src, codes, scales, stream=None) -> None:
+    """MXFP8 codes [R, K] (uint8) and E8M0 block scales [R, K/32] (uint8) of
+    the rows of a bf16 matrix src [R, K]."""
+    R, K = src.shape
+    assert src.stride(1) == 1 and codes.stride(1) == 1 and scales.stride(1) == 1
+    assert tuple(codes.shape) == (R, K) and tuple(scales.shape) == (R, K // 32)
+    check(lib().moe_pack_mxfp8(ptr(src), R, K, src.stride(0), ptr(codes), codes.stride(0),
+                               ptr(scales), scales.stride(0), stream_handle(stream)))
 
 
 def rmsnorm_stats(x, eps, r, gamma=None, xg=None, stream=None) -> None:

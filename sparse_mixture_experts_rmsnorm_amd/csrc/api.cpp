@@ -75,6 +75,8 @@ struct ExpertGeo {
   int bt2 = 256;       // rows per tile of the second linear (128 fills a small dense layer)
   int fold = 1;        // first-linear output columns = packed features / fold
   bool bcsr = false, atomic = false;
+  bool mx = false;     // MXFP8 operands (E4M3 codes + E8M0 block scales)
+  bool mx_split = false;   // every ffn size a multiple of 256: K halves stay whole stages
 };
 
 int check_experts(const moe_experts_desc* X, int dtype, int64_t d, ExpertGeo* g) {
@@ -131,6 +133,24 @@ int check_experts(const moe_experts_desc* X, int dtype, int64_t d, ExpertGeo* g)
     geo.Fmax = std::max(geo.Fmax, f);
   }
   REQUIRE(geo.F < (int64_t(1) << 31) / 2, MOE_ESHAPE, "total ffn width too large");
+  REQUIRE(X->quant == MOE_QUANT_NONE || X->quant == MOE_QUANT_MXFP8, MOE_EDTYPE,
+          "unknown quant %d", X->quant);
+  if (X->quant == MOE_QUANT_MXFP8) {
+    REQUIRE(dtype == MOE_BF16 && !geo.bcsr, MOE_EUNSUPPORTED,
+            "MXFP8 experts are implemented for bf16 grouped experts");
+    REQUIRE(X->w13_scale && X->w2_scale, MOE_EINVAL, "MXFP8 experts need w13_scale and w2_scale");
+    geo.mx = true;
+    geo.mx_split = true;
+    for (int64_t e = 0; e < X->E; ++e) {
+      REQUIRE(X->ffn_sizes[e] % 128 == 0, MOE_ESHAPE,
+              "MXFP8 ffn sizes must be multiples of 128 (expert %lld: %lld)", (long long)e,
+              (long long)X->ffn_sizes[e]);
+      geo.mx_split = geo.mx_split && X->ffn_sizes[e] % 256 == 0;
+    }
+    // the kernels address operands with 32-bit byte offsets
+    REQUIRE(geo.F * geo.pf * d < (int64_t(1) << 31) && geo.F * d < (int64_t(1) << 31), MOE_ESHAPE,
+            "MXFP8 weights must stay below 2 GiB per matrix");
+  }
   if (geo.bcsr) {
     REQUIRE(X->block == 128, MOE_EUNSUPPORTED, "BCSR block must be 128 (got %d)", X->block);
     REQUIRE(X->size_blocks && X->block_offsets, MOE_EINVAL, "BCSR needs size_blocks and block_offsets");
@@ -159,6 +179,8 @@ int64_t nnz_max_of(const moe_experts_desc* X, int64_t rows_max) {
   return (rows_max / 128) * sbmax;
 }
 
+constexpr int64_t kMxRowPad = 256;   // rows per MXFP8 GEMM tile
+
 struct ExpertWs {
   void* h = nullptr;
   Tile* tiles1 = nullptr;
@@ -169,6 +191,12 @@ struct ExpertWs {
   int ksplit = 1;        // K halves of the second linear
   void* ypart = nullptr;   // [ksplit][rows_max][d] gated partials (ksplit 2), dtype
   int64_t plane = 0;
+  int64_t rows_max = 0;
+  // MXFP8: the quantised GEMM rows and hidden activation with their scales
+  uint8_t* xq = nullptr;   // [rows_max, d]
+  uint8_t* xqs = nullptr;  // [rows_max, d / 32]
+  uint8_t* hq = nullptr;   // [rows_max, Fmax]
+  uint8_t* hqs = nullptr;  // [rows_max, Fmax / 32]
 };
 
 // Compute units of the current device (cached; a host query, no sync).
@@ -188,7 +216,7 @@ int device_cus() {
 // A dense layer (the shared FFN) whose second linear has fewer 256-row tiles
 // than compute units takes 128-row tiles there instead.
 void fit_dense_tiles(ExpertGeo* g, int dtype, int64_t d, int64_t T) {
-  if (dtype != MOE_BF16 || g->bcsr || g->atomic) return;
+  if (dtype != MOE_BF16 || g->bcsr || g->atomic || g->mx) return;
   const int64_t tiles = (T + 255) / 256 * (d / g->bf2);
   if (tiles < device_cus()) g->bt2 = 128;
 }
@@ -198,7 +226,7 @@ void fit_dense_tiles(ExpertGeo* g, int dtype, int64_t d, int64_t T) {
 // slice) and splits K in two when that evens out the last round of tiles
 // across the compute units (the two fp32 partials are summed by combine).
 int choose_ksplit(const ExpertGeo& g, int dtype, int64_t d, int64_t rows_used_est) {
-  if (g.bcsr || g.atomic || dtype != MOE_BF16) return 1;
+  if (g.bcsr || g.atomic || dtype != MOE_BF16 || (g.mx && !g.mx_split)) return 1;
   const double cus = device_cus();
   const double n = (double(rows_used_est) / g.bt + 0.5 * double(g.E)) * double(d / g.bf2);
   auto eff = [&](double t) { return t <= 0 ? 1.0 : (t / cus) / std::ceil(t / cus); };
@@ -218,7 +246,18 @@ void carve_expert_ws(Carve& c, const ExpertGeo& g, int dtype, int64_t d, int64_t
     w->plane = rows_max * d;
     w->ypart = c.take(size_t(ksplit * w->plane) * esize(dtype));
   }
-  w->h = c.take(size_t(rows_max) * g.Fmax * esize(dtype));
+  w->rows_max = rows_max;
+  if (g.mx) {
+    // a tile reads all of its 256 rows (the ones past the group's end are
+    // never stored), so the MXFP8 row buffers carry one tile of spare rows
+    const int64_t rp = rows_max + kMxRowPad;
+    w->xq = c.take_n<uint8_t>(rp * d);
+    w->xqs = c.take_n<uint8_t>(rp * (d / 32));
+    w->hq = c.take_n<uint8_t>(rp * g.Fmax);
+    w->hqs = c.take_n<uint8_t>(rp * (g.Fmax / 32));
+  } else {
+    w->h = c.take(size_t(rows_max) * g.Fmax * esize(dtype));
+  }
   w->tiles1 = c.take_n<Tile>(w->mt1);
   w->tiles2 = c.take_n<Tile>(w->mt2);
   w->nt = c.take_n<int>(2);
@@ -246,6 +285,73 @@ namespace {
 void timer_mark(moe_timer* t, int call, int idx, hipStream_t s) {
   if (!t || call < 0) return;
   (void)hipEventRecord(t->ev[size_t(call) * (MOE_STAGE_COUNT + 1) + idx], s);
+}
+
+// MXFP8 experts: the GEMM rows are quantised as they are gathered (xrow, or
+// the rows themselves), the first linear writes MXFP8 h, the second reads it.
+int run_expert_gemms_mx(const moe_experts_desc* X, const ExpertGeo& g, int64_t d,
+                        const int32_t* offsets, int dense_rows, const void* x_in,
+                        const float* row_r, const float* row_w, void* y, const ExpertWs& w,
+                        hipStream_t s, moe_timer* timer, int call, const int32_t* xrow) {
+  const int64_t R = w.rows_max, RP = R + kMxRowPad;
+  const int64_t P = g.F * g.pf;
+  if (std::max(RP * d, RP * g.Fmax) >= (int64_t(1) << 31))
+    return fail(MOE_ESHAPE, "MXFP8 row buffers must stay below 2 GiB (rows %lld)", (long long)R);
+  MOE_HIP(launch_quant_mx(x_in, R, d, d, xrow, offsets ? offsets + X->E : nullptr, w.xq, d, w.xqs,
+                          d / 32, s));
+  MxGemmArgs a{};
+  a.g.X = w.xq;
+  a.g.ldx = d;
+  a.g.W = X->w13_t;
+  a.g.ldw = d;
+  a.g.tiles = w.tiles1;
+  a.g.ntiles = w.nt;
+  a.g.Y = w.hq;
+  a.g.ldy = g.Fmax;
+  a.g.row_r = row_r;
+  a.g.epi = X->act == MOE_ACT_SWIGLU ? EPI_SWIGLU : EPI_ACT;
+  a.g.act = X->act == MOE_ACT_GELU_TANH ? 1 : 0;
+  a.xs = w.xqs;
+  a.ldxs = d / 32;
+  a.ws = X->w13_scale;
+  a.ldws = d / 32;
+  a.ys = w.hqs;
+  a.ldys = g.Fmax / 32;
+  a.x_bytes = RP * d;
+  a.w_bytes = P * d;
+  a.xs_bytes = RP * (d / 32);
+  a.ws_bytes = P * (d / 32);
+  MOE_HIP(launch_gemm_mx(a, int(w.mt1), s));
+  timer_mark(timer, call, MOE_STAGE_GEMM1 + 1, s);
+
+  MxGemmArgs b{};
+  b.g.X = w.hq;
+  b.g.ldx = g.Fmax;
+  b.g.W = X->w2_t;
+  b.g.ldw = g.F;
+  b.g.tiles = w.tiles2;
+  b.g.ntiles = w.nt + 1;
+  b.g.Y = y;
+  b.g.ldy = d;
+  b.g.row_w = row_w;
+  b.g.epi = EPI_GATE;
+  if (w.ksplit > 1) {
+    b.g.epi = EPI_GATE_SPLIT;
+    b.g.Y = w.ypart;
+    b.g.ysplit = w.plane;
+  }
+  b.xs = w.hqs;
+  b.ldxs = g.Fmax / 32;
+  b.ws = X->w2_scale;
+  b.ldws = g.F / 32;
+  b.x_bytes = RP * g.Fmax;
+  b.w_bytes = d * g.F;
+  b.xs_bytes = RP * (g.Fmax / 32);
+  b.ws_bytes = d * (g.F / 32);
+  MOE_HIP(launch_gemm_mx(b, int(w.mt2), s));
+  timer_mark(timer, call, MOE_STAGE_GEMM2 + 1, s);
+  (void)dense_rows;
+  return MOE_OK;
 }
 
 int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, int64_t d,
@@ -287,6 +393,9 @@ int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, i
   p.bt = g.bt2;
   MOE_HIP(launch_plan(p, s));
   timer_mark(timer, call, MOE_STAGE_PLAN + 1, s);
+
+  if (g.mx) return run_expert_gemms_mx(X, g, d, offsets, dense_rows, x_in, row_r, row_w, y, w, s,
+                                       timer, call, xrow);
 
   GemmArgs a{};
   a.X = x_in;
@@ -392,6 +501,19 @@ int moe_pack_swiglu(const void* w1, const void* w3, int dtype, int64_t d, const 
     F += ffn_sizes[e];
   }
   MOE_HIP(launch_pack_swiglu(w1, w3, dtype, d, F, nullptr, ffn_sizes, E, w13_t, stream));
+  return ok();
+}
+
+int moe_pack_mxfp8(const void* src, int64_t R, int64_t K, int64_t lds, void* codes, int64_t ldc,
+                   void* scales, int64_t ldsc, hipStream_t stream) {
+  REQUIRE(R >= 0 && K > 0 && K % 32 == 0, MOE_ESHAPE, "MXFP8 pack needs K %% 32 == 0 (K=%lld)",
+          (long long)K);
+  REQUIRE(lds >= K && lds % 8 == 0 && ldc >= K && ldc % 8 == 0 && ldsc >= K / 32, MOE_ESHAPE,
+          "bad row strides (lds %% 8 == 0 and ldc %% 8 == 0 needed)");
+  REQUIRE(R == 0 || (src && codes && scales), MOE_EINVAL, "NULL pointer");
+  REQUIRE(reinterpret_cast<uintptr_t>(src) % 16 == 0 && reinterpret_cast<uintptr_t>(codes) % 8 == 0,
+          MOE_EINVAL, "src must be 16-byte and codes 8-byte aligned");
+  MOE_HIP(launch_quant_mx(src, R, K, lds, nullptr, nullptr, codes, ldc, scales, ldsc, stream));
   return ok();
 }
 

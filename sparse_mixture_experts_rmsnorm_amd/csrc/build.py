@@ -20,7 +20,7 @@ ROOT = PKG.parent
 BUILD = PKG / "_build"
 LIB = PKG / "libmoe_mi355x.so"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["router.hip", "dispatch.hip", "topology.hip", "gemm.hip", "combine.hip",
+SOURCES = ["router.hip", "dispatch.hip", "topology.hip", "gemm.hip", "gemm_mx.hip", "combine.hip",
            "atomic.hip", "api.cpp"]
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"-I{ROOT / 'include'}", f"-I{HERE}",
           "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]

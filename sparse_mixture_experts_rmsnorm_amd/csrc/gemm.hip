@@ -35,17 +35,12 @@
 #include <algorithm>
 
 #include "common.h"
+#include "gemm_common.h"
 #include "internal.h"
 
 namespace moe {
 namespace {
 
-
-__device__ __forceinline__ int remap_xcd(int b, int nt) {
-  const int xcd = b & 7, slot = b >> 3;
-  const int q = nt >> 3, rem = nt & 7;
-  return xcd * q + min(xcd, rem) + slot;
-}
 
 __device__ __forceinline__ float apply_act(float z, int act) {
   return act == 1 ? gelu_tanh(z) : gelu_erf(z);
@@ -124,40 +119,6 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const Tile& til
 }
 
 // ---------------------------------------------------------------- bf16 MFMA GEMM, LDS-DMA ring
-
-typedef __attribute__((address_space(3))) void* lds_void_ptr;
-typedef __attribute__((address_space(1))) const void* global_void_ptr;
-
-// s_waitcnt vmcnt(n) with the other counters left free (gfx9 encoding).
-#define MOE_WAIT_VMCNT(n) \
-  __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
-
-// Swizzle of 16-byte chunk q in row r for C chunks per row: any 16 consecutive
-// rows read at one logical chunk land in 16 distinct 16-byte bank groups.  It
-// depends on r & 15 only, so a fragment read (rows base + lane & 31, base a
-// multiple of 32) can compute it from the lane index.
-template <int C>
-__device__ __forceinline__ int chunk_swz(int r) {
-  if constexpr (C == 8) return (r & 7) ^ ((r >> 3) & 1);
-  else return (r >> 2) & 3;
-}
-
-// Scheduling pattern for one K sub-step: NR fragment reads of the next
-// sub-step spread over the first MFMAs of this one (one MFMA, two reads, ...),
-// then the remaining MFMAs, so that the reads are in flight under MFMAs and
-// have had most of the sub-step to land before they are waited for.
-template <int NR, int NM>
-__device__ __forceinline__ void sched_interleave() {
-  if constexpr (NR > 0 && NM > 0) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, NR >= 2 ? 2 : 1, 0);
-    sched_interleave<NR - (NR >= 2 ? 2 : 1), NM - 1>();
-  } else if constexpr (NR > 0) {
-    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
-  } else if constexpr (NM > 0) {
-    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
-  }
-}
 
 // BF features x BT rows per workgroup, WGF x WGT waves, each wave a
 // (BF / WGF) x (BT / WGT) sub-tile of 32 x 32 MFMA blocks.  Global -> LDS

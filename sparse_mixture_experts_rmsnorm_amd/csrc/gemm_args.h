@@ -54,6 +54,19 @@ struct PlanArgs {
   int block;
 };
 
+// MXFP8 GEMM: X and W hold E4M3 codes (ldx / ldw in bytes), xs / ws their
+// E8M0 block scales [rows, K / 32]; the first-linear epilogues write MXFP8 h
+// (codes to Y with ldy bytes, scales to ys), the gate epilogues bf16 Y.
+struct MxGemmArgs {
+  GemmArgs g;
+  const uint8_t* xs; int64_t ldxs;
+  const uint8_t* ws; int64_t ldws;
+  uint8_t* ys; int64_t ldys;
+  // byte extents of X, W, xs and ws (each below 2 GiB: the kernel reads
+  // them through buffer resources with 32-bit offsets)
+  int64_t x_bytes, w_bytes, xs_bytes, ws_bytes;
+};
+
 hipError_t launch_plan(const PlanArgs& p, hipStream_t s);
 hipError_t launch_gemm(int dtype, const GemmArgs& a, int bf, int bt, int grid, hipStream_t s);
 int gemm_tile_bf(int dtype);   // packed features per tile the GEMM kernels use

@@ -8,6 +8,15 @@
 
 namespace moe {
 
+// MXFP8 (gemm_mx.hip): bf16 rows [R, K] (row stride lds) -> E4M3 codes
+// [R, K] (stride ldc) and E8M0 scales [R, K / 32] (stride ldsc); the GEMM.
+// Output row r reads source row map[r] (map NULL: r; -1: zeros); rows at or
+// past *rows_used (when given) are left untouched.
+hipError_t launch_quant_mx(const void* src, int64_t R, int64_t K, int64_t lds, const int32_t* map,
+                           const int32_t* rows_used, void* codes, int64_t ldc, void* scales,
+                           int64_t ldsc, hipStream_t s);
+hipError_t launch_gemm_mx(const MxGemmArgs& m, int grid, hipStream_t s);
+
 hipError_t launch_pack_transpose(const void* src, int dtype, int64_t K, int64_t N, void* dst,
                                  hipStream_t s);
 hipError_t launch_pack_swiglu(const void* w1, const void* w3, int dtype, int64_t d, int64_t F,

@@ -63,7 +63,7 @@ class MoELayer:
         X = desc.experts
         self._fill_experts(X, wl, params, keep, "w1", "w3", "w2", wl.sizes, wl.act,
                            {"grouped": B.EXPERTS_GROUPED, "bcsr": B.EXPERTS_BCSR,
-                            "atomic": B.EXPERTS_ATOMIC}[wl.expert_kind])
+                            "atomic": B.EXPERTS_ATOMIC}[wl.expert_kind], wl.quant)
         # shared experts
         self.shared_desc = None
         if wl.shared_ffn:
@@ -76,7 +76,7 @@ class MoELayer:
         self._keep = keep
         torch.cuda.current_stream().synchronize()
 
-    def _fill_experts(self, X, wl, params, keep, n1, n3, n2, sizes, act, kind):
+    def _fill_experts(self, X, wl, params, keep, n1, n3, n2, sizes, act, kind, quant="none"):
         import torch
         d = wl.d
         X.kind = kind
@@ -107,6 +107,21 @@ class MoELayer:
             B.pack_transpose(params[n1], w13)
         w2t = torch.empty((d, F), dtype=self.tdtype, device=self.device)
         B.pack_transpose(params[n2], w2t)
+        if quant == "mxfp8":
+            # E4M3 codes + E8M0 block scales along K of each packed row
+            packed = []
+            for w in (w13, w2t):
+                q = torch.empty(w.shape, dtype=torch.uint8, device=self.device)
+                sc = torch.empty((w.shape[0], w.shape[1] // 32), dtype=torch.uint8,
+                                 device=self.device)
+                B.pack_mxfp8(w, q, sc)
+                packed.append((q, sc))
+            torch.cuda.current_stream().synchronize()
+            (w13, s13), (w2t, s2) = packed
+            X.quant = B.QUANT_MXFP8
+            X.w13_scale = s13.data_ptr()
+            X.w2_scale = s2.data_ptr()
+            keep += [s13, s2]
         X.w13_t = w13.data_ptr()
         X.w2_t = w2t.data_ptr()
         keep += [w13, w2t]

@@ -51,6 +51,7 @@ class Workload:
     gamma: bool = False            # draw a non-trivial RMSNorm gain
     seed: int = 0
     w_std: float = 0.02
+    quant: str = "none"            # "none" or "mxfp8" (routed and shared grouped experts)
 
     @property
     def sizes(self) -> list:
@@ -85,6 +86,8 @@ WORKLOADS = {
                           ffn=256, cf=0.0, seed=1001),
     "mixtral_bf16": Workload("mixtral_bf16", T=4096, d=4096, E=8, k=2, act="swiglu",
                              ffn=14336, cf=1.25, seed=1002),
+    "mixtral_mxfp8": Workload("mixtral_mxfp8", T=4096, d=4096, E=8, k=2, act="swiglu",
+                              ffn=14336, cf=1.25, quant="mxfp8", seed=1002),
     "variable_bcsr_bf16": Workload("variable_bcsr_bf16", T=8192, d=768, E=8, k=2, act="gelu",
                                    expert_sizes=((1, 2048), (7, 1024)), cf=0.0,
                                    bias="normal", expert_kind="bcsr", seed=1003),

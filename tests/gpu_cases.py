@@ -28,6 +28,11 @@ SMALL = {
                            seed=13),
     "finegrained_small": Workload("finegrained_small", T=500, d=256, E=64, k=6, act="swiglu",
                                   ffn=128, cf=1.5, bias="zipf", shared_ffn=256, seed=14),
+    "mixtral_small_mxfp8": Workload("mixtral_small_mxfp8", T=700, d=512, E=8, k=2,
+                                    act="swiglu", ffn=640, cf=1.25, quant="mxfp8", seed=19),
+    "gelu_mxfp8_split": Workload("gelu_mxfp8_split", T=333, d=256, E=4, k=2, act="gelu",
+                                 ffn=512, cf=1.0, bias="normal", shared_ffn=256,
+                                 shared_act="gelu", quant="mxfp8", seed=20),
     "atomic_small": Workload("atomic_small", T=200, d=512, E=128 * 128, k=8, act="gelu",
                              router="cartesian", Nr=128, Nc=128, expert_kind="atomic",
                              shared_ffn=512, shared_act="gelu", seed=15),
@@ -53,6 +58,8 @@ def oracle_params(wl: Workload, inp: dict) -> dict:
     else:
         p.update(router="dense", w_router=inp["w_router"], bias=inp.get("bias"), w1=inp["w1"],
                  w3=inp.get("w3"), w2=inp["w2"], f_offsets=wl.f_offsets)
+    if wl.quant != "none":
+        p.update(quant=wl.quant)
     if wl.shared_ffn:
         p.update(ws1=inp["ws1"], ws3=inp.get("ws3"), ws2=inp["ws2"], shared_act=wl.shared_act)
     return p

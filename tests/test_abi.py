@@ -133,6 +133,40 @@ def test_expert_descriptor_checks():
     assert lib.moe_expert_workspace_size(C.byref(X), 1, 512, 100, 2, 200) == 0
     X.act = 2
     assert lib.moe_expert_workspace_size(C.byref(X), 1, 500, 100, 2, 200) == 0   # d % 256
+    # MXFP8: scales required, bf16 grouped only, ffn sizes multiples of 128
+    n_bf16 = lib.moe_expert_workspace_size(C.byref(X), 1, 512, 100, 2, 200)
+    X.quant = B.QUANT_MXFP8
+    assert lib.moe_expert_workspace_size(C.byref(X), 1, 512, 100, 2, 200) == 0
+    assert "w13_scale" in B.last_error()
+    X.w13_scale, X.w2_scale = 16, 16
+    n_mx = lib.moe_expert_workspace_size(C.byref(X), 1, 512, 100, 2, 200)
+    assert n_mx > 0 and n_mx != n_bf16
+    assert lib.moe_expert_workspace_size(C.byref(X), 0, 512, 100, 2, 200) == 0   # f32
+    X.kind = 1
+    assert lib.moe_expert_workspace_size(C.byref(X), 1, 512, 100, 2, 200) == 0   # BCSR
+    X.kind = 0
+    sizes2 = B.i64_array([320, 256])
+    X.ffn_sizes = C.cast(sizes2, C.POINTER(C.c_int64))
+    assert lib.moe_expert_workspace_size(C.byref(X), 1, 512, 100, 2, 200) == 0
+    assert "multiples of 128" in B.last_error()
+    X.quant = 7
+    X.ffn_sizes = C.cast(sizes, C.POINTER(C.c_int64))
+    assert lib.moe_expert_workspace_size(C.byref(X), 1, 512, 100, 2, 200) == 0
+    assert "quant" in B.last_error()
+
+
+def test_mxfp8_pack_argument_checks():
+    lib = B.lib()
+    P = C.c_void_p(256)
+    rc, msg = _err(lib.moe_pack_mxfp8(P, 4, 48, 48, P, 48, P, 2, None))
+    assert rc == -2 and "K % 32" in msg
+    rc, msg = _err(lib.moe_pack_mxfp8(P, 4, 64, 60, P, 64, P, 2, None))
+    assert rc == -2 and "strides" in msg
+    rc, _ = _err(lib.moe_pack_mxfp8(None, 4, 64, 64, P, 64, P, 2, None))
+    assert rc == -1
+    rc, msg = _err(lib.moe_pack_mxfp8(C.c_void_p(264), 4, 64, 64, P, 64, P, 2, None))
+    assert rc == -1 and "aligned" in msg
+    assert lib.moe_pack_mxfp8(None, 0, 64, 64, None, 64, None, 2, None) == 0   # nothing to do
 
 
 def test_layer_workspace_validation():

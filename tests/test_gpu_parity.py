@@ -160,10 +160,18 @@ def test_layer_parity(name, dev):
     torch.cuda.synchronize()
     p0 = dict(p, residual=False)
     ref0 = O.layer_forward(p0, inp["x"], ids_override=ids)
-    e_moe = rel_err(f64(synth.to_host(moe)), ref0["out"])
+    moe_np = f64(synth.to_host(moe))
+    e_moe = rel_err(moe_np, ref0["out"])
     _say(f"  {name}: rel err out {e_out:.2e}, experts only {e_moe:.2e}, dropped {disp['dropped']}")
     assert e_out <= tol
     assert e_moe <= tol
+    if wl.quant != "none":
+        # MXFP8 experts: the oracle's MXFP8 layer is much closer than its
+        # unquantised one (the quantisation really happens, and as specified)
+        ref_fp = O.layer_forward(dict(p0, quant=None), inp["x"], ids_override=ids)
+        e_fp = rel_err(moe_np, ref_fp["out"])
+        _say(f"  {name}: experts only vs the unquantised oracle {e_fp:.2e}")
+        assert e_moe < 0.5 * e_fp
     # fully dropped tokens pass through bit-exactly (and get exactly 0 without the
     # residual) -- unless always-on shared experts add to every token
     gone = np.all(pos < 0, axis=1)
@@ -515,3 +523,54 @@ def test_atomic_schedules_agree(dev):
                                          ids, rt["w"].cpu().numpy().astype(np.float64),
                                          O.as_f64(inp["W"]), O.as_f64(inp["V"]))
     assert rel_err(f64(synth.to_host(y_tc)), ref) < TOL["bf16"]
+
+
+def _mx_pack_input():
+    """bf16 rows that exercise the MXFP8 conversion: random magnitudes over
+    a wide exponent range, and rows of special blocks (all zero, -0, the
+    E8M0 clamp at -127, saturation above 448, round-half-even ties in the
+    normal and the subnormal range)."""
+    rng = np.random.default_rng(21)
+    R, K = 67, 1120                                  # ragged: K = 2 x 512 + 96, R % 4 = 3
+    v = rng.standard_normal((R, K)).astype(np.float32)
+    v *= np.exp2(rng.integers(-30, 30, size=(R, K // 32, 1))).repeat(32, axis=2).reshape(R, K)
+    v[0, :32] = 0.0
+    v[0, 32:64] = -0.0
+    v[0, 64:96] = np.float32(2.0 ** -125) * rng.standard_normal(32).astype(np.float32)  # clamp
+    v[0, 96:128] = np.float32(2.0 ** -131)           # bf16 subnormals under the clamp
+    # amax 256 (scale 2^0): ties 1 + 1/16 (-> 1), 1 + 3/16 (-> 1.25), 3 * 2^-10 (-> 2^-8),
+    # 2^-10 (-> 0), 464 is not reachable (amax < 512 maps to < 512); 448 and 480 saturate
+    v[1, :32] = 256.0
+    v[1, 1:8] = [1.0625, 1.1875, 3 * 2.0 ** -10, 2.0 ** -10, -1.0625, 5 * 2.0 ** -10, 2.0 ** -6]
+    v[1, 32:64] = 480.0                              # scale 2^0, elements at 480 -> 448
+    v[1, 40] = 500.0
+    v[1, 64:96] = np.float32(2.0 ** 120)             # large exponents
+    v[1, 96:128] = -np.float32(2.0 ** -100)
+    return synth._to_bf16_bits(v)
+
+
+def test_pack_mxfp8_bit_exact(dev):
+    """moe_pack_mxfp8 (the quantiser of the MXFP8 path) against the oracle's
+    OCP MX conversion: codes and E8M0 scales bit-exact."""
+    _say("[gpu] MXFP8 pack: codes and scales bit-exact")
+    bits = _mx_pack_input()
+    R, K = bits.shape
+    src = synth.to_device(bits, dev)
+    codes = torch.full((R, K), 0xAA, dtype=torch.uint8, device=dev)
+    scales = torch.full((R, K // 32), 0xAA, dtype=torch.uint8, device=dev)
+    B.pack_mxfp8(src, codes, scales)
+    torch.cuda.synchronize()
+    c_ref, s_ref = O.mx_quantize(O.as_f64(bits), axis=1)
+    c, s = codes.cpu().numpy(), scales.cpu().numpy()
+    bad = np.argwhere(c != c_ref)
+    assert len(bad) == 0, (bad[:8], c[tuple(bad[0])], c_ref[tuple(bad[0])])
+    assert np.array_equal(s, s_ref)
+    # a strided source and destination (a column window of a wider matrix)
+    c2 = torch.zeros((R, K + 64), dtype=torch.uint8, device=dev)
+    s2 = torch.zeros((R, K // 32 + 4), dtype=torch.uint8, device=dev)
+    wide = synth.to_device(np.hstack([bits, bits[:, :64]]), dev)
+    B.pack_mxfp8(wide[:, :K], c2[:, :K], s2[:, :K // 32])
+    torch.cuda.synchronize()
+    assert np.array_equal(c2[:, :K].cpu().numpy(), c_ref)
+    assert np.array_equal(s2[:, :K // 32].cpu().numpy(), s_ref)
+    assert not c2[:, K:].any() and not s2[:, K // 32:].any()
