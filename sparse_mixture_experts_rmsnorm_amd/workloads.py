@@ -16,6 +16,9 @@ Five layer shapes are used throughout (tests, smoke check, benchmark):
                      1024 x 1024 Cartesian router, top-32, plus a dense
                      GELU shared MLP of 4096
 
+and mixtral_mxfp8, the Mixtral-shaped layer with MXFP8 routed experts (OCP
+Microscaling: E4M3 elements, one E8M0 scale per 32 along K).
+
 The variable-size expert spec follows the "Variable-size experts" nanoMOE
 notes (configuration section: [(count, size), ...]); the capacity factor and
 top-k follow the "Mixture of Experts (MoE)" glossary; the atomic experts and
