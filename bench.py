@@ -27,35 +27,41 @@ METRIC = "MoE layer fwd tokens/s + expert-GEMM TFLOP/s (% bf16 MFMA peak), 1 MI3
 PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "f32": 157.3}
 PEAK_HBM_GBPS = 8000.0
 
-# HBM bytes per launch of the first expert GEMM on the Mixtral-shaped workload,
-# from two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)
-# scaled by what the same counters read for a plain 1 GiB device copy
-# (bench.py --copy-calibration).  Valid only for the kernel source it was
-# taken on: any change to gemm.hip or the headers it uses reports null.
+# HBM bytes per launch of the first expert GEMM, per workload, from two
+# rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) scaled by
+# what the same counters read for a plain 1 GiB device copy
+# (bench.py --copy-calibration: FETCH_SIZE 524302.4 KiB, WRITE_SIZE 1048576 KiB).
+# Valid only for the kernel sources they were taken on: any change to those
+# files reports null.
+COPY_SCALE = {"fetch": 1048576.0 / 524302.4, "write": 1048576.0 / 1048576.0}
 TRAFFIC = {
-    "workload": "mixtral_bf16",
-    "source_sha256": "f96c9ab6daf8f20ec49cb3c2efe1d92b3b29ea3002c8a64a9c0e840eb2dddee9",
-    "fetch_kib": 1888629.7, "write_kib": 229522.2,
-    "fetch_scale": 1048576.0 / 524302.4, "write_scale": 1048576.0 / 1048576.0,
+    "mixtral_bf16": {
+        "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
+                                                 "common.h"),
+        "source_sha256": "fe3256bee1a58b43d61675771aca39b4dab00fb4c65800ebdb023ae9ef9cf49e",
+        "fetch_kib": 1934593.7, "write_kib": 229534.7},
+    "mixtral_mxfp8": {
+        "kernel": "k_gemm_mx", "sources": ("gemm_mx.hip", "gemm_args.h", "gemm_common.h",
+                                           "common.h"),
+        "source_sha256": "eb17b4edbe0c4bc093c1a20e8d8f57ca59d0a954f90b950a11fcd6f705f7b4fb",
+        "fetch_kib": 1122805.5, "write_kib": 130668.3},
 }
 
 
-def gemm_source_sha256():
+def source_sha256(files):
     import hashlib
     h = hashlib.sha256()
-    for f in ("gemm.hip", "gemm_args.h", "gemm_common.h", "common.h"):
+    for f in files:
         with open(os.path.join(ROOT, "sparse_mixture_experts_rmsnorm_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
 def measured_traffic(workload):
-    t = TRAFFIC
-    if t["source_sha256"] is None or workload != t["workload"]:
+    t = TRAFFIC.get(workload)
+    if t is None or source_sha256(t["sources"]) != t["source_sha256"]:
         return None
-    if gemm_source_sha256() != t["source_sha256"]:
-        return None
-    return (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024.0
+    return (t["fetch_kib"] * COPY_SCALE["fetch"] + t["write_kib"] * COPY_SCALE["write"]) * 1024.0
 
 
 def parse():
@@ -201,7 +207,7 @@ def mx_variant(B, wl, params, x, steps, warmup):
            "stages_ms": stages, "gemm1_tflops": f1 / (g1 * 1e-3) / 1e12,
            "gemm2_tflops": f2 / (g2 * 1e-3) / 1e12,
            "frac_fp8_peak": (f1 + f2) / ((g1 + g2) * 1e-3) / 1e12 / PEAK_TFLOPS["mxfp8"],
-           "note": "gemm1 includes the per-slot MXFP8 quantisation of the gathered rows"}
+           "note": "dispatch includes the per-slot MXFP8 quantisation of the gathered rows"}
     del layer, ws
     torch.cuda.empty_cache()
     return res
@@ -300,7 +306,7 @@ def main():
                               "traffic": measured_traffic(wl.name),
                               "traffic_unit": "bytes per launch (HBM, from PMC counters)",
                               "kernel": ("k_gemm_mx (first expert linear, SwiGLU epilogue, "
-                                         "MXFP8; includes the row quantiser)"
+                                         "MXFP8 h)"
                                          if dtype == "mxfp8" else
                                          "k_gemm_bf16_dma (first expert linear, SwiGLU epilogue)"),
                               "algorithmic_flop_per_launch": f1}

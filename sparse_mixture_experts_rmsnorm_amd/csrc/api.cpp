@@ -197,6 +197,8 @@ struct ExpertWs {
   uint8_t* xqs = nullptr;  // [rows_max, d / 32]
   uint8_t* hq = nullptr;   // [rows_max, Fmax]
   uint8_t* hqs = nullptr;  // [rows_max, Fmax / 32]
+  bool xq_ready = false;   // the caller already quantised the rows into xq (the layer
+                           // does it as its dispatch gather)
 };
 
 // Compute units of the current device (cached; a host query, no sync).
@@ -297,8 +299,9 @@ int run_expert_gemms_mx(const moe_experts_desc* X, const ExpertGeo& g, int64_t d
   const int64_t P = g.F * g.pf;
   if (std::max(RP * d, RP * g.Fmax) >= (int64_t(1) << 31))
     return fail(MOE_ESHAPE, "MXFP8 row buffers must stay below 2 GiB (rows %lld)", (long long)R);
-  MOE_HIP(launch_quant_mx(x_in, R, d, d, xrow, offsets ? offsets + X->E : nullptr, w.xq, d, w.xqs,
-                          d / 32, s));
+  if (!w.xq_ready)
+    MOE_HIP(launch_quant_mx(x_in, R, d, d, xrow, offsets ? offsets + X->E : nullptr, w.xq, d,
+                            w.xqs, d / 32, s));
   MxGemmArgs a{};
   a.g.X = w.xq;
   a.g.ldx = d;
@@ -1102,6 +1105,12 @@ int moe_layer_forward(const moe_layer_desc* L, const void* x, int64_t T, void* o
     a.ws = w.disp_ws;
     a.ws_bytes = w.disp_ws_bytes;
     MOE_HIP(launch_dispatch(a, stream));
+    if (g.mx) {
+      // the MXFP8 path's gather: each routed row quantised once as it is read
+      MOE_HIP(launch_quant_mx(xhat, w.rows_max, d, d, w.row_token, w.offsets + E, w.ex.xq, d,
+                              w.ex.xqs, d / 32, stream));
+      w.ex.xq_ready = true;
+    }
   }
   timer_mark(tm, call, MOE_STAGE_DISPATCH + 1, stream);
 
