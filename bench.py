@@ -256,8 +256,8 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the MoE layer here runs on a single MI355X "
-              f"(--gpus {args.gpus} is not supported; how the layer would shard is described "
-              f"in DESIGN.md)", file=sys.stderr)
+              f"(--gpus {args.gpus} is not supported; sharding the layer over several GPUs "
+              f"is a design note of this repository, not built)", file=sys.stderr)
         sys.exit(2)
     import torch
     from sparse_mixture_experts_rmsnorm_amd import binding as B, synth

@@ -24,7 +24,7 @@ Sources (web pages; cited by title and section):
            (atomic experts, dynamic expert assembly, shared dense MLP) and
            section 2.2 (Cartesian-product router, expert-centric scheduling).
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   * RMSNorm is x * (mean(x^2) + eps)^-1/2 * gamma, eps inside the root.
   * The r-scale multiplies the accumulator of every GEMM that consumes the
     normed activation (router, W1, W3) before bias / activation; never W2.
