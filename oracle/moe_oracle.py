@@ -74,6 +74,7 @@ __all__ = [
     "cartesian_scores", "cartesian_topk", "cartesian_topk_bruteforce",
     "atomic_experts_token_centric", "atomic_experts_expert_centric",
     "combine", "layer_forward",
+    "gelu_grad", "gelu_tanh_grad", "silu_grad", "ffn_backward", "gates_backward", "layer_backward",
 ]
 
 
@@ -822,4 +823,178 @@ def layer_forward(p: dict, x, ids_override=None, tokens=None, faithful=False) ->
         shared = rnd(shared)
     out = combine(x64[tok], shared, slot_out, pos, p.get("residual", True))
     res.update(slot_out=slot_out, shared=shared, out=rnd(out), tokens=tok)
+    return res
+
+
+# --------------------------------------------------------------------------
+# The backward pass ([CODA]: the RMSNorm backward is fused into the backward
+# of the linear that consumed the normed input, and needs the saved r;
+# [VAREXP] validation list: forward / backward and gradient checks)
+# --------------------------------------------------------------------------
+
+def gelu_grad(z):
+    """d/dz of the exact GELU: Phi(z) + z * phi(z)."""
+    z = np.asarray(z, dtype=np.float64)
+    return 0.5 * (1.0 + erf(z / math.sqrt(2.0))) + z * np.exp(-0.5 * z * z) / math.sqrt(2.0 * math.pi)
+
+
+def gelu_tanh_grad(z):
+    """d/dz of the tanh form: with u = c (z + 0.044715 z^3),
+    0.5 (1 + tanh u) + 0.5 z (1 - tanh^2 u) c (1 + 3 * 0.044715 z^2)."""
+    z = np.asarray(z, dtype=np.float64)
+    c = math.sqrt(2.0 / math.pi)
+    t = np.tanh(c * (z + 0.044715 * z ** 3))
+    return 0.5 * (1.0 + t) + 0.5 * z * (1.0 - t * t) * c * (1.0 + 3.0 * 0.044715 * z * z)
+
+
+def silu_grad(z):
+    """d/dz of z * sigmoid(z): sigmoid(z) (1 + z (1 - sigmoid(z)))."""
+    z = np.asarray(z, dtype=np.float64)
+    s = 1.0 / (1.0 + np.exp(-z))
+    return s * (1.0 + z * (1.0 - s))
+
+
+def ffn_backward(xhat, r, w1, w2, act: str, dy, w3=None) -> dict:
+    """Gradients of the rows' FFN outputs y = ffn(xhat, r, ...) for the
+    upstream gradient dy of y: with a = r (xhat w1) (and u = r (xhat w3)),
+    h = act(a) (or silu(a) u), y = h w2:
+      dw2 = h^T dy,  dh = dy w2^T,
+      da = dh act'(a)  (SwiGLU: da = dh u silu'(a), du = dh silu(a)),
+      dw1 = (r xhat)^T da  (dw3 = (r xhat)^T du),
+      dxhat = r (da w1^T + du w3^T),
+      dr = sum over units of (xhat w1) da + (xhat w3) du.
+    """
+    xhat = np.asarray(xhat, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)[:, None]
+    dy = np.asarray(dy, dtype=np.float64)
+    z1 = xhat @ w1
+    a = r * z1
+    out = {}
+    if act == "swiglu":
+        z3 = xhat @ w3
+        u = r * z3
+        h = silu(a) * u
+    else:
+        h = _act(act)(a)
+    out["dw2"] = h.T @ dy
+    dh = dy @ w2.T
+    rx = r * xhat
+    if act == "swiglu":
+        da = dh * u * silu_grad(a)
+        du = dh * silu(a)
+        out["dw3"] = rx.T @ du
+        out["dxhat"] = r * (da @ w1.T + du @ w3.T)
+        out["dr"] = np.sum(z1 * da + z3 * du, axis=1)
+    else:
+        grad = {"gelu": gelu_grad, "gelu_tanh": gelu_tanh_grad}[act]
+        da = dh * grad(a)
+        out["dxhat"] = r * (da @ w1.T)
+        out["dr"] = np.sum(z1 * da, axis=1)
+    out["dw1"] = rx.T @ da
+    return out
+
+
+def gates_backward(logits, ids, renorm: int, dg) -> np.ndarray:
+    """Gradient of the router logits from the gradient of the gates (the
+    selection itself is piecewise constant).  renorm=1, g = softmax of the k
+    selected logits: dl[sel_j] = g_j (dg_j - sum_i g_i dg_i).  renorm=0,
+    g_j = P[sel_j] with P the full softmax:
+    dl[e] = P[e] (sum over j with sel_j = e of dg_j - sum_j P[sel_j] dg_j)."""
+    l = np.asarray(logits, dtype=np.float64)
+    ids = np.asarray(ids, dtype=np.int64)
+    dg = np.asarray(dg, dtype=np.float64)
+    T, E = l.shape
+    dl = np.zeros((T, E))
+    g = gates(l, ids, renorm)
+    rows = np.arange(T)[:, None]
+    if renorm:
+        s = np.sum(g * dg, axis=1, keepdims=True)
+        np.add.at(dl, (np.broadcast_to(rows, ids.shape), ids), g * (dg - s))
+    else:
+        m = l.max(axis=1, keepdims=True)
+        P = np.exp(l - m)
+        P /= P.sum(axis=1, keepdims=True)
+        s = np.sum(g * dg, axis=1, keepdims=True)
+        np.add.at(dl, (np.broadcast_to(rows, ids.shape), ids), dg)
+        dl = P * (dl - s)
+    return dl
+
+
+def layer_backward(p: dict, x, dout, ids_override=None) -> dict:
+    """Gradients of layer_forward's output for the upstream gradient dout
+    (dense router, routed grouped experts, shared experts).
+
+    Returns dx, dgamma (with a gain), dw_router [d, E], dbias [E], dw1,
+    dw3, dw2 (routed, the pages' layouts), dws1, dws3, dws2 (shared) and the
+    intermediate dg [T, k] (gates), dl [T, E] (logits), dxhat, dr.
+    The chain: dropped slots get no gradient; top-k selection and the
+    capacity rule are piecewise constant; the router logit is
+    l = r (xhat w_router) + b; the RMSNorm backward uses the saved r:
+    with xhat = x gamma and r = (mean x^2 + eps)^-1/2,
+    dx = dout + gamma dxhat - (r^3 / d) dr x  and  dgamma = sum_t dxhat x.
+    """
+    if p.get("router", "dense") != "dense":
+        raise NotImplementedError("the backward covers the dense router")
+    if p.get("quant"):
+        raise NotImplementedError("the backward covers unquantised experts")
+    x64 = as_f64(x)
+    G = as_f64(dout)
+    T, d = x64.shape
+    k = int(p["k"])
+    eps = float(p["eps"])
+    gamma = as_f64(p.get("gamma"))
+    r = rmsnorm_scale(x64, eps)
+    xh = _xhat(x64, p.get("gamma"))
+    wr = as_f64(p["w_router"])
+    bias = p.get("bias")
+    logits = router_logits(x64, p.get("gamma"), r, wr, bias)
+    E = logits.shape[1]
+    ids = select_topk(logits, k) if ids_override is None else np.asarray(ids_override)
+    renorm = int(p.get("renorm", 1))
+    g = gates(logits, ids, renorm)
+    cap = capacity(T, k, E, float(p.get("cf", 0.0)))
+    pos = dispatch(ids, E, cap, int(p.get("pad", 1)))["pos"]
+
+    act = p["act"]
+    w1, w2 = as_f64(p["w1"]), as_f64(p["w2"])
+    w3 = as_f64(p.get("w3"))
+    foff = np.asarray(p["f_offsets"], dtype=np.int64)
+    dxh = np.zeros((T, d))
+    dr = np.zeros(T)
+    dg = np.zeros((T, k))
+    res = dict(dw1=np.zeros_like(w1), dw2=np.zeros_like(w2),
+               dw3=None if w3 is None else np.zeros_like(w3))
+    tt, jj = np.nonzero(pos >= 0)
+    e_rows = np.asarray(ids)[tt, jj].astype(np.int64)
+    for e in np.unique(e_rows):
+        m = e_rows == e
+        ts, js = tt[m], jj[m]
+        lo, hi = int(foff[e]), int(foff[e + 1])
+        w1e, w2e = w1[:, lo:hi], w2[lo:hi, :]
+        w3e = None if w3 is None else w3[:, lo:hi]
+        y = ffn(xh[ts], r[ts], w1e, w2e, act, w3e)
+        dg[ts, js] = np.sum(G[ts] * y, axis=1)
+        b = ffn_backward(xh[ts], r[ts], w1e, w2e, act, g[ts, js][:, None] * G[ts], w3e)
+        np.add.at(dxh, ts, b["dxhat"])
+        np.add.at(dr, ts, b["dr"])
+        res["dw1"][:, lo:hi] += b["dw1"]
+        res["dw2"][lo:hi, :] += b["dw2"]
+        if w3 is not None:
+            res["dw3"][:, lo:hi] += b["dw3"]
+    if p.get("ws1") is not None:
+        sact = p.get("shared_act", "swiglu" if p.get("ws3") is not None else "gelu")
+        b = ffn_backward(xh, r, as_f64(p["ws1"]), as_f64(p["ws2"]), sact, G, as_f64(p.get("ws3")))
+        dxh += b["dxhat"]
+        dr += b["dr"]
+        res.update(dws1=b["dw1"], dws2=b["dw2"], dws3=b.get("dw3"))
+    dl = gates_backward(logits, ids, renorm, dg)
+    z = xh @ wr
+    res["dw_router"] = (r[:, None] * xh).T @ dl
+    res["dbias"] = dl.sum(axis=0)
+    dxh += r[:, None] * (dl @ wr.T)
+    dr += np.sum(z * dl, axis=1)
+    dx = G.copy() if p.get("residual", True) else np.zeros_like(G)
+    dx += (dxh * gamma if gamma is not None else dxh) - (r ** 3 / d)[:, None] * dr[:, None] * x64
+    res.update(dx=dx, dgamma=None if gamma is None else np.sum(dxh * x64, axis=0), dg=dg, dl=dl,
+               dxhat=dxh, dr=dr, ids=np.asarray(ids, dtype=np.int32), pos=pos)
     return res

@@ -596,3 +596,112 @@ def test_mx_ffn_reduces_to_dense_on_grid_values():
     # and MX quantisation error stays within the E4M3 bound relative to block max
     full = O.ffn(x, r, w1, w2, "gelu")
     assert np.max(np.abs(O.ffn_mxfp8(x, r, w1, w2, "gelu") - full)) < 0.1 * np.max(np.abs(full))
+
+
+# ---------------------------------------------------------------- backward pass
+
+def test_activation_derivatives_match_finite_differences():
+    z = np.linspace(-6.0, 6.0, 241)
+    h = 1e-5
+    for f, df in ((O.gelu, O.gelu_grad), (O.gelu_tanh, O.gelu_tanh_grad), (O.silu, O.silu_grad)):
+        fd = (f(z + h) - f(z - h)) / (2 * h)
+        assert np.max(np.abs(df(z) - fd)) < 1e-8
+    # textbook values: GELU'(0) = SiLU'(0) = 1/2, GELU'(z) = Phi(z) + z phi(z)
+    assert O.gelu_grad(0.0) == 0.5 and O.silu_grad(0.0) == 0.5 and O.gelu_tanh_grad(0.0) == 0.5
+    assert abs(O.gelu_grad(1.0) - (ndtr(1.0) + math.exp(-0.5) / math.sqrt(2 * math.pi))) < 1e-15
+
+
+def _bwd_case(act, renorm, gamma, bias, shared, cf, k, seed):
+    rng = _rng(seed)
+    T, d, E, f = 7, 8, 4, 16
+    p = dict(k=k, eps=1e-6, renorm=renorm, cf=cf, act=act, residual=True, pad=1,
+             gamma=(1.0 + 0.1 * rng.standard_normal(d)) if gamma else None,
+             router="dense", w_router=rng.standard_normal((d, E)),
+             bias=rng.standard_normal(E) if bias else None,
+             w1=0.5 * rng.standard_normal((d, E * f)), w2=0.5 * rng.standard_normal((E * f, d)),
+             w3=0.5 * rng.standard_normal((d, E * f)) if act == "swiglu" else None,
+             f_offsets=[i * f for i in range(E + 1)])
+    if shared:
+        p.update(ws1=0.5 * rng.standard_normal((d, 2 * f)), ws2=0.5 * rng.standard_normal((2 * f, d)),
+                 shared_act=act, ws3=0.5 * rng.standard_normal((d, 2 * f)) if act == "swiglu" else None)
+    x = rng.standard_normal((T, d))
+    G = rng.standard_normal((T, d))
+    return p, x, G
+
+
+@pytest.mark.parametrize("act,renorm,gamma,bias,shared,cf,k,seed", [
+    ("gelu", 1, True, True, False, 0.75, 2, 1),       # drops, gain, bias
+    ("swiglu", 0, False, False, True, 0.0, 2, 2),      # full-softmax gates, shared experts
+    ("gelu_tanh", 1, True, False, True, 0.0, 4, 3),    # k = E
+    ("swiglu", 1, True, True, False, 0.5, 1, 4),       # switch routing with drops
+])
+def test_layer_backward_matches_finite_differences(act, renorm, gamma, bias, shared, cf, k, seed):
+    """Every gradient of the oracle's backward against central differences
+    of the oracle's forward (the routing frozen at the forward's own ids; the
+    selection and the capacity rule are piecewise constant)."""
+    p, x, G = _bwd_case(act, renorm, gamma, bias, shared, cf, k, seed)
+    base = O.layer_forward(p, x)
+    ids = base["ids"]
+    grads = O.layer_backward(p, x, G, ids_override=ids)
+    assert np.array_equal(grads["ids"], ids)
+    if cf > 0:
+        assert np.any(grads["pos"] < 0)               # the case really drops slots
+    h = 1e-6
+
+    def loss(pp, xx):
+        return float(np.sum(O.layer_forward(pp, xx, ids_override=ids)["out"] * G))
+
+    def fd(name):
+        if name == "x":
+            v = x
+        else:
+            v = p[name]
+        g = np.zeros_like(v)
+        for idx in np.ndindex(v.shape):
+            vp, vm = v.copy(), v.copy()
+            vp[idx] += h
+            vm[idx] -= h
+            if name == "x":
+                g[idx] = (loss(p, vp) - loss(p, vm)) / (2 * h)
+            else:
+                g[idx] = (loss(dict(p, **{name: vp}), x) - loss(dict(p, **{name: vm}), x)) / (2 * h)
+        return g
+
+    pairs = [("x", "dx"), ("w_router", "dw_router"), ("w1", "dw1"), ("w2", "dw2")]
+    if gamma:
+        pairs.append(("gamma", "dgamma"))
+    if bias:
+        pairs.append(("bias", "dbias"))
+    if act == "swiglu":
+        pairs.append(("w3", "dw3"))
+    if shared:
+        pairs += [("ws1", "dws1"), ("ws2", "dws2")] + ([("ws3", "dws3")] if act == "swiglu" else [])
+    for name, gname in pairs:
+        num = fd(name)
+        ana = grads[gname]
+        scale = max(np.max(np.abs(num)), 1e-3)
+        assert np.max(np.abs(ana - num)) < 1e-6 * scale, (name, np.max(np.abs(ana - num)), scale)
+
+
+def test_gates_backward_special_cases():
+    rng = _rng(9)
+    l = rng.standard_normal((5, 6))
+    # k = E with renorm: the gates are the full softmax in selection order, so
+    # both readings give the same logit gradient (the softmax Jacobian)
+    ids = O.select_topk(l, 6)
+    dg = rng.standard_normal((5, 6))
+    a = O.gates_backward(l, ids, 1, dg)
+    b = O.gates_backward(l, ids, 0, dg)
+    assert np.allclose(a, b, atol=1e-14)
+    P = sp_softmax(l, axis=1)
+    dP = np.zeros_like(l)
+    np.put_along_axis(dP, ids.astype(np.int64), dg, axis=1)
+    J = np.einsum("te,ef->tef", P, np.eye(6)) - np.einsum("te,tf->tef", P, P)
+    assert np.allclose(a, np.einsum("tef,te->tf", J, dP), atol=1e-14)
+    # switch routing (k = 1, renorm): the gate is identically 1, so no gradient
+    ids1 = O.select_topk(l, 1)
+    assert np.all(O.gates_backward(l, ids1, 1, rng.standard_normal((5, 1))) == 0)
+    # the logit gradient of renormalised gates sums to zero per token (shift invariance)
+    ids2 = O.select_topk(l, 3)
+    assert np.allclose(O.gates_backward(l, ids2, 1, rng.standard_normal((5, 3))).sum(axis=1), 0,
+                       atol=1e-14)
