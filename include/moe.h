@@ -147,6 +147,12 @@ typedef struct moe_experts_desc {
   int quant;
   const uint8_t* w13_scale;
   const uint8_t* w2_scale;
+  /* Needed by moe_layer_backward only (GROUPED / BCSR, bf16): the second
+   * linear as the pages store it, w2 [F, d] (= w2_t transposed), and the
+   * packed first linear transposed, w13_dk [d, P] (moe_pack_transpose of
+   * w13_t viewed as [P, d]).  Ignored by the forward calls. */
+  const void* w2_fk;
+  const void* w13_dk;
 } moe_experts_desc;
 
 /* Results of moe_dispatch, consumed by moe_expert_gemm and moe_combine. */
@@ -224,7 +230,32 @@ typedef struct moe_layer_desc {
   moe_timer* timer;                /* NULL, or per-stage event timing          */
   const moe_router_extras* router_extras;  /* [host] NULL, or noise / statistics
                                                of the dense router            */
+  int save_for_backward;           /* 1: moe_layer_forward also keeps in its
+                                      workspace what moe_layer_backward needs
+                                      (pre-activations, router logits); bf16,
+                                      dense router, unquantised grouped or
+                                      BCSR experts only                       */
 } moe_layer_desc;
+
+/* Gradients written by moe_layer_backward (device pointers; fp32 unless
+ * noted).  Weight gradients are in the layouts the forward reads (packed
+ * rows are features, K = d contiguous), so that an optimizer updates the
+ * packed weights in place:
+ *   dw13  [P, d]  gradient of w13_t (P = F, or 2F for SwiGLU)
+ *   dw2   [F, d]  gradient of the pages' w2 (the transpose of w2_t)
+ *   dw_router [E, d]  gradient of wr_t
+ * Every pointer that applies is required: dbias with a router bias, dgamma
+ * with a gain, dws13 / dws2 with shared experts. */
+typedef struct moe_layer_grads {
+  void* dx;          /* [T, d] dtype                                          */
+  float* dgamma;     /* [d]                                                   */
+  float* dw_router;  /* [E, d]                                                */
+  float* dbias;      /* [E]                                                   */
+  float* dw13;       /* [P, d]                                                */
+  float* dw2;        /* [F, d]                                                */
+  float* dws13;      /* [P_s, d]                                              */
+  float* dws2;       /* [F_s, d]                                              */
+} moe_layer_grads;
 
 /* Last error message of the calling thread ("" after success). */
 const char* moe_last_error(void);
@@ -370,6 +401,32 @@ int moe_layer_forward(const moe_layer_desc* L, const void* x, int64_t T, void* o
  * fills *rt with pointers into ws (valid until the workspace is reused). */
 int moe_layer_routing(const moe_layer_desc* L, int64_t T, void* ws, size_t ws_bytes,
                       moe_routing* rt);
+
+/* ---- backward pass ----
+ * CODA thread, the paragraph on the backward: the RMSNorm backward is fused
+ * into the backward of the linear that consumed the normed input, using the
+ * saved r.  For an upstream gradient dout [T, d] of the layer output, after
+ * moe_layer_forward(L with save_for_backward = 1, x, T, ...) on the same
+ * fwd_ws (untouched since), writes the gradients of moe_layer_grads:
+ *   expert rows:  dy = g dout,  dg = dout . y,  dh = dy w2^T,
+ *                 da = dh act'(a)  (SwiGLU: da = dh u silu'(a), du = dh silu(a)),
+ *                 dw2 += h^T dy,  dw13 += [da | du]^T (r xhat),
+ *                 dxhat += r [da | du] w13,  dr += (xhat w13) . [da | du]
+ *   shared experts: the same with gate 1 over all tokens
+ *   router:       top-k selection and the capacity rule are piecewise
+ *                 constant; dl from dg through the gate softmax (renorm 1:
+ *                 over the k selected; renorm 0: over all E);
+ *                 dw_router = dl^T (r xhat), dbias = sum_t dl,
+ *                 dxhat += r dl wr, dr += (xhat wr) . dl
+ *   RMSNorm:      dx = dout (residual) + gamma dxhat - (r^3 / d) dr x,
+ *                 dgamma = sum_t dxhat x
+ * Dropped slots get no gradient.  Needs w2_fk and w13_dk in the expert
+ * descriptors; router extras with noise are not supported.  Every sum is in
+ * a fixed order (deterministic).  ws: moe_layer_backward_workspace_size bytes. */
+size_t moe_layer_backward_workspace_size(const moe_layer_desc* L, int64_t T);
+int moe_layer_backward(const moe_layer_desc* L, const void* x, int64_t T, const void* dout,
+                       const void* fwd_ws, size_t fwd_ws_bytes, const moe_layer_grads* grads,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---- per-stage timing (hipEvents; the only calls here that synchronise) ---- */
 int moe_timer_create(moe_timer** out, int max_calls);

@@ -28,6 +28,7 @@ EXPORTED = [
     "moe_expert_workspace_size", "moe_expert_gemm", "moe_shared_workspace_size", "moe_shared_ffn",
     "moe_combine", "moe_layer_workspace_size", "moe_layer_forward", "moe_layer_routing",
     "moe_timer_create", "moe_timer_destroy", "moe_timer_reset", "moe_timer_stage_ms",
+    "moe_layer_backward_workspace_size", "moe_layer_backward",
 ]
 
 
@@ -42,7 +43,8 @@ class ExpertsDesc(C.Structure):
                 ("w13_t", C.c_void_p), ("w2_t", C.c_void_p), ("W", C.c_void_p), ("V", C.c_void_p),
                 ("block", C.c_int), ("size_blocks", C.c_void_p), ("block_offsets", C.c_void_p),
                 ("row_offsets", C.c_void_p), ("column_indices", C.c_void_p),
-                ("quant", C.c_int), ("w13_scale", C.c_void_p), ("w2_scale", C.c_void_p)]
+                ("quant", C.c_int), ("w13_scale", C.c_void_p), ("w2_scale", C.c_void_p),
+                ("w2_fk", C.c_void_p), ("w13_dk", C.c_void_p)]
 
 
 class Routing(C.Structure):
@@ -63,7 +65,13 @@ class LayerDesc(C.Structure):
                 ("router", RouterDesc), ("k", C.c_int), ("renorm", C.c_int),
                 ("capacity_factor", C.c_double), ("experts", ExpertsDesc),
                 ("shared", C.POINTER(ExpertsDesc)), ("residual", C.c_int), ("timer", C.c_void_p),
-                ("router_extras", C.POINTER(RouterExtras))]
+                ("router_extras", C.POINTER(RouterExtras)), ("save_for_backward", C.c_int)]
+
+
+class LayerGrads(C.Structure):
+    _fields_ = [("dx", C.c_void_p), ("dgamma", C.c_void_p), ("dw_router", C.c_void_p),
+                ("dbias", C.c_void_p), ("dw13", C.c_void_p), ("dw2", C.c_void_p),
+                ("dws13", C.c_void_p), ("dws2", C.c_void_p)]
 
 
 class Stats(C.Structure):
@@ -111,6 +119,9 @@ def lib() -> C.CDLL:
             "moe_layer_workspace_size": (SZ, [C.POINTER(LayerDesc), I64]),
             "moe_layer_forward": (I, [C.POINTER(LayerDesc), P, I64, P, P, P, SZ, P]),
             "moe_layer_routing": (I, [C.POINTER(LayerDesc), I64, P, SZ, C.POINTER(Routing)]),
+            "moe_layer_backward_workspace_size": (SZ, [C.POINTER(LayerDesc), I64]),
+            "moe_layer_backward": (I, [C.POINTER(LayerDesc), P, I64, P, P, SZ,
+                                       C.POINTER(LayerGrads), P, SZ, P]),
             "moe_timer_create": (I, [C.POINTER(P), I]),
             "moe_timer_destroy": (I, [P]),
             "moe_timer_reset": (I, [P]),

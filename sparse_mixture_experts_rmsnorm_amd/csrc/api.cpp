@@ -199,6 +199,9 @@ struct ExpertWs {
   uint8_t* hqs = nullptr;  // [rows_max, Fmax / 32]
   bool xq_ready = false;   // the caller already quantised the rows into xq (the layer
                            // does it as its dispatch gather)
+  // saved for the backward pass: pre-activations [rows_max, pf * Fmax] (bf16)
+  void* pre = nullptr;
+  int64_t ldpre = 0;
 };
 
 // Compute units of the current device (cached; a host query, no sync).
@@ -236,7 +239,7 @@ int choose_ksplit(const ExpertGeo& g, int dtype, int64_t d, int64_t rows_used_es
 }
 
 void carve_expert_ws(Carve& c, const ExpertGeo& g, int dtype, int64_t d, int64_t rows_max,
-                     int64_t nnz_max, ExpertWs* w, int ksplit = 1) {
+                     int64_t nnz_max, ExpertWs* w, int ksplit = 1, bool save = false) {
   if (g.atomic) {
     w->a_rows = c.take_n<float>(rows_max);
     return;
@@ -259,6 +262,10 @@ void carve_expert_ws(Carve& c, const ExpertGeo& g, int dtype, int64_t d, int64_t
     w->hqs = c.take_n<uint8_t>(rp * (g.Fmax / 32));
   } else {
     w->h = c.take(size_t(rows_max) * g.Fmax * esize(dtype));
+  }
+  if (save) {
+    w->ldpre = g.pf * g.Fmax;
+    w->pre = c.take(size_t(rows_max) * w->ldpre * esize(dtype));
   }
   w->tiles1 = c.take_n<Tile>(w->mt1);
   w->tiles2 = c.take_n<Tile>(w->mt2);
@@ -414,6 +421,8 @@ int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, i
   a.xrow = xrow;
   a.epi = X->act == MOE_ACT_SWIGLU ? EPI_SWIGLU : EPI_ACT;
   a.act = X->act == MOE_ACT_GELU_TANH ? 1 : 0;
+  a.pre = w.pre;
+  a.ldpre = w.ldpre;
   MOE_HIP(launch_gemm(dtype, a, g.bf1, g.bt, int(w.mt1), s));
   timer_mark(timer, call, MOE_STAGE_GEMM1 + 1, s);
 
@@ -919,6 +928,8 @@ struct LayerWs {
   int64_t rows_max, cap;
 };
 
+bool d_ok_for_backward(int64_t d) { return d > 0 && d % 256 == 0; }
+
 int check_layer(const moe_layer_desc* L, int64_t T, ExpertGeo* g, ExpertGeo* gs) {
   REQUIRE(L, MOE_EINVAL, "layer descriptor is NULL");
   REQUIRE(T >= 0 && T < (int64_t(1) << 30), MOE_ESHAPE, "bad T");
@@ -948,6 +959,16 @@ int check_layer(const moe_layer_desc* L, int64_t T, ExpertGeo* g, ExpertGeo* gs)
   if (g->atomic)
     REQUIRE(!(L->capacity_factor > 0) || moe_capacity(T, L->k, L->experts.E, L->capacity_factor) >= T,
             MOE_EUNSUPPORTED, "atomic experts run without a capacity limit");
+  REQUIRE(L->save_for_backward == 0 || L->save_for_backward == 1, MOE_EINVAL,
+          "save_for_backward must be 0 or 1");
+  if (L->save_for_backward) {
+    REQUIRE(L->dtype == MOE_BF16 && L->router.kind == MOE_ROUTER_DENSE && !g->atomic && !g->mx &&
+                !(L->shared && gs->mx),
+            MOE_EUNSUPPORTED,
+            "the backward pass covers bf16 layers with a dense router and unquantised grouped "
+            "or BCSR experts");
+    REQUIRE(d_ok_for_backward(L->d), MOE_ESHAPE, "bad d");
+  }
   return MOE_OK;
 }
 
@@ -964,8 +985,9 @@ void carve_layer(Carve& c, const moe_layer_desc* L, int64_t T, const ExpertGeo& 
   w->xg = L->gamma ? c.take(size_t(T) * d * es) : nullptr;
   w->ids = c.take_n<int32_t>(T * k);
   w->w = c.take_n<float>(T * k);
-  w->logits = (L->router.kind == MOE_ROUTER_DENSE && L->dtype == MOE_F32) ? c.take_n<float>(T * E)
-                                                                          : nullptr;
+  w->logits = (L->router.kind == MOE_ROUTER_DENSE && (L->dtype == MOE_F32 || L->save_for_backward))
+                  ? c.take_n<float>(T * E)
+                  : nullptr;
   const size_t rws = moe_router_workspace_size(&L->router, T);
   w->router_ws = rws ? c.take(rws) : nullptr;
   w->counts = c.take_n<int32_t>(E);
@@ -992,10 +1014,10 @@ void carve_layer(Carve& c, const moe_layer_desc* L, int64_t T, const ExpertGeo& 
   }
   const int64_t rows_est = std::min(T * k, E * std::min(w->cap, T));
   const int ks = choose_ksplit(g, L->dtype, d, rows_est);
-  carve_expert_ws(c, g, L->dtype, d, w->rows_max, nnz_max, &w->ex, ks);
+  carve_expert_ws(c, g, L->dtype, d, w->rows_max, nnz_max, &w->ex, ks, L->save_for_backward != 0);
   w->y = ks > 1 ? nullptr : c.take(size_t(g.atomic ? T : w->rows_max) * d * es);
   if (L->shared) {
-    carve_expert_ws(c, gs, L->dtype, d, T, 0, &w->sh);
+    carve_expert_ws(c, gs, L->dtype, d, T, 0, &w->sh, 1, L->save_for_backward != 0);
     w->s = c.take(size_t(T) * d * es);
   } else {
     w->s = nullptr;
@@ -1165,6 +1187,484 @@ int moe_layer_forward(const moe_layer_desc* L, const void* x, int64_t T, void* o
   timer_mark(tm, call, MOE_STAGE_COMBINE + 1, stream);
   return ok();
 }
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- backward pass
+
+namespace {
+
+int64_t pad64(int64_t n) { return (n + 63) / 64 * 64; }
+
+// Pointers into the backward workspace.
+struct BwdWs {
+  int64_t L = 0, Tpad = 0;     // K extents of the routed / token-wide weight-gradient GEMMs
+  int nft = 0;                 // routed feature tiles per row (ceil(Fmax / 256))
+  void* dpre = nullptr;        // [rows_max, pf Fmax] bf16
+  float* part = nullptr;       // [rows_max, 2 nft]
+  float* dg_row = nullptr;     // [rows_max]
+  float* dr_row = nullptr;
+  float* dxperm = nullptr;     // [rows_max, d]
+  uint16_t* hT = nullptr;      // [F, L]
+  uint16_t* dpreT = nullptr;   // [P, L]
+  uint16_t* dyT = nullptr;     // [E d, L]
+  uint16_t* rxT = nullptr;     // [E d, L]
+  float* dl = nullptr;         // [T, E]
+  uint16_t* dlT = nullptr;     // [E, Tpad]
+  float* drr = nullptr;        // [T]
+  uint16_t* rxT_all = nullptr; // [d, Tpad]
+  float* dgamma_part = nullptr;
+  // shared experts
+  int nft_s = 0;
+  void* dpre_s = nullptr;      // [T, P_s]
+  float* part_s = nullptr;     // [T, 2 nft_s]
+  float* dr_s = nullptr;       // [T]
+  float* dxs = nullptr;        // [T, d]
+  uint16_t* hT_s = nullptr;    // [F_s, Tpad]
+  uint16_t* dpreT_s = nullptr; // [P_s, Tpad]
+  uint16_t* GT = nullptr;      // [d, Tpad]
+  // tile lists: B1, B2, dW13, dW2 (routed), router, B1s, B2s, dW13s, dW2s
+  Tile* tiles[9] = {};
+  int64_t mt[9] = {};
+  int* nt = nullptr;           // [9]
+};
+
+void carve_backward(Carve& c, const moe_layer_desc* L, int64_t T, const ExpertGeo& g,
+                    const ExpertGeo& gs, const LayerWs& fw, BwdWs* b) {
+  const int64_t d = L->d, E = L->experts.E;
+  const int pad = g.bcsr ? 128 : 1;
+  const int64_t rm = fw.rows_max;
+  const int64_t P = g.F * g.pf, Pmax = g.Fmax * g.pf;
+  b->L = pad64((std::min(fw.cap, T) + pad - 1) / pad * pad);
+  b->Tpad = pad64(T);
+  b->nft = int((g.Fmax + 255) / 256);
+  b->dpre = c.take(size_t(rm) * Pmax * 2);
+  b->part = c.take_n<float>(rm * 2 * b->nft);
+  b->dg_row = c.take_n<float>(rm);
+  b->dr_row = c.take_n<float>(rm);
+  b->dxperm = c.take_n<float>(rm * d);
+  b->hT = c.take_n<uint16_t>(g.F * b->L);
+  b->dpreT = c.take_n<uint16_t>(P * b->L);
+  b->dyT = c.take_n<uint16_t>(E * d * b->L);
+  b->rxT = c.take_n<uint16_t>(E * d * b->L);
+  b->dl = c.take_n<float>(T * E);
+  b->dlT = c.take_n<uint16_t>(E * b->Tpad);
+  b->drr = c.take_n<float>(T);
+  b->rxT_all = c.take_n<uint16_t>(d * b->Tpad);
+  b->dgamma_part = L->gamma ? c.take_n<float>(int64_t(token_bwd_blocks(T)) * d) : nullptr;
+  const int64_t nd = d / 256;
+  b->mt[0] = (rm / 256 + E) * b->nft;
+  b->mt[1] = (rm / 256 + E) * nd;
+  b->mt[2] = (P / 256 + E) * nd;
+  b->mt[3] = (g.F / 256 + E) * nd;
+  b->mt[4] = ((E + 255) / 256) * nd;
+  if (L->shared) {
+    const int64_t Ps = gs.F * gs.pf;
+    b->nft_s = int((gs.F + 255) / 256);
+    b->dpre_s = c.take(size_t(T) * Ps * 2);
+    b->part_s = c.take_n<float>(T * 2 * b->nft_s);
+    b->dr_s = c.take_n<float>(T);
+    b->dxs = c.take_n<float>(T * d);
+    b->hT_s = c.take_n<uint16_t>(gs.F * b->Tpad);
+    b->dpreT_s = c.take_n<uint16_t>(Ps * b->Tpad);
+    b->GT = c.take_n<uint16_t>(d * b->Tpad);
+    const int64_t mtT = (T + 255) / 256;
+    b->mt[5] = mtT * b->nft_s;
+    b->mt[6] = mtT * nd;
+    b->mt[7] = ((Ps + 255) / 256) * nd;
+    b->mt[8] = ((gs.F + 255) / 256) * nd;
+  }
+  for (int i = 0; i < 9; ++i) {
+    b->mt[i] = std::max<int64_t>(1, b->mt[i]);
+    b->tiles[i] = c.take_n<Tile>(b->mt[i]);
+  }
+  b->nt = c.take_n<int>(9);
+}
+
+int check_backward(const moe_layer_desc* L, int64_t T, ExpertGeo* g, ExpertGeo* gs) {
+  int rc = check_layer(L, T, g, gs);
+  if (rc) return rc;
+  REQUIRE(L->save_for_backward == 1, MOE_EINVAL,
+          "the backward needs a layer descriptor with save_for_backward = 1");
+  REQUIRE(L->experts.w2_fk && L->experts.w13_dk, MOE_EINVAL,
+          "the backward needs w2_fk and w13_dk in the expert descriptor");
+  REQUIRE(!L->shared || (L->shared->w2_fk && L->shared->w13_dk), MOE_EINVAL,
+          "the backward needs w2_fk and w13_dk in the shared-expert descriptor");
+  REQUIRE(!L->router_extras || !L->router_extras->noise, MOE_EUNSUPPORTED,
+          "the backward does not take noise top-k");
+  REQUIRE(L->experts.E <= 4096, MOE_EUNSUPPORTED, "the backward supports E <= 4096");
+  REQUIRE(L->d % 256 == 0, MOE_ESHAPE, "the backward needs d %% 256 == 0");
+  return MOE_OK;
+}
+
+// The two GEMMs of one expert set's backward on the rows of its segments
+// (routed: the dispatch's offsets; shared: one dense group of T rows).
+struct ExpertBwdIo {
+  const moe_experts_desc* X;
+  const ExpertGeo* g;
+  const int32_t* offsets;      // NULL: dense group of T rows
+  int64_t rows;                // rows_max, or T
+  const int32_t* xrow;         // row -> token (routed) or NULL
+  const float* row_w;          // gate per row, NULL = 1
+  const float* row_r;          // r per row
+  const int32_t* row_expert;   // routed rows' expert (for the partial reduction)
+  const void* h;               // saved h [rows, Fmax]
+  const void* pre;             // saved pre-activations [rows, pf Fmax]
+  void* dpre; float* part; int nft; float* dg_row; float* dr_row; float* dx_rows;
+  Tile* t_b1; int64_t mt_b1; int* nt_b1;
+  Tile* t_b2; int64_t mt_b2; int* nt_b2;
+};
+
+int run_expert_bwd(const ExpertBwdIo& io, int64_t d, int64_t T, const void* dout, hipStream_t s) {
+  const ExpertGeo& g = *io.g;
+  const int64_t Pmax = g.pf * g.Fmax;
+  PlanArgs p{};
+  p.offsets = io.offsets;
+  p.dense_rows = int(T);
+  p.dense_n = int(g.Fmax);
+  p.foff = io.X->ffn_offsets;
+  p.E = int(io.X->E);
+  p.swiglu = 0;
+  p.d = int(d);
+  p.bt = 256;
+  p.bf = 256;
+  p.fold = 1;
+  p.ksplit = 1;
+  p.block = 128;
+  p.gemm = 1;
+  p.ragged = 1;
+  p.tiles = io.t_b1;
+  p.ntiles = io.nt_b1;
+  p.max_tiles = int(io.mt_b1);
+  MOE_HIP(launch_plan(p, s));
+  p.gemm = 2;
+  p.ragged = 0;
+  p.kmul = g.pf;
+  p.dense_n = int(d);
+  p.tiles = io.t_b2;
+  p.ntiles = io.nt_b2;
+  p.max_tiles = int(io.mt_b2);
+  MOE_HIP(launch_plan(p, s));
+
+  GemmArgs a{};
+  a.X = dout;
+  a.ldx = d;
+  a.xrow = io.xrow;
+  a.W = io.X->w2_fk;
+  a.ldw = d;
+  a.tiles = io.t_b1;
+  a.ntiles = io.nt_b1;
+  a.Y = io.dpre;
+  a.ldy = Pmax;
+  a.row_w = io.row_w;
+  a.row_r = io.row_r;
+  a.epi = io.X->act == MOE_ACT_SWIGLU ? EPI_BWD_SWIGLU : EPI_BWD_ACT;
+  a.act = io.X->act == MOE_ACT_GELU_TANH ? 1 : 0;
+  a.pre = const_cast<void*>(io.pre);
+  a.ldpre = Pmax;
+  a.hsav = io.h;
+  a.ldh = g.Fmax;
+  a.part = io.part;
+  a.ldpart = 2 * io.nft;
+  MOE_HIP(launch_gemm(MOE_BF16, a, 256, 256, int(io.mt_b1), s));
+  MOE_HIP(launch_reduce_part(io.part, 2 * io.nft, io.rows, io.row_expert, io.X->ffn_offsets,
+                             io.nft, io.dg_row, io.dr_row, s));
+  GemmArgs b{};
+  b.X = io.dpre;
+  b.ldx = Pmax;
+  b.W = io.X->w13_dk;
+  b.ldw = g.F * g.pf;
+  b.tiles = io.t_b2;
+  b.ntiles = io.nt_b2;
+  b.Y = io.dx_rows;
+  b.ldy = d;
+  b.row_r = io.row_r;
+  b.epi = EPI_SCALE_F32;
+  MOE_HIP(launch_gemm(MOE_BF16, b, 256, 256, int(io.mt_b2), s));
+  return MOE_OK;
+}
+
+// Y [xrows, d] = sum over each segment's rows of X^T W (fp32, plain).
+int run_wgrad(const WgradPlanArgs& wp, const uint16_t* X, int64_t ldx, const uint16_t* W,
+              int64_t ldw, float* Y, int64_t ldy, hipStream_t s) {
+  MOE_HIP(launch_plan_wgrad(wp, s));
+  GemmArgs a{};
+  a.X = X;
+  a.ldx = ldx;
+  a.W = W;
+  a.ldw = ldw;
+  a.tiles = wp.tiles;
+  a.ntiles = wp.ntiles;
+  a.Y = Y;
+  a.ldy = ldy;
+  a.epi = EPI_SCALE_F32;
+  MOE_HIP(launch_gemm(MOE_BF16, a, 256, 256, wp.max_tiles, s));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_layer_backward_workspace_size(const moe_layer_desc* L, int64_t T) {
+  ExpertGeo g, gs;
+  if (check_backward(L, T, &g, &gs)) return 0;
+  Carve c0(nullptr);
+  LayerWs fw;
+  carve_layer(c0, L, T, g, gs, &fw);
+  Carve c(nullptr);
+  BwdWs b;
+  carve_backward(c, L, T, g, gs, fw, &b);
+  return c.used;
+}
+
+int moe_layer_backward(const moe_layer_desc* L, const void* x, int64_t T, const void* dout,
+                       const void* fwd_ws, size_t fwd_ws_bytes, const moe_layer_grads* grads,
+                       void* ws, size_t ws_bytes, hipStream_t stream) {
+  ExpertGeo g, gs;
+  int rc = check_backward(L, T, &g, &gs);
+  if (rc) return rc;
+  REQUIRE(grads, MOE_EINVAL, "grads is NULL");
+  REQUIRE(T == 0 || (x && dout && grads->dx && grads->dw_router && grads->dw13 && grads->dw2),
+          MOE_EINVAL, "x, dout, dx, dw_router, dw13 and dw2 are required");
+  REQUIRE(!L->router.bias || grads->dbias, MOE_EINVAL, "a router bias needs dbias");
+  REQUIRE(!L->gamma || grads->dgamma, MOE_EINVAL, "a gain needs dgamma");
+  REQUIRE(!L->shared || (grads->dws13 && grads->dws2), MOE_EINVAL,
+          "shared experts need dws13 and dws2");
+  Carve c0(const_cast<void*>(fwd_ws));
+  LayerWs fw;
+  carve_layer(c0, L, T, g, gs, &fw);
+  REQUIRE(fwd_ws && fwd_ws_bytes >= c0.used, MOE_EWORKSPACE,
+          "the forward workspace needs %zu bytes (got %zu)", c0.used, fwd_ws_bytes);
+  Carve c(ws);
+  BwdWs b;
+  carve_backward(c, L, T, g, gs, fw, &b);
+  REQUIRE(ws && ws_bytes >= c.used, MOE_EWORKSPACE, "backward workspace needs %zu bytes (got %zu)",
+          c.used, ws_bytes);
+  if (T == 0) return ok();
+  const int64_t d = L->d, E = L->experts.E;
+  const int k = L->k;
+  const void* xhat = L->gamma ? fw.xg : x;
+  const uint16_t* dout16 = static_cast<const uint16_t*>(dout);
+  const uint16_t* xhat16 = static_cast<const uint16_t*>(xhat);
+
+  // 1. routed experts: dh / da (and the gate's and r's per-row sums), dxhat rows
+  ExpertBwdIo io{};
+  io.X = &L->experts;
+  io.g = &g;
+  io.offsets = fw.offsets;
+  io.rows = fw.rows_max;
+  io.xrow = fw.row_token;
+  io.row_w = fw.row_w;
+  io.row_r = fw.row_r;
+  io.row_expert = fw.row_expert;
+  io.h = fw.ex.h;
+  io.pre = fw.ex.pre;
+  io.dpre = b.dpre;
+  io.part = b.part;
+  io.nft = b.nft;
+  io.dg_row = b.dg_row;
+  io.dr_row = b.dr_row;
+  io.dx_rows = b.dxperm;
+  io.t_b1 = b.tiles[0];
+  io.mt_b1 = b.mt[0];
+  io.nt_b1 = b.nt;
+  io.t_b2 = b.tiles[1];
+  io.mt_b2 = b.mt[1];
+  io.nt_b2 = b.nt + 1;
+  rc = run_expert_bwd(io, d, T, dout, stream);
+  if (rc) return rc;
+
+  // 2. routed weight gradients over each expert's rows
+  {
+    GatherTArgs t{};
+    t.offsets = fw.offsets;
+    t.E = int(E);
+    t.foff = L->experts.ffn_offsets;
+    t.ldo = b.L;
+    t.src = static_cast<const uint16_t*>(fw.ex.h);
+    t.lds = g.Fmax;
+    t.wmul = 1;
+    t.out = b.hT;
+    MOE_HIP(launch_gather_t(t, int(g.Fmax), int(b.L), int(E), stream));
+    t.src = static_cast<const uint16_t*>(b.dpre);
+    t.lds = g.Fmax * g.pf;
+    t.wmul = g.pf;
+    t.out = b.dpreT;
+    MOE_HIP(launch_gather_t(t, int(g.Fmax * g.pf), int(b.L), int(E), stream));
+    t.wfix = int(d);
+    t.rowmap = fw.row_token;
+    t.src = dout16;
+    t.lds = d;
+    t.rscale = fw.row_w;
+    t.out = b.dyT;
+    MOE_HIP(launch_gather_t(t, int(d), int(b.L), int(E), stream));
+    t.src = xhat16;
+    t.rscale = fw.row_r;
+    t.out = b.rxT;
+    MOE_HIP(launch_gather_t(t, int(d), int(b.L), int(E), stream));
+    WgradPlanArgs wp{};
+    wp.offsets = fw.offsets;
+    wp.E = int(E);
+    wp.foff = L->experts.ffn_offsets;
+    wp.xmul = g.pf;
+    wp.wstride = int(d);
+    wp.d = int(d);
+    wp.tiles = b.tiles[2];
+    wp.ntiles = b.nt + 2;
+    wp.max_tiles = int(b.mt[2]);
+    rc = run_wgrad(wp, b.dpreT, b.L, b.rxT, b.L, grads->dw13, d, stream);
+    if (rc) return rc;
+    wp.xmul = 1;
+    wp.tiles = b.tiles[3];
+    wp.ntiles = b.nt + 3;
+    wp.max_tiles = int(b.mt[3]);
+    rc = run_wgrad(wp, b.hT, b.L, b.dyT, b.L, grads->dw2, d, stream);
+    if (rc) return rc;
+  }
+
+  // 3. token-wide operands: r xhat transposed (router and shared experts)
+  {
+    GatherTArgs t{};
+    t.dense_rows = int(T);
+    t.E = 1;
+    t.wfix = int(d);
+    t.src = xhat16;
+    t.lds = d;
+    t.rscale = fw.r;
+    t.out = b.rxT_all;
+    t.ldo = b.Tpad;
+    MOE_HIP(launch_gather_t(t, int(d), int(b.Tpad), 1, stream));
+  }
+
+  // 4. shared experts (gate 1, every token)
+  if (L->shared) {
+    const int64_t Ps = gs.F * gs.pf;
+    ExpertBwdIo si{};
+    si.X = L->shared;
+    si.g = &gs;
+    si.offsets = nullptr;
+    si.rows = T;
+    si.row_r = fw.r;
+    si.h = fw.sh.h;
+    si.pre = fw.sh.pre;
+    si.dpre = b.dpre_s;
+    si.part = b.part_s;
+    si.nft = b.nft_s;
+    si.dr_row = b.dr_s;
+    si.dx_rows = b.dxs;
+    si.t_b1 = b.tiles[5];
+    si.mt_b1 = b.mt[5];
+    si.nt_b1 = b.nt + 5;
+    si.t_b2 = b.tiles[6];
+    si.mt_b2 = b.mt[6];
+    si.nt_b2 = b.nt + 6;
+    rc = run_expert_bwd(si, d, T, dout, stream);
+    if (rc) return rc;
+    GatherTArgs t{};
+    t.dense_rows = int(T);
+    t.E = 1;
+    t.ldo = b.Tpad;
+    t.src = static_cast<const uint16_t*>(fw.sh.h);
+    t.lds = gs.F;
+    t.wfix = int(gs.F);
+    t.out = b.hT_s;
+    MOE_HIP(launch_gather_t(t, int(gs.F), int(b.Tpad), 1, stream));
+    t.src = static_cast<const uint16_t*>(b.dpre_s);
+    t.lds = Ps;
+    t.wfix = int(Ps);
+    t.out = b.dpreT_s;
+    MOE_HIP(launch_gather_t(t, int(Ps), int(b.Tpad), 1, stream));
+    t.src = dout16;
+    t.lds = d;
+    t.wfix = int(d);
+    t.out = b.GT;
+    MOE_HIP(launch_gather_t(t, int(d), int(b.Tpad), 1, stream));
+    WgradPlanArgs wp{};
+    wp.dense_rows = int(T);
+    wp.E = 1;
+    wp.wstride = 0;
+    wp.d = int(d);
+    wp.xfix = int(Ps);
+    wp.tiles = b.tiles[7];
+    wp.ntiles = b.nt + 7;
+    wp.max_tiles = int(b.mt[7]);
+    rc = run_wgrad(wp, b.dpreT_s, b.Tpad, b.rxT_all, b.Tpad, grads->dws13, d, stream);
+    if (rc) return rc;
+    wp.xfix = int(gs.F);
+    wp.tiles = b.tiles[8];
+    wp.ntiles = b.nt + 8;
+    wp.max_tiles = int(b.mt[8]);
+    rc = run_wgrad(wp, b.hT_s, b.Tpad, b.GT, b.Tpad, grads->dws2, d, stream);
+    if (rc) return rc;
+  }
+
+  // 5. router: gate -> logit gradients, its weight / bias gradients
+  {
+    RouterBwdArgs r{};
+    r.T = T;
+    r.Tpad = b.Tpad;
+    r.E = int(E);
+    r.k = k;
+    r.renorm = L->renorm;
+    r.logits = fw.logits;
+    r.ids = fw.ids;
+    r.w = fw.w;
+    r.pos = fw.pos;
+    r.dg_row = b.dg_row;
+    r.bias = L->router.bias;
+    r.r = fw.r;
+    r.dl = b.dl;
+    r.dlT = b.dlT;
+    r.ldt = b.Tpad;
+    r.dr = b.drr;
+    MOE_HIP(launch_router_bwd(r, stream));
+    WgradPlanArgs wp{};
+    wp.dense_rows = int(T);
+    wp.E = 1;
+    wp.xfix = int(E);
+    wp.wstride = 0;
+    wp.d = int(d);
+    wp.tiles = b.tiles[4];
+    wp.ntiles = b.nt + 4;
+    wp.max_tiles = int(b.mt[4]);
+    rc = run_wgrad(wp, b.dlT, b.Tpad, b.rxT_all, b.Tpad, grads->dw_router, d, stream);
+    if (rc) return rc;
+    if (grads->dbias) MOE_HIP(launch_colsum(b.dl, T, E, E, grads->dbias, stream));
+  }
+
+  // 6. back to token order, with the RMSNorm backward (saved r)
+  {
+    TokenBwdArgs t{};
+    t.T = T;
+    t.d = d;
+    t.k = k;
+    t.E = int(E);
+    t.residual = L->residual;
+    t.x = static_cast<const uint16_t*>(x);
+    t.dout = dout16;
+    t.gamma = static_cast<const uint16_t*>(L->gamma);
+    t.r = fw.r;
+    t.pos = fw.pos;
+    t.dxperm = b.dxperm;
+    t.dr_row = b.dr_row;
+    t.dxs = L->shared ? b.dxs : nullptr;
+    t.dr_shared = L->shared ? b.dr_s : nullptr;
+    t.dl = b.dl;
+    t.wr = static_cast<const uint16_t*>(L->router.wr_t);
+    t.dr_router = b.drr;
+    t.dx = static_cast<uint16_t*>(grads->dx);
+    t.dgamma_part = b.dgamma_part;
+    MOE_HIP(launch_token_bwd(t, stream));
+    if (L->gamma)
+      MOE_HIP(launch_colsum(b.dgamma_part, token_bwd_blocks(T), d, d, grads->dgamma, stream));
+  }
+  return ok();
+}
+
+}  // extern "C"
+
+extern "C" {
 
 // ---------------------------------------------------------------- timer
 

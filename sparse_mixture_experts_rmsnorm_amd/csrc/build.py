@@ -21,7 +21,7 @@ BUILD = PKG / "_build"
 LIB = PKG / "libmoe_mi355x.so"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["router.hip", "dispatch.hip", "topology.hip", "gemm.hip", "gemm_mx.hip", "combine.hip",
-           "atomic.hip", "api.cpp"]
+           "atomic.hip", "backward.hip", "api.cpp"]
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"-I{ROOT / 'include'}", f"-I{HERE}",
           "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
 # gfx950 only; packed-fp32 instructions are turned off in the device pass.

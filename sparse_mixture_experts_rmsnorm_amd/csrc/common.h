@@ -64,6 +64,19 @@ __device__ __forceinline__ float gelu_tanh(float z) {
 }
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// Derivatives (the backward pass): GELU' = Phi(z) + z phi(z); the tanh
+// form's derivative with u = c (z + 0.044715 z^3); SiLU' = s (1 + z (1 - s)).
+__device__ __forceinline__ float gelu_erf_grad(float z) {
+  return 0.5f * (1.0f + erff(z * 0.70710678118654752f)) +
+         z * 0.39894228040143268f * expf(-0.5f * z * z);
+}
+__device__ __forceinline__ float gelu_tanh_grad(float z) {
+  const float c = 0.79788456080286536f;
+  const float t = tanhf(c * (z + 0.044715f * z * z * z));
+  return 0.5f * (1.0f + t) + 0.5f * z * (1.0f - t * t) * c * (1.0f + 0.134145f * z * z);
+}
+__device__ __forceinline__ float sigmoidf(float z) { return 1.0f / (1.0f + expf(-z)); }
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
   return (uint64_t(1) << (threadIdx.x & 63)) - 1;
 }

@@ -58,8 +58,25 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const Tile& til
     const int row = tile.row0 + wt * WTT + j * 32 + fr;
     if (row >= tile.row_end) continue;
     float rs = 1.f;
-    if (EPI == EPI_ACT || EPI == EPI_SWIGLU || EPI == EPI_SCALE_F32) rs = a.row_r[row];
+    if (EPI == EPI_ACT || EPI == EPI_SWIGLU) rs = a.row_r[row];
+    if (EPI == EPI_SCALE_F32) rs = a.row_r ? a.row_r[row] : 1.f;
     if (EPI == EPI_GATE || EPI == EPI_GATE_SPLIT) rs = a.row_w ? a.row_w[row] : 1.f;
+    if ((EPI == EPI_SWIGLU || EPI == EPI_ACT) && a.pre) {
+      // pre-activations for the backward pass, in the packed feature order
+      uint16_t* P = static_cast<uint16_t*>(a.pre) + int64_t(row) * a.ldpre +
+                    (EPI == EPI_SWIGLU ? 2 : 1) * tile.ocol0 + wf * WTF;
+#pragma unroll
+      for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int v = g * 4;
+          const uint32_t lo = uint32_t(f2bf(rs * acc[i][j][v])) |
+                              (uint32_t(f2bf(rs * acc[i][j][v + 1])) << 16);
+          const uint32_t hi = uint32_t(f2bf(rs * acc[i][j][v + 2])) |
+                              (uint32_t(f2bf(rs * acc[i][j][v + 3])) << 16);
+          *reinterpret_cast<uint2*>(P + i * 32 + g * 8 + fh * 4) = make_uint2(lo, hi);
+        }
+    }
     if (EPI == EPI_SWIGLU) {
       uint16_t* Y = static_cast<uint16_t*>(a.Y) + int64_t(row) * a.ldy + tile.ocol0 + wf * (WTF / 2);
 #pragma unroll
@@ -118,6 +135,107 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const Tile& til
   }
 }
 
+// Epilogue of the second linear's backward (EPI_BWD_ACT / EPI_BWD_SWIGLU).
+// acc = dout_row . w2^T over the tile's hidden units; with the gate g and r
+// of the row, dh = g acc and, from the saved pre-activations a (and u),
+//   GELU:   da = dh act'(a)
+//   SwiGLU: da = dh u silu'(a),  du = dh silu(a)
+// written in the packed order of the pre-activations.  Per row the tile
+// also sums acc * h (the gate's gradient) and a da + u du (r times the
+// statistic's gradient): in the lane, over the lane pair that holds the
+// row's other features, then over the feature waves in a fixed order
+// through LDS (red: 2 x WGF x BT floats).
+template <int BF, int BT, int WGF, int WGT, int EPI, int MF, int MT>
+__device__ __forceinline__ void gemm_epilogue_bwd(const GemmArgs& a, const Tile& tile,
+                                                  f32x16 (&acc)[MF][MT], int wf, int wt, int fr,
+                                                  int fh, float* red) {
+  constexpr int WTF = BF / WGF, WTT = BT / WGT;
+  constexpr bool SWI = EPI == EPI_BWD_SWIGLU;
+  const uint16_t* __restrict__ P = static_cast<const uint16_t*>(a.pre);
+  const uint16_t* __restrict__ H = static_cast<const uint16_t*>(a.hsav);
+  uint16_t* __restrict__ Y = static_cast<uint16_t*>(a.Y);
+  const int valid = tile.spare;                 // features of the tile that exist
+#pragma unroll
+  for (int j = 0; j < MT; ++j) {
+    const int row = tile.row0 + wt * WTT + j * 32 + fr;
+    float dgp = 0.f, drp = 0.f;
+    if (row < tile.row_end) {
+      const float gate = a.row_w ? a.row_w[row] : 1.f;
+      const uint16_t* prow = P + int64_t(row) * a.ldpre;
+      const uint16_t* hrow = H + int64_t(row) * a.ldh;
+      uint16_t* yrow = Y + int64_t(row) * a.ldy;
+#pragma unroll
+      for (int i = 0; i < MF; ++i) {
+        const int fl = wf * WTF + i * 32;       // wave-uniform
+        if (fl >= valid) continue;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int f = tile.ocol0 + fl + g * 8 + fh * 4;   // hidden unit of v = 0
+          const uint2 hv = *reinterpret_cast<const uint2*>(hrow + f);
+          const float hh[4] = {__uint_as_float(hv.x << 16), __uint_as_float(hv.x & 0xffff0000u),
+                               __uint_as_float(hv.y << 16), __uint_as_float(hv.y & 0xffff0000u)};
+          const int pk = SWI ? (f / 32) * 64 + (f % 32) : f;
+          const uint2 av = *reinterpret_cast<const uint2*>(prow + pk);
+          const float aa[4] = {__uint_as_float(av.x << 16), __uint_as_float(av.x & 0xffff0000u),
+                               __uint_as_float(av.y << 16), __uint_as_float(av.y & 0xffff0000u)};
+          float da[4], du[4], uu[4] = {0.f, 0.f, 0.f, 0.f};
+          if (SWI) {
+            const uint2 uv = *reinterpret_cast<const uint2*>(prow + pk + 32);
+            uu[0] = __uint_as_float(uv.x << 16);
+            uu[1] = __uint_as_float(uv.x & 0xffff0000u);
+            uu[2] = __uint_as_float(uv.y << 16);
+            uu[3] = __uint_as_float(uv.y & 0xffff0000u);
+          }
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float t = acc[i][j][g * 4 + v];
+            dgp += t * hh[v];
+            const float dh = gate * t;
+            if (SWI) {
+              const float s = sigmoidf(aa[v]);
+              da[v] = dh * uu[v] * s * (1.f + aa[v] * (1.f - s));
+              du[v] = dh * aa[v] * s;
+              drp += aa[v] * da[v] + uu[v] * du[v];
+            } else {
+              da[v] = dh * (a.act == 1 ? gelu_tanh_grad(aa[v]) : gelu_erf_grad(aa[v]));
+              du[v] = 0.f;
+              drp += aa[v] * da[v];
+            }
+          }
+          *reinterpret_cast<uint2*>(yrow + pk) =
+              make_uint2(uint32_t(f2bf(da[0])) | (uint32_t(f2bf(da[1])) << 16),
+                         uint32_t(f2bf(da[2])) | (uint32_t(f2bf(da[3])) << 16));
+          if (SWI)
+            *reinterpret_cast<uint2*>(yrow + pk + 32) =
+                make_uint2(uint32_t(f2bf(du[0])) | (uint32_t(f2bf(du[1])) << 16),
+                           uint32_t(f2bf(du[2])) | (uint32_t(f2bf(du[3])) << 16));
+        }
+      }
+    }
+    dgp += __shfl_xor(dgp, 32, 64);
+    drp += __shfl_xor(drp, 32, 64);
+    if (fh == 0) {
+      red[wf * BT + wt * WTT + j * 32 + fr] = dgp;
+      red[(WGF + wf) * BT + wt * WTT + j * 32 + fr] = drp;
+    }
+  }
+  __syncthreads();
+  for (int r = threadIdx.x; r < BT; r += 64 * WGF * WGT) {
+    const int row = tile.row0 + r;
+    if (row >= tile.row_end) continue;
+    float sg = 0.f, sr = 0.f;
+#pragma unroll
+    for (int w = 0; w < WGF; ++w) {
+      sg += red[w * BT + r];
+      sr += red[(WGF + w) * BT + r];
+    }
+    const float rr = a.row_r[row];
+    float* pp = a.part + int64_t(row) * a.ldpart + 2 * (tile.ocol0 / BF);
+    pp[0] = sg;
+    pp[1] = rr > 0.f ? sr / rr : 0.f;
+  }
+}
+
 // ---------------------------------------------------------------- bf16 MFMA GEMM, LDS-DMA ring
 
 // BF features x BT rows per workgroup, WGF x WGT waves, each wave a
@@ -163,7 +281,10 @@ __global__ void __launch_bounds__(64 * WGF * WGT, MINB) k_gemm_bf16_dma(GemmArgs
     const uint16_t* g;
     if (sg < SEGW) {
       row = sg * RSEG + srow;
-      g = W + int64_t(tile.wrow0 + row) * a.ldw + tile.kofs;
+      // a partial feature tile (backward of the second linear) reads its last
+      // existing weight row in place of the missing ones
+      const int wr = (EPI == EPI_BWD_ACT || EPI == EPI_BWD_SWIGLU) ? min(row, tile.spare - 1) : row;
+      g = W + int64_t(tile.wrow0 + wr) * a.ldw + tile.kofs;
     } else {
       row = (sg - SEGW) * RSEG + srow;
       // a K-split tile reads its own half of the activation row; with a row
@@ -254,7 +375,12 @@ __global__ void __launch_bounds__(64 * WGF * WGT, MINB) k_gemm_bf16_dma(GemmArgs
       }
     }
 #undef MOE_FRAGS2
-    gemm_epilogue<BF, BT, WGF, WGT, EPI>(a, tile, acc, wf, wt, fr, fh);
+    if constexpr (EPI == EPI_BWD_ACT || EPI == EPI_BWD_SWIGLU) {
+      __shared__ float red[2 * WGF * BT];
+      gemm_epilogue_bwd<BF, BT, WGF, WGT, EPI>(a, tile, acc, wf, wt, fr, fh, red);
+    } else {
+      gemm_epilogue<BF, BT, WGF, WGT, EPI>(a, tile, acc, wf, wt, fr, fh);
+    }
     return;
   }
 #pragma unroll
@@ -302,7 +428,8 @@ __global__ void __launch_bounds__(64 * WGF * WGT, MINB) k_gemm_bf16_dma(GemmArgs
     }
 #undef MOE_FRAGS
   }
-  gemm_epilogue<BF, BT, WGF, WGT, EPI>(a, tile, acc, wf, wt, fr, fh);
+  if constexpr (EPI != EPI_BWD_ACT && EPI != EPI_BWD_SWIGLU)
+    gemm_epilogue<BF, BT, WGF, WGT, EPI>(a, tile, acc, wf, wt, fr, fh);
 }
 
 // ---------------------------------------------------------------- fp32 SIMT GEMM
@@ -374,7 +501,8 @@ __global__ void __launch_bounds__(256) k_gemm_f32(GemmArgs a) {
     const int row = tile.row0 + ty + 16 * j;
     if (row >= tile.row_end) continue;
     float rs = 1.f;
-    if (EPI == EPI_ACT || EPI == EPI_SWIGLU || EPI == EPI_SCALE_F32) rs = a.row_r[row];
+    if (EPI == EPI_ACT || EPI == EPI_SWIGLU) rs = a.row_r[row];
+    if (EPI == EPI_SCALE_F32) rs = a.row_r ? a.row_r[row] : 1.f;
     if (EPI == EPI_GATE || EPI == EPI_GATE_SPLIT) rs = a.row_w ? a.row_w[row] : 1.f;
     float* Y = static_cast<float*>(a.Y) + int64_t(row) * a.ldy + tile.ocol0;
 #pragma unroll
@@ -409,6 +537,7 @@ __global__ void __launch_bounds__(1024) k_plan(PlanArgs p) {
   const bool dense = p.offsets == nullptr;
   const bool bcsr = !dense && p.row_offsets != nullptr;
   const int pf = p.swiglu && p.gemm == 1 ? 2 : 1;   // packed rows per hidden unit
+  const int km = p.kmul > 0 ? p.kmul : 1;            // second linear: K per hidden unit
   const int nunits = dense ? 1 : bcsr ? p.offsets[p.E] / p.block : p.E;
   // per unit tile count, then exclusive scan (each thread owns a contiguous run)
   const int per = (nunits + blockDim.x - 1) / blockDim.x;
@@ -417,14 +546,15 @@ __global__ void __launch_bounds__(1024) k_plan(PlanArgs p) {
   for (int u = lo; u < hi; ++u) {
     int cnt;
     if (dense) {
-      cnt = ((p.dense_rows + p.bt - 1) / p.bt) * (p.dense_n / p.bf);
+      cnt = ((p.dense_rows + p.bt - 1) / p.bt) * ((p.dense_n + (p.ragged ? p.bf - 1 : 0)) / p.bf);
     } else if (bcsr) {
       const int nz = p.row_offsets[u + 1] - p.row_offsets[u];
       cnt = p.gemm == 1 ? nz * p.block * pf / p.bf : p.d / p.bf;
     } else {
       const int rows = p.offsets[u + 1] - p.offsets[u];
       const int mt = (rows + p.bt - 1) / p.bt;
-      const int nf = p.gemm == 1 ? (p.foff[u + 1] - p.foff[u]) * pf / p.bf : p.d / p.bf;
+      const int nf = p.gemm == 1 ? ((p.foff[u + 1] - p.foff[u]) * pf + (p.ragged ? p.bf - 1 : 0)) / p.bf
+                                 : p.d / p.bf;
       cnt = mt * nf * (p.gemm == 2 ? p.ksplit : 1);
     }
     base_s[u] = cnt;
@@ -477,9 +607,10 @@ __global__ void __launch_bounds__(1024) k_plan(PlanArgs p) {
       if (p.gemm == 1) {
         t.kofs = 0;
         t.klen = p.d;
+        if (p.ragged) t.spare = min(p.bf, p.dense_n - nf * p.bf);
       } else {
-        t.kofs = p.foff[0];
-        t.klen = p.foff[1] - p.foff[0];
+        t.kofs = km * p.foff[0];
+        t.klen = km * (p.foff[1] - p.foff[0]);
       }
       t.ocol0 = nf * p.bf / p.fold;
     } else if (bcsr) {
@@ -505,7 +636,8 @@ __global__ void __launch_bounds__(1024) k_plan(PlanArgs p) {
     } else {
       const int rows = p.offsets[u + 1] - p.offsets[u];
       const int mt = (rows + p.bt - 1) / p.bt;
-      const int nfe = p.gemm == 1 ? (p.foff[u + 1] - p.foff[u]) * pf / p.bf : p.d / p.bf;
+      const int nfe = p.gemm == 1 ? ((p.foff[u + 1] - p.foff[u]) * pf + (p.ragged ? p.bf - 1 : 0)) / p.bf
+                                  : p.d / p.bf;
       const int sp = n / (mt * nfe);           // K split (second linear only)
       const int nn = n - sp * mt * nfe;
       const int nf = nn / mt, m = nn - nf * mt;
@@ -518,10 +650,11 @@ __global__ void __launch_bounds__(1024) k_plan(PlanArgs p) {
         t.kofs = 0;
         t.klen = p.d;
         t.ocol0 = nf * p.bf / p.fold;
+        if (p.ragged) t.spare = min(p.bf, (p.foff[u + 1] - p.foff[u]) * pf - nf * p.bf);
       } else {
-        const int kl = (p.foff[u + 1] - p.foff[u]) / p.ksplit;
+        const int kl = km * (p.foff[u + 1] - p.foff[u]) / p.ksplit;
         t.wrow0 = nf * p.bf;
-        t.kofs = p.foff[u] + sp * kl;
+        t.kofs = km * p.foff[u] + sp * kl;
         t.klen = kl;
         t.ocol0 = nf * p.bf;
       }
@@ -605,7 +738,10 @@ hipError_t launch_gemm(int dtype, const GemmArgs& a, int bf, int bt, int grid, h
       case EPI_SWIGLU: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_SWIGLU>), g, b8, 0, s, a); break;
       case EPI_GATE: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_GATE>), g, b8, 0, s, a); break;
       case EPI_SCALE_F32: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_SCALE_F32>), g, b8, 0, s, a); break;
-      default: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_GATE_SPLIT>), g, b8, 0, s, a); break;
+      case EPI_GATE_SPLIT: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_GATE_SPLIT>), g, b8, 0, s, a); break;
+      case EPI_BWD_ACT: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_BWD_ACT>), g, b8, 0, s, a); break;
+      case EPI_BWD_SWIGLU: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_BWD_SWIGLU>), g, b8, 0, s, a); break;
+      default: return hipErrorInvalidValue;
     }
   } else {
     switch (a.epi) {

@@ -20,7 +20,13 @@ struct Tile {
 };
 
 // EPI_GATE_SPLIT: gated partial of one K split, written to Y + split * ysplit.
-enum Epi { EPI_ACT = 0, EPI_SWIGLU = 1, EPI_GATE = 2, EPI_SCALE_F32 = 3, EPI_GATE_SPLIT = 4 };
+// EPI_BWD_ACT / EPI_BWD_SWIGLU: the backward of the second linear (see
+// GemmArgs.pre / hsav / part).  EPI_SCALE_F32 with row_r NULL stores the
+// plain fp32 accumulator (the weight-gradient GEMMs).
+enum Epi {
+  EPI_ACT = 0, EPI_SWIGLU = 1, EPI_GATE = 2, EPI_SCALE_F32 = 3, EPI_GATE_SPLIT = 4,
+  EPI_BWD_ACT = 5, EPI_BWD_SWIGLU = 6
+};
 
 struct GemmArgs {
   const void* X; int64_t ldx;      // activations, row = GEMM row
@@ -33,6 +39,17 @@ struct GemmArgs {
   int64_t ysplit;                  // EPI_GATE_SPLIT: elements between split planes
   const int32_t* xrow;             // NULL, or X row of each GEMM row (-1: any row;
                                    // its result is never read)
+  // First linear (EPI_ACT / EPI_SWIGLU): when non-NULL, the pre-activations
+  // r * acc are also stored (bf16) at pre[row * ldpre + packed feature], in
+  // the expert-local packed order of the weights.  Backward of the second
+  // linear (EPI_BWD_*): acc = dout . w2^T of the row; pre holds the saved
+  // pre-activations, hsav the saved h [row * ldh + unit]; Y receives the
+  // pre-activation gradients (bf16, packed order), and part[row * ldpart +
+  // 2 * tile] the tile's sums over its units of acc * h and of
+  // (pre * dpre) / r (the gate's and the statistic's gradients).
+  void* pre; int64_t ldpre;
+  const void* hsav; int64_t ldh;
+  float* part; int64_t ldpart;
 };
 
 // Plan of GEMM tiles for grouped experts.  gemm = 1: first linear (features
@@ -49,6 +66,9 @@ struct PlanArgs {
   int fold;                  // output columns per packed feature divisor (2 for SwiGLU GEMM1)
   Tile* tiles; int* ntiles; int max_tiles;
   int ksplit;                // second linear: K halves per tile (1 or 2); tile.spare = split
+  int kmul;                  // second linear: K = kmul * f_e at kmul * foff[e] (0 means 1)
+  int ragged;                // first linear: last feature tile of a group may be partial
+                             // (tile.spare = its valid features, a multiple of 32)
   // BCSR (topology walk) when row_offsets != NULL
   const int32_t* row_offsets; const int32_t* column_indices; const int32_t* block_offsets;
   int block;

@@ -88,6 +88,54 @@ struct AtomicArgs {
   const float* r_tok = nullptr;   // [T]
 };
 hipError_t launch_atomic(const AtomicArgs& a, hipStream_t s);
+
+// ---- backward pass (backward.hip)
+// out[base_e + m, j] = rscale[row] * src[rowmap[row], m], row = offsets[e] + j,
+// for j < rows_e (zero rows past the map's -1 and for rows_e <= j <
+// pad64(rows_e)), m < width_e: width_e = wfix (base e * wfix) when wfix > 0,
+// else wmul * f_e (base wmul * foff[e]).  offsets NULL: one segment of
+// dense_rows rows.  Every width is a multiple of 64.
+struct GatherTArgs {
+  const uint16_t* src; int64_t lds;
+  const int32_t* rowmap;    // NULL: the row itself
+  const float* rscale;      // NULL: 1
+  const int32_t* offsets; int dense_rows; int E;
+  const int32_t* foff; int wmul; int wfix;
+  uint16_t* out; int64_t ldo;
+};
+hipError_t launch_gather_t(const GatherTArgs& a, int max_width, int max_rows, int units,
+                           hipStream_t s);
+// Weight-gradient tiles: X rows xmul * foff[e] .. xmul * foff[e+1] (or xfix
+// rows from 0), W rows e * wstride + [0, d), K = pad64(rows of segment e).
+struct WgradPlanArgs {
+  const int32_t* offsets; int dense_rows; int E;
+  const int32_t* foff; int xmul; int xfix;
+  int wstride; int d;
+  Tile* tiles; int* ntiles; int max_tiles;
+};
+hipError_t launch_plan_wgrad(const WgradPlanArgs& p, hipStream_t s);
+hipError_t launch_reduce_part(const float* part, int64_t ldpart, int64_t rows,
+                              const int32_t* row_expert, const int32_t* foff, int dense_nft,
+                              float* dg_row, float* dr_row, hipStream_t s);
+hipError_t launch_colsum(const float* in, int64_t n, int64_t ld, int64_t cols, float* out,
+                         hipStream_t s);
+struct RouterBwdArgs {
+  int64_t T, Tpad; int E, k, renorm;
+  const float* logits; const int32_t* ids; const float* w; const int32_t* pos;
+  const float* dg_row; const float* bias; const float* r;
+  float* dl; uint16_t* dlT; int64_t ldt; float* dr;
+};
+hipError_t launch_router_bwd(const RouterBwdArgs& a, hipStream_t s);
+struct TokenBwdArgs {
+  int64_t T, d; int k, E, residual;
+  const uint16_t* x; const uint16_t* dout; const uint16_t* gamma; const float* r;
+  const int32_t* pos; const float* dxperm; const float* dr_row;
+  const float* dxs; const float* dr_shared;
+  const float* dl; const uint16_t* wr; const float* dr_router;
+  uint16_t* dx; float* dgamma_part;   // [token_bwd_blocks(T), d] or NULL
+};
+int token_bwd_blocks(int64_t T);
+hipError_t launch_token_bwd(const TokenBwdArgs& a, hipStream_t s);
 // Slot counters of a layer that runs no dispatch (its router's ids are in
 // range by construction): rows = n, dropped = 0, max_load = -1, errors = 0.
 hipError_t launch_slot_stats(int64_t n, void* stats, hipStream_t s);

@@ -13,9 +13,12 @@ from .workloads import Workload
 
 
 class MoELayer:
-    def __init__(self, wl: Workload, params: dict, device="cuda"):
+    def __init__(self, wl: Workload, params: dict, device="cuda", train: bool = False):
+        """train=True: the forward keeps what backward() needs, and the
+        expert descriptors carry the backward's weight layouts."""
         import torch
         self.wl = wl
+        self.train = train
         self.device = device
         self.tdtype = torch.float32 if wl.dtype == "f32" else torch.bfloat16
         self.dtype = B.MOE_F32 if wl.dtype == "f32" else B.MOE_BF16
@@ -32,6 +35,7 @@ class MoELayer:
         desc.capacity_factor = wl.cf
         desc.residual = 1
         desc.timer = None
+        desc.save_for_backward = 1 if train else 0
 
         def empty(*shape):
             return torch.empty(shape, dtype=self.tdtype, device=device)
@@ -125,6 +129,14 @@ class MoELayer:
         X.w13_t = w13.data_ptr()
         X.w2_t = w2t.data_ptr()
         keep += [w13, w2t]
+        if self.train:
+            # backward layouts: the pages' w2 [F, d] as given, w13_t transposed
+            w2fk = params[n2].contiguous()
+            w13dk = torch.empty((d, w13.shape[0]), dtype=self.tdtype, device=self.device)
+            B.pack_transpose(w13, w13dk)
+            X.w2_fk = w2fk.data_ptr()
+            X.w13_dk = w13dk.data_ptr()
+            keep += [w2fk, w13dk]
         X.block = 128
         if kind == B.EXPERTS_BCSR:
             sb = torch.tensor([s // 128 for s in sizes], dtype=torch.int32, device=self.device)
@@ -164,6 +176,45 @@ class MoELayer:
             self.desc.timer = None
             self.desc.router_extras = None
         return out
+
+    def backward_workspace_size(self, T: int) -> int:
+        n = int(B.lib().moe_layer_backward_workspace_size(C.byref(self.desc), T))
+        if n == 0:
+            raise B.MoeError(-1, B.last_error() or "invalid layer descriptor for the backward")
+        return n
+
+    def backward(self, x, dout, ws, bws=None, grads: dict | None = None, stream=None) -> dict:
+        """Gradients for dout = dL/d(out) of the last forward on ws (fp32
+        weight gradients in the forward's packed layouts; dx in x's dtype)."""
+        import torch
+        if not self.train:
+            raise RuntimeError("the layer was built without train=True")
+        wl, d, T = self.wl, self.wl.d, x.shape[0]
+        dev = x.device
+        if bws is None:
+            bws = torch.empty(self.backward_workspace_size(T), dtype=torch.uint8, device=dev)
+        if grads is None:
+            f32 = dict(dtype=torch.float32, device=dev)
+            E = wl.E
+            F = sum(wl.sizes)
+            P = 2 * F if wl.act == "swiglu" else F
+            grads = dict(dx=torch.empty_like(x), dw_router=torch.empty((E, d), **f32),
+                         dw13=torch.empty((P, d), **f32), dw2=torch.empty((F, d), **f32))
+            if self.desc.router.bias:
+                grads["dbias"] = torch.empty(E, **f32)
+            if self.desc.gamma:
+                grads["dgamma"] = torch.empty(d, **f32)
+            if wl.shared_ffn:
+                Ps = 2 * wl.shared_ffn if wl.shared_act == "swiglu" else wl.shared_ffn
+                grads["dws13"] = torch.empty((Ps, d), **f32)
+                grads["dws2"] = torch.empty((wl.shared_ffn, d), **f32)
+        g = B.LayerGrads()
+        for name in ("dx", "dgamma", "dw_router", "dbias", "dw13", "dw2", "dws13", "dws2"):
+            setattr(g, name, B.ptr(grads.get(name)))
+        B.check(B.lib().moe_layer_backward(C.byref(self.desc), B.ptr(x), T, B.ptr(dout), B.ptr(ws),
+                                           ws.numel(), C.byref(g), B.ptr(bws), bws.numel(),
+                                           B.stream_handle(stream)))
+        return grads
 
     def routing(self, T: int, ws) -> dict:
         """Views into the workspace of the routing of the last forward."""

@@ -43,10 +43,13 @@ TOL = {"f32": 1e-3, "bf16": 2e-2}
 
 
 def rel_err(gpu, ref) -> float:
+    """max |gpu - ref| / max |ref| (the absolute error when ref is all zero)."""
     gpu = np.asarray(gpu, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
-    den = np.max(np.abs(ref)) if ref.size else 1.0
-    return float(np.max(np.abs(gpu - ref)) / den) if ref.size else 0.0
+    if not ref.size:
+        return 0.0
+    den = np.max(np.abs(ref))
+    return float(np.max(np.abs(gpu - ref)) / (den if den > 0 else 1.0))
 
 
 def oracle_params(wl: Workload, inp: dict) -> dict:
