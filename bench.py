@@ -71,6 +71,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mixtral_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the training step (forward + backward) measurement")
     ap.add_argument("--no-mx", action="store_true",
                     help="skip the MXFP8 variant of a grouped bf16 workload")
     ap.add_argument("--cpu-sample", type=int, default=4096,
@@ -187,6 +189,51 @@ def expert_kept(wl, layer, ws):
     if wl.pad > 1:
         kept = [int(min(c, offsets[e + 1] - offsets[e])) for e, c in enumerate(counts)]
     return kept, offsets
+
+
+def train_step(B, wl, params, x, steps, warmup):
+    """Forward (keeping what the backward needs) + backward of the same
+    layer for a seeded upstream gradient: the training step of the layer."""
+    import torch
+    from sparse_mixture_experts_rmsnorm_amd.layer import MoELayer
+    layer = MoELayer(wl, params, x.device, train=True)
+    ws = layer.alloc_workspace(wl.T)
+    bws = torch.empty(layer.backward_workspace_size(wl.T), dtype=torch.uint8, device=x.device)
+    out = torch.empty_like(x)
+    gen = torch.Generator(device=x.device).manual_seed(wl.seed + 7)
+    dout = torch.randn(x.shape, generator=gen, device=x.device).to(x.dtype)
+    grads = None
+    for _ in range(warmup):
+        layer.forward(x, out=out, ws=ws)
+        grads = layer.backward(x, dout, ws, bws=bws, grads=grads)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    fwd = bwd = 0.0
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        ev[0].record()
+        layer.forward(x, out=out, ws=ws)
+        ev[1].record()
+        layer.backward(x, dout, ws, bws=bws, grads=grads)
+        ev[2].record()
+        ev[2].synchronize()
+        fwd += ev[0].elapsed_time(ev[1])
+        bwd += ev[1].elapsed_time(ev[2])
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    kept, _ = expert_kept(wl, layer, ws)
+    f_fwd = flops_gemm1(wl, kept) + flops_gemm2(wl, kept)
+    bwd_ms = bwd / steps
+    res = {"fwd_ms": fwd / steps, "bwd_ms": bwd_ms, "step_ms": wall,
+           "tokens_per_s": wl.T / (wall * 1e-3),
+           "bwd_expert_tflop": 2 * f_fwd / 1e12,
+           "bwd_tflops_incl_all": 2 * f_fwd / (bwd_ms * 1e-3) / 1e12,
+           "note": ("fwd with save_for_backward, then moe_layer_backward for a seeded dout; "
+                    "bwd_tflops_incl_all = the four expert GEMMs' algorithmic FLOP (twice the "
+                    "forward's, kept rows only) over the whole backward time, router, "
+                    "transposes and token pass included")}
+    del layer, ws, bws, grads
+    torch.cuda.empty_cache()
+    return res
 
 
 def mx_variant(B, wl, params, x, steps, warmup):
@@ -328,6 +375,12 @@ def main():
                      "row once, write each permuted row once) timed on the layer's ids")}
     if wl.router == "dense":
         result["router_extras"] = time_router_extras(B, wl, layer, x, out, ws, args.steps)
+    if (not args.no_backward and wl.router == "dense" and wl.dtype == "bf16"
+            and wl.quant == "none" and wl.expert_kind in ("grouped", "bcsr")):
+        del layer, ws
+        torch.cuda.empty_cache()
+        layer = ws = None
+        result["train_step"] = train_step(B, wl, params, x, args.steps, args.warmup)
     if (not args.no_mx and wl.expert_kind == "grouped" and wl.dtype == "bf16"
             and wl.quant == "none" and all(f % 128 == 0 for f in wl.sizes)):
         del layer, ws

@@ -75,6 +75,7 @@ __all__ = [
     "atomic_experts_token_centric", "atomic_experts_expert_centric",
     "combine", "layer_forward",
     "gelu_grad", "gelu_tanh_grad", "silu_grad", "ffn_backward", "gates_backward", "layer_backward",
+    "expert_unit_grads",
 ]
 
 
@@ -920,7 +921,7 @@ def gates_backward(logits, ids, renorm: int, dg) -> np.ndarray:
     return dl
 
 
-def layer_backward(p: dict, x, dout, ids_override=None) -> dict:
+def layer_backward(p: dict, x, dout, ids_override=None, tokens=None) -> dict:
     """Gradients of layer_forward's output for the upstream gradient dout
     (dense router, routed grouped experts, shared experts).
 
@@ -932,6 +933,11 @@ def layer_backward(p: dict, x, dout, ids_override=None) -> dict:
     l = r (xhat w_router) + b; the RMSNorm backward uses the saved r:
     with xhat = x gamma and r = (mean x^2 + eps)^-1/2,
     dx = dout + gamma dxhat - (r^3 / d) dr x  and  dgamma = sum_t dxhat x.
+
+    tokens (optional) restricts the computation to those tokens' own
+    gradients: dx, dxhat, dr, dg and dl of the tokens (in that order); the
+    weight gradients, which sum over every token, are then not returned.
+    The routing (selection, capacity, positions) still covers all tokens.
     """
     if p.get("router", "dense") != "dense":
         raise NotImplementedError("the backward covers the dense router")
@@ -956,45 +962,87 @@ def layer_backward(p: dict, x, dout, ids_override=None) -> dict:
     pos = dispatch(ids, E, cap, int(p.get("pad", 1)))["pos"]
 
     act = p["act"]
-    w1, w2 = as_f64(p["w1"]), as_f64(p["w2"])
-    w3 = as_f64(p.get("w3"))
+    # weights stay in their stored form; each expert's slices are widened
+    # to float64 when used
+    w1, w2, w3 = np.asarray(p["w1"]), np.asarray(p["w2"]), p.get("w3")
+    w3 = None if w3 is None else np.asarray(w3)
     foff = np.asarray(p["f_offsets"], dtype=np.int64)
     dxh = np.zeros((T, d))
     dr = np.zeros(T)
     dg = np.zeros((T, k))
-    res = dict(dw1=np.zeros_like(w1), dw2=np.zeros_like(w2),
-               dw3=None if w3 is None else np.zeros_like(w3))
-    tt, jj = np.nonzero(pos >= 0)
+    sub = tokens is not None
+    res = {} if sub else dict(dw1=np.zeros(w1.shape), dw2=np.zeros(w2.shape),
+                              dw3=None if w3 is None else np.zeros(w3.shape))
+    tok = np.arange(T) if not sub else np.asarray(tokens, dtype=np.int64)
+    keep = np.zeros(T, dtype=bool)
+    keep[tok] = True
+    tt, jj = np.nonzero((pos >= 0) & keep[:, None])
     e_rows = np.asarray(ids)[tt, jj].astype(np.int64)
     for e in np.unique(e_rows):
         m = e_rows == e
         ts, js = tt[m], jj[m]
         lo, hi = int(foff[e]), int(foff[e + 1])
-        w1e, w2e = w1[:, lo:hi], w2[lo:hi, :]
-        w3e = None if w3 is None else w3[:, lo:hi]
+        w1e, w2e = as_f64(w1[:, lo:hi]), as_f64(w2[lo:hi, :])
+        w3e = None if w3 is None else as_f64(w3[:, lo:hi])
         y = ffn(xh[ts], r[ts], w1e, w2e, act, w3e)
         dg[ts, js] = np.sum(G[ts] * y, axis=1)
         b = ffn_backward(xh[ts], r[ts], w1e, w2e, act, g[ts, js][:, None] * G[ts], w3e)
         np.add.at(dxh, ts, b["dxhat"])
         np.add.at(dr, ts, b["dr"])
-        res["dw1"][:, lo:hi] += b["dw1"]
-        res["dw2"][lo:hi, :] += b["dw2"]
-        if w3 is not None:
-            res["dw3"][:, lo:hi] += b["dw3"]
+        if not sub:
+            res["dw1"][:, lo:hi] += b["dw1"]
+            res["dw2"][lo:hi, :] += b["dw2"]
+            if w3 is not None:
+                res["dw3"][:, lo:hi] += b["dw3"]
     if p.get("ws1") is not None:
         sact = p.get("shared_act", "swiglu" if p.get("ws3") is not None else "gelu")
-        b = ffn_backward(xh, r, as_f64(p["ws1"]), as_f64(p["ws2"]), sact, G, as_f64(p.get("ws3")))
-        dxh += b["dxhat"]
-        dr += b["dr"]
+        b = ffn_backward(xh[tok], r[tok], as_f64(p["ws1"]), as_f64(p["ws2"]), sact, G[tok],
+                         as_f64(p.get("ws3")))
+        dxh[tok] += b["dxhat"]
+        dr[tok] += b["dr"]
         res.update(dws1=b["dw1"], dws2=b["dw2"], dws3=b.get("dw3"))
-    dl = gates_backward(logits, ids, renorm, dg)
-    z = xh @ wr
+    dl = np.zeros((T, E))
+    dl[tok] = gates_backward(logits[tok], np.asarray(ids)[tok], renorm, dg[tok])
+    z = xh[tok] @ wr
     res["dw_router"] = (r[:, None] * xh).T @ dl
     res["dbias"] = dl.sum(axis=0)
-    dxh += r[:, None] * (dl @ wr.T)
-    dr += np.sum(z * dl, axis=1)
+    dxh[tok] += r[tok, None] * (dl[tok] @ wr.T)
+    dr[tok] += np.sum(z * dl[tok], axis=1)
     dx = G.copy() if p.get("residual", True) else np.zeros_like(G)
     dx += (dxh * gamma if gamma is not None else dxh) - (r ** 3 / d)[:, None] * dr[:, None] * x64
-    res.update(dx=dx, dgamma=None if gamma is None else np.sum(dxh * x64, axis=0), dg=dg, dl=dl,
-               dxhat=dxh, dr=dr, ids=np.asarray(ids, dtype=np.int32), pos=pos)
+    res.update(dx=dx[tok], dgamma=None if gamma is None else np.sum(dxh * x64, axis=0),
+               dg=dg[tok], dl=dl[tok], dxhat=dxh[tok], dr=dr[tok],
+               ids=np.asarray(ids, dtype=np.int32), pos=pos, tokens=tok)
+    if sub:
+        for key in ("dw1", "dw2", "dw3", "dws1", "dws2", "dws3", "dw_router", "dbias", "dgamma"):
+            res.pop(key, None)
     return res
+
+
+def expert_unit_grads(p: dict, x, dout, ids, e: int, units) -> dict:
+    """Weight gradients of routed expert e restricted to some of its hidden
+    units: dw1[:, units], dw3[:, units], dw2[units, :] summed over all of the
+    expert's kept rows.  The FFN is separable over hidden units (each unit's
+    pre-activation, activation and down-projection row involve only that
+    unit), so this is the same computation as layer_backward on the units'
+    slices of the weights."""
+    x64 = as_f64(x)
+    G = as_f64(dout)
+    T, d = x64.shape
+    k = int(p["k"])
+    r = rmsnorm_scale(x64, float(p["eps"]))
+    xh = _xhat(x64, p.get("gamma"))
+    logits = router_logits(x64, p.get("gamma"), r, as_f64(p["w_router"]), p.get("bias"))
+    E = logits.shape[1]
+    ids = np.asarray(ids)
+    g = gates(logits, ids, int(p.get("renorm", 1)))
+    cap = capacity(T, k, E, float(p.get("cf", 0.0)))
+    pos = dispatch(ids, E, cap, int(p.get("pad", 1)))["pos"]
+    foff = np.asarray(p["f_offsets"], dtype=np.int64)
+    cols = int(foff[e]) + np.asarray(units, dtype=np.int64)
+    tt, jj = np.nonzero((pos >= 0) & (ids == e))
+    w1e = as_f64(np.asarray(p["w1"])[:, cols])
+    w2e = as_f64(np.asarray(p["w2"])[cols, :])
+    w3e = None if p.get("w3") is None else as_f64(np.asarray(p["w3"])[:, cols])
+    b = ffn_backward(xh[tt], r[tt], w1e, w2e, p["act"], g[tt, jj][:, None] * G[tt], w3e)
+    return dict(dw1=b["dw1"], dw2=b["dw2"], dw3=b.get("dw3"))

@@ -128,3 +128,73 @@ def test_backward_argument_checks(dev):
     small = torch.empty(16, dtype=torch.uint8, device=dev)
     with pytest.raises(B.MoeError, match="forward workspace"):
         layer.backward(params["x"], params["x"], small)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name", ["mixtral_bf16", "finegrained_bf16"])
+def test_backward_fullsize(name, dev):
+    """The backward at the full workload sizes, in the configuration the
+    benchmark times.  Checked on what the oracle can compute in pieces: dx of
+    sampled tokens (with and without the residual), and the routed and shared
+    expert weight gradients on sampled hidden units of a few experts (the FFN
+    is separable over hidden units).  The router and gain gradients sum every
+    token's expert outputs; they are checked at the small sizes above."""
+    from sparse_mixture_experts_rmsnorm_amd.workloads import WORKLOADS
+    _say(f"[gpu] full-size backward {name}")
+    wl = WORKLOADS[name]
+    params = synth.make_torch(wl, dev)
+    layer = MoELayer(wl, params, dev, train=True)
+    x = params["x"]
+    ws = layer.alloc_workspace(wl.T)
+    layer.forward(x, ws=ws)
+    gen = torch.Generator(device=dev).manual_seed(wl.seed + 7)
+    dout = torch.randn((wl.T, wl.d), generator=gen, device=dev).to(torch.bfloat16)
+    g = layer.backward(x, dout, ws)
+    layer.desc.residual = 0
+    g0 = layer.backward(x, dout, ws, grads={k: torch.empty_like(v) for k, v in g.items()})
+    layer.desc.residual = 1
+    torch.cuda.synchronize()
+    ids = layer.routing(wl.T, ws)["ids"].cpu().numpy()
+    inp = {k: synth.to_host(v) for k, v in params.items()}
+    dout_np = synth.to_host(dout)
+    p = oracle_params(wl, inp)
+    rng = np.random.default_rng(wl.seed)
+    tok = np.sort(rng.choice(wl.T, size=12, replace=False))
+    _say(f"  oracle: dx of {len(tok)} tokens")
+    ref = O.layer_backward(p, inp["x"], dout_np, ids_override=ids, tokens=tok)
+    ref0 = O.layer_backward(dict(p, residual=False), inp["x"], dout_np, ids_override=ids, tokens=tok)
+    e_dx = rel_err(f64(synth.to_host(g["dx"]))[tok], ref["dx"])
+    e_dx0 = rel_err(f64(synth.to_host(g0["dx"]))[tok], ref0["dx"])
+    # expert weight gradients on sampled units
+    foff = wl.f_offsets
+    sw = wl.act == "swiglu"
+    dw13 = g["dw13"].cpu().numpy()
+    dw2 = g["dw2"].cpu().numpy()
+    errs = []
+    for e in (0, wl.E - 1):
+        units = np.sort(rng.choice(wl.sizes[e], size=32, replace=False))
+        _say(f"  oracle: expert {e}, {len(units)} units")
+        u = O.expert_unit_grads(p, inp["x"], dout_np, ids, e, units)
+        f = foff[e] + units
+        rows1 = 2 * foff[e] + (units // 32) * 64 + units % 32 if sw else f
+        errs.append(rel_err(dw13[rows1], u["dw1"].T))
+        if sw:
+            errs.append(rel_err(dw13[rows1 + 32], u["dw3"].T))
+        errs.append(rel_err(dw2[f], u["dw2"]))
+    if wl.shared_ffn:
+        units = np.sort(rng.choice(wl.shared_ffn, size=32, replace=False))
+        x64 = f64(inp["x"])
+        r = O.rmsnorm_scale(x64, wl.eps)
+        ssw = wl.shared_act == "swiglu"
+        b = O.ffn_backward(x64, r, f64(inp["ws1"])[:, units], f64(inp["ws2"])[units, :],
+                           wl.shared_act, f64(dout_np), f64(inp["ws3"])[:, units] if ssw else None)
+        dws13 = g["dws13"].cpu().numpy()
+        rows1 = (units // 32) * 64 + units % 32 if ssw else units
+        errs.append(rel_err(dws13[rows1], b["dw1"].T))
+        if ssw:
+            errs.append(rel_err(dws13[rows1 + 32], b["dw3"].T))
+        errs.append(rel_err(g["dws2"].cpu().numpy()[units], b["dw2"]))
+    _say(f"  {name}: dx {e_dx:.2e}, dx without residual {e_dx0:.2e}, "
+         f"sampled weight gradients max {max(errs):.2e}")
+    assert e_dx <= TOL_BWD and e_dx0 <= TOL_BWD
+    assert max(errs) <= TOL_BWD

@@ -705,3 +705,24 @@ def test_gates_backward_special_cases():
     ids2 = O.select_topk(l, 3)
     assert np.allclose(O.gates_backward(l, ids2, 1, rng.standard_normal((5, 3))).sum(axis=1), 0,
                        atol=1e-14)
+
+
+def test_backward_token_subset_and_unit_slices_agree_with_the_whole():
+    """The two restrictions the full-size GPU tests use: layer_backward on a
+    token subset returns those tokens' rows of the full computation, and
+    expert_unit_grads returns the units' slices of the full weight gradients."""
+    p, x, G = _bwd_case("swiglu", 0, True, True, True, 0.75, 2, 5)
+    ids = O.layer_forward(p, x)["ids"]
+    full = O.layer_backward(p, x, G, ids_override=ids)
+    tok = np.array([0, 3, 6])
+    part = O.layer_backward(p, x, G, ids_override=ids, tokens=tok)
+    for key in ("dx", "dxhat", "dr", "dg", "dl"):
+        assert np.allclose(part[key], full[key][tok], rtol=1e-12, atol=1e-14), key
+    assert "dw1" not in part and "dw_router" not in part
+    units = np.array([1, 5, 15])
+    for e in range(4):
+        u = O.expert_unit_grads(p, x, G, ids, e, units)
+        cols = p["f_offsets"][e] + units
+        assert np.allclose(u["dw1"], full["dw1"][:, cols], rtol=1e-12, atol=1e-14)
+        assert np.allclose(u["dw3"], full["dw3"][:, cols], rtol=1e-12, atol=1e-14)
+        assert np.allclose(u["dw2"], full["dw2"][cols, :], rtol=1e-12, atol=1e-14)
