@@ -1204,7 +1204,9 @@ struct BwdWs {
   float* part = nullptr;       // [rows_max, 2 nft]
   float* dg_row = nullptr;     // [rows_max]
   float* dr_row = nullptr;
-  float* dxperm = nullptr;     // [rows_max, d]
+  float* dxperm = nullptr;     // [ksplit][rows_max, d]
+  int ksplit = 1;              // K halves of the dxhat GEMM (partial planes summed by the
+                               // token pass)
   uint16_t* hT = nullptr;      // [F, L]
   uint16_t* dpreT = nullptr;   // [P, L]
   uint16_t* dyT = nullptr;     // [E d, L]
@@ -1242,7 +1244,19 @@ void carve_backward(Carve& c, const moe_layer_desc* L, int64_t T, const ExpertGe
   b->part = c.take_n<float>(rm * 2 * b->nft);
   b->dg_row = c.take_n<float>(rm);
   b->dr_row = c.take_n<float>(rm);
-  b->dxperm = c.take_n<float>(rm * d);
+  {
+    // split K of the dxhat GEMM when its tile count leaves the last round of
+    // tiles badly filled (each half a whole number of 64-wide stages)
+    bool halves = true;
+    for (int64_t e = 0; e < E; ++e)
+      halves = halves && (L->experts.ffn_sizes[e] * g.pf) % 128 == 0;
+    const double cus = device_cus();
+    const int64_t rows_est = std::min(T * L->k, E * std::min(fw.cap, T));
+    const double n = (double(rows_est) / 256 + 0.5 * double(E)) * double(d / 256);
+    auto eff = [&](double t) { return t <= 0 ? 1.0 : (t / cus) / std::ceil(t / cus); };
+    b->ksplit = halves && eff(2 * n) > eff(n) + 0.08 ? 2 : 1;
+  }
+  b->dxperm = c.take_n<float>(b->ksplit * rm * d);
   b->hT = c.take_n<uint16_t>(g.F * b->L);
   b->dpreT = c.take_n<uint16_t>(P * b->L);
   b->dyT = c.take_n<uint16_t>(E * d * b->L);
@@ -1254,7 +1268,7 @@ void carve_backward(Carve& c, const moe_layer_desc* L, int64_t T, const ExpertGe
   b->dgamma_part = L->gamma ? c.take_n<float>(int64_t(token_bwd_blocks(T)) * d) : nullptr;
   const int64_t nd = d / 256;
   b->mt[0] = (rm / 256 + E) * b->nft;
-  b->mt[1] = (rm / 256 + E) * nd;
+  b->mt[1] = (rm / 256 + E) * nd * b->ksplit;
   b->mt[2] = (P / 256 + E) * nd;
   b->mt[3] = (g.F / 256 + E) * nd;
   b->mt[4] = ((E + 255) / 256) * nd;
@@ -1311,6 +1325,7 @@ struct ExpertBwdIo {
   const void* h;               // saved h [rows, Fmax]
   const void* pre;             // saved pre-activations [rows, pf Fmax]
   void* dpre; float* part; int nft; float* dg_row; float* dr_row; float* dx_rows;
+  int ksplit; int64_t plane;   // K halves of the dxhat GEMM, elements between planes
   Tile* t_b1; int64_t mt_b1; int* nt_b1;
   Tile* t_b2; int64_t mt_b2; int* nt_b2;
 };
@@ -1340,6 +1355,7 @@ int run_expert_bwd(const ExpertBwdIo& io, int64_t d, int64_t T, const void* dout
   p.gemm = 2;
   p.ragged = 0;
   p.kmul = g.pf;
+  p.ksplit = std::max(1, io.ksplit);
   p.dense_n = int(d);
   p.tiles = io.t_b2;
   p.ntiles = io.nt_b2;
@@ -1378,6 +1394,7 @@ int run_expert_bwd(const ExpertBwdIo& io, int64_t d, int64_t T, const void* dout
   b.ntiles = io.nt_b2;
   b.Y = io.dx_rows;
   b.ldy = d;
+  b.ysplit = io.plane;
   b.row_r = io.row_r;
   b.epi = EPI_SCALE_F32;
   MOE_HIP(launch_gemm(MOE_BF16, b, 256, 256, int(io.mt_b2), s));
@@ -1466,6 +1483,8 @@ int moe_layer_backward(const moe_layer_desc* L, const void* x, int64_t T, const 
   io.dg_row = b.dg_row;
   io.dr_row = b.dr_row;
   io.dx_rows = b.dxperm;
+  io.ksplit = b.ksplit;
+  io.plane = fw.rows_max * d;
   io.t_b1 = b.tiles[0];
   io.mt_b1 = b.mt[0];
   io.nt_b1 = b.nt;
@@ -1553,6 +1572,7 @@ int moe_layer_backward(const moe_layer_desc* L, const void* x, int64_t T, const 
     si.nft = b.nft_s;
     si.dr_row = b.dr_s;
     si.dx_rows = b.dxs;
+    si.ksplit = 1;
     si.t_b1 = b.tiles[5];
     si.mt_b1 = b.mt[5];
     si.nt_b1 = b.nt + 5;
@@ -1647,6 +1667,8 @@ int moe_layer_backward(const moe_layer_desc* L, const void* x, int64_t T, const 
     t.r = fw.r;
     t.pos = fw.pos;
     t.dxperm = b.dxperm;
+    t.ksplit = b.ksplit;
+    t.plane = fw.rows_max * d;
     t.dr_row = b.dr_row;
     t.dxs = L->shared ? b.dxs : nullptr;
     t.dr_shared = L->shared ? b.dr_s : nullptr;

@@ -266,6 +266,7 @@ __global__ void __launch_bounds__(256) k_router_bwd(RouterBwdArgs a) {
 // One block per TB tokens.  For token t, with its kept slots' rows p_j:
 //   dr_t   = sum_j dr_row[p_j] + dr_shared[t] + dr_router[t]
 //   dxh[c] = sum_j dxperm[p_j, c] + dxs[t, c] + r_t sum_e dl[t, e] wr[e, c]
+// (dxperm summed over its K-split planes)
 //   dx[c]  = dout[t, c] (residual) + gamma[c] dxh[c] - (r_t^3 / d) dr_t x[t, c]
 // (the RMSNorm backward with the saved r), and the block's partial of
 // dgamma[c] = sum_t dxh[c] x[t, c].  Each thread owns 8 consecutive columns.
@@ -297,10 +298,13 @@ __global__ void __launch_bounds__(256) k_bwd_token(TokenBwdArgs a) {
         const int p = a.pos[int64_t(t) * a.k + j];
         if (p < 0) continue;
         dr += a.dr_row[p];
-        const float4* s = reinterpret_cast<const float4*>(a.dxperm + int64_t(p) * d + c0);
-        const float4 u = s[0], v = s[1];
-        dxh[0] += u.x; dxh[1] += u.y; dxh[2] += u.z; dxh[3] += u.w;
-        dxh[4] += v.x; dxh[5] += v.y; dxh[6] += v.z; dxh[7] += v.w;
+        for (int sp = 0; sp < a.ksplit; ++sp) {
+          const float4* s =
+              reinterpret_cast<const float4*>(a.dxperm + sp * a.plane + int64_t(p) * d + c0);
+          const float4 u = s[0], v = s[1];
+          dxh[0] += u.x; dxh[1] += u.y; dxh[2] += u.z; dxh[3] += u.w;
+          dxh[4] += v.x; dxh[5] += v.y; dxh[6] += v.z; dxh[7] += v.w;
+        }
       }
       if (a.dxs) {
         const float4* s = reinterpret_cast<const float4*>(a.dxs + int64_t(t) * d + c0);

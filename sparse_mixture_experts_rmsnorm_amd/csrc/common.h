@@ -16,12 +16,14 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
-// fp32 -> bf16 with round-to-nearest-even (quiet NaN kept).
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
+// fp32 -> bf16 with round-to-nearest-even: gfx950's v_cvt_pk_bf16_f32
+// (NaN stays NaN).  pk_bf16 converts a pair in one instruction, a in the
+// low half.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 // element <-> float for the two storage types (float, or bf16 bits)
@@ -53,7 +55,7 @@ __device__ __forceinline__ uint4 pack16(const float* o, const float*) {
 __device__ __forceinline__ uint4 pack16(const float* o, const uint16_t*) {
   uint32_t w[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) w[i] = uint32_t(f2bf(o[2 * i])) | (uint32_t(f2bf(o[2 * i + 1])) << 16);
+  for (int i = 0; i < 4; ++i) w[i] = pk_bf16(o[2 * i], o[2 * i + 1]);
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
@@ -62,7 +64,11 @@ __device__ __forceinline__ float gelu_tanh(float z) {
   const float c = 0.79788456080286536f;  // sqrt(2/pi)
   return 0.5f * z * (1.0f + tanhf(c * (z + 0.044715f * z * z * z)));
 }
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// 1 / (1 + e^-z) by the hardware exp2 and reciprocal (about 2 ulp)
+__device__ __forceinline__ float sigmoidf(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
+}
+__device__ __forceinline__ float silu(float z) { return z * sigmoidf(z); }
 
 // Derivatives (the backward pass): GELU' = Phi(z) + z phi(z); the tanh
 // form's derivative with u = c (z + 0.044715 z^3); SiLU' = s (1 + z (1 - s)).
@@ -75,7 +81,6 @@ __device__ __forceinline__ float gelu_tanh_grad(float z) {
   const float t = tanhf(c * (z + 0.044715f * z * z * z));
   return 0.5f * (1.0f + t) + 0.5f * z * (1.0f - t * t) * c * (1.0f + 0.134145f * z * z);
 }
-__device__ __forceinline__ float sigmoidf(float z) { return 1.0f / (1.0f + expf(-z)); }
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
   return (uint64_t(1) << (threadIdx.x & 63)) - 1;

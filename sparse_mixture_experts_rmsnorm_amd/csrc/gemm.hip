@@ -70,10 +70,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const Tile& til
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int v = g * 4;
-          const uint32_t lo = uint32_t(f2bf(rs * acc[i][j][v])) |
-                              (uint32_t(f2bf(rs * acc[i][j][v + 1])) << 16);
-          const uint32_t hi = uint32_t(f2bf(rs * acc[i][j][v + 2])) |
-                              (uint32_t(f2bf(rs * acc[i][j][v + 3])) << 16);
+          const uint32_t lo = pk_bf16(rs * acc[i][j][v], rs * acc[i][j][v + 1]);
+          const uint32_t hi = pk_bf16(rs * acc[i][j][v + 2], rs * acc[i][j][v + 3]);
           *reinterpret_cast<uint2*>(P + i * 32 + g * 8 + fh * 4) = make_uint2(lo, hi);
         }
     }
@@ -94,12 +92,13 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const Tile& til
               const float up = rs * acc[2 * p + 1][j][v];
               o[e] = silu(gate) * up;
             }
-            pk[h] = uint32_t(f2bf(o[0])) | (uint32_t(f2bf(o[1])) << 16);
+            pk[h] = pk_bf16(o[0], o[1]);
           }
           *reinterpret_cast<uint2*>(Y + p * 32 + g * 8 + fh * 4) = make_uint2(pk[0], pk[1]);
         }
     } else if (EPI == EPI_SCALE_F32) {
-      float* Y = static_cast<float*>(a.Y) + int64_t(row) * a.ldy + tile.ocol0 + wf * WTF;
+      float* Y = static_cast<float*>(a.Y) + int64_t(row) * a.ldy + tile.ocol0 + wf * WTF +
+                 int64_t(tile.spare) * a.ysplit;
 #pragma unroll
       for (int i = 0; i < MF; ++i)
 #pragma unroll
@@ -127,7 +126,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const Tile& til
               const float z = rs * acc[i][j][g * 4 + h * 2 + e];
               o[e] = EPI == EPI_ACT ? apply_act(z, a.act) : z;
             }
-            pk[h] = uint32_t(f2bf(o[0])) | (uint32_t(f2bf(o[1])) << 16);
+            pk[h] = pk_bf16(o[0], o[1]);
           }
           *reinterpret_cast<uint2*>(Y + i * 32 + g * 8 + fh * 4) = make_uint2(pk[0], pk[1]);
         }
@@ -164,28 +163,39 @@ __device__ __forceinline__ void gemm_epilogue_bwd(const GemmArgs& a, const Tile&
       const uint16_t* prow = P + int64_t(row) * a.ldpre;
       const uint16_t* hrow = H + int64_t(row) * a.ldh;
       uint16_t* yrow = Y + int64_t(row) * a.ldy;
+      // every saved value of the row block is requested before the first
+      // store (the stores could alias them as far as the compiler knows, so
+      // interleaving would serialise one memory latency per group)
+      uint2 hv[MF][4], av[MF][4], uv[MF][4];
 #pragma unroll
       for (int i = 0; i < MF; ++i) {
         const int fl = wf * WTF + i * 32;       // wave-uniform
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          hv[i][g] = av[i][g] = uv[i][g] = make_uint2(0, 0);
+          if (fl >= valid) continue;
+          const int f = tile.ocol0 + fl + g * 8 + fh * 4;   // hidden unit of v = 0
+          const int pk = SWI ? (f / 32) * 64 + (f % 32) : f;
+          hv[i][g] = *reinterpret_cast<const uint2*>(hrow + f);
+          av[i][g] = *reinterpret_cast<const uint2*>(prow + pk);
+          if (SWI) uv[i][g] = *reinterpret_cast<const uint2*>(prow + pk + 32);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < MF; ++i) {
+        const int fl = wf * WTF + i * 32;
         if (fl >= valid) continue;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int f = tile.ocol0 + fl + g * 8 + fh * 4;   // hidden unit of v = 0
-          const uint2 hv = *reinterpret_cast<const uint2*>(hrow + f);
-          const float hh[4] = {__uint_as_float(hv.x << 16), __uint_as_float(hv.x & 0xffff0000u),
-                               __uint_as_float(hv.y << 16), __uint_as_float(hv.y & 0xffff0000u)};
+          const int f = tile.ocol0 + fl + g * 8 + fh * 4;
           const int pk = SWI ? (f / 32) * 64 + (f % 32) : f;
-          const uint2 av = *reinterpret_cast<const uint2*>(prow + pk);
-          const float aa[4] = {__uint_as_float(av.x << 16), __uint_as_float(av.x & 0xffff0000u),
-                               __uint_as_float(av.y << 16), __uint_as_float(av.y & 0xffff0000u)};
-          float da[4], du[4], uu[4] = {0.f, 0.f, 0.f, 0.f};
-          if (SWI) {
-            const uint2 uv = *reinterpret_cast<const uint2*>(prow + pk + 32);
-            uu[0] = __uint_as_float(uv.x << 16);
-            uu[1] = __uint_as_float(uv.x & 0xffff0000u);
-            uu[2] = __uint_as_float(uv.y << 16);
-            uu[3] = __uint_as_float(uv.y & 0xffff0000u);
-          }
+          const float hh[4] = {__uint_as_float(hv[i][g].x << 16), __uint_as_float(hv[i][g].x & 0xffff0000u),
+                               __uint_as_float(hv[i][g].y << 16), __uint_as_float(hv[i][g].y & 0xffff0000u)};
+          const float aa[4] = {__uint_as_float(av[i][g].x << 16), __uint_as_float(av[i][g].x & 0xffff0000u),
+                               __uint_as_float(av[i][g].y << 16), __uint_as_float(av[i][g].y & 0xffff0000u)};
+          const float uu[4] = {__uint_as_float(uv[i][g].x << 16), __uint_as_float(uv[i][g].x & 0xffff0000u),
+                               __uint_as_float(uv[i][g].y << 16), __uint_as_float(uv[i][g].y & 0xffff0000u)};
+          float da[4], du[4];
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const float t = acc[i][j][g * 4 + v];
@@ -202,13 +212,10 @@ __device__ __forceinline__ void gemm_epilogue_bwd(const GemmArgs& a, const Tile&
               drp += aa[v] * da[v];
             }
           }
-          *reinterpret_cast<uint2*>(yrow + pk) =
-              make_uint2(uint32_t(f2bf(da[0])) | (uint32_t(f2bf(da[1])) << 16),
-                         uint32_t(f2bf(da[2])) | (uint32_t(f2bf(da[3])) << 16));
+          *reinterpret_cast<uint2*>(yrow + pk) = make_uint2(pk_bf16(da[0], da[1]), pk_bf16(da[2], da[3]));
           if (SWI)
             *reinterpret_cast<uint2*>(yrow + pk + 32) =
-                make_uint2(uint32_t(f2bf(du[0])) | (uint32_t(f2bf(du[1])) << 16),
-                           uint32_t(f2bf(du[2])) | (uint32_t(f2bf(du[3])) << 16));
+                make_uint2(pk_bf16(du[0], du[1]), pk_bf16(du[2], du[3]));
         }
       }
     }
@@ -289,7 +296,7 @@ __global__ void __launch_bounds__(64 * WGF * WGT, MINB) k_gemm_bf16_dma(GemmArgs
       row = (sg - SEGW) * RSEG + srow;
       // a K-split tile reads its own half of the activation row; with a row
       // map the rows are gathered from the token rows (dispatch fused here)
-      const int xk0 = EPI == EPI_GATE_SPLIT ? tile.spare * tile.klen : 0;
+      const int xk0 = (EPI == EPI_GATE_SPLIT || EPI == EPI_SCALE_F32) ? tile.spare * tile.klen : 0;
       int xr = min(tile.row0 + row, xlast);
       if (a.xrow) xr = max(a.xrow[xr], 0);
       g = X + int64_t(xr) * a.ldx + xk0;

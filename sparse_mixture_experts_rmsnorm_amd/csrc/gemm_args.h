@@ -36,7 +36,8 @@ struct GemmArgs {
   const float* row_r;              // r per GEMM row (EPI_ACT / SWIGLU / SCALE)
   const float* row_w;              // gate per GEMM row (EPI_GATE), NULL = 1
   int epi; int act;                // act: 0 GELU erf, 1 GELU tanh
-  int64_t ysplit;                  // EPI_GATE_SPLIT: elements between split planes
+  int64_t ysplit;                  // EPI_GATE_SPLIT / EPI_SCALE_F32: elements between the
+                                   // K-split planes (tile.spare = split)
   const int32_t* xrow;             // NULL, or X row of each GEMM row (-1: any row;
                                    // its result is never read)
   // First linear (EPI_ACT / EPI_SWIGLU): when non-NULL, the pre-activations

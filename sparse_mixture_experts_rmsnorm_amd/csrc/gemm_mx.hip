@@ -342,8 +342,7 @@ __global__ void __launch_bounds__(512) k_gemm_mx(MxGemmArgs m) {
           uint32_t pk[2];
 #pragma unroll
           for (int h = 0; h < 2; ++h)
-            pk[h] = uint32_t(f2bf(rs * acc[i][j][g * 4 + h * 2])) |
-                    (uint32_t(f2bf(rs * acc[i][j][g * 4 + h * 2 + 1])) << 16);
+            pk[h] = pk_bf16(rs * acc[i][j][g * 4 + h * 2], rs * acc[i][j][g * 4 + h * 2 + 1]);
           *reinterpret_cast<uint2*>(Y + i * 32 + g * 8 + fh * 4) = make_uint2(pk[0], pk[1]);
         }
     }

@@ -129,7 +129,7 @@ hipError_t launch_router_bwd(const RouterBwdArgs& a, hipStream_t s);
 struct TokenBwdArgs {
   int64_t T, d; int k, E, residual;
   const uint16_t* x; const uint16_t* dout; const uint16_t* gamma; const float* r;
-  const int32_t* pos; const float* dxperm; const float* dr_row;
+  const int32_t* pos; const float* dxperm; int ksplit; int64_t plane; const float* dr_row;
   const float* dxs; const float* dr_shared;
   const float* dl; const uint16_t* wr; const float* dr_router;
   uint16_t* dx; float* dgamma_part;   // [token_bwd_blocks(T), d] or NULL
