@@ -38,13 +38,13 @@ TRAFFIC = {
     "mixtral_bf16": {
         "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
                                                  "common.h"),
-        "source_sha256": "fe3256bee1a58b43d61675771aca39b4dab00fb4c65800ebdb023ae9ef9cf49e",
-        "fetch_kib": 1934593.7, "write_kib": 229534.7},
+        "source_sha256": "1e26a41cecfb0aff04f80960bdc07508fed4ac239f803045828b8fdcf4252a50",
+        "fetch_kib": 1616241.7, "write_kib": 229387.5},
     "mixtral_mxfp8": {
         "kernel": "k_gemm_mx", "sources": ("gemm_mx.hip", "gemm_args.h", "gemm_common.h",
                                            "common.h"),
-        "source_sha256": "eb17b4edbe0c4bc093c1a20e8d8f57ca59d0a954f90b950a11fcd6f705f7b4fb",
-        "fetch_kib": 1122805.5, "write_kib": 130668.3},
+        "source_sha256": "a58389c36bc19ab350ffaafe9afea03698b23b427d5810727db888b227854535",
+        "fetch_kib": 1159218.7, "write_kib": 128142.8},
 }
 
 
