@@ -1196,10 +1196,16 @@ namespace {
 
 int64_t pad64(int64_t n) { return (n + 63) / 64 * 64; }
 
+// Tile edge of the weight-gradient GEMMs (256 x 256; 128 x 128 tiles with
+// two workgroups per compute unit measured slower: 4.9 against 3.85 ms for
+// the Mixtral-shaped layer's two weight gradients).
+constexpr int kWgTile = 256;
+
 // Pointers into the backward workspace.
 struct BwdWs {
   int64_t L = 0, Tpad = 0;     // K extents of the routed / token-wide weight-gradient GEMMs
-  int nft = 0;                 // routed feature tiles per row (ceil(Fmax / 256))
+  int nft = 0;                 // routed 64-unit blocks per row (ceil(Fmax / 64))
+  void* tbuf = nullptr;        // [rows_max, Fmax] bf16: dout . w2^T per row
   void* dpre = nullptr;        // [rows_max, pf Fmax] bf16
   float* part = nullptr;       // [rows_max, 2 nft]
   float* dg_row = nullptr;     // [rows_max]
@@ -1218,6 +1224,7 @@ struct BwdWs {
   float* dgamma_part = nullptr;
   // shared experts
   int nft_s = 0;
+  void* tbuf_s = nullptr;      // [T, F_s]
   void* dpre_s = nullptr;      // [T, P_s]
   float* part_s = nullptr;     // [T, 2 nft_s]
   float* dr_s = nullptr;       // [T]
@@ -1239,7 +1246,8 @@ void carve_backward(Carve& c, const moe_layer_desc* L, int64_t T, const ExpertGe
   const int64_t P = g.F * g.pf, Pmax = g.Fmax * g.pf;
   b->L = pad64((std::min(fw.cap, T) + pad - 1) / pad * pad);
   b->Tpad = pad64(T);
-  b->nft = int((g.Fmax + 255) / 256);
+  b->nft = int((g.Fmax + 63) / 64);
+  b->tbuf = c.take(size_t(rm) * g.Fmax * 2);
   b->dpre = c.take(size_t(rm) * Pmax * 2);
   b->part = c.take_n<float>(rm * 2 * b->nft);
   b->dg_row = c.take_n<float>(rm);
@@ -1267,14 +1275,17 @@ void carve_backward(Carve& c, const moe_layer_desc* L, int64_t T, const ExpertGe
   b->rxT_all = c.take_n<uint16_t>(d * b->Tpad);
   b->dgamma_part = L->gamma ? c.take_n<float>(int64_t(token_bwd_blocks(T)) * d) : nullptr;
   const int64_t nd = d / 256;
-  b->mt[0] = (rm / 256 + E) * b->nft;
+  b->mt[0] = (rm / 256 + E) * ((g.Fmax + 255) / 256);
   b->mt[1] = (rm / 256 + E) * nd * b->ksplit;
-  b->mt[2] = (P / 256 + E) * nd;
-  b->mt[3] = (g.F / 256 + E) * nd;
-  b->mt[4] = ((E + 255) / 256) * nd;
+  // weight-gradient GEMMs: 128 x 128 tiles (kWgTile)
+  const int64_t ndw = d / kWgTile;
+  b->mt[2] = (P / kWgTile + E) * ndw;
+  b->mt[3] = (g.F / kWgTile + E) * ndw;
+  b->mt[4] = ((E + kWgTile - 1) / kWgTile) * ndw;
   if (L->shared) {
     const int64_t Ps = gs.F * gs.pf;
-    b->nft_s = int((gs.F + 255) / 256);
+    b->nft_s = int((gs.F + 63) / 64);
+    b->tbuf_s = c.take(size_t(T) * gs.F * 2);
     b->dpre_s = c.take(size_t(T) * Ps * 2);
     b->part_s = c.take_n<float>(T * 2 * b->nft_s);
     b->dr_s = c.take_n<float>(T);
@@ -1283,10 +1294,10 @@ void carve_backward(Carve& c, const moe_layer_desc* L, int64_t T, const ExpertGe
     b->dpreT_s = c.take_n<uint16_t>(Ps * b->Tpad);
     b->GT = c.take_n<uint16_t>(d * b->Tpad);
     const int64_t mtT = (T + 255) / 256;
-    b->mt[5] = mtT * b->nft_s;
+    b->mt[5] = mtT * ((gs.F + 255) / 256);
     b->mt[6] = mtT * nd;
-    b->mt[7] = ((Ps + 255) / 256) * nd;
-    b->mt[8] = ((gs.F + 255) / 256) * nd;
+    b->mt[7] = ((Ps + kWgTile - 1) / kWgTile) * (d / kWgTile);
+    b->mt[8] = ((gs.F + kWgTile - 1) / kWgTile) * (d / kWgTile);
   }
   for (int i = 0; i < 9; ++i) {
     b->mt[i] = std::max<int64_t>(1, b->mt[i]);
@@ -1324,7 +1335,8 @@ struct ExpertBwdIo {
   const int32_t* row_expert;   // routed rows' expert (for the partial reduction)
   const void* h;               // saved h [rows, Fmax]
   const void* pre;             // saved pre-activations [rows, pf Fmax]
-  void* dpre; float* part; int nft; float* dg_row; float* dr_row; float* dx_rows;
+  void* tbuf; void* dpre; float* part; int nft; float* dg_row; float* dr_row; float* dx_rows;
+  uint16_t* hT; uint16_t* dpreT; int64_t ldo; int64_t seg_rows;   // transposed outputs
   int ksplit; int64_t plane;   // K halves of the dxhat GEMM, elements between planes
   Tile* t_b1; int64_t mt_b1; int* nt_b1;
   Tile* t_b2; int64_t mt_b2; int* nt_b2;
@@ -1370,19 +1382,33 @@ int run_expert_bwd(const ExpertBwdIo& io, int64_t d, int64_t T, const void* dout
   a.ldw = d;
   a.tiles = io.t_b1;
   a.ntiles = io.nt_b1;
-  a.Y = io.dpre;
-  a.ldy = Pmax;
-  a.row_w = io.row_w;
-  a.row_r = io.row_r;
-  a.epi = io.X->act == MOE_ACT_SWIGLU ? EPI_BWD_SWIGLU : EPI_BWD_ACT;
-  a.act = io.X->act == MOE_ACT_GELU_TANH ? 1 : 0;
-  a.pre = const_cast<void*>(io.pre);
-  a.ldpre = Pmax;
-  a.hsav = io.h;
-  a.ldh = g.Fmax;
-  a.part = io.part;
-  a.ldpart = 2 * io.nft;
+  a.Y = io.tbuf;
+  a.ldy = g.Fmax;
+  a.epi = EPI_STORE_T;
   MOE_HIP(launch_gemm(MOE_BF16, a, 256, 256, int(io.mt_b1), s));
+  ActBwdArgs ab{};
+  ab.t = static_cast<const uint16_t*>(io.tbuf);
+  ab.ldt = g.Fmax;
+  ab.h = static_cast<const uint16_t*>(io.h);
+  ab.ldh = g.Fmax;
+  ab.pre = static_cast<const uint16_t*>(io.pre);
+  ab.ldpre = Pmax;
+  ab.row_w = io.row_w;
+  ab.row_r = io.row_r;
+  ab.offsets = io.offsets;
+  ab.dense_rows = int(T);
+  ab.E = int(io.X->E);
+  ab.foff = io.X->ffn_offsets;
+  ab.swiglu = io.X->act == MOE_ACT_SWIGLU;
+  ab.act = io.X->act == MOE_ACT_GELU_TANH ? 1 : 0;
+  ab.dpre = static_cast<uint16_t*>(io.dpre);
+  ab.lddp = Pmax;
+  ab.dpreT = io.dpreT;
+  ab.hT = io.hT;
+  ab.ldo = io.ldo;
+  ab.part = io.part;
+  ab.ldpart = 2 * io.nft;
+  MOE_HIP(launch_act_bwd(ab, int(g.Fmax), int(io.seg_rows), int(io.offsets ? io.X->E : 1), s));
   MOE_HIP(launch_reduce_part(io.part, 2 * io.nft, io.rows, io.row_expert, io.X->ffn_offsets,
                              io.nft, io.dg_row, io.dr_row, s));
   GemmArgs b{};
@@ -1402,8 +1428,9 @@ int run_expert_bwd(const ExpertBwdIo& io, int64_t d, int64_t T, const void* dout
 }
 
 // Y [xrows, d] = sum over each segment's rows of X^T W (fp32, plain).
-int run_wgrad(const WgradPlanArgs& wp, const uint16_t* X, int64_t ldx, const uint16_t* W,
+int run_wgrad(WgradPlanArgs wp, const uint16_t* X, int64_t ldx, const uint16_t* W,
               int64_t ldw, float* Y, int64_t ldy, hipStream_t s) {
+  wp.tile = kWgTile;
   MOE_HIP(launch_plan_wgrad(wp, s));
   GemmArgs a{};
   a.X = X;
@@ -1415,7 +1442,7 @@ int run_wgrad(const WgradPlanArgs& wp, const uint16_t* X, int64_t ldx, const uin
   a.Y = Y;
   a.ldy = ldy;
   a.epi = EPI_SCALE_F32;
-  MOE_HIP(launch_gemm(MOE_BF16, a, 256, 256, wp.max_tiles, s));
+  MOE_HIP(launch_gemm(MOE_BF16, a, kWgTile, kWgTile, wp.max_tiles, s));
   return MOE_OK;
 }
 
@@ -1477,7 +1504,12 @@ int moe_layer_backward(const moe_layer_desc* L, const void* x, int64_t T, const 
   io.row_expert = fw.row_expert;
   io.h = fw.ex.h;
   io.pre = fw.ex.pre;
+  io.tbuf = b.tbuf;
   io.dpre = b.dpre;
+  io.hT = b.hT;
+  io.dpreT = b.dpreT;
+  io.ldo = b.L;
+  io.seg_rows = b.L;
   io.part = b.part;
   io.nft = b.nft;
   io.dg_row = b.dg_row;
@@ -1501,16 +1533,6 @@ int moe_layer_backward(const moe_layer_desc* L, const void* x, int64_t T, const 
     t.E = int(E);
     t.foff = L->experts.ffn_offsets;
     t.ldo = b.L;
-    t.src = static_cast<const uint16_t*>(fw.ex.h);
-    t.lds = g.Fmax;
-    t.wmul = 1;
-    t.out = b.hT;
-    MOE_HIP(launch_gather_t(t, int(g.Fmax), int(b.L), int(E), stream));
-    t.src = static_cast<const uint16_t*>(b.dpre);
-    t.lds = g.Fmax * g.pf;
-    t.wmul = g.pf;
-    t.out = b.dpreT;
-    MOE_HIP(launch_gather_t(t, int(g.Fmax * g.pf), int(b.L), int(E), stream));
     t.wfix = int(d);
     t.rowmap = fw.row_token;
     t.src = dout16;
@@ -1567,7 +1589,12 @@ int moe_layer_backward(const moe_layer_desc* L, const void* x, int64_t T, const 
     si.row_r = fw.r;
     si.h = fw.sh.h;
     si.pre = fw.sh.pre;
+    si.tbuf = b.tbuf_s;
     si.dpre = b.dpre_s;
+    si.hT = b.hT_s;
+    si.dpreT = b.dpreT_s;
+    si.ldo = b.Tpad;
+    si.seg_rows = b.Tpad;
     si.part = b.part_s;
     si.nft = b.nft_s;
     si.dr_row = b.dr_s;
@@ -1585,16 +1612,6 @@ int moe_layer_backward(const moe_layer_desc* L, const void* x, int64_t T, const 
     t.dense_rows = int(T);
     t.E = 1;
     t.ldo = b.Tpad;
-    t.src = static_cast<const uint16_t*>(fw.sh.h);
-    t.lds = gs.F;
-    t.wfix = int(gs.F);
-    t.out = b.hT_s;
-    MOE_HIP(launch_gather_t(t, int(gs.F), int(b.Tpad), 1, stream));
-    t.src = static_cast<const uint16_t*>(b.dpre_s);
-    t.lds = Ps;
-    t.wfix = int(Ps);
-    t.out = b.dpreT_s;
-    MOE_HIP(launch_gather_t(t, int(Ps), int(b.Tpad), 1, stream));
     t.src = dout16;
     t.lds = d;
     t.wfix = int(d);

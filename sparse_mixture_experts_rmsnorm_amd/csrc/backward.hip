@@ -80,25 +80,148 @@ __global__ void __launch_bounds__(256) k_gather_t(GatherTArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- activation backward
+
+// One block per (64 rows of an expert segment, 64 hidden units).  From the
+// second linear's backward product t = dout_row . w2^T (ungated, bf16), the
+// gate g and r of the row and the saved h and pre-activations a (and u):
+//   dh = g t;  GELU: da = dh act'(a);  SwiGLU: da = dh u silu'(a), du = dh silu(a)
+// written row-major in the packed order (dpre, the dxhat GEMM's operand) and
+// transposed per segment (dpreT, and hT from h: the weight gradients'
+// K-contiguous operands, zero past the segment's rows up to a multiple of
+// 64), with the row's sums over the block's units of t * h (the gate's
+// gradient) and (a da + u du) / r (the statistic's) in part[row, 2 blk].
+__global__ void __launch_bounds__(256) k_act_bwd(ActBwdArgs a) {
+  __shared__ uint16_t th[64][64 + 2];
+  __shared__ uint16_t tda[64][64 + 2];
+  __shared__ uint16_t tdu[64][64 + 2];
+  const int e = blockIdx.z;
+  const int seg0 = a.offsets ? a.offsets[e] : 0;
+  const int cnt = a.offsets ? a.offsets[e + 1] - seg0 : a.dense_rows;
+  const int j0 = int(blockIdx.y) * 64;
+  if (j0 >= pad64(cnt)) return;
+  const int fe = a.foff[e + 1] - a.foff[e];
+  const int f0 = int(blockIdx.x) * 64;
+  if (f0 >= fe) return;
+  const bool swi = a.swiglu != 0;
+  const int t = threadIdx.x;
+  {
+    const int jj = t >> 2, cq = (t & 3) * 16;
+    const int j = j0 + jj;
+    const int row = seg0 + j;
+    const bool live = j < cnt;
+    const int f = f0 + cq;                       // first of this thread's 16 units
+    const int pk = swi ? (f / 32) * 64 + (f % 32) : f;
+    float tv[16], hv[16], av[16], uv[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) tv[q] = hv[q] = av[q] = uv[q] = 0.f;
+    float gate = 0.f, rr = 0.f;
+    if (live) {
+      gate = a.row_w ? a.row_w[row] : 1.f;
+      rr = a.row_r[row];
+      const uint4* pt = reinterpret_cast<const uint4*>(a.t + int64_t(row) * a.ldt + f);
+      const uint4* ph = reinterpret_cast<const uint4*>(a.h + int64_t(row) * a.ldh + f);
+      const uint4* pa = reinterpret_cast<const uint4*>(a.pre + int64_t(row) * a.ldpre + pk);
+      const uint4 t0 = pt[0], t1 = pt[1], h0 = ph[0], h1 = ph[1], a0 = pa[0], a1 = pa[1];
+      unpack16(t0, tv, (const uint16_t*)nullptr);
+      unpack16(t1, tv + 8, (const uint16_t*)nullptr);
+      unpack16(h0, hv, (const uint16_t*)nullptr);
+      unpack16(h1, hv + 8, (const uint16_t*)nullptr);
+      unpack16(a0, av, (const uint16_t*)nullptr);
+      unpack16(a1, av + 8, (const uint16_t*)nullptr);
+      if (swi) {
+        const uint4* pu = reinterpret_cast<const uint4*>(a.pre + int64_t(row) * a.ldpre + pk + 32);
+        const uint4 u0 = pu[0], u1 = pu[1];
+        unpack16(u0, uv, (const uint16_t*)nullptr);
+        unpack16(u1, uv + 8, (const uint16_t*)nullptr);
+      }
+    }
+    float da[16], du[16], sg = 0.f, sr = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      sg += tv[q] * hv[q];
+      const float dh = gate * tv[q];
+      if (swi) {
+        const float sgm = sigmoidf(av[q]);
+        da[q] = dh * uv[q] * sgm * (1.f + av[q] * (1.f - sgm));
+        du[q] = dh * av[q] * sgm;
+        sr += av[q] * da[q] + uv[q] * du[q];
+      } else {
+        da[q] = dh * (a.act == 1 ? gelu_tanh_grad(av[q]) : gelu_erf_grad(av[q]));
+        du[q] = 0.f;
+        sr += av[q] * da[q];
+      }
+    }
+    // the four threads of a row are adjacent lanes: sum them in a fixed order
+    sg += __shfl_xor(sg, 1, 64);
+    sr += __shfl_xor(sr, 1, 64);
+    sg += __shfl_xor(sg, 2, 64);
+    sr += __shfl_xor(sr, 2, 64);
+    if (live) {
+      uint4* pd = reinterpret_cast<uint4*>(a.dpre + int64_t(row) * a.lddp + pk);
+      pd[0] = pack16(da, (const uint16_t*)nullptr);
+      pd[1] = pack16(da + 8, (const uint16_t*)nullptr);
+      if (swi) {
+        pd = reinterpret_cast<uint4*>(a.dpre + int64_t(row) * a.lddp + pk + 32);
+        pd[0] = pack16(du, (const uint16_t*)nullptr);
+        pd[1] = pack16(du + 8, (const uint16_t*)nullptr);
+      }
+      if (cq == 0) {
+        float* pp = a.part + int64_t(row) * a.ldpart + 2 * (f0 / 64);
+        pp[0] = sg;
+        pp[1] = rr > 0.f ? sr / rr : 0.f;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      th[jj][cq + q] = f2bf(hv[q]);
+      tda[jj][cq + q] = f2bf(da[q]);
+      tdu[jj][cq + q] = f2bf(du[q]);
+    }
+  }
+  __syncthreads();
+  {
+    // transposed stores: unit m (64) x 16 rows per thread; SwiGLU writes the
+    // gate and up rows of the packed order
+    const int m = t >> 2, jq = (t & 3) * 16;
+    const int fu = f0 + m;
+    const int pku = swi ? (fu / 32) * 64 + (fu % 32) : fu;
+    auto put = [&](uint16_t (*tile)[66], uint16_t* out, int64_t orow) {
+      uint32_t w[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        w[q] = uint32_t(tile[jq + 2 * q][m]) | (uint32_t(tile[jq + 2 * q + 1][m]) << 16);
+      uint4* o = reinterpret_cast<uint4*>(out + orow * a.ldo + j0 + jq);
+      o[0] = make_uint4(w[0], w[1], w[2], w[3]);
+      o[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    };
+    put(th, a.hT, int64_t(a.foff[e]) + fu);
+    const int64_t pbase = int64_t(swi ? 2 : 1) * a.foff[e];
+    put(tda, a.dpreT, pbase + pku);
+    if (swi) put(tdu, a.dpreT, pbase + pku + 32);
+  }
+}
+
 // ---------------------------------------------------------------- weight-gradient tile plan
 
 // Tiles of Y[xrow, c] = sum_j X[xrow, j] W[wbase_e + c, j] over each
 // expert's K = pad64(rows_e): X rows of expert e are xb_e .. xb_e + xr_e - 1
 // (xr_e = xmul * f_e at xmul * foff[e], or xfix rows at 0), c covers d in
-// blocks of 256, W rows start at e * wstride.
+// blocks of the tile edge, W rows start at e * wstride.
 constexpr int kWgPlanMax = 4096;
 
 __global__ void __launch_bounds__(1024) k_plan_wgrad(WgradPlanArgs p) {
   __shared__ int base_s[kWgPlanMax + 1];
   __shared__ long long sh[33];
   const int nunits = p.offsets ? p.E : 1;
-  const int nf = p.d / 256;
+  const int bt = p.tile;                       // tile edge (rows and columns)
+  const int nf = p.d / bt;
   const int per = (nunits + blockDim.x - 1) / blockDim.x;
   const int lo = min(nunits, int(threadIdx.x) * per), hi = min(nunits, lo + per);
   auto xr_of = [&](int u) { return p.xfix > 0 ? p.xfix : p.xmul * (p.foff[u + 1] - p.foff[u]); };
   long long local = 0;
   for (int u = lo; u < hi; ++u) {
-    const int c = ((xr_of(u) + 255) / 256) * nf;
+    const int c = ((xr_of(u) + bt - 1) / bt) * nf;
     base_s[u] = c;
     local += c;
   }
@@ -153,20 +276,20 @@ __global__ void __launch_bounds__(1024) k_plan_wgrad(WgradPlanArgs p) {
     Tile t;
     t.expert = u;
     t.spare = 0;
-    t.row0 = xb + mb * 256;
+    t.row0 = xb + mb * bt;
     t.row_end = xb + xr;
-    t.wrow0 = u * p.wstride + cb * 256;
+    t.wrow0 = u * p.wstride + cb * bt;
     t.kofs = 0;
     t.klen = pad64(rows);
-    t.ocol0 = cb * 256;
+    t.ocol0 = cb * bt;
     p.tiles[idx] = t;
   }
 }
 
 // ---------------------------------------------------------------- reductions
 
-// dg_row[row] / dr_row[row]: sums over the row's feature tiles of the
-// second-linear backward's partials (fixed order).  Rows of no expert get 0.
+// dg_row[row] / dr_row[row]: sums over the row's 64-unit blocks of the
+// activation backward's partials (fixed order).  Rows of no expert get 0.
 __global__ void __launch_bounds__(256) k_reduce_part(const float* __restrict__ part, int64_t ldpart,
                                                      int64_t rows, const int32_t* __restrict__ row_expert,
                                                      const int32_t* __restrict__ foff, int dense_nft,
@@ -177,7 +300,7 @@ __global__ void __launch_bounds__(256) k_reduce_part(const float* __restrict__ p
   int nft = dense_nft;
   if (row_expert) {
     const int e = row_expert[row];
-    nft = e < 0 ? 0 : (foff[e + 1] - foff[e] + 255) / 256;
+    nft = e < 0 ? 0 : (foff[e + 1] - foff[e] + 63) / 64;
   }
   float sg = 0.f, sr = 0.f;
   for (int f = 0; f < nft; ++f) {
@@ -353,6 +476,14 @@ hipError_t launch_gather_t(const GatherTArgs& a, int max_width, int max_rows, in
   if (max_width <= 0 || max_rows <= 0 || units <= 0) return hipSuccess;
   const dim3 g(unsigned((max_width + 63) / 64), unsigned((max_rows + 63) / 64), unsigned(units));
   hipLaunchKernelGGL(k_gather_t, g, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_act_bwd(const ActBwdArgs& a, int max_units, int max_rows, int units,
+                          hipStream_t s) {
+  if (max_units <= 0 || max_rows <= 0 || units <= 0) return hipSuccess;
+  const dim3 g(unsigned((max_units + 63) / 64), unsigned((max_rows + 63) / 64), unsigned(units));
+  hipLaunchKernelGGL(k_act_bwd, g, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

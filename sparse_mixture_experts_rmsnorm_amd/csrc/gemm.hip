@@ -117,6 +117,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const Tile& til
       for (int i = 0; i < MF; ++i)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
+          if (EPI == EPI_STORE_T && wf * WTF + i * 32 >= tile.spare) continue;   // missing features
           uint32_t pk[2];
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
@@ -131,115 +132,6 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const Tile& til
           *reinterpret_cast<uint2*>(Y + i * 32 + g * 8 + fh * 4) = make_uint2(pk[0], pk[1]);
         }
     }
-  }
-}
-
-// Epilogue of the second linear's backward (EPI_BWD_ACT / EPI_BWD_SWIGLU).
-// acc = dout_row . w2^T over the tile's hidden units; with the gate g and r
-// of the row, dh = g acc and, from the saved pre-activations a (and u),
-//   GELU:   da = dh act'(a)
-//   SwiGLU: da = dh u silu'(a),  du = dh silu(a)
-// written in the packed order of the pre-activations.  Per row the tile
-// also sums acc * h (the gate's gradient) and a da + u du (r times the
-// statistic's gradient): in the lane, over the lane pair that holds the
-// row's other features, then over the feature waves in a fixed order
-// through LDS (red: 2 x WGF x BT floats).
-template <int BF, int BT, int WGF, int WGT, int EPI, int MF, int MT>
-__device__ __forceinline__ void gemm_epilogue_bwd(const GemmArgs& a, const Tile& tile,
-                                                  f32x16 (&acc)[MF][MT], int wf, int wt, int fr,
-                                                  int fh, float* red) {
-  constexpr int WTF = BF / WGF, WTT = BT / WGT;
-  constexpr bool SWI = EPI == EPI_BWD_SWIGLU;
-  const uint16_t* __restrict__ P = static_cast<const uint16_t*>(a.pre);
-  const uint16_t* __restrict__ H = static_cast<const uint16_t*>(a.hsav);
-  uint16_t* __restrict__ Y = static_cast<uint16_t*>(a.Y);
-  const int valid = tile.spare;                 // features of the tile that exist
-#pragma unroll
-  for (int j = 0; j < MT; ++j) {
-    const int row = tile.row0 + wt * WTT + j * 32 + fr;
-    float dgp = 0.f, drp = 0.f;
-    if (row < tile.row_end) {
-      const float gate = a.row_w ? a.row_w[row] : 1.f;
-      const uint16_t* prow = P + int64_t(row) * a.ldpre;
-      const uint16_t* hrow = H + int64_t(row) * a.ldh;
-      uint16_t* yrow = Y + int64_t(row) * a.ldy;
-      // every saved value of the row block is requested before the first
-      // store (the stores could alias them as far as the compiler knows, so
-      // interleaving would serialise one memory latency per group)
-      uint2 hv[MF][4], av[MF][4], uv[MF][4];
-#pragma unroll
-      for (int i = 0; i < MF; ++i) {
-        const int fl = wf * WTF + i * 32;       // wave-uniform
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          hv[i][g] = av[i][g] = uv[i][g] = make_uint2(0, 0);
-          if (fl >= valid) continue;
-          const int f = tile.ocol0 + fl + g * 8 + fh * 4;   // hidden unit of v = 0
-          const int pk = SWI ? (f / 32) * 64 + (f % 32) : f;
-          hv[i][g] = *reinterpret_cast<const uint2*>(hrow + f);
-          av[i][g] = *reinterpret_cast<const uint2*>(prow + pk);
-          if (SWI) uv[i][g] = *reinterpret_cast<const uint2*>(prow + pk + 32);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < MF; ++i) {
-        const int fl = wf * WTF + i * 32;
-        if (fl >= valid) continue;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int f = tile.ocol0 + fl + g * 8 + fh * 4;
-          const int pk = SWI ? (f / 32) * 64 + (f % 32) : f;
-          const float hh[4] = {__uint_as_float(hv[i][g].x << 16), __uint_as_float(hv[i][g].x & 0xffff0000u),
-                               __uint_as_float(hv[i][g].y << 16), __uint_as_float(hv[i][g].y & 0xffff0000u)};
-          const float aa[4] = {__uint_as_float(av[i][g].x << 16), __uint_as_float(av[i][g].x & 0xffff0000u),
-                               __uint_as_float(av[i][g].y << 16), __uint_as_float(av[i][g].y & 0xffff0000u)};
-          const float uu[4] = {__uint_as_float(uv[i][g].x << 16), __uint_as_float(uv[i][g].x & 0xffff0000u),
-                               __uint_as_float(uv[i][g].y << 16), __uint_as_float(uv[i][g].y & 0xffff0000u)};
-          float da[4], du[4];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float t = acc[i][j][g * 4 + v];
-            dgp += t * hh[v];
-            const float dh = gate * t;
-            if (SWI) {
-              const float s = sigmoidf(aa[v]);
-              da[v] = dh * uu[v] * s * (1.f + aa[v] * (1.f - s));
-              du[v] = dh * aa[v] * s;
-              drp += aa[v] * da[v] + uu[v] * du[v];
-            } else {
-              da[v] = dh * (a.act == 1 ? gelu_tanh_grad(aa[v]) : gelu_erf_grad(aa[v]));
-              du[v] = 0.f;
-              drp += aa[v] * da[v];
-            }
-          }
-          *reinterpret_cast<uint2*>(yrow + pk) = make_uint2(pk_bf16(da[0], da[1]), pk_bf16(da[2], da[3]));
-          if (SWI)
-            *reinterpret_cast<uint2*>(yrow + pk + 32) =
-                make_uint2(pk_bf16(du[0], du[1]), pk_bf16(du[2], du[3]));
-        }
-      }
-    }
-    dgp += __shfl_xor(dgp, 32, 64);
-    drp += __shfl_xor(drp, 32, 64);
-    if (fh == 0) {
-      red[wf * BT + wt * WTT + j * 32 + fr] = dgp;
-      red[(WGF + wf) * BT + wt * WTT + j * 32 + fr] = drp;
-    }
-  }
-  __syncthreads();
-  for (int r = threadIdx.x; r < BT; r += 64 * WGF * WGT) {
-    const int row = tile.row0 + r;
-    if (row >= tile.row_end) continue;
-    float sg = 0.f, sr = 0.f;
-#pragma unroll
-    for (int w = 0; w < WGF; ++w) {
-      sg += red[w * BT + r];
-      sr += red[(WGF + w) * BT + r];
-    }
-    const float rr = a.row_r[row];
-    float* pp = a.part + int64_t(row) * a.ldpart + 2 * (tile.ocol0 / BF);
-    pp[0] = sg;
-    pp[1] = rr > 0.f ? sr / rr : 0.f;
   }
 }
 
@@ -288,9 +180,9 @@ __global__ void __launch_bounds__(64 * WGF * WGT, MINB) k_gemm_bf16_dma(GemmArgs
     const uint16_t* g;
     if (sg < SEGW) {
       row = sg * RSEG + srow;
-      // a partial feature tile (backward of the second linear) reads its last
-      // existing weight row in place of the missing ones
-      const int wr = (EPI == EPI_BWD_ACT || EPI == EPI_BWD_SWIGLU) ? min(row, tile.spare - 1) : row;
+      // a partial feature tile (EPI_STORE_T) reads its last existing weight
+      // row in place of the missing ones
+      const int wr = EPI == EPI_STORE_T ? min(row, tile.spare - 1) : row;
       g = W + int64_t(tile.wrow0 + wr) * a.ldw + tile.kofs;
     } else {
       row = (sg - SEGW) * RSEG + srow;
@@ -382,12 +274,7 @@ __global__ void __launch_bounds__(64 * WGF * WGT, MINB) k_gemm_bf16_dma(GemmArgs
       }
     }
 #undef MOE_FRAGS2
-    if constexpr (EPI == EPI_BWD_ACT || EPI == EPI_BWD_SWIGLU) {
-      __shared__ float red[2 * WGF * BT];
-      gemm_epilogue_bwd<BF, BT, WGF, WGT, EPI>(a, tile, acc, wf, wt, fr, fh, red);
-    } else {
-      gemm_epilogue<BF, BT, WGF, WGT, EPI>(a, tile, acc, wf, wt, fr, fh);
-    }
+    gemm_epilogue<BF, BT, WGF, WGT, EPI>(a, tile, acc, wf, wt, fr, fh);
     return;
   }
 #pragma unroll
@@ -435,8 +322,7 @@ __global__ void __launch_bounds__(64 * WGF * WGT, MINB) k_gemm_bf16_dma(GemmArgs
     }
 #undef MOE_FRAGS
   }
-  if constexpr (EPI != EPI_BWD_ACT && EPI != EPI_BWD_SWIGLU)
-    gemm_epilogue<BF, BT, WGF, WGT, EPI>(a, tile, acc, wf, wt, fr, fh);
+  gemm_epilogue<BF, BT, WGF, WGT, EPI>(a, tile, acc, wf, wt, fr, fh);
 }
 
 // ---------------------------------------------------------------- fp32 SIMT GEMM
@@ -746,8 +632,7 @@ hipError_t launch_gemm(int dtype, const GemmArgs& a, int bf, int bt, int grid, h
       case EPI_GATE: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_GATE>), g, b8, 0, s, a); break;
       case EPI_SCALE_F32: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_SCALE_F32>), g, b8, 0, s, a); break;
       case EPI_GATE_SPLIT: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_GATE_SPLIT>), g, b8, 0, s, a); break;
-      case EPI_BWD_ACT: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_BWD_ACT>), g, b8, 0, s, a); break;
-      case EPI_BWD_SWIGLU: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_BWD_SWIGLU>), g, b8, 0, s, a); break;
+      case EPI_STORE_T: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_STORE_T>), g, b8, 0, s, a); break;
       default: return hipErrorInvalidValue;
     }
   } else {

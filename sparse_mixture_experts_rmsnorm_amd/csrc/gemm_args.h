@@ -20,12 +20,13 @@ struct Tile {
 };
 
 // EPI_GATE_SPLIT: gated partial of one K split, written to Y + split * ysplit.
-// EPI_BWD_ACT / EPI_BWD_SWIGLU: the backward of the second linear (see
-// GemmArgs.pre / hsav / part).  EPI_SCALE_F32 with row_r NULL stores the
-// plain fp32 accumulator (the weight-gradient GEMMs).
+// EPI_STORE_T: the plain accumulator in bf16 over a tile whose last
+// features may be missing (tile.spare = the features that exist, a multiple
+// of 32; the backward of the second linear).  EPI_SCALE_F32 with row_r NULL
+// stores the plain fp32 accumulator (the weight-gradient GEMMs).
 enum Epi {
   EPI_ACT = 0, EPI_SWIGLU = 1, EPI_GATE = 2, EPI_SCALE_F32 = 3, EPI_GATE_SPLIT = 4,
-  EPI_BWD_ACT = 5, EPI_BWD_SWIGLU = 6
+  EPI_STORE_T = 5
 };
 
 struct GemmArgs {
@@ -42,15 +43,8 @@ struct GemmArgs {
                                    // its result is never read)
   // First linear (EPI_ACT / EPI_SWIGLU): when non-NULL, the pre-activations
   // r * acc are also stored (bf16) at pre[row * ldpre + packed feature], in
-  // the expert-local packed order of the weights.  Backward of the second
-  // linear (EPI_BWD_*): acc = dout . w2^T of the row; pre holds the saved
-  // pre-activations, hsav the saved h [row * ldh + unit]; Y receives the
-  // pre-activation gradients (bf16, packed order), and part[row * ldpart +
-  // 2 * tile] the tile's sums over its units of acc * h and of
-  // (pre * dpre) / r (the gate's and the statistic's gradients).
+  // the expert-local packed order of the weights (for the backward pass).
   void* pre; int64_t ldpre;
-  const void* hsav; int64_t ldh;
-  float* part; int64_t ldpart;
 };
 
 // Plan of GEMM tiles for grouped experts.  gemm = 1: first linear (features

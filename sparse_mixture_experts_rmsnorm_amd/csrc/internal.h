@@ -105,12 +105,28 @@ struct GatherTArgs {
 };
 hipError_t launch_gather_t(const GatherTArgs& a, int max_width, int max_rows, int units,
                            hipStream_t s);
+// Activation backward over expert segments (offsets NULL: one segment of
+// dense_rows rows); foff gives each segment's hidden units (multiples of 64).
+struct ActBwdArgs {
+  const uint16_t* t; int64_t ldt;       // [rows, Fmax] dout . w2^T (ungated)
+  const uint16_t* h; int64_t ldh;       // saved h
+  const uint16_t* pre; int64_t ldpre;   // saved pre-activations (packed order)
+  const float* row_w; const float* row_r;
+  const int32_t* offsets; int dense_rows; int E;
+  const int32_t* foff; int swiglu; int act;
+  uint16_t* dpre; int64_t lddp;         // [rows, pf Fmax]
+  uint16_t* dpreT; uint16_t* hT; int64_t ldo;
+  float* part; int64_t ldpart;          // [rows, 2 ceil(Fmax / 64)]
+};
+hipError_t launch_act_bwd(const ActBwdArgs& a, int max_units, int max_rows, int units,
+                          hipStream_t s);
 // Weight-gradient tiles: X rows xmul * foff[e] .. xmul * foff[e+1] (or xfix
 // rows from 0), W rows e * wstride + [0, d), K = pad64(rows of segment e).
 struct WgradPlanArgs {
   const int32_t* offsets; int dense_rows; int E;
   const int32_t* foff; int xmul; int xfix;
   int wstride; int d;
+  int tile;                 // tile edge: 128 or 256
   Tile* tiles; int* ntiles; int max_tiles;
 };
 hipError_t launch_plan_wgrad(const WgradPlanArgs& p, hipStream_t s);
