@@ -33,6 +33,8 @@ SMALL = {
     "gelu_mxfp8_split": Workload("gelu_mxfp8_split", T=333, d=256, E=4, k=2, act="gelu",
                                  ffn=512, cf=1.0, bias="normal", shared_ffn=256,
                                  shared_act="gelu", quant="mxfp8", seed=20),
+    "mxfp8_tiny": Workload("mxfp8_tiny", T=13, d=256, E=8, k=2, act="gelu", ffn=256, cf=0.0,
+                           quant="mxfp8", seed=22),
     "atomic_small": Workload("atomic_small", T=200, d=512, E=128 * 128, k=8, act="gelu",
                              router="cartesian", Nr=128, Nc=128, expert_kind="atomic",
                              shared_ffn=512, shared_act="gelu", seed=15),

@@ -198,3 +198,45 @@ def test_backward_fullsize(name, dev):
          f"sampled weight gradients max {max(errs):.2e}")
     assert e_dx <= TOL_BWD and e_dx0 <= TOL_BWD
     assert max(errs) <= TOL_BWD
+
+
+def test_backward_empty_experts_and_tiny_batch(dev):
+    """Experts that receive no rows get exactly zero weight gradients (their
+    weight-gradient tiles have K = 0), a batch smaller than one tile works,
+    and T = 0 is a no-op."""
+    _say("[gpu] backward: empty experts, tiny batch, T = 0")
+    wl = SMALL["mixtral_small"].scaled(name="tiny_bwd", T=9, E=8, k=2, bias="normal", seed=23)
+    inp = synth.make_numpy(wl)
+    b = np.asarray(O.as_f64(inp["bias"]), dtype=np.float32) if inp.get("bias") is not None else None
+    bias = np.zeros(wl.E, dtype=np.float32) if b is None else b.copy()
+    bias[[3, 6]] = -1e4                       # never selected (k < E)
+    inp["bias"] = bias
+    params = {k: synth.to_device(v, dev) for k, v in inp.items()}
+    layer = MoELayer(wl, params, dev, train=True)
+    x = params["x"]
+    ws = layer.alloc_workspace(wl.T)
+    layer.forward(x, ws=ws)
+    rng = np.random.default_rng(5)
+    dout_np = synth._to_bf16_bits(rng.standard_normal((wl.T, wl.d)).astype(np.float32))
+    g = layer.backward(x, synth.to_device(dout_np, dev), ws)
+    torch.cuda.synchronize()
+    ids = layer.routing(wl.T, ws)["ids"].cpu().numpy()
+    assert not np.isin(ids, [3, 6]).any()
+    foff = wl.f_offsets
+    dw13 = g["dw13"].cpu().numpy()
+    dw2 = g["dw2"].cpu().numpy()
+    for e in (3, 6):
+        assert not dw13[2 * foff[e]:2 * foff[e + 1]].any()
+        assert not dw2[foff[e]:foff[e + 1]].any()
+    p = oracle_params(wl, inp)
+    ref = O.layer_backward(p, inp["x"], dout_np, ids_override=ids)
+    assert rel_err(f64(synth.to_host(g["dx"])), ref["dx"]) <= TOL_BWD
+    assert rel_err(dw13, pack_w13(ref["dw1"], ref["dw3"], wl.sizes)) <= TOL_BWD
+    assert rel_err(dw2, ref["dw2"]) <= TOL_BWD
+    # T = 0
+    x0 = x[:0]
+    ws0 = layer.alloc_workspace(0)
+    layer.forward(x0, ws=ws0)
+    g0 = layer.backward(x0, x0, ws0)
+    torch.cuda.synchronize()
+    assert g0["dx"].numel() == 0
