@@ -180,6 +180,30 @@ def time_layer(B, layer, x, out, ws, stats, steps, warmup):
     return (t1 - t0) * 1e3 / steps, stages
 
 
+def time_layer_graph(layer, x, out, ws, stats, steps):
+    """The same forward captured once in a HIP graph and replayed K times
+    (no host launch work inside the timed region)."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer.forward(x, out=out, ws=ws, stats=stats)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward(x, out=out, ws=ws, stats=stats)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    del g
+    return ms
+
+
 def expert_kept(wl, layer, ws):
     """Rows each expert computes, without padding rows."""
     rt = layer.routing(wl.T, ws)
@@ -373,6 +397,9 @@ def main():
             "note": ("combine bytes count one bf16 row per kept slot; dispatch_gather is "
                      "moe_dispatch with the row permutation into x_perm (read each token "
                      "row once, write each permuted row once) timed on the layer's ids")}
+    gms = time_layer_graph(layer, x, out, ws, stats, args.steps)
+    result["graph_replay"] = {"ms_per_step": gms, "tokens_per_s": wl.T / (gms * 1e-3),
+                              "note": "the same forward captured in one HIP graph and replayed"}
     if wl.router == "dense":
         result["router_extras"] = time_router_extras(B, wl, layer, x, out, ws, args.steps)
     if (not args.no_backward and wl.router == "dense" and wl.dtype == "bf16"
