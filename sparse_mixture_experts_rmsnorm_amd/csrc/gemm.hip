@@ -33,6 +33,7 @@
 // remapped so that each XCD (workgroup id mod 8) runs a contiguous run of
 // the list: the row tiles that share a weight tile run together in one L2.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "gemm_common.h"
@@ -164,7 +165,10 @@ __global__ void __launch_bounds__(64 * WGF * WGT, MINB) k_gemm_bf16_dma(GemmArgs
   if (int(blockIdx.x) >= nt) return;
   const Tile tile = a.tiles[remap_xcd(blockIdx.x, nt)];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wf = wid / WGT, wt = wid % WGT;
+  // waves wid and wid + 4 share a SIMD: give them the same feature rows and
+  // the two row halves, so that a tile with few rows still keeps every SIMD
+  // equally busy
+  const int wt = wid / WGF, wf = wid % WGF;
   const uint16_t* __restrict__ X = static_cast<const uint16_t*>(a.X);
   const uint16_t* __restrict__ W = static_cast<const uint16_t*>(a.W);
 
@@ -221,59 +225,74 @@ __global__ void __launch_bounds__(64 * WGF * WGT, MINB) k_gemm_bf16_dma(GemmArgs
     // that sub-step cover both the refill of the buffer just drained (stage
     // kt + 2) and the first fragment reads of stage kt + 1.
     static_assert(NS == 2 && KS % 2 == 0, "early-barrier ring is two stages of even sub-steps");
-    bf16x8 af[2][MF], bfr[2][MT];
+    // Row blocks of this wave that hold rows of the tile: a partial tile (the
+    // last rows of an expert) skips the MFMAs and fragment reads of the rest,
+    // whose results the epilogue never stores.  One copy of the loop per count
+    // keeps the inner loop free of branches.
+    const int mta = __builtin_amdgcn_readfirstlane(
+        max(0, min(MT, (tile.row_end - tile.row0 - wt * WTT + 31) / 32)));
+    auto main_loop = [&](auto mta_c) {
+      constexpr int MTA = decltype(mta_c)::value;
+      bf16x8 af[2][MF], bfr[2][MT];
 #define MOE_FRAGS2(SW, SX, KSV, SLOT)                                                          \
-    {                                                                                        \
-      const int qo_ = ((2 * (KSV) + fh) ^ fswz) * 8;                                         \
-      _Pragma("unroll") for (int i = 0; i < MF; ++i)                                         \
-        af[SLOT][i] = *reinterpret_cast<const bf16x8*>((SW) + (wf * WTF + i * 32 + fr) * BKD + qo_); \
-      _Pragma("unroll") for (int j = 0; j < MT; ++j)                                         \
-        bfr[SLOT][j] = *reinterpret_cast<const bf16x8*>((SX) + (wt * WTT + j * 32 + fr) * BKD + qo_); \
-    }
-    if (nk > 0) issue(0, 0);
-    if (nk > 1) issue(1, 1);
-    if (nk > 1) MOE_WAIT_VMCNT(SPW);
-    else MOE_WAIT_VMCNT(0);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (nk > 0) MOE_FRAGS2(lds, lds + BF * BKD, 0, 0)
-    __builtin_amdgcn_sched_barrier(0);
-    for (int kt = 0; kt < nk; ++kt) {
-      const uint16_t* sw = lds + (kt & 1) * LS;
-      const uint16_t* sx = sw + BF * BKD;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (ks + 1 < KS) {
-          MOE_FRAGS2(sw, sx, ks + 1, (ks + 1) & 1)
-        } else {
-          // the last sub-step's fragments in registers on every path, so the
-          // MFMAs below never wait for the next stage's reads
-          __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-        }
-        if (ks + 1 == KS && kt + 1 < nk) {
-          // this wave's reads of stage kt are in registers and its share of
-          // stage kt + 1 has landed; after the barrier the same holds for
-          // every wave, so buffer kt & 1 may be refilled with stage kt + 2
-          __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
-          asm volatile("" ::: "memory");
-          __builtin_amdgcn_s_barrier();
-          asm volatile("" ::: "memory");
-          if (kt + 2 < nk) issue(kt + 2, kt & 1);
-          const uint16_t* nw = lds + ((kt + 1) & 1) * LS;
-          MOE_FRAGS2(nw, nw + BF * BKD, 0, 0)
-        }
-#pragma unroll
-        for (int i = 0; i < MF; ++i)
-#pragma unroll
-          for (int j = 0; j < MT; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j],
-                                                                acc[i][j], 0, 0, 0);
-        sched_interleave<MF + MT, MF * MT>();
-        __builtin_amdgcn_sched_barrier(0);
+      {                                                                                      \
+        const int qo_ = ((2 * (KSV) + fh) ^ fswz) * 8;                                       \
+        _Pragma("unroll") for (int i = 0; i < MF; ++i)                                       \
+          af[SLOT][i] = *reinterpret_cast<const bf16x8*>((SW) + (wf * WTF + i * 32 + fr) * BKD + qo_); \
+        _Pragma("unroll") for (int j = 0; j < MTA; ++j)                                      \
+          bfr[SLOT][j] = *reinterpret_cast<const bf16x8*>((SX) + (wt * WTT + j * 32 + fr) * BKD + qo_); \
       }
-    }
+      if (nk > 0) issue(0, 0);
+      if (nk > 1) issue(1, 1);
+      if (nk > 1) MOE_WAIT_VMCNT(SPW);
+      else MOE_WAIT_VMCNT(0);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (MTA > 0 && nk > 0) MOE_FRAGS2(lds, lds + BF * BKD, 0, 0)
+      __builtin_amdgcn_sched_barrier(0);
+      for (int kt = 0; kt < nk; ++kt) {
+        const uint16_t* sw = lds + (kt & 1) * LS;
+        const uint16_t* sx = sw + BF * BKD;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          if (ks + 1 < KS) {
+            if (MTA > 0) MOE_FRAGS2(sw, sx, ks + 1, (ks + 1) & 1)
+          } else {
+            // the last sub-step's fragments in registers on every path, so the
+            // MFMAs below never wait for the next stage's reads
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+          }
+          if (ks + 1 == KS && kt + 1 < nk) {
+            // this wave's reads of stage kt are in registers and its share of
+            // stage kt + 1 has landed; after the barrier the same holds for
+            // every wave, so buffer kt & 1 may be refilled with stage kt + 2
+            __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            if (kt + 2 < nk) issue(kt + 2, kt & 1);
+            const uint16_t* nw = lds + ((kt + 1) & 1) * LS;
+            if (MTA > 0) MOE_FRAGS2(nw, nw + BF * BKD, 0, 0)
+          }
+#pragma unroll
+          for (int i = 0; i < MF; ++i)
+#pragma unroll
+            for (int j = 0; j < MTA; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j],
+                                                                  acc[i][j], 0, 0, 0);
+          if (MTA > 0) sched_interleave<MF + MTA, MF * MTA>();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
 #undef MOE_FRAGS2
+    };
+    static_assert(MT <= 4, "one loop copy per row-block count");
+    if (mta >= MT) main_loop(std::integral_constant<int, MT>{});
+    else if (mta == 3) main_loop(std::integral_constant<int, (MT > 3 ? 3 : MT)>{});
+    else if (mta == 2) main_loop(std::integral_constant<int, (MT > 2 ? 2 : MT)>{});
+    else if (mta == 1) main_loop(std::integral_constant<int, 1>{});
+    else main_loop(std::integral_constant<int, 0>{});
     gemm_epilogue<BF, BT, WGF, WGT, EPI>(a, tile, acc, wf, wt, fr, fh);
     return;
   }
