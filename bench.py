@@ -132,6 +132,42 @@ def time_dispatch_gather(B, wl, layer, ws, x, steps):
     return e0.elapsed_time(e1) / steps
 
 
+def _time_calls(run, steps):
+    """Average ms of run() over back-to-back calls between two events."""
+    import torch
+    for _ in range(2):
+        run()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def time_combine_standalone(B, wl, layer, ws, x, steps):
+    """moe_combine (one expert-output plane, residual) on the layer's slot positions."""
+    import torch
+    rt = layer.routing(wl.T, ws)
+    y = torch.randn((rt["rows_max"], wl.d), device=x.device).to(x.dtype)
+    out = torch.empty_like(x)
+    pos = rt["pos"].clone()
+    return _time_calls(lambda: B.combine(y, pos, x, None, wl.T, wl.d, wl.k, out), steps)
+
+
+def time_router_standalone(B, wl, layer, ws, x, steps):
+    """moe_router_topk alone (RMSNorm statistic, router GEMM, top-k) on x."""
+    import torch
+    dev = x.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    ids = torch.empty((wl.T, wl.k), dtype=torch.int32, device=dev)
+    w, r = torch.empty((wl.T, wl.k), **f32), torch.empty(wl.T, **f32)
+    R = layer.desc.router
+    rws = torch.empty(max(B.router_workspace_size(R, wl.T), 1), dtype=torch.uint8, device=dev)
+    return _time_calls(lambda: B.router_topk(R, x, wl.k, wl.renorm, ids, w, r_out=r, ws=rws), steps)
+
+
 def time_router_extras(B, wl, layer, x, out, ws, steps):
     """The layer with noise top-k and the routing statistics switched on
     (outside the headline figure): router stage and whole-step times."""
@@ -383,20 +419,30 @@ def main():
                               "algorithmic_flop_per_launch": f1}
         es = 4 if dtype == "f32" else 2
         rows = int(offsets[-1])
-        # combine: read every kept expert row (two K-split planes when the second
-        # GEMM is split), read x, write out; the layer's dispatch moves indices
-        # only (the first GEMM gathers token rows through row_token)
+        # Algorithmic bytes.  combine: every kept expert row, x read, out written
+        # (the layer's own combine also reads the second K-split plane of the
+        # expert outputs when the second GEMM is split).  dispatch: each token row
+        # read once and each kept row written once (moe_dispatch with x_perm; the
+        # layer's dispatch moves indices only, the first GEMM gathers the rows).
+        # router: x and the router weights read once.
         comb_bytes = (rows + 2 * wl.T) * wl.d * es
-        gather_ms = time_dispatch_gather(B, wl, layer, ws, x, args.steps)
         disp_bytes = (wl.T + rows) * wl.d * es
+        router_bytes = (wl.T + wl.E) * wl.d * es
+        gather_ms = time_dispatch_gather(B, wl, layer, ws, x, args.steps)
+        comb_ms = time_combine_standalone(B, wl, layer, ws, x, args.steps)
+        router_ms = time_router_standalone(B, wl, layer, ws, x, args.steps)
         result["memory_bound"] = {
-            "combine_GBps": comb_bytes / (stages["combine"] * 1e-3) / 1e9,
+            "combine_ms": comb_ms, "combine_GBps": comb_bytes / (comb_ms * 1e-3) / 1e9,
+            "combine_layer_stage_ms": stages["combine"],
             "dispatch_gather_ms": gather_ms,
             "dispatch_gather_GBps": disp_bytes / (gather_ms * 1e-3) / 1e9,
+            "router_ms": router_ms, "router_GBps": router_bytes / (router_ms * 1e-3) / 1e9,
             "peak_GBps": PEAK_HBM_GBPS,
-            "note": ("combine bytes count one bf16 row per kept slot; dispatch_gather is "
-                     "moe_dispatch with the row permutation into x_perm (read each token "
-                     "row once, write each permuted row once) timed on the layer's ids")}
+            "note": ("algorithmic bytes over back-to-back calls of the public entry points "
+                     "on the layer's routing: moe_combine (one kept bf16 row per slot + x + "
+                     "out), moe_dispatch with x_perm (token rows read once, kept rows written "
+                     "once; its time includes the count / scan / rank index kernels), "
+                     "moe_router_topk (x + router weights)")}
     gms = time_layer_graph(layer, x, out, ws, stats, args.steps)
     result["graph_replay"] = {"ms_per_step": gms, "tokens_per_s": wl.T / (gms * 1e-3),
                               "note": "the same forward captured in one HIP graph and replayed"}

@@ -16,23 +16,27 @@
 namespace moe {
 namespace {
 
-// One wave per token.  The token's slot positions are read once (lane j holds
-// slot j + 64 q) and broadcast slot by slot; the expert rows of four slots
-// are loaded together before they are added, so several gathers are in
-// flight.  SPLIT: each expert row is the sum of two K-split partial planes
+// One wave per token and part of the row (P parts of d / P features, so that
+// a wave's loads are few rounds deep and the whole grid has many loads in
+// flight).  The token's slot positions are read once (lane j holds slot
+// j + 64 q) and broadcast slot by slot; the expert rows of four slots are
+// loaded together before they are added, so several gathers are in flight.  SPLIT: each expert row is the sum of two K-split partial planes
 // (y0 and y0 + plane), added as (p0 + p1).  The sum starts from x itself, so
 // a token whose slots were all dropped stores x bit for bit.
 template <typename T, int SPLIT>
 __global__ void __launch_bounds__(256) k_combine(const T* __restrict__ y, int64_t plane,
                                                  const int32_t* __restrict__ pos,
                                                  const T* __restrict__ x, const T* __restrict__ sh,
-                                                 int64_t Tn, int64_t d, int k, T* __restrict__ out) {
+                                                 int64_t Tn, int64_t d, int k, int parts,
+                                                 T* __restrict__ out) {
   constexpr int N = Vec16<T>::N;
   constexpr int SB = 4;                         // slots per batch of loads
   const int lane = threadIdx.x & 63;
-  const int64_t t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t g = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t t = g / parts;
   if (t >= Tn) return;
   const int64_t nvec = d / N;
+  const int64_t vlen = nvec / parts, v0 = (g - t * parts) * vlen;
   const uint4* ys = reinterpret_cast<const uint4*>(y);
   const int64_t pv = plane / N;
   int pl[4];
@@ -42,7 +46,7 @@ __global__ void __launch_bounds__(256) k_combine(const T* __restrict__ y, int64_
     pl[q] = (pos && j < k) ? pos[t * k + j] : -1;
   }
 #pragma unroll 2
-  for (int64_t v = lane; v < nvec; v += 64) {
+  for (int64_t v = v0 + lane; v < v0 + vlen; v += 64) {
     float acc[8];
     if (x) {
       unpack16(reinterpret_cast<const uint4*>(x)[t * nvec + v], acc, (const T*)nullptr);
@@ -99,36 +103,47 @@ __global__ void __launch_bounds__(256) k_combine(const T* __restrict__ y, int64_
 
 }  // namespace
 
+// parts per token row: as many as keep every wave's share a whole number of
+// 64-lane rounds of 16-byte vectors, at most 4
+static int combine_parts(int64_t d, int dtype) {
+  const int64_t nvec = d / (dtype == 0 ? 4 : 8);
+  int p = 4;
+  while (p > 1 && nvec % (64 * p) != 0) p /= 2;
+  return p;
+}
+
 hipError_t launch_combine_split(const void* y0, int64_t rows_max, const int32_t* pos,
                                 const void* x, const void* shared, int dtype, int64_t T,
                                 int64_t d, int k, void* out, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const dim3 g(unsigned((T + 3) / 4));
+  const int parts = combine_parts(d, dtype);
+  const dim3 g(unsigned((T * parts + 3) / 4));
   if (dtype == 0)
     hipLaunchKernelGGL((k_combine<float, 1>), g, dim3(256), 0, s, static_cast<const float*>(y0),
                        rows_max * d, pos, static_cast<const float*>(x),
-                       static_cast<const float*>(shared), T, d, k, static_cast<float*>(out));
+                       static_cast<const float*>(shared), T, d, k, parts, static_cast<float*>(out));
   else
     hipLaunchKernelGGL((k_combine<uint16_t, 1>), g, dim3(256), 0, s,
                        static_cast<const uint16_t*>(y0), rows_max * d, pos,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(shared), T,
-                       d, k, static_cast<uint16_t*>(out));
+                       d, k, parts, static_cast<uint16_t*>(out));
   return hipGetLastError();
 }
 
 hipError_t launch_combine(const void* y, const int32_t* pos, const void* x, const void* shared,
                           int dtype, int64_t T, int64_t d, int k, void* out, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const dim3 g(unsigned((T + 3) / 4));
+  const int parts = combine_parts(d, dtype);
+  const dim3 g(unsigned((T * parts + 3) / 4));
   if (dtype == 0)
     hipLaunchKernelGGL((k_combine<float, 0>), g, dim3(256), 0, s, static_cast<const float*>(y),
                        int64_t(0), pos, static_cast<const float*>(x),
-                       static_cast<const float*>(shared), T, d, k, static_cast<float*>(out));
+                       static_cast<const float*>(shared), T, d, k, parts, static_cast<float*>(out));
   else
     hipLaunchKernelGGL((k_combine<uint16_t, 0>), g, dim3(256), 0, s,
                        static_cast<const uint16_t*>(y), int64_t(0), pos,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(shared), T,
-                       d, k, static_cast<uint16_t*>(out));
+                       d, k, parts, static_cast<uint16_t*>(out));
   return hipGetLastError();
 }
 

@@ -296,10 +296,13 @@ __device__ void write_gates(const float (&sv)[QS], const int (&si)[QS], const fl
 
 constexpr int kRouterTok = 16;  // tokens per workgroup (one 16-wide MFMA block)
 
-// Workgroup: 4 waves split K; each wave runs 16x16x32 MFMAs with the router
-// rows as the A operand (16 experts per block) and 16 token rows as B.
-template <int NB>
-__global__ void __launch_bounds__(256) k_router_bf16(
+// Workgroup: NW waves split K; each wave runs 16x16x32 MFMAs with the router
+// rows as the A operand (16 experts per block) and 16 token rows as B.  More
+// waves per workgroup keep fewer loads outstanding per wave and more per CU
+// (the token rows are read once, so the kernel is bound by how many loads
+// are in flight).
+template <int NB, int NW>
+__global__ void __launch_bounds__(64 * NW) k_router_bf16(
     const uint16_t* __restrict__ x, int T, int d, const uint16_t* __restrict__ wr,
     const float* __restrict__ bias, int E, const float* __restrict__ r_in, float eps,
     float* __restrict__ r_out, int k, int renorm, int32_t* __restrict__ ids,
@@ -308,12 +311,13 @@ __global__ void __launch_bounds__(256) k_router_bf16(
   __shared__ float lg[kRouterTok][NB * 16 + 1];
   __shared__ float ssq[kRouterTok];
   __shared__ float rs[kRouterTok];
-  __shared__ uint32_t cand_s[4][64];
-  __shared__ float selv_s[4][64];
-  __shared__ int seli_s[4][64];
-  __shared__ float pacc_s[4][NB * 16];
-  __shared__ float gacc_s[4][NB * 16];
-  __shared__ int cacc_s[4][NB * 16];
+  __shared__ uint32_t cand_s[NW][64];
+  __shared__ float selv_s[NW][64];
+  __shared__ int seli_s[NW][64];
+  __shared__ float pacc_s[NW][NB * 16];
+  __shared__ float gacc_s[NW][NB * 16];
+  __shared__ int cacc_s[NW][NB * 16];
+  static_assert(kRouterTok % NW == 0, "whole tokens per wave in the epilogue");
   const bool stats = ex.part_p != nullptr;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int t0 = blockIdx.x * kRouterTok;
@@ -321,7 +325,7 @@ __global__ void __launch_bounds__(256) k_router_bf16(
   const int kg = lane >> 4;       // which 8-element K group
   const int t = t0 + tl;
   const bool tok_ok = t < T;
-  const int kw = d / 4;           // K range of this wave
+  const int kw = d / NW;          // K range of this wave
   const int kb = wid * kw;
   if (stats)
     for (int e = lane; e < NB * 16; e += 64) {
@@ -361,8 +365,8 @@ __global__ void __launch_bounds__(256) k_router_bf16(
   // sum of squares of the token over this wave's K range (lanes tl, tl+16, ...)
   ss += __shfl_xor(ss, 16, 64);
   ss += __shfl_xor(ss, 32, 64);
-  // ordered cross-wave reduction (wave 0, then 1, 2, 3): deterministic
-  for (int w = 0; w < 4; ++w) {
+  // ordered cross-wave reduction (wave 0, then 1, 2, ...): deterministic
+  for (int w = 0; w < NW; ++w) {
     if (wid == w) {
 #pragma unroll
       for (int b = 0; b < NB; ++b)
@@ -389,9 +393,9 @@ __global__ void __launch_bounds__(256) k_router_bf16(
     rs[threadIdx.x] = rr;
   }
   __syncthreads();
-  // epilogue: r-scale + bias, then top-k per token (each wave: 4 tokens)
-  for (int q = 0; q < kRouterTok / 4; ++q) {
-    const int tl2 = wid * (kRouterTok / 4) + q;
+  // epilogue: r-scale + bias, then top-k per token (each wave: 16 / NW tokens)
+  for (int q = 0; q < kRouterTok / NW; ++q) {
+    const int tl2 = wid * (kRouterTok / NW) + q;
     const int tt = t0 + tl2;
     if (tt >= T) break;
     const float rr = rs[tl2];
@@ -421,12 +425,18 @@ __global__ void __launch_bounds__(256) k_router_bf16(
   if (stats) {
     // the workgroup's partial sums: waves combined in a fixed order
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += 256) {
-      ex.part_p[int64_t(blockIdx.x) * E + e] =
-          ((pacc_s[0][e] + pacc_s[1][e]) + pacc_s[2][e]) + pacc_s[3][e];
-      ex.part_g[int64_t(blockIdx.x) * E + e] =
-          ((gacc_s[0][e] + gacc_s[1][e]) + gacc_s[2][e]) + gacc_s[3][e];
-      ex.part_c[int64_t(blockIdx.x) * E + e] = cacc_s[0][e] + cacc_s[1][e] + cacc_s[2][e] + cacc_s[3][e];
+    for (int e = threadIdx.x; e < E; e += 64 * NW) {
+      float sp = 0.f, sg = 0.f;
+      int sc = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        sp += pacc_s[w][e];
+        sg += gacc_s[w][e];
+        sc += cacc_s[w][e];
+      }
+      ex.part_p[int64_t(blockIdx.x) * E + e] = sp;
+      ex.part_g[int64_t(blockIdx.x) * E + e] = sg;
+      ex.part_c[int64_t(blockIdx.x) * E + e] = sc;
     }
   }
 }
@@ -497,11 +507,17 @@ __global__ void __launch_bounds__(256) k_topk_rows(float* __restrict__ lg, int T
   if (stats) {
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += 256) {
-      ex.part_p[int64_t(blockIdx.x) * E + e] =
-          ((pacc_s[0][e] + pacc_s[1][e]) + pacc_s[2][e]) + pacc_s[3][e];
-      ex.part_g[int64_t(blockIdx.x) * E + e] =
-          ((gacc_s[0][e] + gacc_s[1][e]) + gacc_s[2][e]) + gacc_s[3][e];
-      ex.part_c[int64_t(blockIdx.x) * E + e] = cacc_s[0][e] + cacc_s[1][e] + cacc_s[2][e] + cacc_s[3][e];
+      float sp = 0.f, sg = 0.f;
+      int sc = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        sp += pacc_s[w][e];
+        sg += gacc_s[w][e];
+        sc += cacc_s[w][e];
+      }
+      ex.part_p[int64_t(blockIdx.x) * E + e] = sp;
+      ex.part_g[int64_t(blockIdx.x) * E + e] = sg;
+      ex.part_c[int64_t(blockIdx.x) * E + e] = sc;
     }
   }
 }
@@ -769,15 +785,27 @@ hipError_t launch_router_dense(const void* x, int dtype, int64_t T, int64_t d, c
   } else {
     const dim3 g(unsigned((T + kRouterTok - 1) / kRouterTok));
     const int nb = int((E + 15) / 16);
-#define MOE_ROUTER_CASE(NBV)                                                                   \
-    hipLaunchKernelGGL(k_router_bf16<NBV>, g, dim3(256), 0, s, static_cast<const uint16_t*>(x),   \
-                       int(T), int(d), static_cast<const uint16_t*>(wr_t), bias, int(E), r_in,     \
-                       eps, r_out, k, renorm, ids, w, logits, ex)
-    if (nb <= 1) MOE_ROUTER_CASE(1);
-    else if (nb <= 2) MOE_ROUTER_CASE(2);
-    else if (nb <= 4) MOE_ROUTER_CASE(4);
-    else if (nb <= 8) MOE_ROUTER_CASE(8);
-    else MOE_ROUTER_CASE(16);
+    // waves per workgroup: each wave's K range a multiple of 32
+    const int nw = d % (16 * 32) == 0 ? 16 : d % (8 * 32) == 0 ? 8 : 4;
+#define MOE_ROUTER_CASE(NBV, NWV)                                                              \
+    hipLaunchKernelGGL((k_router_bf16<NBV, NWV>), g, dim3(64 * NWV), 0, s,                       \
+                       static_cast<const uint16_t*>(x), int(T), int(d),                         \
+                       static_cast<const uint16_t*>(wr_t), bias, int(E), r_in, eps, r_out, k,   \
+                       renorm, ids, w, logits, ex)
+#define MOE_ROUTER_NB(NWV)                                                                     \
+    if (nb <= 1) MOE_ROUTER_CASE(1, NWV);                                                      \
+    else if (nb <= 2) MOE_ROUTER_CASE(2, NWV);                                                 \
+    else if (nb <= 4) MOE_ROUTER_CASE(4, NWV);                                                 \
+    else if (nb <= 8) MOE_ROUTER_CASE(8, NWV);                                                 \
+    else MOE_ROUTER_CASE(16, NWV);
+    if (nw == 16) {
+      MOE_ROUTER_NB(16)
+    } else if (nw == 8) {
+      MOE_ROUTER_NB(8)
+    } else {
+      MOE_ROUTER_NB(4)
+    }
+#undef MOE_ROUTER_NB
 #undef MOE_ROUTER_CASE
   }
   if (ex.part_p) {

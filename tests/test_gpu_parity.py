@@ -574,3 +574,32 @@ def test_pack_mxfp8_bit_exact(dev):
     assert np.array_equal(c2[:, :K].cpu().numpy(), c_ref)
     assert np.array_equal(s2[:, :K // 32].cpu().numpy(), s_ref)
     assert not c2[:, K:].any() and not s2[:, K // 32:].any()
+
+
+@pytest.mark.parametrize("d,T", [(384, 77), (256, 300), (1536, 40), (4096, 33)])
+def test_dense_router_k_splits(dev, d, T):
+    """bf16 router with each workgroup shape (the K range of d split over 4,
+    8 or 16 waves, chosen by d): r, logits, ids and gates against the oracle
+    on the same bf16 inputs, with a token count that leaves a partial block."""
+    _say(f"[gpu] dense bf16 router d={d} T={T}")
+    E, k = 24, 3
+    R, keep, rng, tdt = _dense_router(dev, E, d, "bf16", 7000 + d)
+    xb = torch.from_numpy(rng.standard_normal((T, d)).astype(np.float32)).to(dev).to(tdt)
+    bias = torch.from_numpy(rng.standard_normal(E).astype(np.float32) * 0.1).to(dev)
+    R.bias = bias.data_ptr()
+    f32 = dict(dtype=torch.float32, device=dev)
+    logits, w, r = torch.empty((T, E), **f32), torch.empty((T, k), **f32), torch.empty(T, **f32)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(B.router_workspace_size(R, T), 1), dtype=torch.uint8, device=dev)
+    B.router_topk(R, xb, k, 1, ids, w, r_out=r, logits=logits, ws=ws, eps=1e-6)
+    torch.cuda.synchronize()
+    x64 = xb.float().cpu().numpy().astype(np.float64)
+    wr64 = keep.float().cpu().numpy().astype(np.float64).T          # [d, E]
+    r_ref = O.rmsnorm_scale(x64, 1e-6)
+    assert rel_err(r.cpu().numpy(), r_ref) < 1e-5
+    lg = logits.cpu().numpy()
+    ref = O.router_logits(x64, None, r_ref, wr64, bias.cpu().numpy())
+    assert np.abs(lg - ref).max() < 1e-4 * np.abs(ref).max() + 1e-6
+    got_ids = ids.cpu().numpy()
+    assert np.array_equal(got_ids, O.select_topk(lg, k))
+    assert rel_err(w.cpu().numpy(), O.gates(lg.astype(np.float64), got_ids, 1)) < 1e-5
