@@ -164,7 +164,9 @@ __global__ void __launch_bounds__(64 * WGF * WGT, MINB) k_gemm_bf16_dma(GemmArgs
   const int nt = *a.ntiles;
   if (int(blockIdx.x) >= nt) return;
   const Tile tile = a.tiles[remap_xcd(blockIdx.x, nt)];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave-uniform (the LDS destinations of the DMA are then scalar arithmetic)
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   // waves wid and wid + 4 share a SIMD: give them the same feature rows and
   // the two row halves, so that a tile with few rows still keeps every SIMD
   // equally busy
@@ -242,49 +244,79 @@ __global__ void __launch_bounds__(64 * WGF * WGT, MINB) k_gemm_bf16_dma(GemmArgs
         _Pragma("unroll") for (int j = 0; j < MTA; ++j)                                      \
           bfr[SLOT][j] = *reinterpret_cast<const bf16x8*>((SX) + (wt * WTT + j * 32 + fr) * BKD + qo_); \
       }
-      if (nk > 0) issue(0, 0);
-      if (nk > 1) issue(1, 1);
-      if (nk > 1) MOE_WAIT_VMCNT(SPW);
-      else MOE_WAIT_VMCNT(0);
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      if (MTA > 0 && nk > 0) MOE_FRAGS2(lds, lds + BF * BKD, 0, 0)
-      __builtin_amdgcn_sched_barrier(0);
-      for (int kt = 0; kt < nk; ++kt) {
-        const uint16_t* sw = lds + (kt & 1) * LS;
-        const uint16_t* sx = sw + BF * BKD;
+#define MOE_MFMAS2(KSV)                                                                       \
+      _Pragma("unroll") for (int i = 0; i < MF; ++i)                                          \
+        _Pragma("unroll") for (int j = 0; j < MTA; ++j)                                       \
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[(KSV) & 1][i], bfr[(KSV) & 1][j], \
+                                                              acc[i][j], 0, 0, 0);
+      if (nk > 0) {
+        issue(0, 0);
+        if (nk > 1) issue(1, 1);
+        if (nk > 1) MOE_WAIT_VMCNT(SPW);
+        else MOE_WAIT_VMCNT(0);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (MTA > 0) MOE_FRAGS2(lds, lds + BF * BKD, 0, 0)
+        __builtin_amdgcn_sched_barrier(0);
+        // Every stage but the last.  The body has no branch, so the refill DMA
+        // and the next stage's first fragment reads are scheduled between the
+        // last sub-step's MFMAs: past the last stage the refill repeats stage
+        // nk - 1, in bounds, into the buffer just drained, which is not read
+        // again (the DMA queue is drained before the workgroup exits).
+        for (int kt = 0; kt + 1 < nk; ++kt) {
+          const uint16_t* sw = lds + (kt & 1) * LS;
+          const uint16_t* sx = sw + BF * BKD;
+          const int knext = min(kt + 2, nk - 1);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          if (ks + 1 < KS) {
-            if (MTA > 0) MOE_FRAGS2(sw, sx, ks + 1, (ks + 1) & 1)
-          } else {
-            // the last sub-step's fragments in registers on every path, so the
-            // MFMAs below never wait for the next stage's reads
-            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+          for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 1 < KS) {
+              if (MTA > 0) MOE_FRAGS2(sw, sx, ks + 1, (ks + 1) & 1)
+              MOE_MFMAS2(ks)
+              if (MTA > 0) sched_interleave<MF + MTA, MF * MTA>();
+            } else {
+              // this wave's reads of stage kt are in registers and its share
+              // of stage kt + 1 has landed; after the barrier the same holds
+              // for every wave, so buffer kt & 1 may be refilled
+              __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+              asm volatile("" ::: "memory");
+              __builtin_amdgcn_s_barrier();
+              asm volatile("" ::: "memory");
+              // the next stage's first fragment reads under the first row of
+              // MFMAs, then the refill DMA under the rest
+              const uint16_t* nw = lds + ((kt + 1) & 1) * LS;
+              if (MTA > 0) MOE_FRAGS2(nw, nw + BF * BKD, 0, 0)
+#pragma unroll
+              for (int j = 0; j < MTA; ++j)
+                acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][0], bfr[ks & 1][j],
+                                                                    acc[0][j], 0, 0, 0);
+              if (MTA > 0) sched_interleave<MF + MTA, MTA>();
+              __builtin_amdgcn_sched_barrier(0);
+              issue(knext, kt & 1);
+#pragma unroll
+              for (int i = 1; i < MF; ++i)
+#pragma unroll
+                for (int j = 0; j < MTA; ++j)
+                  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j],
+                                                                      acc[i][j], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
           }
-          if (ks + 1 == KS && kt + 1 < nk) {
-            // this wave's reads of stage kt are in registers and its share of
-            // stage kt + 1 has landed; after the barrier the same holds for
-            // every wave, so buffer kt & 1 may be refilled with stage kt + 2
-            __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_s_barrier();
-            asm volatile("" ::: "memory");
-            if (kt + 2 < nk) issue(kt + 2, kt & 1);
-            const uint16_t* nw = lds + ((kt + 1) & 1) * LS;
-            if (MTA > 0) MOE_FRAGS2(nw, nw + BF * BKD, 0, 0)
-          }
-#pragma unroll
-          for (int i = 0; i < MF; ++i)
-#pragma unroll
-            for (int j = 0; j < MTA; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j],
-                                                                  acc[i][j], 0, 0, 0);
-          if (MTA > 0) sched_interleave<MF + MTA, MF * MTA>();
-          __builtin_amdgcn_sched_barrier(0);
         }
+        {
+          const uint16_t* sw = lds + ((nk - 1) & 1) * LS;
+          const uint16_t* sx = sw + BF * BKD;
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 1 < KS && MTA > 0) MOE_FRAGS2(sw, sx, ks + 1, (ks + 1) & 1)
+            MOE_MFMAS2(ks)
+            if (ks + 1 < KS && MTA > 0) sched_interleave<MF + MTA, MF * MTA>();
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        MOE_WAIT_VMCNT(0);
       }
+#undef MOE_MFMAS2
 #undef MOE_FRAGS2
     };
     static_assert(MT <= 4, "one loop copy per row-block count");
