@@ -76,7 +76,8 @@ struct ExpertGeo {
   int fold = 1;        // first-linear output columns = packed features / fold
   bool bcsr = false, atomic = false;
   bool mx = false;     // MXFP8 operands (E4M3 codes + E8M0 block scales)
-  bool mx_split = false;   // every ffn size a multiple of 256: K halves stay whole stages
+  int kdiv = 1;        // largest second-linear K split (1, 2 or 4) whose parts are
+                       // whole K stages of every expert
 };
 
 int check_experts(const moe_experts_desc* X, int dtype, int64_t d, ExpertGeo* g) {
@@ -140,16 +141,20 @@ int check_experts(const moe_experts_desc* X, int dtype, int64_t d, ExpertGeo* g)
             "MXFP8 experts are implemented for bf16 grouped experts");
     REQUIRE(X->w13_scale && X->w2_scale, MOE_EINVAL, "MXFP8 experts need w13_scale and w2_scale");
     geo.mx = true;
-    geo.mx_split = true;
-    for (int64_t e = 0; e < X->E; ++e) {
+    for (int64_t e = 0; e < X->E; ++e)
       REQUIRE(X->ffn_sizes[e] % 128 == 0, MOE_ESHAPE,
               "MXFP8 ffn sizes must be multiples of 128 (expert %lld: %lld)", (long long)e,
               (long long)X->ffn_sizes[e]);
-      geo.mx_split = geo.mx_split && X->ffn_sizes[e] % 256 == 0;
-    }
     // the kernels address operands with 32-bit byte offsets
     REQUIRE(geo.F * geo.pf * d < (int64_t(1) << 31) && geo.F * d < (int64_t(1) << 31), MOE_ESHAPE,
             "MXFP8 weights must stay below 2 GiB per matrix");
+  }
+  // K stage of the second linear: 64 elements (bf16), 128 (MXFP8)
+  const int64_t kstage = geo.mx ? 128 : 64;
+  for (int div = 4; div >= 2 && geo.kdiv == 1; div /= 2) {
+    bool whole = true;
+    for (int64_t e = 0; e < X->E; ++e) whole = whole && X->ffn_sizes[e] % (div * kstage) == 0;
+    if (whole) geo.kdiv = div;
   }
   if (geo.bcsr) {
     REQUIRE(X->block == 128, MOE_EUNSUPPORTED, "BCSR block must be 128 (got %d)", X->block);
@@ -228,14 +233,27 @@ void fit_dense_tiles(ExpertGeo* g, int dtype, int64_t d, int64_t T) {
 
 // Second-linear K split: the tile count of a grouped layer is only known on
 // the device, so the host estimates it (T k / bt + E / 2 row tiles per output
-// slice) and splits K in two when that evens out the last round of tiles
-// across the compute units (the two fp32 partials are summed by combine).
+// slice) and models the time of split s in units of one full-K tile: the
+// rounds of tiles over the compute units, each 1 / s of a tile, plus a fixed
+// cost per round (a tile's prologue and epilogue) and per extra partial plane
+// (written by the GEMM, read by combine).  Splits of 1, 2 or 4 whose parts are
+// whole K stages of every expert are considered.
 int choose_ksplit(const ExpertGeo& g, int dtype, int64_t d, int64_t rows_used_est) {
-  if (g.bcsr || g.atomic || dtype != MOE_BF16 || (g.mx && !g.mx_split)) return 1;
+  if (g.bcsr || g.atomic || dtype != MOE_BF16 || g.kdiv < 2) return 1;
+  constexpr double kRoundCost = 0.017, kPlaneCost = 0.031;
   const double cus = device_cus();
   const double n = (double(rows_used_est) / g.bt + 0.5 * double(g.E)) * double(d / g.bf2);
-  auto eff = [&](double t) { return t <= 0 ? 1.0 : (t / cus) / std::ceil(t / cus); };
-  return eff(2 * n) > eff(n) + 0.08 ? 2 : 1;
+  int best = 1;
+  double best_t = 0;
+  for (int s = 1; s <= g.kdiv; s *= 2) {
+    const double rounds = std::ceil(s * n / cus);
+    const double t = rounds / s + kRoundCost * rounds + kPlaneCost * (s - 1);
+    if (s == 1 || t < best_t) {
+      best = s;
+      best_t = t;
+    }
+  }
+  return best;
 }
 
 void carve_expert_ws(Carve& c, const ExpertGeo& g, int dtype, int64_t d, int64_t rows_max,
@@ -1179,8 +1197,8 @@ int moe_layer_forward(const moe_layer_desc* L, const void* x, int64_t T, void* o
 
   // 5. combine
   if (w.ex.ksplit > 1)
-    MOE_HIP(launch_combine_split(w.ex.ypart, w.rows_max, w.pos, L->residual ? x : nullptr, w.s,
-                                 L->dtype, T, d, k, out, stream));
+    MOE_HIP(launch_combine_split(w.ex.ypart, w.ex.ksplit, w.rows_max, w.pos,
+                                 L->residual ? x : nullptr, w.s, L->dtype, T, d, k, out, stream));
   else
     MOE_HIP(launch_combine(w.y, g.atomic ? nullptr : w.pos, L->residual ? x : nullptr, w.s,
                            L->dtype, T, d, k, out, stream));

@@ -67,10 +67,11 @@ hipError_t launch_topology(const int32_t* offsets, const int32_t* size_blocks,
 
 hipError_t launch_combine(const void* y, const int32_t* pos, const void* x, const void* shared,
                           int dtype, int64_t T, int64_t d, int k, void* out, hipStream_t s);
-// Combine over the two K-split partial planes (y0, y0 + rows_max * d), dtype.
-hipError_t launch_combine_split(const void* y0, int64_t rows_max, const int32_t* pos, const void* x,
-                                const void* shared, int dtype, int64_t T, int64_t d, int k,
-                                void* out, hipStream_t s);
+// Combine over nplanes (2 or 4) K-split partial planes y0 + p * rows_max * d,
+// dtype; each slot's row is the sum of its planes in plane order.
+hipError_t launch_combine_split(const void* y0, int nplanes, int64_t rows_max, const int32_t* pos,
+                                const void* x, const void* shared, int dtype, int64_t T, int64_t d,
+                                int k, void* out, hipStream_t s);
 
 struct AtomicArgs {
   const void* xhat; int dtype; int64_t T, d; int k; int64_t N;
