@@ -23,9 +23,9 @@
 // Tiling for gfx950: a 256 x 256 output tile per workgroup of 8 wave64s (a
 // 4 x 2 grid of 64 x 128 wave tiles; 128-row BCSR blocks use 4 waves).
 // Operands are both K-contiguous (weights packed as [features, K]) and move
-// global -> LDS by the global_load_lds_dwordx4 DMA into a double-buffered
-// ring with a 16-byte-chunk XOR swizzle (conflict-free for the 64-bank LDS),
-// so no registers are spent on staging.  v_mfma_f32_32x32x16_bf16 takes the
+// global -> LDS by the global_load_lds_dwordx4 DMA into LDS rings (three
+// stages of weights, two of activations) with a 16-byte-chunk XOR swizzle
+// (conflict-free for the 64-bank LDS), so no registers are spent on staging.  v_mfma_f32_32x32x16_bf16 takes the
 // weights as the A operand (features = MFMA rows) and tokens as B (MFMA
 // columns), so a lane's accumulators hold four consecutive features of one
 // token and the epilogue stores 8 bytes per group.  Fragments of the next
@@ -139,27 +139,35 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const Tile& til
 // ---------------------------------------------------------------- bf16 MFMA GEMM, LDS-DMA ring
 
 // BF features x BT rows per workgroup, WGF x WGT waves, each wave a
-// (BF / WGF) x (BT / WGT) sub-tile of 32 x 32 MFMA blocks.  Global -> LDS
-// moves by the global_load_lds_dwordx4 DMA (each wave instruction writes
-// 1 KB of LDS, lane i at byte 16 i) through a ring of NS LDS stages of BKD
-// columns.  EARLY (two stages) places the one barrier per stage before its
-// last K sub-step; otherwise stages kt + 1 .. kt + NS - 1 are in flight while
-// stage kt is computed and the barrier opens each stage.
-template <int BF, int BT, int WGF, int WGT, int BKD, int NS, int EPI, bool EARLY = true, int MINB = 1>
-__global__ void __launch_bounds__(64 * WGF * WGT, MINB) k_gemm_bf16_dma(GemmArgs a) {
+// (BF / WGF) x (BT / WGT) sub-tile of 32 x 32 MFMA blocks, K in stages of 64.
+// Global -> LDS moves by the global_load_lds_dwordx4 DMA (each wave
+// instruction writes 1 KB of LDS, lane i at byte 16 i).  The weights go
+// through a ring of three LDS stages and the activation rows through two
+// (3 x 32 KB + 2 x 32 KB = the whole 160 KB of a CU at 256 x 256): the
+// weights stream from HBM and get two stages of lookahead, the activation
+// rows (L2-resident) one.  Every wave moves its share of both operands, the
+// activation segments first, so at a barrier vmcnt(weight segments) leaves
+// only the newest weight stage in flight.  One barrier per stage, before its
+// last K sub-step: by then every wave holds that sub-step's fragments, so
+// behind the barrier its MFMAs cover the next stage's first fragment reads
+// and the refill of the two buffers just drained.
+template <int BF, int BT, int WGF, int WGT, int EPI>
+__global__ void __launch_bounds__(64 * WGF * WGT, 1) k_gemm_bf16_dma(GemmArgs a) {
   constexpr int NW = WGF * WGT;
   constexpr int WTF = BF / WGF, WTT = BT / WGT;
   constexpr int MF = WTF / 32, MT = WTT / 32;
+  constexpr int BKD = 64;                       // K per stage
   constexpr int C = BKD / 8;                    // 16-byte chunks per LDS row
   constexpr int RSEG = 64 / C;                  // rows per 1 KB DMA segment
-  constexpr int SEGW = BF / RSEG, SEGX = BT / RSEG;
-  constexpr int SPW = (SEGW + SEGX) / NW;       // DMA instructions per wave per stage
-  constexpr int LS = (BF + BT) * BKD;           // elements per stage
-  static_assert((SEGW + SEGX) % NW == 0, "segments must divide among waves");
-  static_assert(MF >= 1 && MT >= 1, "tile too small for the waves");
+  constexpr int SPW = BF / RSEG / NW;           // weight segments per wave per stage
+  constexpr int SPX = BT / RSEG / NW;           // activation segments per wave per stage
+  constexpr int WS = BF * BKD, XS = BT * BKD;   // elements per stage buffer
+  constexpr int KS = BKD / 16;                  // MFMA sub-steps per stage
+  static_assert(SPW * RSEG * NW == BF && SPX * RSEG * NW == BT, "segments must divide among waves");
+  static_assert(MF >= 1 && MT >= 1 && MT <= 4, "wave tile of 1..4 row blocks");
   static_assert(EPI != EPI_SWIGLU || MF % 2 == 0, "SwiGLU needs gate/up block pairs per wave");
-  static_assert(BKD == 32 || BKD == 64, "BKD must be 32 or 64");
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * LS];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[3 * WS + 2 * XS];
+  uint16_t* const ldsx = lds + 3 * WS;
 
   const int nt = *a.ntiles;
   if (int(blockIdx.x) >= nt) return;
@@ -178,35 +186,40 @@ __global__ void __launch_bounds__(64 * WGF * WGT, MINB) k_gemm_bf16_dma(GemmArgs
   // invariant; a K step only adds kt * BKD)
   const int srow = lane / C;                  // row within a segment
   const int xlast = tile.row_end - 1;
-  const uint16_t* src[SPW];
+  // a K-split tile reads its own part of the activation row
+  const int xk0 = (EPI == EPI_GATE_SPLIT || EPI == EPI_SCALE_F32) ? tile.spare * tile.klen : 0;
+  const uint16_t* srcw[SPW];
+  const uint16_t* srcx[SPX];
 #pragma unroll
   for (int u = 0; u < SPW; ++u) {
-    const int sg = wid * SPW + u;             // wave-uniform segment index
-    int row;
-    const uint16_t* g;
-    if (sg < SEGW) {
-      row = sg * RSEG + srow;
-      // a partial feature tile (EPI_STORE_T) reads its last existing weight
-      // row in place of the missing ones
-      const int wr = EPI == EPI_STORE_T ? min(row, tile.spare - 1) : row;
-      g = W + int64_t(tile.wrow0 + wr) * a.ldw + tile.kofs;
-    } else {
-      row = (sg - SEGW) * RSEG + srow;
-      // a K-split tile reads its own half of the activation row; with a row
-      // map the rows are gathered from the token rows (dispatch fused here)
-      const int xk0 = (EPI == EPI_GATE_SPLIT || EPI == EPI_SCALE_F32) ? tile.spare * tile.klen : 0;
-      int xr = min(tile.row0 + row, xlast);
-      if (a.xrow) xr = max(a.xrow[xr], 0);
-      g = X + int64_t(xr) * a.ldx + xk0;
-    }
-    src[u] = g + ((lane % C) ^ chunk_swz<C>(row)) * 8;
+    const int row = (wid * SPW + u) * RSEG + srow;
+    // a partial feature tile (EPI_STORE_T) reads its last existing weight
+    // row in place of the missing ones
+    const int wr = EPI == EPI_STORE_T ? min(row, tile.spare - 1) : row;
+    srcw[u] = W + int64_t(tile.wrow0 + wr) * a.ldw + tile.kofs + ((lane % C) ^ chunk_swz<C>(row)) * 8;
   }
-  auto issue = [&](int kt, int stage) {
-    uint16_t* base = lds + stage * LS;
+#pragma unroll
+  for (int u = 0; u < SPX; ++u) {
+    const int row = (wid * SPX + u) * RSEG + srow;
+    // with a row map the rows are gathered from the token rows (dispatch
+    // fused here)
+    int xr = min(tile.row0 + row, xlast);
+    if (a.xrow) xr = max(a.xrow[xr], 0);
+    srcx[u] = X + int64_t(xr) * a.ldx + xk0 + ((lane % C) ^ chunk_swz<C>(row)) * 8;
+  }
+  auto issue_w = [&](int kt, int buf) {
+    uint16_t* base = lds + buf * WS;
 #pragma unroll
     for (int u = 0; u < SPW; ++u)
-      __builtin_amdgcn_global_load_lds((global_void_ptr)(src[u] + kt * BKD),
+      __builtin_amdgcn_global_load_lds((global_void_ptr)(srcw[u] + kt * BKD),
                                        (lds_void_ptr)(base + (wid * SPW + u) * 512), 16, 0, 0);
+  };
+  auto issue_x = [&](int kt, int buf) {
+    uint16_t* base = ldsx + buf * XS;
+#pragma unroll
+    for (int u = 0; u < SPX; ++u)
+      __builtin_amdgcn_global_load_lds((global_void_ptr)(srcx[u] + kt * BKD),
+                                       (lds_void_ptr)(base + (wid * SPX + u) * 512), 16, 0, 0);
   };
 
   f32x16 acc[MF][MT];
@@ -219,160 +232,110 @@ __global__ void __launch_bounds__(64 * WGF * WGT, MINB) k_gemm_bf16_dma(GemmArgs
 
   const int fr = lane & 31, fh = lane >> 5, fswz = chunk_swz<C>(lane & 15);
   const int nk = tile.klen / BKD;
-  constexpr int KS = BKD / 16;
-  if constexpr (EARLY) {
-    // Two LDS buffers; the barrier sits before the last K sub-step of each
-    // stage instead of at its start.  By then every wave holds the last
-    // sub-step's fragments in registers, so after the barrier the MFMAs of
-    // that sub-step cover both the refill of the buffer just drained (stage
-    // kt + 2) and the first fragment reads of stage kt + 1.
-    static_assert(NS == 2 && KS % 2 == 0, "early-barrier ring is two stages of even sub-steps");
-    // Row blocks of this wave that hold rows of the tile: a partial tile (the
-    // last rows of an expert) skips the MFMAs and fragment reads of the rest,
-    // whose results the epilogue never stores.  One copy of the loop per count
-    // keeps the inner loop free of branches.
-    const int mta = __builtin_amdgcn_readfirstlane(
-        max(0, min(MT, (tile.row_end - tile.row0 - wt * WTT + 31) / 32)));
-    auto main_loop = [&](auto mta_c) {
-      constexpr int MTA = decltype(mta_c)::value;
-      bf16x8 af[2][MF], bfr[2][MT];
-#define MOE_FRAGS2(SW, SX, KSV, SLOT)                                                          \
-      {                                                                                      \
-        const int qo_ = ((2 * (KSV) + fh) ^ fswz) * 8;                                       \
-        _Pragma("unroll") for (int i = 0; i < MF; ++i)                                       \
-          af[SLOT][i] = *reinterpret_cast<const bf16x8*>((SW) + (wf * WTF + i * 32 + fr) * BKD + qo_); \
-        _Pragma("unroll") for (int j = 0; j < MTA; ++j)                                      \
-          bfr[SLOT][j] = *reinterpret_cast<const bf16x8*>((SX) + (wt * WTT + j * 32 + fr) * BKD + qo_); \
-      }
-#define MOE_MFMAS2(KSV)                                                                       \
-      _Pragma("unroll") for (int i = 0; i < MF; ++i)                                          \
-        _Pragma("unroll") for (int j = 0; j < MTA; ++j)                                       \
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[(KSV) & 1][i], bfr[(KSV) & 1][j], \
-                                                              acc[i][j], 0, 0, 0);
-      if (nk > 0) {
-        issue(0, 0);
-        if (nk > 1) issue(1, 1);
-        if (nk > 1) MOE_WAIT_VMCNT(SPW);
-        else MOE_WAIT_VMCNT(0);
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        if (MTA > 0) MOE_FRAGS2(lds, lds + BF * BKD, 0, 0)
-        __builtin_amdgcn_sched_barrier(0);
-        // Every stage but the last.  The body has no branch, so the refill DMA
-        // and the next stage's first fragment reads are scheduled between the
-        // last sub-step's MFMAs: past the last stage the refill repeats stage
-        // nk - 1, in bounds, into the buffer just drained, which is not read
-        // again (the DMA queue is drained before the workgroup exits).
-        for (int kt = 0; kt + 1 < nk; ++kt) {
-          const uint16_t* sw = lds + (kt & 1) * LS;
-          const uint16_t* sx = sw + BF * BKD;
-          const int knext = min(kt + 2, nk - 1);
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            if (ks + 1 < KS) {
-              if (MTA > 0) MOE_FRAGS2(sw, sx, ks + 1, (ks + 1) & 1)
-              MOE_MFMAS2(ks)
-              if (MTA > 0) sched_interleave<MF + MTA, MF * MTA>();
-            } else {
-              // this wave's reads of stage kt are in registers and its share
-              // of stage kt + 1 has landed; after the barrier the same holds
-              // for every wave, so buffer kt & 1 may be refilled
-              __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
-              asm volatile("" ::: "memory");
-              __builtin_amdgcn_s_barrier();
-              asm volatile("" ::: "memory");
-              // the next stage's first fragment reads under the first row of
-              // MFMAs, then the refill DMA under the rest
-              const uint16_t* nw = lds + ((kt + 1) & 1) * LS;
-              if (MTA > 0) MOE_FRAGS2(nw, nw + BF * BKD, 0, 0)
-#pragma unroll
-              for (int j = 0; j < MTA; ++j)
-                acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][0], bfr[ks & 1][j],
-                                                                    acc[0][j], 0, 0, 0);
-              if (MTA > 0) sched_interleave<MF + MTA, MTA>();
-              __builtin_amdgcn_sched_barrier(0);
-              issue(knext, kt & 1);
-#pragma unroll
-              for (int i = 1; i < MF; ++i)
-#pragma unroll
-                for (int j = 0; j < MTA; ++j)
-                  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j],
-                                                                      acc[i][j], 0, 0, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        }
-        {
-          const uint16_t* sw = lds + ((nk - 1) & 1) * LS;
-          const uint16_t* sx = sw + BF * BKD;
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            if (ks + 1 < KS && MTA > 0) MOE_FRAGS2(sw, sx, ks + 1, (ks + 1) & 1)
-            MOE_MFMAS2(ks)
-            if (ks + 1 < KS && MTA > 0) sched_interleave<MF + MTA, MF * MTA>();
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        }
-        MOE_WAIT_VMCNT(0);
-      }
-#undef MOE_MFMAS2
-#undef MOE_FRAGS2
-    };
-    static_assert(MT <= 4, "one loop copy per row-block count");
-    if (mta >= MT) main_loop(std::integral_constant<int, MT>{});
-    else if (mta == 3) main_loop(std::integral_constant<int, (MT > 3 ? 3 : MT)>{});
-    else if (mta == 2) main_loop(std::integral_constant<int, (MT > 2 ? 2 : MT)>{});
-    else if (mta == 1) main_loop(std::integral_constant<int, 1>{});
-    else main_loop(std::integral_constant<int, 0>{});
-    gemm_epilogue<BF, BT, WGF, WGT, EPI>(a, tile, acc, wf, wt, fr, fh);
-    return;
-  }
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < nk) issue(s, s);
-  for (int kt = 0; kt < nk; ++kt) {
-    // stage kt is complete once at most (NS - 2) later stages are pending
-    if (kt + NS - 2 < nk) MOE_WAIT_VMCNT((NS - 2) * SPW);
-    else MOE_WAIT_VMCNT(0);
-    // Workgroup barrier without the memory fence of __syncthreads (which would
-    // drain every in-flight stage): each wave has waited for its own part of
-    // stage kt above, so after the barrier all of stage kt is in LDS, and every
-    // wave's reads of stage kt - 1 (consumed by its MFMAs) are done, so that
-    // buffer may be refilled.  The empty asm statements keep the compiler
-    // from moving LDS accesses across the barrier.
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
-    const uint16_t* sw = lds + (kt % NS) * LS;
-    const uint16_t* sx = sw + BF * BKD;
-    // fragments of sub-step ks + 1 are read while the MFMAs of ks run
+  // Row blocks of this wave that hold rows of the tile: a partial tile (the
+  // last rows of an expert) skips the MFMAs and fragment reads of the rest,
+  // whose results the epilogue never stores.  One copy of the loop per count
+  // keeps the inner loop free of branches.
+  const int mta = __builtin_amdgcn_readfirstlane(
+      max(0, min(MT, (tile.row_end - tile.row0 - wt * WTT + 31) / 32)));
+  auto main_loop = [&](auto mta_c) {
+    constexpr int MTA = decltype(mta_c)::value;
     bf16x8 af[2][MF], bfr[2][MT];
-#define MOE_FRAGS(KSV, SLOT)                                                                 \
+#define MOE_FRAGS2(SW, SX, KSV, SLOT)                                                          \
     {                                                                                        \
       const int qo_ = ((2 * (KSV) + fh) ^ fswz) * 8;                                         \
       _Pragma("unroll") for (int i = 0; i < MF; ++i)                                         \
-        af[SLOT][i] = *reinterpret_cast<const bf16x8*>(sw + (wf * WTF + i * 32 + fr) * BKD + qo_); \
-      _Pragma("unroll") for (int j = 0; j < MT; ++j)                                         \
-        bfr[SLOT][j] = *reinterpret_cast<const bf16x8*>(sx + (wt * WTT + j * 32 + fr) * BKD + qo_); \
+        af[SLOT][i] = *reinterpret_cast<const bf16x8*>((SW) + (wf * WTF + i * 32 + fr) * BKD + qo_); \
+      _Pragma("unroll") for (int j = 0; j < MTA; ++j)                                        \
+        bfr[SLOT][j] = *reinterpret_cast<const bf16x8*>((SX) + (wt * WTT + j * 32 + fr) * BKD + qo_); \
     }
-    MOE_FRAGS(0, 0)
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (ks + 1 < KS) MOE_FRAGS(ks + 1, (ks + 1) & 1)
-#pragma unroll
-      for (int i = 0; i < MF; ++i)
-#pragma unroll
-        for (int j = 0; j < MT; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j],
-                                                              acc[i][j], 0, 0, 0);
-      if (ks + 1 < KS) sched_interleave<MF + MT, MF * MT>();
+#define MOE_MFMA2(I, J, KSV)                                                                   \
+    acc[I][J] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[(KSV) & 1][I], bfr[(KSV) & 1][J],  \
+                                                        acc[I][J], 0, 0, 0);
+    if (nk > 0) {
+      // stages 0 and 1 of both operands and stage 2 of the weights (past the
+      // last stage a load repeats stage nk - 1, in bounds, into a buffer that
+      // is not read again; the DMA queue is drained before the exit)
+      issue_x(0, 0);
+      issue_w(0, 0);
+      issue_x(min(1, nk - 1), 1);
+      issue_w(min(1, nk - 1), 1);
+      issue_w(min(2, nk - 1), 2);
+      MOE_WAIT_VMCNT(SPX + 2 * SPW);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (MTA > 0) MOE_FRAGS2(lds, ldsx, 0, 0)
       __builtin_amdgcn_sched_barrier(0);
+      int wb = 0;                                // weight buffer of stage kt (kt % 3)
+      // every stage but the last; the body has no branch, so the refills and
+      // the next stage's first fragment reads are scheduled between the last
+      // sub-step's MFMAs
+      for (int kt = 0; kt + 1 < nk; ++kt) {
+        const uint16_t* sw = lds + wb * WS;
+        const uint16_t* sx = ldsx + (kt & 1) * XS;
+        const int wn = wb == 2 ? 0 : wb + 1;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          if (ks + 1 < KS) {
+            if (MTA > 0) MOE_FRAGS2(sw, sx, ks + 1, (ks + 1) & 1)
+#pragma unroll
+            for (int i = 0; i < MF; ++i)
+#pragma unroll
+              for (int j = 0; j < MTA; ++j) MOE_MFMA2(i, j, ks)
+            if (MTA > 0) sched_interleave<MF + MTA, MF * MTA>();
+          } else {
+            // this wave's reads of stage kt are in registers and its share
+            // of stage kt + 1 has landed (in flight: the weights of stage
+            // kt + 2); after the barrier the same holds for every wave, so
+            // the buffers of stage kt may be refilled
+            MOE_WAIT_VMCNT(SPW);
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            // the next stage's first fragment reads under the first row of
+            // MFMAs, then the refills under the rest
+            if (MTA > 0) MOE_FRAGS2(lds + wn * WS, ldsx + ((kt + 1) & 1) * XS, 0, 0)
+#pragma unroll
+            for (int j = 0; j < MTA; ++j) MOE_MFMA2(0, j, ks)
+            if (MTA > 0) sched_interleave<MF + MTA, MTA>();
+            __builtin_amdgcn_sched_barrier(0);
+            issue_x(min(kt + 2, nk - 1), kt & 1);
+            issue_w(min(kt + 3, nk - 1), wb);
+#pragma unroll
+            for (int i = 1; i < MF; ++i)
+#pragma unroll
+              for (int j = 0; j < MTA; ++j) MOE_MFMA2(i, j, ks)
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        wb = wn;
+      }
+      {
+        const uint16_t* sw = lds + wb * WS;
+        const uint16_t* sx = ldsx + ((nk - 1) & 1) * XS;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          if (ks + 1 < KS && MTA > 0) MOE_FRAGS2(sw, sx, ks + 1, (ks + 1) & 1)
+#pragma unroll
+          for (int i = 0; i < MF; ++i)
+#pragma unroll
+            for (int j = 0; j < MTA; ++j) MOE_MFMA2(i, j, ks)
+          if (ks + 1 < KS && MTA > 0) sched_interleave<MF + MTA, MF * MTA>();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      MOE_WAIT_VMCNT(0);
     }
-#undef MOE_FRAGS
-  }
+#undef MOE_MFMA2
+#undef MOE_FRAGS2
+  };
+  if (mta >= MT) main_loop(std::integral_constant<int, MT>{});
+  else if (mta == 3) main_loop(std::integral_constant<int, (MT > 3 ? 3 : MT)>{});
+  else if (mta == 2) main_loop(std::integral_constant<int, (MT > 2 ? 2 : MT)>{});
+  else if (mta == 1) main_loop(std::integral_constant<int, 1>{});
+  else main_loop(std::integral_constant<int, 0>{});
   gemm_epilogue<BF, BT, WGF, WGT, EPI>(a, tile, acc, wf, wt, fr, fh);
 }
 
@@ -678,20 +641,20 @@ hipError_t launch_gemm(int dtype, const GemmArgs& a, int bf, int bt, int grid, h
   if (bt == 256) {
     const dim3 b8(512);
     switch (a.epi) {
-      case EPI_ACT: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_ACT>), g, b8, 0, s, a); break;
-      case EPI_SWIGLU: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_SWIGLU>), g, b8, 0, s, a); break;
-      case EPI_GATE: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_GATE>), g, b8, 0, s, a); break;
-      case EPI_SCALE_F32: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_SCALE_F32>), g, b8, 0, s, a); break;
-      case EPI_GATE_SPLIT: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_GATE_SPLIT>), g, b8, 0, s, a); break;
-      case EPI_STORE_T: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, 64, 2, EPI_STORE_T>), g, b8, 0, s, a); break;
+      case EPI_ACT: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, EPI_ACT>), g, b8, 0, s, a); break;
+      case EPI_SWIGLU: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, EPI_SWIGLU>), g, b8, 0, s, a); break;
+      case EPI_GATE: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, EPI_GATE>), g, b8, 0, s, a); break;
+      case EPI_SCALE_F32: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, EPI_SCALE_F32>), g, b8, 0, s, a); break;
+      case EPI_GATE_SPLIT: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, EPI_GATE_SPLIT>), g, b8, 0, s, a); break;
+      case EPI_STORE_T: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, EPI_STORE_T>), g, b8, 0, s, a); break;
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (a.epi) {
-      case EPI_ACT: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 128, 2, 2, 64, 2, EPI_ACT>), g, b, 0, s, a); break;
-      case EPI_SWIGLU: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 128, 2, 2, 64, 2, EPI_SWIGLU>), g, b, 0, s, a); break;
-      case EPI_GATE: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 128, 2, 2, 64, 2, EPI_GATE>), g, b, 0, s, a); break;
-      case EPI_SCALE_F32: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 128, 2, 2, 64, 2, EPI_SCALE_F32>), g, b, 0, s, a); break;
+      case EPI_ACT: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 128, 2, 2, EPI_ACT>), g, b, 0, s, a); break;
+      case EPI_SWIGLU: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 128, 2, 2, EPI_SWIGLU>), g, b, 0, s, a); break;
+      case EPI_GATE: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 128, 2, 2, EPI_GATE>), g, b, 0, s, a); break;
+      case EPI_SCALE_F32: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 128, 2, 2, EPI_SCALE_F32>), g, b, 0, s, a); break;
       default: return hipErrorInvalidValue;
     }
   }
