@@ -550,8 +550,15 @@ __global__ void __launch_bounds__(1024) k_plan(PlanArgs p) {
       const int nf = nn / mt, m = nn - nf * mt;
       t.expert = u;
       t.spare = sp;
-      t.row0 = p.offsets[u] + m * p.bt;
-      t.row_end = min(p.offsets[u + 1], t.row0 + p.bt);
+      // the group's rows split evenly over its mt row tiles, in multiples of
+      // 32 (the MFMA row block): tiles of one group then cost the same (the
+      // kernels skip whole row blocks past a tile's end), so the row tiles
+      // that share a weight tile stay in step and share it through L2
+      // instead of one short tile running ahead; rt <= bt keeps every tile
+      // non-empty
+      const int rt = min(p.bt, ((rows + mt - 1) / max(mt, 1) + 31) / 32 * 32);
+      t.row0 = p.offsets[u] + m * rt;
+      t.row_end = min(p.offsets[u + 1], t.row0 + rt);
       if (p.gemm == 1) {
         t.wrow0 = p.foff[u] * pf + nf * p.bf;
         t.kofs = 0;
