@@ -21,6 +21,8 @@
 // MFMA work per stage doubles.
 #include <algorithm>
 
+#include <type_traits>
+
 #include "common.h"
 #include "gemm_common.h"
 #include "internal.h"
@@ -135,7 +137,9 @@ __global__ void __launch_bounds__(512) k_gemm_mx(MxGemmArgs m) {
   const Tile tile = a.tiles[remap_xcd(blockIdx.x, nt)];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  const int wf = wid / WGT, wt = wid % WGT;
+  // waves wid and wid + 4 share a SIMD: the same feature rows, the two row
+  // halves (a tile with few rows keeps every SIMD equally busy)
+  const int wt = wid / WGF, wf = wid % WGF;
   const uint8_t* __restrict__ X = static_cast<const uint8_t*>(a.X);
   const uint8_t* __restrict__ W = static_cast<const uint8_t*>(a.W);
   const int xk0 = EPI == EPI_GATE_SPLIT ? tile.spare * tile.klen : 0;
@@ -186,7 +190,6 @@ __global__ void __launch_bounds__(512) k_gemm_mx(MxGemmArgs m) {
   };
 
   const int fr = lane & 31, fh = lane >> 5, fswz = chunk_swz<C>(lane & 15);
-  uint32_t sa[MF], sb[MT];
 
   f32x16 acc[MF][MT];
 #pragma unroll
@@ -203,7 +206,6 @@ __global__ void __launch_bounds__(512) k_gemm_mx(MxGemmArgs m) {
   // so the slot offset is one per-lane base XORed with 64 ksv + 32 h.
   const uint32_t a_off = uint32_t((wf * WTF + fr) * BK + ((fh ^ fswz) << 4));
   const uint32_t b_off = uint32_t(BF * BK + (wt * WTT + fr) * BK + ((fh ^ fswz) << 4));
-  i32x8 af[MF], bfr[MT];
 #define MOE_MX_LOAD(DST, SW, OFF, KSV)                                                         \
   {                                                                                            \
     const u32x4 lo_ = *reinterpret_cast<const u32x4*>((SW) + ((OFF) ^ (64u * (KSV))));         \
@@ -215,13 +217,13 @@ __global__ void __launch_bounds__(512) k_gemm_mx(MxGemmArgs m) {
   {                                                                                            \
     _Pragma("unroll") for (int i = 0; i < MF; ++i)                                            \
       MOE_MX_LOAD(af[i], (SW) + i * 32 * BK, a_off, KSV)                                       \
-    _Pragma("unroll") for (int j = 0; j < MT; ++j)                                            \
+    _Pragma("unroll") for (int j = 0; j < MTA; ++j)                                           \
       MOE_MX_LOAD(bfr[j], (SW) + j * 32 * BK, b_off, KSV)                                      \
   }
 #define MOE_MX_MFMAS(KSV, SA, SB)                                                              \
   {                                                                                            \
     _Pragma("unroll") for (int i = 0; i < MF; ++i)                                            \
-      _Pragma("unroll") for (int j = 0; j < MT; ++j)                                          \
+      _Pragma("unroll") for (int j = 0; j < MTA; ++j)                                         \
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                           \
             af[i], bfr[j], acc[i][j], 0, 0, 0, int(SA[i]), 0, int(SB[j]));                     \
   }
@@ -231,13 +233,13 @@ __global__ void __launch_bounds__(512) k_gemm_mx(MxGemmArgs m) {
   {                                                                                            \
     const int sh_ = 8 * (2 * (KSV) + fh);                                                      \
     _Pragma("unroll") for (int i = 0; i < MF; ++i) SA[i] = (sa[i] >> sh_) & 0xFFu;            \
-    _Pragma("unroll") for (int j = 0; j < MT; ++j) SB[j] = (sb[j] >> sh_) & 0xFFu;            \
+    _Pragma("unroll") for (int j = 0; j < MTA; ++j) SB[j] = (sb[j] >> sh_) & 0xFFu;            \
   }
 #define MOE_MX_SCALES(SW)                                                                      \
   {                                                                                            \
     _Pragma("unroll") for (int i = 0; i < MF; ++i)                                            \
       sa[i] = *reinterpret_cast<const uint32_t*>((SW) + LT + (wf * WTF + i * 32 + fr) * 4);    \
-    _Pragma("unroll") for (int j = 0; j < MT; ++j)                                            \
+    _Pragma("unroll") for (int j = 0; j < MTA; ++j)                                           \
       sb[j] = *reinterpret_cast<const uint32_t*>((SW) + LT + BF * 4 + (wt * WTT + j * 32 + fr) * 4); \
   }
 
@@ -248,51 +250,67 @@ __global__ void __launch_bounds__(512) k_gemm_mx(MxGemmArgs m) {
   // MFMAs below the barrier, which keeps both fragment sets live): past the
   // last stage the refill repeats stage nk - 1, in bounds, into a buffer that
   // is not read again.
-  constexpr int SPI = SPW + 1;                  // DMA instructions per wave per stage
-  if (nk > 0) {
-    issue(0, 0);
-    if (nk > 1) issue(1, 1);
-    if (nk > 1) MOE_WAIT_VMCNT(SPI);
-    else MOE_WAIT_VMCNT(0);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    for (int kt = 0; kt + 1 < nk; ++kt) {
-      const uint8_t* sw = lds + (kt & 1) * LS;
-      const int knext = min(kt + 2, nk - 1);
+  // Row blocks of this wave that hold rows of the tile: the MFMAs, fragment
+  // and scale reads of the rest (never stored) are skipped, one loop copy
+  // per count.
+  const int mta = __builtin_amdgcn_readfirstlane(
+      max(0, min(MT, (tile.row_end - tile.row0 - wt * WTT + 31) / 32)));
+  auto main_loop = [&](auto mta_c) {
+    constexpr int MTA = decltype(mta_c)::value;
+    uint32_t sa[MF], sb[MT];
+    i32x8 af[MF], bfr[MT];
+    constexpr int SPI = SPW + 1;                  // DMA instructions per wave per stage
+    if (nk > 0) {
+      issue(0, 0);
+      if (nk > 1) issue(1, 1);
+      if (nk > 1) MOE_WAIT_VMCNT(SPI);
+      else MOE_WAIT_VMCNT(0);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      for (int kt = 0; kt + 1 < nk; ++kt) {
+        const uint8_t* sw = lds + (kt & 1) * LS;
+        const int knext = min(kt + 2, nk - 1);
+        MOE_MX_SCALES(sw)
+        MOE_MX_FRAGS(sw, 0)
+        {
+          MOE_MX_BYTES(0, s0a, s0b)
+          MOE_MX_MFMAS(0, s0a, s0b)
+        }
+        __builtin_amdgcn_sched_barrier(0);         // one fragment set live at a time
+        MOE_MX_FRAGS(sw, 1)
+        MOE_MX_BYTES(1, s1a, s1b)
+        asm volatile("s_waitcnt 0x0070" ::: "memory");   // vmcnt(0) lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        issue(knext, kt & 1);
+        MOE_MX_MFMAS(1, s1a, s1b)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const uint8_t* sw = lds + ((nk - 1) & 1) * LS;
       MOE_MX_SCALES(sw)
       MOE_MX_FRAGS(sw, 0)
       {
         MOE_MX_BYTES(0, s0a, s0b)
         MOE_MX_MFMAS(0, s0a, s0b)
       }
-      __builtin_amdgcn_sched_barrier(0);         // one fragment set live at a time
-      MOE_MX_FRAGS(sw, 1)
-      MOE_MX_BYTES(1, s1a, s1b)
-      asm volatile("s_waitcnt 0x0070" ::: "memory");   // vmcnt(0) lgkmcnt(0)
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      issue(knext, kt & 1);
-      MOE_MX_MFMAS(1, s1a, s1b)
       __builtin_amdgcn_sched_barrier(0);
+      MOE_MX_FRAGS(sw, 1)
+      {
+        MOE_MX_BYTES(1, s1a, s1b)
+        MOE_MX_MFMAS(1, s1a, s1b)
+      }
+      // the repeated refill may still be in flight: the workgroup's LDS must
+      // not be released under it
+      MOE_WAIT_VMCNT(0);
     }
-    const uint8_t* sw = lds + ((nk - 1) & 1) * LS;
-    MOE_MX_SCALES(sw)
-    MOE_MX_FRAGS(sw, 0)
-    {
-      MOE_MX_BYTES(0, s0a, s0b)
-      MOE_MX_MFMAS(0, s0a, s0b)
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    MOE_MX_FRAGS(sw, 1)
-    {
-      MOE_MX_BYTES(1, s1a, s1b)
-      MOE_MX_MFMAS(1, s1a, s1b)
-    }
-    // the repeated refill may still be in flight: the workgroup's LDS must
-    // not be released under it
-    MOE_WAIT_VMCNT(0);
-  }
+  };
+  static_assert(MT == 4, "one loop copy per row-block count");
+  if (mta >= 4) main_loop(std::integral_constant<int, 4>{});
+  else if (mta == 3) main_loop(std::integral_constant<int, 3>{});
+  else if (mta == 2) main_loop(std::integral_constant<int, 2>{});
+  else if (mta == 1) main_loop(std::integral_constant<int, 1>{});
+  else main_loop(std::integral_constant<int, 0>{});
 
 #undef MOE_MX_LOAD
 #undef MOE_MX_FRAGS
