@@ -38,13 +38,13 @@ TRAFFIC = {
     "mixtral_bf16": {
         "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
                                                  "common.h"),
-        "source_sha256": "1e26a41cecfb0aff04f80960bdc07508fed4ac239f803045828b8fdcf4252a50",
-        "fetch_kib": 1616241.7, "write_kib": 229387.5},
+        "source_sha256": "a1bbba5adf5596d5fd110a5040c926fa5b971589be117ad49134f7c748d60e25",
+        "fetch_kib": 1939955.7, "write_kib": 229408.8},
     "mixtral_mxfp8": {
         "kernel": "k_gemm_mx", "sources": ("gemm_mx.hip", "gemm_args.h", "gemm_common.h",
                                            "common.h"),
-        "source_sha256": "a58389c36bc19ab350ffaafe9afea03698b23b427d5810727db888b227854535",
-        "fetch_kib": 1159218.7, "write_kib": 128142.8},
+        "source_sha256": "298223c752a95ec3564b311202049d1805438166908030bc25ab6a4850c8066a",
+        "fetch_kib": 842272.5, "write_kib": 123362.6},
 }
 
 
