@@ -169,9 +169,15 @@ __global__ void __launch_bounds__(64 * WGF * WGT, 1) k_gemm_bf16_dma(GemmArgs a)
   __shared__ __attribute__((aligned(1024))) uint16_t lds[3 * WS + 2 * XS];
   uint16_t* const ldsx = lds + 3 * WS;
 
+  // Persistent: workgroup b takes tiles b, b + G, b + 2 G, ... of the remapped
+  // list (G a multiple of 8, so all of them come from its own XCD's run).
+  // The first loads of the next tile are issued before this tile's
+  // epilogue, so their latency hides behind the epilogue's arithmetic and
+  // stores.
   const int nt = *a.ntiles;
-  if (int(blockIdx.x) >= nt) return;
-  const Tile tile = a.tiles[remap_xcd(blockIdx.x, nt)];
+  const int G = gridDim.x;
+  int tb = blockIdx.x;
+  if (tb >= nt) return;
   const int tid = threadIdx.x, lane = tid & 63;
   // wave-uniform (the LDS destinations of the DMA are then scalar arithmetic)
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -181,32 +187,35 @@ __global__ void __launch_bounds__(64 * WGF * WGT, 1) k_gemm_bf16_dma(GemmArgs a)
   const int wt = wid / WGF, wf = wid % WGF;
   const uint16_t* __restrict__ X = static_cast<const uint16_t*>(a.X);
   const uint16_t* __restrict__ W = static_cast<const uint16_t*>(a.W);
+  const int srow = lane / C;                  // row within a segment
+  const int fr = lane & 31, fh = lane >> 5, fswz = chunk_swz<C>(lane & 15);
 
   // this lane's source address inside each of its wave's segments (loop
-  // invariant; a K step only adds kt * BKD)
-  const int srow = lane / C;                  // row within a segment
-  const int xlast = tile.row_end - 1;
-  // a K-split tile reads its own part of the activation row
-  const int xk0 = (EPI == EPI_GATE_SPLIT || EPI == EPI_SCALE_F32) ? tile.spare * tile.klen : 0;
+  // invariant within a tile; a K step only adds kt * BKD)
   const uint16_t* srcw[SPW];
   const uint16_t* srcx[SPX];
+  auto set_sources = [&](const Tile& t) {
+    const int xlast = t.row_end - 1;
+    // a K-split tile reads its own part of the activation row
+    const int xk0 = (EPI == EPI_GATE_SPLIT || EPI == EPI_SCALE_F32) ? t.spare * t.klen : 0;
 #pragma unroll
-  for (int u = 0; u < SPW; ++u) {
-    const int row = (wid * SPW + u) * RSEG + srow;
-    // a partial feature tile (EPI_STORE_T) reads its last existing weight
-    // row in place of the missing ones
-    const int wr = EPI == EPI_STORE_T ? min(row, tile.spare - 1) : row;
-    srcw[u] = W + int64_t(tile.wrow0 + wr) * a.ldw + tile.kofs + ((lane % C) ^ chunk_swz<C>(row)) * 8;
-  }
+    for (int u = 0; u < SPW; ++u) {
+      const int row = (wid * SPW + u) * RSEG + srow;
+      // a partial feature tile (EPI_STORE_T) reads its last existing weight
+      // row in place of the missing ones
+      const int wr = EPI == EPI_STORE_T ? min(row, t.spare - 1) : row;
+      srcw[u] = W + int64_t(t.wrow0 + wr) * a.ldw + t.kofs + ((lane % C) ^ chunk_swz<C>(row)) * 8;
+    }
 #pragma unroll
-  for (int u = 0; u < SPX; ++u) {
-    const int row = (wid * SPX + u) * RSEG + srow;
-    // with a row map the rows are gathered from the token rows (dispatch
-    // fused here)
-    int xr = min(tile.row0 + row, xlast);
-    if (a.xrow) xr = max(a.xrow[xr], 0);
-    srcx[u] = X + int64_t(xr) * a.ldx + xk0 + ((lane % C) ^ chunk_swz<C>(row)) * 8;
-  }
+    for (int u = 0; u < SPX; ++u) {
+      const int row = (wid * SPX + u) * RSEG + srow;
+      // with a row map the rows are gathered from the token rows (dispatch
+      // fused here)
+      int xr = min(t.row0 + row, xlast);
+      if (a.xrow) xr = max(a.xrow[xr], 0);
+      srcx[u] = X + int64_t(xr) * a.ldx + xk0 + ((lane % C) ^ chunk_swz<C>(row)) * 8;
+    }
+  };
   auto issue_w = [&](int kt, int buf) {
     uint16_t* base = lds + buf * WS;
 #pragma unroll
@@ -221,122 +230,152 @@ __global__ void __launch_bounds__(64 * WGF * WGT, 1) k_gemm_bf16_dma(GemmArgs a)
       __builtin_amdgcn_global_load_lds((global_void_ptr)(srcx[u] + kt * BKD),
                                        (lds_void_ptr)(base + (wid * SPX + u) * 512), 16, 0, 0);
   };
+  // stages 0 and 1 of both operands and stage 2 of the weights (past the
+  // last stage a load repeats stage nk - 1, in bounds, into a buffer that is
+  // not read again)
+  auto prologue = [&](int nk) {
+    issue_x(0, 0);
+    issue_w(0, 0);
+    issue_x(min(1, nk - 1), 1);
+    issue_w(min(1, nk - 1), 1);
+    issue_w(min(2, nk - 1), 2);
+  };
 
+  Tile tile = a.tiles[remap_xcd(tb, nt)];
+  int nk = tile.klen / BKD;
+  set_sources(tile);
+  if (nk > 0) prologue(nk);
+  bool first = true;
   f32x16 acc[MF][MT];
+  for (;;) {
 #pragma unroll
-  for (int i = 0; i < MF; ++i)
+    for (int i = 0; i < MF; ++i)
 #pragma unroll
-    for (int j = 0; j < MT; ++j)
+      for (int j = 0; j < MT; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-  const int fr = lane & 31, fh = lane >> 5, fswz = chunk_swz<C>(lane & 15);
-  const int nk = tile.klen / BKD;
-  // Row blocks of this wave that hold rows of the tile: a partial tile (the
-  // last rows of an expert) skips the MFMAs and fragment reads of the rest,
-  // whose results the epilogue never stores.  One copy of the loop per count
-  // keeps the inner loop free of branches.
-  const int mta = __builtin_amdgcn_readfirstlane(
-      max(0, min(MT, (tile.row_end - tile.row0 - wt * WTT + 31) / 32)));
-  auto main_loop = [&](auto mta_c) {
-    constexpr int MTA = decltype(mta_c)::value;
-    bf16x8 af[2][MF], bfr[2][MT];
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    // Row blocks of this wave that hold rows of the tile: a partial tile (the
+    // last rows of an expert) skips the MFMAs and fragment reads of the rest,
+    // whose results the epilogue never stores.  One copy of the loop per count
+    // keeps the inner loop free of branches.
+    const int mta = __builtin_amdgcn_readfirstlane(
+        max(0, min(MT, (tile.row_end - tile.row0 - wt * WTT + 31) / 32)));
+    auto main_loop = [&](auto mta_c) {
+      constexpr int MTA = decltype(mta_c)::value;
+      bf16x8 af[2][MF], bfr[2][MT];
 #define MOE_FRAGS2(SW, SX, KSV, SLOT)                                                          \
-    {                                                                                        \
-      const int qo_ = ((2 * (KSV) + fh) ^ fswz) * 8;                                         \
-      _Pragma("unroll") for (int i = 0; i < MF; ++i)                                         \
-        af[SLOT][i] = *reinterpret_cast<const bf16x8*>((SW) + (wf * WTF + i * 32 + fr) * BKD + qo_); \
-      _Pragma("unroll") for (int j = 0; j < MTA; ++j)                                        \
-        bfr[SLOT][j] = *reinterpret_cast<const bf16x8*>((SX) + (wt * WTT + j * 32 + fr) * BKD + qo_); \
-    }
+      {                                                                                      \
+        const int qo_ = ((2 * (KSV) + fh) ^ fswz) * 8;                                       \
+        _Pragma("unroll") for (int i = 0; i < MF; ++i)                                       \
+          af[SLOT][i] = *reinterpret_cast<const bf16x8*>((SW) + (wf * WTF + i * 32 + fr) * BKD + qo_); \
+        _Pragma("unroll") for (int j = 0; j < MTA; ++j)                                      \
+          bfr[SLOT][j] = *reinterpret_cast<const bf16x8*>((SX) + (wt * WTT + j * 32 + fr) * BKD + qo_); \
+      }
 #define MOE_MFMA2(I, J, KSV)                                                                   \
-    acc[I][J] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[(KSV) & 1][I], bfr[(KSV) & 1][J],  \
-                                                        acc[I][J], 0, 0, 0);
-    if (nk > 0) {
-      // stages 0 and 1 of both operands and stage 2 of the weights (past the
-      // last stage a load repeats stage nk - 1, in bounds, into a buffer that
-      // is not read again; the DMA queue is drained before the exit)
-      issue_x(0, 0);
-      issue_w(0, 0);
-      issue_x(min(1, nk - 1), 1);
-      issue_w(min(1, nk - 1), 1);
-      issue_w(min(2, nk - 1), 2);
-      MOE_WAIT_VMCNT(SPX + 2 * SPW);
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      if (MTA > 0) MOE_FRAGS2(lds, ldsx, 0, 0)
-      __builtin_amdgcn_sched_barrier(0);
-      int wb = 0;                                // weight buffer of stage kt (kt % 3)
-      // every stage but the last; the body has no branch, so the refills and
-      // the next stage's first fragment reads are scheduled between the last
-      // sub-step's MFMAs
-      for (int kt = 0; kt + 1 < nk; ++kt) {
-        const uint16_t* sw = lds + wb * WS;
-        const uint16_t* sx = ldsx + (kt & 1) * XS;
-        const int wn = wb == 2 ? 0 : wb + 1;
+      acc[I][J] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[(KSV) & 1][I], bfr[(KSV) & 1][J], \
+                                                          acc[I][J], 0, 0, 0);
+      if (nk > 0) {
+        // stage 0 has landed (after the previous tile's epilogue its stores
+        // are counted too, so everything is waited for)
+        if (first) MOE_WAIT_VMCNT(SPX + 2 * SPW);
+        else MOE_WAIT_VMCNT(0);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (MTA > 0) MOE_FRAGS2(lds, ldsx, 0, 0)
+        __builtin_amdgcn_sched_barrier(0);
+        int wb = 0;                              // weight buffer of stage kt (kt % 3)
+        // every stage but the last; the body has no branch, so the refills and
+        // the next stage's first fragment reads are scheduled between the last
+        // sub-step's MFMAs
+        for (int kt = 0; kt + 1 < nk; ++kt) {
+          const uint16_t* sw = lds + wb * WS;
+          const uint16_t* sx = ldsx + (kt & 1) * XS;
+          const int wn = wb == 2 ? 0 : wb + 1;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          if (ks + 1 < KS) {
-            if (MTA > 0) MOE_FRAGS2(sw, sx, ks + 1, (ks + 1) & 1)
+          for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 1 < KS) {
+              if (MTA > 0) MOE_FRAGS2(sw, sx, ks + 1, (ks + 1) & 1)
+#pragma unroll
+              for (int i = 0; i < MF; ++i)
+#pragma unroll
+                for (int j = 0; j < MTA; ++j) MOE_MFMA2(i, j, ks)
+              if (MTA > 0) sched_interleave<MF + MTA, MF * MTA>();
+            } else {
+              // this wave's reads of stage kt are in registers and its share
+              // of stage kt + 1 has landed (in flight: the weights of stage
+              // kt + 2); after the barrier the same holds for every wave, so
+              // the buffers of stage kt may be refilled
+              MOE_WAIT_VMCNT(SPW);
+              __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+              asm volatile("" ::: "memory");
+              __builtin_amdgcn_s_barrier();
+              asm volatile("" ::: "memory");
+              // the next stage's first fragment reads under the first row of
+              // MFMAs, then the refills under the rest
+              if (MTA > 0) MOE_FRAGS2(lds + wn * WS, ldsx + ((kt + 1) & 1) * XS, 0, 0)
+#pragma unroll
+              for (int j = 0; j < MTA; ++j) MOE_MFMA2(0, j, ks)
+              if (MTA > 0) sched_interleave<MF + MTA, MTA>();
+              __builtin_amdgcn_sched_barrier(0);
+              issue_x(min(kt + 2, nk - 1), kt & 1);
+              issue_w(min(kt + 3, nk - 1), wb);
+#pragma unroll
+              for (int i = 1; i < MF; ++i)
+#pragma unroll
+                for (int j = 0; j < MTA; ++j) MOE_MFMA2(i, j, ks)
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          wb = wn;
+        }
+        {
+          const uint16_t* sw = lds + wb * WS;
+          const uint16_t* sx = ldsx + ((nk - 1) & 1) * XS;
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 1 < KS && MTA > 0) MOE_FRAGS2(sw, sx, ks + 1, (ks + 1) & 1)
 #pragma unroll
             for (int i = 0; i < MF; ++i)
 #pragma unroll
               for (int j = 0; j < MTA; ++j) MOE_MFMA2(i, j, ks)
-            if (MTA > 0) sched_interleave<MF + MTA, MF * MTA>();
-          } else {
-            // this wave's reads of stage kt are in registers and its share
-            // of stage kt + 1 has landed (in flight: the weights of stage
-            // kt + 2); after the barrier the same holds for every wave, so
-            // the buffers of stage kt may be refilled
-            MOE_WAIT_VMCNT(SPW);
-            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_s_barrier();
-            asm volatile("" ::: "memory");
-            // the next stage's first fragment reads under the first row of
-            // MFMAs, then the refills under the rest
-            if (MTA > 0) MOE_FRAGS2(lds + wn * WS, ldsx + ((kt + 1) & 1) * XS, 0, 0)
-#pragma unroll
-            for (int j = 0; j < MTA; ++j) MOE_MFMA2(0, j, ks)
-            if (MTA > 0) sched_interleave<MF + MTA, MTA>();
+            if (ks + 1 < KS && MTA > 0) sched_interleave<MF + MTA, MF * MTA>();
             __builtin_amdgcn_sched_barrier(0);
-            issue_x(min(kt + 2, nk - 1), kt & 1);
-            issue_w(min(kt + 3, nk - 1), wb);
-#pragma unroll
-            for (int i = 1; i < MF; ++i)
-#pragma unroll
-              for (int j = 0; j < MTA; ++j) MOE_MFMA2(i, j, ks)
           }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        wb = wn;
-      }
-      {
-        const uint16_t* sw = lds + wb * WS;
-        const uint16_t* sx = ldsx + ((nk - 1) & 1) * XS;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          if (ks + 1 < KS && MTA > 0) MOE_FRAGS2(sw, sx, ks + 1, (ks + 1) & 1)
-#pragma unroll
-          for (int i = 0; i < MF; ++i)
-#pragma unroll
-            for (int j = 0; j < MTA; ++j) MOE_MFMA2(i, j, ks)
-          if (ks + 1 < KS && MTA > 0) sched_interleave<MF + MTA, MF * MTA>();
-          __builtin_amdgcn_sched_barrier(0);
         }
       }
-      MOE_WAIT_VMCNT(0);
-    }
 #undef MOE_MFMA2
 #undef MOE_FRAGS2
-  };
-  if (mta >= MT) main_loop(std::integral_constant<int, MT>{});
-  else if (mta == 3) main_loop(std::integral_constant<int, (MT > 3 ? 3 : MT)>{});
-  else if (mta == 2) main_loop(std::integral_constant<int, (MT > 2 ? 2 : MT)>{});
-  else if (mta == 1) main_loop(std::integral_constant<int, 1>{});
-  else main_loop(std::integral_constant<int, 0>{});
-  gemm_epilogue<BF, BT, WGF, WGT, EPI>(a, tile, acc, wf, wt, fr, fh);
+    };
+    if (mta >= MT) main_loop(std::integral_constant<int, MT>{});
+    else if (mta == 3) main_loop(std::integral_constant<int, (MT > 3 ? 3 : MT)>{});
+    else if (mta == 2) main_loop(std::integral_constant<int, (MT > 2 ? 2 : MT)>{});
+    else if (mta == 1) main_loop(std::integral_constant<int, 1>{});
+    else main_loop(std::integral_constant<int, 0>{});
+    // every wave's LDS reads of this tile are in registers and its DMA has
+    // landed: after the barrier the next tile may refill any buffer
+    MOE_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const int tn = tb + G;
+    const bool more = tn < nt;
+    Tile next = tile;
+    int nk2 = 0;
+    if (more) {
+      next = a.tiles[remap_xcd(tn, nt)];
+      nk2 = next.klen / BKD;
+      set_sources(next);
+      if (nk2 > 0) prologue(nk2);
+    }
+    gemm_epilogue<BF, BT, WGF, WGT, EPI>(a, tile, acc, wf, wt, fr, fh);
+    if (!more) break;
+    tile = next;
+    nk = nk2;
+    tb = tn;
+    first = false;
+  }
 }
 
 // ---------------------------------------------------------------- fp32 SIMT GEMM
@@ -631,8 +670,29 @@ hipError_t launch_plan(const PlanArgs& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// A persistent launch of the bf16 GEMM: one workgroup per compute unit (its
+// LDS ring fills a CU), in a multiple of 8 so that each keeps to one XCD's
+// tiles.  (With a grid of one workgroup per tile the kernel's tile loop runs
+// once.)
+static int persistent_grid(int grid) {
+  static thread_local int dev_cached = -1, cus = 256;
+  int dev = 0;
+  if (hipGetDevice(&dev) == hipSuccess && dev != dev_cached) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n >= 8)
+      cus = n / 8 * 8;
+    dev_cached = dev;
+  }
+  return std::min(grid, cus);
+}
+
 hipError_t launch_gemm(int dtype, const GemmArgs& a, int bf, int bt, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
+  // Persistent only for the forward epilogues: the next tile's first wait
+  // also covers this tile's stores (vmcnt counts both), which costs more than
+  // it saves when a tile stores 256 KB of fp32 (the backward's EPI_SCALE_F32
+  // ran 4% slower persistent) or bf16 rows of the backward's EPI_STORE_T.
+  if (dtype != 0 && a.epi != EPI_SCALE_F32 && a.epi != EPI_STORE_T) grid = persistent_grid(grid);
   const dim3 g(grid), b(256);
   if (dtype == 0) {
     switch (a.epi) {
