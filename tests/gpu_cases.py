@@ -38,6 +38,11 @@ SMALL = {
     "atomic_small": Workload("atomic_small", T=200, d=512, E=128 * 128, k=8, act="gelu",
                              router="cartesian", Nr=128, Nc=128, expert_kind="atomic",
                              shared_ffn=512, shared_act="gelu", seed=15),
+    # more tiles than compute units in both expert GEMMs (512 and ~400 with the
+    # second one split), so each persistent workgroup runs several tiles and
+    # issues the next tile's first loads before its epilogue
+    "persistent_tiles": Workload("persistent_tiles", T=4096, d=512, E=8, k=2, act="swiglu",
+                                 ffn=2048, cf=1.25, seed=23),
 }
 
 # max |gpu - ref| / max |ref| per output tensor
