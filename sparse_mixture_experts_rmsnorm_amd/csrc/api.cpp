@@ -408,18 +408,18 @@ int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, i
   p.tiles = w.tiles1;
   p.ntiles = w.nt;
   p.max_tiles = int(w.mt1);
-  MOE_HIP(launch_plan(p, s));
   // second linear
-  p.gemm = 2;
-  p.bf = g.bf2;
-  p.fold = 1;
-  p.dense_n = int(d);
-  p.tiles = w.tiles2;
-  p.ntiles = w.nt + 1;
-  p.max_tiles = int(w.mt2);
-  p.ksplit = w.ksplit;
-  p.bt = g.bt2;
-  MOE_HIP(launch_plan(p, s));
+  PlanArgs p2 = p;
+  p2.gemm = 2;
+  p2.bf = g.bf2;
+  p2.fold = 1;
+  p2.dense_n = int(d);
+  p2.tiles = w.tiles2;
+  p2.ntiles = w.nt + 1;
+  p2.max_tiles = int(w.mt2);
+  p2.ksplit = w.ksplit;
+  p2.bt = g.bt2;
+  MOE_HIP(launch_plan_pair(p, p2, s));
   timer_mark(timer, call, MOE_STAGE_PLAN + 1, s);
 
   if (g.mx) return run_expert_gemms_mx(X, g, d, offsets, dense_rows, x_in, row_r, row_w, y, w, s,
@@ -1381,16 +1381,16 @@ int run_expert_bwd(const ExpertBwdIo& io, int64_t d, int64_t T, const void* dout
   p.tiles = io.t_b1;
   p.ntiles = io.nt_b1;
   p.max_tiles = int(io.mt_b1);
-  MOE_HIP(launch_plan(p, s));
-  p.gemm = 2;
-  p.ragged = 0;
-  p.kmul = g.pf;
-  p.ksplit = std::max(1, io.ksplit);
-  p.dense_n = int(d);
-  p.tiles = io.t_b2;
-  p.ntiles = io.nt_b2;
-  p.max_tiles = int(io.mt_b2);
-  MOE_HIP(launch_plan(p, s));
+  PlanArgs p2 = p;
+  p2.gemm = 2;
+  p2.ragged = 0;
+  p2.kmul = g.pf;
+  p2.ksplit = std::max(1, io.ksplit);
+  p2.dense_n = int(d);
+  p2.tiles = io.t_b2;
+  p2.ntiles = io.nt_b2;
+  p2.max_tiles = int(io.mt_b2);
+  MOE_HIP(launch_plan_pair(p, p2, s));
 
   GemmArgs a{};
   a.X = dout;

@@ -135,30 +135,31 @@ __global__ void __launch_bounds__(1024) k_scan(int32_t* __restrict__ cc,
   __shared__ int padded_s[kDenseMaxE];
   long long dropped = 0, errs = 0;
   int maxl = 0;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+  // one wave per expert: the expert's column of chunk counts is scanned 64
+  // chunks at a time (a shuffle scan per round), in place, to exclusive
+  // per-chunk bases
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  for (int e = wv; e < E; e += nw) {
     int run = 0;
-    int c = 0;
-    // eight independent loads in flight per step (the chunk walk is serial)
-    for (; c + 8 <= nchunks; c += 8) {
-      int v[8];
+    for (int c0 = 0; c0 < nchunks; c0 += 64) {
+      const int c = c0 + lane;
+      const int v = c < nchunks ? cc[int64_t(c) * E + e] : 0;
+      int inc = v;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = cc[int64_t(c + u) * E + e];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        cc[int64_t(c + u) * E + e] = run;
-        run += v[u];
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += t;
       }
+      if (c < nchunks) cc[int64_t(c) * E + e] = run + inc - v;
+      run += __shfl(inc, 63, 64);
     }
-    for (; c < nchunks; ++c) {
-      const int v = cc[int64_t(c) * E + e];
-      cc[int64_t(c) * E + e] = run;
-      run += v;
+    if (lane == 0) {
+      counts[e] = run;
+      const int kept = min(run, cap);
+      padded_s[e] = (kept + pad - 1) / pad * pad;
+      dropped += run - kept;
+      maxl = max(maxl, run);
     }
-    counts[e] = run;
-    const int kept = min(run, cap);
-    padded_s[e] = (kept + pad - 1) / pad * pad;
-    dropped += run - kept;
-    maxl = max(maxl, run);
   }
   for (int c = threadIdx.x; c < nchunks; c += blockDim.x) errs += cerr[c];
   __syncthreads();

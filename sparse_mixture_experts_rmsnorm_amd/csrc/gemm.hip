@@ -477,7 +477,7 @@ __device__ __forceinline__ int upper_bound_i(const int* a, int n, int key) {
 
 constexpr int kPlanMax = 4096;   // experts (grouped) or token-block rows (BCSR)
 
-__global__ void __launch_bounds__(1024) k_plan(PlanArgs p) {
+__device__ __forceinline__ void plan_tiles(const PlanArgs& p) {
   __shared__ int base_s[kPlanMax + 1];
   __shared__ long long sh[33];
   const bool dense = p.offsets == nullptr;
@@ -619,6 +619,15 @@ __global__ void __launch_bounds__(1024) k_plan(PlanArgs p) {
 // ---------------------------------------------------------------- packing
 
 // dst[n, k] = src[k, n], 32 x 32 tiles through LDS.
+
+__global__ void __launch_bounds__(1024) k_plan(PlanArgs p) { plan_tiles(p); }
+
+// Both expert GEMMs' lists in one launch, one workgroup each.
+__global__ void __launch_bounds__(1024) k_plan_pair(PlanArgs p0, PlanArgs p1) {
+  if (blockIdx.x == 0) plan_tiles(p0);
+  else plan_tiles(p1);
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256) k_transpose(const T* __restrict__ src, int64_t K, int64_t N,
                                                    T* __restrict__ dst) {
@@ -667,6 +676,11 @@ int gemm_tile_bt(int dtype, int bcsr) { return dtype == 0 ? 64 : (bcsr ? 128 : 2
 
 hipError_t launch_plan(const PlanArgs& p, hipStream_t s) {
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan_pair(const PlanArgs& p0, const PlanArgs& p1, hipStream_t s) {
+  hipLaunchKernelGGL(k_plan_pair, dim3(2), dim3(1024), 0, s, p0, p1);
   return hipGetLastError();
 }
 

@@ -83,6 +83,8 @@ struct MxGemmArgs {
 };
 
 hipError_t launch_plan(const PlanArgs& p, hipStream_t s);
+// Two tile lists (independent outputs) in one launch.
+hipError_t launch_plan_pair(const PlanArgs& p0, const PlanArgs& p1, hipStream_t s);
 hipError_t launch_gemm(int dtype, const GemmArgs& a, int bf, int bt, int grid, hipStream_t s);
 int gemm_tile_bf(int dtype);   // packed features per tile the GEMM kernels use
 int gemm_tile_bt(int dtype, int bcsr);
