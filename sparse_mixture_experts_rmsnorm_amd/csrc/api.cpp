@@ -193,8 +193,8 @@ struct ExpertWs {
   int* nt = nullptr;   // [2]
   float* a_rows = nullptr;
   int64_t mt1 = 0, mt2 = 0;
-  int ksplit = 1;        // K halves of the second linear
-  void* ypart = nullptr;   // [ksplit][rows_max][d] gated partials (ksplit 2), dtype
+  int ksplit = 1;        // K parts of the second linear (1, 2 or 4)
+  void* ypart = nullptr;   // [ksplit][rows_max][d] gated partials (ksplit > 1), dtype
   int64_t plane = 0;
   int64_t rows_max = 0;
   // MXFP8: the quantised GEMM rows and hidden activation with their scales

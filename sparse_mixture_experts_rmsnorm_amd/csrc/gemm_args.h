@@ -60,7 +60,8 @@ struct PlanArgs {
   int bf;                    // packed features per tile
   int fold;                  // output columns per packed feature divisor (2 for SwiGLU GEMM1)
   Tile* tiles; int* ntiles; int max_tiles;
-  int ksplit;                // second linear: K halves per tile (1 or 2); tile.spare = split
+  int ksplit;                // second linear: K parts per tile (1, 2 or 4, equal and whole
+                             // K stages); tile.spare = part
   int kmul;                  // second linear: K = kmul * f_e at kmul * foff[e] (0 means 1)
   int ragged;                // first linear: last feature tile of a group may be partial
                              // (tile.spare = its valid features, a multiple of 32)
