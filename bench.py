@@ -38,13 +38,13 @@ TRAFFIC = {
     "mixtral_bf16": {
         "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
                                                  "common.h"),
-        "source_sha256": "a1bbba5adf5596d5fd110a5040c926fa5b971589be117ad49134f7c748d60e25",
-        "fetch_kib": 1939955.7, "write_kib": 229408.8},
+        "source_sha256": "381a9597e08a724704d9c1b1f6022bbb78da742fa3ff1f8b16d0f098bf43b889",
+        "fetch_kib": 1853392.5, "write_kib": 229417.1},
     "mixtral_mxfp8": {
         "kernel": "k_gemm_mx", "sources": ("gemm_mx.hip", "gemm_args.h", "gemm_common.h",
                                            "common.h"),
-        "source_sha256": "298223c752a95ec3564b311202049d1805438166908030bc25ab6a4850c8066a",
-        "fetch_kib": 842272.5, "write_kib": 123362.6},
+        "source_sha256": "72efd1cb92b6477d577440b074798707f52307125a3daf0ee295c8c09b1d9037",
+        "fetch_kib": 840839.7, "write_kib": 123306.7},
 }
 
 
