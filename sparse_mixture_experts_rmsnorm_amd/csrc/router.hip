@@ -365,23 +365,51 @@ __global__ void __launch_bounds__(64 * NW) k_router_bf16(
   // sum of squares of the token over this wave's K range (lanes tl, tl+16, ...)
   ss += __shfl_xor(ss, 16, 64);
   ss += __shfl_xor(ss, 32, 64);
-  // ordered cross-wave reduction (wave 0, then 1, 2, ...): deterministic
-  for (int w = 0; w < NW; ++w) {
-    if (wid == w) {
+  // ordered cross-wave reduction (wave 0, then 1, 2, ...): deterministic.
+  // With few experts every wave's partial goes to LDS at once and one pass
+  // sums them in wave order; otherwise the waves add into one row in turn.
+  constexpr bool kOnePass = NW * kRouterTok * (NB * 16 + 1) * 4 <= 32768;
+  if constexpr (kOnePass) {
+    __shared__ float part[kOnePass ? NW : 1][kRouterTok][NB * 16 + 1];
+    __shared__ float sq_part[NW][kRouterTok];
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int e = b * 16 + kg * 4 + v;
-          if (w == 0) lg[tl][e] = acc[b][v];
-          else lg[tl][e] += acc[b][v];
-        }
-      if (lane < 16) {
-        if (w == 0) ssq[tl] = ss;
-        else ssq[tl] += ss;
-      }
+      for (int v = 0; v < 4; ++v) part[wid][tl][b * 16 + kg * 4 + v] = acc[b][v];
+    if (lane < 16) sq_part[wid][tl] = ss;
+    __syncthreads();
+    for (int i = threadIdx.x; i < kRouterTok * NB * 16; i += 64 * NW) {
+      const int t2 = i / (NB * 16), e = i - t2 * (NB * 16);
+      float sum = part[0][t2][e];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) sum += part[w][t2][e];
+      lg[t2][e] = sum;
+    }
+    if (threadIdx.x < kRouterTok) {
+      float sum = sq_part[0][threadIdx.x];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) sum += sq_part[w][threadIdx.x];
+      ssq[threadIdx.x] = sum;
     }
     __syncthreads();
+  } else {
+    for (int w = 0; w < NW; ++w) {
+      if (wid == w) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int e = b * 16 + kg * 4 + v;
+            if (w == 0) lg[tl][e] = acc[b][v];
+            else lg[tl][e] += acc[b][v];
+          }
+        if (lane < 16) {
+          if (w == 0) ssq[tl] = ss;
+          else ssq[tl] += ss;
+        }
+      }
+      __syncthreads();
+    }
   }
   if (threadIdx.x < kRouterTok) {
     const int tt = t0 + threadIdx.x;
