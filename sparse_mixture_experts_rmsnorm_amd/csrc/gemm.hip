@@ -136,6 +136,48 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const Tile& til
   }
 }
 
+// EPI_SCALE_F32 epilogue through LDS: the tile's fp32 rows are written by
+// the waves that hold them (one 128-row half at a time, 128 KB), then every
+// wave stores whole rows (1 KB per instruction, contiguous) instead of 32
+// bytes of each of 32 rows.  r scales each row as it is stored.  The row
+// pitch carries 4 floats of padding, so the fragment writes (32 rows at a
+// time) spread over the banks.
+template <int BF, int BT, int WGF, int WGT, int MF, int MT>
+__device__ __forceinline__ void epilogue_f32_lds(const GemmArgs& a, const Tile& tile,
+                                                 f32x16 (&acc)[MF][MT], int wf, int wt, int fr,
+                                                 int fh, int lane, int wid, float* st) {
+  constexpr int WTF = BF / WGF, WTT = BT / WGT, NW = WGF * WGT;
+  constexpr int P = BF + 4;                     // row pitch (floats)
+  static_assert(BF == 256 && WTT * P * 4 <= 160 * 1024, "one 256-feature half tile in LDS");
+#pragma unroll
+  for (int h = 0; h < WGT; ++h) {
+    if (wt == h) {
+#pragma unroll
+      for (int j = 0; j < MT; ++j)
+#pragma unroll
+        for (int i = 0; i < MF; ++i)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 o = {acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2],
+                             acc[i][j][g * 4 + 3]};
+            *reinterpret_cast<f32x4*>(st + (j * 32 + fr) * P + wf * WTF + i * 32 + g * 8 + fh * 4) = o;
+          }
+    }
+    __syncthreads();
+    for (int r = wid; r < WTT; r += NW) {
+      const int row = tile.row0 + h * WTT + r;
+      if (row >= tile.row_end) break;
+      const float rs = a.row_r ? a.row_r[row] : 1.f;
+      f32x4 v = *reinterpret_cast<const f32x4*>(st + r * P + lane * 4);
+      v *= rs;
+      float* Y = static_cast<float*>(a.Y) + int64_t(row) * a.ldy + tile.ocol0 +
+                 int64_t(tile.spare) * a.ysplit;
+      *reinterpret_cast<f32x4*>(Y + lane * 4) = v;
+    }
+    __syncthreads();
+  }
+}
+
 // ---------------------------------------------------------------- bf16 MFMA GEMM, LDS-DMA ring
 
 // BF features x BT rows per workgroup, WGF x WGT waves, each wave a
@@ -363,14 +405,28 @@ __global__ void __launch_bounds__(64 * WGF * WGT, 1) k_gemm_bf16_dma(GemmArgs a)
     const bool more = tn < nt;
     Tile next = tile;
     int nk2 = 0;
-    if (more) {
+    if constexpr (EPI == EPI_SCALE_F32 && WGT == 2 && BT == 256) {
+      // fp32 rows staged through the (now idle) LDS, so that every store
+      // writes whole rows; the next tile's loads wait for the LDS
+      epilogue_f32_lds<BF, BT, WGF, WGT>(a, tile, acc, wf, wt, fr, fh, lane, wid,
+                                         reinterpret_cast<float*>(lds));
+      if (!more) break;
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
       next = a.tiles[remap_xcd(tn, nt)];
       nk2 = next.klen / BKD;
       set_sources(next);
       if (nk2 > 0) prologue(nk2);
+    } else {
+      if (more) {
+        next = a.tiles[remap_xcd(tn, nt)];
+        nk2 = next.klen / BKD;
+        set_sources(next);
+        if (nk2 > 0) prologue(nk2);
+      }
+      gemm_epilogue<BF, BT, WGF, WGT, EPI>(a, tile, acc, wf, wt, fr, fh);
+      if (!more) break;
     }
-    gemm_epilogue<BF, BT, WGF, WGT, EPI>(a, tile, acc, wf, wt, fr, fh);
-    if (!more) break;
     tile = next;
     nk = nk2;
     tb = tn;
