@@ -38,13 +38,13 @@ TRAFFIC = {
     "mixtral_bf16": {
         "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
                                                  "common.h"),
-        "source_sha256": "381a9597e08a724704d9c1b1f6022bbb78da742fa3ff1f8b16d0f098bf43b889",
-        "fetch_kib": 1853392.5, "write_kib": 229417.1},
+        "source_sha256": "7dd4196bd7e6cb9a46e10af9de3f4e07a02af735e1dafa7c55abeb2423ee936c",
+        "fetch_kib": 1861829.1, "write_kib": 229417.3},
     "mixtral_mxfp8": {
         "kernel": "k_gemm_mx", "sources": ("gemm_mx.hip", "gemm_args.h", "gemm_common.h",
                                            "common.h"),
         "source_sha256": "72efd1cb92b6477d577440b074798707f52307125a3daf0ee295c8c09b1d9037",
-        "fetch_kib": 840839.7, "write_kib": 123306.7},
+        "fetch_kib": 843933.7, "write_kib": 123440.5},
 }
 
 
