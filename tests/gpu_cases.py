@@ -43,6 +43,10 @@ SMALL = {
     # issues the next tile's first loads before its epilogue
     "persistent_tiles": Workload("persistent_tiles", T=4096, d=512, E=8, k=2, act="swiglu",
                                  ffn=2048, cf=1.25, seed=23),
+    # ffn a multiple of 256 and few tiles: the second GEMM splits K in four
+    # partial planes, which combine adds in plane order
+    "split4_small": Workload("split4_small", T=600, d=512, E=8, k=2, act="swiglu", ffn=512,
+                             cf=1.25, seed=24),
 }
 
 # max |gpu - ref| / max |ref| per output tensor
