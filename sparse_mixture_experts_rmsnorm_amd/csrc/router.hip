@@ -368,7 +368,7 @@ __global__ void __launch_bounds__(64 * NW) k_router_bf16(
   // ordered cross-wave reduction (wave 0, then 1, 2, ...): deterministic.
   // With few experts every wave's partial goes to LDS at once and one pass
   // sums them in wave order; otherwise the waves add into one row in turn.
-  constexpr bool kOnePass = NW * kRouterTok * (NB * 16 + 1) * 4 <= 32768;
+  constexpr bool kOnePass = NW * kRouterTok * (NB * 16 + 1) * 4 <= 40960;
   if constexpr (kOnePass) {
     __shared__ float part[kOnePass ? NW : 1][kRouterTok][NB * 16 + 1];
     __shared__ float sq_part[NW][kRouterTok];
@@ -813,8 +813,10 @@ hipError_t launch_router_dense(const void* x, int dtype, int64_t T, int64_t d, c
   } else {
     const dim3 g(unsigned((T + kRouterTok - 1) / kRouterTok));
     const int nb = int((E + 15) / 16);
-    // waves per workgroup: each wave's K range a multiple of 32
-    const int nw = d % (16 * 32) == 0 ? 16 : d % (8 * 32) == 0 ? 8 : 4;
+    // waves per workgroup: each wave's K range a multiple of 32; with more
+    // than 32 experts 8 waves, whose partial logits still fit the one-pass
+    // reduction in LDS
+    const int nw = d % (16 * 32) == 0 && nb <= 2 ? 16 : d % (8 * 32) == 0 ? 8 : 4;
 #define MOE_ROUTER_CASE(NBV, NWV)                                                              \
     hipLaunchKernelGGL((k_router_bf16<NBV, NWV>), g, dim3(64 * NWV), 0, s,                       \
                        static_cast<const uint16_t*>(x), int(T), int(d),                         \
