@@ -47,6 +47,9 @@ SMALL = {
     # partial planes, which combine adds in plane order
     "split4_small": Workload("split4_small", T=600, d=512, E=8, k=2, act="swiglu", ffn=512,
                              cf=1.25, seed=24),
+    # one expert, k = 1: every token's gate is 1 and the layer is a dense FFN
+    "single_expert": Workload("single_expert", T=300, d=256, E=1, k=1, act="gelu", ffn=512,
+                              cf=0.0, seed=25),
 }
 
 # max |gpu - ref| / max |ref| per output tensor
