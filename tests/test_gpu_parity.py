@@ -200,7 +200,7 @@ def test_determinism(name, dev):
 @pytest.mark.parametrize("E,k,cap,pad,T", [(8, 2, 5, 1, 40), (8, 2, 1000, 128, 300),
                                            (64, 6, 30, 1, 1000), (5, 3, 2, 4, 1),
                                            (256, 8, 7, 1, 513), (3000, 4, 10 ** 6, 1, 777),
-                                           (16, 4, 900, 1, 5000),
+                                           (16, 4, 6000, 1, 20000),
                                            (1 << 20, 32, 10 ** 6, 1, 300)])
 def test_dispatch_bit_exact(E, k, cap, pad, T, dev):
     _say(f"[gpu] dispatch E={E} k={k} cap={cap} pad={pad} T={T}")
