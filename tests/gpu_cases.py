@@ -50,6 +50,10 @@ SMALL = {
     # one expert, k = 1: every token's gate is 1 and the layer is a dense FFN
     "single_expert": Workload("single_expert", T=300, d=256, E=1, k=1, act="gelu", ffn=512,
                               cf=0.0, seed=25),
+    # a wide model: K of 8192 in the router and the first GEMM (128 stages),
+    # 32 output tiles in the second
+    "wide_d": Workload("wide_d", T=96, d=8192, E=4, k=2, act="swiglu", ffn=256, cf=1.5,
+                       seed=26),
 }
 
 # max |gpu - ref| / max |ref| per output tensor
