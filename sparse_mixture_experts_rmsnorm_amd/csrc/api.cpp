@@ -137,8 +137,8 @@ int check_experts(const moe_experts_desc* X, int dtype, int64_t d, ExpertGeo* g)
   REQUIRE(X->quant == MOE_QUANT_NONE || X->quant == MOE_QUANT_MXFP8, MOE_EDTYPE,
           "unknown quant %d", X->quant);
   if (X->quant == MOE_QUANT_MXFP8) {
-    REQUIRE(dtype == MOE_BF16 && !geo.bcsr, MOE_EUNSUPPORTED,
-            "MXFP8 experts are implemented for bf16 grouped experts");
+    REQUIRE(dtype == MOE_BF16, MOE_EUNSUPPORTED,
+            "MXFP8 experts are implemented for bf16 grouped and BCSR experts");
     REQUIRE(X->w13_scale && X->w2_scale, MOE_EINVAL, "MXFP8 experts need w13_scale and w2_scale");
     geo.mx = true;
     for (int64_t e = 0; e < X->E; ++e)

@@ -16,8 +16,9 @@ Five layer shapes are used throughout (tests, smoke check, benchmark):
                      1024 x 1024 Cartesian router, top-32, plus a dense
                      GELU shared MLP of 4096
 
-and mixtral_mxfp8, the Mixtral-shaped layer with MXFP8 routed experts (OCP
-Microscaling: E4M3 elements, one E8M0 scale per 32 along K).
+and mixtral_mxfp8 / variable_bcsr_mxfp8, the Mixtral-shaped and the
+variable-size BCSR layers with MXFP8 routed experts (OCP Microscaling: E4M3
+elements, one E8M0 scale per 32 along K).
 
 The variable-size expert spec follows the "Variable-size experts" nanoMOE
 notes (configuration section: [(count, size), ...]); the capacity factor and
@@ -94,6 +95,10 @@ WORKLOADS = {
     "variable_bcsr_bf16": Workload("variable_bcsr_bf16", T=8192, d=768, E=8, k=2, act="gelu",
                                    expert_sizes=((1, 2048), (7, 1024)), cf=0.0,
                                    bias="normal", expert_kind="bcsr", seed=1003),
+    "variable_bcsr_mxfp8": Workload("variable_bcsr_mxfp8", T=8192, d=768, E=8, k=2,
+                                    act="gelu", expert_sizes=((1, 2048), (7, 1024)), cf=0.0,
+                                    bias="normal", expert_kind="bcsr", quant="mxfp8",
+                                    seed=1003),
     "finegrained_bf16": Workload("finegrained_bf16", T=16384, d=2048, E=64, k=6, act="swiglu",
                                  ffn=1408, cf=1.5, bias="zipf", shared_ffn=2 * 1408,
                                  shared_act="swiglu", seed=1004),

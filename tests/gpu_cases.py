@@ -54,6 +54,11 @@ SMALL = {
     # 32 output tiles in the second
     "wide_d": Workload("wide_d", T=96, d=8192, E=4, k=2, act="swiglu", ffn=256, cf=1.5,
                        seed=26),
+    # MXFP8 operands on the block-sparse (BCSR) walk: 128-row token blocks,
+    # variable expert sizes
+    "bcsr_small_mxfp8": Workload("bcsr_small_mxfp8", T=600, d=256, E=4, k=2, act="gelu",
+                                 expert_sizes=((1, 512), (3, 256)), bias="normal",
+                                 expert_kind="bcsr", quant="mxfp8", seed=27),
 }
 
 # max |gpu - ref| / max |ref| per output tensor

@@ -133,7 +133,7 @@ def test_expert_descriptor_checks():
     assert lib.moe_expert_workspace_size(C.byref(X), 1, 512, 100, 2, 200) == 0
     X.act = 2
     assert lib.moe_expert_workspace_size(C.byref(X), 1, 500, 100, 2, 200) == 0   # d % 256
-    # MXFP8: scales required, bf16 grouped only, ffn sizes multiples of 128
+    # MXFP8: scales required, bf16 grouped or BCSR, ffn sizes multiples of 128
     n_bf16 = lib.moe_expert_workspace_size(C.byref(X), 1, 512, 100, 2, 200)
     X.quant = B.QUANT_MXFP8
     assert lib.moe_expert_workspace_size(C.byref(X), 1, 512, 100, 2, 200) == 0
@@ -143,8 +143,11 @@ def test_expert_descriptor_checks():
     assert n_mx > 0 and n_mx != n_bf16
     assert lib.moe_expert_workspace_size(C.byref(X), 0, 512, 100, 2, 200) == 0   # f32
     X.kind = 1
-    assert lib.moe_expert_workspace_size(C.byref(X), 1, 512, 100, 2, 200) == 0   # BCSR
-    X.kind = 0
+    assert lib.moe_expert_workspace_size(C.byref(X), 1, 512, 100, 2, 200) == 0   # BCSR, block 0
+    assert "block" in B.last_error()
+    X.block, X.size_blocks, X.block_offsets = 128, 16, 16
+    assert lib.moe_expert_workspace_size(C.byref(X), 1, 512, 100, 2, 256) > 0    # MXFP8 BCSR
+    X.kind, X.block, X.size_blocks, X.block_offsets = 0, 0, None, None
     sizes2 = B.i64_array([320, 256])
     X.ffn_sizes = C.cast(sizes2, C.POINTER(C.c_int64))
     assert lib.moe_expert_workspace_size(C.byref(X), 1, 512, 100, 2, 200) == 0

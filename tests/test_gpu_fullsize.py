@@ -27,7 +27,7 @@ SAMPLE = 24
 
 @pytest.mark.timeout(300)   # the MXFP8 oracle quantises six 4096 x 14336 weight slices
 @pytest.mark.parametrize("name", ["mixtral_bf16", "mixtral_mxfp8", "variable_bcsr_bf16",
-                                  "finegrained_bf16", "atomic_bf16"])
+                                  "variable_bcsr_mxfp8", "finegrained_bf16", "atomic_bf16"])
 def test_fullsize_parity(name):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
