@@ -133,7 +133,7 @@ typedef struct moe_experts_desc {
   const int32_t* block_offsets; /* [E+1] prefix sum of size_blocks            */
   const int32_t* row_offsets;   /* [rows_max/block + 1] CSR row pointer       */
   const int32_t* column_indices;/* [nnz_max] column block of each nonzero     */
-  /* MOE_QUANT_MXFP8 (GROUPED, bf16 layers only): w13_t and w2_t hold E4M3
+  /* MOE_QUANT_MXFP8 (GROUPED or BCSR, bf16 layers only): w13_t and w2_t hold E4M3
    * codes (one byte per element, same packed layouts) and w13_scale [P, d/32],
    * w2_scale [d, F/32] their E8M0 block scales, as written by moe_pack_mxfp8
    * from the bf16 packs (P = F, or 2F for SwiGLU).  Following the CODA
