@@ -50,7 +50,8 @@ def _capture(fn):
 
 
 @pytest.mark.parametrize("name", ["mixtral_small_drops", "finegrained_small", "bcsr_small",
-                                  "atomic_small", "mixtral_small_mxfp8"])
+                                  "atomic_small", "mixtral_small_mxfp8", "bcsr_small_mxfp8",
+                                  "persistent_tiles"])
 def test_forward_graph_replay(name, dev):
     _say(f"[gpu] graph replay forward {name}")
     wl = SMALL[name]
