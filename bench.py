@@ -77,6 +77,9 @@ def parse():
                     help="skip the MXFP8 variant of a grouped bf16 workload")
     ap.add_argument("--cpu-sample", type=int, default=4096,
                     help="tokens whose expert FFNs the CPU oracle computes")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="also time torch.bmm (hipBLASLt) on per-expert GEMMs of the same "
+                         "shapes, for context (outside the headline figure)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale HBM byte counters)")
     return ap.parse_args()
@@ -101,6 +104,36 @@ def flops_gemm1(wl, kept):
 
 def flops_gemm2(wl, kept):
     return sum(2.0 * wl.d * f * m for f, m in zip(wl.sizes, kept))
+
+
+def vendor_gemm(wl, kept, stages, steps):
+    """torch.bmm (hipBLASLt) on the uniform-routing form of the two expert
+    linears: every expert takes the mean kept row count, one weight matrix per
+    expert, bf16 in and out, no epilogue.  Context for the expert GEMMs' rate on
+    the same chip; best of three timed runs of `steps` calls each."""
+    import torch
+    dev = "cuda"
+    E, F = wl.E, wl.sizes[0]
+    R = max(32, int(round(sum(kept) / E / 32)) * 32)
+    n1 = F * (2 if wl.act == "swiglu" else 1)
+    out = {"rows_per_expert": R}
+    g = torch.Generator(device=dev).manual_seed(1)
+    for name, k, n, ours in (("gemm1", wl.d, n1, stages["gemm1"]), ("gemm2", F, wl.d, stages["gemm2"])):
+        a = torch.randn((E, R, k), generator=g, device=dev).to(torch.bfloat16)
+        b = torch.randn((E, k, n), generator=g, device=dev).to(torch.bfloat16).contiguous()
+        c = torch.bmm(a, b)
+        best = min(_time_calls(lambda: torch.bmm(a, b, out=c), steps) for _ in range(3))
+        fl = 2.0 * E * R * k * n
+        ours_fl = (flops_gemm1 if name == "gemm1" else flops_gemm2)(wl, kept)
+        out[name] = {"ms": best, "tflops": fl / (best * 1e-3) / 1e12,
+                     "ours_tflops": ours_fl / (ours * 1e-3) / 1e12}
+        out[name]["ours_over_vendor"] = out[name]["ours_tflops"] / out[name]["tflops"]
+        del a, b, c
+    torch.cuda.empty_cache()
+    out["note"] = ("torch.bmm over E experts x the mean kept rows, uniform (no ragged rows, "
+                   "no SwiGLU / gate / r-scale epilogue, no K-split planes); the expert GEMMs "
+                   "compared here run on the layer's real routing")
+    return out
 
 
 def time_dispatch_gather(B, wl, layer, ws, x, steps):
@@ -443,6 +476,9 @@ def main():
                      "out), moe_dispatch with x_perm (token rows read once, kept rows written "
                      "once; its time includes the count / scan / rank index kernels), "
                      "moe_router_topk (x + router weights)")}
+    if (args.vendor_gemm and wl.expert_kind == "grouped" and wl.dtype == "bf16"
+            and wl.quant == "none" and len(set(wl.sizes)) == 1):
+        result["vendor_gemm"] = vendor_gemm(wl, kept, stages, args.steps)
     gms = time_layer_graph(layer, x, out, ws, stats, args.steps)
     result["graph_replay"] = {"ms_per_step": gms, "tokens_per_s": wl.T / (gms * 1e-3),
                               "note": "the same forward captured in one HIP graph and replayed"}
