@@ -598,6 +598,121 @@ def test_mx_ffn_reduces_to_dense_on_grid_values():
     assert np.max(np.abs(O.ffn_mxfp8(x, r, w1, w2, "gelu") - full)) < 0.1 * np.max(np.abs(full))
 
 
+def _e4m3_positive_grid():
+    """Every finite non-negative E4M3 value, from the bit fields: exponent 0
+    is subnormal m * 2^-9, otherwise (1 + m/8) * 2^(e-7); S.1111.111 is NaN."""
+    vals = [m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+            for e in range(16) for m in range(8) if not (e == 15 and m == 7)]
+    return np.array(sorted(set(vals)))
+
+
+def _mx_grid_operand(rng, shape, axis, grid, s_lo, s_hi):
+    """(Q, A): Q lies on the MXFP8 grid along `axis` (each block of 32 shares
+    a power-of-two scale 2^s, s drawn from [s_lo, s_hi), and holds E4M3 values
+    in [32, 416] times 2^s, its largest in [288, 416] so that
+    floor(log2 max) = s + 8); A = Q plus a perturbation of
+    at most a fifth of each element's quantum, so MXFP8 quantisation of A along
+    `axis` gives back exactly Q (the perturbation keeps every block's binade of
+    the maximum and stays inside each element's rounding interval)."""
+    normal = grid[(grid >= 32.0) & (grid <= 416.0)]
+    big = grid[(grid >= 288.0) & (grid <= 416.0)]
+    q = np.moveaxis(rng.choice(normal, size=shape) * rng.choice([-1.0, 1.0], size=shape), axis, -1)
+    nb = q.shape[-1] // 32
+    qb = q.reshape(q.shape[:-1] + (nb, 32))
+    flat = qb.reshape(-1, 32)
+    at = rng.integers(0, 32, size=flat.shape[0])
+    flat[np.arange(flat.shape[0]), at] = rng.choice(big, size=flat.shape[0]) * \
+        rng.choice([-1.0, 1.0], size=flat.shape[0])
+    s = rng.integers(s_lo, s_hi, size=qb.shape[:-1])
+    qb = flat.reshape(qb.shape) * np.exp2(s)[..., None]
+    quantum = np.exp2(np.floor(np.log2(np.abs(qb))) - 3.0)
+    a = qb + 0.2 * rng.uniform(-1.0, 1.0, size=qb.shape) * quantum
+    back = lambda t: np.moveaxis(t.reshape(q.shape), -1, axis)  # noqa: E731
+    return back(qb), back(a)
+
+
+def _bruteforce_qdq_rows(h, grid):
+    """MXFP8 quantise-dequantise along axis 1 by brute force: per block of 32
+    the scale is 2^(floor(log2 max|v|) - 8); each element goes to the nearest
+    grid value of |v| / scale (clamped to 448), with its sign."""
+    out = np.empty_like(h)
+    for i in range(h.shape[0]):
+        for b in range(h.shape[1] // 32):
+            blk = h[i, 32 * b:32 * b + 32]
+            scale = 2.0 ** (math.floor(math.log2(np.max(np.abs(blk)))) - 8)
+            t = np.minimum(np.abs(blk) / scale, 448.0)
+            near = grid[np.argmin(np.abs(grid[None, :] - t[:, None]), axis=1)]
+            out[i, 32 * b:32 * b + 32] = np.sign(blk) * near * scale
+    return out
+
+
+def _mx_ffn_case(act, seed):
+    """Operands off the MXFP8 grid whose quantised values are known by
+    construction, r far from 1 and not a power of two, and the expected
+    output of the MXFP8 expert FFN built from those values by hand: x rows
+    quantised along d, w1 / w3 along d (per column), r on the first linear's
+    accumulator, SiLU(gate) * up (or GELU), h quantised along f, w2 along f."""
+    rng = _rng(seed)
+    grid = _e4m3_positive_grid()
+    T, d, f = 6, 64, 96
+    # blocks of x at 2^-3 .. 2^1, of the weights at 2^-8 .. 2^-4, so the hidden
+    # pre-activations are O(1) and blocks of one row differ in scale
+    qx, x = _mx_grid_operand(rng, (T, d), 1, grid, -11, -7)
+    q1, w1 = _mx_grid_operand(rng, (d, f), 0, grid, -16, -12)
+    q3, w3 = _mx_grid_operand(rng, (d, f), 0, grid, -16, -12)
+    q2, w2 = _mx_grid_operand(rng, (f, d), 0, grid, -16, -12)
+    r = rng.uniform(0.55, 1.45, size=T)
+    a = r[:, None] * (qx @ q1)
+    if act == "swiglu":
+        h = a / (1.0 + np.exp(-a)) * (r[:, None] * (qx @ q3))
+    else:
+        h = 0.5 * a * (1.0 + np.vectorize(math.erf)(a / math.sqrt(2.0)))
+    ref = _bruteforce_qdq_rows(h, grid) @ q2
+    return dict(x=x, r=r, w1=w1, w3=w3 if act == "swiglu" else None, w2=w2, ref=ref)
+
+
+def _mx_ffn_mutant(kind):
+    """Plausible mistakes in the MXFP8 FFN, each a copy of the composition
+    with one step changed (planted on the CPU only, to show the pin sees it)."""
+    def run(xhat, r, w1, w2, act, w3=None):
+        r = np.asarray(r, dtype=np.float64)[:, None]
+        if kind == "r_before_quant":
+            xq = O.mx_qdq(r * xhat, axis=1)
+            a = xq @ O.mx_qdq(w1, axis=0)
+            u = None if w3 is None else xq @ O.mx_qdq(w3, axis=0)
+        else:
+            xq = O.mx_qdq(xhat, axis=1)
+            a = r * (xq @ O.mx_qdq(w1, axis=0))
+            w3q = {"w3_unquantised": lambda w: w, "w3_wrong_axis": lambda w: O.mx_qdq(w, axis=1),
+                   "w1_wrong_axis": lambda w: O.mx_qdq(w, axis=0)}[kind](w3) if w3 is not None else None
+            if kind == "w1_wrong_axis":
+                a = r * (xq @ O.mx_qdq(w1, axis=1))
+            u = None if w3q is None else r * (xq @ w3q)
+        h = O.silu(a) * u if act == "swiglu" else O.gelu(a)
+        return O.mx_qdq(h, axis=1) @ O.mx_qdq(w2, axis=0)
+    return run
+
+
+@pytest.mark.parametrize("act", ["swiglu", "gelu"])
+def test_mx_ffn_matches_hand_built_quantised_product(act):
+    """The MXFP8 expert FFN with r != 1 equals the product built by hand from
+    operand values known to be the MXFP8 quantisation of the inputs; each
+    plausible misplacement of a quantiser or of r misses it by orders of
+    magnitude more than the oracle does."""
+    c = _mx_ffn_case(act, 31 if act == "swiglu" else 32)
+    den = np.max(np.abs(c["ref"]))
+    err = lambda fn: float(np.max(np.abs(fn(c["x"], c["r"], c["w1"], c["w2"], act, c["w3"])  # noqa: E731
+                                        - c["ref"])) / den)
+    e0 = err(O.ffn_mxfp8)
+    assert e0 < 1e-12
+    mutants = ["r_before_quant", "w1_wrong_axis"]
+    if act == "swiglu":
+        mutants += ["w3_unquantised", "w3_wrong_axis"]
+    for kind in mutants:
+        em = err(_mx_ffn_mutant(kind))
+        assert em > 2e-3, (kind, em)
+
+
 # ---------------------------------------------------------------- backward pass
 
 def test_activation_derivatives_match_finite_differences():
