@@ -372,11 +372,16 @@ int moe_build_topology(const int32_t* offsets, const int32_t* size_blocks,
  *   by expert as OmniMoE 2.2 schedules it) the two-phase expert-centric
  *   form runs; with row_expert NULL the single-pass token-centric form runs
  *   from ids, w and r alone (moe_layer_forward uses it).  Both give the same
- *   bits.  Hidden activations live in the workspace. */
+ *   bits.  A slot whose id lies outside [0, N) is dropped (no row is read)
+ *   and added to stats->errors (stats nullable; the count is added to what
+ *   stats holds, never reset here); a task row whose token lies outside
+ *   [0, T) is dropped.  Hidden activations live in the workspace.
+ * stats is not used by the GROUPED / BCSR kinds (they read no expert ids). */
 size_t moe_expert_workspace_size(const moe_experts_desc* X, int dtype, int64_t d,
                                  int64_t T, int k, int64_t rows_max);
 int moe_expert_gemm(const moe_experts_desc* X, int dtype, int64_t d, const moe_routing* rt,
-                    const void* x_in, void* y, void* ws, size_t ws_bytes, hipStream_t stream);
+                    const void* x_in, void* y, moe_stats* stats, void* ws, size_t ws_bytes,
+                    hipStream_t stream);
 
 /* Always-on shared FFN over all T tokens with gate 1 (one expert, kind
  * GROUPED): s[t] = FFN(r[t] * xhat[t]). */
@@ -385,14 +390,46 @@ int moe_shared_ffn(const moe_experts_desc* S, int dtype, int64_t d, int64_t T, c
                    const float* r, void* s, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---- step 5: combine ----
- * out[t] = x[t] + shared[t] + sum_{j : pos[t,j] >= 0} y[pos[t,j]], summed in
- * fp32 in exactly that order and stored once.  residual / shared may be
- * NULL.  With pos == NULL, y is [T, d] in token order (the atomic branch).
- * A token whose slots are all dropped gets out = x bit-exactly.  k <= 256. */
+ * "Mixture of Experts (MoE)" glossary: the layer output is the sum of the
+ * selected experts' outputs weighted by their router scores (gating-network
+ * and top-k entries), and a token that overflows every chosen expert's
+ * capacity skips the experts and passes through unchanged (expert-capacity
+ * and dropped-token entries); OmniMoE summary 2.1: the shared dense MLP's
+ * output is added to the routed branch.  The gate is already applied by the
+ * second expert linear's epilogue, so here:
+ *   out[t] = x[t] + shared[t] + sum_{j : pos[t,j] >= 0} y[pos[t,j]],
+ * summed in fp32 in exactly that order and stored once.
+ *   y        [rows_max, d] expert outputs in permuted order (dtype), or with
+ *            pos == NULL [T, d] in token order (the atomic branch);
+ *   pos      [T, k] int32 rows of the token's slots, -1 = dropped;
+ *   residual [T, d] (nullable: no residual), shared [T, d] (nullable);
+ *   out      [T, d], fully overwritten; may not alias y.
+ * A token whose slots are all dropped gets out = x bit-exactly.  Errors:
+ * MOE_EDTYPE for an unknown dtype, MOE_ESHAPE for T < 0, d < 1, k < 1 or a
+ * row that does not fill 16-byte vectors, MOE_EUNSUPPORTED for k > 256,
+ * MOE_EINVAL for a NULL y / out with T > 0. */
 int moe_combine(const void* y, const int32_t* pos, const void* residual, const void* shared,
                 int dtype, int64_t T, int64_t d, int k, void* out, hipStream_t stream);
 
-/* ---- the whole layer ---- */
+/* ---- the whole layer ----
+ * The forward pass the pages compose: the CODA sparse-MoE thread's RMSNorm
+ * with the r-scale commuted into the router's and the first expert linear's
+ * epilogues, the glossary's gating network with top-k / switch routing and
+ * the expert-capacity rule, the dispatch (the glossary's fused-MoE-kernels
+ * entry: routing, permutation and expert GEMMs without host round trips),
+ * the expert FFNs (grouped, the nanoMOE notes' variable-size BCSR walk, or
+ * OmniMoE 2.1 atomic experts behind the 2.2 Cartesian router), the shared
+ * experts (OmniMoE 2.1) and the combine above.  Steps 1-5 run on `stream`
+ * with every tile list built on the device: no host read-back of the loads.
+ *   L     [host] layer descriptor (weights packed as described at the top);
+ *   x     [T, d] in L->dtype; out [T, d], fully overwritten (not aliasing x);
+ *   stats nullable: rows, dropped slots, max load, data errors (int32 x 4);
+ *   ws    moe_layer_workspace_size(L, T) bytes, caller-owned; it also keeps
+ *         the routing for moe_layer_routing and, with save_for_backward,
+ *         what moe_layer_backward reads.
+ * Errors (nothing enqueued): MOE_EINVAL / MOE_ESHAPE for a bad descriptor or
+ * T < 0, MOE_EWORKSPACE when ws_bytes is too small, MOE_EUNSUPPORTED for a
+ * combination no kernel covers, MOE_EHIP for a failed launch. */
 size_t moe_layer_workspace_size(const moe_layer_desc* L, int64_t T);
 int moe_layer_forward(const moe_layer_desc* L, const void* x, int64_t T, void* out,
                       moe_stats* stats, void* ws, size_t ws_bytes, hipStream_t stream);

@@ -112,7 +112,7 @@ def lib() -> C.CDLL:
             "moe_build_topology": (I, [P, P, P, I64, I, I64, P, P, P, P]),
             "moe_expert_workspace_size": (SZ, [C.POINTER(ExpertsDesc), I, I64, I64, I, I64]),
             "moe_expert_gemm": (I, [C.POINTER(ExpertsDesc), I, I64, C.POINTER(Routing), P, P, P,
-                                    SZ, P]),
+                                    P, SZ, P]),
             "moe_shared_workspace_size": (SZ, [C.POINTER(ExpertsDesc), I, I64, I64]),
             "moe_shared_ffn": (I, [C.POINTER(ExpertsDesc), I, I64, I64, P, P, P, P, SZ, P]),
             "moe_combine": (I, [P, P, P, P, I, I64, I64, I, P, P]),
@@ -291,9 +291,10 @@ def expert_workspace_size(desc: ExpertsDesc, dtype: int, d: int, T: int, k: int,
 
 
 def expert_gemm(desc: ExpertsDesc, dtype: int, d: int, routing: Routing, x_in, y, ws,
-                stream=None) -> None:
+                stream=None, stats=None) -> None:
     check(lib().moe_expert_gemm(C.byref(desc), dtype, d, C.byref(routing), ptr(x_in), ptr(y),
-                                ptr(ws), ws.numel() * ws.element_size(), stream_handle(stream)))
+                                ptr(stats), ptr(ws), ws.numel() * ws.element_size(),
+                                stream_handle(stream)))
 
 
 def shared_workspace_size(desc: ExpertsDesc, dtype: int, d: int, T: int) -> int:

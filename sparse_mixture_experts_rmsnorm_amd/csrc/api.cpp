@@ -810,7 +810,8 @@ size_t moe_expert_workspace_size(const moe_experts_desc* X, int dtype, int64_t d
 }
 
 int moe_expert_gemm(const moe_experts_desc* X, int dtype, int64_t d, const moe_routing* rt,
-                    const void* x_in, void* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+                    const void* x_in, void* y, moe_stats* stats, void* ws, size_t ws_bytes,
+                    hipStream_t stream) {
   ExpertGeo g;
   int rc = check_experts(X, dtype, d, &g);
   if (rc) return rc;
@@ -862,6 +863,7 @@ int moe_expert_gemm(const moe_experts_desc* X, int dtype, int64_t d, const moe_r
     a.token_centric = rt->row_expert ? 0 : 1;
     a.w_tok = rt->w;
     a.r_tok = rt->r;
+    a.errors = stats ? &stats->errors : nullptr;
     MOE_HIP(launch_atomic(a, stream));
     return ok();
   }
@@ -1174,6 +1176,7 @@ int moe_layer_forward(const moe_layer_desc* L, const void* x, int64_t T, void* o
     a.token_centric = 1;
     a.w_tok = w.w;
     a.r_tok = w.r;
+    a.errors = &st->errors;
     MOE_HIP(launch_atomic(a, stream));
     timer_mark(tm, call, MOE_STAGE_GEMM1 + 1, stream);
     timer_mark(tm, call, MOE_STAGE_GEMM2 + 1, stream);

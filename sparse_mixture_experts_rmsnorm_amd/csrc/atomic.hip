@@ -29,14 +29,17 @@ template <int CH>
 constexpr int batch_of() { return CH >= 8 ? 1 : 8 / CH; }
 
 // CH = d / 512 16-byte chunks per lane (bf16), d in {512, 1024, 2048, 4096}.
+// Rows whose expert is outside [0, N) or whose token is outside [0, T) are
+// dropped (a = 0, nothing loaded); the rows in use are clamped to rows_max.
 template <int CH>
 __global__ void __launch_bounds__(256) k_atomic_phase1(
-    const uint16_t* __restrict__ xhat, int d, const uint16_t* __restrict__ W,
-    const int32_t* __restrict__ rows_used, const int32_t* __restrict__ row_token,
-    const int32_t* __restrict__ row_expert, const float* __restrict__ row_r,
-    const float* __restrict__ row_w, int act, float* __restrict__ a_rows) {
+    const uint16_t* __restrict__ xhat, int d, const uint16_t* __restrict__ W, int64_t N,
+    int64_t Tn, const int32_t* __restrict__ rows_used, int64_t rows_max,
+    const int32_t* __restrict__ row_token, const int32_t* __restrict__ row_expert,
+    const float* __restrict__ row_r, const float* __restrict__ row_w, int act,
+    float* __restrict__ a_rows) {
   constexpr int NB = batch_of<CH>();
-  const int rows = *rows_used;
+  const int rows = int(min(int64_t(max(*rows_used, 0)), rows_max));
   const int lane = threadIdx.x & 63;
   const int64_t first = (int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6)) * kTasksPerWave;
   if (first >= rows) return;
@@ -48,7 +51,7 @@ __global__ void __launch_bounds__(256) k_atomic_phase1(
       const int64_t row = first + i0 + b;
       const int n = row < rows ? row_expert[row] : -1;
       const int t = row < rows ? row_token[row] : -1;
-      live[b] = n >= 0 && t >= 0;
+      live[b] = uint64_t(uint32_t(n)) < uint64_t(N) && uint64_t(uint32_t(t)) < uint64_t(Tn);
       const u32x4* ws = reinterpret_cast<const u32x4*>(W + int64_t(live[b] ? n : 0) * d);
       const u32x4* xs = reinterpret_cast<const u32x4*>(xhat + int64_t(live[b] ? t : 0) * d);
 #pragma unroll
@@ -92,11 +95,13 @@ __global__ void __launch_bounds__(256) k_atomic_phase1(
   }
 }
 
+// A kept slot (pos >= 0) whose expert id is outside [0, N), or whose row is
+// past rows_max, is dropped and, for a bad id, counted in *errors.
 template <int CH>
 __global__ void __launch_bounds__(256) k_atomic_phase2(
-    const uint16_t* __restrict__ V, int d, int64_t Tn, int k, const int32_t* __restrict__ ids,
-    const int32_t* __restrict__ pos, const float* __restrict__ a_rows,
-    uint16_t* __restrict__ routed) {
+    const uint16_t* __restrict__ V, int d, int64_t N, int64_t Tn, int k,
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ pos, int64_t rows_max,
+    const float* __restrict__ a_rows, uint16_t* __restrict__ routed, int32_t* __restrict__ errors) {
   constexpr int NB = batch_of<CH>();
   const int lane = threadIdx.x & 63;
   const int64_t t = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
@@ -106,6 +111,7 @@ __global__ void __launch_bounds__(256) k_atomic_phase2(
   for (int c = 0; c < CH; ++c)
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[c][q] = 0.f;
+  int bad = 0;
   for (int j0 = 0; j0 < k; j0 += NB) {
     u32x4 vv[NB][CH];
     float a[NB];
@@ -113,11 +119,14 @@ __global__ void __launch_bounds__(256) k_atomic_phase2(
     for (int b = 0; b < NB; ++b) {
       const int j = j0 + b;
       const int p = j < k ? pos[t * k + j] : -1;
-      a[b] = p >= 0 ? a_rows[p] : 0.f;
-      const u32x4* vs =
-          reinterpret_cast<const u32x4*>(V + int64_t(p >= 0 ? ids[t * k + j] : 0) * d);
+      const int n = p >= 0 ? ids[t * k + j] : 0;
+      const bool id_ok = uint64_t(uint32_t(n)) < uint64_t(N);
+      bad += (p >= 0 && !id_ok) ? 1 : 0;
+      const bool live = p >= 0 && int64_t(p) < rows_max && id_ok;
+      a[b] = live ? a_rows[p] : 0.f;
+      const u32x4* vs = reinterpret_cast<const u32x4*>(V + int64_t(live ? n : 0) * d);
 #pragma unroll
-      for (int c = 0; c < CH; ++c) vv[b][c] = p >= 0 ? vs[lane + 64 * c] : u32x4{0u, 0u, 0u, 0u};
+      for (int c = 0; c < CH; ++c) vv[b][c] = live ? vs[lane + 64 * c] : u32x4{0u, 0u, 0u, 0u};
     }
     // slots added in slot order: the sum is the same as one slot at a time
 #pragma unroll
@@ -131,6 +140,7 @@ __global__ void __launch_bounds__(256) k_atomic_phase2(
         for (int q = 0; q < 8; ++q) acc[c][q] = fmaf(a[b], vf[q], acc[c][q]);
       }
   }
+  if (bad && lane == 0 && errors) atomicAdd(errors, bad);
   uint4* out = reinterpret_cast<uint4*>(routed + t * d);
 #pragma unroll
   for (int c = 0; c < CH; ++c) out[lane + 64 * c] = pack16(acc[c], (const uint16_t*)nullptr);
@@ -139,13 +149,16 @@ __global__ void __launch_bounds__(256) k_atomic_phase2(
 // Token-centric single pass: one wave per token keeps x[t] in registers and
 // walks its k slots in order, NB at a time with all 2 NB row gathers (W[n]
 // and V[n]) issued before any is used: a = g * act(r * x.W[n]), then
-// routed[t] += a * V[n] in slot order (the same sum as the two phases).
+// routed[t] += a * V[n] in slot order (the same sum as the two phases).  A
+// slot whose expert id is outside [0, N) is dropped (nothing loaded) and
+// counted in *errors.
 template <int CH>
 __global__ void __launch_bounds__(256) k_atomic_token(
     const uint16_t* __restrict__ xhat, int d, const uint16_t* __restrict__ W,
-    const uint16_t* __restrict__ V, int64_t Tn, int k, const int32_t* __restrict__ ids,
-    const float* __restrict__ w_tok, const float* __restrict__ r_tok, int act,
-    uint16_t* __restrict__ routed) {
+    const uint16_t* __restrict__ V, int64_t N, int64_t Tn, int k,
+    const int32_t* __restrict__ ids, const float* __restrict__ w_tok,
+    const float* __restrict__ r_tok, int act, uint16_t* __restrict__ routed,
+    int32_t* __restrict__ errors) {
   constexpr int NB = CH >= 4 ? 2 : 4;
   const int lane = threadIdx.x & 63;
   const int64_t t = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
@@ -162,14 +175,18 @@ __global__ void __launch_bounds__(256) k_atomic_token(
   for (int c = 0; c < CH; ++c)
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[c][q] = 0.f;
+  int bad = 0;
   for (int j0 = 0; j0 < k; j0 += NB) {
     u32x4 wv[NB][CH], vv[NB][CH];
     float g[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int j = j0 + b;
-      const bool live = j < k;
-      const int n = live ? ids[t * k + j] : 0;
+      const int id = j < k ? ids[t * k + j] : 0;
+      const bool id_ok = uint64_t(uint32_t(id)) < uint64_t(N);
+      bad += (j < k && !id_ok) ? 1 : 0;
+      const bool live = j < k && id_ok;
+      const int n = live ? id : 0;
       g[b] = live ? w_tok[t * k + j] : 0.f;
       const u32x4* ws = reinterpret_cast<const u32x4*>(W + int64_t(n) * d);
       const u32x4* vs = reinterpret_cast<const u32x4*>(V + int64_t(n) * d);
@@ -211,6 +228,7 @@ __global__ void __launch_bounds__(256) k_atomic_token(
       }
     }
   }
+  if (bad && lane == 0 && errors) atomicAdd(errors, bad);
   uint4* out = reinterpret_cast<uint4*>(routed + t * d);
 #pragma unroll
   for (int c = 0; c < CH; ++c) out[lane + 64 * c] = pack16(acc[c], (const uint16_t*)nullptr);
@@ -222,20 +240,21 @@ hipError_t launch_ch(const AtomicArgs& a, hipStream_t s) {
     if (a.T > 0)
       hipLaunchKernelGGL(k_atomic_token<CH>, dim3(unsigned((a.T + 3) / 4)), dim3(256), 0, s,
                          static_cast<const uint16_t*>(a.xhat), int(a.d),
-                         static_cast<const uint16_t*>(a.W), static_cast<const uint16_t*>(a.V), a.T,
-                         a.k, a.ids, a.w_tok, a.r_tok, a.act, static_cast<uint16_t*>(a.routed));
+                         static_cast<const uint16_t*>(a.W), static_cast<const uint16_t*>(a.V), a.N,
+                         a.T, a.k, a.ids, a.w_tok, a.r_tok, a.act,
+                         static_cast<uint16_t*>(a.routed), a.errors);
     return hipGetLastError();
   }
   const int64_t waves1 = (a.rows + kTasksPerWave - 1) / kTasksPerWave;
   if (waves1 > 0)
     hipLaunchKernelGGL(k_atomic_phase1<CH>, dim3(unsigned((waves1 + 3) / 4)), dim3(256), 0, s,
                        static_cast<const uint16_t*>(a.xhat), int(a.d),
-                       static_cast<const uint16_t*>(a.W), a.rows_used, a.row_token, a.row_expert,
-                       a.row_r, a.row_w, a.act, a.a_rows);
+                       static_cast<const uint16_t*>(a.W), a.N, a.T, a.rows_used, a.rows,
+                       a.row_token, a.row_expert, a.row_r, a.row_w, a.act, a.a_rows);
   if (a.T > 0)
     hipLaunchKernelGGL(k_atomic_phase2<CH>, dim3(unsigned((a.T + 3) / 4)), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(a.V), int(a.d), a.T, a.k, a.ids, a.pos,
-                       a.a_rows, static_cast<uint16_t*>(a.routed));
+                       static_cast<const uint16_t*>(a.V), int(a.d), a.N, a.T, a.k, a.ids, a.pos,
+                       a.rows, a.a_rows, static_cast<uint16_t*>(a.routed), a.errors);
   return hipGetLastError();
 }
 

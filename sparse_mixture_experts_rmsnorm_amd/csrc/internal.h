@@ -87,6 +87,7 @@ struct AtomicArgs {
   int token_centric = 0;
   const float* w_tok = nullptr;   // [T, k]
   const float* r_tok = nullptr;   // [T]
+  int32_t* errors = nullptr;      // device, nullable: += slots with ids outside [0, N)
 };
 hipError_t launch_atomic(const AtomicArgs& a, hipStream_t s);
 

@@ -159,12 +159,23 @@ class MoELayer:
 
     def forward(self, x, out=None, ws=None, stats=None, timer: B.StageTimer | None = None,
                 stream=None, router_extras: B.RouterExtras | None = None):
+        """moe_layer_forward on `stream` (torch's current stream by default).
+
+        An `out` or `ws` left to this wrapper is allocated from the pool of
+        the stream the layer runs on, so the caching allocator cannot hand
+        the workspace (freed when this returns) to another stream while the
+        layer's kernels still use it.  Buffers the caller passes are the
+        caller's to keep alive until the stream has finished with them."""
+        import contextlib
+
         import torch
         T = x.shape[0]
-        if out is None:
-            out = torch.empty_like(x)
-        if ws is None:
-            ws = self.alloc_workspace(T)
+        ctx = torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+        with ctx:
+            if out is None:
+                out = torch.empty_like(x)
+            if ws is None:
+                ws = self.alloc_workspace(T)
         self.desc.timer = None if timer is None else timer.handle
         if router_extras is not None:
             self.desc.router_extras = C.pointer(router_extras)
@@ -185,29 +196,35 @@ class MoELayer:
 
     def backward(self, x, dout, ws, bws=None, grads: dict | None = None, stream=None) -> dict:
         """Gradients for dout = dL/d(out) of the last forward on ws (fp32
-        weight gradients in the forward's packed layouts; dx in x's dtype)."""
+        weight gradients in the forward's packed layouts; dx in x's dtype).
+        Buffers left to the wrapper come from the pool of the stream the
+        backward runs on (as in forward)."""
+        import contextlib
+
         import torch
         if not self.train:
             raise RuntimeError("the layer was built without train=True")
         wl, d, T = self.wl, self.wl.d, x.shape[0]
         dev = x.device
-        if bws is None:
-            bws = torch.empty(self.backward_workspace_size(T), dtype=torch.uint8, device=dev)
-        if grads is None:
-            f32 = dict(dtype=torch.float32, device=dev)
-            E = wl.E
-            F = sum(wl.sizes)
-            P = 2 * F if wl.act == "swiglu" else F
-            grads = dict(dx=torch.empty_like(x), dw_router=torch.empty((E, d), **f32),
-                         dw13=torch.empty((P, d), **f32), dw2=torch.empty((F, d), **f32))
-            if self.desc.router.bias:
-                grads["dbias"] = torch.empty(E, **f32)
-            if self.desc.gamma:
-                grads["dgamma"] = torch.empty(d, **f32)
-            if wl.shared_ffn:
-                Ps = 2 * wl.shared_ffn if wl.shared_act == "swiglu" else wl.shared_ffn
-                grads["dws13"] = torch.empty((Ps, d), **f32)
-                grads["dws2"] = torch.empty((wl.shared_ffn, d), **f32)
+        ctx = torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+        with ctx:
+            if bws is None:
+                bws = torch.empty(self.backward_workspace_size(T), dtype=torch.uint8, device=dev)
+            if grads is None:
+                f32 = dict(dtype=torch.float32, device=dev)
+                E = wl.E
+                F = sum(wl.sizes)
+                P = 2 * F if wl.act == "swiglu" else F
+                grads = dict(dx=torch.empty_like(x), dw_router=torch.empty((E, d), **f32),
+                             dw13=torch.empty((P, d), **f32), dw2=torch.empty((F, d), **f32))
+                if self.desc.router.bias:
+                    grads["dbias"] = torch.empty(E, **f32)
+                if self.desc.gamma:
+                    grads["dgamma"] = torch.empty(d, **f32)
+                if wl.shared_ffn:
+                    Ps = 2 * wl.shared_ffn if wl.shared_act == "swiglu" else wl.shared_ffn
+                    grads["dws13"] = torch.empty((Ps, d), **f32)
+                    grads["dws2"] = torch.empty((wl.shared_ffn, d), **f32)
         g = B.LayerGrads()
         for name in ("dx", "dgamma", "dw_router", "dbias", "dw13", "dw2", "dws13", "dws2"):
             setattr(g, name, B.ptr(grads.get(name)))

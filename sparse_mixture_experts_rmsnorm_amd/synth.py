@@ -133,3 +133,39 @@ def to_device(a: np.ndarray, device="cuda"):
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
     return torch.from_numpy(a).to(device)
+
+
+def make_integer_routing(T: int, d: int, E: int, seed: int, dup_pairs=(), bias_int=None) -> dict:
+    """Router inputs on which every fp32 sum is exact, whatever its order.
+
+    x      entries +-1 (bf16), feature 0 is +1 for every token;
+    w_r    small integers in [-3, 3] times 2^-6 (bf16), [d, E];
+    row 0 of w_r holds bias_int[e] * 2^-6 (|bias_int| <= 256, so still exact
+    in bf16): with feature 0 fixed at +1 it acts as a per-expert bias inside
+    the product, skewing the load so that the capacity rule drops slots;
+    dup_pairs (a, b): column b is a copy of column a, so experts a and b tie
+    exactly on every token.
+    Returns bf16 bit patterns (uint16) for both.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.choice(np.array([-1.0, 1.0], dtype=np.float32), size=(T, d))
+    x[:, 0] = 1.0
+    w = rng.integers(-3, 4, size=(d, E)).astype(np.float32)
+    if bias_int is not None:
+        b = np.asarray(bias_int, dtype=np.float32)
+        if b.shape != (E,) or np.max(np.abs(b)) > 256:
+            raise ValueError("bias_int must hold E integers of magnitude <= 256")
+        w[0, :] = b
+    for a, c in dup_pairs:
+        w[:, c] = w[:, a]
+    w *= np.float32(2.0 ** -6)
+    return dict(x=_to_bf16_bits(x), w_router=_to_bf16_bits(w))
+
+
+def zipf_bias_int(E: int, s: float, seed: int, unit: float = 0.5) -> np.ndarray:
+    """Zipf-shaped integer bias for make_integer_routing: round(-s ln(rank_e)
+    * unit / 2^-6), rank a seeded permutation of 1..E, i.e. the bias
+    -s ln(rank_e) * unit in multiples of 2^-6."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    rank = rng.permutation(E).astype(np.float64) + 1.0
+    return np.rint(-s * np.log(rank) * unit / 2.0 ** -6).astype(np.int64)

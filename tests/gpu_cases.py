@@ -64,6 +64,15 @@ SMALL = {
 # max |gpu - ref| / max |ref| per output tensor
 TOL = {"f32": 1e-3, "bf16": 2e-2}
 
+# measured errors of this session's parity tests, printed at the end of the
+# run by the terminal-summary hook in conftest.py
+RESULTS: list = []
+
+
+def record(test: str, **errs) -> None:
+    """Keep the measured errors of one parity case for the session summary."""
+    RESULTS.append((test, errs))
+
 
 def rel_err(gpu, ref) -> float:
     """max |gpu - ref| / max |ref| (the absolute error when ref is all zero)."""
@@ -93,3 +102,24 @@ def oracle_params(wl: Workload, inp: dict) -> dict:
 
 def f64(a) -> np.ndarray:
     return O.as_f64(a)
+
+
+def near_tie_tokens(ref_sorted: np.ndarray, k: int, tau: float) -> np.ndarray:
+    """Tokens whose reference scores, sorted in descending order, have two
+    neighbours among the first k+1 closer than tau: there the k selected ids
+    or their order are decided by rounding, not by the scores."""
+    m = min(k + 1, ref_sorted.shape[1])
+    gaps = ref_sorted[:, :m - 1] - ref_sorted[:, 1:m]
+    return np.nonzero(np.any(gaps < tau, axis=1))[0]
+
+
+def check_ids_against_reference(ids_gpu, ids_ref, ref_sorted, k, tau, what=""):
+    """ids_gpu must equal ids_ref on every token except near-ties (step 4 of
+    the routing protocol); returns (mismatches, near-tie tokens)."""
+    bad = np.nonzero(np.any(np.asarray(ids_gpu) != np.asarray(ids_ref), axis=1))[0]
+    near = near_tie_tokens(ref_sorted, k, tau)
+    unexplained = np.setdiff1d(bad, near)
+    print(f"  {what}ids against the oracle's own routing: {len(bad)} differ, "
+          f"{len(near)} near-ties under tau={tau:.3e}", flush=True)
+    assert len(unexplained) == 0, unexplained[:10]
+    return len(bad), len(near)

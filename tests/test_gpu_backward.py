@@ -5,17 +5,19 @@ evaluated on the GPU's own routing (ids), as in the forward parity tests.
 Every gradient (dx, dgamma, router weight and bias, routed and shared
 expert weights) is compared as max|gpu - ref| / max|ref|.
 
-Tolerance: the backward's GEMM operands are bf16 (dout scaled by the gate,
-r xhat, the saved h and pre-activations, the pre-activation gradients) with
-fp32 accumulation, and dx is stored in bf16: each rounding is 2^-9 relative
-and they compound over two GEMM stages, so 3e-2 of the largest magnitude
-(the forward's 2e-2 plus one more bf16 stage).
+Tolerance: the bf16 bound of the forward, 2e-2 of the largest magnitude
+per gradient tensor.  The backward's GEMM operands are bf16 (dout scaled by
+the gate, r xhat, the saved h and pre-activations, the pre-activation
+gradients) with fp32 accumulation, and dx is stored in bf16; each rounding
+is at most 2^-9 relative, so even compounded over the two GEMM stages the
+error stays an order of magnitude inside the bound.  The measured errors are
+printed and kept in the session summary.
 """
 import numpy as np
 import pytest
 
 import oracle as O
-from gpu_cases import SMALL, f64, oracle_params, rel_err
+from gpu_cases import SMALL, f64, oracle_params, record, rel_err
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -24,7 +26,7 @@ from sparse_mixture_experts_rmsnorm_amd import binding as B  # noqa: E402
 from sparse_mixture_experts_rmsnorm_amd import synth  # noqa: E402
 from sparse_mixture_experts_rmsnorm_amd.layer import MoELayer  # noqa: E402
 
-TOL_BWD = 3e-2
+TOL_BWD = 2e-2
 
 CASES = {
     "mixtral_small_drops": SMALL["mixtral_small_drops"],          # SwiGLU, bias, drops
@@ -113,6 +115,7 @@ def test_backward_parity(name, dev):
     ref0 = O.layer_backward(dict(p, residual=False), inp["x"], dout_np, ids_override=ids)
     e0 = rel_err(f64(synth.to_host(g0["dx"])), ref0["dx"])
     _say(f"  dx without the residual {e0:.2e}")
+    record(f"backward {name}", **errs, dx_no_residual=e0)
     assert e0 <= TOL_BWD
 
 
@@ -196,6 +199,7 @@ def test_backward_fullsize(name, dev):
         errs.append(rel_err(g["dws2"].cpu().numpy()[units], b["dw2"]))
     _say(f"  {name}: dx {e_dx:.2e}, dx without residual {e_dx0:.2e}, "
          f"sampled weight gradients max {max(errs):.2e}")
+    record(f"full-size backward {name}", dx=e_dx, dx_no_residual=e_dx0, dw_sampled=max(errs))
     assert e_dx <= TOL_BWD and e_dx0 <= TOL_BWD
     assert max(errs) <= TOL_BWD
 

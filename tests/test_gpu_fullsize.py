@@ -3,16 +3,20 @@ benchmark times (same workload shapes, device-generated inputs, one
 moe_layer_forward over all tokens).
 
 Integer results are checked over every token: the top-k decision against
-the GPU's own logits / scores, and the whole dispatch (counts, offsets,
-positions, dropped set, row order) against the oracle on the same ids.
-Floating-point outputs are checked on a sample of tokens the oracle computes
-one by one, within max|gpu-ref|/max|ref| <= 2e-2 (bf16).
+the GPU's own logits / scores (bit-exact), the ids against the oracle's own
+float64 routing (equal except where two of the top k+1 reference scores lie
+within 1e-5 max|l|), and the whole dispatch (counts, offsets, positions,
+dropped set, row order) against the oracle on the same ids.  The Cartesian
+router's ids are also checked against brute force over all 2^20 experts on
+a token subset.  Floating-point outputs are checked on a sample of tokens
+the oracle computes one by one, within max|gpu-ref|/max|ref| <= 2e-2 (bf16),
+for the layer output and for the experts alone (no residual).
 """
 import numpy as np
 import pytest
 
 import oracle as O
-from gpu_cases import TOL, f64, oracle_params, rel_err
+from gpu_cases import TOL, check_ids_against_reference, f64, oracle_params, record, rel_err
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -23,6 +27,8 @@ from sparse_mixture_experts_rmsnorm_amd.layer import MoELayer  # noqa: E402
 from sparse_mixture_experts_rmsnorm_amd.workloads import WORKLOADS  # noqa: E402
 
 SAMPLE = 24
+TAU = 1e-5          # near-tie allowance, relative to max |logit|
+BRUTE = 16          # tokens of the Cartesian brute force over all experts
 
 
 @pytest.mark.timeout(300)   # the MXFP8 oracle quantises six 4096 x 14336 weight slices
@@ -70,12 +76,32 @@ def test_fullsize_parity(name):
     if wl.router == "dense":
         assert np.array_equal(O.select_topk(lg, wl.k), ids)
         l_ref = O.router_logits(inp["x"], None, r_ref, inp["w_router"], inp.get("bias"))
-        assert rel_err(lg, l_ref) < 1e-2
+        e_l = rel_err(lg, l_ref)
+        print(f"  logits rel err {e_l:.2e}", flush=True)
+        assert e_l < 1e-4
+        tau = TAU * np.max(np.abs(l_ref))
+        n_bad, n_near = check_ids_against_reference(ids, O.select_topk(l_ref, wl.k),
+                                                    -np.sort(-l_ref, axis=1), wl.k, tau)
         E = wl.E
     else:
         sel, _ = O.cartesian_topk(lg[:, :wl.Nr], lg[:, wl.Nr:], wl.k)
         assert np.array_equal(sel, ids)
+        s1r, s2r = O.cartesian_scores(inp["x"], None, r_ref, inp["k_rows"], inp["k_cols"])
+        e_l = rel_err(lg, np.hstack([s1r, s2r]))
+        print(f"  scores rel err {e_l:.2e}", flush=True)
+        assert e_l < 1e-4
+        own, own_sc = O.cartesian_topk(s1r, s2r, wl.k)
+        tau = TAU * np.max(np.abs(own_sc[:, 0]))
+        # the k+1 best float64 scores of every token, for the near-tie test
+        top = O.cartesian_topk(s1r, s2r, wl.k + 1)[1]
+        n_bad, n_near = check_ids_against_reference(ids, own, top, wl.k, tau, "two-stage: ")
+        # brute force over the whole 1024 x 1024 grid on a token subset
+        bt = np.sort(np.random.default_rng(wl.seed + 1).choice(wl.T, size=BRUTE, replace=False))
+        bf, bf_sc = O.cartesian_topk_bruteforce(s1r[bt], s2r[bt], wl.k + 1)
+        assert np.array_equal(bf[:, :wl.k], own[bt])   # the two-stage search is exact here
+        check_ids_against_reference(ids[bt], bf[:, :wl.k], bf_sc, wl.k, tau, "brute force: ")
         E = wl.Nr * wl.Nc
+        del s1r, s2r
     del logits, rws
 
     # dispatch over all tokens: bit-exact (atomic experts: the standalone
@@ -112,9 +138,22 @@ def test_fullsize_parity(name):
     ref = O.layer_forward(p, inp["x"], ids_override=ids, tokens=tok)
     got = f64(synth.to_host(out))[tok]
     err = rel_err(got, ref["out"])
-    print(f"  {name}: sampled rel err {err:.2e} over {len(tok)} tokens, "
-          f"dropped {disp['dropped']}, rows {disp['rows']}", flush=True)
+    # the experts alone (no residual), so that x cannot mask the expert path
+    layer.desc.residual = 0
+    moe = layer.forward(x, ws=ws)
+    layer.desc.residual = 1
+    torch.cuda.synchronize()
+    if wl.router == "dense":
+        ref0 = O.combine(inp["x"][tok], ref["shared"], ref["slot_out"], pos[tok], residual=False)
+    else:
+        ref0 = ref["routed"] + (ref["shared"] if ref["shared"] is not None else 0.0)
+    err0 = rel_err(f64(synth.to_host(moe))[tok], ref0)
+    print(f"  {name}: sampled rel err {err:.2e}, experts only {err0:.2e}, over {len(tok)} "
+          f"tokens, dropped {disp['dropped']}, rows {disp['rows']}", flush=True)
+    record(f"full-size {name}", out=err, experts_only=err0, logits=e_l, id_mismatch=n_bad,
+           near_ties=n_near, dropped=int(disp["dropped"]))
     assert err <= TOL["bf16"]
+    assert err0 <= TOL["bf16"]
     if len(gone) and not wl.shared_ffn:
         xb = synth.to_host(x)
         g = np.intersect1d(tok, gone)
