@@ -347,6 +347,27 @@ int moe_dispatch(const int32_t* ids, const float* w, const float* r, const void*
                  void* x_perm, moe_stats* stats, void* ws, size_t ws_bytes,
                  hipStream_t stream);
 
+/* ---- allocation-free dispatch ----
+ * For callers that cannot allocate device memory at all (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same operation, checks, outputs and error codes as moe_dispatch, with the
+ * workspace replaced by a static device array of MOE_NOALLOC_SCRATCH_BYTES
+ * that each GPU the library runs on holds until the process ends (its
+ * address is looked up on the first call on each device).  No call
+ * allocates.  A (T, k, E) whose moe_dispatch_workspace_size exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES returns MOE_EWORKSPACE with a message naming
+ * both sizes (8 MiB covers every dense dispatch with E * ceil(T / 256) below
+ * about two million, and the radix dispatch of up to about 300k slots).
+ * Calls on one GPU share its array: calls that overlap on one GPU (streams
+ * with no ordering between them) race; calls ordered on one stream do not. */
+#define MOE_NOALLOC_SCRATCH_BYTES (8u << 20)
+int moe_dispatch_noalloc(const int32_t* ids, const float* w, const float* r, const void* x,
+                         int dtype, int64_t T, int64_t d, int64_t E, int k, int64_t capacity,
+                         int pad, int64_t rows_max, int32_t* counts, int32_t* offsets,
+                         int32_t* pos, int32_t* row_token, float* row_r, float* row_w,
+                         int32_t* row_expert, void* x_perm, moe_stats* stats,
+                         hipStream_t stream);
+
 /* ---- BCSR topology ("Variable-size experts", sections 3-4) ----
  * From offsets [E+1] (padded to `block`), size_blocks [E] and block_offsets
  * [E+1] build row_offsets [rows_max/block + 1] and column_indices: token

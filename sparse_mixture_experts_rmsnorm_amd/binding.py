@@ -28,8 +28,10 @@ EXPORTED = [
     "moe_expert_workspace_size", "moe_expert_gemm", "moe_shared_workspace_size", "moe_shared_ffn",
     "moe_combine", "moe_layer_workspace_size", "moe_layer_forward", "moe_layer_routing",
     "moe_timer_create", "moe_timer_destroy", "moe_timer_reset", "moe_timer_stage_ms",
-    "moe_layer_backward_workspace_size", "moe_layer_backward",
+    "moe_layer_backward_workspace_size", "moe_layer_backward", "moe_dispatch_noalloc",
 ]
+# size of the static scratch behind moe_dispatch_noalloc (MOE_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 class RouterDesc(C.Structure):
@@ -108,6 +110,8 @@ def lib() -> C.CDLL:
             "moe_dispatch_workspace_size": (SZ, [I64, I, I64]),
             "moe_dispatch": (I, [P, P, P, P, I, I64, I64, I64, I, I64, I, I64, P, P, P, P, P, P, P,
                                  P, P, P, SZ, P]),
+            "moe_dispatch_noalloc": (I, [P, P, P, P, I, I64, I64, I64, I, I64, I, I64, P, P, P, P,
+                                         P, P, P, P, P, P]),
             "moe_topology_nnz_max": (I64, [I64, I, C.POINTER(I64), I64]),
             "moe_build_topology": (I, [P, P, P, I64, I, I64, P, P, P, P]),
             "moe_expert_workspace_size": (SZ, [C.POINTER(ExpertsDesc), I, I64, I64, I, I64]),
@@ -259,6 +263,19 @@ def dispatch(ids, w, r, E, cap, pad, rows_max_, out: dict, x=None, x_perm=None, 
                              ptr(out["row_token"]), ptr(out["row_r"]), ptr(out["row_w"]),
                              ptr(out.get("row_expert")), ptr(x_perm), ptr(stats), ptr(ws), nbytes,
                              stream_handle(stream)))
+
+
+def dispatch_noalloc(ids, w, r, E, cap, pad, rows_max_, out: dict, x=None, x_perm=None,
+                     stats=None, stream=None, dtype=None) -> None:
+    """moe_dispatch_noalloc: moe_dispatch on the library's static scratch."""
+    T, k = ids.shape
+    d = 0 if x is None else x.shape[1]
+    dt = dtype_code(x) if x is not None else (MOE_BF16 if dtype is None else dtype)
+    check(lib().moe_dispatch_noalloc(ptr(ids), ptr(w), ptr(r), ptr(x), dt, T, d, E, k, cap, pad,
+                                     rows_max_, ptr(out["counts"]), ptr(out["offsets"]),
+                                     ptr(out["pos"]), ptr(out["row_token"]), ptr(out["row_r"]),
+                                     ptr(out["row_w"]), ptr(out.get("row_expert")), ptr(x_perm),
+                                     ptr(stats), stream_handle(stream)))
 
 
 def topology_nnz_max(rows_max_: int, block: int, ffn_sizes) -> int:

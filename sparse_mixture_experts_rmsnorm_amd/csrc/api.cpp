@@ -34,6 +34,16 @@ int ok() {
   return MOE_OK;
 }
 
+}  // namespace
+
+// Error reporting for entry points defined in other source files.
+int moe::report_error(int code, const char* msg) {
+  g_err = msg;
+  return code;
+}
+
+namespace {
+
 #define MOE_HIP(call)                                                                   \
   do {                                                                                  \
     hipError_t e_ = (call);                                                             \

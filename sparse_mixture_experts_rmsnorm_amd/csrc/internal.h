@@ -73,6 +73,10 @@ hipError_t launch_combine_split(const void* y0, int nplanes, int64_t rows_max, c
                                 const void* x, const void* shared, int dtype, int64_t T, int64_t d,
                                 int k, void* out, hipStream_t s);
 
+// Sets the message moe_last_error() returns and gives back `code` (for
+// entry points outside api.cpp).
+int report_error(int code, const char* msg);
+
 struct AtomicArgs {
   const void* xhat; int dtype; int64_t T, d; int k; int64_t N;
   const void* W; const void* V; int act;
