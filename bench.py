@@ -40,6 +40,22 @@ TRAFFIC = {
                                                  "common.h"),
         "source_sha256": "7dd4196bd7e6cb9a46e10af9de3f4e07a02af735e1dafa7c55abeb2423ee936c",
         "fetch_kib": 1861829.1, "write_kib": 229417.3},
+    "variable_bcsr_bf16": {
+        "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
+                                                 "common.h"),
+        "source_sha256": "7dd4196bd7e6cb9a46e10af9de3f4e07a02af735e1dafa7c55abeb2423ee936c",
+        "fetch_kib": 36256.0, "write_kib": 35537.5},
+    # the routed first GEMM only (the shared experts' first GEMM is the same
+    # kernel; the dispatches alternate, routed first)
+    "finegrained_bf16": {
+        "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
+                                                 "common.h"),
+        "source_sha256": "7dd4196bd7e6cb9a46e10af9de3f4e07a02af735e1dafa7c55abeb2423ee936c",
+        "fetch_kib": 713819.1, "write_kib": 113959.3},
+    "atomic_bf16": {
+        "kernel": "k_atomic_token", "sources": ("atomic.hip", "common.h"),
+        "source_sha256": "33fc89490ffe0f0aebfb6635519684c32ffa2b3c463f2a628f53c19237805823",
+        "fetch_kib": 535770.9, "write_kib": 16384.0},
     "mixtral_mxfp8": {
         "kernel": "k_gemm_mx", "sources": ("gemm_mx.hip", "gemm_args.h", "gemm_common.h",
                                            "common.h"),
@@ -229,16 +245,21 @@ def time_router_extras(B, wl, layer, x, out, ws, steps):
 
 def time_layer(B, layer, x, out, ws, stats, steps, warmup):
     """W untimed forwards, then K timed ones bracketed by device syncs; the
-    per-stage times come from the library's hipEvents on its own stream."""
+    per-stage times come from the library's hipEvents on its own stream, and
+    an event between consecutive steps on that stream gives each step's time
+    (median and minimum)."""
     import torch
     for _ in range(warmup):
         layer.forward(x, out=out, ws=ws, stats=stats)
     torch.cuda.synchronize()
     timer = B.StageTimer(steps)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
+    ev[0].record()
+    for i in range(steps):
         layer.forward(x, out=out, ws=ws, stats=stats, timer=timer)
+        ev[i + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     stages = {}
@@ -246,7 +267,11 @@ def time_layer(B, layer, x, out, ws, stats, steps, warmup):
         tot, n = timer.stage_ms(s)
         stages[s] = tot / max(n, 1)
     timer.close()
-    return (t1 - t0) * 1e3 / steps, stages
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    step_ms = {"median": per[len(per) // 2] if len(per) % 2 else
+               0.5 * (per[len(per) // 2 - 1] + per[len(per) // 2]),
+               "min": per[0], "max": per[-1], "mean_events": sum(per) / len(per)}
+    return (t1 - t0) * 1e3 / steps, stages, step_ms
 
 
 def time_layer_graph(layer, x, out, ws, stats, steps):
@@ -339,12 +364,12 @@ def mx_variant(B, wl, params, x, steps, warmup):
     ws = layer.alloc_workspace(wq.T)
     out = torch.empty_like(x)
     stats = torch.zeros(4, dtype=torch.int32, device=x.device)
-    ms, stages = time_layer(B, layer, x, out, ws, stats, steps, warmup)
+    ms, stages, step_ms = time_layer(B, layer, x, out, ws, stats, steps, warmup)
     kept, _ = expert_kept(wq, layer, ws)
     f1, f2 = flops_gemm1(wq, kept), flops_gemm2(wq, kept)
     g1, g2 = stages["gemm1"], stages["gemm2"]
     res = {"workload": wq.name, "ms_per_step": ms, "tokens_per_s": wq.T / (ms * 1e-3),
-           "stages_ms": stages, "gemm1_tflops": f1 / (g1 * 1e-3) / 1e12,
+           "step_ms": step_ms, "stages_ms": stages, "gemm1_tflops": f1 / (g1 * 1e-3) / 1e12,
            "gemm2_tflops": f2 / (g2 * 1e-3) / 1e12,
            "frac_fp8_peak": (f1 + f2) / ((g1 + g2) * 1e-3) / 1e12 / PEAK_TFLOPS["mxfp8"],
            "note": "dispatch includes the per-slot MXFP8 quantisation of the gathered rows"}
@@ -353,14 +378,28 @@ def mx_variant(B, wl, params, x, steps, warmup):
     return res
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, params, sample_tokens):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
+    """The oracle, as it stands, on a bounded sample of the same workload, in
+    its float32 work precision (BLAS sgemm with the library's thread pool):
+    one untimed warm-up run, then the median of three timed runs."""
     import numpy as np
     import oracle as O
     from sparse_mixture_experts_rmsnorm_amd import synth
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [os.cpu_count() or 1])
     except Exception:
         threads = os.cpu_count() or 1
     host = {k: synth.to_host(v) for k, v in params.items()}
@@ -378,15 +417,21 @@ def cpu_baseline(wl, params, sample_tokens):
         p.update(quant=wl.quant)
     rng = np.random.default_rng(0)
     tok = np.sort(rng.choice(wl.T, size=min(sample_tokens, wl.T), replace=False))
-    t0 = time.perf_counter()
-    O.layer_forward(p, host["x"], tokens=tok)
-    dt = time.perf_counter() - t0
+    runs = []
+    with O.work_precision(np.float32):
+        for i in range(4):
+            t0 = time.perf_counter()
+            O.layer_forward(p, host["x"], tokens=tok)
+            if i:
+                runs.append(time.perf_counter() - t0)
+    dt = sorted(runs)[1]
     return {"value": len(tok) / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "seconds": dt,
-            "sample": (f"{len(tok)} of {wl.T} tokens through the float64 oracle "
-                       f"(routing, capacity and dispatch over all {wl.T} tokens; expert FFNs, "
-                       f"shared FFN and combine for the sample; weights widened to float64 "
-                       f"inside the timed call)")}
+            "cpu_model": cpu_model(), "precision": "float32 (BLAS sgemm)",
+            "seconds": dt, "runs_s": runs,
+            "sample": (f"{len(tok)} of {wl.T} tokens through the oracle in its float32 work "
+                       f"precision (routing, capacity and dispatch over all {wl.T} tokens; "
+                       f"expert FFNs, shared FFN and combine for the sample; bf16 weights "
+                       f"widened inside the timed call); one warm-up, median of three runs")}
 
 
 def main():
@@ -414,7 +459,8 @@ def main():
     ws = layer.alloc_workspace(wl.T)
     out = torch.empty_like(x)
     stats = torch.zeros(4, dtype=torch.int32, device=dev)
-    ms_per_step, stages = time_layer(B, layer, x, out, ws, stats, args.steps, args.warmup)
+    ms_per_step, stages, step_ms = time_layer(B, layer, x, out, ws, stats, args.steps,
+                                              args.warmup)
     st = stats.cpu().numpy().tolist()
     tokens_per_s = wl.T / (ms_per_step / 1e3)
     dtype = "f32" if wl.dtype == "f32" else ("mxfp8" if wl.quant == "mxfp8" else "bf16")
@@ -428,6 +474,7 @@ def main():
                    "top_k": wl.k, "d_ffn": wl.sizes[0] if wl.sizes else 1, "act": wl.act,
                    "capacity_factor": wl.cf, "expert_kind": wl.expert_kind,
                    "router": wl.router, "shared_ffn": wl.shared_ffn, "quant": wl.quant},
+        "step_ms": step_ms,
         "stages_ms": stages,
         "routing": {"rows": st[0], "dropped": st[1], "max_load": st[2], "errors": st[3]},
     }
@@ -441,16 +488,30 @@ def main():
             "tflops": (f1 + f2) / ((g1 + g2) * 1e-3) / 1e12,
             "frac_peak": (f1 + f2) / ((g1 + g2) * 1e-3) / 1e12 / PEAK_TFLOPS[dtype],
             "gemm1_tflops": a1, "gemm2_tflops": f2 / (g2 * 1e-3) / 1e12}
+        es = 4 if dtype == "f32" else 2
+        epi = "SwiGLU" if wl.act == "swiglu" else "GELU"
         result["roofline"] = {"bound": "mfma", "achieved": a1, "peak": PEAK_TFLOPS[dtype],
                               "unit": "TFLOP/s", "frac": a1 / PEAK_TFLOPS[dtype],
                               "traffic": measured_traffic(wl.name),
                               "traffic_unit": "bytes per launch (HBM, from PMC counters)",
-                              "kernel": ("k_gemm_mx (first expert linear, SwiGLU epilogue, "
+                              "kernel": (f"k_gemm_mx (first expert linear, {epi} epilogue, "
                                          "MXFP8 h)"
                                          if dtype == "mxfp8" else
-                                         "k_gemm_bf16_dma (first expert linear, SwiGLU epilogue)"),
+                                         f"k_gemm_bf16_dma (first expert linear, {epi} epilogue"
+                                         + (", BCSR tile list)" if wl.expert_kind == "bcsr"
+                                            else ")")),
                               "algorithmic_flop_per_launch": f1}
-        es = 4 if dtype == "f32" else 2
+        # the same launch's HBM floor: each expert's weight tile read once, its
+        # rows read once, h written once (kept rows only)
+        mult = 2 if wl.act == "swiglu" else 1
+        g1_bytes = sum(mult * wl.d * f * es + m * (wl.d + f) * es for f, m in zip(wl.sizes, kept)
+                       if m > 0)
+        floor_ms = max(f1 / (PEAK_TFLOPS[dtype] * 1e12), g1_bytes / (PEAK_HBM_GBPS * 1e9)) * 1e3
+        result["roofline"].update({
+            "hbm_bytes_algorithmic": g1_bytes,
+            "hbm_floor_ms": g1_bytes / (PEAK_HBM_GBPS * 1e9) * 1e3,
+            "mfma_floor_ms": f1 / (PEAK_TFLOPS[dtype] * 1e12) * 1e3,
+            "frac_of_floor": floor_ms / g1})
         rows = int(offsets[-1])
         # Algorithmic bytes.  combine: every kept expert row, x read, out written
         # (the layer's own combine also reads the second K-split plane of the
@@ -476,6 +537,33 @@ def main():
                      "out), moe_dispatch with x_perm (token rows read once, kept rows written "
                      "once; its time includes the count / scan / rank index kernels), "
                      "moe_router_topk (x + router weights)")}
+    if wl.expert_kind == "atomic":
+        # the dominant kernel is the atomic experts' row gather (k_atomic_token):
+        # HBM-bound on the W and V rows of the distinct experts the batch draws,
+        # plus the token rows read and the routed rows written
+        es = 2
+        ids = layer.routing(wl.T, ws)["ids"]
+        distinct = int(torch.unique(ids).numel())
+        a_bytes = (2 * distinct + 2 * wl.T) * wl.d * es
+        g1 = stages["gemm1"]
+        ach = a_bytes / (g1 * 1e-3) / 1e9
+        result["roofline"] = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBPS,
+                              "unit": "GB/s", "frac": ach / PEAK_HBM_GBPS,
+                              "traffic": measured_traffic(wl.name),
+                              "traffic_unit": "bytes per launch (HBM, from PMC counters)",
+                              "kernel": "k_atomic_token (atomic experts, W / V row gathers)",
+                              "algorithmic_bytes_per_launch": a_bytes,
+                              "distinct_experts": distinct,
+                              "slot_row_bytes": 2 * wl.T * wl.k * wl.d * es}
+        cf = 2.0 * wl.T * wl.d * (wl.Nr + wl.Nc)
+        result["router_gemm"] = {"tflop": cf / 1e12, "stage_ms": stages["router"],
+                                 "note": "Cartesian score GEMM plus the three top-32 selections"}
+    if wl.shared_ffn:
+        sf = 2.0 * wl.T * wl.d * wl.shared_ffn * (3 if wl.shared_act == "swiglu" else 2)
+        result["shared_gemm"] = {"tflop": sf / 1e12, "ms": stages["shared"],
+                                 "tflops": sf / (stages["shared"] * 1e-3) / 1e12,
+                                 "frac_peak": sf / (stages["shared"] * 1e-3) / 1e12
+                                 / PEAK_TFLOPS["bf16"]}
     if (args.vendor_gemm and wl.expert_kind == "grouped" and wl.dtype == "bf16"
             and wl.quant == "none" and len(set(wl.sizes)) == 1):
         result["vendor_gemm"] = vendor_gemm(wl, kept, stages, args.steps)

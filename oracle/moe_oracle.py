@@ -57,6 +57,7 @@ float64 oracle is the check for the floating-point outputs.
 """
 from __future__ import annotations
 
+import contextlib
 import math
 from fractions import Fraction
 
@@ -64,7 +65,7 @@ import numpy as np
 from scipy.special import erf
 
 __all__ = [
-    "bf16_to_f64", "f64_to_bf16_bits", "as_f64",
+    "bf16_to_f64", "f64_to_bf16_bits", "as_f64", "work_precision",
     "capacity", "rmsnorm_scale", "rmsnorm", "router_logits", "router_logits_unfused",
     "E4M3_MAX", "MX_BLOCK", "e4m3_decode", "e4m3_round", "e4m3_encode", "mx_quantize",
     "mx_dequantize", "mx_qdq", "ffn_mxfp8",
@@ -119,6 +120,44 @@ def as_f64(a) -> np.ndarray | None:
     return a.astype(np.float64)
 
 
+# Work precision of the forward pass's floating-point arithmetic.  Every
+# test runs the default, float64.  work_precision(np.float32) switches the
+# products and sums of the forward (RMSNorm, router, expert and shared FFNs,
+# Cartesian scores, atomic experts, combine) to float32 -- the precision the
+# benchmark's CPU baseline is timed in; the definitions are the same, and the
+# integer decisions (top-k, capacity, dispatch) and the MXFP8 quantiser keep
+# their own precision.
+_WORK = [np.float64]
+
+
+@contextlib.contextmanager
+def work_precision(dtype):
+    """Run the enclosed forward-pass calls in `dtype` (np.float32 or np.float64)."""
+    if dtype not in (np.float32, np.float64):
+        raise ValueError("work precision must be float32 or float64")
+    prev = _WORK[0]
+    _WORK[0] = dtype
+    try:
+        yield
+    finally:
+        _WORK[0] = prev
+
+
+def _wd():
+    return _WORK[0]
+
+
+def _aw(a) -> np.ndarray | None:
+    """An input tensor in the work precision: uint16 means bf16 bits (widened
+    exactly), else a float."""
+    if a is None:
+        return None
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(_wd())
+    return a.astype(_wd())
+
+
 # --------------------------------------------------------------------------
 # [GLOSS] expert capacity
 # --------------------------------------------------------------------------
@@ -151,22 +190,22 @@ def rmsnorm_scale(x: np.ndarray, eps: float) -> np.ndarray:
     [CODA]: the normalisation is a per-row scale by this statistic, which is
     what gets commuted across the following GEMM into its epilogue.
     """
-    x = as_f64(x)
+    x = _aw(x)
     return 1.0 / np.sqrt(np.mean(x * x, axis=1) + eps)
 
 
 def rmsnorm(x: np.ndarray, gamma, eps: float) -> np.ndarray:
     """Unfused RMSNorm output x * r[:,None] * gamma (the textbook form)."""
-    x = as_f64(x)
+    x = _aw(x)
     r = rmsnorm_scale(x, eps)
     y = x * r[:, None]
-    g = as_f64(gamma)
+    g = _aw(gamma)
     return y if g is None else y * g[None, :]
 
 
 def _xhat(x, gamma):
-    x = as_f64(x)
-    g = as_f64(gamma)
+    x = _aw(x)
+    g = _aw(gamma)
     return x if g is None else x * g[None, :]
 
 
@@ -178,18 +217,18 @@ def router_logits(x, gamma, r, w_router, bias=None) -> np.ndarray:
     right before the top-k.  ([GLOSS] gating network: a linear layer giving
     one logit per expert.)
     """
-    acc = _xhat(x, gamma) @ as_f64(w_router)
-    logits = np.asarray(r, dtype=np.float64)[:, None] * acc
+    acc = _xhat(x, gamma) @ _aw(w_router)
+    logits = np.asarray(r, dtype=_wd())[:, None] * acc
     if bias is not None:
-        logits = logits + as_f64(bias)[None, :]
+        logits = logits + _aw(bias)[None, :]
     return logits
 
 
 def router_logits_unfused(x, gamma, eps, w_router, bias=None) -> np.ndarray:
     """The same logits the textbook way: RMSNorm first, then the GEMM."""
-    logits = rmsnorm(x, gamma, eps) @ as_f64(w_router)
+    logits = rmsnorm(x, gamma, eps) @ _aw(w_router)
     if bias is not None:
-        logits = logits + as_f64(bias)[None, :]
+        logits = logits + _aw(bias)[None, :]
     return logits
 
 
@@ -490,20 +529,27 @@ def bcsr_topology(offsets, size_blocks, block_offsets, block: int = 128) -> dict
 # activations and FFNs
 # --------------------------------------------------------------------------
 
+def _float(z) -> np.ndarray:
+    """z as a float array: float32 stays float32 (the float32 work
+    precision), everything else becomes float64."""
+    z = np.asarray(z)
+    return z if z.dtype == np.float32 else z.astype(np.float64)
+
+
 def gelu(z):
     """Exact GELU: z * Phi(z) = z/2 * (1 + erf(z/sqrt 2))."""
-    z = np.asarray(z, dtype=np.float64)
+    z = _float(z)
     return 0.5 * z * (1.0 + erf(z / math.sqrt(2.0)))
 
 
 def gelu_tanh(z):
     """tanh approximation of GELU."""
-    z = np.asarray(z, dtype=np.float64)
+    z = _float(z)
     return 0.5 * z * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (z + 0.044715 * z ** 3)))
 
 
 def silu(z):
-    z = np.asarray(z, dtype=np.float64)
+    z = _float(z)
     return z / (1.0 + np.exp(-z))
 
 
@@ -519,8 +565,8 @@ def ffn(xhat, r, w1, w2, act: str, w3=None, faithful: bool = False):
     With faithful=True the hidden activation is rounded to bf16, the storage
     point of the bf16 path.
     """
-    xhat = np.asarray(xhat, dtype=np.float64)
-    r = np.asarray(r, dtype=np.float64)[:, None]
+    xhat = np.asarray(xhat, dtype=_wd())
+    r = np.asarray(r, dtype=_wd())[:, None]
     a = r * (xhat @ w1)
     if act == "swiglu":
         h = silu(a) * (r * (xhat @ w3))
@@ -559,17 +605,17 @@ def grouped_expert_ffn(xhat_rows, r_rows, e_of_row, w1, w2, f_offsets, act,
     slices of experts that have rows are widened to float64.
     """
     d = np.asarray(w2).shape[1]
-    out = np.zeros((len(e_of_row), d), dtype=np.float64)
+    out = np.zeros((len(e_of_row), d), dtype=_wd())
     for e in np.unique(e_of_row):
         m = e_of_row == e
         lo, hi = int(f_offsets[e]), int(f_offsets[e + 1])
-        w3e = None if w3 is None else as_f64(np.asarray(w3)[:, lo:hi])
+        w3e = None if w3 is None else _aw(np.asarray(w3)[:, lo:hi])
         if quant == "mxfp8":
-            out[m] = ffn_mxfp8(xhat_rows[m], r_rows[m], as_f64(np.asarray(w1)[:, lo:hi]),
-                               as_f64(np.asarray(w2)[lo:hi, :]), act, w3e)
+            out[m] = ffn_mxfp8(xhat_rows[m], r_rows[m], _aw(np.asarray(w1)[:, lo:hi]),
+                               _aw(np.asarray(w2)[lo:hi, :]), act, w3e)
         else:
-            out[m] = ffn(xhat_rows[m], r_rows[m], as_f64(np.asarray(w1)[:, lo:hi]),
-                         as_f64(np.asarray(w2)[lo:hi, :]), act, w3e, faithful)
+            out[m] = ffn(xhat_rows[m], r_rows[m], _aw(np.asarray(w1)[:, lo:hi]),
+                         _aw(np.asarray(w2)[lo:hi, :]), act, w3e, faithful)
     return out
 
 
@@ -613,8 +659,8 @@ def cartesian_scores(x, gamma, r, k_rows, k_cols):
     the Nc column keys; expert n = i*Nc + j scores s1[i] + s2[j].
     """
     xh = _xhat(x, gamma)
-    r = np.asarray(r, dtype=np.float64)[:, None]
-    return r * (xh @ as_f64(k_rows)), r * (xh @ as_f64(k_cols))
+    r = np.asarray(r, dtype=_wd())[:, None]
+    return r * (xh @ _aw(k_rows)), r * (xh @ _aw(k_cols))
 
 
 def _topk_lex(v: np.ndarray, k: int) -> np.ndarray:
@@ -671,17 +717,17 @@ def atomic_experts_token_centric(xhat, r, ids, g, W, V, act="gelu"):
 
     For token t, its k atomic experts' rows W[n], V[n] are gathered into a
     token-specific block; routed[t] = sum_j g[t,j] * act(r_t * xhat_t.W[n_j]) * V[n_j].
-    Only the gathered rows are widened to float64.
+    Only the gathered rows are widened (to the work precision).
     """
-    xhat = np.asarray(xhat, dtype=np.float64)
-    r = np.asarray(r, dtype=np.float64)
+    xhat = np.asarray(xhat, dtype=_wd())
+    r = np.asarray(r, dtype=_wd())
     T = xhat.shape[0]
-    out = np.zeros((T, np.asarray(V).shape[1]), dtype=np.float64)
+    out = np.zeros((T, np.asarray(V).shape[1]), dtype=_wd())
     f = _act(act)
     for t in range(T):
-        Wt = as_f64(np.asarray(W)[ids[t]])      # [k, d] assembled block
-        Vt = as_f64(np.asarray(V)[ids[t]])
-        a = np.asarray(g[t], dtype=np.float64) * f(r[t] * (Wt @ xhat[t]))
+        Wt = _aw(np.asarray(W)[ids[t]])      # [k, d] assembled block
+        Vt = _aw(np.asarray(V)[ids[t]])
+        a = np.asarray(g[t], dtype=_wd()) * f(r[t] * (Wt @ xhat[t]))
         out[t] = a @ Vt
     return out
 
@@ -730,7 +776,7 @@ def combine(x, shared, slot_out, pos, residual=True):
     contribute nothing, so a token with every slot dropped returns x (or 0
     without the residual) -- [GLOSS] capacity: dropped tokens pass through.
     """
-    x = as_f64(x)
+    x = _aw(x)
     T, d = x.shape
     out = x.copy() if residual else np.zeros_like(x)
     if shared is not None:
@@ -743,8 +789,8 @@ def combine(x, shared, slot_out, pos, residual=True):
 
 def _shared_ffn(xh, r, p, faithful):
     act = p.get("shared_act", "swiglu" if p.get("ws3") is not None else "gelu")
-    return ffn(xh, r, as_f64(p["ws1"]), as_f64(p["ws2"]), act,
-               as_f64(p.get("ws3")), faithful)
+    return ffn(xh, r, _aw(p["ws1"]), _aw(p["ws2"]), act,
+               _aw(p.get("ws3")), faithful)
 
 
 def layer_forward(p: dict, x, ids_override=None, tokens=None, faithful=False) -> dict:
@@ -763,7 +809,7 @@ def layer_forward(p: dict, x, ids_override=None, tokens=None, faithful=False) ->
     faithful=True rounds h, the gated expert outputs, the shared output and
     the layer output to bf16 at the storage points of the bf16 path.
     """
-    x64 = as_f64(x)
+    x64 = _aw(x)
     T, d = x64.shape
     k = int(p["k"])
     eps = float(p["eps"])
@@ -812,7 +858,7 @@ def layer_forward(p: dict, x, ids_override=None, tokens=None, faithful=False) ->
     foff = np.asarray(p["f_offsets"], dtype=np.int64)
     act = p["act"]
     pos = disp["pos"][tok]
-    slot_out = np.zeros((len(tok), k, d), dtype=np.float64)
+    slot_out = np.zeros((len(tok), k, d), dtype=_wd())
     tt, jj = np.nonzero(pos >= 0)
     if len(tt):
         e_rows = np.asarray(ids)[tok[tt], jj].astype(np.int64)

@@ -841,3 +841,41 @@ def test_backward_token_subset_and_unit_slices_agree_with_the_whole():
         assert np.allclose(u["dw1"], full["dw1"][:, cols], rtol=1e-12, atol=1e-14)
         assert np.allclose(u["dw3"], full["dw3"][:, cols], rtol=1e-12, atol=1e-14)
         assert np.allclose(u["dw2"], full["dw2"][cols, :], rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------- work precision
+
+@pytest.mark.parametrize("kind", ["dense_swiglu_shared", "cartesian_atomic"])
+def test_float32_work_precision_matches_float64(kind):
+    """The float32 work precision (used only to time the CPU baseline) computes
+    the same layer: outputs within float32 rounding of the float64 default,
+    the same routing except at near-ties, and float64 is the default."""
+    rng = _rng(41)
+    T, d = 40, 64
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    if kind == "dense_swiglu_shared":
+        E, f, k = 6, 96, 2
+        p = dict(k=k, eps=1e-6, renorm=1, cf=1.0, act="swiglu", residual=True, pad=1,
+                 router="dense", w_router=0.1 * rng.standard_normal((d, E)), bias=None,
+                 w1=0.1 * rng.standard_normal((d, E * f)), w3=0.1 * rng.standard_normal((d, E * f)),
+                 w2=0.1 * rng.standard_normal((E * f, d)), f_offsets=[f * e for e in range(E + 1)],
+                 ws1=0.1 * rng.standard_normal((d, 64)), ws3=0.1 * rng.standard_normal((d, 64)),
+                 ws2=0.1 * rng.standard_normal((64, d)), shared_act="swiglu")
+    else:
+        Nr = Nc = 16
+        k = 8
+        p = dict(k=k, eps=1e-6, renorm=1, act="gelu", residual=True, router="cartesian",
+                 k_rows=0.2 * rng.standard_normal((d, Nr)), k_cols=0.2 * rng.standard_normal((d, Nc)),
+                 W=0.2 * rng.standard_normal((Nr * Nc, d)), V=0.2 * rng.standard_normal((Nr * Nc, d)),
+                 ws1=0.1 * rng.standard_normal((d, 64)), ws2=0.1 * rng.standard_normal((64, d)),
+                 shared_act="gelu")
+    p = {key: (v.astype(np.float32) if isinstance(v, np.ndarray) else v) for key, v in p.items()}
+    ref = O.layer_forward(p, x)
+    assert ref["out"].dtype == np.float64
+    with O.work_precision(np.float32):
+        got = O.layer_forward(p, x)
+    assert got["out"].dtype == np.float32
+    assert O.layer_forward(p, x)["out"].dtype == np.float64       # restored on exit
+    err = np.max(np.abs(got["out"] - ref["out"])) / np.max(np.abs(ref["out"]))
+    assert err < 1e-5, err
+    assert np.array_equal(got["ids"], ref["ids"])
