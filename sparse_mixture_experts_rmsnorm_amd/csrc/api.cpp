@@ -200,7 +200,13 @@ struct ExpertWs {
   void* h = nullptr;
   Tile* tiles1 = nullptr;
   Tile* tiles2 = nullptr;
-  int* nt = nullptr;   // [2]
+  int* nt = nullptr;   // [32]: the first list's counts at nt, the second's at nt + 16
+  // bf16 persistent launches: workgroups of each GEMM (the plans cut the last
+  // round's tiles into K pieces for exactly this grid), fp32 partials of the
+  // pieces and the list entry of each split tile (grid1 + grid2 ints)
+  int grid1 = 0, grid2 = 0;
+  float* part = nullptr;
+  int* counters = nullptr;
   float* a_rows = nullptr;
   int64_t mt1 = 0, mt2 = 0;
   int ksplit = 1;        // K parts of the second linear (1, 2 or 4)
@@ -272,9 +278,23 @@ void carve_expert_ws(Carve& c, const ExpertGeo& g, int dtype, int64_t d, int64_t
     w->a_rows = c.take_n<float>(rows_max);
     return;
   }
+  // bf16 experts whose second linear needs its K split to fill the last
+  // round of tiles (ksplit > 1) cut only that round's tiles into K pieces,
+  // summed in fp32 by the fixup kernel, instead of splitting every tile into
+  // partial planes that combine adds (measured: the same balance with one
+  // quarter of the partial traffic and a single rounding of y).  Elsewhere
+  // the pieces' partial stores and fixup cost more than the idle compute
+  // units of the last round.
+  const bool pieces = dtype == MOE_BF16 && !g.mx && ksplit > 1;
+  if (pieces) ksplit = 1;
   w->ksplit = ksplit;
   w->mt1 = std::max<int64_t>(1, max_tiles_gemm1(g, rows_max, nnz_max));
   w->mt2 = std::max<int64_t>(1, max_tiles_gemm2(g, d, rows_max) * ksplit);
+  if (pieces) {
+    w->grid2 = gemm_persistent_grid(int(std::min<int64_t>(w->mt2, 1 << 30)));
+    w->part = c.take_n<float>(int64_t(w->grid2) * g.bf2 * g.bt2);
+    w->counters = c.take_n<int>(w->grid2);
+  }
   if (ksplit > 1) {
     w->plane = rows_max * d;
     w->ypart = c.take(size_t(ksplit * w->plane) * esize(dtype));
@@ -295,9 +315,10 @@ void carve_expert_ws(Carve& c, const ExpertGeo& g, int dtype, int64_t d, int64_t
     w->ldpre = g.pf * g.Fmax;
     w->pre = c.take(size_t(rows_max) * w->ldpre * esize(dtype));
   }
-  w->tiles1 = c.take_n<Tile>(w->mt1);
-  w->tiles2 = c.take_n<Tile>(w->mt2);
-  w->nt = c.take_n<int>(2);
+  // a plan for a persistent grid adds at most one entry per workgroup
+  w->tiles1 = c.take_n<Tile>(w->mt1 + w->grid1);
+  w->tiles2 = c.take_n<Tile>(w->mt2 + w->grid2);
+  w->nt = c.take_n<int>(32);
 }
 
 // Launch the two expert GEMMs of a grouped / BCSR expert set over the rows of
@@ -368,7 +389,7 @@ int run_expert_gemms_mx(const moe_experts_desc* X, const ExpertGeo& g, int64_t d
   b.g.W = X->w2_t;
   b.g.ldw = g.F;
   b.g.tiles = w.tiles2;
-  b.g.ntiles = w.nt + 1;
+  b.g.ntiles = w.nt + 16;
   b.g.Y = y;
   b.g.ldy = d;
   b.g.row_w = row_w;
@@ -418,6 +439,9 @@ int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, i
   p.tiles = w.tiles1;
   p.ntiles = w.nt;
   p.max_tiles = int(w.mt1);
+  p.grid = w.grid1;
+  p.max_parts = 4;
+  p.counters = nullptr;
   // second linear
   PlanArgs p2 = p;
   p2.gemm = 2;
@@ -425,10 +449,12 @@ int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, i
   p2.fold = 1;
   p2.dense_n = int(d);
   p2.tiles = w.tiles2;
-  p2.ntiles = w.nt + 1;
+  p2.ntiles = w.nt + 16;
   p2.max_tiles = int(w.mt2);
   p2.ksplit = w.ksplit;
   p2.bt = g.bt2;
+  p2.grid = w.grid2;
+  p2.counters = w.counters;
   MOE_HIP(launch_plan_pair(p, p2, s));
   timer_mark(timer, call, MOE_STAGE_PLAN + 1, s);
 
@@ -451,7 +477,11 @@ int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, i
   a.act = X->act == MOE_ACT_GELU_TANH ? 1 : 0;
   a.pre = w.pre;
   a.ldpre = w.ldpre;
-  MOE_HIP(launch_gemm(dtype, a, g.bf1, g.bt, int(w.mt1), s));
+  a.xcd_runs = w.grid1 > 0;
+  a.part = w.part;
+  a.counters = w.counters;
+  MOE_HIP(launch_gemm(dtype, a, g.bf1, g.bt, w.grid1 > 0 ? w.grid1 : int(w.mt1), s));
+  if (w.grid1 > 0) MOE_HIP(launch_piece_fixup(a, g.bf1, g.bt, w.grid1, s));
   timer_mark(timer, call, MOE_STAGE_GEMM1 + 1, s);
 
   GemmArgs b{};
@@ -460,7 +490,7 @@ int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, i
   b.W = X->w2_t;
   b.ldw = g.F;
   b.tiles = w.tiles2;
-  b.ntiles = w.nt + 1;
+  b.ntiles = w.nt + 16;
   b.Y = y;
   b.ldy = d;
   b.row_r = nullptr;
@@ -471,7 +501,11 @@ int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, i
     b.Y = w.ypart;
     b.ysplit = w.plane;
   }
-  MOE_HIP(launch_gemm(dtype, b, g.bf2, g.bt2, int(w.mt2), s));
+  b.xcd_runs = w.grid2 > 0;
+  b.part = w.part;
+  b.counters = w.counters;
+  MOE_HIP(launch_gemm(dtype, b, g.bf2, g.bt2, w.grid2 > 0 ? w.grid2 : int(w.mt2), s));
+  if (w.grid2 > 0) MOE_HIP(launch_piece_fixup(b, g.bf2, g.bt2, w.grid2, s));
   timer_mark(timer, call, MOE_STAGE_GEMM2 + 1, s);
   return MOE_OK;
 }
@@ -1045,7 +1079,8 @@ void carve_layer(Carve& c, const moe_layer_desc* L, int64_t T, const ExpertGeo& 
   const int64_t rows_est = std::min(T * k, E * std::min(w->cap, T));
   const int ks = choose_ksplit(g, L->dtype, d, rows_est);
   carve_expert_ws(c, g, L->dtype, d, w->rows_max, nnz_max, &w->ex, ks, L->save_for_backward != 0);
-  w->y = ks > 1 ? nullptr : c.take(size_t(g.atomic ? T : w->rows_max) * d * es);
+  // y_perm in one plane unless the second linear writes K-split planes
+  w->y = w->ex.ksplit > 1 ? nullptr : c.take(size_t(g.atomic ? T : w->rows_max) * d * es);
   if (L->shared) {
     carve_expert_ws(c, gs, L->dtype, d, T, 0, &w->sh, 1, L->save_for_backward != 0);
     w->s = c.take(size_t(T) * d * es);

@@ -273,7 +273,7 @@ __global__ void __launch_bounds__(1024) k_plan_wgrad(WgradPlanArgs p) {
     const int xb = p.xfix > 0 ? 0 : p.xmul * p.foff[u];
     const int mb = n / nf, cb = n - mb * nf;
     const int rows = p.offsets ? p.offsets[u + 1] - p.offsets[u] : p.dense_rows;
-    Tile t;
+    Tile t{};
     t.expert = u;
     t.spare = 0;
     t.row0 = xb + mb * bt;

@@ -178,6 +178,71 @@ __device__ __forceinline__ void epilogue_f32_lds(const GemmArgs& a, const Tile& 
   }
 }
 
+// K pieces of a split tile.  Each piece stores its fp32 partial sums at its
+// slot of the partial buffer in fragment order (block (i, j) of wave w at
+// ((w MF + i) MT + j) 1024 + 16 lane floats), so that the lane of the fixup
+// kernel that reads them back holds exactly the values the same lane of a
+// whole tile would.  No workgroup waits for another: the fixup kernel runs
+// after the GEMM on the same stream.
+template <int BF, int BT, int MF, int MT>
+__device__ __forceinline__ int64_t piece_frag_offset(int wid, int lane, int i, int j) {
+  return int64_t(wid) * (MF * MT * 1024) + (i * MT + j) * 1024 + lane * 16;
+}
+
+template <int BF, int BT, int MF, int MT>
+__device__ __forceinline__ void store_piece(const GemmArgs& a, const Tile& tile,
+                                            const f32x16 (&acc)[MF][MT], int wid, int lane) {
+  float* const dst0 = a.part + (int64_t(tile.pslot0) + tile.part) * (int64_t(BF) * BT);
+#pragma unroll
+  for (int i = 0; i < MF; ++i)
+#pragma unroll
+    for (int j = 0; j < MT; ++j) {
+      f32x4* dst = reinterpret_cast<f32x4*>(dst0 + piece_frag_offset<BF, BT, MF, MT>(wid, lane, i, j));
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        dst[v] = f32x4{acc[i][j][4 * v], acc[i][j][4 * v + 1], acc[i][j][4 * v + 2],
+                       acc[i][j][4 * v + 3]};
+    }
+}
+
+// Fixup of split tiles: workgroup g sums the nparts partials of split tile g
+// in part order (part 0 first: the same fp32 sum every run) and applies the
+// tile's epilogue.  group_tile[g] is the list entry of the tile's part 0;
+// a.ntiles[10] holds the number of split tiles.
+template <int BF, int BT, int WGF, int WGT, int EPI>
+__global__ void __launch_bounds__(64 * WGF * WGT) k_piece_fixup(GemmArgs a) {
+  constexpr int WTF = BF / WGF, WTT = BT / WGT;
+  constexpr int MF = WTF / 32, MT = WTT / 32;
+  const int g = blockIdx.x;
+  if (g >= a.ntiles[10]) return;
+  const Tile tile = a.tiles[a.counters[g]];
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wt = wid / WGF, wf = wid % WGF;
+  const int fr = lane & 31, fh = lane >> 5;
+  const float* const src0 = a.part + int64_t(tile.pslot0) * (int64_t(BF) * BT);
+  f32x16 acc[MF][MT];
+#pragma unroll
+  for (int i = 0; i < MF; ++i)
+#pragma unroll
+    for (int j = 0; j < MT; ++j) {
+      for (int pt = 0; pt < tile.nparts; ++pt) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(
+            src0 + int64_t(pt) * (int64_t(BF) * BT) + piece_frag_offset<BF, BT, MF, MT>(wid, lane, i, j));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 w = src[q];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (pt == 0) acc[i][j][4 * q + e] = w[e];
+            else acc[i][j][4 * q + e] += w[e];
+          }
+        }
+      }
+    }
+  gemm_epilogue<BF, BT, WGF, WGT, EPI>(a, tile, acc, wf, wt, fr, fh);
+}
+
 // ---------------------------------------------------------------- bf16 MFMA GEMM, LDS-DMA ring
 
 // BF features x BT rows per workgroup, WGF x WGT waves, each wave a
@@ -216,10 +281,18 @@ __global__ void __launch_bounds__(64 * WGF * WGT, 1) k_gemm_bf16_dma(GemmArgs a)
   // The first loads of the next tile are issued before this tile's
   // epilogue, so their latency hides behind the epilogue's arithmetic and
   // stores.
-  const int nt = *a.ntiles;
+  // The tile list either follows the XCD remap of list index tb = b, b + G,
+  // ... (remap_xcd), or, planned for this grid (xcd_runs), gives each XCD's
+  // run explicitly: entries base[x] + slot, + S, ... with x = b % NX.
+  const int nt = a.ntiles[0];
   const int G = gridDim.x;
-  int tb = blockIdx.x;
-  if (tb >= nt) return;
+  const int NX = a.xcd_runs && G % 8 == 0 ? 8 : 1;
+  const int S = G / NX;
+  const int run_end = a.xcd_runs ? a.ntiles[2 + int(blockIdx.x) % NX] : nt;
+  int tb = a.xcd_runs ? a.ntiles[1 + int(blockIdx.x) % NX] + int(blockIdx.x) / NX : int(blockIdx.x);
+  const int step = a.xcd_runs ? S : G;
+  auto list_index = [&](int i) { return a.xcd_runs ? i : remap_xcd(i, nt); };
+  if (tb >= run_end) return;
   const int tid = threadIdx.x, lane = tid & 63;
   // wave-uniform (the LDS destinations of the DMA are then scalar arithmetic)
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -239,7 +312,7 @@ __global__ void __launch_bounds__(64 * WGF * WGT, 1) k_gemm_bf16_dma(GemmArgs a)
   auto set_sources = [&](const Tile& t) {
     const int xlast = t.row_end - 1;
     // a K-split tile reads its own part of the activation row
-    const int xk0 = (EPI == EPI_GATE_SPLIT || EPI == EPI_SCALE_F32) ? t.spare * t.klen : 0;
+    const int xk0 = ((EPI == EPI_GATE_SPLIT || EPI == EPI_SCALE_F32) ? t.spare * t.klen : 0) + t.xk;
 #pragma unroll
     for (int u = 0; u < SPW; ++u) {
       const int row = (wid * SPW + u) * RSEG + srow;
@@ -283,7 +356,7 @@ __global__ void __launch_bounds__(64 * WGF * WGT, 1) k_gemm_bf16_dma(GemmArgs a)
     issue_w(min(2, nk - 1), 2);
   };
 
-  Tile tile = a.tiles[remap_xcd(tb, nt)];
+  Tile tile = a.tiles[list_index(tb)];
   int nk = tile.klen / BKD;
   set_sources(tile);
   if (nk > 0) prologue(nk);
@@ -401,8 +474,8 @@ __global__ void __launch_bounds__(64 * WGF * WGT, 1) k_gemm_bf16_dma(GemmArgs a)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    const int tn = tb + G;
-    const bool more = tn < nt;
+    const int tn = tb + step;
+    const bool more = tn < run_end;
     Tile next = tile;
     int nk2 = 0;
     if constexpr (EPI == EPI_SCALE_F32 && WGT == 2 && BT == 256) {
@@ -413,13 +486,24 @@ __global__ void __launch_bounds__(64 * WGF * WGT, 1) k_gemm_bf16_dma(GemmArgs a)
       if (!more) break;
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      next = a.tiles[remap_xcd(tn, nt)];
+      next = a.tiles[list_index(tn)];
       nk2 = next.klen / BKD;
       set_sources(next);
       if (nk2 > 0) prologue(nk2);
+    } else if (tile.nparts > 1) {
+      // a K piece: its partial sums go to the partial buffer, and the fixup
+      // kernel applies the epilogue to the sum of the tile's pieces
+      if (more) {
+        next = a.tiles[list_index(tn)];
+        nk2 = next.klen / BKD;
+        set_sources(next);
+        if (nk2 > 0) prologue(nk2);
+      }
+      store_piece<BF, BT, MF, MT>(a, tile, acc, wid, lane);
+      if (!more) break;
     } else {
       if (more) {
-        next = a.tiles[remap_xcd(tn, nt)];
+        next = a.tiles[list_index(tn)];
         nk2 = next.klen / BKD;
         set_sources(next);
         if (nk2 > 0) prologue(nk2);
@@ -593,11 +677,69 @@ __device__ __forceinline__ void plan_tiles(const PlanArgs& p) {
   }
   __syncthreads();
   const int ntot = int(min<long long>(total, p.max_tiles));
-  if (threadIdx.x == 0) *p.ntiles = ntot;
-  for (int idx = threadIdx.x; idx < ntot; idx += blockDim.x) {
+  // Persistent launch of p.grid workgroups: the XCD remap gives each XCD a
+  // contiguous run of the list, run S = grid / NX tiles at a time.  The
+  // run's last round holds r = q % S tiles and leaves S - r compute units
+  // idle for a whole tile; its r tiles are cut along K into P = S / r pieces
+  // (at most max_parts), so the last round takes about 1 / P of a tile.
+  __shared__ int xfirst_s[8], xfull_s[8], xp_s[8], xout_s[9], xgrp_s[8], xpc_s[8];
+  int nout = ntot;
+  const int NX = p.grid > 0 && p.grid % 8 == 0 ? 8 : 1;
+  if (p.grid > 0) {
+    const int S = p.grid / NX;
+    if (threadIdx.x == 0) {
+      const int q = ntot / NX, rem = ntot % NX;
+      int out = 0, grp = 0, pcs = 0;
+      for (int x = 0; x < NX; ++x) {
+        const int qx = q + (x < rem ? 1 : 0);
+        int r = qx % S;
+        int P = r > 0 ? min(p.max_parts, S / r) : 1;
+        if (P < 2) {
+          P = 1;
+          r = 0;
+        }
+        xfirst_s[x] = x * q + min(x, rem);
+        xfull_s[x] = qx - r;
+        xp_s[x] = P;
+        xout_s[x] = out;
+        xgrp_s[x] = grp;
+        xpc_s[x] = pcs;
+        out += (qx - r) + r * P;
+        if (P > 1) {
+          grp += r;
+          pcs += r * P;
+        }
+      }
+      xout_s[NX] = out;
+      p.ntiles[0] = out;
+      for (int x = 0; x <= NX; ++x) p.ntiles[1 + x] = xout_s[x];
+      p.ntiles[10] = grp;
+    }
+    __syncthreads();
+    nout = xout_s[NX];
+  } else if (threadIdx.x == 0) {
+    *p.ntiles = ntot;
+  }
+  for (int o = threadIdx.x; o < nout; o += blockDim.x) {
+    int idx = o, part = 0, nparts = 1, group = 0, pslot0 = 0;
+    if (p.grid > 0) {
+      int x = 0;
+      while (x + 1 < NX && xout_s[x + 1] <= o) ++x;
+      const int local = o - xout_s[x];
+      if (local < xfull_s[x]) {
+        idx = xfirst_s[x] + local;
+      } else {
+        const int j = local - xfull_s[x], P = xp_s[x], gl = j / P;
+        part = j - gl * P;
+        nparts = P;
+        idx = xfirst_s[x] + xfull_s[x] + gl;
+        group = xgrp_s[x] + gl;
+        pslot0 = xpc_s[x] + gl * P;
+      }
+    }
     const int u = upper_bound_i(base_s, nunits + 1, idx) - 1;
     const int n = idx - base_s[u];
-    Tile t;
+    Tile t{};
     t.spare = 0;
     if (dense) {
       const int mt = (p.dense_rows + p.bt - 1) / p.bt;
@@ -668,7 +810,19 @@ __device__ __forceinline__ void plan_tiles(const PlanArgs& p) {
         t.ocol0 = nf * p.bf;
       }
     }
-    p.tiles[idx] = t;
+    t.part = part;
+    t.nparts = nparts;
+    t.pslot0 = pslot0;
+    if (nparts > 1 && part == 0) p.counters[group] = o;
+    if (nparts > 1) {
+      // whole 64-wide K stages: part j takes stages [j nk / P, (j + 1) nk / P)
+      const int nk = t.klen / 64;
+      const int k0 = part * nk / nparts, k1 = (part + 1) * nk / nparts;
+      t.kofs += k0 * 64;
+      t.xk = k0 * 64;
+      t.klen = (k1 - k0) * 64;
+    }
+    p.tiles[o] = t;
   }
 }
 
@@ -744,7 +898,7 @@ hipError_t launch_plan_pair(const PlanArgs& p0, const PlanArgs& p1, hipStream_t 
 // LDS ring fills a CU), in a multiple of 8 so that each keeps to one XCD's
 // tiles.  (With a grid of one workgroup per tile the kernel's tile loop runs
 // once.)
-static int persistent_grid(int grid) {
+int gemm_persistent_grid(int grid) {
   static thread_local int dev_cached = -1, cus = 256;
   int dev = 0;
   if (hipGetDevice(&dev) == hipSuccess && dev != dev_cached) {
@@ -762,7 +916,7 @@ hipError_t launch_gemm(int dtype, const GemmArgs& a, int bf, int bt, int grid, h
   // also covers this tile's stores (vmcnt counts both), which costs more than
   // it saves when a tile stores 256 KB of fp32 (the backward's EPI_SCALE_F32
   // ran 4% slower persistent) or bf16 rows of the backward's EPI_STORE_T.
-  if (dtype != 0 && a.epi != EPI_SCALE_F32 && a.epi != EPI_STORE_T) grid = persistent_grid(grid);
+  if (dtype != 0 && a.epi != EPI_SCALE_F32 && a.epi != EPI_STORE_T) grid = gemm_persistent_grid(grid);
   const dim3 g(grid), b(256);
   if (dtype == 0) {
     switch (a.epi) {
@@ -792,6 +946,27 @@ hipError_t launch_gemm(int dtype, const GemmArgs& a, int bf, int bt, int grid, h
       case EPI_SWIGLU: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 128, 2, 2, EPI_SWIGLU>), g, b, 0, s, a); break;
       case EPI_GATE: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 128, 2, 2, EPI_GATE>), g, b, 0, s, a); break;
       case EPI_SCALE_F32: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 128, 2, 2, EPI_SCALE_F32>), g, b, 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_piece_fixup(const GemmArgs& a, int bf, int bt, int grid, hipStream_t s) {
+  if (grid <= 0) return hipSuccess;
+  if (bf != 256 || (bt != 256 && bt != 128)) return hipErrorInvalidValue;
+  if (bt == 256) {
+    switch (a.epi) {
+      case EPI_ACT: hipLaunchKernelGGL((k_piece_fixup<256, 256, 4, 2, EPI_ACT>), dim3(grid), dim3(512), 0, s, a); break;
+      case EPI_SWIGLU: hipLaunchKernelGGL((k_piece_fixup<256, 256, 4, 2, EPI_SWIGLU>), dim3(grid), dim3(512), 0, s, a); break;
+      case EPI_GATE: hipLaunchKernelGGL((k_piece_fixup<256, 256, 4, 2, EPI_GATE>), dim3(grid), dim3(512), 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (a.epi) {
+      case EPI_ACT: hipLaunchKernelGGL((k_piece_fixup<256, 128, 2, 2, EPI_ACT>), dim3(grid), dim3(256), 0, s, a); break;
+      case EPI_SWIGLU: hipLaunchKernelGGL((k_piece_fixup<256, 128, 2, 2, EPI_SWIGLU>), dim3(grid), dim3(256), 0, s, a); break;
+      case EPI_GATE: hipLaunchKernelGGL((k_piece_fixup<256, 128, 2, 2, EPI_GATE>), dim3(grid), dim3(256), 0, s, a); break;
       default: return hipErrorInvalidValue;
     }
   }

@@ -8,7 +8,13 @@
 namespace moe {
 
 // One output tile of a grouped / BCSR / dense GEMM:  Y[row, ocol0 + f] =
-// epilogue(sum_k X[row, k] * W[wrow0 + f, kofs + k]),  rows [row0, row_end).
+// epilogue(sum_k X[row, xk + k] * W[wrow0 + f, kofs + k]),  rows [row0, row_end).
+//
+// A tile of the last round of a persistent launch may be cut along K into
+// nparts pieces (part = 0 .. nparts - 1) that run on different compute
+// units: each piece stores its fp32 partial sums at piece slot pslot0 + part;
+// the fixup kernel that follows the GEMM adds the nparts partials in part
+// order and applies the tile's epilogue.
 struct Tile {
   int row0, row_end;  // GEMM rows (permuted rows, or tokens)
   int wrow0;          // first packed weight row (feature) of the tile
@@ -17,6 +23,9 @@ struct Tile {
   int ocol0;          // first output column
   int expert;
   int spare;
+  int xk;             // K offset into the activation rows (a K piece's start)
+  int part, nparts;   // K piece of the tile (0, 1 for a whole tile)
+  int pslot0;         // partial-buffer slot of part 0 (pieces only)
 };
 
 // EPI_GATE_SPLIT: gated partial of one K split, written to Y + split * ysplit.
@@ -45,6 +54,16 @@ struct GemmArgs {
   // r * acc are also stored (bf16) at pre[row * ldpre + packed feature], in
   // the expert-local packed order of the weights (for the backward pass).
   void* pre; int64_t ldpre;
+  // Persistent launches planned per XCD (PlanArgs.grid > 0): ntiles[0] is
+  // the list length and ntiles[1 .. NX + 1] the first tile of each XCD's run
+  // (NX = 8 when the grid is a multiple of 8, else 1); workgroup b runs
+  // entries base[b % NX] + b / NX, + grid / NX, ... of its run; ntiles[10]
+  // is the number of split tiles.  part: fp32 partials of K pieces (grid x
+  // BF x BT floats); counters: the list entry of each split tile's part 0
+  // (read by the fixup kernel).
+  int xcd_runs;
+  float* part;
+  int* counters;
 };
 
 // Plan of GEMM tiles for grouped experts.  gemm = 1: first linear (features
@@ -68,6 +87,14 @@ struct PlanArgs {
   // BCSR (topology walk) when row_offsets != NULL
   const int32_t* row_offsets; const int32_t* column_indices; const int32_t* block_offsets;
   int block;
+  // grid > 0: the list is laid out for a persistent launch of `grid`
+  // workgroups: each XCD's run of tiles (as the XCD remap splits the list)
+  // ends with its last-round remainder cut along K into up to max_parts
+  // pieces so that the run fills its last round (ntiles[1..9] get the runs'
+  // bases, ntiles[10] the number of split tiles, counters[g] the list entry
+  // of split tile g's part 0).  The tile buffer must hold max_tiles + grid
+  // entries.
+  int grid; int max_parts; int* counters;
 };
 
 // MXFP8 GEMM: X and W hold E4M3 codes (ldx / ldw in bytes), xs / ws their
@@ -87,6 +114,12 @@ hipError_t launch_plan(const PlanArgs& p, hipStream_t s);
 // Two tile lists (independent outputs) in one launch.
 hipError_t launch_plan_pair(const PlanArgs& p0, const PlanArgs& p1, hipStream_t s);
 hipError_t launch_gemm(int dtype, const GemmArgs& a, int bf, int bt, int grid, hipStream_t s);
+// Workgroups of a persistent launch of the bf16 GEMM over at most `tiles`
+// tiles (one per compute unit, a multiple of 8 when there are enough tiles).
+int gemm_persistent_grid(int tiles);
+// The epilogue of the split tiles of a persistent launch planned for it
+// (grid: workgroups, at least the number of split tiles).
+hipError_t launch_piece_fixup(const GemmArgs& a, int bf, int bt, int grid, hipStream_t s);
 int gemm_tile_bf(int dtype);   // packed features per tile the GEMM kernels use
 int gemm_tile_bt(int dtype, int bcsr);
 

@@ -43,8 +43,9 @@ SMALL = {
     # issues the next tile's first loads before its epilogue
     "persistent_tiles": Workload("persistent_tiles", T=4096, d=512, E=8, k=2, act="swiglu",
                                  ffn=2048, cf=1.25, seed=23),
-    # ffn a multiple of 256 and few tiles: the second GEMM splits K in four
-    # partial planes, which combine adds in plane order
+    # ffn a multiple of 256 and few tiles: a K split would fill the second
+    # GEMM's last round, so that round's tiles are cut into K pieces whose
+    # fp32 partials the fixup kernel sums in part order
     "split4_small": Workload("split4_small", T=600, d=512, E=8, k=2, act="swiglu", ffn=512,
                              cf=1.25, seed=24),
     # one expert, k = 1: every token's gate is 1 and the layer is a dense FFN
