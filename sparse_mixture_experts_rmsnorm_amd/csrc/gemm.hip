@@ -617,6 +617,27 @@ __device__ __forceinline__ int upper_bound_i(const int* a, int n, int key) {
 
 constexpr int kPlanMax = 4096;   // experts (grouped) or token-block rows (BCSR)
 
+// Position of the n-th tile of a group of mt row tiles x nf column tiles.
+// A group of at most kRowBlock row tiles runs row tile fastest, so the tiles
+// an XCD runs together share each weight tile through L2 and hold all of the
+// group's rows.  A taller group (a dense shared FFN over every token, a hot
+// expert) runs in blocks of kRowBlock row tiles, column tile next, so that a
+// window of 32 tiles reads 8 row tiles and 4 weight tiles instead of 32 row
+// tiles and one weight tile.
+constexpr int kRowBlock = 8;
+__device__ __forceinline__ void tile_coords(int n, int mt, int nf_total, int* m, int* nf) {
+  if (mt <= kRowBlock) {
+    *nf = n / mt;
+    *m = n - *nf * mt;
+    return;
+  }
+  const int blk = n / (kRowBlock * nf_total);
+  const int rem = n - blk * kRowBlock * nf_total;
+  const int rows = min(kRowBlock, mt - blk * kRowBlock);
+  *nf = rem / rows;
+  *m = blk * kRowBlock + (rem - *nf * rows);
+}
+
 __device__ __forceinline__ void plan_tiles(const PlanArgs& p) {
   __shared__ int base_s[kPlanMax + 1];
   __shared__ long long sh[33];
@@ -743,7 +764,9 @@ __device__ __forceinline__ void plan_tiles(const PlanArgs& p) {
     t.spare = 0;
     if (dense) {
       const int mt = (p.dense_rows + p.bt - 1) / p.bt;
-      const int nf = n / mt, m = n - nf * mt;
+      const int nft = (p.dense_n + (p.ragged ? p.bf - 1 : 0)) / p.bf;
+      int m, nf;
+      tile_coords(n, mt, nft, &m, &nf);
       t.expert = 0;
       t.row0 = m * p.bt;
       t.row_end = min(p.dense_rows, t.row0 + p.bt);
@@ -784,7 +807,8 @@ __device__ __forceinline__ void plan_tiles(const PlanArgs& p) {
                                   : p.d / p.bf;
       const int sp = n / (mt * nfe);           // K split (second linear only)
       const int nn = n - sp * mt * nfe;
-      const int nf = nn / mt, m = nn - nf * mt;
+      int m, nf;
+      tile_coords(nn, mt, nfe, &m, &nf);
       t.expert = u;
       t.spare = sp;
       // the group's rows split evenly over its mt row tiles, in multiples of
