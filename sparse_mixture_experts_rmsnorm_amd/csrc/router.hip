@@ -346,21 +346,44 @@ __global__ void __launch_bounds__(64 * NW) k_router_bf16(
     wok[b] = e < E;
     wrow[b] = wr + int64_t(wok[b] ? e : 0) * d + kb + kg * 8;
   }
-#pragma unroll 8
-  for (int kk = 0; kk < kw; kk += 32) {
-    uint4 xv = tok_ok ? *reinterpret_cast<const uint4*>(xrow + kk) : make_uint4(0, 0, 0, 0);
-    {
-      float f[8];
-      unpack16(xv, f, (const uint16_t*)nullptr);
+  // K steps of 32 in groups of U: the loads of a group are issued together
+  // and unconditionally (rows past T or E read row 0, in bounds, and are
+  // zeroed by a select), so no branch puts a wait between a load and the
+  // next one; then the group's MFMAs run in K order
+  constexpr int U = 4;
+  const uint4 zero4 = make_uint4(0, 0, 0, 0);
+  auto kstep = [&](const uint4& xv_in, const uint4 (&wv)[NB]) __attribute__((always_inline)) {
+    const uint4 xv = tok_ok ? xv_in : zero4;
+    float f[8];
+    unpack16(xv, f, (const uint16_t*)nullptr);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ss = fmaf(f[i], f[i], ss);
-    }
+    for (int i = 0; i < 8; ++i) ss = fmaf(f[i], f[i], ss);
     const bf16x8 bx = __builtin_bit_cast(bf16x8, xv);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const uint4 wv = wok[b] ? *reinterpret_cast<const uint4*>(wrow[b] + kk) : make_uint4(0, 0, 0, 0);
-      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wv), bx, acc[b], 0, 0, 0);
+      const uint4 wb = wok[b] ? wv[b] : zero4;
+      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wb), bx, acc[b], 0, 0, 0);
     }
+  };
+  const int nit = kw / 32;
+  int it = 0;
+  for (; it + U <= nit; it += U) {
+    uint4 xv[U], wv[U][NB];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      xv[u] = *reinterpret_cast<const uint4*>(xrow + (it + u) * 32);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) wv[u][b] = *reinterpret_cast<const uint4*>(wrow[b] + (it + u) * 32);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) kstep(xv[u], wv[u]);
+  }
+  for (; it < nit; ++it) {
+    uint4 wv[NB];
+    const uint4 xv = *reinterpret_cast<const uint4*>(xrow + it * 32);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) wv[b] = *reinterpret_cast<const uint4*>(wrow[b] + it * 32);
+    kstep(xv, wv);
   }
   // sum of squares of the token over this wave's K range (lanes tl, tl+16, ...)
   ss += __shfl_xor(ss, 16, 64);

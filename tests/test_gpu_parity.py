@@ -237,7 +237,10 @@ def test_determinism(name, dev):
                                            (64, 6, 30, 1, 1000), (5, 3, 2, 4, 1),
                                            (256, 8, 7, 1, 513), (3000, 4, 10 ** 6, 1, 777),
                                            (16, 4, 6000, 1, 20000),
-                                           (1 << 20, 32, 10 ** 6, 1, 300)])
+                                           (1 << 20, 32, 10 ** 6, 1, 300),
+                                           # 16384 slots in groups padded to 128 rows;
+                                           # 256 experts at k=6 with a ragged T
+                                           (8, 2, 8192, 128, 8192), (256, 6, 40, 1, 2730)])
 def test_dispatch_bit_exact(E, k, cap, pad, T, dev):
     _say(f"[gpu] dispatch E={E} k={k} cap={cap} pad={pad} T={T}")
     rng = np.random.default_rng(E + k + T)
