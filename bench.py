@@ -80,6 +80,11 @@ def measured_traffic(workload):
     return (t["fetch_kib"] * COPY_SCALE["fetch"] + t["write_kib"] * COPY_SCALE["write"]) * 1024.0
 
 
+def say(msg):
+    """One progress line on stderr per finished leg of the run."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -93,6 +98,9 @@ def parse():
                     help="skip the MXFP8 variant of a grouped bf16 workload")
     ap.add_argument("--cpu-sample", type=int, default=4096,
                     help="tokens whose expert FFNs the CPU oracle computes")
+    ap.add_argument("--cpu-baseline-mx", action="store_true",
+                    help="also time the CPU oracle on an MXFP8 workload (its quantiser "
+                         "re-quantises every expert weight on each call: minutes per run)")
     ap.add_argument("--vendor-gemm", action="store_true",
                     help="also time torch.bmm (hipBLASLt) on per-expert GEMMs of the same "
                          "shapes, for context (outside the headline figure)")
@@ -244,33 +252,39 @@ def time_router_extras(B, wl, layer, x, out, ws, steps):
 
 
 def time_layer(B, layer, x, out, ws, stats, steps, warmup):
-    """W untimed forwards, then K timed ones bracketed by device syncs; the
-    per-stage times come from the library's hipEvents on its own stream, and
-    an event between consecutive steps on that stream gives each step's time
-    (median and minimum)."""
+    """W untimed forwards, then K timed ones bracketed by device syncs, with
+    an event between consecutive steps on the stream the layer runs on (the
+    median and minimum step).  Then K more forwards with the library's stage
+    timer, whose hipEvents between the stages give the per-stage times; they
+    stay out of the headline pass, since each adds a marker to the stream."""
     import torch
     for _ in range(warmup):
         layer.forward(x, out=out, ws=ws, stats=stats)
     torch.cuda.synchronize()
-    timer = B.StageTimer(steps)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev[0].record()
     for i in range(steps):
-        layer.forward(x, out=out, ws=ws, stats=stats, timer=timer)
+        layer.forward(x, out=out, ws=ws, stats=stats)
         ev[i + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    step_ms = {"median": per[len(per) // 2] if len(per) % 2 else
+               0.5 * (per[len(per) // 2 - 1] + per[len(per) // 2]),
+               "min": per[0], "max": per[-1], "mean_events": sum(per) / len(per)}
+    timer = B.StageTimer(steps)
+    t2 = time.perf_counter()
+    for i in range(steps):
+        layer.forward(x, out=out, ws=ws, stats=stats, timer=timer)
+    torch.cuda.synchronize()
+    step_ms["mean_with_stage_timer"] = (time.perf_counter() - t2) * 1e3 / steps
     stages = {}
     for s in B.STAGES:
         tot, n = timer.stage_ms(s)
         stages[s] = tot / max(n, 1)
     timer.close()
-    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
-    step_ms = {"median": per[len(per) // 2] if len(per) % 2 else
-               0.5 * (per[len(per) // 2 - 1] + per[len(per) // 2]),
-               "min": per[0], "max": per[-1], "mean_events": sum(per) / len(per)}
     return (t1 - t0) * 1e3 / steps, stages, step_ms
 
 
@@ -422,8 +436,10 @@ def cpu_baseline(wl, params, sample_tokens):
         for i in range(4):
             t0 = time.perf_counter()
             O.layer_forward(p, host["x"], tokens=tok)
+            dt = time.perf_counter() - t0
+            say(f"cpu baseline {'warm-up' if i == 0 else f'run {i}'}: {dt:.2f} s")
             if i:
-                runs.append(time.perf_counter() - t0)
+                runs.append(dt)
     dt = sorted(runs)[1]
     return {"value": len(tok) / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "cpu_model": cpu_model(), "precision": "float32 (BLAS sgemm)",
@@ -459,8 +475,10 @@ def main():
     ws = layer.alloc_workspace(wl.T)
     out = torch.empty_like(x)
     stats = torch.zeros(4, dtype=torch.int32, device=dev)
+    say(f"{wl.name}: layer built, timing {args.steps} steps")
     ms_per_step, stages, step_ms = time_layer(B, layer, x, out, ws, stats, args.steps,
                                               args.warmup)
+    say(f"layer timed: {ms_per_step:.4f} ms per step")
     st = stats.cpu().numpy().tolist()
     tokens_per_s = wl.T / (ms_per_step / 1e3)
     dtype = "f32" if wl.dtype == "f32" else ("mxfp8" if wl.quant == "mxfp8" else "bf16")
@@ -567,7 +585,9 @@ def main():
     if (args.vendor_gemm and wl.expert_kind == "grouped" and wl.dtype == "bf16"
             and wl.quant == "none" and len(set(wl.sizes)) == 1):
         result["vendor_gemm"] = vendor_gemm(wl, kept, stages, args.steps)
+    say("standalone entry points timed")
     gms = time_layer_graph(layer, x, out, ws, stats, args.steps)
+    say("graph replay timed")
     result["graph_replay"] = {"ms_per_step": gms, "tokens_per_s": wl.T / (gms * 1e-3),
                               "note": "the same forward captured in one HIP graph and replayed"}
     if wl.router == "dense":
@@ -578,12 +598,23 @@ def main():
         torch.cuda.empty_cache()
         layer = ws = None
         result["train_step"] = train_step(B, wl, params, x, args.steps, args.warmup)
+        say("training step timed")
     if (not args.no_mx and wl.expert_kind == "grouped" and wl.dtype == "bf16"
             and wl.quant == "none" and all(f % 128 == 0 for f in wl.sizes)):
         del layer, ws
         torch.cuda.empty_cache()
         result["mxfp8_variant"] = mx_variant(B, wl, params, x, args.steps, args.warmup)
-    if not args.no_cpu_baseline:
+        say("MXFP8 variant timed")
+    if args.no_cpu_baseline:
+        pass
+    elif wl.quant != "none" and not args.cpu_baseline_mx:
+        result["cpu_baseline"] = {
+            "value": None, "unit": "tokens/s", "kind": "oracle",
+            "skipped": ("the oracle's MX quantiser re-quantises all expert weights on every "
+                        "call (about 4 minutes per run at any sample size on a 8-core host), "
+                        "so this workload's CPU leg runs only with --cpu-baseline-mx; the "
+                        "bf16 layer of the same shape carries the CPU baseline")}
+    else:
         result["cpu_baseline"] = cpu_baseline(wl, params, args.cpu_sample)
     print(json.dumps(result))
 

@@ -205,41 +205,49 @@ __device__ __forceinline__ void store_piece(const GemmArgs& a, const Tile& tile,
     }
 }
 
-// Fixup of split tiles: workgroup g sums the nparts partials of split tile g
-// in part order (part 0 first: the same fp32 sum every run) and applies the
-// tile's epilogue.  group_tile[g] is the list entry of the tile's part 0;
-// a.ntiles[10] holds the number of split tiles.
+// Fixup of split tiles: one wave per workgroup, WGF x WGT workgroups per
+// split tile, workgroup (g, w) taking wave w's share of tile g.  It sums the
+// nparts partials in part order (part 0 first: the same fp32 sum every run)
+// and applies the tile's epilogue, which is per wave.  All loads of one part
+// are issued before the adds.  counters[g] is the list entry of the tile's
+// part 0; a.ntiles[10] holds the number of split tiles.
 template <int BF, int BT, int WGF, int WGT, int EPI>
-__global__ void __launch_bounds__(64 * WGF * WGT) k_piece_fixup(GemmArgs a) {
+__global__ void __launch_bounds__(64) k_piece_fixup(GemmArgs a) {
+  constexpr int NW = WGF * WGT;
   constexpr int WTF = BF / WGF, WTT = BT / WGT;
   constexpr int MF = WTF / 32, MT = WTT / 32;
-  const int g = blockIdx.x;
+  const int g = blockIdx.x / NW;
   if (g >= a.ntiles[10]) return;
+  const int wid = blockIdx.x % NW;
   const Tile tile = a.tiles[a.counters[g]];
-  const int lane = threadIdx.x & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x;
   const int wt = wid / WGF, wf = wid % WGF;
   const int fr = lane & 31, fh = lane >> 5;
   const float* const src0 = a.part + int64_t(tile.pslot0) * (int64_t(BF) * BT);
   f32x16 acc[MF][MT];
+  for (int pt = 0; pt < tile.nparts; ++pt) {
+    f32x4 w[MF][MT][4];
 #pragma unroll
-  for (int i = 0; i < MF; ++i)
+    for (int i = 0; i < MF; ++i)
 #pragma unroll
-    for (int j = 0; j < MT; ++j) {
-      for (int pt = 0; pt < tile.nparts; ++pt) {
+      for (int j = 0; j < MT; ++j) {
         const f32x4* src = reinterpret_cast<const f32x4*>(
             src0 + int64_t(pt) * (int64_t(BF) * BT) + piece_frag_offset<BF, BT, MF, MT>(wid, lane, i, j));
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 w = src[q];
+        for (int q = 0; q < 4; ++q) w[i][j][q] = src[q];
+      }
+#pragma unroll
+    for (int i = 0; i < MF; ++i)
+#pragma unroll
+      for (int j = 0; j < MT; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            if (pt == 0) acc[i][j][4 * q + e] = w[e];
-            else acc[i][j][4 * q + e] += w[e];
+            if (pt == 0) acc[i][j][4 * q + e] = w[i][j][q][e];
+            else acc[i][j][4 * q + e] += w[i][j][q][e];
           }
-        }
-      }
-    }
+  }
   gemm_epilogue<BF, BT, WGF, WGT, EPI>(a, tile, acc, wf, wt, fr, fh);
 }
 
@@ -977,20 +985,23 @@ hipError_t launch_gemm(int dtype, const GemmArgs& a, int bf, int bt, int grid, h
 }
 
 hipError_t launch_piece_fixup(const GemmArgs& a, int bf, int bt, int grid, hipStream_t s) {
+  // grid = the GEMM's persistent grid, which bounds the number of split tiles
   if (grid <= 0) return hipSuccess;
   if (bf != 256 || (bt != 256 && bt != 128)) return hipErrorInvalidValue;
   if (bt == 256) {
+    const dim3 g(grid * 8);
     switch (a.epi) {
-      case EPI_ACT: hipLaunchKernelGGL((k_piece_fixup<256, 256, 4, 2, EPI_ACT>), dim3(grid), dim3(512), 0, s, a); break;
-      case EPI_SWIGLU: hipLaunchKernelGGL((k_piece_fixup<256, 256, 4, 2, EPI_SWIGLU>), dim3(grid), dim3(512), 0, s, a); break;
-      case EPI_GATE: hipLaunchKernelGGL((k_piece_fixup<256, 256, 4, 2, EPI_GATE>), dim3(grid), dim3(512), 0, s, a); break;
+      case EPI_ACT: hipLaunchKernelGGL((k_piece_fixup<256, 256, 4, 2, EPI_ACT>), g, dim3(64), 0, s, a); break;
+      case EPI_SWIGLU: hipLaunchKernelGGL((k_piece_fixup<256, 256, 4, 2, EPI_SWIGLU>), g, dim3(64), 0, s, a); break;
+      case EPI_GATE: hipLaunchKernelGGL((k_piece_fixup<256, 256, 4, 2, EPI_GATE>), g, dim3(64), 0, s, a); break;
       default: return hipErrorInvalidValue;
     }
   } else {
+    const dim3 g(grid * 4);
     switch (a.epi) {
-      case EPI_ACT: hipLaunchKernelGGL((k_piece_fixup<256, 128, 2, 2, EPI_ACT>), dim3(grid), dim3(256), 0, s, a); break;
-      case EPI_SWIGLU: hipLaunchKernelGGL((k_piece_fixup<256, 128, 2, 2, EPI_SWIGLU>), dim3(grid), dim3(256), 0, s, a); break;
-      case EPI_GATE: hipLaunchKernelGGL((k_piece_fixup<256, 128, 2, 2, EPI_GATE>), dim3(grid), dim3(256), 0, s, a); break;
+      case EPI_ACT: hipLaunchKernelGGL((k_piece_fixup<256, 128, 2, 2, EPI_ACT>), g, dim3(64), 0, s, a); break;
+      case EPI_SWIGLU: hipLaunchKernelGGL((k_piece_fixup<256, 128, 2, 2, EPI_SWIGLU>), g, dim3(64), 0, s, a); break;
+      case EPI_GATE: hipLaunchKernelGGL((k_piece_fixup<256, 128, 2, 2, EPI_GATE>), g, dim3(64), 0, s, a); break;
       default: return hipErrorInvalidValue;
     }
   }

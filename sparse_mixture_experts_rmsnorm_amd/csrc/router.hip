@@ -349,8 +349,10 @@ __global__ void __launch_bounds__(64 * NW) k_router_bf16(
   // K steps of 32 in groups of U: the loads of a group are issued together
   // and unconditionally (rows past T or E read row 0, in bounds, and are
   // zeroed by a select), so no branch puts a wait between a load and the
-  // next one; then the group's MFMAs run in K order
-  constexpr int U = 4;
+  // next one; then the group's MFMAs run in K order.  With one expert block
+  // a group of 8 (64 registers of loads) covers a 256-wide K range in one
+  // round trip to memory.
+  constexpr int U = NB == 1 ? 8 : 4;
   const uint4 zero4 = make_uint4(0, 0, 0, 0);
   auto kstep = [&](const uint4& xv_in, const uint4 (&wv)[NB]) __attribute__((always_inline)) {
     const uint4 xv = tok_ok ? xv_in : zero4;
