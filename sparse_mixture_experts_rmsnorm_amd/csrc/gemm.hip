@@ -646,7 +646,11 @@ __device__ __forceinline__ void tile_coords(int n, int mt, int nf_total, int* m,
   *m = blk * kRowBlock + (rem - *nf * rows);
 }
 
-__device__ __forceinline__ void plan_tiles(const PlanArgs& p) {
+// Workgroup `slice` of `nslices` writes list entries slice * blockDim + tid,
+// stepping by nslices * blockDim; every workgroup computes the per-unit
+// counts and the XCD runs itself (a few reads of the offsets), and slice 0
+// writes the list's header.
+__device__ __forceinline__ void plan_tiles(const PlanArgs& p, int slice, int nslices) {
   __shared__ int base_s[kPlanMax + 1];
   __shared__ long long sh[33];
   const bool dense = p.offsets == nullptr;
@@ -740,16 +744,19 @@ __device__ __forceinline__ void plan_tiles(const PlanArgs& p) {
         }
       }
       xout_s[NX] = out;
-      p.ntiles[0] = out;
-      for (int x = 0; x <= NX; ++x) p.ntiles[1 + x] = xout_s[x];
-      p.ntiles[10] = grp;
+      if (slice == 0) {
+        p.ntiles[0] = out;
+        for (int x = 0; x <= NX; ++x) p.ntiles[1 + x] = xout_s[x];
+        p.ntiles[10] = grp;
+      }
     }
     __syncthreads();
     nout = xout_s[NX];
-  } else if (threadIdx.x == 0) {
+  } else if (threadIdx.x == 0 && slice == 0) {
     *p.ntiles = ntot;
   }
-  for (int o = threadIdx.x; o < nout; o += blockDim.x) {
+  for (int o = slice * int(blockDim.x) + int(threadIdx.x); o < nout;
+       o += nslices * int(blockDim.x)) {
     int idx = o, part = 0, nparts = 1, group = 0, pslot0 = 0;
     if (p.grid > 0) {
       int x = 0;
@@ -862,12 +869,16 @@ __device__ __forceinline__ void plan_tiles(const PlanArgs& p) {
 
 // dst[n, k] = src[k, n], 32 x 32 tiles through LDS.
 
-__global__ void __launch_bounds__(1024) k_plan(PlanArgs p) { plan_tiles(p); }
+constexpr int kPlanSlices = 8;   // workgroups writing one list
 
-// Both expert GEMMs' lists in one launch, one workgroup each.
+__global__ void __launch_bounds__(1024) k_plan(PlanArgs p) {
+  plan_tiles(p, blockIdx.x, kPlanSlices);
+}
+
+// Both expert GEMMs' lists in one launch, kPlanSlices workgroups each.
 __global__ void __launch_bounds__(1024) k_plan_pair(PlanArgs p0, PlanArgs p1) {
-  if (blockIdx.x == 0) plan_tiles(p0);
-  else plan_tiles(p1);
+  if (int(blockIdx.x) < kPlanSlices) plan_tiles(p0, blockIdx.x, kPlanSlices);
+  else plan_tiles(p1, blockIdx.x - kPlanSlices, kPlanSlices);
 }
 
 template <typename T>
@@ -917,12 +928,12 @@ int gemm_tile_bf(int dtype) { return dtype == 0 ? 64 : 256; }
 int gemm_tile_bt(int dtype, int bcsr) { return dtype == 0 ? 64 : (bcsr ? 128 : 256); }
 
 hipError_t launch_plan(const PlanArgs& p, hipStream_t s) {
-  hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, p);
+  hipLaunchKernelGGL(k_plan, dim3(kPlanSlices), dim3(1024), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_plan_pair(const PlanArgs& p0, const PlanArgs& p1, hipStream_t s) {
-  hipLaunchKernelGGL(k_plan_pair, dim3(2), dim3(1024), 0, s, p0, p1);
+  hipLaunchKernelGGL(k_plan_pair, dim3(2 * kPlanSlices), dim3(1024), 0, s, p0, p1);
   return hipGetLastError();
 }
 

@@ -719,7 +719,11 @@ __global__ void __launch_bounds__(256) k_cartesian_topk(const float* __restrict_
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
   // stage 2: candidate c = a * k + b pairs row choice a with column choice b
+  // (a, b) of c = lane + 64 q advance by (64 / k, 64 % k) per q with one
+  // carry, instead of a division per candidate
   const int nc = k * k;
+  const int da = 64 / k, db = 64 - da * k;
+  int a = lane / k, b = lane - (lane / k) * k;
   float cv[Q];
   int cid[Q];
   uint32_t cu[Q];
@@ -727,7 +731,6 @@ __global__ void __launch_bounds__(256) k_cartesian_topk(const float* __restrict_
   for (int q = 0; q < Q; ++q) {
     const int c = lane + 64 * q;
     if (c < nc) {
-      const int a = c / k, b = c - a * k;
       cv[q] = sel_v[wid][0][a] + sel_v[wid][1][b];
       cid[q] = sel_i[wid][0][a] * Nc + sel_i[wid][1][b];
       cu[q] = score_key(cv[q]);
@@ -735,6 +738,12 @@ __global__ void __launch_bounds__(256) k_cartesian_topk(const float* __restrict_
       cv[q] = -INFINITY;
       cid[q] = 0x7fffffff;
       cu[q] = 0u;
+    }
+    a += da;
+    b += db;
+    if (b >= k) {
+      b -= k;
+      ++a;
     }
   }
   const uint32_t th = kth_largest_key_fast<Q>(cu, k, cand_s[wid]);
