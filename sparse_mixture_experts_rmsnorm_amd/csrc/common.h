@@ -86,6 +86,14 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return (uint64_t(1) << (threadIdx.x & 63)) - 1;
 }
 
+// Set bits of a wave-uniform lane mask in the lanes below this one (the
+// lane's rank among the set lanes), by the mbcnt pair: two instructions,
+// where popcount(mask & lanemask_lt()) takes a 64-bit AND and two counts.
+__device__ __forceinline__ int rank_below(uint64_t mask) {
+  return int(__builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32),
+                                       __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u)));
+}
+
 // Wave-wide sum (all 64 lanes get the result).
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -225,7 +225,7 @@ __global__ void __launch_bounds__(kThreads) k_rank(
     if (unsigned(e) >= unsigned(E)) e = -1;
     const bool ok = e >= 0;
     const uint64_t peers = match_peers(e, ok, nbits);
-    const int lr = __popcll(peers & lanemask_lt());
+    const int lr = rank_below(peers);
     const int tag = b + 1;
     if (ok && lr == 0) wtag[wid * E + e] = (tag << 8) | __popcll(peers);
     __syncthreads();
@@ -403,7 +403,7 @@ __global__ void __launch_bounds__(kThreads) k_radix_scatter(
     const int key = ok ? keys_in[i0 + i] : 0;
     const int dig = (key >> shift) & (nb - 1);
     const uint64_t peers = match_peers(dig, ok, bits);
-    const int lr = __popcll(peers & lanemask_lt());
+    const int lr = rank_below(peers);
     const int tag = b + 1;
     if (ok && lr == 0) wtag[wid * nb + dig] = (tag << 8) | __popcll(peers);
     __syncthreads();

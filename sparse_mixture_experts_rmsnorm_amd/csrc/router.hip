@@ -160,12 +160,11 @@ __device__ __forceinline__ uint32_t kth_largest_key_fast(const uint32_t (&u)[Q],
   for (int q = 0; q < Q; ++q) c += __popcll(__ballot(u[q] >= lo));
   if (c > 64) return kth_largest_key<Q>(u, k);
   const int lane = threadIdx.x & 63;
-  const uint64_t below = lanemask_lt();
   int base = 0;
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
     const uint64_t m = __ballot(u[q] >= lo);
-    if (u[q] >= lo) cand[base + __popcll(m & below)] = u[q];
+    if (u[q] >= lo) cand[base + rank_below(m)] = u[q];
     base += __popcll(m);
   }
   __builtin_amdgcn_wave_barrier();
@@ -190,7 +189,6 @@ __device__ void wave_select_gates(const float (&vals)[Q], int n, int k, int reno
                                   uint32_t* cand, float* selv, int* seli, float* pacc = nullptr,
                                   float* gacc = nullptr, int* cacc = nullptr) {
   const int lane = threadIdx.x & 63;
-  const uint64_t below = lanemask_lt();
   uint32_t u[Q];
 #pragma unroll
   for (int q = 0; q < Q; ++q) u[q] = lane + 64 * q < n ? score_key(vals[q]) : 0u;
@@ -204,12 +202,12 @@ __device__ void wave_select_gates(const float (&vals)[Q], int n, int k, int reno
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
     const uint64_t eq = __ballot(u[q] == th);
-    const bool take_eq = ((eq >> lane) & 1) && __popcll(eq & below) < need;
+    const bool take_eq = u[q] == th && rank_below(eq) < need;
     need -= min(need, __popcll(eq));
     const bool sel = u[q] > th || take_eq;
     const uint64_t sm = __ballot(sel);
     if (sel) {
-      const int p = base + __popcll(sm & below);
+      const int p = base + rank_below(sm);
       selv[p] = vals[q];
       seli[p] = lane + 64 * q;
     }
@@ -664,7 +662,6 @@ __global__ void __launch_bounds__(256) k_cartesian_topk(const float* __restrict_
   const int t = blockIdx.x * 4 + wid;
   if (t >= T) return;
   const float* row = scores + int64_t(t) * (Nr + Nc);
-  const uint64_t below = lanemask_lt();
   float m[2] = {-INFINITY, -INFINITY}, z[2] = {0.f, 0.f};
 
   // stage 1: list 0 = rows of s1, list 1 = columns of s2
@@ -702,12 +699,12 @@ __global__ void __launch_bounds__(256) k_cartesian_topk(const float* __restrict_
     for (int q = 0; q < Q; ++q) {
       // ties at the threshold go to the lowest indices: q ascending, then lane
       const uint64_t eq = __ballot(u[q] == th);
-      const bool take_eq = ((eq >> lane) & 1) && __popcll(eq & below) < need;
+      const bool take_eq = u[q] == th && rank_below(eq) < need;
       need -= min(need, __popcll(eq));
       const bool sel = u[q] > th || take_eq;
       const uint64_t sm = __ballot(sel);
       if (sel) {
-        const int p = base + __popcll(sm & below);
+        const int p = base + rank_below(sm);
         sel_v[wid][list][p] = v[q];
         sel_i[wid][list][p] = lane + 64 * q;
       }
@@ -774,7 +771,7 @@ __global__ void __launch_bounds__(256) k_cartesian_topk(const float* __restrict_
   for (int q = 0; q < Q; ++q) {
     const uint64_t sm = __ballot(sel[q]);
     if (sel[q]) {
-      const int p = base + __popcll(sm & below);
+      const int p = base + rank_below(sm);
       sel_v[wid][0][p] = cv[q];
       sel_i[wid][0][p] = cid[q];
     }
