@@ -126,7 +126,9 @@ int check_experts(const moe_experts_desc* X, int dtype, int64_t d, ExpertGeo* g)
     REQUIRE(d % 256 == 0 && d > 0, MOE_ESHAPE, "bf16 experts need d %% 256 == 0 (got %lld)", (long long)d);
     geo.bf1 = 256;
     geo.bf2 = 256;
-    geo.bt = geo.bcsr ? 128 : 256;
+    // BCSR: tiles of two 128-row token blocks of one expert (a lone last
+    // block makes a 128-row tile), so both walks run the 8-wave kernel
+    geo.bt = 256;
   }
   geo.bt2 = geo.bt;
   geo.fold = geo.pf;

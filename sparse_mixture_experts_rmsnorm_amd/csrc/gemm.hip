@@ -624,6 +624,7 @@ __device__ __forceinline__ int upper_bound_i(const int* a, int n, int key) {
 }
 
 constexpr int kPlanMax = 4096;   // experts (grouped) or token-block rows (BCSR)
+constexpr int kPlanOffsMax = 2048;   // experts of a grouped / BCSR layer
 
 // Position of the n-th tile of a group of mt row tiles x nf column tiles.
 // A group of at most kRowBlock row tiles runs row tile fastest, so the tiles
@@ -650,11 +651,39 @@ __device__ __forceinline__ void tile_coords(int n, int mt, int nf_total, int* m,
 // stepping by nslices * blockDim; every workgroup computes the per-unit
 // counts and the XCD runs itself (a few reads of the offsets), and slice 0
 // writes the list's header.
+// BCSR with tiles of two token blocks (bt = 2 block): token-block rows pair
+// up within an expert (its blocks 0-1, 2-3, ...), and a pair shares its tiles
+// when both topology rows hold the same column blocks.  Returns the rows'
+// share: 2 = first row of a pair (its tiles span both rows), 0 = second row
+// of a pair (no tiles of its own), 1 = a row on its own.
+__device__ __forceinline__ int bcsr_span(const PlanArgs& p, const int* offs, int u) {
+  if (p.bt < 2 * p.block) return 1;
+  const int row = u * p.block;
+  const int e = upper_bound_i(offs, p.E + 1, row) - 1;
+  const int i = (row - offs[e]) / p.block;
+  const int u0 = u - (i & 1);
+  if ((u0 + 1) * p.block >= offs[e + 1]) return 1;   // no second block
+  const int f0 = p.row_offsets[u0], f1 = p.row_offsets[u0 + 1];
+  const int nz = f1 - f0;
+  if (p.row_offsets[u0 + 2] - f1 != nz) return 1;
+  bool same = true;
+#pragma unroll 4
+  for (int c = 0; c < nz; ++c) same = same && p.column_indices[f0 + c] == p.column_indices[f1 + c];
+  if (!same) return 1;
+  return (i & 1) ? 0 : 2;
+}
+
 __device__ __forceinline__ void plan_tiles(const PlanArgs& p, int slice, int nslices) {
   __shared__ int base_s[kPlanMax + 1];
+  __shared__ unsigned char span_s[kPlanMax];   // BCSR: bcsr_span of each token-block row
+  __shared__ int offs_s[kPlanOffsMax + 1];      // BCSR: the expert row offsets
   __shared__ long long sh[33];
   const bool dense = p.offsets == nullptr;
   const bool bcsr = !dense && p.row_offsets != nullptr;
+  if (bcsr) {
+    for (int e = threadIdx.x; e <= p.E; e += blockDim.x) offs_s[e] = p.offsets[e];
+    __syncthreads();
+  }
   const int pf = p.swiglu && p.gemm == 1 ? 2 : 1;   // packed rows per hidden unit
   const int km = p.kmul > 0 ? p.kmul : 1;            // second linear: K per hidden unit
   const int nunits = dense ? 1 : bcsr ? p.offsets[p.E] / p.block : p.E;
@@ -668,7 +697,9 @@ __device__ __forceinline__ void plan_tiles(const PlanArgs& p, int slice, int nsl
       cnt = ((p.dense_rows + p.bt - 1) / p.bt) * ((p.dense_n + (p.ragged ? p.bf - 1 : 0)) / p.bf);
     } else if (bcsr) {
       const int nz = p.row_offsets[u + 1] - p.row_offsets[u];
-      cnt = p.gemm == 1 ? nz * p.block * pf / p.bf : p.d / p.bf;
+      const int sp = bcsr_span(p, offs_s, u);
+      span_s[u] = static_cast<unsigned char>(sp);
+      cnt = sp == 0 ? 0 : p.gemm == 1 ? nz * p.block * pf / p.bf : p.d / p.bf;
     } else {
       const int rows = p.offsets[u + 1] - p.offsets[u];
       const int mt = (rows + p.bt - 1) / p.bt;
@@ -801,7 +832,7 @@ __device__ __forceinline__ void plan_tiles(const PlanArgs& p, int slice, int nsl
       const int e = upper_bound_i(p.block_offsets, p.E + 1, cb0) - 1;
       t.expert = e;
       t.row0 = u * p.block;
-      t.row_end = t.row0 + p.block;
+      t.row_end = t.row0 + span_s[u] * p.block;
       if (p.gemm == 1) {
         const int cb = p.column_indices[first + n * (p.bf / (p.block * pf))];
         t.wrow0 = cb * p.block * pf;
@@ -925,7 +956,7 @@ __global__ void __launch_bounds__(256) k_pack_swiglu(const T* __restrict__ w1,
 }  // namespace
 
 int gemm_tile_bf(int dtype) { return dtype == 0 ? 64 : 256; }
-int gemm_tile_bt(int dtype, int bcsr) { return dtype == 0 ? 64 : (bcsr ? 128 : 256); }
+int gemm_tile_bt(int dtype, int bcsr) { return dtype == 0 ? 64 : 256; }
 
 hipError_t launch_plan(const PlanArgs& p, hipStream_t s) {
   hipLaunchKernelGGL(k_plan, dim3(kPlanSlices), dim3(1024), 0, s, p);
