@@ -89,7 +89,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mixtral_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
@@ -252,15 +252,27 @@ def time_router_extras(B, wl, layer, x, out, ws, steps):
 
 
 def time_layer(B, layer, x, out, ws, stats, steps, warmup):
-    """W untimed forwards, then K timed ones bracketed by device syncs, with
-    an event between consecutive steps on the stream the layer runs on (the
-    median and minimum step).  Then K more forwards with the library's stage
-    timer, whose hipEvents between the stages give the per-stage times; they
-    stay out of the headline pass, since each adds a marker to the stream."""
+    """W untimed forwards; then K forwards with the library's stage timer, whose
+    hipEvents between the stages give the per-stage times (kept out of the
+    headline pass, since each event adds a marker to the stream; running this
+    pass first also lets the clock settle after the set-up's idle time); then
+    the K timed forwards, bracketed by device syncs, with an event between
+    consecutive steps on the stream the layer runs on (median and minimum)."""
     import torch
     for _ in range(warmup):
         layer.forward(x, out=out, ws=ws, stats=stats)
     torch.cuda.synchronize()
+    timer = B.StageTimer(steps)
+    t2 = time.perf_counter()
+    for i in range(steps):
+        layer.forward(x, out=out, ws=ws, stats=stats, timer=timer)
+    torch.cuda.synchronize()
+    with_timer = (time.perf_counter() - t2) * 1e3 / steps
+    stages = {}
+    for s in B.STAGES:
+        tot, n = timer.stage_ms(s)
+        stages[s] = tot / max(n, 1)
+    timer.close()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -273,18 +285,8 @@ def time_layer(B, layer, x, out, ws, stats, steps, warmup):
     per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
     step_ms = {"median": per[len(per) // 2] if len(per) % 2 else
                0.5 * (per[len(per) // 2 - 1] + per[len(per) // 2]),
-               "min": per[0], "max": per[-1], "mean_events": sum(per) / len(per)}
-    timer = B.StageTimer(steps)
-    t2 = time.perf_counter()
-    for i in range(steps):
-        layer.forward(x, out=out, ws=ws, stats=stats, timer=timer)
-    torch.cuda.synchronize()
-    step_ms["mean_with_stage_timer"] = (time.perf_counter() - t2) * 1e3 / steps
-    stages = {}
-    for s in B.STAGES:
-        tot, n = timer.stage_ms(s)
-        stages[s] = tot / max(n, 1)
-    timer.close()
+               "min": per[0], "max": per[-1], "mean_events": sum(per) / len(per),
+               "mean_with_stage_timer": with_timer}
     return (t1 - t0) * 1e3 / steps, stages, step_ms
 
 

@@ -255,7 +255,9 @@ void fit_dense_tiles(ExpertGeo* g, int dtype, int64_t d, int64_t T) {
 // rounds of tiles over the compute units, each 1 / s of a tile, plus a fixed
 // cost per round (a tile's prologue and epilogue) and per extra partial plane
 // (written by the GEMM, read by combine).  Splits of 1, 2 or 4 whose parts are
-// whole K stages of every expert are considered.
+// whole K stages of every expert are considered.  The MXFP8 path then writes s
+// planes; the bf16 path takes any s > 1 as the signal to cut only the last
+// round of tiles into K pieces (carve_expert_ws).
 int choose_ksplit(const ExpertGeo& g, int dtype, int64_t d, int64_t rows_used_est) {
   if (g.bcsr || g.atomic || dtype != MOE_BF16 || g.kdiv < 2) return 1;
   constexpr double kRoundCost = 0.017, kPlaneCost = 0.031;
