@@ -31,36 +31,38 @@ PEAK_HBM_GBPS = 8000.0
 # rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) scaled by
 # what the same counters read for a plain 1 GiB device copy
 # (bench.py --copy-calibration: FETCH_SIZE 524302.4 KiB, WRITE_SIZE 1048576 KiB).
-# Valid only for the kernel sources they were taken on: any change to those
-# files reports null.
+# The mean over the first 18 launches of the run (warm-up, stage-timer and
+# timed forwards on the workload's own routing; the router-extras pass after
+# them routes with noise and is left out).  Valid only for the kernel sources
+# they were taken on: any change to those files reports null.
 COPY_SCALE = {"fetch": 1048576.0 / 524302.4, "write": 1048576.0 / 1048576.0}
 TRAFFIC = {
     "mixtral_bf16": {
         "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
                                                  "common.h"),
-        "source_sha256": "7dd4196bd7e6cb9a46e10af9de3f4e07a02af735e1dafa7c55abeb2423ee936c",
-        "fetch_kib": 1861829.1, "write_kib": 229417.3},
+        "source_sha256": "b43dc4164ba0a01f87d59dfc6b1d464a7e9ada118d471174db4d31acb56bf6b1",
+        "fetch_kib": 1846332.5, "write_kib": 230445.3},
     "variable_bcsr_bf16": {
         "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
                                                  "common.h"),
-        "source_sha256": "7dd4196bd7e6cb9a46e10af9de3f4e07a02af735e1dafa7c55abeb2423ee936c",
-        "fetch_kib": 36256.0, "write_kib": 35537.5},
+        "source_sha256": "b43dc4164ba0a01f87d59dfc6b1d464a7e9ada118d471174db4d31acb56bf6b1",
+        "fetch_kib": 30982.6, "write_kib": 55356.9},
     # the routed first GEMM only (the shared experts' first GEMM is the same
     # kernel; the dispatches alternate, routed first)
     "finegrained_bf16": {
         "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
                                                  "common.h"),
-        "source_sha256": "7dd4196bd7e6cb9a46e10af9de3f4e07a02af735e1dafa7c55abeb2423ee936c",
-        "fetch_kib": 713819.1, "write_kib": 113959.3},
+        "source_sha256": "b43dc4164ba0a01f87d59dfc6b1d464a7e9ada118d471174db4d31acb56bf6b1",
+        "fetch_kib": 753263.7, "write_kib": 114982.1},
     "atomic_bf16": {
         "kernel": "k_atomic_token", "sources": ("atomic.hip", "common.h"),
-        "source_sha256": "33fc89490ffe0f0aebfb6635519684c32ffa2b3c463f2a628f53c19237805823",
-        "fetch_kib": 535770.9, "write_kib": 16384.0},
+        "source_sha256": "57cff026d7a755084011a9121682f1fde2bbc20b57f600a1a1a4583a0a9b3c50",
+        "fetch_kib": 535716.2, "write_kib": 16384.0},
     "mixtral_mxfp8": {
         "kernel": "k_gemm_mx", "sources": ("gemm_mx.hip", "gemm_args.h", "gemm_common.h",
                                            "common.h"),
-        "source_sha256": "72efd1cb92b6477d577440b074798707f52307125a3daf0ee295c8c09b1d9037",
-        "fetch_kib": 843933.7, "write_kib": 123440.5},
+        "source_sha256": "5b2ff55fdb3f2ee19e4c61ce2c70fa55f61c8cbdeed9419514b749502e637156",
+        "fetch_kib": 853991.1, "write_kib": 123547.3},
 }
 
 
@@ -155,7 +157,7 @@ def vendor_gemm(wl, kept, stages, steps):
         del a, b, c
     torch.cuda.empty_cache()
     out["note"] = ("torch.bmm over E experts x the mean kept rows, uniform (no ragged rows, "
-                   "no SwiGLU / gate / r-scale epilogue, no K-split planes); the expert GEMMs "
+                   "no SwiGLU / gate / r-scale epilogue, no K pieces); the expert GEMMs "
                    "compared here run on the layer's real routing")
     return out
 
@@ -522,9 +524,11 @@ def main():
                                             else ")")),
                               "algorithmic_flop_per_launch": f1}
         # the same launch's HBM floor: each expert's weight tile read once, its
-        # rows read once, h written once (kept rows only)
+        # rows read once, h written once (kept rows only); MXFP8 operands are one
+        # code byte per element plus one scale byte per 32
         mult = 2 if wl.act == "swiglu" else 1
-        g1_bytes = sum(mult * wl.d * f * es + m * (wl.d + f) * es for f, m in zip(wl.sizes, kept)
+        eg = 33.0 / 32.0 if dtype == "mxfp8" else es
+        g1_bytes = sum(mult * wl.d * f * eg + m * (wl.d + f) * eg for f, m in zip(wl.sizes, kept)
                        if m > 0)
         floor_ms = max(f1 / (PEAK_TFLOPS[dtype] * 1e12), g1_bytes / (PEAK_HBM_GBPS * 1e9)) * 1e3
         result["roofline"].update({

@@ -396,7 +396,10 @@ int moe_build_topology(const int32_t* offsets, const int32_t* size_blocks,
  *   bits.  A slot whose id lies outside [0, N) is dropped (no row is read)
  *   and added to stats->errors (stats nullable; the count is added to what
  *   stats holds, never reset here); a task row whose token lies outside
- *   [0, T) is dropped.  Hidden activations live in the workspace.
+ *   [0, T) is dropped.  The workspace holds the hidden activations, the
+ *   device-built tile lists and, for bf16 experts whose second linear cuts
+ *   its last round of tiles along K, the pieces' fp32 partial sums (added in
+ *   a fixed order, so y is rounded to the dtype once and repeats bit for bit).
  * stats is not used by the GROUPED / BCSR kinds (they read no expert ids). */
 size_t moe_expert_workspace_size(const moe_experts_desc* X, int dtype, int64_t d,
                                  int64_t T, int k, int64_t rows_max);
