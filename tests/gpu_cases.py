@@ -26,6 +26,11 @@ SMALL = {
     "bcsr_small": Workload("bcsr_small", T=600, d=256, E=4, k=2, act="gelu",
                            expert_sizes=((1, 512), (3, 256)), bias="normal", expert_kind="bcsr",
                            seed=13),
+    # BCSR under a skewed router (Zipf bias): token-block counts 3, 1, 1, 0, 4, 1 per
+    # expert, so the walk pairs blocks, leaves lone last blocks and skips an empty expert
+    "bcsr_skew": Workload("bcsr_skew", T=500, d=256, E=6, k=2, act="gelu",
+                          expert_sizes=((2, 512), (4, 256)), bias="zipf", zipf_s=0.8,
+                          expert_kind="bcsr", seed=40),
     "finegrained_small": Workload("finegrained_small", T=500, d=256, E=64, k=6, act="swiglu",
                                   ffn=128, cf=1.5, bias="zipf", shared_ffn=256, seed=14),
     "mixtral_small_mxfp8": Workload("mixtral_small_mxfp8", T=700, d=512, E=8, k=2,
