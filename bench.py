@@ -40,19 +40,19 @@ TRAFFIC = {
     "mixtral_bf16": {
         "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
                                                  "common.h"),
-        "source_sha256": "b43dc4164ba0a01f87d59dfc6b1d464a7e9ada118d471174db4d31acb56bf6b1",
+        "source_sha256": "1e82a91c95e4d3900492127637559a37ac9095fadfe783c510c27b9c2631442d",
         "fetch_kib": 1846332.5, "write_kib": 230445.3},
     "variable_bcsr_bf16": {
         "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
                                                  "common.h"),
-        "source_sha256": "b43dc4164ba0a01f87d59dfc6b1d464a7e9ada118d471174db4d31acb56bf6b1",
+        "source_sha256": "1e82a91c95e4d3900492127637559a37ac9095fadfe783c510c27b9c2631442d",
         "fetch_kib": 30982.6, "write_kib": 55356.9},
     # the routed first GEMM only (the shared experts' first GEMM is the same
     # kernel; the dispatches alternate, routed first)
     "finegrained_bf16": {
         "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
                                                  "common.h"),
-        "source_sha256": "b43dc4164ba0a01f87d59dfc6b1d464a7e9ada118d471174db4d31acb56bf6b1",
+        "source_sha256": "1e82a91c95e4d3900492127637559a37ac9095fadfe783c510c27b9c2631442d",
         "fetch_kib": 753263.7, "write_kib": 114982.1},
     "atomic_bf16": {
         "kernel": "k_atomic_token", "sources": ("atomic.hip", "common.h"),

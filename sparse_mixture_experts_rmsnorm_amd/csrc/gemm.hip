@@ -18,10 +18,14 @@
 // walking the topology of the "Variable-size experts" nanoMOE notes
 // (sections 3-4): first linear = one tile per run of nonzero column blocks
 // of a token-block row (SDD), second linear = one tile per token-block row
-// and output slice, with K over that row's nonzero blocks (DSD).
+// and output slice, with K over that row's nonzero blocks (DSD); two
+// consecutive token-block rows of an expert that hold the same column blocks
+// share their tiles (256 rows).  The last round of a persistent launch may
+// cut its tiles along K into pieces whose fp32 partials k_piece_fixup sums.
 //
 // Tiling for gfx950: a 256 x 256 output tile per workgroup of 8 wave64s (a
-// 4 x 2 grid of 64 x 128 wave tiles; 128-row BCSR blocks use 4 waves).
+// 4 x 2 grid of 64 x 128 wave tiles; a 4-wave 256 x 128 variant serves
+// dense second linears with fewer 256-row tiles than compute units).
 // Operands are both K-contiguous (weights packed as [features, K]) and move
 // global -> LDS by the global_load_lds_dwordx4 DMA into LDS rings (three
 // stages of weights, two of activations) with a 16-byte-chunk XOR swizzle
