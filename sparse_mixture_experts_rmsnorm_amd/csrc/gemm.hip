@@ -118,24 +118,32 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const Tile& til
     } else {
       uint16_t* Y = static_cast<uint16_t*>(a.Y) + int64_t(row) * a.ldy + tile.ocol0 + wf * WTF +
                     (EPI == EPI_GATE_SPLIT ? int64_t(tile.spare) * a.ysplit : 0);
+      // one loop nest per activation, chosen by a uniform branch: inside the
+      // unrolled loop a runtime choice would be if-converted into computing
+      // both activations of every value
+      auto store_rows = [&](auto act_c) __attribute__((always_inline)) {
+        constexpr int ACT = decltype(act_c)::value;
 #pragma unroll
-      for (int i = 0; i < MF; ++i)
+        for (int i = 0; i < MF; ++i)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          if (EPI == EPI_STORE_T && wf * WTF + i * 32 >= tile.spare) continue;   // missing features
-          uint32_t pk[2];
+          for (int g = 0; g < 4; ++g) {
+            if (EPI == EPI_STORE_T && wf * WTF + i * 32 >= tile.spare) continue;   // missing features
+            uint32_t pk[2];
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            float o[2];
+            for (int h = 0; h < 2; ++h) {
+              float o[2];
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              const float z = rs * acc[i][j][g * 4 + h * 2 + e];
-              o[e] = EPI == EPI_ACT ? apply_act(z, a.act) : z;
+              for (int e = 0; e < 2; ++e) {
+                const float z = rs * acc[i][j][g * 4 + h * 2 + e];
+                o[e] = EPI != EPI_ACT ? z : ACT == 1 ? gelu_tanh(z) : gelu_erf(z);
+              }
+              pk[h] = pk_bf16(o[0], o[1]);
             }
-            pk[h] = pk_bf16(o[0], o[1]);
+            *reinterpret_cast<uint2*>(Y + i * 32 + g * 8 + fh * 4) = make_uint2(pk[0], pk[1]);
           }
-          *reinterpret_cast<uint2*>(Y + i * 32 + g * 8 + fh * 4) = make_uint2(pk[0], pk[1]);
-        }
+      };
+      if (EPI == EPI_ACT && a.act == 1) store_rows(std::integral_constant<int, 1>{});
+      else store_rows(std::integral_constant<int, 0>{});
     }
   }
 }
