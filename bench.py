@@ -40,29 +40,29 @@ TRAFFIC = {
     "mixtral_bf16": {
         "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
                                                  "common.h"),
-        "source_sha256": "1e82a91c95e4d3900492127637559a37ac9095fadfe783c510c27b9c2631442d",
-        "fetch_kib": 1846332.5, "write_kib": 230445.3},
+        "source_sha256": "fc86d9cdea1b988988232414c56d2fa4015ca5d6ea737f0f9d850a091033c66a",
+        "fetch_kib": 1836491.8, "write_kib": 230442.4},
     "variable_bcsr_bf16": {
         "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
                                                  "common.h"),
-        "source_sha256": "1e82a91c95e4d3900492127637559a37ac9095fadfe783c510c27b9c2631442d",
-        "fetch_kib": 30982.6, "write_kib": 55356.9},
+        "source_sha256": "fc86d9cdea1b988988232414c56d2fa4015ca5d6ea737f0f9d850a091033c66a",
+        "fetch_kib": 30441.6, "write_kib": 48309.5},
     # the routed first GEMM only (the shared experts' first GEMM is the same
     # kernel; the dispatches alternate, routed first)
     "finegrained_bf16": {
         "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
                                                  "common.h"),
-        "source_sha256": "1e82a91c95e4d3900492127637559a37ac9095fadfe783c510c27b9c2631442d",
-        "fetch_kib": 753263.7, "write_kib": 114982.1},
+        "source_sha256": "fc86d9cdea1b988988232414c56d2fa4015ca5d6ea737f0f9d850a091033c66a",
+        "fetch_kib": 750787.4, "write_kib": 114981.5},
     "atomic_bf16": {
         "kernel": "k_atomic_token", "sources": ("atomic.hip", "common.h"),
-        "source_sha256": "57cff026d7a755084011a9121682f1fde2bbc20b57f600a1a1a4583a0a9b3c50",
-        "fetch_kib": 535716.2, "write_kib": 16384.0},
+        "source_sha256": "1e687dcc3a4401774b2ae1ae164576426d5288005556b988989946c3a48945dd",
+        "fetch_kib": 535640.4, "write_kib": 16384.0},
     "mixtral_mxfp8": {
         "kernel": "k_gemm_mx", "sources": ("gemm_mx.hip", "gemm_args.h", "gemm_common.h",
                                            "common.h"),
-        "source_sha256": "5b2ff55fdb3f2ee19e4c61ce2c70fa55f61c8cbdeed9419514b749502e637156",
-        "fetch_kib": 853991.1, "write_kib": 123547.3},
+        "source_sha256": "feb07cc4747523912574bcde94f43817e257fd6c6ec09f6296db5181f86e42f9",
+        "fetch_kib": 854637.0, "write_kib": 123550.0},
 }
 
 
