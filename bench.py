@@ -40,28 +40,28 @@ TRAFFIC = {
     "mixtral_bf16": {
         "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
                                                  "common.h"),
-        "source_sha256": "fc86d9cdea1b988988232414c56d2fa4015ca5d6ea737f0f9d850a091033c66a",
+        "source_sha256": "bd3814653cb09c5764dabee86f17fb80c0429e1125a86f412ec8243769ddd731",
         "fetch_kib": 1836491.8, "write_kib": 230442.4},
     "variable_bcsr_bf16": {
         "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
                                                  "common.h"),
-        "source_sha256": "fc86d9cdea1b988988232414c56d2fa4015ca5d6ea737f0f9d850a091033c66a",
+        "source_sha256": "bd3814653cb09c5764dabee86f17fb80c0429e1125a86f412ec8243769ddd731",
         "fetch_kib": 30441.6, "write_kib": 48309.5},
     # the routed first GEMM only (the shared experts' first GEMM is the same
     # kernel; the dispatches alternate, routed first)
     "finegrained_bf16": {
         "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
                                                  "common.h"),
-        "source_sha256": "fc86d9cdea1b988988232414c56d2fa4015ca5d6ea737f0f9d850a091033c66a",
+        "source_sha256": "bd3814653cb09c5764dabee86f17fb80c0429e1125a86f412ec8243769ddd731",
         "fetch_kib": 750787.4, "write_kib": 114981.5},
     "atomic_bf16": {
         "kernel": "k_atomic_token", "sources": ("atomic.hip", "common.h"),
-        "source_sha256": "1e687dcc3a4401774b2ae1ae164576426d5288005556b988989946c3a48945dd",
+        "source_sha256": "7020a44046cfa9c4bc2ee1d7087ff80709367bd331479c1dadda27f72bc9993a",
         "fetch_kib": 535640.4, "write_kib": 16384.0},
     "mixtral_mxfp8": {
         "kernel": "k_gemm_mx", "sources": ("gemm_mx.hip", "gemm_args.h", "gemm_common.h",
                                            "common.h"),
-        "source_sha256": "feb07cc4747523912574bcde94f43817e257fd6c6ec09f6296db5181f86e42f9",
+        "source_sha256": "858494e9dbffc4975986048088043e850b9cfdc72cc04d29d3cabf033fb5ea5d",
         "fetch_kib": 854637.0, "write_kib": 123550.0},
 }
 

@@ -101,13 +101,10 @@ __device__ __forceinline__ float gelu_tanh_grad(float z) {
   return 0.5f * (1.0f + t) + 0.5f * z * (1.0f - t * t) * c * (1.0f + 0.134145f * z * z);
 }
 
-__device__ __forceinline__ uint64_t lanemask_lt() {
-  return (uint64_t(1) << (threadIdx.x & 63)) - 1;
-}
-
 // Set bits of a wave-uniform lane mask in the lanes below this one (the
 // lane's rank among the set lanes), by the mbcnt pair: two instructions,
-// where popcount(mask & lanemask_lt()) takes a 64-bit AND and two counts.
+// where a popcount of the mask ANDed with a per-lane mask of the lower lanes
+// takes a 64-bit AND and two counts.
 __device__ __forceinline__ int rank_below(uint64_t mask) {
   return int(__builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32),
                                        __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u)));

@@ -967,8 +967,6 @@ __global__ void __launch_bounds__(256) k_pack_swiglu(const T* __restrict__ w1,
 
 }  // namespace
 
-int gemm_tile_bf(int dtype) { return dtype == 0 ? 64 : 256; }
-int gemm_tile_bt(int dtype, int bcsr) { return dtype == 0 ? 64 : 256; }
 
 hipError_t launch_plan(const PlanArgs& p, hipStream_t s) {
   hipLaunchKernelGGL(k_plan, dim3(kPlanSlices), dim3(1024), 0, s, p);

@@ -120,7 +120,5 @@ int gemm_persistent_grid(int tiles);
 // The epilogue of the split tiles of a persistent launch planned for it
 // (grid: workgroups, at least the number of split tiles).
 hipError_t launch_piece_fixup(const GemmArgs& a, int bf, int bt, int grid, hipStream_t s);
-int gemm_tile_bf(int dtype);   // packed features per tile the GEMM kernels use
-int gemm_tile_bt(int dtype, int bcsr);
 
 }  // namespace moe
