@@ -36,16 +36,22 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 // reads past num_records return zero).
 constexpr int kRsrcWord3 = 0x00020000;
 
-// E4M3 code of a finite a: nearest-even on 3 mantissa bits, magnitudes of
-// 448 and above saturated to 448, subnormals on the 2^-9 grid.
-__device__ __forceinline__ uint32_t e4m3_code(float a) {
-  const uint32_t sign = (__float_as_uint(a) >> 24) & 0x80u;
-  const float m = fabsf(a);
-  if (!(m < 448.f)) return sign | 0x7Eu;
-  if (m < 0.015625f) return sign | uint32_t(__builtin_rintf(m * 512.f));   // 0..8
-  uint32_t b = __float_as_uint(m);
-  b += 0x7FFFFu + ((b >> 20) & 1u);            // round to 3 mantissa bits, ties to even
-  return sign | ((((b >> 23) - 120u) & 0xFu) << 3) | ((b >> 20) & 7u);
+// E4M3 codes of four finite values, the first in the low byte: nearest-even
+// on 3 mantissa bits, magnitudes of 448 and above saturated to 448,
+// subnormals on the 2^-9 grid.  gfx950's v_cvt_pk_fp8_f32 converts a pair
+// to OCP E4M3 with round-to-nearest-even; clamped to +-448 first (past the
+// largest normal the instruction itself would give NaN), its codes equal this
+// rounding exactly, checked on the GPU for both signs over a dense mantissa
+// sweep of every exponent a block-scaled value can take, every midpoint
+// between neighbouring codes and the floats either side of it, the
+// subnormals, zero and the saturation range.
+__device__ __forceinline__ uint32_t e4m3_pk_pair(float a, float b) {
+  const float ca = __builtin_fminf(__builtin_fmaxf(a, -448.f), 448.f);
+  const float cb = __builtin_fminf(__builtin_fmaxf(b, -448.f), 448.f);
+  return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false)) & 0xFFFFu;
+}
+__device__ __forceinline__ uint32_t e4m3_x4(float a, float b, float c, float d) {
+  return e4m3_pk_pair(a, b) | (e4m3_pk_pair(c, d) << 16);
 }
 
 // Shared exponent of a block whose largest magnitude is amax:
@@ -87,8 +93,7 @@ __global__ void __launch_bounds__(256) k_quant_mx(const uint16_t* __restrict__ s
     uint32_t w[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      w[h] = e4m3_code(f[4 * h] * inv) | (e4m3_code(f[4 * h + 1] * inv) << 8) |
-             (e4m3_code(f[4 * h + 2] * inv) << 16) | (e4m3_code(f[4 * h + 3] * inv) << 24);
+      w[h] = e4m3_x4(f[4 * h] * inv, f[4 * h + 1] * inv, f[4 * h + 2] * inv, f[4 * h + 3] * inv);
     *reinterpret_cast<uint2*>(codes + row * ldc + k0) = make_uint2(w[0], w[1]);
     if ((lane & 3) == 0) scales[row * ldsc + k0 / 32] = uint8_t(s + 127);
   }
@@ -106,8 +111,7 @@ __device__ __forceinline__ int mx_block_codes(const float (&o)[16], uint32_t (&w
   const float inv = ldexpf(1.f, -s);
 #pragma unroll
   for (int g = 0; g < 4; ++g)
-    w[g] = e4m3_code(o[4 * g] * inv) | (e4m3_code(o[4 * g + 1] * inv) << 8) |
-           (e4m3_code(o[4 * g + 2] * inv) << 16) | (e4m3_code(o[4 * g + 3] * inv) << 24);
+    w[g] = e4m3_x4(o[4 * g] * inv, o[4 * g + 1] * inv, o[4 * g + 2] * inv, o[4 * g + 3] * inv);
   return s;
 }
 

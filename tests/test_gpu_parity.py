@@ -641,7 +641,35 @@ def _mx_pack_input():
     v[1, 40] = 500.0
     v[1, 64:96] = np.float32(2.0 ** 120)             # large exponents
     v[1, 96:128] = -np.float32(2.0 ** -100)
+    # every midpoint between neighbouring E4M3 codes and the bf16 values just
+    # below and above it, both signs, in blocks whose largest element 256 sets
+    # the scale (rows 2-4: block exponents 0, -20 and +10); all exactly bf16
+    tests = _e4m3_midpoint_values()
+    per = 31
+    for row, t in ((2, 0), (3, -20), (4, 10)):
+        for b in range(0, len(tests), per):
+            blk = b // per
+            chunk = tests[b:b + per]
+            v[row, 32 * blk] = 256.0 * 2.0 ** t
+            v[row, 32 * blk + 1:32 * blk + 1 + len(chunk)] = chunk * 2.0 ** t
+            v[row, 32 * blk + 1 + len(chunk):32 * (blk + 1)] = 0.0
     return synth._to_bf16_bits(v)
+
+
+def _e4m3_midpoint_values():
+    """The midpoint between each pair of neighbouring positive E4M3 values
+    (codes 0..126; normals have 3 mantissa bits, subnormals step 2^-9), the
+    bf16 values one unit below and above it, and the negatives of all."""
+    def value(c):
+        e, m = (c >> 3) & 15, c & 7
+        return m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+    out = []
+    for c in range(126):
+        mid = 0.5 * (value(c) + value(c + 1))
+        ulp = 2.0 ** (np.floor(np.log2(mid)) - 7)     # bf16 unit at mid
+        out += [mid, mid - ulp, mid + ulp]
+    out = np.array(out, dtype=np.float64)
+    return np.concatenate([out, -out]).astype(np.float32)
 
 
 def test_pack_mxfp8_bit_exact(dev):
