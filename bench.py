@@ -61,8 +61,8 @@ TRAFFIC = {
     "mixtral_mxfp8": {
         "kernel": "k_gemm_mx", "sources": ("gemm_mx.hip", "gemm_args.h", "gemm_common.h",
                                            "common.h"),
-        "source_sha256": "858494e9dbffc4975986048088043e850b9cfdc72cc04d29d3cabf033fb5ea5d",
-        "fetch_kib": 854637.0, "write_kib": 123550.0},
+        "source_sha256": "37cbba53bcbae836fdb2aeb8855be3c81d72f25c3fd15e7d85ed92a6e85d8925",
+        "fetch_kib": 868020.1, "write_kib": 132105.6},
 }
 
 
