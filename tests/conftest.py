@@ -13,8 +13,8 @@ def pytest_configure(config):
 
 def pytest_terminal_summary(terminalreporter, exitstatus, config):
     """Print the errors the parity tests measured (max|gpu-ref|/max|ref| per
-    output, mismatch counts), one line per case, and keep them in
-    gpurun_out/parity_errors.txt when that folder exists."""
+    output, mismatch counts), one line per case, and also write them to the
+    file that the environment variable MOE_PARITY_ERRORS names, if set."""
     try:
         import gpu_cases
     except Exception:
@@ -29,7 +29,7 @@ def pytest_terminal_summary(terminalreporter, exitstatus, config):
     terminalreporter.write_sep("-", "measured parity errors")
     for line in lines:
         terminalreporter.write_line(line)
-    out = os.path.join(ROOT, "gpurun_out")
-    if os.path.isdir(out):
-        with open(os.path.join(out, "parity_errors.txt"), "w") as fh:
+    path = os.environ.get("MOE_PARITY_ERRORS")
+    if path:
+        with open(path, "w") as fh:
             fh.write("\n".join(lines) + "\n")
