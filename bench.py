@@ -40,19 +40,19 @@ TRAFFIC = {
     "mixtral_bf16": {
         "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
                                                  "common.h"),
-        "source_sha256": "bd3814653cb09c5764dabee86f17fb80c0429e1125a86f412ec8243769ddd731",
+        "source_sha256": "57e127141eff60a7a0ee524974ca69b8055745814db4bf6b00de8966b775fa5b",
         "fetch_kib": 1836491.8, "write_kib": 230442.4},
     "variable_bcsr_bf16": {
         "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
                                                  "common.h"),
-        "source_sha256": "bd3814653cb09c5764dabee86f17fb80c0429e1125a86f412ec8243769ddd731",
+        "source_sha256": "57e127141eff60a7a0ee524974ca69b8055745814db4bf6b00de8966b775fa5b",
         "fetch_kib": 30441.6, "write_kib": 48309.5},
     # the routed first GEMM only (the shared experts' first GEMM is the same
     # kernel; the dispatches alternate, routed first)
     "finegrained_bf16": {
         "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
                                                  "common.h"),
-        "source_sha256": "bd3814653cb09c5764dabee86f17fb80c0429e1125a86f412ec8243769ddd731",
+        "source_sha256": "57e127141eff60a7a0ee524974ca69b8055745814db4bf6b00de8966b775fa5b",
         "fetch_kib": 750787.4, "write_kib": 114981.5},
     "atomic_bf16": {
         "kernel": "k_atomic_token", "sources": ("atomic.hip", "common.h"),
@@ -537,9 +537,8 @@ def main():
             "mfma_floor_ms": f1 / (PEAK_TFLOPS[dtype] * 1e12) * 1e3,
             "frac_of_floor": floor_ms / g1})
         rows = int(offsets[-1])
-        # Algorithmic bytes.  combine: every kept expert row, x read, out written
-        # (the layer's own combine also reads the second K-split plane of the
-        # expert outputs when the second GEMM is split).  dispatch: each token row
+        # Algorithmic bytes.  combine: every kept expert row, x read, out written.
+        # dispatch: each token row
         # read once and each kept row written once (moe_dispatch with x_perm; the
         # layer's dispatch moves indices only, the first GEMM gathers the rows).
         # router: x and the router weights read once.

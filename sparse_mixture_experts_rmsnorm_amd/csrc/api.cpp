@@ -211,9 +211,6 @@ struct ExpertWs {
   int* counters = nullptr;
   float* a_rows = nullptr;
   int64_t mt1 = 0, mt2 = 0;
-  int ksplit = 1;        // K parts of the second linear (1, 2 or 4)
-  void* ypart = nullptr;   // [ksplit][rows_max][d] gated partials (ksplit > 1), dtype
-  int64_t plane = 0;
   int64_t rows_max = 0;
   // MXFP8: the quantised GEMM rows and hidden activation with their scales
   uint8_t* xq = nullptr;   // [rows_max, d]
@@ -249,59 +246,54 @@ void fit_dense_tiles(ExpertGeo* g, int dtype, int64_t d, int64_t T) {
   if (tiles < device_cus()) g->bt2 = 128;
 }
 
-// Second-linear K split: the tile count of a grouped layer is only known on
-// the device, so the host estimates it (T k / bt + E / 2 row tiles per output
-// slice) and models the time of split s in units of one full-K tile: the
-// rounds of tiles over the compute units, each 1 / s of a tile, plus a fixed
-// cost per round (a tile's prologue and epilogue) and per extra partial plane
-// (written by the GEMM, read by combine).  Splits of 1, 2 or 4 whose parts are
-// whole K stages of every expert are considered.  The MXFP8 path then writes s
-// planes; the bf16 path takes any s > 1 as the signal to cut only the last
-// round of tiles into K pieces (carve_expert_ws).
-int choose_ksplit(const ExpertGeo& g, int dtype, int64_t d, int64_t rows_used_est) {
-  if (g.bcsr || g.atomic || dtype != MOE_BF16 || g.kdiv < 2) return 1;
-  constexpr double kRoundCost = 0.017, kPlaneCost = 0.031;
+// Whether the second linear's last round of tiles is worth cutting into K
+// pieces.  The tile count of a grouped layer is only known on the device, so
+// the host estimates it (T k / bt + E / 2 row tiles per output slice) and
+// models the time of splitting every tile in s parts, in units of one full-K
+// tile: the rounds of tiles over the compute units, each 1 / s of a tile, plus
+// a fixed cost per round (a tile's prologue and epilogue) and per extra part
+// (its partial stores and their reduction).  Splits of 1, 2 or 4 whose parts
+// are whole K stages of every expert are considered; a split that beats whole
+// tiles says that the last round leaves compute units idle, and then only
+// that round's tiles are cut (carve_expert_ws).
+bool want_pieces(const ExpertGeo& g, int dtype, int64_t d, int64_t rows_used_est) {
+  if (g.bcsr || g.atomic || dtype != MOE_BF16 || g.kdiv < 2) return false;
+  constexpr double kRoundCost = 0.017, kPartCost = 0.031;
   const double cus = device_cus();
   const double n = (double(rows_used_est) / g.bt + 0.5 * double(g.E)) * double(d / g.bf2);
   int best = 1;
   double best_t = 0;
   for (int s = 1; s <= g.kdiv; s *= 2) {
     const double rounds = std::ceil(s * n / cus);
-    const double t = rounds / s + kRoundCost * rounds + kPlaneCost * (s - 1);
+    const double t = rounds / s + kRoundCost * rounds + kPartCost * (s - 1);
     if (s == 1 || t < best_t) {
       best = s;
       best_t = t;
     }
   }
-  return best;
+  return best > 1;
 }
 
 void carve_expert_ws(Carve& c, const ExpertGeo& g, int dtype, int64_t d, int64_t rows_max,
-                     int64_t nnz_max, ExpertWs* w, int ksplit = 1, bool save = false) {
+                     int64_t nnz_max, ExpertWs* w, bool pieces = false, bool save = false) {
   if (g.atomic) {
     w->a_rows = c.take_n<float>(rows_max);
     return;
   }
-  // bf16 experts whose second linear needs its K split to fill the last
-  // round of tiles (ksplit > 1) cut only that round's tiles into K pieces,
-  // summed in fp32 by the fixup kernel, instead of splitting every tile into
-  // partial planes that combine adds (measured: the same balance with one
-  // quarter of the partial traffic and a single rounding of y).  Elsewhere
-  // the pieces' partial stores and fixup cost more than the idle compute
-  // units of the last round.
-  const bool pieces = dtype == MOE_BF16 && !g.mx && ksplit > 1;
-  if (pieces) ksplit = 1;
-  w->ksplit = ksplit;
+  // bf16 and MXFP8 experts whose second linear leaves compute units idle in
+  // its last round of tiles (pieces) cut only that round's tiles into K
+  // pieces, summed in fp32 by the fixup kernel (measured against splitting
+  // every tile into partial planes that combine adds: the same balance with
+  // one quarter of the partial traffic and a single rounding of y).
+  // Elsewhere the pieces' partial stores and fixup cost more than the idle
+  // compute units of the last round.
+  pieces = pieces && dtype == MOE_BF16;
   w->mt1 = std::max<int64_t>(1, max_tiles_gemm1(g, rows_max, nnz_max));
-  w->mt2 = std::max<int64_t>(1, max_tiles_gemm2(g, d, rows_max) * ksplit);
+  w->mt2 = std::max<int64_t>(1, max_tiles_gemm2(g, d, rows_max));
   if (pieces) {
     w->grid2 = gemm_persistent_grid(int(std::min<int64_t>(w->mt2, 1 << 30)));
     w->part = c.take_n<float>(int64_t(w->grid2) * g.bf2 * g.bt2);
     w->counters = c.take_n<int>(w->grid2);
-  }
-  if (ksplit > 1) {
-    w->plane = rows_max * d;
-    w->ypart = c.take(size_t(ksplit * w->plane) * esize(dtype));
   }
   w->rows_max = rows_max;
   if (g.mx) {
@@ -380,11 +372,15 @@ int run_expert_gemms_mx(const moe_experts_desc* X, const ExpertGeo& g, int64_t d
   a.ldws = d / 32;
   a.ys = w.hqs;
   a.ldys = g.Fmax / 32;
+  a.g.xcd_runs = w.grid1 > 0;
+  a.g.part = w.part;
+  a.g.counters = w.counters;
   a.x_bytes = RP * d;
   a.w_bytes = P * d;
   a.xs_bytes = RP * (d / 32);
   a.ws_bytes = P * (d / 32);
-  MOE_HIP(launch_gemm_mx(a, int(w.mt1), s));
+  MOE_HIP(launch_gemm_mx(a, w.grid1 > 0 ? w.grid1 : int(w.mt1), s));
+  if (w.grid1 > 0) MOE_HIP(launch_piece_fixup(a.g, g.bf1, g.bt, w.grid1, s));
   timer_mark(timer, call, MOE_STAGE_GEMM1 + 1, s);
 
   MxGemmArgs b{};
@@ -398,11 +394,9 @@ int run_expert_gemms_mx(const moe_experts_desc* X, const ExpertGeo& g, int64_t d
   b.g.ldy = d;
   b.g.row_w = row_w;
   b.g.epi = EPI_GATE;
-  if (w.ksplit > 1) {
-    b.g.epi = EPI_GATE_SPLIT;
-    b.g.Y = w.ypart;
-    b.g.ysplit = w.plane;
-  }
+  b.g.xcd_runs = w.grid2 > 0;
+  b.g.part = w.part;
+  b.g.counters = w.counters;
   b.xs = w.hqs;
   b.ldxs = g.Fmax / 32;
   b.ws = X->w2_scale;
@@ -411,7 +405,8 @@ int run_expert_gemms_mx(const moe_experts_desc* X, const ExpertGeo& g, int64_t d
   b.w_bytes = d * g.F;
   b.xs_bytes = RP * (g.Fmax / 32);
   b.ws_bytes = d * (g.F / 32);
-  MOE_HIP(launch_gemm_mx(b, int(w.mt2), s));
+  MOE_HIP(launch_gemm_mx(b, w.grid2 > 0 ? w.grid2 : int(w.mt2), s));
+  if (w.grid2 > 0) MOE_HIP(launch_piece_fixup(b.g, g.bf2, g.bt2, w.grid2, s));
   timer_mark(timer, call, MOE_STAGE_GEMM2 + 1, s);
   (void)dense_rows;
   return MOE_OK;
@@ -446,6 +441,7 @@ int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, i
   p.grid = w.grid1;
   p.max_parts = 4;
   p.counters = nullptr;
+  p.kstage = g.mx ? 128 : 64;   // the GEMM kernel's K stage (pieces are whole stages)
   // second linear
   PlanArgs p2 = p;
   p2.gemm = 2;
@@ -455,7 +451,7 @@ int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, i
   p2.tiles = w.tiles2;
   p2.ntiles = w.nt + 16;
   p2.max_tiles = int(w.mt2);
-  p2.ksplit = w.ksplit;
+  p2.ksplit = 1;
   p2.bt = g.bt2;
   p2.grid = w.grid2;
   p2.counters = w.counters;
@@ -500,11 +496,6 @@ int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, i
   b.row_r = nullptr;
   b.row_w = row_w;
   b.epi = EPI_GATE;
-  if (w.ksplit > 1) {
-    b.epi = EPI_GATE_SPLIT;
-    b.Y = w.ypart;
-    b.ysplit = w.plane;
-  }
   b.xcd_runs = w.grid2 > 0;
   b.part = w.part;
   b.counters = w.counters;
@@ -1081,12 +1072,12 @@ void carve_layer(Carve& c, const moe_layer_desc* L, int64_t T, const ExpertGeo& 
     w->row_offsets = w->column_indices = w->nnz = nullptr;
   }
   const int64_t rows_est = std::min(T * k, E * std::min(w->cap, T));
-  const int ks = choose_ksplit(g, L->dtype, d, rows_est);
-  carve_expert_ws(c, g, L->dtype, d, w->rows_max, nnz_max, &w->ex, ks, L->save_for_backward != 0);
-  // y_perm in one plane unless the second linear writes K-split planes
-  w->y = w->ex.ksplit > 1 ? nullptr : c.take(size_t(g.atomic ? T : w->rows_max) * d * es);
+  const bool pieces = want_pieces(g, L->dtype, d, rows_est);
+  carve_expert_ws(c, g, L->dtype, d, w->rows_max, nnz_max, &w->ex, pieces,
+                  L->save_for_backward != 0);
+  w->y = c.take(size_t(g.atomic ? T : w->rows_max) * d * es);
   if (L->shared) {
-    carve_expert_ws(c, gs, L->dtype, d, T, 0, &w->sh, 1, L->save_for_backward != 0);
+    carve_expert_ws(c, gs, L->dtype, d, T, 0, &w->sh, false, L->save_for_backward != 0);
     w->s = c.take(size_t(T) * d * es);
   } else {
     w->s = nullptr;
@@ -1248,12 +1239,8 @@ int moe_layer_forward(const moe_layer_desc* L, const void* x, int64_t T, void* o
   timer_mark(tm, call, MOE_STAGE_SHARED + 1, stream);
 
   // 5. combine
-  if (w.ex.ksplit > 1)
-    MOE_HIP(launch_combine_split(w.ex.ypart, w.ex.ksplit, w.rows_max, w.pos,
-                                 L->residual ? x : nullptr, w.s, L->dtype, T, d, k, out, stream));
-  else
-    MOE_HIP(launch_combine(w.y, g.atomic ? nullptr : w.pos, L->residual ? x : nullptr, w.s,
-                           L->dtype, T, d, k, out, stream));
+  MOE_HIP(launch_combine(w.y, g.atomic ? nullptr : w.pos, L->residual ? x : nullptr, w.s,
+                         L->dtype, T, d, k, out, stream));
   timer_mark(tm, call, MOE_STAGE_COMBINE + 1, stream);
   return ok();
 }

@@ -21,18 +21,16 @@ namespace {
 // flight).  The token's slot positions are read once (lane j holds slot
 // j + 64 q) and broadcast slot by slot; the expert rows of four slots are
 // loaded together before they are added, so several gathers are in flight.
-// NP > 1: each expert row is the sum of NP K-split partial planes
-// (y, y + plane, ...), added in plane order before it joins the token's sum.
 // The sum starts from x itself, so a token whose slots were all dropped
 // stores x bit for bit.
-template <typename T, int NP>
-__global__ void __launch_bounds__(256) k_combine(const T* __restrict__ y, int64_t plane,
+template <typename T>
+__global__ void __launch_bounds__(256) k_combine(const T* __restrict__ y,
                                                  const int32_t* __restrict__ pos,
                                                  const T* __restrict__ x, const T* __restrict__ sh,
                                                  int64_t Tn, int64_t d, int k, int parts,
                                                  T* __restrict__ out) {
   constexpr int N = Vec16<T>::N;
-  constexpr int SB = NP > 2 ? 2 : 4;            // slots per batch of loads
+  constexpr int SB = 4;                         // slots per batch of loads
   const int lane = threadIdx.x & 63;
   const int64_t g = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t t = g / parts;
@@ -40,7 +38,6 @@ __global__ void __launch_bounds__(256) k_combine(const T* __restrict__ y, int64_
   const int64_t nvec = d / N;
   const int64_t vlen = nvec / parts, v0 = (g - t * parts) * vlen;
   const uint4* ys = reinterpret_cast<const uint4*>(y);
-  const int64_t pv = plane / N;
   int pl[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -67,30 +64,21 @@ __global__ void __launch_bounds__(256) k_combine(const T* __restrict__ y, int64_
       for (int q = 0; q < 4; ++q) {
         const int nq = min(64, k - 64 * q);
         for (int j0 = 0; j0 < nq; j0 += SB) {
-          uint4 a[SB][NP];
+          uint4 a[SB];
           bool ok[SB];
 #pragma unroll
           for (int u = 0; u < SB; ++u) {
             const int p = j0 + u < nq ? __builtin_amdgcn_readlane(pl[q], j0 + u) : -1;
             ok[u] = p >= 0;
-#pragma unroll
-            for (int c = 0; c < NP; ++c)
-              a[u][c] = ok[u] ? ys[c * pv + int64_t(p) * nvec + v] : make_uint4(0, 0, 0, 0);
+            a[u] = ok[u] ? ys[int64_t(p) * nvec + v] : make_uint4(0, 0, 0, 0);
           }
 #pragma unroll
           for (int u = 0; u < SB; ++u) {
             if (!ok[u]) continue;
-            float f0[8];
-            unpack16(a[u][0], f0, (const T*)nullptr);
+            float f[8];
+            unpack16(a[u], f, (const T*)nullptr);
 #pragma unroll
-            for (int c = 1; c < NP; ++c) {
-              float f1[8];
-              unpack16(a[u][c], f1, (const T*)nullptr);
-#pragma unroll
-              for (int i = 0; i < N; ++i) f0[i] += f1[i];
-            }
-#pragma unroll
-            for (int i = 0; i < N; ++i) acc[i] += f0[i];
+            for (int i = 0; i < N; ++i) acc[i] += f[i];
           }
         }
       }
@@ -115,42 +103,19 @@ static int combine_parts(int64_t d, int dtype) {
   return p;
 }
 
-hipError_t launch_combine_split(const void* y0, int nplanes, int64_t rows_max, const int32_t* pos,
-                                const void* x, const void* shared, int dtype, int64_t T,
-                                int64_t d, int k, void* out, hipStream_t s) {
-  if (T == 0) return hipSuccess;
-  if (nplanes != 2 && nplanes != 4) return hipErrorInvalidValue;
-  const int parts = combine_parts(d, dtype);
-  const dim3 g(unsigned((T * parts + 3) / 4));
-#define MOE_COMBINE_SPLIT(TY, NPV)                                                             \
-  hipLaunchKernelGGL((k_combine<TY, NPV>), g, dim3(256), 0, s, static_cast<const TY*>(y0),     \
-                     rows_max * d, pos, static_cast<const TY*>(x),                             \
-                     static_cast<const TY*>(shared), T, d, k, parts, static_cast<TY*>(out))
-  if (dtype == 0) {
-    if (nplanes == 2) MOE_COMBINE_SPLIT(float, 2);
-    else MOE_COMBINE_SPLIT(float, 4);
-  } else {
-    if (nplanes == 2) MOE_COMBINE_SPLIT(uint16_t, 2);
-    else MOE_COMBINE_SPLIT(uint16_t, 4);
-  }
-#undef MOE_COMBINE_SPLIT
-  return hipGetLastError();
-}
-
 hipError_t launch_combine(const void* y, const int32_t* pos, const void* x, const void* shared,
                           int dtype, int64_t T, int64_t d, int k, void* out, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int parts = combine_parts(d, dtype);
   const dim3 g(unsigned((T * parts + 3) / 4));
   if (dtype == 0)
-    hipLaunchKernelGGL((k_combine<float, 1>), g, dim3(256), 0, s, static_cast<const float*>(y),
-                       int64_t(0), pos, static_cast<const float*>(x),
-                       static_cast<const float*>(shared), T, d, k, parts, static_cast<float*>(out));
+    hipLaunchKernelGGL(k_combine<float>, g, dim3(256), 0, s, static_cast<const float*>(y), pos,
+                       static_cast<const float*>(x), static_cast<const float*>(shared), T, d, k,
+                       parts, static_cast<float*>(out));
   else
-    hipLaunchKernelGGL((k_combine<uint16_t, 1>), g, dim3(256), 0, s,
-                       static_cast<const uint16_t*>(y), int64_t(0), pos,
-                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(shared), T,
-                       d, k, parts, static_cast<uint16_t*>(out));
+    hipLaunchKernelGGL(k_combine<uint16_t>, g, dim3(256), 0, s, static_cast<const uint16_t*>(y),
+                       pos, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(shared),
+                       T, d, k, parts, static_cast<uint16_t*>(out));
   return hipGetLastError();
 }
 

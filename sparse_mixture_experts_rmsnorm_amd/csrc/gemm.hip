@@ -65,7 +65,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const Tile& til
     float rs = 1.f;
     if (EPI == EPI_ACT || EPI == EPI_SWIGLU) rs = a.row_r[row];
     if (EPI == EPI_SCALE_F32) rs = a.row_r ? a.row_r[row] : 1.f;
-    if (EPI == EPI_GATE || EPI == EPI_GATE_SPLIT) rs = a.row_w ? a.row_w[row] : 1.f;
+    if (EPI == EPI_GATE) rs = a.row_w ? a.row_w[row] : 1.f;
     if ((EPI == EPI_SWIGLU || EPI == EPI_ACT) && a.pre) {
       // pre-activations for the backward pass, in the packed feature order
       uint16_t* P = static_cast<uint16_t*>(a.pre) + int64_t(row) * a.ldpre +
@@ -116,8 +116,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const Tile& til
           *reinterpret_cast<float4*>(Y + i * 32 + g * 8 + fh * 4) = o;
         }
     } else {
-      uint16_t* Y = static_cast<uint16_t*>(a.Y) + int64_t(row) * a.ldy + tile.ocol0 + wf * WTF +
-                    (EPI == EPI_GATE_SPLIT ? int64_t(tile.spare) * a.ysplit : 0);
+      uint16_t* Y = static_cast<uint16_t*>(a.Y) + int64_t(row) * a.ldy + tile.ocol0 + wf * WTF;
       // one loop nest per activation, chosen by a uniform branch: inside the
       // unrolled loop a runtime choice would be if-converted into computing
       // both activations of every value
@@ -188,33 +187,6 @@ __device__ __forceinline__ void epilogue_f32_lds(const GemmArgs& a, const Tile& 
     }
     __syncthreads();
   }
-}
-
-// K pieces of a split tile.  Each piece stores its fp32 partial sums at its
-// slot of the partial buffer in fragment order (block (i, j) of wave w at
-// ((w MF + i) MT + j) 1024 + 16 lane floats), so that the lane of the fixup
-// kernel that reads them back holds exactly the values the same lane of a
-// whole tile would.  No workgroup waits for another: the fixup kernel runs
-// after the GEMM on the same stream.
-template <int BF, int BT, int MF, int MT>
-__device__ __forceinline__ int64_t piece_frag_offset(int wid, int lane, int i, int j) {
-  return int64_t(wid) * (MF * MT * 1024) + (i * MT + j) * 1024 + lane * 16;
-}
-
-template <int BF, int BT, int MF, int MT>
-__device__ __forceinline__ void store_piece(const GemmArgs& a, const Tile& tile,
-                                            const f32x16 (&acc)[MF][MT], int wid, int lane) {
-  float* const dst0 = a.part + (int64_t(tile.pslot0) + tile.part) * (int64_t(BF) * BT);
-#pragma unroll
-  for (int i = 0; i < MF; ++i)
-#pragma unroll
-    for (int j = 0; j < MT; ++j) {
-      f32x4* dst = reinterpret_cast<f32x4*>(dst0 + piece_frag_offset<BF, BT, MF, MT>(wid, lane, i, j));
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        dst[v] = f32x4{acc[i][j][4 * v], acc[i][j][4 * v + 1], acc[i][j][4 * v + 2],
-                       acc[i][j][4 * v + 3]};
-    }
 }
 
 // Fixup of split tiles: one wave per workgroup, WGF x WGT workgroups per
@@ -332,7 +304,7 @@ __global__ void __launch_bounds__(64 * WGF * WGT, 1) k_gemm_bf16_dma(GemmArgs a)
   auto set_sources = [&](const Tile& t) {
     const int xlast = t.row_end - 1;
     // a K-split tile reads its own part of the activation row
-    const int xk0 = ((EPI == EPI_GATE_SPLIT || EPI == EPI_SCALE_F32) ? t.spare * t.klen : 0) + t.xk;
+    const int xk0 = (EPI == EPI_SCALE_F32 ? t.spare * t.klen : 0) + t.xk;
 #pragma unroll
     for (int u = 0; u < SPW; ++u) {
       const int row = (wid * SPW + u) * RSEG + srow;
@@ -609,7 +581,7 @@ __global__ void __launch_bounds__(256) k_gemm_f32(GemmArgs a) {
     float rs = 1.f;
     if (EPI == EPI_ACT || EPI == EPI_SWIGLU) rs = a.row_r[row];
     if (EPI == EPI_SCALE_F32) rs = a.row_r ? a.row_r[row] : 1.f;
-    if (EPI == EPI_GATE || EPI == EPI_GATE_SPLIT) rs = a.row_w ? a.row_w[row] : 1.f;
+    if (EPI == EPI_GATE) rs = a.row_w ? a.row_w[row] : 1.f;
     float* Y = static_cast<float*>(a.Y) + int64_t(row) * a.ldy + tile.ocol0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -897,12 +869,13 @@ __device__ __forceinline__ void plan_tiles(const PlanArgs& p, int slice, int nsl
     t.pslot0 = pslot0;
     if (nparts > 1 && part == 0) p.counters[group] = o;
     if (nparts > 1) {
-      // whole 64-wide K stages: part j takes stages [j nk / P, (j + 1) nk / P)
-      const int nk = t.klen / 64;
+      // whole K stages: part j takes stages [j nk / P, (j + 1) nk / P)
+      const int ks = p.kstage > 0 ? p.kstage : 64;
+      const int nk = t.klen / ks;
       const int k0 = part * nk / nparts, k1 = (part + 1) * nk / nparts;
-      t.kofs += k0 * 64;
-      t.xk = k0 * 64;
-      t.klen = (k1 - k0) * 64;
+      t.kofs += k0 * ks;
+      t.xk = k0 * ks;
+      t.klen = (k1 - k0) * ks;
     }
     p.tiles[o] = t;
   }
@@ -1020,7 +993,6 @@ hipError_t launch_gemm(int dtype, const GemmArgs& a, int bf, int bt, int grid, h
       case EPI_SWIGLU: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, EPI_SWIGLU>), g, b8, 0, s, a); break;
       case EPI_GATE: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, EPI_GATE>), g, b8, 0, s, a); break;
       case EPI_SCALE_F32: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, EPI_SCALE_F32>), g, b8, 0, s, a); break;
-      case EPI_GATE_SPLIT: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, EPI_GATE_SPLIT>), g, b8, 0, s, a); break;
       case EPI_STORE_T: hipLaunchKernelGGL((k_gemm_bf16_dma<256, 256, 4, 2, EPI_STORE_T>), g, b8, 0, s, a); break;
       default: return hipErrorInvalidValue;
     }

@@ -28,14 +28,12 @@ struct Tile {
   int pslot0;         // partial-buffer slot of part 0 (pieces only)
 };
 
-// EPI_GATE_SPLIT: gated partial of one K split, written to Y + split * ysplit.
 // EPI_STORE_T: the plain accumulator in bf16 over a tile whose last
 // features may be missing (tile.spare = the features that exist, a multiple
 // of 32; the backward of the second linear).  EPI_SCALE_F32 with row_r NULL
 // stores the plain fp32 accumulator (the weight-gradient GEMMs).
 enum Epi {
-  EPI_ACT = 0, EPI_SWIGLU = 1, EPI_GATE = 2, EPI_SCALE_F32 = 3, EPI_GATE_SPLIT = 4,
-  EPI_STORE_T = 5
+  EPI_ACT = 0, EPI_SWIGLU = 1, EPI_GATE = 2, EPI_SCALE_F32 = 3, EPI_STORE_T = 5
 };
 
 struct GemmArgs {
@@ -46,8 +44,8 @@ struct GemmArgs {
   const float* row_r;              // r per GEMM row (EPI_ACT / SWIGLU / SCALE)
   const float* row_w;              // gate per GEMM row (EPI_GATE), NULL = 1
   int epi; int act;                // act: 0 GELU erf, 1 GELU tanh
-  int64_t ysplit;                  // EPI_GATE_SPLIT / EPI_SCALE_F32: elements between the
-                                   // K-split planes (tile.spare = split)
+  int64_t ysplit;                  // EPI_SCALE_F32: elements between the K-split
+                                   // planes (tile.spare = split)
   const int32_t* xrow;             // NULL, or X row of each GEMM row (-1: any row;
                                    // its result is never read)
   // First linear (EPI_ACT / EPI_SWIGLU): when non-NULL, the pre-activations
@@ -93,8 +91,10 @@ struct PlanArgs {
   // pieces so that the run fills its last round (ntiles[1..9] get the runs'
   // bases, ntiles[10] the number of split tiles, counters[g] the list entry
   // of split tile g's part 0).  The tile buffer must hold max_tiles + grid
-  // entries.
+  // entries.  Pieces are cut at whole K stages of kstage elements (the GEMM
+  // kernel's stage: 64 for bf16, 128 for MXFP8; 0 means 64).
   int grid; int max_parts; int* counters;
+  int kstage;
 };
 
 // MXFP8 GEMM: X and W hold E4M3 codes (ldx / ldw in bytes), xs / ws their

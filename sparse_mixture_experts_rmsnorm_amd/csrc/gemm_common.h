@@ -1,8 +1,11 @@
 // Device helpers shared by the expert GEMM kernels (bf16 and MXFP8): the
-// XCD-aware tile order, the LDS chunk swizzle, the DMA wait and the MFMA /
-// fragment-read scheduling pattern.
+// XCD-aware tile order, the LDS chunk swizzle, the DMA wait, the MFMA /
+// fragment-read scheduling pattern and the K pieces' partial stores.
 #pragma once
 #include <hip/hip_runtime.h>
+
+#include "common.h"
+#include "gemm_args.h"
 
 namespace moe {
 
@@ -47,6 +50,33 @@ __device__ __forceinline__ void sched_interleave() {
   } else if constexpr (NM > 0) {
     __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
   }
+}
+
+// K pieces of a split tile.  Each piece stores its fp32 partial sums at its
+// slot of the partial buffer in fragment order (block (i, j) of wave w at
+// ((w MF + i) MT + j) 1024 + 16 lane floats), so that the lane of the fixup
+// kernel that reads them back holds exactly the values the same lane of a
+// whole tile would.  No workgroup waits for another: the fixup kernel runs
+// after the GEMM on the same stream.
+template <int BF, int BT, int MF, int MT>
+__device__ __forceinline__ int64_t piece_frag_offset(int wid, int lane, int i, int j) {
+  return int64_t(wid) * (MF * MT * 1024) + (i * MT + j) * 1024 + lane * 16;
+}
+
+template <int BF, int BT, int MF, int MT>
+__device__ __forceinline__ void store_piece(const GemmArgs& a, const Tile& tile,
+                                            const f32x16 (&acc)[MF][MT], int wid, int lane) {
+  float* const dst0 = a.part + (int64_t(tile.pslot0) + tile.part) * (int64_t(BF) * BT);
+#pragma unroll
+  for (int i = 0; i < MF; ++i)
+#pragma unroll
+    for (int j = 0; j < MT; ++j) {
+      f32x4* dst = reinterpret_cast<f32x4*>(dst0 + piece_frag_offset<BF, BT, MF, MT>(wid, lane, i, j));
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        dst[v] = f32x4{acc[i][j][4 * v], acc[i][j][4 * v + 1], acc[i][j][4 * v + 2],
+                       acc[i][j][4 * v + 3]};
+    }
 }
 
 }  // namespace moe

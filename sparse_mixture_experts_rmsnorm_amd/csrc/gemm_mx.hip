@@ -120,6 +120,12 @@ __device__ __forceinline__ int mx_block_codes(const float (&o)[16], uint32_t (&w
 // (32 bytes per block) are read just before its MFMAs: the other wave on the
 // SIMD runs its MFMAs meanwhile, and one fragment set keeps the wave within
 // 256 registers.
+//
+// Persistent, as the bf16 kernel: workgroup b takes tiles b, b + G, ... of the
+// XCD-remapped list, or of its XCD's run when the list was planned for this
+// grid (xcd_runs), and issues the next tile's first two stages before this
+// tile's epilogue.  A K piece (tile.nparts > 1) stores its fp32 partial tile
+// for the fixup kernel, which applies the epilogue to the sum of the pieces.
 template <int EPI>
 __global__ void __launch_bounds__(512) k_gemm_mx(MxGemmArgs m) {
   constexpr int BF = 256, BT = 256, WGF = 4, WGT = 2, NW = 8;
@@ -132,21 +138,25 @@ __global__ void __launch_bounds__(512) k_gemm_mx(MxGemmArgs m) {
   constexpr int LT = (BF + BT) * BK;            // operand bytes per stage
   constexpr int LS = LT + (BF + BT) * 4;        // + one E8M0 scale word per row
   constexpr int KS = BK / 64;                   // MFMA sub-steps per stage
+  constexpr int SPI = SPW + 1;                  // DMA instructions per wave per stage
   static_assert(EPI != EPI_SWIGLU || MF % 2 == 0, "SwiGLU pairs gate and up blocks per wave");
+  static_assert(KS == 2, "two sub-steps per stage");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * LS];
   const GemmArgs& a = m.g;
 
-  const int nt = *a.ntiles;
-  if (int(blockIdx.x) >= nt) return;
-  const Tile tile = a.tiles[remap_xcd(blockIdx.x, nt)];
+  const int nt = a.ntiles[0];
+  const int G = gridDim.x;
+  const int NX = a.xcd_runs && G % 8 == 0 ? 8 : 1;
+  const int run_end = a.xcd_runs ? a.ntiles[2 + int(blockIdx.x) % NX] : nt;
+  int tb = a.xcd_runs ? a.ntiles[1 + int(blockIdx.x) % NX] + int(blockIdx.x) / NX : int(blockIdx.x);
+  const int step = a.xcd_runs ? G / NX : G;
+  auto list_index = [&](int i) { return a.xcd_runs ? i : remap_xcd(i, nt); };
+  if (tb >= run_end) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   // waves wid and wid + 4 share a SIMD: the same feature rows, the two row
   // halves (a tile with few rows keeps every SIMD equally busy)
   const int wt = wid / WGF, wf = wid % WGF;
-  const uint8_t* __restrict__ X = static_cast<const uint8_t*>(a.X);
-  const uint8_t* __restrict__ W = static_cast<const uint8_t*>(a.W);
-  const int xk0 = EPI == EPI_GATE_SPLIT ? tile.spare * tile.klen : 0;
 
   // Operands are read through buffer resources: uniform base and size in
   // scalar registers, a 32-bit per-lane offset, and every uniform part of the
@@ -160,16 +170,12 @@ __global__ void __launch_bounds__(512) k_gemm_mx(MxGemmArgs m) {
   const int srow = lane / C;
   const bool wseg = wid * SPW < SEGW;
   const __amdgpu_buffer_rsrc_t rsrc =
-      wseg ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(W), 0, int(m.w_bytes), kRsrcWord3)
-           : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(X), 0, int(m.x_bytes), kRsrcWord3);
+      wseg ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(static_cast<const uint8_t*>(a.W)),
+                                               0, int(m.w_bytes), kRsrcWord3)
+           : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(static_cast<const uint8_t*>(a.X)),
+                                               0, int(m.x_bytes), kRsrcWord3);
   const int64_t ld = wseg ? a.ldw : a.ldx;
   const int sg0 = wseg ? wid * SPW : wid * SPW - SEGW;      // first segment of this wave
-  const int64_t rbase = (wseg ? int64_t(tile.wrow0) : int64_t(tile.row0)) + srow;
-  const int64_t kbase = wseg ? tile.kofs : xk0;
-  uint32_t voff[2];                              // even / odd segments (swizzle parity)
-#pragma unroll
-  for (int p = 0; p < 2; ++p)
-    voff[p] = uint32_t(rbase * ld + kbase + ((lane % C) ^ srow ^ p) * 16);
   // Scale words ride with the operands: the 4 E8M0 bytes of a row's stage
   // (K offsets are multiples of 128, so they are one aligned 32-bit word)
   // land after the operand tiles, W rows then X rows, one 4-byte DMA per
@@ -179,9 +185,20 @@ __global__ void __launch_bounds__(512) k_gemm_mx(MxGemmArgs m) {
       wsc ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(m.ws), 0, int(m.ws_bytes), kRsrcWord3)
           : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(m.xs), 0, int(m.xs_bytes), kRsrcWord3);
   const int64_t srow_s = (wsc ? wid : wid - NW / 2) * 64 + lane;
-  const uint32_t s_voff =
-      wsc ? uint32_t((int64_t(tile.wrow0) + srow_s) * m.ldws + tile.kofs / 32)
-          : uint32_t((int64_t(tile.row0) + srow_s) * m.ldxs + xk0 / 32);
+  // this lane's offsets into its operand and scale rows for a tile (a K
+  // piece starts at tile.kofs in the weights and tile.xk in the rows)
+  uint32_t voff[2];                              // even / odd segments (swizzle parity)
+  uint32_t s_voff;
+  auto set_sources = [&](const Tile& t) {
+    const int xk0 = t.xk;
+    const int64_t rbase = (wseg ? int64_t(t.wrow0) : int64_t(t.row0)) + srow;
+    const int64_t kbase = wseg ? t.kofs : xk0;
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+      voff[p] = uint32_t(rbase * ld + kbase + ((lane % C) ^ srow ^ p) * 16);
+    s_voff = wsc ? uint32_t((int64_t(t.wrow0) + srow_s) * m.ldws + t.kofs / 32)
+                 : uint32_t((int64_t(t.row0) + srow_s) * m.ldxs + xk0 / 32);
+  };
   auto issue = [&](int kt, int stage) {
     uint8_t* base = lds + stage * LS;
 #pragma unroll
@@ -192,24 +209,35 @@ __global__ void __launch_bounds__(512) k_gemm_mx(MxGemmArgs m) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_void_ptr)(base + LT + wid * 256), 4,
                                              s_voff, kt * 4, 0, 0);
   };
+  // stages 0 and 1 (a one-stage tile loads stage 0 twice, the second copy
+  // into a buffer that is not read)
+  auto prologue = [&](int nk) {
+    issue(0, 0);
+    issue(min(1, nk - 1), 1);
+  };
 
   const int fr = lane & 31, fh = lane >> 5, fswz = chunk_swz<C>(lane & 15);
-
-  f32x16 acc[MF][MT];
-#pragma unroll
-  for (int i = 0; i < MF; ++i)
-#pragma unroll
-    for (int j = 0; j < MT; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-  const int nk = tile.klen / BK;
   // Fragment addresses: the 16-byte chunk c of a row sits at slot c ^ swz(row)
   // (the DMA wrote it there), and a lane's chunks in sub-step ksv are
   // 4 ksv + 2 h + fh, h = 0, 1.  Row offsets are multiples of the 128-byte row,
   // so the slot offset is one per-lane base XORed with 64 ksv + 32 h.
   const uint32_t a_off = uint32_t((wf * WTF + fr) * BK + ((fh ^ fswz) << 4));
   const uint32_t b_off = uint32_t(BF * BK + (wt * WTT + fr) * BK + ((fh ^ fswz) << 4));
+
+  Tile tile = a.tiles[list_index(tb)];
+  int nk = tile.klen / BK;
+  set_sources(tile);
+  if (nk > 0) prologue(nk);
+  bool first = true;
+  f32x16 acc[MF][MT];
+  for (;;) {
+#pragma unroll
+    for (int i = 0; i < MF; ++i)
+#pragma unroll
+      for (int j = 0; j < MT; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
 #define MOE_MX_LOAD(DST, SW, OFF, KSV)                                                         \
   {                                                                                            \
     const u32x4 lo_ = *reinterpret_cast<const u32x4*>((SW) + ((OFF) ^ (64u * (KSV))));         \
@@ -247,74 +275,70 @@ __global__ void __launch_bounds__(512) k_gemm_mx(MxGemmArgs m) {
       sb[j] = *reinterpret_cast<const uint32_t*>((SW) + LT + BF * 4 + (wt * WTT + j * 32 + fr) * 4); \
   }
 
-  // Two LDS stages and one barrier per stage, placed after the last
-  // sub-step's fragments are in registers: behind it the drained buffer is
-  // refilled (stage kt + 2) while that sub-step's MFMAs run.  The loop body
-  // has no branch (a branch lets the compiler sink the first sub-step's
-  // MFMAs below the barrier, which keeps both fragment sets live): past the
-  // last stage the refill repeats stage nk - 1, in bounds, into a buffer that
-  // is not read again.
-  // Row blocks of this wave that hold rows of the tile: the MFMAs, fragment
-  // and scale reads of the rest (never stored) are skipped, one loop copy
-  // per count.
-  const int mta = __builtin_amdgcn_readfirstlane(
-      max(0, min(MT, (tile.row_end - tile.row0 - wt * WTT + 31) / 32)));
-  auto main_loop = [&](auto mta_c) {
-    constexpr int MTA = decltype(mta_c)::value;
-    uint32_t sa[MF], sb[MT];
-    i32x8 af[MF], bfr[MT];
-    constexpr int SPI = SPW + 1;                  // DMA instructions per wave per stage
-    if (nk > 0) {
-      issue(0, 0);
-      if (nk > 1) issue(1, 1);
-      if (nk > 1) MOE_WAIT_VMCNT(SPI);
-      else MOE_WAIT_VMCNT(0);
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      for (int kt = 0; kt + 1 < nk; ++kt) {
-        const uint8_t* sw = lds + (kt & 1) * LS;
-        const int knext = min(kt + 2, nk - 1);
+    // Two LDS stages and one barrier per stage, placed after the last
+    // sub-step's fragments are in registers: behind it the drained buffer is
+    // refilled (stage kt + 2) while that sub-step's MFMAs run.  The loop body
+    // has no branch (a branch lets the compiler sink the first sub-step's
+    // MFMAs below the barrier, which keeps both fragment sets live): past the
+    // last stage the refill repeats stage nk - 1, in bounds, into a buffer that
+    // is not read again.
+    // Row blocks of this wave that hold rows of the tile: the MFMAs, fragment
+    // and scale reads of the rest (never stored) are skipped, one loop copy
+    // per count.
+    const int mta = __builtin_amdgcn_readfirstlane(
+        max(0, min(MT, (tile.row_end - tile.row0 - wt * WTT + 31) / 32)));
+    auto main_loop = [&](auto mta_c) {
+      constexpr int MTA = decltype(mta_c)::value;
+      uint32_t sa[MF], sb[MT];
+      i32x8 af[MF], bfr[MT];
+      if (nk > 0) {
+        // stage 0 has landed (after a previous tile's epilogue its stores
+        // are counted too, so everything is waited for)
+        if (first) MOE_WAIT_VMCNT(SPI);
+        else MOE_WAIT_VMCNT(0);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        for (int kt = 0; kt + 1 < nk; ++kt) {
+          const uint8_t* sw = lds + (kt & 1) * LS;
+          const int knext = min(kt + 2, nk - 1);
+          MOE_MX_SCALES(sw)
+          MOE_MX_FRAGS(sw, 0)
+          {
+            MOE_MX_BYTES(0, s0a, s0b)
+            MOE_MX_MFMAS(0, s0a, s0b)
+          }
+          __builtin_amdgcn_sched_barrier(0);         // one fragment set live at a time
+          MOE_MX_FRAGS(sw, 1)
+          MOE_MX_BYTES(1, s1a, s1b)
+          asm volatile("s_waitcnt 0x0070" ::: "memory");   // vmcnt(0) lgkmcnt(0)
+          __builtin_amdgcn_s_barrier();
+          asm volatile("" ::: "memory");
+          issue(knext, kt & 1);
+          MOE_MX_MFMAS(1, s1a, s1b)
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        const uint8_t* sw = lds + ((nk - 1) & 1) * LS;
         MOE_MX_SCALES(sw)
         MOE_MX_FRAGS(sw, 0)
         {
           MOE_MX_BYTES(0, s0a, s0b)
           MOE_MX_MFMAS(0, s0a, s0b)
         }
-        __builtin_amdgcn_sched_barrier(0);         // one fragment set live at a time
-        MOE_MX_FRAGS(sw, 1)
-        MOE_MX_BYTES(1, s1a, s1b)
-        asm volatile("s_waitcnt 0x0070" ::: "memory");   // vmcnt(0) lgkmcnt(0)
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        issue(knext, kt & 1);
-        MOE_MX_MFMAS(1, s1a, s1b)
         __builtin_amdgcn_sched_barrier(0);
+        MOE_MX_FRAGS(sw, 1)
+        {
+          MOE_MX_BYTES(1, s1a, s1b)
+          MOE_MX_MFMAS(1, s1a, s1b)
+        }
       }
-      const uint8_t* sw = lds + ((nk - 1) & 1) * LS;
-      MOE_MX_SCALES(sw)
-      MOE_MX_FRAGS(sw, 0)
-      {
-        MOE_MX_BYTES(0, s0a, s0b)
-        MOE_MX_MFMAS(0, s0a, s0b)
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      MOE_MX_FRAGS(sw, 1)
-      {
-        MOE_MX_BYTES(1, s1a, s1b)
-        MOE_MX_MFMAS(1, s1a, s1b)
-      }
-      // the repeated refill may still be in flight: the workgroup's LDS must
-      // not be released under it
-      MOE_WAIT_VMCNT(0);
-    }
-  };
-  static_assert(MT == 4, "one loop copy per row-block count");
-  if (mta >= 4) main_loop(std::integral_constant<int, 4>{});
-  else if (mta == 3) main_loop(std::integral_constant<int, 3>{});
-  else if (mta == 2) main_loop(std::integral_constant<int, 2>{});
-  else if (mta == 1) main_loop(std::integral_constant<int, 1>{});
-  else main_loop(std::integral_constant<int, 0>{});
+    };
+    static_assert(MT == 4, "one loop copy per row-block count");
+    if (mta >= 4) main_loop(std::integral_constant<int, 4>{});
+    else if (mta == 3) main_loop(std::integral_constant<int, 3>{});
+    else if (mta == 2) main_loop(std::integral_constant<int, 2>{});
+    else if (mta == 1) main_loop(std::integral_constant<int, 1>{});
+    else main_loop(std::integral_constant<int, 0>{});
 
 #undef MOE_MX_LOAD
 #undef MOE_MX_FRAGS
@@ -322,52 +346,81 @@ __global__ void __launch_bounds__(512) k_gemm_mx(MxGemmArgs m) {
 #undef MOE_MX_SCALES
 #undef MOE_MX_BYTES
 
-  // epilogues: lane holds token column fr of each block and features
-  // 8 g + 4 fh + {0..3}, g = 0..3
+    // the repeated refill may still be in flight, and every wave's LDS reads
+    // of this tile must be done before the next tile's loads overwrite the
+    // ring: after the barrier the next tile's first two stages are issued,
+    // under this tile's epilogue
+    MOE_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const int tn = tb + step;
+    const bool more = tn < run_end;
+    Tile next = tile;
+    int nk2 = 0;
+    if (more) {
+      next = a.tiles[list_index(tn)];
+      nk2 = next.klen / BK;
+      set_sources(next);
+      if (nk2 > 0) prologue(nk2);
+    }
+
+    if (tile.nparts > 1) {
+      store_piece<BF, BT, MF, MT>(a, tile, acc, wid, lane);
+    } else {
+      // epilogues: lane holds token column fr of each block and features
+      // 8 g + 4 fh + {0..3}, g = 0..3
 #pragma unroll
-  for (int j = 0; j < MT; ++j) {
-    const int row = tile.row0 + wt * WTT + j * 32 + fr;
-    const bool live = row < tile.row_end;       // (the shuffles below need every lane)
-    if (EPI == EPI_SWIGLU || EPI == EPI_ACT) {
-      const float rs = live ? a.row_r[row] : 0.f;
-      constexpr int NBLK = EPI == EPI_SWIGLU ? MF / 2 : MF;
+      for (int j = 0; j < MT; ++j) {
+        const int row = tile.row0 + wt * WTT + j * 32 + fr;
+        const bool live = row < tile.row_end;       // (the shuffles below need every lane)
+        if (EPI == EPI_SWIGLU || EPI == EPI_ACT) {
+          const float rs = live ? a.row_r[row] : 0.f;
+          constexpr int NBLK = EPI == EPI_SWIGLU ? MF / 2 : MF;
 #pragma unroll
-      for (int p = 0; p < NBLK; ++p) {
-        float o[16];
+          for (int p = 0; p < NBLK; ++p) {
+            float o[16];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          if (EPI == EPI_SWIGLU) {
-            o[v] = silu(rs * acc[2 * p][j][v]) * (rs * acc[2 * p + 1][j][v]);
-          } else {
-            const float z = rs * acc[p][j][v];
-            o[v] = a.act == 1 ? gelu_tanh(z) : gelu_erf(z);
+            for (int v = 0; v < 16; ++v) {
+              if (EPI == EPI_SWIGLU) {
+                o[v] = silu(rs * acc[2 * p][j][v]) * (rs * acc[2 * p + 1][j][v]);
+              } else {
+                const float z = rs * acc[p][j][v];
+                o[v] = a.act == 1 ? gelu_tanh(z) : gelu_erf(z);
+              }
+            }
+            uint32_t w[4];
+            const int s = mx_block_codes(o, w);
+            if (live) {
+              const int col = tile.ocol0 + wf * (EPI == EPI_SWIGLU ? WTF / 2 : WTF) + p * 32;
+              uint8_t* Y = static_cast<uint8_t*>(a.Y) + int64_t(row) * a.ldy + col;
+#pragma unroll
+              for (int g = 0; g < 4; ++g) *reinterpret_cast<uint32_t*>(Y + g * 8 + fh * 4) = w[g];
+              if (fh == 0) m.ys[int64_t(row) * m.ldys + col / 32] = uint8_t(s + 127);
+            }
           }
-        }
-        uint32_t w[4];
-        const int s = mx_block_codes(o, w);
-        if (live) {
-          const int col = tile.ocol0 + wf * (EPI == EPI_SWIGLU ? WTF / 2 : WTF) + p * 32;
-          uint8_t* Y = static_cast<uint8_t*>(a.Y) + int64_t(row) * a.ldy + col;
+        } else if (live) {
+          const float rs = a.row_w ? a.row_w[row] : 1.f;
+          uint16_t* Y = static_cast<uint16_t*>(a.Y) + int64_t(row) * a.ldy + tile.ocol0 + wf * WTF;
 #pragma unroll
-          for (int g = 0; g < 4; ++g) *reinterpret_cast<uint32_t*>(Y + g * 8 + fh * 4) = w[g];
-          if (fh == 0) m.ys[int64_t(row) * m.ldys + col / 32] = uint8_t(s + 127);
+          for (int i = 0; i < MF; ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              uint32_t pk[2];
+#pragma unroll
+              for (int h = 0; h < 2; ++h)
+                pk[h] = pk_bf16(rs * acc[i][j][g * 4 + h * 2], rs * acc[i][j][g * 4 + h * 2 + 1]);
+              *reinterpret_cast<uint2*>(Y + i * 32 + g * 8 + fh * 4) = make_uint2(pk[0], pk[1]);
+            }
         }
       }
-    } else if (live) {
-      const float rs = a.row_w ? a.row_w[row] : 1.f;
-      uint16_t* Y = static_cast<uint16_t*>(a.Y) + int64_t(row) * a.ldy + tile.ocol0 + wf * WTF +
-                    (EPI == EPI_GATE_SPLIT ? int64_t(tile.spare) * a.ysplit : 0);
-#pragma unroll
-      for (int i = 0; i < MF; ++i)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          uint32_t pk[2];
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-            pk[h] = pk_bf16(rs * acc[i][j][g * 4 + h * 2], rs * acc[i][j][g * 4 + h * 2 + 1]);
-          *reinterpret_cast<uint2*>(Y + i * 32 + g * 8 + fh * 4) = make_uint2(pk[0], pk[1]);
-        }
     }
+    if (!more) break;
+    tile = next;
+    nk = nk2;
+    tb = tn;
+    first = false;
   }
 }
 
@@ -386,12 +439,12 @@ hipError_t launch_quant_mx(const void* src, int64_t R, int64_t K, int64_t lds, c
 
 hipError_t launch_gemm_mx(const MxGemmArgs& m, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  const dim3 g(grid), b(512);
+  // persistent: one workgroup per compute unit, as the bf16 kernel
+  const dim3 g(gemm_persistent_grid(grid)), b(512);
   switch (m.g.epi) {
     case EPI_ACT: hipLaunchKernelGGL(k_gemm_mx<EPI_ACT>, g, b, 0, s, m); break;
     case EPI_SWIGLU: hipLaunchKernelGGL(k_gemm_mx<EPI_SWIGLU>, g, b, 0, s, m); break;
     case EPI_GATE: hipLaunchKernelGGL(k_gemm_mx<EPI_GATE>, g, b, 0, s, m); break;
-    case EPI_GATE_SPLIT: hipLaunchKernelGGL(k_gemm_mx<EPI_GATE_SPLIT>, g, b, 0, s, m); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

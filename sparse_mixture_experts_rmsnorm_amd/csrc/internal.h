@@ -67,11 +67,6 @@ hipError_t launch_topology(const int32_t* offsets, const int32_t* size_blocks,
 
 hipError_t launch_combine(const void* y, const int32_t* pos, const void* x, const void* shared,
                           int dtype, int64_t T, int64_t d, int k, void* out, hipStream_t s);
-// Combine over nplanes (2 or 4) K-split partial planes y0 + p * rows_max * d,
-// dtype; each slot's row is the sum of its planes in plane order.
-hipError_t launch_combine_split(const void* y0, int nplanes, int64_t rows_max, const int32_t* pos,
-                                const void* x, const void* shared, int dtype, int64_t T, int64_t d,
-                                int k, void* out, hipStream_t s);
 
 // Sets the message moe_last_error() returns and gives back `code` (for
 // entry points outside api.cpp).
