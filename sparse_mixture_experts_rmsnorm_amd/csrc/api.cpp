@@ -372,15 +372,12 @@ int run_expert_gemms_mx(const moe_experts_desc* X, const ExpertGeo& g, int64_t d
   a.ldws = d / 32;
   a.ys = w.hqs;
   a.ldys = g.Fmax / 32;
-  a.g.xcd_runs = w.grid1 > 0;
-  a.g.part = w.part;
-  a.g.counters = w.counters;
   a.x_bytes = RP * d;
   a.w_bytes = P * d;
   a.xs_bytes = RP * (d / 32);
   a.ws_bytes = P * (d / 32);
-  MOE_HIP(launch_gemm_mx(a, w.grid1 > 0 ? w.grid1 : int(w.mt1), s));
-  if (w.grid1 > 0) MOE_HIP(launch_piece_fixup(a.g, g.bf1, g.bt, w.grid1, s));
+  // (no K pieces here: the epilogue quantises h, which needs the whole K)
+  MOE_HIP(launch_gemm_mx(a, int(w.mt1), s));
   timer_mark(timer, call, MOE_STAGE_GEMM1 + 1, s);
 
   MxGemmArgs b{};
