@@ -203,10 +203,12 @@ struct ExpertWs {
   Tile* tiles1 = nullptr;
   Tile* tiles2 = nullptr;
   int* nt = nullptr;   // [32]: the first list's counts at nt, the second's at nt + 16
-  // bf16 persistent launches: workgroups of each GEMM (the plans cut the last
-  // round's tiles into K pieces for exactly this grid), fp32 partials of the
-  // pieces and the list entry of each split tile (grid1 + grid2 ints)
+  // persistent launches planned per XCD: workgroups of each GEMM (0: the
+  // kernel splits the list itself); the second GEMM may cut its last round's
+  // tiles into K pieces for exactly its grid (pieces2), with fp32 partials
+  // and the list entry of each split tile (grid2 ints)
   int grid1 = 0, grid2 = 0;
+  bool pieces2 = false;
   float* part = nullptr;
   int* counters = nullptr;
   float* a_rows = nullptr;
@@ -256,6 +258,7 @@ void fit_dense_tiles(ExpertGeo* g, int dtype, int64_t d, int64_t T) {
 // are whole K stages of every expert are considered; a split that beats whole
 // tiles says that the last round leaves compute units idle, and then only
 // that round's tiles are cut (carve_expert_ws).
+constexpr bool kCostRuns = true;
 bool want_pieces(const ExpertGeo& g, int dtype, int64_t d, int64_t rows_used_est) {
   if (g.bcsr || g.atomic || dtype != MOE_BF16 || g.kdiv < 2) return false;
   constexpr double kRoundCost = 0.017, kPartCost = 0.031;
@@ -275,7 +278,8 @@ bool want_pieces(const ExpertGeo& g, int dtype, int64_t d, int64_t rows_used_est
 }
 
 void carve_expert_ws(Carve& c, const ExpertGeo& g, int dtype, int64_t d, int64_t rows_max,
-                     int64_t nnz_max, ExpertWs* w, bool pieces = false, bool save = false) {
+                     int64_t nnz_max, ExpertWs* w, bool pieces = false, bool save = false,
+                     bool runs = false) {
   if (g.atomic) {
     w->a_rows = c.take_n<float>(rows_max);
     return;
@@ -287,11 +291,16 @@ void carve_expert_ws(Carve& c, const ExpertGeo& g, int dtype, int64_t d, int64_t
   // one quarter of the partial traffic and a single rounding of y).
   // Elsewhere the pieces' partial stores and fixup cost more than the idle
   // compute units of the last round.
+  // Grouped bf16 / MXFP8 layers (runs) also plan both GEMMs' XCD runs on the
+  // device, split by the tiles' modelled cost rather than by count.
   pieces = pieces && dtype == MOE_BF16;
+  runs = runs && dtype == MOE_BF16 && !g.bcsr;
   w->mt1 = std::max<int64_t>(1, max_tiles_gemm1(g, rows_max, nnz_max));
   w->mt2 = std::max<int64_t>(1, max_tiles_gemm2(g, d, rows_max));
+  if (runs) w->grid1 = gemm_persistent_grid(int(std::min<int64_t>(w->mt1, 1 << 30)));
+  if (runs || pieces) w->grid2 = gemm_persistent_grid(int(std::min<int64_t>(w->mt2, 1 << 30)));
+  w->pieces2 = pieces;
   if (pieces) {
-    w->grid2 = gemm_persistent_grid(int(std::min<int64_t>(w->mt2, 1 << 30)));
     w->part = c.take_n<float>(int64_t(w->grid2) * g.bf2 * g.bt2);
     w->counters = c.take_n<int>(w->grid2);
   }
@@ -377,7 +386,8 @@ int run_expert_gemms_mx(const moe_experts_desc* X, const ExpertGeo& g, int64_t d
   a.xs_bytes = RP * (d / 32);
   a.ws_bytes = P * (d / 32);
   // (no K pieces here: the epilogue quantises h, which needs the whole K)
-  MOE_HIP(launch_gemm_mx(a, int(w.mt1), s));
+  a.g.xcd_runs = w.grid1 > 0;
+  MOE_HIP(launch_gemm_mx(a, w.grid1 > 0 ? w.grid1 : int(w.mt1), s));
   timer_mark(timer, call, MOE_STAGE_GEMM1 + 1, s);
 
   MxGemmArgs b{};
@@ -403,7 +413,7 @@ int run_expert_gemms_mx(const moe_experts_desc* X, const ExpertGeo& g, int64_t d
   b.xs_bytes = RP * (g.Fmax / 32);
   b.ws_bytes = d * (g.F / 32);
   MOE_HIP(launch_gemm_mx(b, w.grid2 > 0 ? w.grid2 : int(w.mt2), s));
-  if (w.grid2 > 0) MOE_HIP(launch_piece_fixup(b.g, g.bf2, g.bt2, w.grid2, s));
+  if (w.pieces2) MOE_HIP(launch_piece_fixup(b.g, g.bf2, g.bt2, w.grid2, s));
   timer_mark(timer, call, MOE_STAGE_GEMM2 + 1, s);
   (void)dense_rows;
   return MOE_OK;
@@ -436,8 +446,9 @@ int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, i
   p.ntiles = w.nt;
   p.max_tiles = int(w.mt1);
   p.grid = w.grid1;
-  p.max_parts = 4;
+  p.max_parts = 1;                 // the first GEMM's epilogue needs the whole K
   p.counters = nullptr;
+  p.cost_split = 1;
   p.kstage = g.mx ? 128 : 64;   // the GEMM kernel's K stage (pieces are whole stages)
   // second linear
   PlanArgs p2 = p;
@@ -451,6 +462,8 @@ int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, i
   p2.ksplit = 1;
   p2.bt = g.bt2;
   p2.grid = w.grid2;
+  p2.max_parts = w.pieces2 ? 4 : 1;
+  p2.cost_split = 0;
   p2.counters = w.counters;
   MOE_HIP(launch_plan_pair(p, p2, s));
   timer_mark(timer, call, MOE_STAGE_PLAN + 1, s);
@@ -478,7 +491,6 @@ int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, i
   a.part = w.part;
   a.counters = w.counters;
   MOE_HIP(launch_gemm(dtype, a, g.bf1, g.bt, w.grid1 > 0 ? w.grid1 : int(w.mt1), s));
-  if (w.grid1 > 0) MOE_HIP(launch_piece_fixup(a, g.bf1, g.bt, w.grid1, s));
   timer_mark(timer, call, MOE_STAGE_GEMM1 + 1, s);
 
   GemmArgs b{};
@@ -497,7 +509,7 @@ int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, i
   b.part = w.part;
   b.counters = w.counters;
   MOE_HIP(launch_gemm(dtype, b, g.bf2, g.bt2, w.grid2 > 0 ? w.grid2 : int(w.mt2), s));
-  if (w.grid2 > 0) MOE_HIP(launch_piece_fixup(b, g.bf2, g.bt2, w.grid2, s));
+  if (w.pieces2) MOE_HIP(launch_piece_fixup(b, g.bf2, g.bt2, w.grid2, s));
   timer_mark(timer, call, MOE_STAGE_GEMM2 + 1, s);
   return MOE_OK;
 }
@@ -1071,7 +1083,7 @@ void carve_layer(Carve& c, const moe_layer_desc* L, int64_t T, const ExpertGeo& 
   const int64_t rows_est = std::min(T * k, E * std::min(w->cap, T));
   const bool pieces = want_pieces(g, L->dtype, d, rows_est);
   carve_expert_ws(c, g, L->dtype, d, w->rows_max, nnz_max, &w->ex, pieces,
-                  L->save_for_backward != 0);
+                  L->save_for_backward != 0, kCostRuns && !g.atomic);
   w->y = c.take(size_t(g.atomic ? T : w->rows_max) * d * es);
   if (L->shared) {
     carve_expert_ws(c, gs, L->dtype, d, T, 0, &w->sh, false, L->save_for_backward != 0);

@@ -657,10 +657,104 @@ __device__ __forceinline__ int bcsr_span(const PlanArgs& p, const int* offs, int
   return (i & 1) ? 0 : 2;
 }
 
+// Cost model of a grouped unit's tiles for splitting a list over the XCDs:
+// a tile costs (kTileCost0 + its 32-row blocks) per K stage (the kernels skip
+// the row blocks past a tile's end; kTileCost0 stands for the per-stage work
+// that does not shrink with the rows: the weight stage and the barrier).  A
+// unit with a single row tile shares no weight tile with another row tile,
+// so each of its tiles streams its weights alone and is priced as a full
+// tile.  The row tiles of a unit hold rt rows each but the last, which holds
+// the rest (the even split of the planner below).
+constexpr int kTileCost0 = 4;
+struct UnitCost {
+  int mt, nf;        // row tiles, column tiles
+  int wf, wl;        // cost per K stage of a row tile that is not the last / of the last
+  int nk;            // K stages per tile
+};
+
+__device__ __forceinline__ UnitCost unit_cost_shape(const PlanArgs& p, int rows, int nf, int fsize) {
+  UnitCost c{};
+  c.mt = (rows + p.bt - 1) / p.bt;
+  c.nf = nf;
+  if (c.mt == 0) return c;
+  const int rt = min(p.bt, ((rows + c.mt - 1) / c.mt + 31) / 32 * 32);
+  const int ks = p.kstage > 0 ? p.kstage : 64;
+  const int km = p.kmul > 0 ? p.kmul : 1;
+  c.wf = kTileCost0 + rt / 32;
+  c.wl = c.mt == 1 ? kTileCost0 + p.bt / 32 : kTileCost0 + (rows - (c.mt - 1) * rt + 31) / 32;
+  c.nk = p.gemm == 1 ? p.d / ks : km * fsize / ks;
+  return c;
+}
+
+// Packed in two words for LDS: (mt, nf) and (wf, wl, nk).
+__device__ __forceinline__ void unit_cost_pack(const UnitCost& c, int* w0, int* w1) {
+  *w0 = (c.mt << 16) | c.nf;
+  *w1 = (c.wf << 24) | (c.wl << 16) | c.nk;
+}
+__device__ __forceinline__ UnitCost unit_cost_unpack(int w0, int w1) {
+  UnitCost c;
+  c.mt = int(unsigned(w0) >> 16);
+  c.nf = w0 & 0xFFFF;
+  c.wf = int(unsigned(w1) >> 24);
+  c.wl = (w1 >> 16) & 0xFF;
+  c.nk = w1 & 0xFFFF;
+  return c;
+}
+
+// Cost of the unit's first n tiles in list order (tile_coords), in K-stage
+// units.
+__device__ __forceinline__ long long unit_cost_prefix(const UnitCost& c, int n) {
+  if (c.mt == 0 || n <= 0) return 0;
+  if (n >= c.mt * c.nf) return (long long)c.nf * ((c.mt - 1) * c.wf + c.wl) * c.nk;
+  long long pre;
+  if (c.mt <= kRowBlock) {
+    const int g = n / c.mt, i = n - g * c.mt;           // i < mt: tiles 0 .. i-1 are not the last
+    pre = (long long)g * ((c.mt - 1) * c.wf + c.wl) + (long long)i * c.wf;
+  } else {
+    const int blk = n / (kRowBlock * c.nf);
+    const int rem = n - blk * kRowBlock * c.nf;
+    const int rows_b = min(kRowBlock, c.mt - blk * kRowBlock);
+    const bool last_blk = (blk + 1) * kRowBlock >= c.mt;
+    const long long wblk = (long long)(rows_b - 1) * c.wf + (last_blk ? c.wl : c.wf);
+    const int col = rows_b > 0 ? rem / rows_b : 0, i = rem - col * rows_b;
+    pre = (long long)blk * c.nf * kRowBlock * c.wf + col * wblk + (long long)i * c.wf;
+  }
+  return pre * c.nk;
+}
+
+// The unit's tile index (0 .. cnt) whose cost prefix is nearest to `want`
+// (to within one tile), in closed form: whole blocks of row tiles, whole
+// columns of the block, then row tiles of the column.  In double precision:
+// the costs stay far below 2^53, and 64-bit integer division is a long
+// software sequence on the GPU.
+__device__ __forceinline__ int unit_cost_find(const UnitCost& c, int cnt, long long want) {
+  if (c.mt == 0 || cnt == 0 || want <= 0) return 0;
+  const double w = double(want) / c.nk;                 // in cost-per-stage units
+  double blk = 0, rem = w;
+  int rows_b = c.mt;
+  if (c.mt > kRowBlock) {
+    const int nblk = (c.mt + kRowBlock - 1) / kRowBlock;
+    const double full = double(c.nf) * kRowBlock * c.wf;   // a block without the last row tile
+    blk = fmin(double(nblk - 1), floor(w / full));
+    rem = w - blk * full;
+    rows_b = min(kRowBlock, c.mt - int(blk) * kRowBlock);
+  }
+  const bool last_blk = c.mt <= kRowBlock || (int(blk) + 1) * kRowBlock >= c.mt;
+  const double gc = double(rows_b - 1) * c.wf + (last_blk ? c.wl : c.wf);   // one column
+  const double col = fmin(double(c.nf - 1), floor(rem / gc));
+  const double r = rem - col * gc;
+  const double i = fmin(double(rows_b - 1), floor(r / c.wf + 0.5));
+  const double n = blk * kRowBlock * c.nf + col * rows_b + i;
+  return int(fmin(double(cnt), fmax(0.0, n)));
+}
+
 __device__ __forceinline__ void plan_tiles(const PlanArgs& p, int slice, int nslices) {
   __shared__ int base_s[kPlanMax + 1];
   __shared__ unsigned char span_s[kPlanMax];   // BCSR: bcsr_span of each token-block row
   __shared__ int offs_s[kPlanOffsMax + 1];      // BCSR: the expert row offsets
+  __shared__ long long cost_s[kPlanOffsMax + 1];  // cost split: unit costs, then their prefix
+  __shared__ int shape_s[kPlanOffsMax];           // cost split: second word of each unit's shape
+  int* const shape0_s = offs_s;                   // (its first word; offs_s is BCSR-only)
   __shared__ long long sh[33];
   const bool dense = p.offsets == nullptr;
   const bool bcsr = !dense && p.row_offsets != nullptr;
@@ -671,10 +765,13 @@ __device__ __forceinline__ void plan_tiles(const PlanArgs& p, int slice, int nsl
   const int pf = p.swiglu && p.gemm == 1 ? 2 : 1;   // packed rows per hidden unit
   const int km = p.kmul > 0 ? p.kmul : 1;            // second linear: K per hidden unit
   const int nunits = dense ? 1 : bcsr ? p.offsets[p.E] / p.block : p.E;
+  // XCD runs split by cost (grouped lists of a persistent launch, no K split)
+  const bool by_cost = p.cost_split && p.grid > 0 && !dense && !bcsr && p.ksplit <= 1 &&
+                       nunits <= kPlanOffsMax;
   // per unit tile count, then exclusive scan (each thread owns a contiguous run)
   const int per = (nunits + blockDim.x - 1) / blockDim.x;
   const int lo = min(nunits, int(threadIdx.x) * per), hi = min(nunits, lo + per);
-  long long local = 0;
+  long long local = 0, lcost = 0;
   for (int u = lo; u < hi; ++u) {
     int cnt;
     if (dense) {
@@ -690,38 +787,64 @@ __device__ __forceinline__ void plan_tiles(const PlanArgs& p, int slice, int nsl
       const int nf = p.gemm == 1 ? ((p.foff[u + 1] - p.foff[u]) * pf + (p.ragged ? p.bf - 1 : 0)) / p.bf
                                  : p.d / p.bf;
       cnt = mt * nf * (p.gemm == 2 ? p.ksplit : 1);
+      if (by_cost) {
+        const UnitCost c = unit_cost_shape(p, rows, nf, p.foff[u + 1] - p.foff[u]);
+        cost_s[u] = unit_cost_prefix(c, cnt);
+        lcost += cost_s[u];
+        unit_cost_pack(c, &shape0_s[u], &shape_s[u]);
+      }
     }
     base_s[u] = cnt;
     local += cnt;
   }
+  // exclusive scans of the tile counts and (by_cost) the unit costs
   long long total;
   {
+    __shared__ long long shc[33];
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    long long incl = local;
+    long long incl = local, inclc = lcost;
     for (int o = 1; o < 64; o <<= 1) {
       const long long u = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += u;
+      const long long uc = __shfl_up(inclc, o, 64);
+      if (lane >= o) {
+        incl += u;
+        inclc += uc;
+      }
     }
-    if (lane == 63) sh[wid] = incl;
+    if (lane == 63) {
+      sh[wid] = incl;
+      shc[wid] = inclc;
+    }
     __syncthreads();
     if (threadIdx.x == 0) {
-      long long run = 0;
+      long long run = 0, runc = 0;
       for (int w = 0; w < nw; ++w) {
-        const long long t = sh[w];
+        const long long t = sh[w], tc = shc[w];
         sh[w] = run;
+        shc[w] = runc;
         run += t;
+        runc += tc;
       }
       sh[32] = run;
+      shc[32] = runc;
     }
     __syncthreads();
-    long long b = sh[wid] + incl - local;
+    long long b = sh[wid] + incl - local, bc = shc[wid] + inclc - lcost;
     total = sh[32];
     for (int u = lo; u < hi; ++u) {
       const int c = base_s[u];
       base_s[u] = int(b);
       b += c;
+      if (by_cost) {
+        const long long cc = cost_s[u];
+        cost_s[u] = bc;
+        bc += cc;
+      }
     }
-    if (threadIdx.x == 0) base_s[nunits] = int(total);
+    if (threadIdx.x == 0) {
+      base_s[nunits] = int(total);
+      if (by_cost) cost_s[nunits] = shc[32];
+    }
   }
   __syncthreads();
   const int ntot = int(min<long long>(total, p.max_tiles));
@@ -735,18 +858,44 @@ __device__ __forceinline__ void plan_tiles(const PlanArgs& p, int slice, int nsl
   const int NX = p.grid > 0 && p.grid % 8 == 0 ? 8 : 1;
   if (p.grid > 0) {
     const int S = p.grid / NX;
-    if (threadIdx.x == 0) {
+    // XCD x runs list entries [bound[x], bound[x + 1]): equal counts, or
+    // (by_cost) boundaries at equal shares of the list's cost, each placed at
+    // the tile boundary nearest to its share (one thread per boundary)
+    __shared__ int bound_s[9];
+    if (threadIdx.x <= NX) {
+      const int x = threadIdx.x;
       const int q = ntot / NX, rem = ntot % NX;
+      int bx = x == NX ? ntot : x * q + min(x, rem);
+      if (by_cost && x > 0 && x < NX && cost_s[nunits] > 0) {
+        const long long target = NX == 8 ? (cost_s[nunits] * x) >> 3 : cost_s[nunits] * x;
+        int lo = 0, hi = nunits - 1;                    // last unit starting at or before target
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (cost_s[mid] <= target) lo = mid;
+          else hi = mid - 1;
+        }
+        const UnitCost c = unit_cost_unpack(shape0_s[lo], shape_s[lo]);
+        const int cnt = base_s[lo + 1] - base_s[lo];
+        bx = min(ntot, base_s[lo] + unit_cost_find(c, cnt, target - cost_s[lo]));
+      }
+      bound_s[x] = bx;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int bound[9];
+      bound[0] = 0;
+      for (int x = 1; x <= NX; ++x) bound[x] = max(bound[x - 1], min(ntot, bound_s[x]));
+      bound[NX] = ntot;
       int out = 0, grp = 0, pcs = 0;
       for (int x = 0; x < NX; ++x) {
-        const int qx = q + (x < rem ? 1 : 0);
+        const int qx = bound[x + 1] - bound[x];
         int r = qx % S;
         int P = r > 0 ? min(p.max_parts, S / r) : 1;
         if (P < 2) {
           P = 1;
           r = 0;
         }
-        xfirst_s[x] = x * q + min(x, rem);
+        xfirst_s[x] = bound[x];
         xfull_s[x] = qx - r;
         xp_s[x] = P;
         xout_s[x] = out;

@@ -92,9 +92,14 @@ struct PlanArgs {
   // bases, ntiles[10] the number of split tiles, counters[g] the list entry
   // of split tile g's part 0).  The tile buffer must hold max_tiles + grid
   // entries.  Pieces are cut at whole K stages of kstage elements (the GEMM
-  // kernel's stage: 64 for bf16, 128 for MXFP8; 0 means 64).
+  // kernel's stage: 64 for bf16, 128 for MXFP8; 0 means 64).  cost_split:
+  // the runs of a grouped list (ksplit 1) end at equal shares of the list's
+  // modelled cost (row blocks and K stages of each tile) instead of at equal
+  // tile counts, so that XCDs whose experts end in short row tiles take more
+  // tiles.
   int grid; int max_parts; int* counters;
   int kstage;
+  int cost_split;
 };
 
 // MXFP8 GEMM: X and W hold E4M3 codes (ldx / ldw in bytes), xs / ws their
