@@ -462,7 +462,7 @@ int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, i
   p2.ksplit = 1;
   p2.bt = g.bt2;
   p2.grid = w.grid2;
-  p2.max_parts = w.pieces2 ? 4 : 1;
+  p2.max_parts = w.pieces2 ? 8 : 1;
   p2.cost_split = 0;
   p2.counters = w.counters;
   MOE_HIP(launch_plan_pair(p, p2, s));
