@@ -267,6 +267,197 @@ __global__ void __launch_bounds__(kThreads) k_rank(
   }
 }
 
+// Passes 2 and 3 in one launch, for layers whose chunk counts are few
+// (nch * E <= kFusedScanMax): every block reads the whole (chunk, expert)
+// count table itself -- its chunk's bases, the expert totals, the capacity
+// test and the padded offsets -- so no separate scan launch sits between the
+// count and the rank.  Block 0 writes counts, offsets and the statistics.
+// With GATHER the chunk is ranked by `workers` blocks, all of which compute
+// the same ranks; worker 0 writes the slot metadata and each worker copies
+// its share of the chunk's kept rows into x_perm (token row t to row p), so
+// the gather runs in the same launch; the last chunk's workers also zero the
+// padding rows.
+constexpr int kFusedScanMax = 1 << 15;
+
+template <bool GATHER, typename T>
+__global__ void __launch_bounds__(kThreads) k_rank_fused(
+    const int32_t* __restrict__ ids, const float* __restrict__ w, const float* __restrict__ r,
+    int Tn, int k, int E, int nbits, int cap, int pad, int nch, int workers,
+    const int32_t* __restrict__ cc, const int32_t* __restrict__ cerr,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ stats,
+    int32_t* __restrict__ pos, int32_t* __restrict__ row_token, float* __restrict__ row_r,
+    float* __restrict__ row_w, int32_t* __restrict__ row_expert, const T* __restrict__ x,
+    int64_t d, T* __restrict__ x_perm) {
+  extern __shared__ int sm[];
+  int* running = sm;              // [E] slots of this expert in earlier chunks, then running
+  int* wtag = sm + E;             // [4][E]: (batch + 1) << 8 | count
+  int* offs = sm + 5 * E;         // [E + 1] padded expert offsets
+  int* tot_s = sm + 6 * E + 1;    // [E] slots of this expert in all chunks
+  int* slot_p = sm + 7 * E + 1;   // [chunk slots] row of each slot (GATHER)
+  __shared__ long long sh[33];
+  const int c = int(blockIdx.x) / workers, wk = int(blockIdx.x) - c * workers;
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  for (int e = tid; e < E; e += kThreads) {
+    running[e] = 0;
+    tot_s[e] = 0;
+    wtag[e] = wtag[E + e] = wtag[2 * E + e] = wtag[3 * E + e] = 0;
+  }
+  __syncthreads();
+  // 1. per expert, the slots of the chunks before this one and of all chunks:
+  //    G threads per expert, each summing every G-th chunk (integer sums, so
+  //    the LDS atomics give the same totals in any order)
+  {
+    const int G = E >= kThreads ? 1 : kThreads / E;
+    for (int idx = tid; idx < E * G; idx += kThreads) {
+      const int e = idx % E, g = idx / E;
+      int before = 0, all = 0;
+      for (int c2 = g; c2 < nch; c2 += G) {
+        const int v = cc[int64_t(c2) * E + e];
+        all += v;
+        before += c2 < c ? v : 0;
+      }
+      if (before) atomicAdd(&running[e], before);
+      if (all) atomicAdd(&tot_s[e], all);
+    }
+  }
+  __syncthreads();
+  // 2. capacity and padded offsets (each thread owns a contiguous run of experts)
+  const int per = (E + kThreads - 1) / kThreads;
+  const int lo = min(E, tid * per), hi = min(E, lo + per);
+  long long local = 0, dropped = 0;
+  int maxl = 0;
+  for (int e = lo; e < hi; ++e) {
+    const int kept = min(tot_s[e], cap);
+    local += (kept + pad - 1) / pad * pad;
+    dropped += tot_s[e] - kept;
+    maxl = max(maxl, tot_s[e]);
+  }
+  long long total;
+  long long base = block_exscan(local, &total, sh);
+  for (int e = lo; e < hi; ++e) {
+    offs[e] = int(base);
+    base += (min(tot_s[e], cap) + pad - 1) / pad * pad;
+  }
+  if (tid == 0) offs[E] = int(total);
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    for (int e = tid; e <= E; e += kThreads) {
+      offsets[e] = offs[e];
+      if (e < E) counts[e] = tot_s[e];
+    }
+    long long errs = 0;
+    for (int c2 = tid; c2 < nch; c2 += kThreads) errs += cerr[c2];
+    long long tot;
+    block_exscan(dropped, &tot, sh);
+    const long long all_dropped = tot;
+    block_exscan(errs, &tot, sh);
+    const long long all_errs = tot;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) maxl = max(maxl, __shfl_xor(maxl, o, 64));
+    __shared__ int mx[kThreads / 64];
+    if (lane == 0) mx[wid] = maxl;
+    __syncthreads();
+    if (tid == 0 && stats) {
+      int mm = 0;
+      for (int w2 = 0; w2 < kThreads / 64; ++w2) mm = max(mm, mx[w2]);
+      stats[0] = int(total);
+      stats[1] = int(all_dropped);
+      stats[2] = mm;
+      stats[3] = int(all_errs);
+    }
+  }
+  // 3. stable rank inside the chunk (as k_rank), capacity test, row metadata
+  const int t0 = c * kChunkTokens;
+  const int n = min(kChunkTokens, Tn - t0) * k;
+  const int64_t base_flat = int64_t(t0) * k;
+  const bool meta = wk == 0;
+  for (int b = 0; b * kThreads < n; ++b) {
+    const int i = b * kThreads + tid;
+    const bool valid = i < n;
+    int e = valid ? ids[base_flat + i] : -1;
+    if (unsigned(e) >= unsigned(E)) e = -1;
+    const bool ok = e >= 0;
+    const uint64_t peers = match_peers(e, ok, nbits);
+    const int lr = rank_below(peers);
+    const int tag = b + 1;
+    if (ok && lr == 0) wtag[wid * E + e] = (tag << 8) | __popcll(peers);
+    __syncthreads();
+    if (valid) {
+      const int64_t flat = base_flat + i;
+      int p = -1;
+      if (ok) {
+        int rank = running[e] + lr;
+        for (int w2 = 0; w2 < wid; ++w2) {
+          const int v = wtag[w2 * E + e];
+          if ((v >> 8) == tag) rank += v & 255;
+        }
+        if (rank < cap) {
+          p = offs[e] + rank;
+          if (meta) {
+            const int t = int(flat / k);
+            row_token[p] = t;
+            row_r[p] = r[t];
+            row_w[p] = w[flat];
+            if (row_expert) row_expert[p] = e;
+          }
+        }
+      }
+      if (meta) pos[flat] = p;
+      if (GATHER) slot_p[i] = p;
+    }
+    __syncthreads();
+    if (ok && lr == 0) {
+      bool last = true;
+      for (int w2 = wid + 1; w2 < 4; ++w2)
+        if ((wtag[w2 * E + e] >> 8) == tag) last = false;
+      if (last) {
+        int tot = 0;
+        for (int w2 = 0; w2 <= wid; ++w2) {
+          const int v = wtag[w2 * E + e];
+          if ((v >> 8) == tag) tot += v & 255;
+        }
+        running[e] += tot;
+      }
+    }
+    __syncthreads();
+  }
+  if constexpr (GATHER) {
+    // 4. this worker's share of the chunk's slots: one row per wave at a time,
+    //    each lane's loads issued before its stores
+    const int64_t nvec = d / Vec16<T>::N;
+    const u32x4* __restrict__ xs = reinterpret_cast<const u32x4*>(x);
+    u32x4* __restrict__ xp = reinterpret_cast<u32x4*>(x_perm);
+    auto copy_row = [&](int64_t src_row, int64_t dst_row) {
+      for (int64_t v0 = 0; v0 < nvec; v0 += 64 * 8) {
+        u32x4 buf[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int64_t v = v0 + u * 64 + lane;
+          buf[u] = (v < nvec && src_row >= 0) ? xs[src_row * nvec + v] : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int64_t v = v0 + u * 64 + lane;
+          if (v < nvec) xp[dst_row * nvec + v] = buf[u];
+        }
+      }
+    };
+    const int i0 = int(int64_t(n) * wk / workers), i1 = int(int64_t(n) * (wk + 1) / workers);
+    for (int i = i0 + wid; i < i1; i += kThreads / 64) {
+      const int p = slot_p[i];
+      if (p >= 0) copy_row((base_flat + i) / k, p);
+    }
+    // padding rows of every expert, zeroed by the last chunk's workers
+    if (c == nch - 1) {
+      for (int e = wk; e < E; e += workers) {
+        const int kept = min(tot_s[e], cap);
+        for (int row = offs[e] + kept + wid; row < offs[e + 1]; row += kThreads / 64)
+          copy_row(-1, row);
+      }
+    }
+  }
+}
+
 // Row gather: x_perm[row] = x[row_token[row]] (zeros on padding rows).  A
 // wave copies one row; each lane moves up to 8 16-byte chunks, all loads
 // issued before the stores.
@@ -544,9 +735,27 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
                          E * sizeof(int), s, a.ids, T, k, E, cc, cerr, nch, a.rows_max,
                          a.row_token, a.row_r, a.row_w, a.row_expert);
     const int cap = int(std::min<int64_t>(a.cap, int64_t(1) << 30));
+    const int nbits = ceil_log2(E);
+    const int chunk_slots = std::min(kChunkTokens, std::max(T, 1)) * k;
+    const size_t smem_fused = size_t(7 * E + 1 + (a.x_perm ? chunk_slots : 0)) * sizeof(int);
+    if (int64_t(nch) * E <= kFusedScanMax && smem_fused <= 60 * 1024) {
+      // one launch ranks (and, with x_perm, gathers): workers per chunk so that
+      // each wave copies about two rows
+      const int workers = a.x_perm ? std::max(1, std::min(64, (chunk_slots + 7) / 8)) : 1;
+      const dim3 g(unsigned(std::max(nch, 1) * workers));
+#define MOE_RANK_FUSED(G, TY)                                                                  \
+  hipLaunchKernelGGL((k_rank_fused<G, TY>), g, dim3(kThreads), smem_fused, s, a.ids, a.w, a.r, T, \
+                     k, E, nbits, cap, a.pad, nch, workers, cc, cerr, a.counts, a.offsets,     \
+                     stats, a.pos, a.row_token, a.row_r, a.row_w, a.row_expert,               \
+                     static_cast<const TY*>(a.x), a.d, static_cast<TY*>(a.x_perm))
+      if (!a.x_perm) MOE_RANK_FUSED(false, uint16_t);
+      else if (a.dtype == 0) MOE_RANK_FUSED(true, float);
+      else MOE_RANK_FUSED(true, uint16_t);
+#undef MOE_RANK_FUSED
+      return hipGetLastError();
+    }
     hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, cc, cerr, nch, E, cap, a.pad,
                        a.counts, a.offsets, stats);
-    const int nbits = ceil_log2(E);
     if (nch > 0)
       hipLaunchKernelGGL(k_rank, dim3(nch), dim3(kThreads), 5 * E * sizeof(int), s, a.ids, a.w,
                          a.r, T, k, E, nbits, cap, cc, a.offsets, a.pos, a.row_token, a.row_r,
