@@ -240,7 +240,12 @@ def test_determinism(name, dev):
                                            (1 << 20, 32, 10 ** 6, 1, 300),
                                            # 16384 slots in groups padded to 128 rows;
                                            # 256 experts at k=6 with a ragged T
-                                           (8, 2, 8192, 128, 8192), (256, 6, 40, 1, 2730)])
+                                           (8, 2, 8192, 128, 8192), (256, 6, 40, 1, 2730),
+                                           # 2048 experts: a count table of 4 chunks that
+                                           # the rank launch scans itself (one thread
+                                           # per expert), and one of 18 chunks (over
+                                           # 2^15 entries) that takes the separate scan
+                                           (2048, 2, 50, 1, 1000), (2048, 2, 50, 1, 4500)])
 def test_dispatch_bit_exact(E, k, cap, pad, T, dev):
     _say(f"[gpu] dispatch E={E} k={k} cap={cap} pad={pad} T={T}")
     rng = np.random.default_rng(E + k + T)
