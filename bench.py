@@ -30,39 +30,39 @@ PEAK_HBM_GBPS = 8000.0
 # HBM bytes per launch of the first expert GEMM, per workload, from two
 # rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) scaled by
 # what the same counters read for a plain 1 GiB device copy
-# (bench.py --copy-calibration: FETCH_SIZE 524304.9 KiB, WRITE_SIZE 1048576 KiB).
+# (bench.py --copy-calibration: FETCH_SIZE 524302.5 KiB, WRITE_SIZE 1048576 KiB).
 # The mean over the first 18 launches of the run (warm-up, stage-timer and
 # timed forwards on the workload's own routing; the router-extras pass after
 # them routes with noise and is left out).  Valid only for the kernel sources
 # they were taken on: any change to those files reports null.
-COPY_SCALE = {"fetch": 1048576.0 / 524304.9, "write": 1048576.0 / 1048576.0}
+COPY_SCALE = {"fetch": 1048576.0 / 524302.5, "write": 1048576.0 / 1048576.0}
 TRAFFIC = {
     "mixtral_bf16": {
         "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
                                                  "common.h"),
         "source_sha256": "d0c77c445d1ed47ab172f37ebe2506c39b8a5813a9ea18e7481756bf98b5a53d",
-        "fetch_kib": 1826471.2, "write_kib": 230444.0},
+        "fetch_kib": 1813250.1, "write_kib": 230448.3},
     "variable_bcsr_bf16": {
         "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
                                                  "common.h"),
         "source_sha256": "d0c77c445d1ed47ab172f37ebe2506c39b8a5813a9ea18e7481756bf98b5a53d",
-        "fetch_kib": 30445.5, "write_kib": 46724.2},
+        "fetch_kib": 30446.8, "write_kib": 47800.4},
     # the routed first GEMM only (the shared experts' first GEMM is the same
     # kernel; the dispatches alternate, routed first)
     "finegrained_bf16": {
         "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
                                                  "common.h"),
         "source_sha256": "d0c77c445d1ed47ab172f37ebe2506c39b8a5813a9ea18e7481756bf98b5a53d",
-        "fetch_kib": 761191.1, "write_kib": 114981.5},
+        "fetch_kib": 759555.6, "write_kib": 114982.3},
     "atomic_bf16": {
         "kernel": "k_atomic_token", "sources": ("atomic.hip", "common.h"),
         "source_sha256": "7020a44046cfa9c4bc2ee1d7087ff80709367bd331479c1dadda27f72bc9993a",
-        "fetch_kib": 535696.7, "write_kib": 16384.0},
+        "fetch_kib": 535654.4, "write_kib": 16384.0},
     "mixtral_mxfp8": {
         "kernel": "k_gemm_mx", "sources": ("gemm_mx.hip", "gemm_args.h", "gemm_common.h",
                                            "common.h"),
         "source_sha256": "b8b0d5bce01672c5b84281688c740e5a1d9890f96f2aa1988d0a3cbb6319493f",
-        "fetch_kib": 875296.5, "write_kib": 123468.4},
+        "fetch_kib": 873523.3, "write_kib": 123357.8},
 }
 
 
