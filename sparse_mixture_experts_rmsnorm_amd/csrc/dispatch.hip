@@ -272,11 +272,11 @@ __global__ void __launch_bounds__(kThreads) k_rank(
 // count table itself -- its chunk's bases, the expert totals, the capacity
 // test and the padded offsets -- so no separate scan launch sits between the
 // count and the rank.  Block 0 writes counts, offsets and the statistics.
-// With GATHER the chunk is ranked by `workers` blocks, all of which compute
-// the same ranks; worker 0 writes the slot metadata and each worker copies
-// its share of the chunk's kept rows into x_perm (token row t to row p), so
-// the gather runs in the same launch; the last chunk's workers also zero the
-// padding rows.
+// With GATHER (rows of 2 KB and more) the chunk is ranked by `workers`
+// blocks, all of which compute the same ranks; worker 0 writes the slot
+// metadata and each worker copies its share of the chunk's kept rows into
+// x_perm (token row t to row p), so the gather runs in the same launch; the
+// last chunk's workers also zero the padding rows.
 constexpr int kFusedScanMax = 1 << 15;
 
 template <bool GATHER, typename T>
@@ -726,6 +726,7 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   const int T = int(a.T), k = a.k, E = int(a.E);
   int32_t* stats = reinterpret_cast<int32_t*>(a.stats);
   const int64_t fill_blocks = std::min<int64_t>(1024, (a.rows_max + 255) / 256);
+  bool gathered = false;   // the rank launch also wrote x_perm
   if (E <= kDenseMaxE) {
     const int nch = (T + kChunkTokens - 1) / kChunkTokens;
     int32_t* cc = reinterpret_cast<int32_t*>(a.ws);
@@ -737,29 +738,35 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
     const int cap = int(std::min<int64_t>(a.cap, int64_t(1) << 30));
     const int nbits = ceil_log2(E);
     const int chunk_slots = std::min(kChunkTokens, std::max(T, 1)) * k;
-    const size_t smem_fused = size_t(7 * E + 1 + (a.x_perm ? chunk_slots : 0)) * sizeof(int);
+    // the row gather joins the rank launch for rows of 2 KB and more; shorter
+    // rows copy faster with the separate gather kernel's one row per wave
+    // (measured: 1.5 KB rows 19.6 us against 26 us fused, 8 KB rows 22.9
+    // against 30 us)
+    const bool fuse_gather = a.x_perm && a.d * (a.dtype == 0 ? 4 : 2) >= 2048;
+    const size_t smem_fused = size_t(7 * E + 1 + (fuse_gather ? chunk_slots : 0)) * sizeof(int);
     if (int64_t(nch) * E <= kFusedScanMax && smem_fused <= 60 * 1024) {
-      // one launch ranks (and, with x_perm, gathers): workers per chunk so that
-      // each wave copies about two rows
-      const int workers = a.x_perm ? std::max(1, std::min(64, (chunk_slots + 7) / 8)) : 1;
+      // workers per chunk: about 1024 blocks in all (each repeats its chunk's
+      // rank before copying its share of the rows)
+      const int workers = fuse_gather ? std::max(1, std::min(64, 1024 / std::max(nch, 1))) : 1;
       const dim3 g(unsigned(std::max(nch, 1) * workers));
 #define MOE_RANK_FUSED(G, TY)                                                                  \
   hipLaunchKernelGGL((k_rank_fused<G, TY>), g, dim3(kThreads), smem_fused, s, a.ids, a.w, a.r, T, \
                      k, E, nbits, cap, a.pad, nch, workers, cc, cerr, a.counts, a.offsets,     \
                      stats, a.pos, a.row_token, a.row_r, a.row_w, a.row_expert,               \
                      static_cast<const TY*>(a.x), a.d, static_cast<TY*>(a.x_perm))
-      if (!a.x_perm) MOE_RANK_FUSED(false, uint16_t);
+      if (!fuse_gather) MOE_RANK_FUSED(false, uint16_t);
       else if (a.dtype == 0) MOE_RANK_FUSED(true, float);
       else MOE_RANK_FUSED(true, uint16_t);
 #undef MOE_RANK_FUSED
-      return hipGetLastError();
+      gathered = fuse_gather;
+    } else {
+      hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, cc, cerr, nch, E, cap, a.pad,
+                         a.counts, a.offsets, stats);
+      if (nch > 0)
+        hipLaunchKernelGGL(k_rank, dim3(nch), dim3(kThreads), 5 * E * sizeof(int), s, a.ids,
+                           a.w, a.r, T, k, E, nbits, cap, cc, a.offsets, a.pos, a.row_token,
+                           a.row_r, a.row_w, a.row_expert);
     }
-    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, cc, cerr, nch, E, cap, a.pad,
-                       a.counts, a.offsets, stats);
-    if (nch > 0)
-      hipLaunchKernelGGL(k_rank, dim3(nch), dim3(kThreads), 5 * E * sizeof(int), s, a.ids, a.w,
-                         a.r, T, k, E, nbits, cap, cc, a.offsets, a.pos, a.row_token, a.row_r,
-                         a.row_w, a.row_expert);
   } else {
     // two-pass LSD radix sort of the slots by expert id (keys < 2^B, E = sentinel)
     const int64_t N = int64_t(T) * k;
@@ -802,7 +809,7 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
                          a.r, a.pos, a.row_token, a.row_r, a.row_w, a.row_expert);
     }
   }
-  if (a.x_perm) {
+  if (a.x_perm && !gathered) {
     const unsigned g = unsigned(std::max<int64_t>(1, std::min<int64_t>(8192, (a.rows_max + 3) / 4)));
     if (a.dtype == 0)
       hipLaunchKernelGGL(k_gather<float>, dim3(g), dim3(kThreads), 0, s,

@@ -247,7 +247,21 @@ def test_determinism(name, dev):
                                            # 2^15 entries) that takes the separate scan
                                            (2048, 2, 50, 1, 1000), (2048, 2, 50, 1, 4500)])
 def test_dispatch_bit_exact(E, k, cap, pad, T, dev):
-    _say(f"[gpu] dispatch E={E} k={k} cap={cap} pad={pad} T={T}")
+    _check_dispatch(E, k, cap, pad, T, 256, "bf16", dev)
+
+
+# rows of 2 KB and more: the rank launch copies them itself (its blocks split
+# each chunk's rows; the last chunk's blocks zero the padding rows)
+@pytest.mark.parametrize("E,k,cap,pad,T,d,xdt", [(8, 2, 5, 1, 40, 1024, "bf16"),
+                                                 (64, 6, 30, 1, 1000, 1024, "bf16"),
+                                                 (8, 2, 8192, 128, 8192, 2048, "bf16"),
+                                                 (16, 4, 6000, 1, 3000, 512, "f32")])
+def test_dispatch_gather_wide_rows(E, k, cap, pad, T, d, xdt, dev):
+    _check_dispatch(E, k, cap, pad, T, d, xdt, dev)
+
+
+def _check_dispatch(E, k, cap, pad, T, d, xdt, dev):
+    _say(f"[gpu] dispatch E={E} k={k} cap={cap} pad={pad} T={T} d={d} {xdt}")
     rng = np.random.default_rng(E + k + T)
     # skewed ids (many ties in token order), distinct within a token
     pop = rng.zipf(1.3, size=E * 4) % E
@@ -270,10 +284,13 @@ def test_dispatch_bit_exact(E, k, cap, pad, T, dev):
                row_r=torch.empty(max(R, 1), dtype=torch.float32, device=dev),
                row_w=torch.empty(max(R, 1), dtype=torch.float32, device=dev),
                row_expert=torch.empty(max(R, 1), dtype=torch.int32, device=dev))
-    d = 256
-    xb = O.f64_to_bf16_bits(rng.standard_normal((T, d)))
-    x = synth.to_device(xb, dev)
-    x_perm = torch.empty((max(R, 1), d), dtype=torch.bfloat16, device=dev) if E <= 2048 else None
+    if xdt == "bf16":
+        xb = O.f64_to_bf16_bits(rng.standard_normal((T, d)))
+        x = synth.to_device(xb, dev)
+    else:
+        xb = rng.standard_normal((T, d)).astype(np.float32)
+        x = torch.from_numpy(xb).to(dev)
+    x_perm = torch.empty((max(R, 1), d), dtype=x.dtype, device=dev) if E <= 2048 else None
     stats = torch.zeros(4, dtype=torch.int32, device=dev)
     ws = torch.empty(B.dispatch_workspace_size(T, k, E), dtype=torch.uint8, device=dev)
     B.dispatch(torch.from_numpy(ids).to(dev), torch.from_numpy(w).to(dev), torch.from_numpy(r).to(dev),
@@ -299,9 +316,9 @@ def test_dispatch_bit_exact(E, k, cap, pad, T, dev):
     st = stats.cpu().numpy()
     assert st[0] == rows and st[1] == ref["dropped"] and st[2] == ref["max_load"] and st[3] == 0
     if x_perm is not None:
-        xp = synth.to_host(x_perm)[:rows]
+        xp = synth.to_host(x_perm)[:rows] if xdt == "bf16" else x_perm.cpu().numpy()[:rows]
         want = np.where(ref["row_token"][:, None] >= 0, xb[np.maximum(ref["row_token"], 0)], 0)
-        assert np.array_equal(xp, want.astype(np.uint16))
+        assert np.array_equal(xp, want.astype(xb.dtype))
 
 
 def test_dispatch_counts_bad_ids(dev):
