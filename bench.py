@@ -61,7 +61,7 @@ TRAFFIC = {
     "mixtral_mxfp8": {
         "kernel": "k_gemm_mx", "sources": ("gemm_mx.hip", "gemm_args.h", "gemm_common.h",
                                            "common.h"),
-        "source_sha256": "b8b0d5bce01672c5b84281688c740e5a1d9890f96f2aa1988d0a3cbb6319493f",
+        "source_sha256": "d1ec4da245b8679b5f3cca7ebfdba999d44e27aac130f024c2c92e8331b42747",
         "fetch_kib": 873523.3, "write_kib": 123357.8},
 }
 

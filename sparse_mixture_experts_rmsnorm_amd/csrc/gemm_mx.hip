@@ -41,10 +41,9 @@ constexpr int kRsrcWord3 = 0x00020000;
 // subnormals on the 2^-9 grid.  gfx950's v_cvt_pk_fp8_f32 converts a pair
 // to OCP E4M3 with round-to-nearest-even; clamped to +-448 first (past the
 // largest normal the instruction itself would give NaN), its codes equal this
-// rounding exactly, checked on the GPU for both signs over a dense mantissa
-// sweep of every exponent a block-scaled value can take, every midpoint
-// between neighbouring codes and the floats either side of it, the
-// subnormals, zero and the saturation range.
+// rounding exactly: the quantiser's parity test compares them with the
+// oracle's encoder at every midpoint between neighbouring codes and the bf16
+// values either side of it, both signs, at three block scales.
 __device__ __forceinline__ uint32_t e4m3_pk_pair(float a, float b) {
   const float ca = __builtin_fminf(__builtin_fmaxf(a, -448.f), 448.f);
   const float cb = __builtin_fminf(__builtin_fmaxf(b, -448.f), 448.f);
