@@ -40,19 +40,19 @@ TRAFFIC = {
     "mixtral_bf16": {
         "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
                                                  "common.h"),
-        "source_sha256": "d0c77c445d1ed47ab172f37ebe2506c39b8a5813a9ea18e7481756bf98b5a53d",
+        "source_sha256": "f36c2264545e28e357580261725f3223cda38f61ca0e53d273ca5b223738ef6c",
         "fetch_kib": 1813250.1, "write_kib": 230448.3},
     "variable_bcsr_bf16": {
         "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
                                                  "common.h"),
-        "source_sha256": "d0c77c445d1ed47ab172f37ebe2506c39b8a5813a9ea18e7481756bf98b5a53d",
+        "source_sha256": "f36c2264545e28e357580261725f3223cda38f61ca0e53d273ca5b223738ef6c",
         "fetch_kib": 30446.6, "write_kib": 48231.8},
     # the routed first GEMM only (the shared experts' first GEMM is the same
     # kernel; the dispatches alternate, routed first)
     "finegrained_bf16": {
         "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
                                                  "common.h"),
-        "source_sha256": "d0c77c445d1ed47ab172f37ebe2506c39b8a5813a9ea18e7481756bf98b5a53d",
+        "source_sha256": "f36c2264545e28e357580261725f3223cda38f61ca0e53d273ca5b223738ef6c",
         "fetch_kib": 761719.6, "write_kib": 114982.5},
     "atomic_bf16": {
         "kernel": "k_atomic_token", "sources": ("atomic.hip", "common.h"),
@@ -61,7 +61,7 @@ TRAFFIC = {
     "mixtral_mxfp8": {
         "kernel": "k_gemm_mx", "sources": ("gemm_mx.hip", "gemm_args.h", "gemm_common.h",
                                            "common.h"),
-        "source_sha256": "d1ec4da245b8679b5f3cca7ebfdba999d44e27aac130f024c2c92e8331b42747",
+        "source_sha256": "253db08ab50f1b14be6112f00ab352d3a92fea69571d30f55fecd5c4483d34f2",
         "fetch_kib": 873523.3, "write_kib": 123357.8},
 }
 

@@ -259,6 +259,7 @@ void fit_dense_tiles(ExpertGeo* g, int dtype, int64_t d, int64_t T) {
 // tiles says that the last round leaves compute units idle, and then only
 // that round's tiles are cut (carve_expert_ws).
 constexpr bool kCostRuns = true;
+constexpr int kMaxParts2 = 8;   // K pieces per split tile of the second linear
 bool want_pieces(const ExpertGeo& g, int dtype, int64_t d, int64_t rows_used_est) {
   if (g.bcsr || g.atomic || dtype != MOE_BF16 || g.kdiv < 2) return false;
   constexpr double kRoundCost = 0.017, kPartCost = 0.031;
@@ -413,7 +414,7 @@ int run_expert_gemms_mx(const moe_experts_desc* X, const ExpertGeo& g, int64_t d
   b.xs_bytes = RP * (g.Fmax / 32);
   b.ws_bytes = d * (g.F / 32);
   MOE_HIP(launch_gemm_mx(b, w.grid2 > 0 ? w.grid2 : int(w.mt2), s));
-  if (w.pieces2) MOE_HIP(launch_piece_fixup(b.g, g.bf2, g.bt2, w.grid2, s));
+  if (w.pieces2) MOE_HIP(launch_piece_fixup(b.g, g.bf2, g.bt2, w.grid2, kMaxParts2, s));
   timer_mark(timer, call, MOE_STAGE_GEMM2 + 1, s);
   (void)dense_rows;
   return MOE_OK;
@@ -462,7 +463,7 @@ int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, i
   p2.ksplit = 1;
   p2.bt = g.bt2;
   p2.grid = w.grid2;
-  p2.max_parts = w.pieces2 ? 8 : 1;
+  p2.max_parts = w.pieces2 ? kMaxParts2 : 1;
   p2.cost_split = 0;
   p2.counters = w.counters;
   MOE_HIP(launch_plan_pair(p, p2, s));
@@ -509,7 +510,7 @@ int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, i
   b.part = w.part;
   b.counters = w.counters;
   MOE_HIP(launch_gemm(dtype, b, g.bf2, g.bt2, w.grid2 > 0 ? w.grid2 : int(w.mt2), s));
-  if (w.pieces2) MOE_HIP(launch_piece_fixup(b, g.bf2, g.bt2, w.grid2, s));
+  if (w.pieces2) MOE_HIP(launch_piece_fixup(b, g.bf2, g.bt2, w.grid2, kMaxParts2, s));
   timer_mark(timer, call, MOE_STAGE_GEMM2 + 1, s);
   return MOE_OK;
 }

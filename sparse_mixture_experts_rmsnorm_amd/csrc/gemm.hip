@@ -189,50 +189,53 @@ __device__ __forceinline__ void epilogue_f32_lds(const GemmArgs& a, const Tile& 
   }
 }
 
-// Fixup of split tiles: one wave per workgroup, WGF x WGT workgroups per
-// split tile, workgroup (g, w) taking wave w's share of tile g.  It sums the
-// nparts partials in part order (part 0 first: the same fp32 sum every run)
-// and applies the tile's epilogue, which is per wave.  All loads of one part
-// are issued before the adds.  counters[g] is the list entry of the tile's
-// part 0; a.ntiles[10] holds the number of split tiles.
-template <int BF, int BT, int WGF, int WGT, int EPI>
-__global__ void __launch_bounds__(64) k_piece_fixup(GemmArgs a) {
-  constexpr int NW = WGF * WGT;
+// Fixup of split tiles (the second linear's gate epilogue): one wave per
+// 32 x 32 block of a split tile -- item (g, w, i, j): tile g, GEMM wave w,
+// its block (i, j) -- four items per workgroup, so that the loads of every
+// part of a block are in flight together.  The parts are summed in part order
+// (part 0 first: the same fp32 sum every run), then the block is gated and
+// stored as the GEMM's own epilogue stores it.  counters[g] is the list entry
+// of the tile's part 0; a.ntiles[10] holds the number of split tiles.
+constexpr int kFixupMaxParts = 8;
+
+template <int BF, int BT, int WGF, int WGT>
+__global__ void __launch_bounds__(256) k_piece_fixup(GemmArgs a) {
   constexpr int WTF = BF / WGF, WTT = BT / WGT;
   constexpr int MF = WTF / 32, MT = WTT / 32;
-  const int g = blockIdx.x / NW;
+  constexpr int NI = WGF * WGT * MF * MT;       // items per tile
+  const int item = int(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int g = item / NI;
   if (g >= a.ntiles[10]) return;
-  const int wid = blockIdx.x % NW;
+  const int r = item - g * NI;
+  const int wid = r / (MF * MT), ij = r - wid * (MF * MT);
+  const int i = ij / MT, j = ij - i * MT;
   const Tile tile = a.tiles[a.counters[g]];
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63, fr = lane & 31, fh = lane >> 5;
   const int wt = wid / WGF, wf = wid % WGF;
-  const int fr = lane & 31, fh = lane >> 5;
-  const float* const src0 = a.part + int64_t(tile.pslot0) * (int64_t(BF) * BT);
-  f32x16 acc[MF][MT];
-  for (int pt = 0; pt < tile.nparts; ++pt) {
-    f32x4 w[MF][MT][4];
+  const int np = tile.nparts;
+  const f32x4* const src = reinterpret_cast<const f32x4*>(
+      a.part + int64_t(tile.pslot0) * (int64_t(BF) * BT) + piece_frag_offset<BF, BT, MF, MT>(wid, lane, i, j));
+  constexpr int PS = BF * BT / 4;               // f32x4 between parts
+  f32x4 v[kFixupMaxParts][4];
 #pragma unroll
-    for (int i = 0; i < MF; ++i)
+  for (int pt = 0; pt < kFixupMaxParts; ++pt)
+    if (pt < np)
 #pragma unroll
-      for (int j = 0; j < MT; ++j) {
-        const f32x4* src = reinterpret_cast<const f32x4*>(
-            src0 + int64_t(pt) * (int64_t(BF) * BT) + piece_frag_offset<BF, BT, MF, MT>(wid, lane, i, j));
+      for (int q = 0; q < 4; ++q) v[pt][q] = src[pt * PS + q];
+  f32x4 acc[4] = {v[0][0], v[0][1], v[0][2], v[0][3]};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) w[i][j][q] = src[q];
-      }
+  for (int pt = 1; pt < kFixupMaxParts; ++pt)
+    if (pt < np)
 #pragma unroll
-    for (int i = 0; i < MF; ++i)
+      for (int q = 0; q < 4; ++q) acc[q] += v[pt][q];
+  const int row = tile.row0 + wt * WTT + j * 32 + fr;
+  if (row >= tile.row_end) return;
+  const float rs = a.row_w ? a.row_w[row] : 1.f;
+  uint16_t* Y = static_cast<uint16_t*>(a.Y) + int64_t(row) * a.ldy + tile.ocol0 + wf * WTF + i * 32;
 #pragma unroll
-      for (int j = 0; j < MT; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (pt == 0) acc[i][j][4 * q + e] = w[i][j][q][e];
-            else acc[i][j][4 * q + e] += w[i][j][q][e];
-          }
-  }
-  gemm_epilogue<BF, BT, WGF, WGT, EPI>(a, tile, acc, wf, wt, fr, fh);
+  for (int q = 0; q < 4; ++q)
+    *reinterpret_cast<uint2*>(Y + q * 8 + fh * 4) =
+        make_uint2(pk_bf16(rs * acc[q][0], rs * acc[q][1]), pk_bf16(rs * acc[q][2], rs * acc[q][3]));
 }
 
 // ---------------------------------------------------------------- bf16 MFMA GEMM, LDS-DMA ring
@@ -1157,27 +1160,16 @@ hipError_t launch_gemm(int dtype, const GemmArgs& a, int bf, int bt, int grid, h
   return hipGetLastError();
 }
 
-hipError_t launch_piece_fixup(const GemmArgs& a, int bf, int bt, int grid, hipStream_t s) {
-  // grid = the GEMM's persistent grid, which bounds the number of split tiles
+hipError_t launch_piece_fixup(const GemmArgs& a, int bf, int bt, int grid, int max_parts,
+                              hipStream_t s) {
+  // grid = the GEMM's persistent grid; a split tile holds at least two of its
+  // workgroups' pieces, so there are at most grid / 2 split tiles
   if (grid <= 0) return hipSuccess;
-  if (bf != 256 || (bt != 256 && bt != 128)) return hipErrorInvalidValue;
-  if (bt == 256) {
-    const dim3 g(grid * 8);
-    switch (a.epi) {
-      case EPI_ACT: hipLaunchKernelGGL((k_piece_fixup<256, 256, 4, 2, EPI_ACT>), g, dim3(64), 0, s, a); break;
-      case EPI_SWIGLU: hipLaunchKernelGGL((k_piece_fixup<256, 256, 4, 2, EPI_SWIGLU>), g, dim3(64), 0, s, a); break;
-      case EPI_GATE: hipLaunchKernelGGL((k_piece_fixup<256, 256, 4, 2, EPI_GATE>), g, dim3(64), 0, s, a); break;
-      default: return hipErrorInvalidValue;
-    }
-  } else {
-    const dim3 g(grid * 4);
-    switch (a.epi) {
-      case EPI_ACT: hipLaunchKernelGGL((k_piece_fixup<256, 128, 2, 2, EPI_ACT>), g, dim3(64), 0, s, a); break;
-      case EPI_SWIGLU: hipLaunchKernelGGL((k_piece_fixup<256, 128, 2, 2, EPI_SWIGLU>), g, dim3(64), 0, s, a); break;
-      case EPI_GATE: hipLaunchKernelGGL((k_piece_fixup<256, 128, 2, 2, EPI_GATE>), g, dim3(64), 0, s, a); break;
-      default: return hipErrorInvalidValue;
-    }
-  }
+  if (bf != 256 || bt != 256 || a.epi != EPI_GATE || max_parts > kFixupMaxParts)
+    return hipErrorInvalidValue;
+  constexpr int NI = 8 * 2 * 4;                 // items per 256 x 256 tile, 4 per workgroup
+  const dim3 g(unsigned((grid + 1) / 2 * NI / 4));
+  hipLaunchKernelGGL((k_piece_fixup<256, 256, 4, 2>), g, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -124,6 +124,7 @@ hipError_t launch_gemm(int dtype, const GemmArgs& a, int bf, int bt, int grid, h
 int gemm_persistent_grid(int tiles);
 // The epilogue of the split tiles of a persistent launch planned for it
 // (grid: workgroups, at least the number of split tiles).
-hipError_t launch_piece_fixup(const GemmArgs& a, int bf, int bt, int grid, hipStream_t s);
+hipError_t launch_piece_fixup(const GemmArgs& a, int bf, int bt, int grid, int max_parts,
+                              hipStream_t s);
 
 }  // namespace moe
