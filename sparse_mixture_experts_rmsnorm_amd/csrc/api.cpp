@@ -215,10 +215,12 @@ struct ExpertWs {
   int64_t mt1 = 0, mt2 = 0;
   int64_t rows_max = 0;
   // MXFP8: the quantised GEMM rows and hidden activation with their scales
-  uint8_t* xq = nullptr;   // [rows_max, d]
-  uint8_t* xqs = nullptr;  // [rows_max, d / 32]
-  uint8_t* hq = nullptr;   // [rows_max, Fmax]
-  uint8_t* hqs = nullptr;  // [rows_max, Fmax / 32]
+  // (rp = rows_max + one tile of padding rows; the scales are stage-major:
+  // the four bytes of row r in 128-element K stage s at s * 4 rp + 4 r)
+  uint8_t* xq = nullptr;   // [rp, d]
+  uint8_t* xqs = nullptr;  // [d / 128, rp, 4]
+  uint8_t* hq = nullptr;   // [rp, Fmax]
+  uint8_t* hqs = nullptr;  // [Fmax / 128, rp, 4]
   bool xq_ready = false;   // the caller already quantised the rows into xq (the layer
                            // does it as its dispatch gather)
   // saved for the backward pass: pre-activations [rows_max, pf * Fmax] (bf16)
@@ -363,7 +365,7 @@ int run_expert_gemms_mx(const moe_experts_desc* X, const ExpertGeo& g, int64_t d
     return fail(MOE_ESHAPE, "MXFP8 row buffers must stay below 2 GiB (rows %lld)", (long long)R);
   if (!w.xq_ready)
     MOE_HIP(launch_quant_mx(x_in, R, d, d, xrow, offsets ? offsets + X->E : nullptr, w.xq, d,
-                            w.xqs, d / 32, s));
+                            w.xqs, d / 32, RP * 4, s));
   MxGemmArgs a{};
   a.g.X = w.xq;
   a.g.ldx = d;
@@ -377,11 +379,11 @@ int run_expert_gemms_mx(const moe_experts_desc* X, const ExpertGeo& g, int64_t d
   a.g.epi = X->act == MOE_ACT_SWIGLU ? EPI_SWIGLU : EPI_ACT;
   a.g.act = X->act == MOE_ACT_GELU_TANH ? 1 : 0;
   a.xs = w.xqs;
-  a.ldxs = d / 32;
+  a.ldxs = RP * 4;                 // activation scales stage-major: bytes between stages
   a.ws = X->w13_scale;
   a.ldws = d / 32;
   a.ys = w.hqs;
-  a.ldys = g.Fmax / 32;
+  a.ldys = RP * 4;                 // h's scales written stage-major
   a.x_bytes = RP * d;
   a.w_bytes = P * d;
   a.xs_bytes = RP * (d / 32);
@@ -406,7 +408,7 @@ int run_expert_gemms_mx(const moe_experts_desc* X, const ExpertGeo& g, int64_t d
   b.g.part = w.part;
   b.g.counters = w.counters;
   b.xs = w.hqs;
-  b.ldxs = g.Fmax / 32;
+  b.ldxs = RP * 4;
   b.ws = X->w2_scale;
   b.ldws = g.F / 32;
   b.x_bytes = RP * g.Fmax;
@@ -592,7 +594,7 @@ int moe_pack_mxfp8(const void* src, int64_t R, int64_t K, int64_t lds, void* cod
   REQUIRE(R == 0 || (src && codes && scales), MOE_EINVAL, "NULL pointer");
   REQUIRE(reinterpret_cast<uintptr_t>(src) % 16 == 0 && reinterpret_cast<uintptr_t>(codes) % 8 == 0,
           MOE_EINVAL, "src must be 16-byte and codes 8-byte aligned");
-  MOE_HIP(launch_quant_mx(src, R, K, lds, nullptr, nullptr, codes, ldc, scales, ldsc, stream));
+  MOE_HIP(launch_quant_mx(src, R, K, lds, nullptr, nullptr, codes, ldc, scales, ldsc, 0, stream));
   return ok();
 }
 
@@ -1200,7 +1202,7 @@ int moe_layer_forward(const moe_layer_desc* L, const void* x, int64_t T, void* o
     if (g.mx) {
       // the MXFP8 path's gather: each routed row quantised once as it is read
       MOE_HIP(launch_quant_mx(xhat, w.rows_max, d, d, w.row_token, w.offsets + E, w.ex.xq, d,
-                              w.ex.xqs, d / 32, stream));
+                              w.ex.xqs, d / 32, (w.rows_max + kMxRowPad) * 4, stream));
       w.ex.xq_ready = true;
     }
   }

@@ -63,7 +63,11 @@ __device__ __forceinline__ int mx_shared_exp(float amax) {
   return min(127, max(-127, e - 1 - 8));
 }
 
-// Rows of bf16 [R, K] -> E4M3 codes [R, K] and E8M0 scales [R, K / 32].
+// Rows of bf16 [R, K] -> E4M3 codes [R, K] and E8M0 scales, either row-major
+// [R, K / 32] (sstage 0: row r's byte j at r ldsc + j) or stage-major for the
+// GEMM's activation operand (sstage > 0: the four scale bytes of row r in the
+// 128-element K stage s at s sstage + 4 r, so that one stage's scales of
+// consecutive rows are contiguous and the GEMM's scale DMA is coalesced).
 // Output row r reads source row map[r] (map NULL: r; -1: a zero row), so the
 // quantiser is also the dispatch gather of the MXFP8 path.  One wave per
 // row; a lane converts 8 consecutive elements, four lanes make a block.
@@ -72,7 +76,8 @@ __global__ void __launch_bounds__(256) k_quant_mx(const uint16_t* __restrict__ s
                                                   const int32_t* __restrict__ map,
                                                   const int32_t* __restrict__ rows_used,
                                                   uint8_t* __restrict__ codes, int64_t ldc,
-                                                  uint8_t* __restrict__ scales, int64_t ldsc) {
+                                                  uint8_t* __restrict__ scales, int64_t ldsc,
+                                                  int64_t sstage) {
   const int lane = threadIdx.x & 63;
   const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (row >= R || (rows_used && row >= *rows_used)) return;
@@ -94,7 +99,10 @@ __global__ void __launch_bounds__(256) k_quant_mx(const uint16_t* __restrict__ s
     for (int h = 0; h < 2; ++h)
       w[h] = e4m3_x4(f[4 * h] * inv, f[4 * h + 1] * inv, f[4 * h + 2] * inv, f[4 * h + 3] * inv);
     *reinterpret_cast<uint2*>(codes + row * ldc + k0) = make_uint2(w[0], w[1]);
-    if ((lane & 3) == 0) scales[row * ldsc + k0 / 32] = uint8_t(s + 127);
+    if ((lane & 3) == 0) {
+      const int64_t at = sstage > 0 ? (k0 / 128) * sstage + row * 4 + (k0 / 32) % 4 : row * ldsc + k0 / 32;
+      scales[at] = uint8_t(s + 127);
+    }
   }
 }
 
@@ -178,12 +186,16 @@ __global__ void __launch_bounds__(512) k_gemm_mx(MxGemmArgs m) {
   // Scale words ride with the operands: the 4 E8M0 bytes of a row's stage
   // (K offsets are multiples of 128, so they are one aligned 32-bit word)
   // land after the operand tiles, W rows then X rows, one 4-byte DMA per
-  // wave (waves 0-3: W rows 64 w .. 64 w + 63, waves 4-7: X rows).
+  // wave (waves 0-3: W rows 64 w .. 64 w + 63, waves 4-7: X rows).  The
+  // weights' scales are row-major (a stage's words of consecutive rows are a
+  // row pitch apart); the activation rows' are stage-major (consecutive), so
+  // their DMA reads 256 contiguous bytes.
   const bool wsc = wid < NW / 2;
   const __amdgpu_buffer_rsrc_t s_rsrc =
       wsc ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(m.ws), 0, int(m.ws_bytes), kRsrcWord3)
           : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(m.xs), 0, int(m.xs_bytes), kRsrcWord3);
   const int64_t srow_s = (wsc ? wid : wid - NW / 2) * 64 + lane;
+  const int s_step = wsc ? 4 : int(m.ldxs);     // bytes between a row's consecutive stages
   // this lane's offsets into its operand and scale rows for a tile (a K
   // piece starts at tile.kofs in the weights and tile.xk in the rows)
   uint32_t voff[2];                              // even / odd segments (swizzle parity)
@@ -196,7 +208,7 @@ __global__ void __launch_bounds__(512) k_gemm_mx(MxGemmArgs m) {
     for (int p = 0; p < 2; ++p)
       voff[p] = uint32_t(rbase * ld + kbase + ((lane % C) ^ srow ^ p) * 16);
     s_voff = wsc ? uint32_t((int64_t(t.wrow0) + srow_s) * m.ldws + t.kofs / 32)
-                 : uint32_t((int64_t(t.row0) + srow_s) * m.ldxs + xk0 / 32);
+                 : uint32_t((int64_t(t.row0) + srow_s) * 4 + int64_t(xk0 / 128) * m.ldxs);
   };
   auto issue = [&](int kt, int stage) {
     uint8_t* base = lds + stage * LS;
@@ -206,7 +218,7 @@ __global__ void __launch_bounds__(512) k_gemm_mx(MxGemmArgs m) {
           rsrc, (lds_void_ptr)(base + (wid * SPW + u) * 1024), 16, voff[(sg0 + u) & 1],
           int(kt * BK + int64_t(sg0 + u) * RSEG * ld), 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_void_ptr)(base + LT + wid * 256), 4,
-                                             s_voff, kt * 4, 0, 0);
+                                             s_voff, kt * s_step, 0, 0);
   };
   // stages 0 and 1 (a one-stage tile loads stage 0 twice, the second copy
   // into a buffer that is not read)
@@ -396,7 +408,7 @@ __global__ void __launch_bounds__(512) k_gemm_mx(MxGemmArgs m) {
               uint8_t* Y = static_cast<uint8_t*>(a.Y) + int64_t(row) * a.ldy + col;
 #pragma unroll
               for (int g = 0; g < 4; ++g) *reinterpret_cast<uint32_t*>(Y + g * 8 + fh * 4) = w[g];
-              if (fh == 0) m.ys[int64_t(row) * m.ldys + col / 32] = uint8_t(s + 127);
+              if (fh == 0) m.ys[int64_t(col / 128) * m.ldys + int64_t(row) * 4 + (col / 32) % 4] = uint8_t(s + 127);
             }
           }
         } else if (live) {
@@ -427,12 +439,12 @@ __global__ void __launch_bounds__(512) k_gemm_mx(MxGemmArgs m) {
 
 hipError_t launch_quant_mx(const void* src, int64_t R, int64_t K, int64_t lds, const int32_t* map,
                            const int32_t* rows_used, void* codes, int64_t ldc, void* scales,
-                           int64_t ldsc, hipStream_t s) {
+                           int64_t ldsc, int64_t sstage, hipStream_t s) {
   if (R <= 0) return hipSuccess;
   if (K % 32) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_quant_mx, dim3(unsigned((R + 3) / 4)), dim3(256), 0, s,
                      static_cast<const uint16_t*>(src), R, K, lds, map, rows_used,
-                     static_cast<uint8_t*>(codes), ldc, static_cast<uint8_t*>(scales), ldsc);
+                     static_cast<uint8_t*>(codes), ldc, static_cast<uint8_t*>(scales), ldsc, sstage);
   return hipGetLastError();
 }
 

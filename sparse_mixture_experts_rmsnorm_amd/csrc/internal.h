@@ -12,9 +12,12 @@ namespace moe {
 // [R, K] (stride ldc) and E8M0 scales [R, K / 32] (stride ldsc); the GEMM.
 // Output row r reads source row map[r] (map NULL: r; -1: zeros); rows at or
 // past *rows_used (when given) are left untouched.
+// sstage > 0: the scales stage-major instead, the four bytes of row r in
+// the 128-element K stage s at s * sstage + 4 r (the GEMM's activation
+// operand; K a multiple of 128).
 hipError_t launch_quant_mx(const void* src, int64_t R, int64_t K, int64_t lds, const int32_t* map,
                            const int32_t* rows_used, void* codes, int64_t ldc, void* scales,
-                           int64_t ldsc, hipStream_t s);
+                           int64_t ldsc, int64_t sstage, hipStream_t s);
 hipError_t launch_gemm_mx(const MxGemmArgs& m, int grid, hipStream_t s);
 
 hipError_t launch_pack_transpose(const void* src, int dtype, int64_t K, int64_t N, void* dst,
