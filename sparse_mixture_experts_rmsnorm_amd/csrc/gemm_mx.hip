@@ -122,11 +122,29 @@ __device__ __forceinline__ int mx_block_codes(const float (&o)[16], uint32_t (&w
   return s;
 }
 
+// Scheduling of one MXFP8 sub-step: the NA reads of the next A fragments
+// (and scale words) first, then per B block its MFN MFMAs followed by the two
+// reads that refill that block for the next sub-step.
+template <int NJ, int MFN>
+__device__ __forceinline__ void sched_mx_blocks() {
+  if constexpr (NJ > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x008, MFN, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    sched_mx_blocks<NJ - 1, MFN>();
+  }
+}
+template <int NA, int NJ, int MFN>
+__device__ __forceinline__ void sched_mx_step() {
+  __builtin_amdgcn_sched_group_barrier(0x100, NA, 0);
+  sched_mx_blocks<NJ, MFN>();
+}
+
 // 256 features x 256 rows per workgroup, 8 waves in a 4 x 2 grid of 64 x 128
-// wave tiles (MF = 2, MT = 4 blocks of 32 x 32).  A sub-step's fragments
-// (32 bytes per block) are read just before its MFMAs: the other wave on the
-// SIMD runs its MFMAs meanwhile, and one fragment set keeps the wave within
-// 256 registers.
+// wave tiles (MF = 2, MT = 4 blocks of 32 x 32).  Each sub-step's fragments
+// (32 bytes per block) are read under the MFMAs of the sub-step before: two
+// sets of A fragments, and one set of B fragments in which a block is
+// refilled as soon as its last MFMA has been issued, so the wave stays within
+// the 256 registers two waves per SIMD allow (a second full B set would not).
 //
 // Persistent, as the bf16 kernel: workgroup b takes tiles b, b + G, ... of the
 // XCD-remapped list, or of its XCD's run when the list was planned for this
@@ -256,23 +274,32 @@ __global__ void __launch_bounds__(512) k_gemm_mx(MxGemmArgs m) {
     DST = i32x8{int(lo_.x), int(lo_.y), int(lo_.z), int(lo_.w),                               \
                 int(hi_.x), int(hi_.y), int(hi_.z), int(hi_.w)};                              \
   }
-#define MOE_MX_FRAGS(SW, KSV)                                                                  \
+#define MOE_MX_LOADA(AF, SW, KSV)                                                              \
+  _Pragma("unroll") for (int i = 0; i < MF; ++i) MOE_MX_LOAD(AF[i], (SW) + i * 32 * BK, a_off, KSV)
+#define MOE_MX_LOADB(J, SW, KSV) MOE_MX_LOAD(bfr[J], (SW) + (J) * 32 * BK, b_off, KSV)
+// one sub-step's MFMAs, B block by B block; behind the last use of each B
+// block its registers are refilled with the same block of the next sub-step
+// (buffer SWN, sub-step KSVN), and the next sub-step's A fragments go to the
+// other A set first
+#define MOE_MX_STEP(AF, SA, SB, SWN, KSVN, AFN)                                                \
   {                                                                                            \
-    _Pragma("unroll") for (int i = 0; i < MF; ++i)                                            \
-      MOE_MX_LOAD(af[i], (SW) + i * 32 * BK, a_off, KSV)                                       \
-    _Pragma("unroll") for (int j = 0; j < MTA; ++j)                                           \
-      MOE_MX_LOAD(bfr[j], (SW) + j * 32 * BK, b_off, KSV)                                      \
-  }
-#define MOE_MX_MFMAS(KSV, SA, SB)                                                              \
-  {                                                                                            \
-    _Pragma("unroll") for (int i = 0; i < MF; ++i)                                            \
-      _Pragma("unroll") for (int j = 0; j < MTA; ++j)                                         \
+    MOE_MX_LOADA(AFN, SWN, KSVN)                                                               \
+    _Pragma("unroll") for (int j = 0; j < MTA; ++j) {                                         \
+      _Pragma("unroll") for (int i = 0; i < MF; ++i)                                          \
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                           \
-            af[i], bfr[j], acc[i][j], 0, 0, 0, int(SA[i]), 0, int(SB[j]));                     \
+            AF[i], bfr[j], acc[i][j], 0, 0, 0, int(SA[i]), 0, int(SB[j]));                     \
+      MOE_MX_LOADB(j, SWN, KSVN)                                                               \
+    }                                                                                          \
+  }
+#define MOE_MX_MFMAS(AF, SA, SB)                                                               \
+  {                                                                                            \
+    _Pragma("unroll") for (int j = 0; j < MTA; ++j)                                           \
+      _Pragma("unroll") for (int i = 0; i < MF; ++i)                                          \
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                           \
+            AF[i], bfr[j], acc[i][j], 0, 0, 0, int(SA[i]), 0, int(SB[j]));                     \
   }
 // E8M0 bytes of this lane's 32-block (2 ksv + fh of the stage) in sub-step ksv
 #define MOE_MX_BYTES(KSV, SA, SB)                                                              \
-  uint32_t SA[MF], SB[MT];                                                                     \
   {                                                                                            \
     const int sh_ = 8 * (2 * (KSV) + fh);                                                      \
     _Pragma("unroll") for (int i = 0; i < MF; ++i) SA[i] = (sa[i] >> sh_) & 0xFFu;            \
@@ -286,13 +313,14 @@ __global__ void __launch_bounds__(512) k_gemm_mx(MxGemmArgs m) {
       sb[j] = *reinterpret_cast<const uint32_t*>((SW) + LT + BF * 4 + (wt * WTT + j * 32 + fr) * 4); \
   }
 
-    // Two LDS stages and one barrier per stage, placed after the last
-    // sub-step's fragments are in registers: behind it the drained buffer is
-    // refilled (stage kt + 2) while that sub-step's MFMAs run.  The loop body
-    // has no branch (a branch lets the compiler sink the first sub-step's
-    // MFMAs below the barrier, which keeps both fragment sets live): past the
-    // last stage the refill repeats stage nk - 1, in bounds, into a buffer that
-    // is not read again.
+    // Two LDS stages and one barrier per stage, placed after the stage's last
+    // fragments are in registers: behind it the drained buffer is refilled
+    // (stage kt + 2) while the second sub-step's MFMAs run.  The fragments of
+    // each sub-step are read under the MFMAs of the one before (two A sets,
+    // one B set refilled block by block), so a wave's MFMAs never wait for
+    // its own LDS reads except at the barrier.  The loop body has no branch:
+    // past the last stage the refill repeats stage nk - 1, in bounds, into a
+    // buffer that is not read again.
     // Row blocks of this wave that hold rows of the tile: the MFMAs, fragment
     // and scale reads of the rest (never stored) are skipped, one loop copy
     // per count.
@@ -301,7 +329,8 @@ __global__ void __launch_bounds__(512) k_gemm_mx(MxGemmArgs m) {
     auto main_loop = [&](auto mta_c) {
       constexpr int MTA = decltype(mta_c)::value;
       uint32_t sa[MF], sb[MT];
-      i32x8 af[MF], bfr[MT];
+      uint32_t s0a[MF], s0b[MT], s1a[MF], s1b[MT];
+      i32x8 af0[MF], af1[MF], bfr[MT];
       if (nk > 0) {
         // stage 0 has landed (after a previous tile's epilogue its stores
         // are counted too, so everything is waited for)
@@ -310,38 +339,39 @@ __global__ void __launch_bounds__(512) k_gemm_mx(MxGemmArgs m) {
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
+        MOE_MX_SCALES(lds)
+        MOE_MX_LOADA(af0, lds, 0)
+        _Pragma("unroll") for (int j = 0; j < MTA; ++j) MOE_MX_LOADB(j, lds, 0)
+        MOE_MX_BYTES(0, s0a, s0b)
+        __builtin_amdgcn_sched_barrier(0);
         for (int kt = 0; kt + 1 < nk; ++kt) {
           const uint8_t* sw = lds + (kt & 1) * LS;
+          const uint8_t* swn = lds + ((kt + 1) & 1) * LS;
           const int knext = min(kt + 2, nk - 1);
-          MOE_MX_SCALES(sw)
-          MOE_MX_FRAGS(sw, 0)
-          {
-            MOE_MX_BYTES(0, s0a, s0b)
-            MOE_MX_MFMAS(0, s0a, s0b)
-          }
-          __builtin_amdgcn_sched_barrier(0);         // one fragment set live at a time
-          MOE_MX_FRAGS(sw, 1)
+          MOE_MX_STEP(af0, s0a, s0b, sw, 1, af1)
+          sched_mx_step<2 * MF, MTA, MF>();
+          __builtin_amdgcn_sched_barrier(0);
           MOE_MX_BYTES(1, s1a, s1b)
+          // this wave's reads of stage kt are in registers and its share of
+          // stage kt + 1 has landed; after the barrier both hold for every
+          // wave, so stage kt's buffer may be refilled
           asm volatile("s_waitcnt 0x0070" ::: "memory");   // vmcnt(0) lgkmcnt(0)
           __builtin_amdgcn_s_barrier();
           asm volatile("" ::: "memory");
           issue(knext, kt & 1);
-          MOE_MX_MFMAS(1, s1a, s1b)
           __builtin_amdgcn_sched_barrier(0);
+          MOE_MX_SCALES(swn)
+          MOE_MX_STEP(af1, s1a, s1b, swn, 0, af0)
+          sched_mx_step<2 * MF + MF + MTA, MTA, MF>();
+          __builtin_amdgcn_sched_barrier(0);
+          MOE_MX_BYTES(0, s0a, s0b)
         }
         const uint8_t* sw = lds + ((nk - 1) & 1) * LS;
-        MOE_MX_SCALES(sw)
-        MOE_MX_FRAGS(sw, 0)
-        {
-          MOE_MX_BYTES(0, s0a, s0b)
-          MOE_MX_MFMAS(0, s0a, s0b)
-        }
+        MOE_MX_STEP(af0, s0a, s0b, sw, 1, af1)
+        sched_mx_step<2 * MF, MTA, MF>();
         __builtin_amdgcn_sched_barrier(0);
-        MOE_MX_FRAGS(sw, 1)
-        {
-          MOE_MX_BYTES(1, s1a, s1b)
-          MOE_MX_MFMAS(1, s1a, s1b)
-        }
+        MOE_MX_BYTES(1, s1a, s1b)
+        MOE_MX_MFMAS(af1, s1a, s1b)
       }
     };
     static_assert(MT == 4, "one loop copy per row-block count");
@@ -352,7 +382,9 @@ __global__ void __launch_bounds__(512) k_gemm_mx(MxGemmArgs m) {
     else main_loop(std::integral_constant<int, 0>{});
 
 #undef MOE_MX_LOAD
-#undef MOE_MX_FRAGS
+#undef MOE_MX_LOADA
+#undef MOE_MX_LOADB
+#undef MOE_MX_STEP
 #undef MOE_MX_MFMAS
 #undef MOE_MX_SCALES
 #undef MOE_MX_BYTES
