@@ -30,29 +30,29 @@ PEAK_HBM_GBPS = 8000.0
 # HBM bytes per launch of the first expert GEMM, per workload, from two
 # rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) scaled by
 # what the same counters read for a plain 1 GiB device copy
-# (bench.py --copy-calibration: FETCH_SIZE 524304.8 KiB, WRITE_SIZE 1048576 KiB).
+# (bench.py --copy-calibration: FETCH_SIZE 524304.6 KiB, WRITE_SIZE 1048576 KiB).
 # The mean over the first 18 launches of the run (warm-up, stage-timer and
 # timed forwards on the workload's own routing; the router-extras pass after
 # them routes with noise and is left out).  Valid only for the kernel sources
 # they were taken on: any change to those files reports null.
-COPY_SCALE = {"fetch": 1048576.0 / 524304.8, "write": 1048576.0 / 1048576.0}
+COPY_SCALE = {"fetch": 1048576.0 / 524304.6, "write": 1048576.0 / 1048576.0}
 TRAFFIC = {
     "mixtral_bf16": {
         "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
                                                  "common.h"),
-        "source_sha256": "52e32c147832b6c990ce5f40a3836bee935c11635d94de4b9019dccaf97f0abf",
+        "source_sha256": "6d55dd23ea83ad24283f02f1eccec2aea8e6342392c6bb2056c263958e541398",
         "fetch_kib": 1868126.1, "write_kib": 230443.2},
     "variable_bcsr_bf16": {
         "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
                                                  "common.h"),
-        "source_sha256": "52e32c147832b6c990ce5f40a3836bee935c11635d94de4b9019dccaf97f0abf",
+        "source_sha256": "6d55dd23ea83ad24283f02f1eccec2aea8e6342392c6bb2056c263958e541398",
         "fetch_kib": 30461.3, "write_kib": 46232.8},
     # the routed first GEMM only (the shared experts' first GEMM is the same
     # kernel; the dispatches alternate, routed first)
     "finegrained_bf16": {
         "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
                                                  "common.h"),
-        "source_sha256": "52e32c147832b6c990ce5f40a3836bee935c11635d94de4b9019dccaf97f0abf",
+        "source_sha256": "6d55dd23ea83ad24283f02f1eccec2aea8e6342392c6bb2056c263958e541398",
         "fetch_kib": 761650.4, "write_kib": 114982.5},
     "atomic_bf16": {
         "kernel": "k_atomic_token", "sources": ("atomic.hip", "common.h"),
@@ -61,8 +61,8 @@ TRAFFIC = {
     "mixtral_mxfp8": {
         "kernel": "k_gemm_mx", "sources": ("gemm_mx.hip", "gemm_args.h", "gemm_common.h",
                                            "common.h"),
-        "source_sha256": "17731642531f70c2bf8c6d679bea3b7f0dbe5874ae70578e7335b35d8c44ea7c",
-        "fetch_kib": 963137.8, "write_kib": 118324.7},
+        "source_sha256": "9ff5c40b6054037be4b33fb85cf5877ddb426fdbd9d379c1612445c21f1e122a",
+        "fetch_kib": 904039.2, "write_kib": 118330.8},
 }
 
 

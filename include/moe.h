@@ -134,9 +134,10 @@ typedef struct moe_experts_desc {
   const int32_t* row_offsets;   /* [rows_max/block + 1] CSR row pointer       */
   const int32_t* column_indices;/* [nnz_max] column block of each nonzero     */
   /* MOE_QUANT_MXFP8 (GROUPED or BCSR, bf16 layers only): w13_t and w2_t hold E4M3
-   * codes (one byte per element, same packed layouts) and w13_scale [P, d/32],
-   * w2_scale [d, F/32] their E8M0 block scales, as written by moe_pack_mxfp8
-   * from the bf16 packs (P = F, or 2F for SwiGLU).  Following the CODA
+   * codes (one byte per element, same packed layouts) and w13_scale,
+   * w2_scale their E8M0 block scales in the stage-major layout written by
+   * moe_pack_mxfp8_weights from the bf16 packs: w13_scale [d/128][P][4],
+   * w2_scale [F/128][d][4] (P = F, or 2F for SwiGLU).  Following the CODA
    * thread's point that low-precision conversions are free in epilogues, the
    * expert rows are quantised once per (token, slot) as they are gathered,
    * the first linear's epilogue writes the hidden activation h as MXFP8, and
@@ -292,10 +293,25 @@ int moe_pack_swiglu(const void* w1, const void* w3, int dtype, int64_t d,
  * stored as the E4M3 code (bias 7, 3 mantissa bits, subnormals on the 2^-9
  * grid) of v * 2^-s rounded to nearest-even, magnitudes of 448 and above
  * saturated to 448, in codes [R, K] (row stride ldc bytes).  K % 32 == 0,
- * ldc % 8 == 0.  Used once on the packed expert weights (w13_t, w2_t); the
- * layer quantises its activations with the same kernel. */
+ * ldc % 8 == 0.  The layer quantises its activations with the same kernel;
+ * the expert weights take moe_pack_mxfp8_weights (below), which writes the
+ * same values with the scales in the GEMMs' layout. */
 int moe_pack_mxfp8(const void* src, int64_t R, int64_t K, int64_t lds, void* codes, int64_t ldc,
                    void* scales, int64_t ldsc, hipStream_t stream);
+
+/* MXFP8 pack of packed expert weights (w13_t [P, d] or w2_t [d, F], bf16) for
+ * the expert GEMMs: the same codes and block scales as moe_pack_mxfp8 (same
+ * format and rounding), with the scales stored stage-major, scales
+ * [K/128][R][4]: the E8M0 byte of row r for elements 32 j .. 32 j + 31 at
+ * byte 4 (floor(j/4) R + r) + j % 4, so that the four scales of one row
+ * over 128 consecutive elements form one 32-bit word and the words of
+ * consecutive rows are adjacent (a 256-row weight tile's scales for one
+ * 128-element K step are 1 KB of contiguous bytes).  This is the layout
+ * moe_experts_desc.w13_scale and w2_scale hold.  K % 128 == 0, lds and ldc
+ * multiples of 8, src 16-byte and codes 8-byte aligned; scales holds
+ * R * K / 32 bytes (below 2 GiB).  Errors: MOE_ESHAPE, MOE_EINVAL. */
+int moe_pack_mxfp8_weights(const void* src, int64_t R, int64_t K, int64_t lds, void* codes,
+                           int64_t ldc, void* scales, hipStream_t stream);
 
 /* ---- step 1: RMSNorm statistic ----
  * r[T] fp32.  If gamma is non-NULL, also writes xg[T, d] = x * gamma (dtype,

@@ -22,7 +22,7 @@ STAGES = ["router", "dispatch", "plan", "gemm1", "gemm2", "shared", "combine"]
 
 EXPORTED = [
     "moe_last_error", "moe_version", "moe_capacity", "moe_rows_max", "moe_pack_transpose",
-    "moe_pack_swiglu", "moe_pack_mxfp8", "moe_rmsnorm_stats", "moe_router_workspace_size", "moe_router_topk",
+    "moe_pack_swiglu", "moe_pack_mxfp8", "moe_pack_mxfp8_weights", "moe_rmsnorm_stats", "moe_router_workspace_size", "moe_router_topk",
     "moe_router_topk_ex",
     "moe_dispatch_workspace_size", "moe_dispatch", "moe_topology_nnz_max", "moe_build_topology",
     "moe_expert_workspace_size", "moe_expert_gemm", "moe_shared_workspace_size", "moe_shared_ffn",
@@ -101,6 +101,7 @@ def lib() -> C.CDLL:
             "moe_pack_transpose": (I, [P, I, I64, I64, P, P]),
             "moe_pack_swiglu": (I, [P, P, I, I64, C.POINTER(I64), I64, P, P]),
             "moe_pack_mxfp8": (I, [P, I64, I64, I64, P, I64, P, I64, P]),
+            "moe_pack_mxfp8_weights": (I, [P, I64, I64, I64, P, I64, P, P]),
             "moe_rmsnorm_stats": (I, [P, I, I64, I64, P, F, P, P, P]),
             "moe_router_workspace_size": (SZ, [C.POINTER(RouterDesc), I64]),
             "moe_router_topk": (I, [C.POINTER(RouterDesc), P, I, I64, I64, P, F, P, I, I, P, P, P,
@@ -218,6 +219,17 @@ def pack_mxfp8(src, codes, scales, stream=None) -> None:
     assert tuple(codes.shape) == (R, K) and tuple(scales.shape) == (R, K // 32)
     check(lib().moe_pack_mxfp8(ptr(src), R, K, src.stride(0), ptr(codes), codes.stride(0),
                                ptr(scales), scales.stride(0), stream_handle(stream)))
+
+
+def pack_mxfp8_weights(src, codes, scales, stream=None) -> None:
+    """MXFP8 codes [R, K] (uint8) and E8M0 block scales, stage-major
+    [K/128, R, 4] (uint8), of a packed bf16 weight matrix src [R, K]: the
+    layout the expert descriptor's w13_scale / w2_scale hold."""
+    R, K = src.shape
+    assert src.stride(1) == 1 and codes.stride(1) == 1 and scales.is_contiguous()
+    assert tuple(codes.shape) == (R, K) and tuple(scales.shape) == (K // 128, R, 4)
+    check(lib().moe_pack_mxfp8_weights(ptr(src), R, K, src.stride(0), ptr(codes), codes.stride(0),
+                                       ptr(scales), stream_handle(stream)))
 
 
 def rmsnorm_stats(x, eps, r, gamma=None, xg=None, stream=None) -> None:

@@ -381,7 +381,7 @@ int run_expert_gemms_mx(const moe_experts_desc* X, const ExpertGeo& g, int64_t d
   a.xs = w.xqs;
   a.ldxs = RP * 4;                 // activation scales stage-major: bytes between stages
   a.ws = X->w13_scale;
-  a.ldws = d / 32;
+  a.ldws = P * 4;                  // weight scales stage-major (moe_pack_mxfp8_weights)
   a.ys = w.hqs;
   a.ldys = RP * 4;                 // h's scales written stage-major
   a.x_bytes = RP * d;
@@ -410,7 +410,7 @@ int run_expert_gemms_mx(const moe_experts_desc* X, const ExpertGeo& g, int64_t d
   b.xs = w.hqs;
   b.ldxs = RP * 4;
   b.ws = X->w2_scale;
-  b.ldws = g.F / 32;
+  b.ldws = d * 4;
   b.x_bytes = RP * g.Fmax;
   b.w_bytes = d * g.F;
   b.xs_bytes = RP * (g.Fmax / 32);
@@ -595,6 +595,20 @@ int moe_pack_mxfp8(const void* src, int64_t R, int64_t K, int64_t lds, void* cod
   REQUIRE(reinterpret_cast<uintptr_t>(src) % 16 == 0 && reinterpret_cast<uintptr_t>(codes) % 8 == 0,
           MOE_EINVAL, "src must be 16-byte and codes 8-byte aligned");
   MOE_HIP(launch_quant_mx(src, R, K, lds, nullptr, nullptr, codes, ldc, scales, ldsc, 0, stream));
+  return ok();
+}
+
+int moe_pack_mxfp8_weights(const void* src, int64_t R, int64_t K, int64_t lds, void* codes,
+                           int64_t ldc, void* scales, hipStream_t stream) {
+  REQUIRE(R >= 0 && K > 0 && K % 128 == 0, MOE_ESHAPE,
+          "MXFP8 weight pack needs K %% 128 == 0 (K=%lld)", (long long)K);
+  REQUIRE(lds >= K && lds % 8 == 0 && ldc >= K && ldc % 8 == 0, MOE_ESHAPE,
+          "bad row strides (lds %% 8 == 0 and ldc %% 8 == 0 needed)");
+  REQUIRE(R * (K / 32) < (int64_t(1) << 31), MOE_ESHAPE, "MXFP8 weight scales must stay below 2 GiB");
+  REQUIRE(R == 0 || (src && codes && scales), MOE_EINVAL, "NULL pointer");
+  REQUIRE(reinterpret_cast<uintptr_t>(src) % 16 == 0 && reinterpret_cast<uintptr_t>(codes) % 8 == 0,
+          MOE_EINVAL, "src must be 16-byte and codes 8-byte aligned");
+  MOE_HIP(launch_quant_mx(src, R, K, lds, nullptr, nullptr, codes, ldc, scales, K / 32, R * 4, stream));
   return ok();
 }
 

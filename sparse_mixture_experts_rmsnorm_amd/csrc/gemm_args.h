@@ -102,12 +102,12 @@ struct PlanArgs {
   int cost_split;
 };
 
-// MXFP8 GEMM: X and W hold E4M3 codes (ldx / ldw in bytes).  ws: the
-// weights' E8M0 block scales, row-major [rows, K / 32] (ldws bytes per row);
-// xs: the activation rows' scales, stage-major (the four bytes of row r in
-// 128-element K stage s at s * ldxs + 4 r).  The first-linear epilogues write
-// MXFP8 h (codes to Y with ldy bytes, scales stage-major to ys with ldys
-// bytes between stages), the gate epilogues bf16 Y.
+// MXFP8 GEMM: X and W hold E4M3 codes (ldx / ldw in bytes).  ws / xs: the
+// weights' and the activation rows' E8M0 block scales, both stage-major (the
+// four bytes of row r in 128-element K stage s at s * ld + 4 r, ld = ldws /
+// ldxs = 4 x the rows of the array).  The first-linear epilogues write MXFP8
+// h (codes to Y with ldy bytes, scales stage-major to ys with ldys bytes
+// between stages), the gate epilogues bf16 Y.
 struct MxGemmArgs {
   GemmArgs g;
   const uint8_t* xs; int64_t ldxs;

@@ -204,16 +204,19 @@ __global__ void __launch_bounds__(512) k_gemm_mx(MxGemmArgs m) {
   // Scale words ride with the operands: the 4 E8M0 bytes of a row's stage
   // (K offsets are multiples of 128, so they are one aligned 32-bit word)
   // land after the operand tiles, W rows then X rows, one 4-byte DMA per
-  // wave (waves 0-3: W rows 64 w .. 64 w + 63, waves 4-7: X rows).  The
-  // weights' scales are row-major (a stage's words of consecutive rows are a
-  // row pitch apart); the activation rows' are stage-major (consecutive), so
-  // their DMA reads 256 contiguous bytes.
+  // wave (waves 0-3: W rows 64 w .. 64 w + 63, waves 4-7: X rows).  Both
+  // operands' scales are stage-major (the words of consecutive rows for one
+  // stage are adjacent), so each of these DMAs reads 256 contiguous bytes.
+  // The weights have ldws / 4 rows; a tile whose features run past the last
+  // row (a ragged last tile) reads the last row's word for them instead,
+  // which stays inside the array at every stage (those features are never
+  // stored).
   const bool wsc = wid < NW / 2;
   const __amdgpu_buffer_rsrc_t s_rsrc =
       wsc ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(m.ws), 0, int(m.ws_bytes), kRsrcWord3)
           : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(m.xs), 0, int(m.xs_bytes), kRsrcWord3);
   const int64_t srow_s = (wsc ? wid : wid - NW / 2) * 64 + lane;
-  const int s_step = wsc ? 4 : int(m.ldxs);     // bytes between a row's consecutive stages
+  const int s_step = int(wsc ? m.ldws : m.ldxs);  // bytes between a row's consecutive stages
   // this lane's offsets into its operand and scale rows for a tile (a K
   // piece starts at tile.kofs in the weights and tile.xk in the rows)
   uint32_t voff[2];                              // even / odd segments (swizzle parity)
@@ -225,7 +228,8 @@ __global__ void __launch_bounds__(512) k_gemm_mx(MxGemmArgs m) {
 #pragma unroll
     for (int p = 0; p < 2; ++p)
       voff[p] = uint32_t(rbase * ld + kbase + ((lane % C) ^ srow ^ p) * 16);
-    s_voff = wsc ? uint32_t((int64_t(t.wrow0) + srow_s) * m.ldws + t.kofs / 32)
+    s_voff = wsc ? uint32_t(min(int64_t(t.wrow0) + srow_s, m.ldws / 4 - 1) * 4 +
+                            int64_t(t.kofs / 128) * m.ldws)
                  : uint32_t((int64_t(t.row0) + srow_s) * 4 + int64_t(xk0 / 128) * m.ldxs);
   };
   auto issue = [&](int kt, int stage) {

@@ -1,8 +1,9 @@
 """One MoE FFN layer on the GPU: weight packing, descriptors, workspace.
 
 A thin owner of device buffers around the C ABI: it packs the weights once
-(moe_pack_transpose / moe_pack_swiglu), fills the moe_layer_desc and calls
-moe_layer_forward.  No arithmetic of the layer happens here.
+(moe_pack_transpose / moe_pack_swiglu / moe_pack_mxfp8_weights), fills the
+moe_layer_desc and calls moe_layer_forward.  No arithmetic of the layer
+happens here.
 """
 from __future__ import annotations
 
@@ -112,13 +113,14 @@ class MoELayer:
         w2t = torch.empty((d, F), dtype=self.tdtype, device=self.device)
         B.pack_transpose(params[n2], w2t)
         if quant == "mxfp8":
-            # E4M3 codes + E8M0 block scales along K of each packed row
+            # E4M3 codes + E8M0 block scales along K of each packed row (the
+            # scales stage-major, as the expert GEMMs read them)
             packed = []
             for w in (w13, w2t):
                 q = torch.empty(w.shape, dtype=torch.uint8, device=self.device)
-                sc = torch.empty((w.shape[0], w.shape[1] // 32), dtype=torch.uint8,
+                sc = torch.empty((w.shape[1] // 128, w.shape[0], 4), dtype=torch.uint8,
                                  device=self.device)
-                B.pack_mxfp8(w, q, sc)
+                B.pack_mxfp8_weights(w, q, sc)
                 packed.append((q, sc))
             torch.cuda.current_stream().synchronize()
             (w13, s13), (w2t, s2) = packed

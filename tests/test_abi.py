@@ -172,6 +172,24 @@ def test_mxfp8_pack_argument_checks():
     assert lib.moe_pack_mxfp8(None, 0, 64, 64, None, 64, None, 2, None) == 0   # nothing to do
 
 
+def test_mxfp8_weight_pack_argument_checks():
+    lib = B.lib()
+    P = C.c_void_p(256)
+    rc, msg = _err(lib.moe_pack_mxfp8_weights(P, 4, 96, 96, P, 96, P, None))
+    assert rc == -2 and "K % 128" in msg                    # stage-major words need K % 128
+    rc, msg = _err(lib.moe_pack_mxfp8_weights(P, 4, 128, 124, P, 128, P, None))
+    assert rc == -2 and "strides" in msg
+    rc, msg = _err(lib.moe_pack_mxfp8_weights(P, 4, 128, 128, P, 120, P, None))
+    assert rc == -2 and "strides" in msg
+    rc, _ = _err(lib.moe_pack_mxfp8_weights(P, 4, 128, 128, P, 128, None, None))
+    assert rc == -1
+    rc, msg = _err(lib.moe_pack_mxfp8_weights(C.c_void_p(264), 4, 128, 128, P, 128, P, None))
+    assert rc == -1 and "aligned" in msg
+    rc, msg = _err(lib.moe_pack_mxfp8_weights(P, 1 << 26, 1 << 12, 1 << 12, P, 1 << 12, P, None))
+    assert rc == -2 and "2 GiB" in msg
+    assert lib.moe_pack_mxfp8_weights(None, 0, 128, 128, None, 128, None, None) == 0
+
+
 def test_layer_workspace_validation():
     lib = B.lib()
     assert lib.moe_layer_workspace_size(None, 10) == 0

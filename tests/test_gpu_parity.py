@@ -721,6 +721,26 @@ def test_pack_mxfp8_bit_exact(dev):
     assert not c2[:, K:].any() and not s2[:, K // 32:].any()
 
 
+def test_pack_mxfp8_weights_layout(dev):
+    """moe_pack_mxfp8_weights (the expert weights' quantiser): the oracle's
+    OCP MX codes bit-exact, and its E8M0 scales bit-exact in the stage-major
+    layout the expert GEMMs read: byte j % 4 of row r's word in K stage j // 4,
+    at 4 ((j // 4) R + r) + j % 4."""
+    _say("[gpu] MXFP8 weight pack: codes and stage-major scales bit-exact")
+    bits = np.ascontiguousarray(_mx_pack_input()[:, :1024])      # R = 67, K = 8 stages
+    R, K = bits.shape
+    src = synth.to_device(bits, dev)
+    codes = torch.full((R, K), 0xAA, dtype=torch.uint8, device=dev)
+    scales = torch.full((K // 128, R, 4), 0xAA, dtype=torch.uint8, device=dev)
+    B.pack_mxfp8_weights(src, codes, scales)
+    torch.cuda.synchronize()
+    c_ref, s_ref = O.mx_quantize(O.as_f64(bits), axis=1)          # scales [R, K / 32]
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
+    got = scales.cpu().numpy()
+    for j in range(K // 32):
+        assert np.array_equal(got[j // 4, :, j % 4], s_ref[:, j]), j
+
+
 @pytest.mark.parametrize("d,T", [(384, 77), (256, 300), (1536, 40), (4096, 33)])
 def test_dense_router_k_splits(dev, d, T):
     """bf16 router with each workgroup shape (the K range of d split over 4,
