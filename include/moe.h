@@ -123,6 +123,13 @@ typedef struct moe_experts_desc {
   const int32_t* ffn_offsets;   /* [E+1] device copy of their prefix sum     */
   const void* w13_t;            /* packed first linear(s)                    */
   const void* w2_t;             /* packed second linear [d, F]               */
+  int64_t w2_ld;                /* row stride of w2_t in elements; 0: F.
+                                 * >= F, a multiple of 16 bytes, d * w2_ld
+                                 * below 2 GiB for MXFP8.  The MXFP8 second
+                                 * linear ran 13% faster on a Mixtral-sized
+                                 * layer with F + 256 (what the layer uses)
+                                 * than with F = 114688, where every row
+                                 * starts on the same low 14 address bits    */
   const void* W;                /* ATOMIC: [E, d]                             */
   const void* V;                /* ATOMIC: [E, d]                             */
   int block;                    /* BCSR block size (128)                     */

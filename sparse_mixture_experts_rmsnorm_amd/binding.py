@@ -42,7 +42,8 @@ class RouterDesc(C.Structure):
 class ExpertsDesc(C.Structure):
     _fields_ = [("kind", C.c_int), ("act", C.c_int), ("E", C.c_int64),
                 ("ffn_sizes", C.POINTER(C.c_int64)), ("ffn_offsets", C.c_void_p),
-                ("w13_t", C.c_void_p), ("w2_t", C.c_void_p), ("W", C.c_void_p), ("V", C.c_void_p),
+                ("w13_t", C.c_void_p), ("w2_t", C.c_void_p), ("w2_ld", C.c_int64),
+                ("W", C.c_void_p), ("V", C.c_void_p),
                 ("block", C.c_int), ("size_blocks", C.c_void_p), ("block_offsets", C.c_void_p),
                 ("row_offsets", C.c_void_p), ("column_indices", C.c_void_p),
                 ("quant", C.c_int), ("w13_scale", C.c_void_p), ("w2_scale", C.c_void_p),

@@ -88,6 +88,7 @@ struct ExpertGeo {
   bool mx = false;     // MXFP8 operands (E4M3 codes + E8M0 block scales)
   int kdiv = 1;        // largest second-linear K split (1, 2 or 4) whose parts are
                        // whole K stages of every expert
+  int64_t ld2 = 0;     // row stride of w2_t (elements)
 };
 
 int check_experts(const moe_experts_desc* X, int dtype, int64_t d, ExpertGeo* g) {
@@ -159,6 +160,15 @@ int check_experts(const moe_experts_desc* X, int dtype, int64_t d, ExpertGeo* g)
               (long long)X->ffn_sizes[e]);
     // the kernels address operands with 32-bit byte offsets
     REQUIRE(geo.F * geo.pf * d < (int64_t(1) << 31) && geo.F * d < (int64_t(1) << 31), MOE_ESHAPE,
+            "MXFP8 weights must stay below 2 GiB per matrix");
+  }
+  geo.ld2 = X->w2_ld ? X->w2_ld : geo.F;
+  {
+    const int64_t eb = geo.mx ? 1 : esize(dtype);
+    REQUIRE(geo.ld2 >= geo.F && (geo.ld2 * eb) % 16 == 0, MOE_ESHAPE,
+            "w2_ld must be >= F (%lld) and a multiple of 16 bytes (got %lld)", (long long)geo.F,
+            (long long)X->w2_ld);
+    REQUIRE(!geo.mx || geo.ld2 * d < (int64_t(1) << 31), MOE_ESHAPE,
             "MXFP8 weights must stay below 2 GiB per matrix");
   }
   // K stage of the second linear: 64 elements (bf16), 128 (MXFP8)
@@ -397,7 +407,7 @@ int run_expert_gemms_mx(const moe_experts_desc* X, const ExpertGeo& g, int64_t d
   b.g.X = w.hq;
   b.g.ldx = g.Fmax;
   b.g.W = X->w2_t;
-  b.g.ldw = g.F;
+  b.g.ldw = g.ld2;
   b.g.tiles = w.tiles2;
   b.g.ntiles = w.nt + 16;
   b.g.Y = y;
@@ -412,7 +422,7 @@ int run_expert_gemms_mx(const moe_experts_desc* X, const ExpertGeo& g, int64_t d
   b.ws = X->w2_scale;
   b.ldws = d * 4;
   b.x_bytes = RP * g.Fmax;
-  b.w_bytes = d * g.F;
+  b.w_bytes = d * g.ld2;
   b.xs_bytes = RP * (g.Fmax / 32);
   b.ws_bytes = d * (g.F / 32);
   MOE_HIP(launch_gemm_mx(b, w.grid2 > 0 ? w.grid2 : int(w.mt2), s));
@@ -500,7 +510,7 @@ int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, i
   b.X = w.h;
   b.ldx = g.Fmax;
   b.W = X->w2_t;
-  b.ldw = g.F;
+  b.ldw = g.ld2;
   b.tiles = w.tiles2;
   b.ntiles = w.nt + 16;
   b.Y = y;

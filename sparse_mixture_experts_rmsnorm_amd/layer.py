@@ -12,6 +12,9 @@ import ctypes as C
 from . import binding as B
 from .workloads import Workload
 
+# Row padding (bytes) of the MXFP8 second-linear weight codes.
+MX_W2_PAD = 256
+
 
 class MoELayer:
     def __init__(self, wl: Workload, params: dict, device="cuda", train: bool = False):
@@ -114,16 +117,22 @@ class MoELayer:
         B.pack_transpose(params[n2], w2t)
         if quant == "mxfp8":
             # E4M3 codes + E8M0 block scales along K of each packed row (the
-            # scales stage-major, as the expert GEMMs read them)
+            # scales stage-major, as the expert GEMMs read them).  The code
+            # rows of the second linear (F bytes, a multiple of 128) get
+            # MX_W2_PAD bytes of row padding (w2_ld): with F a multiple of a
+            # large power of two, the rows one K step of a weight tile reads
+            # would all start on the same low address bits, which measured
+            # markedly slower.
             packed = []
-            for w in (w13, w2t):
-                q = torch.empty(w.shape, dtype=torch.uint8, device=self.device)
-                sc = torch.empty((w.shape[1] // 128, w.shape[0], 4), dtype=torch.uint8,
-                                 device=self.device)
-                B.pack_mxfp8_weights(w, q, sc)
+            for w, pad in ((w13, 0), (w2t, MX_W2_PAD)):
+                R, K = w.shape
+                q = torch.empty((R, K + pad), dtype=torch.uint8, device=self.device)
+                sc = torch.empty((K // 128, R, 4), dtype=torch.uint8, device=self.device)
+                B.pack_mxfp8_weights(w, q[:, :K], sc)
                 packed.append((q, sc))
             torch.cuda.current_stream().synchronize()
             (w13, s13), (w2t, s2) = packed
+            X.w2_ld = F + MX_W2_PAD
             X.quant = B.QUANT_MXFP8
             X.w13_scale = s13.data_ptr()
             X.w2_scale = s2.data_ptr()

@@ -148,6 +148,19 @@ def test_expert_descriptor_checks():
     X.block, X.size_blocks, X.block_offsets = 128, 16, 16
     assert lib.moe_expert_workspace_size(C.byref(X), 1, 512, 100, 2, 256) > 0    # MXFP8 BCSR
     X.kind, X.block, X.size_blocks, X.block_offsets = 0, 0, None, None
+    # w2_ld: 0 (dense) or a stride >= F in whole 16-byte units
+    X.w2_ld = 512                                                                 # < F = 640
+    assert lib.moe_expert_workspace_size(C.byref(X), 1, 512, 100, 2, 200) == 0
+    assert "w2_ld" in B.last_error()
+    X.w2_ld = 648                                                                 # MXFP8: 648 B
+    assert lib.moe_expert_workspace_size(C.byref(X), 1, 512, 100, 2, 200) == 0
+    X.w2_ld = 656
+    assert lib.moe_expert_workspace_size(C.byref(X), 1, 512, 100, 2, 200) > 0
+    X.quant, X.w2_ld = 0, 644                                                     # bf16: 1288 B
+    assert lib.moe_expert_workspace_size(C.byref(X), 1, 512, 100, 2, 200) == 0
+    X.w2_ld = 648
+    assert lib.moe_expert_workspace_size(C.byref(X), 1, 512, 100, 2, 200) > 0
+    X.quant, X.w2_ld = B.QUANT_MXFP8, 0
     sizes2 = B.i64_array([320, 256])
     X.ffn_sizes = C.cast(sizes2, C.POINTER(C.c_int64))
     assert lib.moe_expert_workspace_size(C.byref(X), 1, 512, 100, 2, 200) == 0

@@ -721,6 +721,35 @@ def test_pack_mxfp8_bit_exact(dev):
     assert not c2[:, K:].any() and not s2[:, K // 32:].any()
 
 
+@pytest.mark.parametrize("name", ["mixtral_small", "mixtral_small_mxfp8", "bcsr_small_mxfp8"])
+def test_w2_row_stride(dev, name):
+    """A padded row stride of w2_t (w2_ld) changes where the second linear
+    reads its weights, not what it computes: the layer output is bit-identical
+    with w2_t repacked at another stride (bf16: dense -> padded by 64
+    elements; MXFP8, which the layer pads by 256 bytes: padded -> dense, and
+    -> padded by 4 KB)."""
+    _say(f"[gpu] w2_ld restride: {name}")
+    wl, inp, params, layer = _setup(name, dev)
+    x = params["x"]
+    ref = layer.forward(x).clone()
+    X = layer.desc.experts
+    F = sum(wl.sizes)
+    d = wl.d
+    eb = 1 if wl.quant == "mxfp8" else 2
+    ld0 = X.w2_ld or F
+    old = [t for t in layer._keep if hasattr(t, "data_ptr") and t.data_ptr() == X.w2_t][0]
+    cur = old.view(torch.uint8).view(d, ld0 * eb)[:, :F * eb]
+    pads = [0, 4096] if wl.quant == "mxfp8" else [128]
+    for pad in pads:
+        w = torch.zeros((d, F * eb + pad), dtype=torch.uint8, device=dev)
+        w[:, :F * eb] = cur
+        X.w2_t, X.w2_ld = w.data_ptr(), (F * eb + pad) // eb if pad else 0
+        out = layer.forward(x)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), pad
+    X.w2_t, X.w2_ld = old.data_ptr(), (ld0 if ld0 != F else 0)
+
+
 def test_pack_mxfp8_weights_layout(dev):
     """moe_pack_mxfp8_weights (the expert weights' quantiser): the oracle's
     OCP MX codes bit-exact, and its E8M0 scales bit-exact in the stage-major
