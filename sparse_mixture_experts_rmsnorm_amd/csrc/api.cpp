@@ -341,11 +341,12 @@ void carve_expert_ws(Carve& c, const ExpertGeo& g, int dtype, int64_t d, int64_t
 
 // Launch the two expert GEMMs of a grouped / BCSR expert set over the rows of
 // a routing (or, for the shared FFN, one dense group of T rows).
+// x_rows: the rows of x_in (the token rows when xrow gathers them).
 int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, int64_t d,
                      const int32_t* offsets, int dense_rows, const int32_t* row_offsets,
-                     const int32_t* column_indices, const void* x_in, const float* row_r,
-                     const float* row_w, void* y, const ExpertWs& w, hipStream_t s,
-                     moe_timer* timer, int call, const int32_t* xrow = nullptr);
+                     const int32_t* column_indices, const void* x_in, int64_t x_rows,
+                     const float* row_r, const float* row_w, void* y, const ExpertWs& w,
+                     hipStream_t s, moe_timer* timer, int call, const int32_t* xrow = nullptr);
 
 }  // namespace
 
@@ -434,9 +435,9 @@ int run_expert_gemms_mx(const moe_experts_desc* X, const ExpertGeo& g, int64_t d
 
 int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, int64_t d,
                      const int32_t* offsets, int dense_rows, const int32_t* row_offsets,
-                     const int32_t* column_indices, const void* x_in, const float* row_r,
-                     const float* row_w, void* y, const ExpertWs& w, hipStream_t s,
-                     moe_timer* timer, int call, const int32_t* xrow) {
+                     const int32_t* column_indices, const void* x_in, int64_t x_rows,
+                     const float* row_r, const float* row_w, void* y, const ExpertWs& w,
+                     hipStream_t s, moe_timer* timer, int call, const int32_t* xrow) {
   PlanArgs p{};
   p.offsets = offsets;
   p.dense_rows = dense_rows;
@@ -503,6 +504,8 @@ int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, i
   a.xcd_runs = w.grid1 > 0;
   a.part = w.part;
   a.counters = w.counters;
+  a.x_bytes = x_rows * d * int64_t(esize(dtype));
+  a.w_bytes = g.F * g.pf * d * int64_t(esize(dtype));
   MOE_HIP(launch_gemm(dtype, a, g.bf1, g.bt, w.grid1 > 0 ? w.grid1 : int(w.mt1), s));
   timer_mark(timer, call, MOE_STAGE_GEMM1 + 1, s);
 
@@ -521,6 +524,8 @@ int run_expert_gemms(const moe_experts_desc* X, const ExpertGeo& g, int dtype, i
   b.xcd_runs = w.grid2 > 0;
   b.part = w.part;
   b.counters = w.counters;
+  b.x_bytes = w.rows_max * g.Fmax * int64_t(esize(dtype));
+  b.w_bytes = d * g.ld2 * int64_t(esize(dtype));
   MOE_HIP(launch_gemm(dtype, b, g.bf2, g.bt2, w.grid2 > 0 ? w.grid2 : int(w.mt2), s));
   if (w.pieces2) MOE_HIP(launch_piece_fixup(b, g.bf2, g.bt2, w.grid2, kMaxParts2, s));
   timer_mark(timer, call, MOE_STAGE_GEMM2 + 1, s);
@@ -760,6 +765,8 @@ int router_run(const moe_router_desc* R, const void* x, int dtype, int64_t T, in
     a.ldy = R->Nr + R->Nc;
     a.row_r = r;
     a.epi = EPI_SCALE_F32;
+    a.x_bytes = T * d * int64_t(esize(dtype));
+    a.w_bytes = (R->Nr + R->Nc) * d * int64_t(esize(dtype));
     MOE_HIP(launch_gemm(dtype, a, 256, 256, int(ntile_max), stream));
   }
   MOE_HIP(launch_cartesian_topk(scores, T, R->Nr, R->Nc, k, renorm, ids, w, stream));
@@ -943,7 +950,7 @@ int moe_expert_gemm(const moe_experts_desc* X, int dtype, int64_t d, const moe_r
     return ok();
   }
   rc = run_expert_gemms(X, g, dtype, d, rt->offsets, 0, X->row_offsets, X->column_indices, x_in,
-                        rt->row_r, rt->row_w, y, w, stream, nullptr, -1);
+                        rt->rows_max, rt->row_r, rt->row_w, y, w, stream, nullptr, -1);
   return rc ? rc : ok();
 }
 
@@ -973,8 +980,8 @@ int moe_shared_ffn(const moe_experts_desc* S, int dtype, int64_t d, int64_t T, c
   ExpertWs w;
   carve_expert_ws(c, g, dtype, d, T, 0, &w);
   fit_dense_tiles(&g, dtype, d, T);
-  rc = run_expert_gemms(S, g, dtype, d, nullptr, int(T), nullptr, nullptr, xhat, r, nullptr, s, w,
-                        stream, nullptr, -1);
+  rc = run_expert_gemms(S, g, dtype, d, nullptr, int(T), nullptr, nullptr, xhat, T, r, nullptr, s,
+                        w, stream, nullptr, -1);
   return rc ? rc : ok();
 }
 
@@ -1261,15 +1268,15 @@ int moe_layer_forward(const moe_layer_desc* L, const void* x, int64_t T, void* o
       MOE_HIP(launch_topology(w.offsets, L->experts.size_blocks, L->experts.block_offsets, E, 128,
                               w.rows_max, w.row_offsets, w.column_indices, w.nnz, stream));
     rc = run_expert_gemms(&L->experts, g, L->dtype, d, w.offsets, 0, w.row_offsets, w.column_indices,
-                          xhat, w.row_r, w.row_w, w.y, w.ex, stream, tm, call, w.row_token);
+                          xhat, T, w.row_r, w.row_w, w.y, w.ex, stream, tm, call, w.row_token);
     if (rc) return rc;
   }
   // shared experts: dense, gate 1, r in the first epilogue
   if (L->shared && T > 0) {
     ExpertGeo gt = gs;
     fit_dense_tiles(&gt, L->dtype, d, T);
-    rc = run_expert_gemms(L->shared, gt, L->dtype, d, nullptr, int(T), nullptr, nullptr, xhat, w.r,
-                          nullptr, w.s, w.sh, stream, nullptr, -1);
+    rc = run_expert_gemms(L->shared, gt, L->dtype, d, nullptr, int(T), nullptr, nullptr, xhat, T,
+                          w.r, nullptr, w.s, w.sh, stream, nullptr, -1);
     if (rc) return rc;
   }
   timer_mark(tm, call, MOE_STAGE_SHARED + 1, stream);
@@ -1478,6 +1485,8 @@ int run_expert_bwd(const ExpertBwdIo& io, int64_t d, int64_t T, const void* dout
   a.Y = io.tbuf;
   a.ldy = g.Fmax;
   a.epi = EPI_STORE_T;
+  a.x_bytes = T * d * 2;
+  a.w_bytes = g.F * d * 2;
   MOE_HIP(launch_gemm(MOE_BF16, a, 256, 256, int(io.mt_b1), s));
   ActBwdArgs ab{};
   ab.t = static_cast<const uint16_t*>(io.tbuf);
@@ -1516,13 +1525,16 @@ int run_expert_bwd(const ExpertBwdIo& io, int64_t d, int64_t T, const void* dout
   b.ysplit = io.plane;
   b.row_r = io.row_r;
   b.epi = EPI_SCALE_F32;
+  b.x_bytes = io.rows * Pmax * 2;
+  b.w_bytes = d * g.F * g.pf * 2;
   MOE_HIP(launch_gemm(MOE_BF16, b, 256, 256, int(io.mt_b2), s));
   return MOE_OK;
 }
 
-// Y [xrows, d] = sum over each segment's rows of X^T W (fp32, plain).
-int run_wgrad(WgradPlanArgs wp, const uint16_t* X, int64_t ldx, const uint16_t* W,
-              int64_t ldw, float* Y, int64_t ldy, hipStream_t s) {
+// Y [xrows, d] = sum over each segment's rows of X^T W (fp32, plain); X has
+// xrows rows and W wrows rows.
+int run_wgrad(WgradPlanArgs wp, const uint16_t* X, int64_t ldx, int64_t xrows, const uint16_t* W,
+              int64_t ldw, int64_t wrows, float* Y, int64_t ldy, hipStream_t s) {
   wp.tile = kWgTile;
   MOE_HIP(launch_plan_wgrad(wp, s));
   GemmArgs a{};
@@ -1535,6 +1547,8 @@ int run_wgrad(WgradPlanArgs wp, const uint16_t* X, int64_t ldx, const uint16_t* 
   a.Y = Y;
   a.ldy = ldy;
   a.epi = EPI_SCALE_F32;
+  a.x_bytes = xrows * ldx * 2;
+  a.w_bytes = wrows * ldw * 2;
   MOE_HIP(launch_gemm(MOE_BF16, a, kWgTile, kWgTile, wp.max_tiles, s));
   return MOE_OK;
 }
@@ -1647,13 +1661,13 @@ int moe_layer_backward(const moe_layer_desc* L, const void* x, int64_t T, const 
     wp.tiles = b.tiles[2];
     wp.ntiles = b.nt + 2;
     wp.max_tiles = int(b.mt[2]);
-    rc = run_wgrad(wp, b.dpreT, b.L, b.rxT, b.L, grads->dw13, d, stream);
+    rc = run_wgrad(wp, b.dpreT, b.L, g.F * g.pf, b.rxT, b.L, E * d, grads->dw13, d, stream);
     if (rc) return rc;
     wp.xmul = 1;
     wp.tiles = b.tiles[3];
     wp.ntiles = b.nt + 3;
     wp.max_tiles = int(b.mt[3]);
-    rc = run_wgrad(wp, b.hT, b.L, b.dyT, b.L, grads->dw2, d, stream);
+    rc = run_wgrad(wp, b.hT, b.L, g.F, b.dyT, b.L, E * d, grads->dw2, d, stream);
     if (rc) return rc;
   }
 
@@ -1719,13 +1733,13 @@ int moe_layer_backward(const moe_layer_desc* L, const void* x, int64_t T, const 
     wp.tiles = b.tiles[7];
     wp.ntiles = b.nt + 7;
     wp.max_tiles = int(b.mt[7]);
-    rc = run_wgrad(wp, b.dpreT_s, b.Tpad, b.rxT_all, b.Tpad, grads->dws13, d, stream);
+    rc = run_wgrad(wp, b.dpreT_s, b.Tpad, Ps, b.rxT_all, b.Tpad, d, grads->dws13, d, stream);
     if (rc) return rc;
     wp.xfix = int(gs.F);
     wp.tiles = b.tiles[8];
     wp.ntiles = b.nt + 8;
     wp.max_tiles = int(b.mt[8]);
-    rc = run_wgrad(wp, b.hT_s, b.Tpad, b.GT, b.Tpad, grads->dws2, d, stream);
+    rc = run_wgrad(wp, b.hT_s, b.Tpad, gs.F, b.GT, b.Tpad, d, grads->dws2, d, stream);
     if (rc) return rc;
   }
 
@@ -1758,7 +1772,7 @@ int moe_layer_backward(const moe_layer_desc* L, const void* x, int64_t T, const 
     wp.tiles = b.tiles[4];
     wp.ntiles = b.nt + 4;
     wp.max_tiles = int(b.mt[4]);
-    rc = run_wgrad(wp, b.dlT, b.Tpad, b.rxT_all, b.Tpad, grads->dw_router, d, stream);
+    rc = run_wgrad(wp, b.dlT, b.Tpad, E, b.rxT_all, b.Tpad, d, grads->dw_router, d, stream);
     if (rc) return rc;
     if (grads->dbias) MOE_HIP(launch_colsum(b.dl, T, E, E, grads->dbias, stream));
   }

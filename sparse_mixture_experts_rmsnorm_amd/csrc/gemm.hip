@@ -27,9 +27,10 @@
 // 4 x 2 grid of 64 x 128 wave tiles; a 4-wave 256 x 128 variant serves
 // dense second linears with fewer 256-row tiles than compute units).
 // Operands are both K-contiguous (weights packed as [features, K]) and move
-// global -> LDS by the global_load_lds_dwordx4 DMA into LDS rings (three
+// global -> LDS by the buffer_load_dwordx4 ... lds DMA into LDS rings (three
 // stages of weights, two of activations) with a 16-byte-chunk XOR swizzle
-// (conflict-free for the 64-bank LDS), so no registers are spent on staging.  v_mfma_f32_32x32x16_bf16 takes the
+// (conflict-free for the 64-bank LDS), so no registers are spent on staging.
+// v_mfma_f32_32x32x16_bf16 takes the
 // weights as the A operand (features = MFMA rows) and tokens as B (MFMA
 // columns), so a lane's accumulators hold four consecutive features of one
 // token and the epilogue stores 8 bytes per group.  Fragments of the next
@@ -238,11 +239,23 @@ __global__ void __launch_bounds__(256) k_piece_fixup(GemmArgs a) {
         make_uint2(pk_bf16(rs * acc[q][0], rs * acc[q][1]), pk_bf16(rs * acc[q][2], rs * acc[q][3]));
 }
 
+// Word 3 of a raw buffer resource on gfx9 (32-bit data format, no swizzle;
+// reads past num_records return zero).
+constexpr int kRsrcWord3Raw = 0x00020000;
+
+// One 16-byte-per-lane DMA from a buffer resource into LDS (lane i's bytes
+// at dst + 16 i).  Kept out of line of the kernel template: with the builtin
+// written in the template's lambdas, the host pass emitted no launch stubs.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_void_ptr dst, uint32_t voff,
+                                      int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
+}
+
 // ---------------------------------------------------------------- bf16 MFMA GEMM, LDS-DMA ring
 
 // BF features x BT rows per workgroup, WGF x WGT waves, each wave a
 // (BF / WGF) x (BT / WGT) sub-tile of 32 x 32 MFMA blocks, K in stages of 64.
-// Global -> LDS moves by the global_load_lds_dwordx4 DMA (each wave
+// Global -> LDS moves by the buffer_load_dwordx4 ... lds DMA (each wave
 // instruction writes 1 KB of LDS, lane i at byte 16 i).  The weights go
 // through a ring of three LDS stages and the activation rows through two
 // (3 x 32 KB + 2 x 32 KB = the whole 160 KB of a CU at 256 x 256): the
@@ -300,10 +313,17 @@ __global__ void __launch_bounds__(64 * WGF * WGT, 1) k_gemm_bf16_dma(GemmArgs a)
   const int srow = lane / C;                  // row within a segment
   const int fr = lane & 31, fh = lane >> 5, fswz = chunk_swz<C>(lane & 15);
 
-  // this lane's source address inside each of its wave's segments (loop
-  // invariant within a tile; a K step only adds kt * BKD)
-  const uint16_t* srcw[SPW];
-  const uint16_t* srcx[SPX];
+  // Operands through raw buffer resources over the whole weight and
+  // activation arrays (x_bytes, w_bytes: each below 4 GiB): a 32-bit byte
+  // offset per lane and segment, set per tile, and the stage step in the
+  // scalar offset.  Every address stays inside the arrays (rows are clamped
+  // to the tile's last row, gathered rows are token rows, weight rows end at
+  // a whole tile); the extents make the hardware return zeros past them.
+  const __amdgpu_buffer_rsrc_t rw =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(W), 0, int(uint32_t(a.w_bytes)), kRsrcWord3Raw);
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(X), 0, int(uint32_t(a.x_bytes)), kRsrcWord3Raw);
+  uint32_t vw[SPW], vx[SPX];
   auto set_sources = [&](const Tile& t) {
     const int xlast = t.row_end - 1;
     // a K-split tile reads its own part of the activation row
@@ -314,7 +334,7 @@ __global__ void __launch_bounds__(64 * WGF * WGT, 1) k_gemm_bf16_dma(GemmArgs a)
       // a partial feature tile (EPI_STORE_T) reads its last existing weight
       // row in place of the missing ones
       const int wr = EPI == EPI_STORE_T ? min(row, t.spare - 1) : row;
-      srcw[u] = W + int64_t(t.wrow0 + wr) * a.ldw + t.kofs + ((lane % C) ^ chunk_swz<C>(row)) * 8;
+      vw[u] = uint32_t((int64_t(t.wrow0 + wr) * a.ldw + t.kofs + ((lane % C) ^ chunk_swz<C>(row)) * 8) * 2);
     }
 #pragma unroll
     for (int u = 0; u < SPX; ++u) {
@@ -323,22 +343,20 @@ __global__ void __launch_bounds__(64 * WGF * WGT, 1) k_gemm_bf16_dma(GemmArgs a)
       // fused here)
       int xr = min(t.row0 + row, xlast);
       if (a.xrow) xr = max(a.xrow[xr], 0);
-      srcx[u] = X + int64_t(xr) * a.ldx + xk0 + ((lane % C) ^ chunk_swz<C>(row)) * 8;
+      vx[u] = uint32_t((int64_t(xr) * a.ldx + xk0 + ((lane % C) ^ chunk_swz<C>(row)) * 8) * 2);
     }
   };
   auto issue_w = [&](int kt, int buf) {
     uint16_t* base = lds + buf * WS;
 #pragma unroll
     for (int u = 0; u < SPW; ++u)
-      __builtin_amdgcn_global_load_lds((global_void_ptr)(srcw[u] + kt * BKD),
-                                       (lds_void_ptr)(base + (wid * SPW + u) * 512), 16, 0, 0);
+      dma16(rw, (lds_void_ptr)(base + (wid * SPW + u) * 512), vw[u], kt * BKD * 2);
   };
   auto issue_x = [&](int kt, int buf) {
     uint16_t* base = ldsx + buf * XS;
 #pragma unroll
     for (int u = 0; u < SPX; ++u)
-      __builtin_amdgcn_global_load_lds((global_void_ptr)(srcx[u] + kt * BKD),
-                                       (lds_void_ptr)(base + (wid * SPX + u) * 512), 16, 0, 0);
+      dma16(rx, (lds_void_ptr)(base + (wid * SPX + u) * 512), vx[u], kt * BKD * 2);
   };
   // stages 0 and 1 of both operands and stage 2 of the weights (past the
   // last stage a load repeats stage nk - 1, in bounds, into a buffer that is
@@ -1138,6 +1156,10 @@ hipError_t launch_gemm(int dtype, const GemmArgs& a, int bf, int bt, int grid, h
     return hipGetLastError();
   }
   if (bf != 256 || (bt != 256 && bt != 128)) return hipErrorInvalidValue;
+  // (an extent of 0 is an empty operand: a launch over no rows reads nothing)
+  if (a.x_bytes < 0 || a.w_bytes < 0 || a.x_bytes >= (int64_t(1) << 32) ||
+      a.w_bytes >= (int64_t(1) << 32))
+    return hipErrorInvalidValue;
   if (bt == 256) {
     const dim3 b8(512);
     switch (a.epi) {

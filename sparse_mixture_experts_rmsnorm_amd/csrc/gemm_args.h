@@ -62,6 +62,11 @@ struct GemmArgs {
   int xcd_runs;
   float* part;
   int* counters;
+  // Bytes of X and W from their bases that the launch may read.  The bf16
+  // kernel reads both through buffer resources with 32-bit offsets, so both
+  // must be below 4 GiB (launch_gemm refuses the launch otherwise); the
+  // hardware returns zeros for anything past them, so every call sets them.
+  int64_t x_bytes, w_bytes;
 };
 
 // Plan of GEMM tiles for grouped experts.  gemm = 1: first linear (features
