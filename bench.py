@@ -30,39 +30,39 @@ PEAK_HBM_GBPS = 8000.0
 # HBM bytes per launch of the first expert GEMM, per workload, from two
 # rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) scaled by
 # what the same counters read for a plain 1 GiB device copy
-# (bench.py --copy-calibration: FETCH_SIZE 524302.4 KiB, WRITE_SIZE 1048576 KiB).
+# (bench.py --copy-calibration: FETCH_SIZE 524302.2 KiB, WRITE_SIZE 1048576 KiB).
 # The mean over the first 18 launches of the run (warm-up, stage-timer and
 # timed forwards on the workload's own routing; the router-extras pass after
 # them routes with noise and is left out).  Valid only for the kernel sources
 # they were taken on: any change to those files reports null.
-COPY_SCALE = {"fetch": 1048576.0 / 524302.4, "write": 1048576.0 / 1048576.0}
+COPY_SCALE = {"fetch": 1048576.0 / 524302.2, "write": 1048576.0 / 1048576.0}
 TRAFFIC = {
     "mixtral_bf16": {
         "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
                                                  "common.h"),
-        "source_sha256": "6d55dd23ea83ad24283f02f1eccec2aea8e6342392c6bb2056c263958e541398",
-        "fetch_kib": 1854707.4, "write_kib": 230445.7},
+        "source_sha256": "ce5c4f874d5a9d58f02235c7bc1837e814967bee547c97cc86894d7cf28d43dc",
+        "fetch_kib": 1980109.6, "write_kib": 229436.5},
     "variable_bcsr_bf16": {
         "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
                                                  "common.h"),
-        "source_sha256": "6d55dd23ea83ad24283f02f1eccec2aea8e6342392c6bb2056c263958e541398",
-        "fetch_kib": 30459.9, "write_kib": 47397.9},
+        "source_sha256": "ce5c4f874d5a9d58f02235c7bc1837e814967bee547c97cc86894d7cf28d43dc",
+        "fetch_kib": 30436.4, "write_kib": 45981.9},
     # the routed first GEMM only (the shared experts' first GEMM is the same
     # kernel; the dispatches alternate, routed first)
     "finegrained_bf16": {
         "kernel": "k_gemm_bf16_dma", "sources": ("gemm.hip", "gemm_args.h", "gemm_common.h",
                                                  "common.h"),
-        "source_sha256": "6d55dd23ea83ad24283f02f1eccec2aea8e6342392c6bb2056c263958e541398",
-        "fetch_kib": 756049.4, "write_kib": 114982.1},
+        "source_sha256": "ce5c4f874d5a9d58f02235c7bc1837e814967bee547c97cc86894d7cf28d43dc",
+        "fetch_kib": 774602.6, "write_kib": 113961.4},
     "atomic_bf16": {
         "kernel": "k_atomic_token", "sources": ("atomic.hip", "common.h"),
         "source_sha256": "7020a44046cfa9c4bc2ee1d7087ff80709367bd331479c1dadda27f72bc9993a",
-        "fetch_kib": 535685.2, "write_kib": 16384.0},
+        "fetch_kib": 535664.1, "write_kib": 16384.0},
     "mixtral_mxfp8": {
         "kernel": "k_gemm_mx", "sources": ("gemm_mx.hip", "gemm_args.h", "gemm_common.h",
                                            "common.h"),
-        "source_sha256": "9ff5c40b6054037be4b33fb85cf5877ddb426fdbd9d379c1612445c21f1e122a",
-        "fetch_kib": 903643.9, "write_kib": 118331.2},
+        "source_sha256": "53018a0e8943184f34489804a04727993c74fdc252bc922f7112adc20271ab4a",
+        "fetch_kib": 905508.5, "write_kib": 118332.6},
 }
 
 
