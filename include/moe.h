@@ -114,7 +114,11 @@ typedef struct moe_router_desc {
  *          moe_build_topology over block x block tiles (dispatch pad = block).
  * ATOMIC:  N = E single-unit experts: routed[t] = sum_j g * act(r xhat.W[n]) V[n].
  * Constraints (else MOE_ESHAPE): d % 256 == 0 for bf16 (d % 64 for f32);
- * every ffn size a multiple of 128 (of 32 for f32); ATOMIC d % 512 == 0. */
+ * every ffn size a multiple of 128 (of 32 for f32); ATOMIC d % 512 == 0.
+ * The bf16 GEMMs address each operand array (the GEMM rows, x or its
+ * gathered token rows, the hidden activation h, each packed weight matrix)
+ * with 32-bit byte offsets: each must stay below 4 GiB, else the GEMM's
+ * launch is refused and the call returns MOE_EHIP (invalid argument). */
 typedef struct moe_experts_desc {
   int kind;                     /* MOE_EXPERTS_*                             */
   int act;                      /* MOE_ACT_* (ATOMIC: GELU or GELU_TANH)     */
